@@ -1,0 +1,198 @@
+"""Double-precision CPU oracle for entropic OT between point clouds.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  The GPU library
+(``sinkhorn_point_cloud_amd``) never imports, links or calls it, and the two
+share no code.
+
+The arithmetic lives in ``sinkhorn_oracle.c`` (plain C99, fp64, OpenMP over
+rows); this module only marshals numpy arrays to it.  What each function
+computes, and which page/section it follows, is documented in that file:
+
+  [FS] "FlashSinkhorn: IO-bewuste Entropische Optimale Transport op GPU",
+       Methodologie 1 (Propositie 1): the log-domain f-update and its attention
+       form; the g-update is its mirror.
+  [AP] "From Theory to Throughput: CUDA-Optimized APML for Large-Batch 3D
+       Learning", Abstract / Innovation: thresholded sparse (COO) plan, loss
+       and gradient on the stored support.
+
+Parity status of each function (what pins it) is listed in ``PINS`` below;
+every entry has at least one pin in ``tests/test_oracle_pins.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "sinkhorn_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+PINS = {
+    "half_update": "scipy logsumexp; brute-force assignment; 2x2 closed form; marginals",
+    "potentials(direct)": "marginals at convergence; brute-force OT bound; large-eps limit;"
+                          " n=1; 2x2 closed form; translation and swap invariance",
+    "potentials(attention)": "agrees with the direct form (two different computations)",
+    "plan_stats": "dense numpy enumeration; strong duality at convergence",
+    "plan_coo": "dense numpy enumeration on small shapes",
+    "loss_grad": "finite differences of the dual (envelope theorem); dense sums",
+}
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (fp64, -O2, OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
+                               "-Wall", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i32, i64, f64 = ctypes.c_int, ctypes.c_int64, ctypes.c_double
+        lib.oracle_num_threads.restype = i32
+        lib.oracle_half_update.argtypes = [P, i32, P, i32, i32, P, P, f64, P, i32, P]
+        lib.oracle_half_update.restype = None
+        lib.oracle_potentials.argtypes = [P, P, P, P, i32, i32, i32, i32, P, P, i32, i32, i32,
+                                          P, P]
+        lib.oracle_potentials.restype = i32
+        lib.oracle_plan_stats.argtypes = [P, P, P, P, P, P, f64, i32, i32, i32, i32, P]
+        lib.oracle_plan_stats.restype = None
+        lib.oracle_plan_coo.argtypes = [P, P, P, P, P, P, f64, f64, i32, i32, i32, i32, i64,
+                                        P, P, P, P]
+        lib.oracle_plan_coo.restype = i64
+        lib.oracle_loss_grad.argtypes = [P, P, i32, i32, i32, i32, P, P, P, P, P, P]
+        lib.oracle_loss_grad.restype = i32
+        _lib = lib
+    return _lib
+
+
+def _d(x):
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _p(x):
+    return x.ctypes.data_as(ctypes.c_void_p)
+
+
+def _shapes(X, Y):
+    X, Y = _d(X), _d(Y)
+    if X.ndim == 2:
+        X = X[None]
+    if Y.ndim == 2:
+        Y = Y[None]
+    B, n, d = X.shape
+    assert Y.shape[0] == B and Y.shape[2] == d
+    return X, Y, B, n, Y.shape[1], d
+
+
+def _weights(w, B, k):
+    if w is None:
+        return np.full((B, k), 1.0 / k)
+    w = _d(w)
+    return np.ascontiguousarray(w.reshape(B, k))
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+def half_update(P, Q, pot_q, w_q, eps, rows=None):
+    """out_r = -eps * LSE_j[(pot_j - ||p_r - q_j||^2)/eps + log w_j] (single pair)."""
+    lib = _load()
+    P, Q = _d(P), _d(Q)
+    pot_q, logw = _d(pot_q), np.log(_d(w_q))
+    np_, d = P.shape
+    nq = Q.shape[0]
+    if rows is None:
+        out = np.empty(np_)
+        lib.oracle_half_update(_p(P), np_, _p(Q), nq, d, _p(pot_q), _p(logw), float(eps),
+                               None, 0, _p(out))
+    else:
+        r = np.ascontiguousarray(np.asarray(rows, dtype=np.int32))
+        out = np.empty(r.size)
+        lib.oracle_half_update(_p(P), np_, _p(Q), nq, d, _p(pot_q), _p(logw), float(eps),
+                               _p(r), int(r.size), _p(out))
+    return out
+
+
+def potentials(X, Y, a=None, b=None, eps=(0.05,), iters=(100,), form="direct",
+               f0=None, g0=None):
+    """Run the schedule; returns (f, g) shaped [B,n], [B,m] (or [n], [m] for 2-D input)."""
+    lib = _load()
+    squeeze = np.asarray(X).ndim == 2
+    X, Y, B, n, m, d = _shapes(X, Y)
+    a, b = _weights(a, B, n), _weights(b, B, m)
+    eps = _d(np.atleast_1d(eps))
+    it = np.ascontiguousarray(np.atleast_1d(iters).astype(np.int32))
+    assert eps.size == it.size
+    warm = g0 is not None
+    f = np.zeros((B, n)) if f0 is None else _d(f0).reshape(B, n).copy()
+    g = np.zeros((B, m)) if g0 is None else _d(g0).reshape(B, m).copy()
+    rc = lib.oracle_potentials(_p(X), _p(Y), _p(a), _p(b), B, n, m, d, _p(eps), _p(it),
+                               int(eps.size), 0 if form == "direct" else 1, int(warm),
+                               _p(f), _p(g))
+    if rc != 0:
+        raise ValueError("oracle_potentials: bad arguments")
+    return (f[0], g[0]) if squeeze else (f, g)
+
+
+def plan_stats(X, Y, a, b, f, g, eps):
+    """Per pair: dict of arrays cost, dual, row_err, col_err, kl (see the C file)."""
+    lib = _load()
+    X, Y, B, n, m, d = _shapes(X, Y)
+    a, b = _weights(a, B, n), _weights(b, B, m)
+    f, g = _d(f).reshape(B, n), _d(g).reshape(B, m)
+    out = np.empty((B, 5))
+    lib.oracle_plan_stats(_p(X), _p(Y), _p(a), _p(b), _p(f), _p(g), float(eps), B, n, m, d,
+                          _p(out))
+    keys = ("cost", "dual", "row_err", "col_err", "kl")
+    return {k: out[:, i].copy() for i, k in enumerate(keys)}
+
+
+def plan_coo(X, Y, a, b, f, g, eps, rel_thr=1e-8):
+    """Thresholded plan: (rows int32, cols int32, vals f64, pair_offsets int64[B+1])."""
+    lib = _load()
+    X, Y, B, n, m, d = _shapes(X, Y)
+    a, b = _weights(a, B, n), _weights(b, B, m)
+    f, g = _d(f).reshape(B, n), _d(g).reshape(B, m)
+    offs = np.zeros(B + 1, dtype=np.int64)
+    args = (_p(X), _p(Y), _p(a), _p(b), _p(f), _p(g), float(eps), float(rel_thr), B, n, m, d)
+    total = lib.oracle_plan_coo(*args, 0, None, None, None, _p(offs))
+    if total < 0:
+        raise ValueError("oracle_plan_coo: bad arguments")
+    rows = np.empty(max(total, 1), dtype=np.int32)
+    cols = np.empty(max(total, 1), dtype=np.int32)
+    vals = np.empty(max(total, 1), dtype=np.float64)
+    total2 = lib.oracle_plan_coo(*args, int(total), _p(rows), _p(cols), _p(vals), _p(offs))
+    assert total2 == total
+    return rows[:total], cols[:total], vals[:total], offs
+
+
+def loss_grad(X, Y, rows, cols, vals, pair_offsets):
+    """(loss[B], dX[B,n,d]) on the stored support."""
+    lib = _load()
+    X, Y, B, n, m, d = _shapes(X, Y)
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int32))
+    cols = np.ascontiguousarray(np.asarray(cols, dtype=np.int32))
+    vals = _d(vals)
+    offs = np.ascontiguousarray(np.asarray(pair_offsets, dtype=np.int64))
+    loss = np.empty(B)
+    dX = np.empty((B, n, d))
+    rc = lib.oracle_loss_grad(_p(X), _p(Y), B, n, m, d, _p(rows), _p(cols), _p(vals), _p(offs),
+                              _p(loss), _p(dX))
+    if rc != 0:
+        raise ValueError("oracle_loss_grad: index out of range")
+    return loss, dX

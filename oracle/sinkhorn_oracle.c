@@ -1,0 +1,458 @@
+/*
+ * sinkhorn_oracle.c -- plain double-precision CPU oracle for entropic optimal
+ * transport between point clouds under squared-Euclidean cost.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This is the slow, obviously-correct reference the
+ * GPU library is checked against.  Only the test-suite, the smoke check and the
+ * benchmark's CPU-baseline leg load it; the library itself never does, and the
+ * two share no code (no headers, helpers, tables or constants).
+ *
+ * Sources, cited by page and section:
+ *   [FS]  "FlashSinkhorn: IO-bewuste Entropische Optimale Transport op GPU"
+ *         (gist.science technical summary, Dutch).
+ *   [AP]  "From Theory to Throughput: CUDA-Optimized APML for Large-Batch 3D
+ *         Learning" (newx.sg paper page).
+ *
+ * What is computed, per pair b of a batch (pairs are independent):
+ *   C_ij = ||x_i - y_j||^2                                   [FS Probleemstelling,
+ *                                                             Methodologie intro]
+ *   f_i <- -eps * LSE_j[(g_j - C_ij)/eps + log b_j]          [FS Methodologie 1,
+ *                                                             Propositie 1]
+ *   g_j <- -eps * LSE_i[(f_i - C_ij)/eps + log a_i]          (mirror of the f-update;
+ *                                                             the page names its bias
+ *                                                             gamma but prints only f)
+ *   LSE_k z_k = M + log sum_k exp(z_k - M),  M = max_k z_k   (stabilised log domain)
+ *
+ * Readings where the pages are silent (each is listed in the design notes):
+ *   - g starts at 0 and f is updated first; one "iteration" is one f-update
+ *     followed by one g-update that already uses the new f; no early stop.
+ *   - an eps schedule is a list of stages (eps_s, iters_s) run back to back,
+ *     potentials carried over (warm start) from stage to stage.
+ *   - the plan at the final eps is
+ *       log P_ij = (f_i + g_j - C_ij)/eps + log a_i + log b_j.
+ *   - transport cost = sum_ij P_ij C_ij (primal), computed with compensated
+ *     summation; the dual <a,f> + <b,g> is reported beside it.
+ *   - the sparse plan [AP Abstract, Innovation] keeps
+ *       P_ij >= rel_thr * max_kl P_kl  (max over the pair), decided in the log
+ *     domain, stored row-major (pair, row, col) without duplicates.
+ *   - loss on the stored support: L_b = sum_S P_ij C_ij (no renormalisation);
+ *     dL/dx_i = sum_{j:(i,j) in S} 2 P_ij (x_i - y_j)   (P held fixed).
+ *   - a zero weight gives log 0 = -inf and drops that term from the other
+ *     side's LSE.
+ *
+ * Attention form [FS Methodologie 1, Propositie 1]: with hat potentials
+ *   fh = f - ||x||^2, gh = g - ||y||^2, Q = sqrt(2) X, K = sqrt(2) Y,
+ *   delta = eps log b, gamma = eps log a:
+ *     fh_i <- -eps * LSE_j[(Q_i . K_j + gh_j + delta_j)/eps]
+ *     gh_j <- -eps * LSE_i[(Q_i . K_j + fh_i + gamma_i)/eps]
+ *   It is the same recurrence written differently; it lives here only so that
+ *   the two forms can be checked against each other.
+ *
+ * Layout: all arrays are double, row-major, batch-major: X[B][n][d],
+ * Y[B][m][d], a[B][n], b[B][m], f[B][n], g[B][m].  No function allocates
+ * anything the caller has to free.  Rows are spread over threads with OpenMP;
+ * the arithmetic of each row is sequential and in the order written.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+static double sq_dist(const double *x, const double *y, int d)
+{
+    double s = 0.0;
+    for (int k = 0; k < d; ++k) {
+        double t = x[k] - y[k];
+        s += t * t;
+    }
+    return s;
+}
+
+static double dot(const double *x, const double *y, int d)
+{
+    double s = 0.0;
+    for (int k = 0; k < d; ++k)
+        s += x[k] * y[k];
+    return s;
+}
+
+/* Stabilised log-sum-exp of z[0..len): max, then log of the shifted sum. */
+static double log_sum_exp(const double *z, int len)
+{
+    double M = -INFINITY;
+    for (int k = 0; k < len; ++k)
+        if (z[k] > M)
+            M = z[k];
+    if (M == -INFINITY)
+        return -INFINITY;
+    double s = 0.0;
+    for (int k = 0; k < len; ++k)
+        s += exp(z[k] - M);
+    return M + log(s);
+}
+
+/*
+ * One half-update of the direct (cost) form, for the rows of P against the
+ * points of Q [FS Methodologie 1]:
+ *     out_r = -eps * LSE_j[(pot_j - ||p_r - q_j||^2)/eps + logw_j]
+ * pot / logw belong to Q.  With P = X, Q = Y this is the f-update; with
+ * P = Y, Q = X it is the g-update.  rows == NULL means every row 0..np-1,
+ * otherwise the nrows listed rows (out has nrows entries in that order).
+ */
+void oracle_half_update(const double *P, int np, const double *Q, int nq, int d,
+                        const double *pot, const double *logw, double eps,
+                        const int *rows, int nrows, double *out)
+{
+    int count = rows ? nrows : np;
+#pragma omp parallel
+    {
+        double *z = (double *)malloc(sizeof(double) * (size_t)(nq > 0 ? nq : 1));
+#pragma omp for schedule(static)
+        for (int t = 0; t < count; ++t) {
+            int r = rows ? rows[t] : t;
+            const double *p = P + (size_t)r * d;
+            for (int j = 0; j < nq; ++j)
+                z[j] = (pot[j] - sq_dist(p, Q + (size_t)j * d, d)) / eps + logw[j];
+            out[t] = -eps * log_sum_exp(z, nq);
+        }
+        free(z);
+    }
+}
+
+/*
+ * One half-update of the attention form [FS Methodologie 1, Propositie 1]:
+ *     out_r = -eps * LSE_j[(sqrt2 p_r . sqrt2 q_j + hat_j + bias_j)/eps]
+ * hat = hat potential of Q, bias = eps * log w of Q.
+ */
+static void half_update_attention(const double *P, int np, const double *Q, int nq, int d,
+                                  const double *hat, const double *bias, double eps,
+                                  double *out)
+{
+    const double r2 = sqrt(2.0);
+#pragma omp parallel
+    {
+        double *z = (double *)malloc(sizeof(double) * (size_t)(nq > 0 ? nq : 1));
+        double *qrow = (double *)malloc(sizeof(double) * (size_t)(d > 0 ? d : 1));
+        double *krow = (double *)malloc(sizeof(double) * (size_t)(d > 0 ? d : 1));
+#pragma omp for schedule(static)
+        for (int r = 0; r < np; ++r) {
+            for (int k = 0; k < d; ++k)
+                qrow[k] = r2 * P[(size_t)r * d + k];
+            for (int j = 0; j < nq; ++j) {
+                for (int k = 0; k < d; ++k)
+                    krow[k] = r2 * Q[(size_t)j * d + k];
+                z[j] = (dot(qrow, krow, d) + hat[j] + bias[j]) / eps;
+            }
+            out[r] = -eps * log_sum_exp(z, nq);
+        }
+        free(krow);
+        free(qrow);
+        free(z);
+    }
+}
+
+static void log_weights(const double *w, int len, double *lw)
+{
+    for (int k = 0; k < len; ++k)
+        lw[k] = log(w[k]); /* log 0 = -inf: the point drops out of the other LSE */
+}
+
+/*
+ * Full solve.  eps[s], iters[s] for s < n_stages; iters counts full
+ * iterations (f-update then g-update).  form 0 = direct, 1 = attention.
+ * warm != 0: g (and f) hold starting potentials; otherwise g starts at 0.
+ * Returns 0, or -1 on bad arguments.
+ */
+int oracle_potentials(const double *X, const double *Y, const double *a, const double *b,
+                      int B, int n, int m, int d,
+                      const double *eps, const int *iters, int n_stages,
+                      int form, int warm, double *f, double *g)
+{
+    if (B < 0 || n < 1 || m < 1 || d < 1 || n_stages < 0)
+        return -1;
+    double *la = (double *)malloc(sizeof(double) * (size_t)n);
+    double *lb = (double *)malloc(sizeof(double) * (size_t)m);
+    double *nx = (double *)malloc(sizeof(double) * (size_t)n);
+    double *ny = (double *)malloc(sizeof(double) * (size_t)m);
+    double *fh = (double *)malloc(sizeof(double) * (size_t)n);
+    double *gh = (double *)malloc(sizeof(double) * (size_t)m);
+    double *ga = (double *)malloc(sizeof(double) * (size_t)n);
+    double *de = (double *)malloc(sizeof(double) * (size_t)m);
+
+    for (int p = 0; p < B; ++p) {
+        const double *Xp = X + (size_t)p * n * d;
+        const double *Yp = Y + (size_t)p * m * d;
+        double *fp = f + (size_t)p * n;
+        double *gp = g + (size_t)p * m;
+        log_weights(a + (size_t)p * n, n, la);
+        log_weights(b + (size_t)p * m, m, lb);
+        if (!warm) {
+            for (int j = 0; j < m; ++j)
+                gp[j] = 0.0;
+            for (int i = 0; i < n; ++i)
+                fp[i] = 0.0;
+        }
+        if (form == 0) {
+            for (int s = 0; s < n_stages; ++s)
+                for (int it = 0; it < iters[s]; ++it) {
+                    oracle_half_update(Xp, n, Yp, m, d, gp, lb, eps[s], NULL, 0, fp);
+                    oracle_half_update(Yp, m, Xp, n, d, fp, la, eps[s], NULL, 0, gp);
+                }
+        } else {
+            for (int i = 0; i < n; ++i) {
+                nx[i] = dot(Xp + (size_t)i * d, Xp + (size_t)i * d, d);
+                fh[i] = fp[i] - nx[i];
+            }
+            for (int j = 0; j < m; ++j) {
+                ny[j] = dot(Yp + (size_t)j * d, Yp + (size_t)j * d, d);
+                gh[j] = gp[j] - ny[j];
+            }
+            for (int s = 0; s < n_stages; ++s) {
+                for (int i = 0; i < n; ++i)
+                    ga[i] = eps[s] * la[i];
+                for (int j = 0; j < m; ++j)
+                    de[j] = eps[s] * lb[j];
+                for (int it = 0; it < iters[s]; ++it) {
+                    half_update_attention(Xp, n, Yp, m, d, gh, de, eps[s], fh);
+                    half_update_attention(Yp, m, Xp, n, d, fh, ga, eps[s], gh);
+                }
+            }
+            for (int i = 0; i < n; ++i)
+                fp[i] = fh[i] + nx[i];
+            for (int j = 0; j < m; ++j)
+                gp[j] = gh[j] + ny[j];
+        }
+    }
+    free(la); free(lb); free(nx); free(ny); free(fh); free(gh); free(ga); free(de);
+    return 0;
+}
+
+/* Neumaier compensated accumulator. */
+typedef struct { double s, c; } acc_t;
+static void acc_add(acc_t *a, double v)
+{
+    double t = a->s + v;
+    if (fabs(a->s) >= fabs(v))
+        a->c += (a->s - t) + v;
+    else
+        a->c += (v - t) + a->s;
+    a->s = t;
+}
+static double acc_get(const acc_t *a) { return a->s + a->c; }
+
+static double log_plan(const double *x, const double *y, int d, double fi, double gj,
+                       double lai, double lbj, double eps)
+{
+    return (fi + gj - sq_dist(x, y, d)) / eps + lai + lbj;
+}
+
+/*
+ * Statistics of the plan at eps, per pair (out has 5 values per pair):
+ *   out[0] = sum_ij P_ij C_ij                  (transport cost, primal)
+ *   out[1] = sum_i a_i f_i + sum_j b_j g_j      (dual value)
+ *   out[2] = sum_i |sum_j P_ij - a_i|           (row-marginal L1 error)
+ *   out[3] = sum_j |sum_i P_ij - b_j|           (column-marginal L1 error)
+ *   out[4] = sum_ij P_ij log(P_ij / (a_i b_j))  (KL of P to a (x) b)
+ * Row quantities are summed per row (compensated), then over rows in order;
+ * column sums are a second pass over the plan, one column at a time.
+ */
+void oracle_plan_stats(const double *X, const double *Y, const double *a, const double *b,
+                       const double *f, const double *g, double eps,
+                       int B, int n, int m, int d, double *out)
+{
+    double *la = (double *)malloc(sizeof(double) * (size_t)n);
+    double *lb = (double *)malloc(sizeof(double) * (size_t)m);
+    double *row_cost = (double *)malloc(sizeof(double) * (size_t)n);
+    double *row_kl = (double *)malloc(sizeof(double) * (size_t)n);
+    double *row_mass = (double *)malloc(sizeof(double) * (size_t)n);
+    double *col_mass = (double *)malloc(sizeof(double) * (size_t)m);
+    for (int p = 0; p < B; ++p) {
+        const double *Xp = X + (size_t)p * n * d, *Yp = Y + (size_t)p * m * d;
+        const double *ap = a + (size_t)p * n, *bp = b + (size_t)p * m;
+        const double *fp = f + (size_t)p * n, *gp = g + (size_t)p * m;
+        log_weights(ap, n, la);
+        log_weights(bp, m, lb);
+#pragma omp parallel for schedule(static)
+        for (int i = 0; i < n; ++i) {
+            acc_t cost = {0, 0}, kl = {0, 0}, mass = {0, 0};
+            for (int j = 0; j < m; ++j) {
+                const double *x = Xp + (size_t)i * d, *y = Yp + (size_t)j * d;
+                double lp = log_plan(x, y, d, fp[i], gp[j], la[i], lb[j], eps);
+                double P = exp(lp);
+                if (P > 0.0) {
+                    acc_add(&cost, P * sq_dist(x, y, d));
+                    acc_add(&kl, P * (lp - la[i] - lb[j]));
+                }
+                acc_add(&mass, P);
+            }
+            row_cost[i] = acc_get(&cost);
+            row_kl[i] = acc_get(&kl);
+            row_mass[i] = acc_get(&mass);
+        }
+#pragma omp parallel for schedule(static)
+        for (int j = 0; j < m; ++j) {
+            acc_t mass = {0, 0};
+            for (int i = 0; i < n; ++i)
+                acc_add(&mass, exp(log_plan(Xp + (size_t)i * d, Yp + (size_t)j * d, d, fp[i],
+                                            gp[j], la[i], lb[j], eps)));
+            col_mass[j] = acc_get(&mass);
+        }
+        acc_t cost = {0, 0}, dual = {0, 0}, row_err = {0, 0}, col_err = {0, 0}, kl = {0, 0};
+        for (int i = 0; i < n; ++i) {
+            acc_add(&cost, row_cost[i]);
+            acc_add(&kl, row_kl[i]);
+            acc_add(&row_err, fabs(row_mass[i] - ap[i]));
+            if (ap[i] > 0.0)
+                acc_add(&dual, ap[i] * fp[i]);
+        }
+        for (int j = 0; j < m; ++j) {
+            acc_add(&col_err, fabs(col_mass[j] - bp[j]));
+            if (bp[j] > 0.0)
+                acc_add(&dual, bp[j] * gp[j]);
+        }
+        out[5 * p + 0] = acc_get(&cost);
+        out[5 * p + 1] = acc_get(&dual);
+        out[5 * p + 2] = acc_get(&row_err);
+        out[5 * p + 3] = acc_get(&col_err);
+        out[5 * p + 4] = acc_get(&kl);
+    }
+    free(la); free(lb); free(row_cost); free(row_kl); free(row_mass); free(col_mass);
+}
+
+/* Largest log P_ij of one pair and the number of entries at or above
+ * that maximum + log rel_thr. */
+static void pair_max_count(const double *Xp, const double *Yp, const double *la,
+                           const double *lb, const double *fp, const double *gp, double eps,
+                           double log_thr, int n, int m, int d, double *max_out,
+                           int64_t *count_out)
+{
+    double M = -INFINITY;
+    for (int i = 0; i < n; ++i)
+        for (int j = 0; j < m; ++j) {
+            double lp = log_plan(Xp + (size_t)i * d, Yp + (size_t)j * d, d, fp[i], gp[j],
+                                 la[i], lb[j], eps);
+            if (lp > M)
+                M = lp;
+        }
+    int64_t c = 0;
+    if (M > -INFINITY)
+        for (int i = 0; i < n; ++i)
+            for (int j = 0; j < m; ++j)
+                if (log_plan(Xp + (size_t)i * d, Yp + (size_t)j * d, d, fp[i], gp[j], la[i],
+                             lb[j], eps) >= M + log_thr)
+                    ++c;
+    *max_out = M;
+    *count_out = c;
+}
+
+/*
+ * Thresholded sparse plan in COO form [AP Abstract, Innovation]: per pair,
+ * M = max_ij log P_ij and the stored set is {(i,j) : log P_ij >= M + log rel_thr},
+ * enumerated row-major.  pair_offsets[B+1] is always written.  The entries are
+ * written only when capacity >= total; the return value is the total number of
+ * kept entries (the required capacity), or -1 on bad arguments.
+ */
+int64_t oracle_plan_coo(const double *X, const double *Y, const double *a, const double *b,
+                        const double *f, const double *g, double eps, double rel_thr,
+                        int B, int n, int m, int d, int64_t capacity,
+                        int32_t *rows, int32_t *cols, double *vals, int64_t *pair_offsets)
+{
+    if (!(rel_thr > 0.0 && rel_thr <= 1.0) || !(eps > 0.0) || B < 0 || n < 1 || m < 1)
+        return -1;
+    double log_thr = log(rel_thr);
+    double *maxes = (double *)malloc(sizeof(double) * (size_t)(B > 0 ? B : 1));
+    int64_t *counts = (int64_t *)malloc(sizeof(int64_t) * (size_t)(B > 0 ? B : 1));
+#pragma omp parallel
+    {
+        double *la = (double *)malloc(sizeof(double) * (size_t)n);
+        double *lb = (double *)malloc(sizeof(double) * (size_t)m);
+#pragma omp for schedule(dynamic, 1)
+        for (int p = 0; p < B; ++p) {
+            log_weights(a + (size_t)p * n, n, la);
+            log_weights(b + (size_t)p * m, m, lb);
+            pair_max_count(X + (size_t)p * n * d, Y + (size_t)p * m * d, la, lb,
+                           f + (size_t)p * n, g + (size_t)p * m, eps, log_thr, n, m, d,
+                           &maxes[p], &counts[p]);
+        }
+        free(la);
+        free(lb);
+    }
+    pair_offsets[0] = 0;
+    for (int p = 0; p < B; ++p)
+        pair_offsets[p + 1] = pair_offsets[p] + counts[p];
+    int64_t total = pair_offsets[B];
+    if (total <= capacity) {
+#pragma omp parallel
+        {
+            double *la = (double *)malloc(sizeof(double) * (size_t)n);
+            double *lb = (double *)malloc(sizeof(double) * (size_t)m);
+#pragma omp for schedule(dynamic, 1)
+            for (int p = 0; p < B; ++p) {
+                const double *Xp = X + (size_t)p * n * d, *Yp = Y + (size_t)p * m * d;
+                const double *fp = f + (size_t)p * n, *gp = g + (size_t)p * m;
+                log_weights(a + (size_t)p * n, n, la);
+                log_weights(b + (size_t)p * m, m, lb);
+                int64_t k = pair_offsets[p];
+                if (maxes[p] > -INFINITY)
+                    for (int i = 0; i < n; ++i)
+                        for (int j = 0; j < m; ++j) {
+                            double lp = log_plan(Xp + (size_t)i * d, Yp + (size_t)j * d, d,
+                                                 fp[i], gp[j], la[i], lb[j], eps);
+                            if (lp >= maxes[p] + log_thr) {
+                                rows[k] = i;
+                                cols[k] = j;
+                                vals[k] = exp(lp);
+                                ++k;
+                            }
+                        }
+            }
+            free(la);
+            free(lb);
+        }
+    }
+    free(maxes);
+    free(counts);
+    return total;
+}
+
+/*
+ * Loss and gradient on the stored support (P held fixed):
+ *   loss[p]    = sum_{k in pair p} vals_k * ||x_{rows_k} - y_{cols_k}||^2
+ *   dX[p][i]   = sum_{k in pair p, rows_k = i} 2 vals_k (x_i - y_{cols_k})
+ * Entries may come in any order.  Returns 0, or -1 on an index out of range.
+ */
+int oracle_loss_grad(const double *X, const double *Y, int B, int n, int m, int d,
+                     const int32_t *rows, const int32_t *cols, const double *vals,
+                     const int64_t *pair_offsets, double *loss, double *dX)
+{
+    for (size_t t = 0; t < (size_t)B * n * d; ++t)
+        dX[t] = 0.0;
+    for (int p = 0; p < B; ++p) {
+        const double *Xp = X + (size_t)p * n * d, *Yp = Y + (size_t)p * m * d;
+        double *dXp = dX + (size_t)p * n * d;
+        acc_t L = {0, 0};
+        for (int64_t k = pair_offsets[p]; k < pair_offsets[p + 1]; ++k) {
+            int i = rows[k], j = cols[k];
+            if (i < 0 || i >= n || j < 0 || j >= m)
+                return -1;
+            const double *x = Xp + (size_t)i * d, *y = Yp + (size_t)j * d;
+            acc_add(&L, vals[k] * sq_dist(x, y, d));
+            for (int c = 0; c < d; ++c)
+                dXp[(size_t)i * d + c] += 2.0 * vals[k] * (x[c] - y[c]);
+        }
+        loss[p] = acc_get(&L);
+    }
+    return 0;
+}

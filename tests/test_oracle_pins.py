@@ -1,0 +1,323 @@
+"""Pins of the CPU oracle to facts it does not compute itself.
+
+Each test checks the fp64 oracle against something fixed by the mathematics
+of entropic optimal transport or by an independent library routine, never
+against a retyped copy of its own formula.  The mistakes these are chosen to
+catch: a dropped log-weight term (non-uniform weights everywhere), a sign or
+scale error in the cost (brute-force assignment, closed forms), a transposed
+operand (n != m, swap symmetry), a wrong half-update order (marginals), and a
+wrong plan/threshold formula (2x2 closed form, dense enumeration, duality).
+
+Pages: FlashSinkhorn technical summary, Methodologie 1 (Propositie 1) for the
+log-domain updates; CUDA-APML page, Abstract / Innovation for the thresholded
+sparse plan and the loss/gradient on the stored support.
+"""
+import itertools
+import math
+
+import numpy as np
+import pytest
+from scipy.optimize import linear_sum_assignment
+from scipy.special import logsumexp
+
+import oracle
+import workloads
+
+
+def _case(seed, n, m, d=3, weights="dirichlet", spread=1.0):
+    # weights renormalised in float64: float32-rounded weights need not have
+    # equal sums, and then no plan can match both marginals exactly
+    c = workloads.random_case(seed, 1, n, m, d, weights=weights, spread=spread)
+    a, b = c["a"][0].astype(np.float64), c["b"][0].astype(np.float64)
+    return (c["X"][0].astype(np.float64), c["Y"][0].astype(np.float64),
+            a / a.sum(), b / b.sum())
+
+
+def _cost_matrix(X, Y):
+    return ((X[:, None, :] - Y[None, :, :]) ** 2).sum(-1)
+
+
+def _converge(X, Y, a, b, eps, iters):
+    f, g = oracle.potentials(X, Y, a, b, eps=[eps], iters=[iters])
+    return f, g
+
+
+# ---------------------------------------------------------------- half-update
+@pytest.mark.parametrize("n,m,d", [(17, 29, 3), (64, 5, 7), (1, 40, 2)])
+def test_half_update_matches_scipy_weighted_logsumexp(n, m, d):
+    rng = np.random.default_rng(n * 100 + m)
+    X, Y = rng.random((n, d)), rng.random((m, d))
+    g = rng.normal(size=m)
+    b = rng.dirichlet(np.ones(m))
+    eps = 0.07
+    f = oracle.half_update(X, Y, g, b, eps)
+    C = _cost_matrix(X, Y)
+    ref = -eps * logsumexp((g[None, :] - C) / eps, b=b[None, :], axis=1)
+    np.testing.assert_allclose(f, ref, rtol=1e-13, atol=1e-13)
+    rows = [n - 1, 0]
+    np.testing.assert_array_equal(oracle.half_update(X, Y, g, b, eps, rows=rows), f[rows])
+
+
+# ------------------------------------------------------- attention vs direct
+@pytest.mark.parametrize("d", [3, 64])
+@pytest.mark.parametrize("k", [1, 10, 100])
+def test_attention_form_agrees_with_direct_form(d, k):
+    X, Y, a, b = _case(11 + d, 37, 23, d=d)
+    eps = 0.05 if d == 3 else 0.5
+    f1, g1 = oracle.potentials(X, Y, a, b, eps=[eps], iters=[k], form="direct")
+    f2, g2 = oracle.potentials(X, Y, a, b, eps=[eps], iters=[k], form="attention")
+    scale = max(np.abs(f1).max(), np.abs(g1).max(), eps)
+    assert np.abs(f1 - f2).max() / scale < 1e-10
+    assert np.abs(g1 - g2).max() / scale < 1e-10
+
+
+def test_attention_form_agrees_on_a_schedule_with_warm_start():
+    X, Y, a, b = _case(5, 41, 31)
+    eps = workloads.geometric_schedule(1.0, 0.01, 4).astype(np.float64)
+    f1, g1 = oracle.potentials(X, Y, a, b, eps=eps, iters=[5] * 4, form="direct")
+    f2, g2 = oracle.potentials(X, Y, a, b, eps=eps, iters=[5] * 4, form="attention")
+    np.testing.assert_allclose(f1, f2, rtol=0, atol=1e-10 * np.abs(f1).max())
+    np.testing.assert_allclose(g1, g2, rtol=0, atol=1e-10 * np.abs(g1).max())
+    # split run == full run (potentials are the complete state)
+    fa, ga = oracle.potentials(X, Y, a, b, eps=eps[:2], iters=[5] * 2)
+    fb, gb = oracle.potentials(X, Y, a, b, eps=eps[2:], iters=[5] * 2, f0=fa, g0=ga)
+    np.testing.assert_array_equal(fb, f1)
+    np.testing.assert_array_equal(gb, g1)
+
+
+# ----------------------------------------------------------- fixed point
+def test_marginals_hold_at_convergence():
+    X, Y, a, b = _case(3, 200, 150)
+    eps = 0.05
+    f, g = _converge(X, Y, a, b, eps, 600)
+    st = oracle.plan_stats(X, Y, a, b, f, g, eps)
+    assert st["col_err"][0] <= 1e-12     # exact after the g-update
+    assert st["row_err"][0] <= 1e-6      # the pages' convergence tolerance
+    # one more f-update barely moves f (fixed point)
+    f_next = oracle.half_update(X, Y, g, b, eps)
+    assert np.abs(f_next - f).max() < 1e-9
+
+
+def test_marginals_fail_before_convergence():
+    # guards the test above against a trivially-satisfied statistic
+    X, Y, a, b = _case(3, 200, 150)
+    f, g = _converge(X, Y, a, b, 0.05, 2)
+    st = oracle.plan_stats(X, Y, a, b, f, g, 0.05)
+    assert st["row_err"][0] > 1e-4
+
+
+def test_strong_duality_at_convergence():
+    # dual value = primal entropic objective <P,C> + eps KL(P || a b^T)
+    X, Y, a, b = _case(8, 60, 45)
+    eps = 0.1
+    f, g = _converge(X, Y, a, b, eps, 3000)
+    st = oracle.plan_stats(X, Y, a, b, f, g, eps)
+    assert st["row_err"][0] < 1e-12
+    primal = st["cost"][0] + eps * st["kl"][0]
+    assert abs(st["dual"][0] - primal) <= 1e-10 * abs(primal)
+    # primal cost and dual differ by eps*KL, a strictly positive amount here
+    assert st["dual"][0] - st["cost"][0] > 1e-3
+
+
+# ----------------------------------------------------- closed forms / limits
+def _two_by_two_plan(C, a1, b1, eps):
+    """Entropic plan of a 2x2 problem from the cross-ratio invariant
+    P11 P22 / (P12 P21) = K11 K22 / (K12 K21), K = exp(-C/eps)."""
+    kappa = math.exp(-(C[0, 0] + C[1, 1] - C[0, 1] - C[1, 0]) / eps)
+    A, Bq, Cq = 1.0 - kappa, 1.0 - a1 - b1 + kappa * (a1 + b1), -kappa * a1 * b1
+    lo, hi = max(0.0, a1 + b1 - 1.0), min(a1, b1)
+    if abs(A) < 1e-15:
+        roots = [-Cq / Bq]
+    else:
+        disc = math.sqrt(Bq * Bq - 4 * A * Cq)
+        roots = [(-Bq + disc) / (2 * A), (-Bq - disc) / (2 * A)]
+    p = [r for r in roots if lo - 1e-15 <= r <= hi + 1e-15]
+    assert len(p) == 1
+    p = p[0]
+    return np.array([[p, a1 - p], [b1 - p, 1.0 - a1 - b1 + p]])
+
+
+@pytest.mark.parametrize("eps", [0.5, 0.1, 0.03])
+def test_two_by_two_closed_form(eps):
+    X = np.array([[0.1, 0.2, 0.0], [0.9, 0.4, 0.3]])
+    Y = np.array([[0.8, 0.5, 0.2], [0.0, 0.1, 0.4]])
+    a = np.array([0.3, 0.7])
+    b = np.array([0.55, 0.45])
+    C = _cost_matrix(X, Y)
+    Pref = _two_by_two_plan(C, a[0], b[0], eps)
+    f, g = _converge(X, Y, a, b, eps, 3000)
+    rows, cols, vals, offs = oracle.plan_coo(X, Y, a, b, f, g, eps, rel_thr=1e-300)
+    P = np.zeros((2, 2))
+    P[rows, cols] = vals
+    np.testing.assert_allclose(P, Pref, rtol=1e-10, atol=1e-14)
+    st = oracle.plan_stats(X, Y, a, b, f, g, eps)
+    assert abs(st["cost"][0] - (Pref * C).sum()) <= 1e-10
+
+
+def test_single_point_pair():
+    X = np.array([[0.3, -1.0, 2.0]])
+    Y = np.array([[1.5, 0.5, -0.5]])
+    C11 = float(((X - Y) ** 2).sum())
+    f, g = oracle.potentials(X, Y, [1.0], [1.0], eps=[0.01], iters=[3])
+    assert abs(f[0] + g[0] - C11) <= 1e-15 * C11
+    st = oracle.plan_stats(X, Y, [1.0], [1.0], f, g, 0.01)
+    assert abs(st["cost"][0] - C11) <= 1e-15 * C11
+
+
+def test_large_eps_limit_is_independent_coupling():
+    X, Y, a, b = _case(21, 30, 40)
+    eps = 1e4
+    f, g = _converge(X, Y, a, b, eps, 20)
+    st = oracle.plan_stats(X, Y, a, b, f, g, eps)
+    ma, mb = a @ X, b @ Y
+    indep = a @ (X ** 2).sum(1) + b @ (Y ** 2).sum(1) - 2 * ma @ mb
+    assert abs(st["cost"][0] - indep) / indep < 1e-3
+
+
+# ------------------------------------------- entropic -> exact assignment
+def _best_permutation_cost(C):
+    n = C.shape[0]
+    best = min(sum(C[i, s[i]] for i in range(n)) for s in itertools.permutations(range(n)))
+    return best / n
+
+
+@pytest.mark.parametrize("n", [1, 2, 4, 6, 7])
+@pytest.mark.parametrize("eps", [1e-2, 1e-3])
+def test_small_eps_approaches_brute_force_assignment(n, eps):
+    # <C,P_eps> - OT_0 <= eps (H(P_eps) - H(P*)) <= eps (2 ln n - ln n): P_eps minimises
+    # <C,P> - eps H(P) over the coupling polytope and a permutation plan has H = ln n
+    X, Y, a, b = _case(40 + n, n, n, weights="uniform")
+    C = _cost_matrix(X, Y)
+    ot0 = _best_permutation_cost(C)
+    sched = list(np.geomspace(1.0, eps, 12)) + [eps]      # annealed, to reach the fixed point
+    f, g = oracle.potentials(X, Y, a, b, eps=sched, iters=[500] * 12 + [100000])
+    st = oracle.plan_stats(X, Y, a, b, f, g, eps)
+    assert st["row_err"][0] < 1e-6
+    slack = st["row_err"][0] * C.max() + 1e-12            # plan off the polytope by row_err
+    assert ot0 - slack <= st["cost"][0] <= ot0 + eps * math.log(max(n, 1)) + slack
+
+
+def test_small_eps_approaches_linear_sum_assignment_n64():
+    X, Y, a, b = _case(77, 64, 64, weights="uniform")
+    C = _cost_matrix(X, Y)
+    r, c = linear_sum_assignment(C)
+    ot0 = C[r, c].sum() / 64
+    eps = 2e-3
+    sched = list(np.geomspace(1.0, eps, 12)) + [eps]
+    f, g = oracle.potentials(X, Y, a, b, eps=sched, iters=[300] * 12 + [20000])
+    st = oracle.plan_stats(X, Y, a, b, f, g, eps)
+    assert st["row_err"][0] < 1e-5
+    slack = st["row_err"][0] * C.max() + 1e-12
+    assert ot0 - slack <= st["cost"][0] <= ot0 + eps * math.log(64) + slack
+
+
+# ---------------------------------------------------------- invariances
+@pytest.mark.parametrize("t", [(3.0, -2.0, 5.0), (100.0, 100.0, 100.0)])
+def test_translation_invariance(t):
+    X, Y, a, b = _case(9, 50, 70)
+    eps = 0.05
+    f1, g1 = oracle.potentials(X, Y, a, b, eps=[eps], iters=[50])
+    f2, g2 = oracle.potentials(X + np.array(t), Y + np.array(t), a, b, eps=[eps], iters=[50])
+    sc = max(np.abs(f1).max(), np.abs(g1).max())
+    assert np.abs(f1 - f2).max() / sc < 1e-9
+    assert np.abs(g1 - g2).max() / sc < 1e-9
+    c1 = oracle.plan_stats(X, Y, a, b, f1, g1, eps)["cost"][0]
+    c2 = oracle.plan_stats(X + np.array(t), Y + np.array(t), a, b, f2, g2, eps)["cost"][0]
+    assert abs(c1 - c2) / c1 < 1e-9
+
+
+def test_swap_symmetry_at_convergence():
+    X, Y, a, b = _case(13, 40, 25)
+    eps = 0.1
+    f, g = _converge(X, Y, a, b, eps, 500)
+    g2, f2 = _converge(Y, X, b, a, eps, 500)   # roles swapped: potentials swap too
+    s1 = oracle.plan_stats(X, Y, a, b, f, g, eps)
+    s2 = oracle.plan_stats(Y, X, b, a, g2, f2, eps)
+    assert abs(s1["cost"][0] - s2["cost"][0]) < 1e-9
+    assert abs(s1["dual"][0] - s2["dual"][0]) < 1e-9
+
+
+def test_zero_weight_points_drop_out():
+    c = workloads.random_case(4, 1, 30, 20, 3, weights="dirichlet", zero_weights=3)
+    X, Y = c["X"][0].astype(float), c["Y"][0].astype(float)
+    a, b = c["a"][0].astype(float), c["b"][0].astype(float)
+    eps = 0.05
+    f, g = oracle.potentials(X, Y, a, b, eps=[eps], iters=[30])
+    fr, gr = oracle.potentials(X[3:], Y[3:], a[3:], b[3:], eps=[eps], iters=[30])
+    np.testing.assert_allclose(f[3:], fr, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(g[3:], gr, rtol=1e-13, atol=1e-13)
+    assert np.all(np.isfinite(f)) and np.all(np.isfinite(g))
+
+
+# ------------------------------------------------------- sparse plan / loss
+def test_coo_matches_dense_enumeration():
+    X, Y, a, b = _case(31, 33, 47)
+    eps = 0.02
+    f, g = oracle.potentials(X, Y, a, b, eps=[eps], iters=[7])
+    for thr in (1e-8, 1e-3, 1.0):
+        rows, cols, vals, offs = oracle.plan_coo(X, Y, a, b, f, g, eps, rel_thr=thr)
+        logP = (f[:, None] + g[None, :] - _cost_matrix(X, Y)) / eps \
+            + np.log(a)[:, None] + np.log(b)[None, :]
+        keep = np.argwhere(logP >= logP.max() + np.log(thr))     # row-major order
+        np.testing.assert_array_equal(rows, keep[:, 0])
+        np.testing.assert_array_equal(cols, keep[:, 1])
+        np.testing.assert_allclose(vals, np.exp(logP[keep[:, 0], keep[:, 1]]), rtol=1e-13)
+        assert offs.tolist() == [0, len(rows)]
+        if thr == 1.0:
+            assert len(rows) >= 1
+
+
+def test_coo_batch_offsets_and_pair_independence():
+    c = workloads.random_case(2, 3, 12, 9, 3, weights="dirichlet")
+    X, Y, a, b = (c[k].astype(float) for k in ("X", "Y", "a", "b"))
+    eps = 0.05
+    f, g = oracle.potentials(X, Y, a, b, eps=[eps], iters=[10])
+    rows, cols, vals, offs = oracle.plan_coo(X, Y, a, b, f, g, eps, rel_thr=1e-4)
+    for p in range(3):
+        r1, c1, v1, o1 = oracle.plan_coo(X[p], Y[p], a[p], b[p], f[p], g[p], eps, rel_thr=1e-4)
+        s = slice(offs[p], offs[p + 1])
+        np.testing.assert_array_equal(rows[s], r1)
+        np.testing.assert_array_equal(cols[s], c1)
+        np.testing.assert_array_equal(vals[s], v1)
+
+
+def test_gradient_is_envelope_derivative_of_ot_value():
+    # at convergence, d OT_eps / d x_i = sum_j 2 P_ij (x_i - y_j)
+    X, Y, a, b = _case(17, 12, 9)
+    eps, iters = 0.1, 3000
+
+    def ot_value(Xv):
+        f, g = oracle.potentials(Xv, Y, a, b, eps=[eps], iters=[iters])
+        return float(a @ f + b @ g)
+
+    f, g = _converge(X, Y, a, b, eps, iters)
+    rows, cols, vals, offs = oracle.plan_coo(X, Y, a, b, f, g, eps, rel_thr=1e-300)
+    assert len(rows) == 12 * 9
+    loss, dX = oracle.loss_grad(X, Y, rows, cols, vals, offs)
+    h = 1e-5
+    fd = np.zeros_like(X)
+    for i in range(X.shape[0]):
+        for k in range(3):
+            Xp, Xm = X.copy(), X.copy()
+            Xp[i, k] += h
+            Xm[i, k] -= h
+            fd[i, k] = (ot_value(Xp) - ot_value(Xm)) / (2 * h)
+    np.testing.assert_allclose(dX[0], fd, rtol=1e-6, atol=1e-8)
+    # with the full support the loss is the transport cost
+    st = oracle.plan_stats(X, Y, a, b, f, g, eps)
+    assert abs(loss[0] - st["cost"][0]) <= 1e-12 * st["cost"][0]
+
+
+def test_loss_grad_any_order_and_truncated_support():
+    X, Y, a, b = _case(19, 20, 15)
+    eps = 0.03
+    f, g = oracle.potentials(X, Y, a, b, eps=[eps], iters=[20])
+    rows, cols, vals, offs = oracle.plan_coo(X, Y, a, b, f, g, eps, rel_thr=1e-2)
+    loss, dX = oracle.loss_grad(X, Y, rows, cols, vals, offs)
+    perm = np.random.default_rng(0).permutation(len(rows))
+    loss2, dX2 = oracle.loss_grad(X, Y, rows[perm], cols[perm], vals[perm], offs)
+    np.testing.assert_allclose(loss2, loss, rtol=1e-13)
+    np.testing.assert_allclose(dX2, dX, rtol=1e-12, atol=1e-15)
+    # rows without stored entries get a zero gradient
+    empty = np.setdiff1d(np.arange(20), rows)
+    assert np.all(dX[0, empty] == 0.0)
