@@ -1,0 +1,166 @@
+/*
+ * sinkhorn.h -- C ABI of the MI355X (gfx950) streaming Sinkhorn library.
+ *
+ * Entropic optimal transport between point clouds under squared-Euclidean
+ * cost, computed with stabilised log-domain Sinkhorn iterations in which every
+ * half-iteration is one streamed row- or column-wise log-sum-exp of a biased
+ * dot-product score; the n x m cost matrix never exists in memory.
+ *
+ * Sources, cited by page and section:
+ *   [FS] "FlashSinkhorn: IO-bewuste Entropische Optimale Transport op GPU"
+ *        (gist.science technical summary): Probleemstelling (problem: EOT
+ *        between point clouds, squared-Euclidean cost); Methodologie 1,
+ *        Propositie 1 (the f-update as the LSE of (Q K^T + 1(g_hat + delta))/eps,
+ *        Q = sqrt2 X, K = sqrt2 Y); Methodologie 2 (tiles streamed, online
+ *        max / sum-exp on chip, one fused pass per update, row-stationary).
+ *   [AP] "From Theory to Throughput: CUDA-Optimized APML for Large-Batch 3D
+ *        Learning" (newx.sg): Abstract and Innovation (negligible assignments
+ *        thresholded away, plan kept in COO form, gradients on the stored
+ *        support).
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are DEVICE pointers unless the argument says "host".  Arrays
+ *     are dense, row-major and batch-major: X[B][n][d], Y[B][m][d],
+ *     a[B][n], b[B][m], f[B][n], g[B][m].  B pairs are independent problems
+ *     of equal sizes.
+ *   - X and Y share one dtype (SK_F32 or SK_BF16); everything else is fp32
+ *     (indices int32, offsets int64).
+ *   - The caller owns every buffer, including the workspace, whose size comes
+ *     from sinkhorn_workspace_bytes().  The library allocates no device or
+ *     pinned memory and keeps no state between calls, apart from a
+ *     thread-local error message.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     and returns without waiting, except sinkhorn_plan_coo (see there).
+ *     Calls are reentrant; two calls that share a workspace must not overlap.
+ *   - Arguments are checked before anything is launched.  On an error no
+ *     output buffer is written and the return value says why; the message
+ *     of sinkhorn_last_error() gives detail.
+ *   - Inputs are not scanned for NaN/Inf: NaN in gives NaN out.
+ *   - Weights must be >= 0.  A zero weight removes that point from the other
+ *     side's log-sum-exp (log 0 = -inf); its own potential stays defined.
+ *     a and b may be NULL, meaning uniform weights 1/n and 1/m.
+ */
+#ifndef SINKHORN_H
+#define SINKHORN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+enum {
+    SK_OK = 0,
+    SK_ERR_INVALID_ARG = 1, /* a size, pointer, eps, threshold or flag is out of range */
+    SK_ERR_UNSUPPORTED = 2, /* no kernel for this dtype / dimension combination */
+    SK_ERR_WORKSPACE = 3,   /* ws is NULL or ws_bytes is below the required size */
+    SK_ERR_CAPACITY = 4,    /* sparse plan larger than the caller's capacity */
+    SK_ERR_HIP = 5          /* the HIP runtime reported an error (message has it) */
+};
+
+/* Point dtypes. */
+enum { SK_F32 = 0, SK_BF16 = 1 };
+
+/* Operation ids for sinkhorn_workspace_bytes(). */
+enum { SK_OP_POTENTIALS = 0, SK_OP_PLAN_COO = 1, SK_OP_LOSS_GRAD = 2 };
+
+/* Flags of sinkhorn_potentials(). */
+#define SK_WARM_START 1u /* f and g hold starting potentials (resume) */
+
+/*
+ * Supported shapes: B >= 1, 1 <= n, m <= 2^24, B*n and B*m <= 2^31, and
+ *   dtype SK_F32 with d == 3             (3-D point-cloud kernel), or
+ *   dtype SK_F32 or SK_BF16, 1 <= d <= 128 (feature kernel; d is padded with
+ *                                          zeros to the next of 8,16,32,64,128).
+ * Anything else returns SK_ERR_UNSUPPORTED.
+ */
+
+/*
+ * Bytes of workspace that operation `op` needs for these sizes (0 if the
+ * arguments are out of range).  The value is an upper bound that depends only
+ * on the arguments; the workspace needs no initialisation and its contents
+ * are undefined after a call.
+ */
+size_t sinkhorn_workspace_bytes(int op, int B, int n, int m, int d, int dtype);
+
+/*
+ * Sinkhorn potentials [FS Methodologie 1, Propositie 1; Methodologie 2].
+ *
+ * For each stage s < n_stages (eps[s] > 0, iters[s] >= 0; both HOST arrays),
+ * runs iters[s] full iterations, each an f-update followed by a g-update that
+ * uses the new f:
+ *     f_i <- -eps_s * LSE_j[(g_j - C_ij)/eps_s + log b_j]
+ *     g_j <- -eps_s * LSE_i[(f_i - C_ij)/eps_s + log a_i],   C_ij = ||x_i - y_j||^2.
+ * Potentials carry over from stage to stage (eps annealing).  Without
+ * SK_WARM_START, g starts at 0 and f is not read; with it, f and g are read
+ * as the starting point (resuming a split run gives the same result as one
+ * long run).
+ *
+ * f [B][n], g [B][m] (fp32, in/out) receive the potentials after the last
+ * g-update.  cost [B] (fp32, may be NULL) receives the transport cost
+ * sum_ij P_ij C_ij of the plan at the last eps,
+ *     log P_ij = (f_i + g_j - C_ij)/eps + log a_i + log b_j.
+ * With n_stages == 0 (or all iters 0) the potentials are returned unchanged
+ * (zero without SK_WARM_START) and cost is that of those potentials, at
+ * eps[n_stages-1] if n_stages > 0; cost must be NULL when n_stages == 0.
+ */
+int sinkhorn_potentials(const void *X, const void *Y, int dtype,
+                        const float *a, const float *b,
+                        int B, int n, int m, int d,
+                        const float *eps, const int *iters, int n_stages,
+                        unsigned flags, float *f, float *g, float *cost,
+                        void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Thresholded sparse plan in COO form [AP Abstract, Innovation].
+ *
+ * From potentials f, g at eps (as returned by sinkhorn_potentials), keeps per
+ * pair p every entry with
+ *     P_ij >= rel_threshold * max_kl P_kl      (max over pair p; 0 < rel_threshold <= 1),
+ * decided in the log domain.  Entries are written in (pair, row, column)
+ * order without duplicates: rows[k], cols[k] (int32, indices within the
+ * pair) and vals[k] = P_ij (fp32), for pair_offsets[p] <= k < pair_offsets[p+1].
+ * pair_offsets has B+1 int64 entries (device).
+ *
+ * *nnz_total (HOST int64) always receives the number of kept entries.  If it
+ * exceeds `capacity`, the call returns SK_ERR_CAPACITY after writing
+ * pair_offsets and *nnz_total only; rows/cols/vals may be NULL when capacity
+ * is 0.  This is the one entry point that waits on `stream`: it synchronises
+ * once to read the count back.
+ */
+int sinkhorn_plan_coo(const void *X, const void *Y, int dtype,
+                      const float *a, const float *b,
+                      int B, int n, int m, int d, float eps,
+                      const float *f, const float *g, float rel_threshold,
+                      int64_t capacity, int32_t *rows, int32_t *cols, float *vals,
+                      int64_t *pair_offsets, int64_t *nnz_total,
+                      void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Loss and gradient on the stored support [AP Abstract] (plan held fixed):
+ *     loss[p]  = sum_{k in pair p} vals_k * ||x_{rows_k} - y_{cols_k}||^2
+ *     dX[p][i] = sum_{k in pair p, rows_k = i} 2 vals_k (x_i - y_{cols_k})
+ * The COO must be in the form sinkhorn_plan_coo writes: within each pair,
+ * entries sorted by row (any column order within a row), indices in range.
+ * loss [B] fp32; dX [B][n][d] fp32 or NULL.  Rows with no entries get a
+ * zero gradient.
+ */
+int sinkhorn_loss_grad(const void *X, const void *Y, int dtype,
+                       int B, int n, int m, int d,
+                       const int32_t *rows, const int32_t *cols, const float *vals,
+                       const int64_t *pair_offsets, float *loss, float *dX,
+                       void *ws, size_t ws_bytes, void *stream);
+
+/* Static text for a return code. */
+const char *sinkhorn_status_string(int status);
+
+/* Detail of the last error raised on the calling thread ("" if none). */
+const char *sinkhorn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SINKHORN_H */

@@ -61,6 +61,10 @@
 #include <omp.h>
 #endif
 
+/* Half-updates smaller than this many entries run on one thread (a parallel
+ * region per tiny update costs more than the update). */
+#define PARALLEL_MIN_WORK 65536L
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP
@@ -116,7 +120,7 @@ void oracle_half_update(const double *P, int np, const double *Q, int nq, int d,
                         const int *rows, int nrows, double *out)
 {
     int count = rows ? nrows : np;
-#pragma omp parallel
+#pragma omp parallel if ((long)count * nq >= PARALLEL_MIN_WORK)
     {
         double *z = (double *)malloc(sizeof(double) * (size_t)(nq > 0 ? nq : 1));
 #pragma omp for schedule(static)
@@ -141,7 +145,7 @@ static void half_update_attention(const double *P, int np, const double *Q, int 
                                   double *out)
 {
     const double r2 = sqrt(2.0);
-#pragma omp parallel
+#pragma omp parallel if ((long)np * nq >= PARALLEL_MIN_WORK)
     {
         double *z = (double *)malloc(sizeof(double) * (size_t)(nq > 0 ? nq : 1));
         double *qrow = (double *)malloc(sizeof(double) * (size_t)(d > 0 ? d : 1));

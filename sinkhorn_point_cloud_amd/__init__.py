@@ -1,0 +1,233 @@
+"""Streaming log-domain Sinkhorn for point clouds on MI355X (gfx950).
+
+A thin ctypes binding over the C ABI of ``libsinkhorn_amd.so`` (declared in
+``include/sinkhorn.h``).  Every step of the computation runs in the library's
+HIP kernels; this module only checks tensors, allocates outputs and workspace
+with torch (device memory and the current stream are all torch provides) and
+marshals pointers.  If the library has not been built, every call raises.
+
+Entry points (same names as the C ABI):
+  potentials(X, Y, a, b, eps, iters, ...)   -> f, g, cost
+  plan_coo(X, Y, a, b, f, g, eps, ...)      -> rows, cols, vals, pair_offsets
+  loss_grad(X, Y, rows, cols, vals, pair_offsets, ...) -> loss, dX
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["SinkhornError", "potentials", "plan_coo", "loss_grad", "workspace_bytes",
+           "library_path", "load_library"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libsinkhorn_amd.so")
+
+SK_OK, SK_ERR_INVALID_ARG, SK_ERR_UNSUPPORTED, SK_ERR_WORKSPACE, SK_ERR_CAPACITY, SK_ERR_HIP = \
+    range(6)
+SK_F32, SK_BF16 = 0, 1
+SK_OP_POTENTIALS, SK_OP_PLAN_COO, SK_OP_LOSS_GRAD = 0, 1, 2
+SK_WARM_START = 1
+
+EXPORTS = ("sinkhorn_workspace_bytes", "sinkhorn_potentials", "sinkhorn_plan_coo",
+           "sinkhorn_loss_grad", "sinkhorn_status_string", "sinkhorn_last_error")
+
+
+class SinkhornError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[{status}] {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load (once) and return the ctypes handle; raises if the library is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                           "`python -m sinkhorn_point_cloud_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I, U, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint, ctypes.c_size_t
+    F, L = ctypes.c_float, ctypes.c_int64
+    lib.sinkhorn_workspace_bytes.argtypes = [I, I, I, I, I, I]
+    lib.sinkhorn_workspace_bytes.restype = Z
+    lib.sinkhorn_potentials.argtypes = [P, P, I, P, P, I, I, I, I, P, P, I, U, P, P, P, P, Z, P]
+    lib.sinkhorn_potentials.restype = I
+    lib.sinkhorn_plan_coo.argtypes = [P, P, I, P, P, I, I, I, I, F, P, P, F, L, P, P, P, P, P,
+                                      P, Z, P]
+    lib.sinkhorn_plan_coo.restype = I
+    lib.sinkhorn_loss_grad.argtypes = [P, P, I, I, I, I, I, P, P, P, P, P, P, P, Z, P]
+    lib.sinkhorn_loss_grad.restype = I
+    lib.sinkhorn_status_string.argtypes = [I]
+    lib.sinkhorn_status_string.restype = ctypes.c_char_p
+    lib.sinkhorn_last_error.argtypes = []
+    lib.sinkhorn_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(rc: int):
+    if rc != SK_OK:
+        lib = load_library()
+        msg = lib.sinkhorn_last_error().decode() or lib.sinkhorn_status_string(rc).decode()
+        raise SinkhornError(rc, msg)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _points(X, Y):
+    if X.dim() == 2:
+        X = X.unsqueeze(0)
+    if Y.dim() == 2:
+        Y = Y.unsqueeze(0)
+    if X.dim() != 3 or Y.dim() != 3 or X.shape[0] != Y.shape[0] or X.shape[2] != Y.shape[2]:
+        raise ValueError(f"X {tuple(X.shape)} and Y {tuple(Y.shape)} must be [B,n,d], [B,m,d]")
+    if X.dtype != Y.dtype or X.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("X and Y must both be float32 or both bfloat16")
+    if not (X.is_cuda and Y.is_cuda):
+        raise ValueError("X and Y must be GPU tensors")
+    dt = SK_F32 if X.dtype == torch.float32 else SK_BF16
+    return X.contiguous(), Y.contiguous(), dt
+
+
+def _weights(w, B, k, device):
+    if w is None:
+        return None
+    w = torch.as_tensor(w, dtype=torch.float32, device=device)
+    if w.numel() != B * k:
+        raise ValueError(f"weights need {B * k} entries, got {w.numel()}")
+    return w.reshape(B, k).contiguous()
+
+
+def workspace_bytes(op: int, B: int, n: int, m: int, d: int, dtype: int) -> int:
+    return int(load_library().sinkhorn_workspace_bytes(op, B, n, m, d, dtype))
+
+
+def _workspace(op, B, n, m, d, dt, device, workspace=None):
+    need = workspace_bytes(op, B, n, m, d, dt)
+    if need == 0:
+        raise SinkhornError(SK_ERR_UNSUPPORTED, f"unsupported shape/dtype B={B} n={n} m={m} d={d}")
+    if workspace is not None and workspace.numel() >= need:
+        return workspace
+    return torch.empty(need, dtype=torch.uint8, device=device)
+
+
+def potentials(X, Y, a=None, b=None, eps=(0.05,), iters=(100,), f0=None, g0=None,
+               cost: bool = True, out=None, workspace=None):
+    """Sinkhorn potentials over an eps schedule (one stage per entry of eps/iters).
+
+    X [B,n,d], Y [B,m,d] (float32, or bfloat16), a [B,n], b [B,m] or None
+    (uniform).  f0/g0 warm-start the run.  Returns (f [B,n], g [B,m], cost [B] or
+    None), all float32 on the device.  ``out`` = (f, g, cost) reuses buffers."""
+    lib = load_library()
+    X, Y, dt = _points(X, Y)
+    B, n, d = X.shape
+    m = Y.shape[1]
+    dev = X.device
+    a, b = _weights(a, B, n, dev), _weights(b, B, m, dev)
+    eps_l = [float(e) for e in (eps if hasattr(eps, "__len__") else [eps])]
+    it_l = [int(i) for i in (iters if hasattr(iters, "__len__") else [iters])]
+    if len(eps_l) != len(it_l):
+        raise ValueError("eps and iters need one entry per stage")
+    if out is not None:
+        f, g, c = out
+    else:
+        f = torch.empty(B, n, dtype=torch.float32, device=dev)
+        g = torch.empty(B, m, dtype=torch.float32, device=dev)
+        c = torch.empty(B, dtype=torch.float32, device=dev) if cost else None
+    flags = 0
+    if (f0 is None) != (g0 is None):
+        raise ValueError("warm start needs both f0 and g0")
+    if f0 is not None:
+        f.copy_(torch.as_tensor(f0, device=dev).reshape(B, n))
+        g.copy_(torch.as_tensor(g0, device=dev).reshape(B, m))
+        flags |= SK_WARM_START
+    ws = _workspace(SK_OP_POTENTIALS, B, n, m, d, dt, dev, workspace)
+    eps_a = (ctypes.c_float * max(1, len(eps_l)))(*eps_l)
+    it_a = (ctypes.c_int * max(1, len(it_l)))(*it_l)
+    rc = lib.sinkhorn_potentials(_ptr(X), _ptr(Y), dt, _ptr(a), _ptr(b), B, n, m, d, eps_a, it_a,
+                                 len(eps_l), flags, _ptr(f), _ptr(g), _ptr(c), _ptr(ws),
+                                 ws.numel(), _stream())
+    _check(rc)
+    return f, g, c
+
+
+def plan_coo(X, Y, a, b, f, g, eps: float, rel_threshold: float = 1e-8, capacity=None,
+             workspace=None):
+    """Thresholded sparse plan: (rows int32, cols int32, vals float32, pair_offsets int64[B+1]).
+
+    With capacity=None the plan is counted first, then emitted into buffers of
+    exactly the right size (two calls of the C entry point)."""
+    lib = load_library()
+    X, Y, dt = _points(X, Y)
+    B, n, d = X.shape
+    m = Y.shape[1]
+    dev = X.device
+    a, b = _weights(a, B, n, dev), _weights(b, B, m, dev)
+    f = f.reshape(B, n).contiguous().float()
+    g = g.reshape(B, m).contiguous().float()
+    ws = _workspace(SK_OP_PLAN_COO, B, n, m, d, dt, dev, workspace)
+    offs = torch.empty(B + 1, dtype=torch.int64, device=dev)
+    nnz = ctypes.c_int64(0)
+
+    def call(cap, rows, cols, vals):
+        return lib.sinkhorn_plan_coo(_ptr(X), _ptr(Y), dt, _ptr(a), _ptr(b), B, n, m, d,
+                                     float(eps), _ptr(f), _ptr(g), float(rel_threshold), cap,
+                                     _ptr(rows), _ptr(cols), _ptr(vals), _ptr(offs),
+                                     ctypes.byref(nnz), _ptr(ws), ws.numel(), _stream())
+
+    cap = 0 if capacity is None else int(capacity)
+    rows = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    cols = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    vals = torch.empty(max(cap, 1), dtype=torch.float32, device=dev)
+    rc = call(cap, rows, cols, vals)
+    if rc == SK_ERR_CAPACITY and capacity is None:
+        cap = int(nnz.value)
+        rows = torch.empty(cap, dtype=torch.int32, device=dev)
+        cols = torch.empty(cap, dtype=torch.int32, device=dev)
+        vals = torch.empty(cap, dtype=torch.float32, device=dev)
+        rc = call(cap, rows, cols, vals)
+    _check(rc)
+    k = int(nnz.value)
+    return rows[:k], cols[:k], vals[:k], offs
+
+
+def loss_grad(X, Y, rows, cols, vals, pair_offsets, grad: bool = True, workspace=None):
+    """Loss [B] and dL/dX [B,n,d] (float32) on the stored support of a row-sorted COO plan."""
+    lib = load_library()
+    X, Y, dt = _points(X, Y)
+    B, n, d = X.shape
+    m = Y.shape[1]
+    dev = X.device
+    rows, cols = rows.contiguous(), cols.contiguous()
+    vals, offs = vals.contiguous(), pair_offsets.contiguous()
+    if rows.dtype != torch.int32 or cols.dtype != torch.int32 or vals.dtype != torch.float32 \
+            or offs.dtype != torch.int64 or offs.numel() != B + 1:
+        raise TypeError("rows/cols int32, vals float32, pair_offsets int64[B+1]")
+    if rows.numel() == 0:   # the C ABI wants real pointers even for an empty plan
+        rows = torch.zeros(1, dtype=torch.int32, device=dev)
+        cols = torch.zeros(1, dtype=torch.int32, device=dev)
+        vals = torch.zeros(1, dtype=torch.float32, device=dev)
+    loss = torch.empty(B, dtype=torch.float32, device=dev)
+    dX = torch.empty(B, n, d, dtype=torch.float32, device=dev) if grad else None
+    ws = _workspace(SK_OP_LOSS_GRAD, B, n, m, d, dt, dev, workspace)
+    rc = lib.sinkhorn_loss_grad(_ptr(X), _ptr(Y), dt, B, n, m, d, _ptr(rows), _ptr(cols),
+                                _ptr(vals), _ptr(offs), _ptr(loss), _ptr(dX), _ptr(ws),
+                                ws.numel(), _stream())
+    _check(rc)
+    return loss, dX

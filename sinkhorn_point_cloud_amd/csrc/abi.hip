@@ -1,0 +1,377 @@
+// abi.hip -- the C ABI declared in include/sinkhorn.h: argument checks,
+// workspace carve-up, the eps-annealing driver and kernel launches.
+#include "common.h"
+#include "sinkhorn.h"
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+namespace sk {
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int hip_fail(hipError_t e, const char *where)
+{
+    return fail(SK_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+constexpr int kMaxPoints = 1 << 24;
+constexpr int kPad = 64;
+
+// hat -> true potential, out = hat + ||x||^2
+template <typename T>
+__global__ void unhat_kernel(const T *__restrict__ X, int d, const float *__restrict__ hat,
+                             size_t count, float *__restrict__ out)
+{
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= count)
+        return;
+    float sq = 0.f;
+    for (int k = 0; k < d; ++k) {
+        const float v = Elem<T>::get(X, i * d + k);
+        sq = fmaf(v, v, sq);
+    }
+    out[i] = hat[i] + sq;
+}
+
+// Bump allocator over the caller's workspace (256-byte aligned pieces).
+struct Carve {
+    char *base;
+    size_t off = 0;
+    template <typename T> T *take(size_t count)
+    {
+        off = (off + 255) & ~(size_t)255;
+        T *p = base ? reinterpret_cast<T *>(base + off) : nullptr;
+        off += count * sizeof(T);
+        return p;
+    }
+};
+
+bool shape_ok(int B, int n, int m, int d)
+{
+    return B >= 1 && n >= 1 && m >= 1 && d >= 1 && n <= kMaxPoints && m <= kMaxPoints &&
+           (long long)B * n <= (1ll << 31) && (long long)B * m <= (1ll << 31);
+}
+
+bool path3(int dtype, int d) { return dtype == SK_F32 && d == 3; }
+
+bool supported(int dtype, int d) { return path3(dtype, d) || lseF_supported(dtype, d); }
+
+struct PotWs {
+    // d = 3 path
+    float4 *px = nullptr, *py = nullptr;
+    // feature path
+    float *xbias = nullptr, *ybias = nullptr;
+    // both
+    float *fhat, *ghat, *l2a, *l2b;
+    float2 *part;
+    double *row_part;
+};
+
+PotWs carve_potentials(Carve &c, int B, int n, int m, int d, int dtype)
+{
+    PotWs w;
+    const int np = round_up(n, kPad), mp = round_up(m, kPad);
+    size_t parts;
+    if (path3(dtype, d)) {
+        w.px = c.take<float4>((size_t)B * np);
+        w.py = c.take<float4>((size_t)B * mp);
+        parts = std::max(lse3_partial_floats2(B, np, mp), lse3_partial_floats2(B, mp, np));
+    } else {
+        w.xbias = c.take<float>((size_t)B * np);
+        w.ybias = c.take<float>((size_t)B * mp);
+        parts = std::max(lseF_partial_floats2(B, np, mp), lseF_partial_floats2(B, mp, np));
+    }
+    w.fhat = c.take<float>((size_t)B * n);
+    w.ghat = c.take<float>((size_t)B * m);
+    w.l2a = c.take<float>((size_t)B * n);
+    w.l2b = c.take<float>((size_t)B * m);
+    w.part = c.take<float2>(parts > 0 ? parts : 1);
+    w.row_part = c.take<double>((size_t)B * n);
+    return w;
+}
+
+struct CooWs {
+    double *row_max, *pair_thr;
+    int32_t *row_count;
+    int64_t *row_off, *pair_tot;
+};
+
+CooWs carve_coo(Carve &c, int B, int n)
+{
+    CooWs w;
+    w.row_max = c.take<double>((size_t)B * n);
+    w.pair_thr = c.take<double>(B);
+    w.row_count = c.take<int32_t>((size_t)B * n);
+    w.row_off = c.take<int64_t>((size_t)B * n);
+    w.pair_tot = c.take<int64_t>(B);
+    return w;
+}
+
+struct LossWs {
+    int64_t *begin, *end;
+    double *row_loss;
+};
+
+LossWs carve_loss(Carve &c, int B, int n)
+{
+    LossWs w;
+    w.begin = c.take<int64_t>((size_t)B * n);
+    w.end = c.take<int64_t>((size_t)B * n);
+    w.row_loss = c.take<double>((size_t)B * n);
+    return w;
+}
+
+size_t ws_size(int op, int B, int n, int m, int d, int dtype)
+{
+    Carve c{nullptr};
+    if (op == SK_OP_POTENTIALS)
+        carve_potentials(c, B, n, m, d, dtype);
+    else if (op == SK_OP_PLAN_COO)
+        carve_coo(c, B, n);
+    else
+        carve_loss(c, B, n);
+    return c.off + 256;
+}
+
+hipError_t unhat(const void *X, int dtype, int d, const float *hat, size_t count, float *out,
+                 hipStream_t st)
+{
+    const unsigned blocks = (unsigned)((count + 255) / 256);
+    if (dtype == SK_BF16)
+        hipLaunchKernelGGL(unhat_kernel<uint16_t>, dim3(blocks), dim3(256), 0, st,
+                           (const uint16_t *)X, d, hat, count, out);
+    else
+        hipLaunchKernelGGL(unhat_kernel<float>, dim3(blocks), dim3(256), 0, st,
+                           (const float *)X, d, hat, count, out);
+    return hipGetLastError();
+}
+
+int check_ws(void *ws, size_t ws_bytes, size_t need)
+{
+    if (!ws || ws_bytes < need)
+        return fail(SK_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", need,
+                    ws_bytes, ws ? "" : " (ws is NULL)");
+    return SK_OK;
+}
+
+int check_common(const void *X, const void *Y, int dtype, int B, int n, int m, int d)
+{
+    if (!X || !Y)
+        return fail(SK_ERR_INVALID_ARG, "X and Y must be non-NULL device pointers");
+    if (dtype != SK_F32 && dtype != SK_BF16)
+        return fail(SK_ERR_INVALID_ARG, "dtype %d is neither SK_F32 nor SK_BF16", dtype);
+    if (!shape_ok(B, n, m, d))
+        return fail(SK_ERR_INVALID_ARG, "bad sizes B=%d n=%d m=%d d=%d", B, n, m, d);
+    if (!supported(dtype, d))
+        return fail(SK_ERR_UNSUPPORTED, "no kernel for dtype %d with d=%d", dtype, d);
+    return SK_OK;
+}
+
+}  // namespace
+}  // namespace sk
+
+using namespace sk;
+
+extern "C" {
+
+size_t sinkhorn_workspace_bytes(int op, int B, int n, int m, int d, int dtype)
+{
+    if (op < SK_OP_POTENTIALS || op > SK_OP_LOSS_GRAD || !shape_ok(B, n, m, d) ||
+        (dtype != SK_F32 && dtype != SK_BF16) || !supported(dtype, d))
+        return 0;
+    return ws_size(op, B, n, m, d, dtype);
+}
+
+const char *sinkhorn_status_string(int s)
+{
+    switch (s) {
+    case SK_OK: return "ok";
+    case SK_ERR_INVALID_ARG: return "invalid argument";
+    case SK_ERR_UNSUPPORTED: return "unsupported dtype/dimension";
+    case SK_ERR_WORKSPACE: return "workspace missing or too small";
+    case SK_ERR_CAPACITY: return "sparse plan exceeds capacity";
+    case SK_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+const char *sinkhorn_last_error(void) { return g_err; }
+
+int sinkhorn_potentials(const void *X, const void *Y, int dtype, const float *a, const float *b,
+                        int B, int n, int m, int d, const float *eps, const int *iters,
+                        int n_stages, unsigned flags, float *f, float *g, float *cost, void *ws,
+                        size_t ws_bytes, void *stream)
+{
+    g_err[0] = '\0';
+    int rc = check_common(X, Y, dtype, B, n, m, d);
+    if (rc)
+        return rc;
+    if (!f || !g)
+        return fail(SK_ERR_INVALID_ARG, "f and g must be non-NULL device pointers");
+    if (n_stages < 0 || (n_stages > 0 && (!eps || !iters)))
+        return fail(SK_ERR_INVALID_ARG, "n_stages=%d needs host arrays eps and iters", n_stages);
+    if (flags & ~SK_WARM_START)
+        return fail(SK_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+    for (int s = 0; s < n_stages; ++s) {
+        if (!(eps[s] > 0.f) || !isfinite(eps[s]))
+            return fail(SK_ERR_INVALID_ARG, "eps[%d]=%g must be finite and > 0", s, eps[s]);
+        if (iters[s] < 0)
+            return fail(SK_ERR_INVALID_ARG, "iters[%d]=%d must be >= 0", s, iters[s]);
+    }
+    if (cost && n_stages == 0)
+        return fail(SK_ERR_INVALID_ARG, "cost needs an eps (n_stages >= 1)");
+    rc = check_ws(ws, ws_bytes, ws_size(SK_OP_POTENTIALS, B, n, m, d, dtype));
+    if (rc)
+        return rc;
+
+    hipStream_t st = (hipStream_t)stream;
+    Carve c{(char *)ws};
+    PotWs w = carve_potentials(c, B, n, m, d, dtype);
+    const int warm = (flags & SK_WARM_START) ? 1 : 0;
+    const int np = round_up(n, kPad), mp = round_up(m, kPad);
+
+    // eps of every half-iteration, in order
+    int first = -1;
+    for (int s = 0; s < n_stages; ++s)
+        if (iters[s] > 0) {
+            first = s;
+            break;
+        }
+    const float c0 = kLog2e / (first >= 0 ? eps[first] : 1.0f);
+    hipError_t e;
+    const bool p3 = path3(dtype, d);
+    Side3 sx3{w.px, w.fhat, w.l2a, n, np}, sy3{w.py, w.ghat, w.l2b, m, mp};
+    SideF sxf{X, w.xbias, w.fhat, w.l2a, nullptr, n, np}, syf{Y, w.ybias, w.ghat, w.l2b, nullptr,
+                                                             m, mp};
+    if (p3) {
+        if ((e = launch_pack3((const float *)X, a, f, warm, B, sx3, c0, st)))
+            return hip_fail(e, "pack X");
+        if ((e = launch_pack3((const float *)Y, b, g, warm, B, sy3, c0, st)))
+            return hip_fail(e, "pack Y");
+    } else {
+        if ((e = launch_packF(X, dtype, d, a, f, warm, B, sxf, c0, st)))
+            return hip_fail(e, "pack X");
+        if ((e = launch_packF(Y, dtype, d, b, g, warm, B, syf, c0, st)))
+            return hip_fail(e, "pack Y");
+    }
+    for (int s = 0; s < n_stages; ++s) {
+        for (int it = 0; it < iters[s]; ++it) {
+            // eps of the f-update that follows this g-update
+            float eps_next = eps[s];
+            if (it == iters[s] - 1)
+                for (int t = s + 1; t < n_stages; ++t)
+                    if (iters[t] > 0) {
+                        eps_next = eps[t];
+                        break;
+                    }
+            if (p3) {
+                if ((e = launch_lse3(sx3, sy3, B, eps[s], eps[s], w.part, 0, st)))
+                    return hip_fail(e, "f-update");
+                if ((e = launch_lse3(sy3, sx3, B, eps[s], eps_next, w.part, 0, st)))
+                    return hip_fail(e, "g-update");
+            } else {
+                if ((e = launch_lseF(sxf, syf, dtype, d, B, eps[s], eps[s], w.part, st)))
+                    return hip_fail(e, "f-update");
+                if ((e = launch_lseF(syf, sxf, dtype, d, B, eps[s], eps_next, w.part, st)))
+                    return hip_fail(e, "g-update");
+            }
+        }
+    }
+    if ((e = unhat(X, dtype, d, w.fhat, (size_t)B * n, f, st)))
+        return hip_fail(e, "unhat f");
+    if ((e = unhat(Y, dtype, d, w.ghat, (size_t)B * m, g, st)))
+        return hip_fail(e, "unhat g");
+    if (cost) {
+        PlanArgs p{X, Y, dtype, d, B, n, m, f, g, a, b, 1.0 / (double)eps[n_stages - 1]};
+        if ((e = launch_cost(p, w.row_part, cost, st)))
+            return hip_fail(e, "cost");
+    }
+    return SK_OK;
+}
+
+int sinkhorn_plan_coo(const void *X, const void *Y, int dtype, const float *a, const float *b,
+                      int B, int n, int m, int d, float eps, const float *f, const float *g,
+                      float rel_threshold, int64_t capacity, int32_t *rows, int32_t *cols,
+                      float *vals, int64_t *pair_offsets, int64_t *nnz_total, void *ws,
+                      size_t ws_bytes, void *stream)
+{
+    g_err[0] = '\0';
+    int rc = check_common(X, Y, dtype, B, n, m, d);
+    if (rc)
+        return rc;
+    if (!f || !g || !pair_offsets || !nnz_total)
+        return fail(SK_ERR_INVALID_ARG, "f, g, pair_offsets and nnz_total must be non-NULL");
+    if (!(eps > 0.f) || !isfinite(eps))
+        return fail(SK_ERR_INVALID_ARG, "eps=%g must be finite and > 0", eps);
+    if (!(rel_threshold > 0.f && rel_threshold <= 1.f))
+        return fail(SK_ERR_INVALID_ARG, "rel_threshold=%g must be in (0, 1]", rel_threshold);
+    if (capacity < 0 || (capacity > 0 && (!rows || !cols || !vals)))
+        return fail(SK_ERR_INVALID_ARG, "capacity=%lld needs rows, cols and vals",
+                    (long long)capacity);
+    rc = check_ws(ws, ws_bytes, ws_size(SK_OP_PLAN_COO, B, n, m, d, dtype));
+    if (rc)
+        return rc;
+
+    hipStream_t st = (hipStream_t)stream;
+    Carve c{(char *)ws};
+    CooWs w = carve_coo(c, B, n);
+    PlanArgs p{X, Y, dtype, d, B, n, m, f, g, a, b, 1.0 / (double)eps};
+    hipError_t e;
+    if ((e = launch_plan_max(p, w.row_max, w.pair_thr, log((double)rel_threshold), st)))
+        return hip_fail(e, "plan max");
+    if ((e = launch_plan_count(p, w.pair_thr, w.row_count, st)))
+        return hip_fail(e, "plan count");
+    if ((e = launch_plan_scan(w.row_count, B, n, w.row_off, pair_offsets, w.pair_tot, st)))
+        return hip_fail(e, "plan scan");
+    int64_t total = 0;
+    if ((e = hipMemcpyAsync(&total, pair_offsets + B, sizeof total, hipMemcpyDeviceToHost, st)))
+        return hip_fail(e, "read nnz");
+    if ((e = hipStreamSynchronize(st)))
+        return hip_fail(e, "sync for nnz");
+    *nnz_total = total;
+    if (total > capacity)
+        return fail(SK_ERR_CAPACITY, "sparse plan has %lld entries, capacity is %lld",
+                    (long long)total, (long long)capacity);
+    if (total > 0 &&
+        (e = launch_plan_emit(p, w.pair_thr, w.row_off, w.row_count, rows, cols, vals, st)))
+        return hip_fail(e, "plan emit");
+    return SK_OK;
+}
+
+int sinkhorn_loss_grad(const void *X, const void *Y, int dtype, int B, int n, int m, int d,
+                       const int32_t *rows, const int32_t *cols, const float *vals,
+                       const int64_t *pair_offsets, float *loss, float *dX, void *ws,
+                       size_t ws_bytes, void *stream)
+{
+    g_err[0] = '\0';
+    int rc = check_common(X, Y, dtype, B, n, m, d);
+    if (rc)
+        return rc;
+    if (!rows || !cols || !vals || !pair_offsets || !loss)
+        return fail(SK_ERR_INVALID_ARG, "rows, cols, vals, pair_offsets and loss must be non-NULL");
+    rc = check_ws(ws, ws_bytes, ws_size(SK_OP_LOSS_GRAD, B, n, m, d, dtype));
+    if (rc)
+        return rc;
+    hipStream_t st = (hipStream_t)stream;
+    Carve c{(char *)ws};
+    LossWs w = carve_loss(c, B, n);
+    hipError_t e = launch_loss_grad(X, Y, dtype, d, B, n, m, rows, cols, vals, pair_offsets,
+                                    w.begin, w.end, w.row_loss, loss, dX, st);
+    if (e)
+        return hip_fail(e, "loss/grad");
+    return SK_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,146 @@
+// common.h -- device helpers and launcher declarations shared by the HIP
+// sources of the streaming Sinkhorn library (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sk {
+
+constexpr int kWave = 64;
+
+// Stand-in for log 0 = -inf.  A finite value keeps every subtraction of two
+// "minus infinities" finite (no NaN), while 2^(kNeg + anything sane) is 0.
+constexpr float kNeg = -1.0e30f;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Hardware base-2 exponential and logarithm (v_exp_f32 / v_log_f32).
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float lg2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ int wave_id_uniform()
+{
+    return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v)
+{
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1)
+        v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1)
+        v = fmaxf(v, __shfl_xor(v, off, kWave));
+    return v;
+}
+
+__device__ __forceinline__ double wave_max(double v)
+{
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1)
+        v = fmax(v, __shfl_xor(v, off, kWave));
+    return v;
+}
+
+// Merge of two partial log-sum-exp states (M, S), meaning S * 2^M.
+__device__ __forceinline__ void lse_merge(float &M, float &S, float M2, float S2)
+{
+    float Mn = fmaxf(M, M2);
+    S = S * ex2(M - Mn) + S2 * ex2(M2 - Mn);
+    M = Mn;
+}
+
+__device__ __forceinline__ float bf16_to_float(uint16_t h)
+{
+    return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Element access for the two point dtypes.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    __device__ __forceinline__ static float get(const float *p, size_t i) { return p[i]; }
+};
+template <> struct Elem<uint16_t> {
+    __device__ __forceinline__ static float get(const uint16_t *p, size_t i)
+    {
+        return bf16_to_float(p[i]);
+    }
+};
+
+inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+inline int round_up(int a, int b) { return ceil_div(a, b) * b; }
+
+// ---------------------------------------------------------------- launchers
+// Every launcher enqueues on `stream` and returns hipGetLastError().
+
+// Points of one side packed for the d = 3 streaming kernel: (x, y, z, bias).
+struct Side3 {
+    float4 *pts;      // [B][n_pad] (x, y, z, bias for the opposite pass)
+    float *hat;       // [B][n]     hat potential (nats)
+    float *l2w;       // [B][n]     log2 of the weights (kNeg for 0)
+    int n, n_pad;
+};
+
+hipError_t launch_pack3(const float *X, const float *w, const float *pot, int warm, int B,
+                        Side3 s, float c0, hipStream_t st);
+// One half-iteration, d = 3: q side rows, k side columns.
+hipError_t launch_lse3(Side3 q, Side3 k, int B, float eps, float eps_next, float2 *part,
+                       int part_cap, hipStream_t st);
+size_t lse3_partial_floats2(int B, int nq_pad, int nk_pad);
+
+// Generic-d feature path (fp32 or bf16 points, VALU).
+struct SideF {
+    const void *pts;  // [B][n][d] original points (fp32 or bf16)
+    float *bias;      // [B][n_pad] bias for the opposite pass
+    float *hat;       // [B][n]
+    float *l2w;       // [B][n]
+    float *sq;        // [B][n] squared norms
+    int n, n_pad;
+};
+hipError_t launch_packF(const void *X, int dtype, int d, const float *w, const float *pot,
+                        int warm, int B, SideF s, float c0, hipStream_t st);
+hipError_t launch_lseF(SideF q, SideF k, int dtype, int d, int B, float eps, float eps_next,
+                       float2 *part, hipStream_t st);
+size_t lseF_partial_floats2(int B, int nq_pad, int nk_pad);
+bool lseF_supported(int dtype, int d);
+
+// hat -> true potential: out = hat + ||x||^2
+hipError_t launch_unhat(const void *X, int dtype, int d, const float *hat, int B, int n,
+                        float *out, hipStream_t st);
+
+// Plan evaluation passes, shared by the cost, max, count and emit steps.
+struct PlanArgs {
+    const void *X, *Y;
+    int dtype, d, B, n, m;
+    const float *f, *g;      // true potentials
+    const float *a, *b;      // weights or NULL (uniform)
+    double inv_eps;
+};
+hipError_t launch_cost(const PlanArgs &p, double *row_part, float *cost, hipStream_t st);
+hipError_t launch_plan_max(const PlanArgs &p, double *row_max, double *pair_thr,
+                           double log_rel_thr, hipStream_t st);
+hipError_t launch_plan_count(const PlanArgs &p, const double *pair_thr, int32_t *row_count,
+                             hipStream_t st);
+hipError_t launch_plan_scan(const int32_t *row_count, int B, int n, int64_t *row_off,
+                            int64_t *pair_offsets, int64_t *pair_tot, hipStream_t st);
+hipError_t launch_plan_emit(const PlanArgs &p, const double *pair_thr, const int64_t *row_off,
+                            const int32_t *row_count, int32_t *rows, int32_t *cols,
+                            float *vals, hipStream_t st);
+
+hipError_t launch_loss_grad(const void *X, const void *Y, int dtype, int d, int B, int n,
+                            int m, const int32_t *rows, const int32_t *cols, const float *vals,
+                            const int64_t *pair_offsets, int64_t *row_begin,
+                            int64_t *row_end, double *row_loss, float *loss, float *dX,
+                            hipStream_t st);
+
+}  // namespace sk

@@ -1,0 +1,227 @@
+// lse_d3.hip -- fused streaming half-iteration for 3-D point clouds (fp32).
+//
+// One launch computes, for every row i of the "query" side and every pair b,
+//     hat_i = -eps * LSE_j[(2 x_i . y_j + hat_j + eps log w_j) / eps]
+// i.e. the stabilised log-domain update in its biased dot-product form
+// (FlashSinkhorn summary, Methodologie 1, Propositie 1: Q = sqrt2 X, K = sqrt2 Y,
+// the row-broadcast bias is the opposite hat potential plus eps log w).  With
+// rows = X this is the f-update, with rows = Y the g-update (the same kernel,
+// roles swapped).  The score matrix only exists tile by tile in registers
+// (Methodologie 2: no n x m matrix in memory, online max / sum-exp on chip,
+// one fused pass per update, query rows held stationary).
+//
+// Work is done in base 2: with c = log2(e)/eps,
+//     s_ij = (2c x_i) . y_j + beta_j,   beta_j = c hat_j + log2 w_j,
+//     hat_i = -(eps ln2) * log2 sum_j 2^(s_ij)
+// beta lives in the 4th lane of the packed key (x, y, z, beta), so one 16-byte
+// load brings a key and its bias.  Keys are read with wave-uniform addresses
+// (scalar loads, shared by all 64 lanes); each lane owns one query row.
+//
+// Online log-sum-exp with a lazy maximum: each lane keeps (M, S) meaning
+// S * 2^M.  Scores are formed relative to M; only when a tile holds a value
+// more than kLazy above M is the tile re-evaluated against the new maximum
+// and S rescaled.  The result is the exact LSE up to fp32 rounding, because
+// LSE(z) = M + log2 sum 2^(z - M) for any M and no term exceeds 2^kLazy.
+//
+// A work-group = 4 waves on the same 64 rows, each streaming every 4th key
+// tile; the four (M, S) states merge through LDS.  When a batch has too few
+// rows to fill the chip the key range is also split across work-groups and a
+// second small kernel merges the partial states.
+#include "common.h"
+
+namespace sk {
+namespace {
+
+constexpr int kTile = 16;      // keys per tile (64 SGPRs)
+constexpr int kWaves = 4;      // waves per work-group, sharing rows
+constexpr float kLazy = 32.0f; // terms may reach 2^kLazy before a rescale
+
+__device__ __forceinline__ float score(float qx, float qy, float qz, float4 k, float base)
+{
+    return fmaf(qz, k.z, fmaf(qy, k.y, fmaf(qx, k.x, base)));
+}
+
+__global__ void pack3_kernel(const float *__restrict__ X, const float *__restrict__ w,
+                             const float *__restrict__ pot, int warm, int n, int n_pad,
+                             float4 *__restrict__ pts, float *__restrict__ hat,
+                             float *__restrict__ l2w, float c0)
+{
+    const int b = blockIdx.y;
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n_pad)
+        return;
+    float4 out = make_float4(0.f, 0.f, 0.f, kNeg);
+    if (i < n) {
+        const float *x = X + ((size_t)b * n + i) * 3;
+        float x0 = x[0], x1 = x[1], x2 = x[2];
+        float sq = fmaf(x2, x2, fmaf(x1, x1, x0 * x0));
+        float lw;
+        if (w) {
+            float wi = w[(size_t)b * n + i];
+            lw = wi > 0.f ? log2f(wi) : kNeg;
+        } else {
+            lw = -log2f((float)n);
+        }
+        float h = (warm ? pot[(size_t)b * n + i] : 0.f) - sq;
+        hat[(size_t)b * n + i] = h;
+        l2w[(size_t)b * n + i] = lw;
+        out = make_float4(x0, x1, x2, fmaf(c0, h, lw));
+    }
+    pts[(size_t)b * n_pad + i] = out;
+}
+
+// part == nullptr: single split, finalise in place.
+__global__ __launch_bounds__(kWaves *kWave) void lse3_kernel(
+    float4 *__restrict__ qpts, const float4 *__restrict__ kpts, float *__restrict__ qhat,
+    const float *__restrict__ ql2w, float2 *__restrict__ part, int nq, int nq_pad,
+    int nk_pad, int tiles_per_split, float two_c, float neg_eps_ln2, float c_next)
+{
+    __shared__ float2 red[kWaves][kWave];
+    const int b = blockIdx.z;
+    const int split = blockIdx.y;
+    const int lane = lane_id();
+    const int w = wave_id_uniform();
+    const int row = blockIdx.x * kWave + lane;
+
+    const float4 p = qpts[(size_t)b * nq_pad + row];
+    const float qx = two_c * p.x, qy = two_c * p.y, qz = two_c * p.z;
+    const float4 *kp = kpts + (size_t)b * nk_pad;
+    const int n_tiles = nk_pad / kTile;
+    const int t_begin = split * tiles_per_split;
+    const int t_end = min(t_begin + tiles_per_split, n_tiles);
+
+    float M = kNeg, S0 = 0.f, S1 = 0.f;
+    for (int t = t_begin + w; t < t_end; t += kWaves) {
+        const float4 *kt = kp + (size_t)t * kTile;
+        float4 kk[kTile];
+#pragma unroll
+        for (int u = 0; u < kTile; ++u)
+            kk[u] = kt[u];
+        float r[kTile];
+#pragma unroll
+        for (int u = 0; u < kTile; ++u)
+            r[u] = score(qx, qy, qz, kk[u], kk[u].w - M);
+        float cm = r[0];
+#pragma unroll
+        for (int u = 1; u < kTile; ++u)
+            cm = fmaxf(cm, r[u]);
+        if (cm > kLazy) {
+            // re-evaluate the tile against its own maximum, then rescale
+            float Mn = M;
+#pragma unroll
+            for (int u = 0; u < kTile; ++u) {
+                r[u] = score(qx, qy, qz, kk[u], kk[u].w);
+                Mn = fmaxf(Mn, r[u]);
+            }
+            const float scale = ex2(M - Mn);
+            S0 *= scale;
+            S1 *= scale;
+#pragma unroll
+            for (int u = 0; u < kTile; ++u)
+                r[u] -= Mn;
+            M = Mn;
+        }
+#pragma unroll
+        for (int u = 0; u < kTile; u += 2) {
+            S0 += ex2(r[u]);
+            S1 += ex2(r[u + 1]);
+        }
+    }
+    float S = S0 + S1;
+
+    red[w][lane] = make_float2(M, S);
+    __syncthreads();
+    if (w != 0)
+        return;
+#pragma unroll
+    for (int v = 1; v < kWaves; ++v) {
+        const float2 o = red[v][lane];
+        lse_merge(M, S, o.x, o.y);
+    }
+    if (part) {
+        part[((size_t)split * gridDim.z + b) * nq_pad + row] = make_float2(M, S);
+        return;
+    }
+    if (row < nq) {
+        const float h = (M + lg2(S)) * neg_eps_ln2;
+        const size_t i = (size_t)b * nq + row;
+        qhat[i] = h;
+        qpts[(size_t)b * nq_pad + row].w = fmaf(c_next, h, ql2w[i]);
+    }
+}
+
+__global__ void lse3_finalize(float4 *__restrict__ qpts, float *__restrict__ qhat,
+                              const float *__restrict__ ql2w, const float2 *__restrict__ part,
+                              int B, int nq, int nq_pad, int splits, float neg_eps_ln2,
+                              float c_next)
+{
+    const int b = blockIdx.y;
+    const int row = blockIdx.x * blockDim.x + threadIdx.x;
+    if (row >= nq)
+        return;
+    float2 s0 = part[(size_t)b * nq_pad + row];
+    float M = s0.x, S = s0.y;
+    for (int s = 1; s < splits; ++s) {
+        const float2 o = part[((size_t)s * B + b) * nq_pad + row];
+        lse_merge(M, S, o.x, o.y);
+    }
+    const float h = (M + lg2(S)) * neg_eps_ln2;
+    const size_t i = (size_t)b * nq + row;
+    qhat[i] = h;
+    qpts[(size_t)b * nq_pad + row].w = fmaf(c_next, h, ql2w[i]);
+}
+
+// Column splits so that a launch has about 4 work-groups per CU.
+int lse3_splits(int B, int nq_pad, int nk_pad)
+{
+    const long groups = (long)B * (nq_pad / kWave);
+    const int tiles = nk_pad / kTile;
+    int splits = (int)((1024 + groups - 1) / groups);
+    const int max_splits = tiles / (2 * kWaves);  // keep >= 2 tiles per wave
+    if (splits > max_splits)
+        splits = max_splits;
+    return splits < 1 ? 1 : splits;
+}
+
+}  // namespace
+
+size_t lse3_partial_floats2(int B, int nq_pad, int nk_pad)
+{
+    const int s = lse3_splits(B, nq_pad, nk_pad);
+    return s > 1 ? (size_t)s * B * nq_pad : 0;
+}
+
+hipError_t launch_pack3(const float *X, const float *w, const float *pot, int warm, int B,
+                        Side3 s, float c0, hipStream_t st)
+{
+    dim3 grid(ceil_div(s.n_pad, 256), B);
+    hipLaunchKernelGGL(pack3_kernel, grid, dim3(256), 0, st, X, w, pot, warm, s.n, s.n_pad,
+                       s.pts, s.hat, s.l2w, c0);
+    return hipGetLastError();
+}
+
+hipError_t launch_lse3(Side3 q, Side3 k, int B, float eps, float eps_next, float2 *part,
+                       int part_cap, hipStream_t st)
+{
+    (void)part_cap;
+    const float c = kLog2e / eps;
+    const float c_next = kLog2e / eps_next;
+    const float neg_eps_ln2 = -eps * kLn2;
+    const int splits = lse3_splits(B, q.n_pad, k.n_pad);
+    const int tiles = k.n_pad / kTile;
+    const int tiles_per_split = ceil_div(tiles, splits);
+    dim3 grid(q.n_pad / kWave, splits, B);
+    hipLaunchKernelGGL(lse3_kernel, grid, dim3(kWaves * kWave), 0, st, q.pts,
+                       (const float4 *)k.pts, q.hat, (const float *)q.l2w,
+                       splits > 1 ? part : nullptr, q.n, q.n_pad, k.n_pad, tiles_per_split,
+                       2.0f * c, neg_eps_ln2, c_next);
+    if (splits > 1) {
+        dim3 g2(ceil_div(q.n, 256), B);
+        hipLaunchKernelGGL(lse3_finalize, g2, dim3(256), 0, st, q.pts, q.hat,
+                           (const float *)q.l2w, (const float2 *)part, B, q.n, q.n_pad, splits,
+                           neg_eps_ln2, c_next);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace sk

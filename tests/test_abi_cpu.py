@@ -1,0 +1,160 @@
+"""Host-side checks of the C ABI that need no GPU.
+
+Argument validation runs before any HIP call, so every call here returns an
+error code without touching a device; output buffers are host sentinels that
+must come back unchanged.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import sinkhorn_point_cloud_amd as sk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sinkhorn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sk.library_path()):
+        pytest.fail("libsinkhorn_amd.so not built: run __graft_entry__.build()")
+    return sk.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sinkhorn_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("sinkhorn_potentials", "sinkhorn_plan_coo", "sinkhorn_loss_grad"):
+        assert required in names
+    assert set(names) == set(sk.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = os.popen(f"nm -D --defined-only {sk.library_path()}").read()
+    for name in declared_functions():
+        assert re.search(rf"\bT {name}$", out, flags=re.M), name
+
+
+def test_status_strings(lib):
+    for code in range(6):
+        assert lib.sinkhorn_status_string(code)
+    assert lib.sinkhorn_status_string(99) == b"unknown status"
+
+
+def test_workspace_bytes(lib):
+    ws = lib.sinkhorn_workspace_bytes
+    for op in (0, 1, 2):
+        assert ws(op, 1, 1024, 1024, 3, 0) > 0
+        assert ws(op, 2, 1024, 1024, 3, 0) > ws(op, 1, 1024, 1024, 3, 0)
+        assert ws(op, 1, 4096, 1024, 3, 0) > ws(op, 1, 1024, 1024, 3, 0)
+    assert ws(0, 1, 65536, 65536, 3, 0) < 64 << 20     # O((n + m)), nothing n x m
+    assert ws(0, 1, 50000, 60000, 64, 1) > 0
+    assert ws(0, 1, 10, 10, 3, 1) > 0                  # bf16 d=3: feature kernel
+    assert ws(0, 1, 10, 10, 200, 0) == 0               # d > 128: no kernel
+    assert ws(0, 0, 10, 10, 3, 0) == 0
+    assert ws(3, 1, 10, 10, 3, 0) == 0
+    assert ws(0, 1, 1 << 25, 10, 3, 0) == 0
+
+
+DUMMY = ctypes.c_void_p(16)   # never dereferenced: validation fails first
+
+
+def _host(arr):
+    return arr.ctypes.data_as(ctypes.c_void_p)
+
+
+def _pot(lib, X=DUMMY, Y=DUMMY, dtype=0, B=1, n=8, m=9, d=3, eps=(0.1,), iters=(3,),
+         flags=0, cost=None, ws=DUMMY, ws_bytes=1 << 40, f=None, g=None):
+    e = (ctypes.c_float * max(1, len(eps)))(*eps)
+    it = (ctypes.c_int * max(1, len(iters)))(*iters)
+    return lib.sinkhorn_potentials(X, Y, dtype, None, None, B, n, m, d, e, it, len(eps), flags,
+                                   f if f is not None else DUMMY, g if g is not None else DUMMY,
+                                   cost, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(X=None), sk.SK_ERR_INVALID_ARG),
+    (dict(B=0), sk.SK_ERR_INVALID_ARG),
+    (dict(n=0), sk.SK_ERR_INVALID_ARG),
+    (dict(m=-1), sk.SK_ERR_INVALID_ARG),
+    (dict(dtype=7), sk.SK_ERR_INVALID_ARG),
+    (dict(eps=(0.0,)), sk.SK_ERR_INVALID_ARG),
+    (dict(eps=(float("nan"),)), sk.SK_ERR_INVALID_ARG),
+    (dict(eps=(0.1, float("inf")), iters=(1, 1)), sk.SK_ERR_INVALID_ARG),
+    (dict(iters=(-1,)), sk.SK_ERR_INVALID_ARG),
+    (dict(flags=4), sk.SK_ERR_INVALID_ARG),
+    (dict(eps=(), iters=(), cost=DUMMY), sk.SK_ERR_INVALID_ARG),
+    (dict(dtype=1, d=200), sk.SK_ERR_UNSUPPORTED),
+    (dict(d=129), sk.SK_ERR_UNSUPPORTED),
+    (dict(ws=None), sk.SK_ERR_WORKSPACE),
+    (dict(ws_bytes=100), sk.SK_ERR_WORKSPACE),
+])
+def test_potentials_rejects_bad_arguments_without_writing(lib, kw, code):
+    f = np.full(8, 123.0, dtype=np.float32)
+    g = np.full(9, 456.0, dtype=np.float32)
+    rc = _pot(lib, f=_host(f), g=_host(g), **kw)
+    assert rc == code, lib.sinkhorn_last_error()
+    assert lib.sinkhorn_last_error()
+    assert np.all(f == 123.0) and np.all(g == 456.0)
+
+
+def _coo(lib, eps=0.1, thr=1e-8, capacity=10, rows=DUMMY, offs=DUMMY, nnz=True, ws_bytes=1 << 40):
+    n_out = ctypes.c_int64(-7)
+    rc = lib.sinkhorn_plan_coo(DUMMY, DUMMY, 0, None, None, 1, 8, 9, 3, eps, DUMMY, DUMMY, thr,
+                               capacity, rows, DUMMY, DUMMY, offs,
+                               ctypes.byref(n_out) if nnz else None, DUMMY, ws_bytes, None)
+    return rc, n_out.value
+
+
+@pytest.mark.parametrize("kw", [dict(eps=0.0), dict(eps=-1.0), dict(thr=0.0), dict(thr=1.5),
+                                dict(capacity=-1), dict(rows=None), dict(offs=None),
+                                dict(nnz=False)])
+def test_plan_coo_rejects_bad_arguments(lib, kw):
+    rc, n_out = _coo(lib, **kw)
+    assert rc == sk.SK_ERR_INVALID_ARG
+    assert n_out == -7
+
+
+def test_plan_coo_workspace_check(lib):
+    rc, _ = _coo(lib, ws_bytes=10)
+    assert rc == sk.SK_ERR_WORKSPACE
+
+
+def test_loss_grad_rejects_bad_arguments(lib):
+    loss = np.full(1, 5.0, dtype=np.float32)
+    rc = lib.sinkhorn_loss_grad(DUMMY, DUMMY, 0, 1, 8, 9, 3, None, DUMMY, DUMMY, DUMMY,
+                                _host(loss), None, DUMMY, 1 << 40, None)
+    assert rc == sk.SK_ERR_INVALID_ARG
+    rc = lib.sinkhorn_loss_grad(DUMMY, DUMMY, 0, 1, 8, 9, 3, DUMMY, DUMMY, DUMMY, DUMMY,
+                                _host(loss), None, DUMMY, 8, None)
+    assert rc == sk.SK_ERR_WORKSPACE
+    assert loss[0] == 5.0
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    X = torch.zeros(1, 4, 3)
+    with pytest.raises(ValueError):
+        sk.potentials(X, X)
+
+
+def test_product_package_does_not_reach_the_oracle():
+    pkg = os.path.dirname(sk.__file__)
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, fn)).read()
+                assert not re.search(r"\b(import|from)\s+oracle|liboracle|sinkhorn_oracle",
+                                     text), fn
+    out = os.popen(f"ldd {sk.library_path()}").read()
+    assert "oracle" not in out

@@ -1,0 +1,303 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 CPU oracle.
+
+Tolerances (the stated targets):
+  potentials   ||f - f_ref||_inf / max(||f_ref||_inf, eps) <= 1e-4   (1e-2 bf16 MFMA config)
+  scalars      |c - c_ref| / |c_ref| <= 1e-4 (cost, each loss)
+  gradient     ||dX - dX_ref||_inf / ||dX_ref||_inf <= 1e-4
+  sparse plan  identical support except entries whose value is within 1e-3
+               (relative) of the threshold; values on the common support
+               agree to 1e-4 relative.
+Both sides always receive the same fp32 (or bf16) inputs; where one stage's
+output is the next one's input (potentials -> plan -> loss), the oracle's own
+values, rounded to fp32, are handed to the GPU, never the other way round.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+torch = pytest.importorskip("torch")
+sk = pytest.importorskip("sinkhorn_point_cloud_amd")
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+
+
+def host(t):
+    return t.detach().cpu().double().numpy()
+
+
+def rel_inf(got, ref, floor=0.0):
+    got, ref = np.asarray(got, dtype=np.float64), np.asarray(ref, dtype=np.float64)
+    return np.abs(got - ref).max() / max(np.abs(ref).max(), floor)
+
+
+def points(c):
+    if c.get("dtype") == "bf16":
+        return (dev(c["X_bits"].view(np.int16)).view(torch.bfloat16),
+                dev(c["Y_bits"].view(np.int16)).view(torch.bfloat16))
+    return dev(c["X"]), dev(c["Y"])
+
+
+def run_gpu(c, eps, iters, **kw):
+    X, Y = points(c)
+    f, g, cost = sk.potentials(X, Y, dev(c["a"]), dev(c["b"]), eps=eps, iters=iters, **kw)
+    torch.cuda.synchronize()
+    return f, g, cost
+
+
+def check_potentials(c, eps, iters, tol=1e-4, cost_tol=1e-4):
+    eps32 = np.float32(eps)
+    f, g, cost = run_gpu(c, eps, iters)
+    fo, go = oracle.potentials(c["X"], c["Y"], c["a"], c["b"], eps=eps32, iters=iters)
+    e_last = float(eps32[-1])
+    for p in range(c["X"].shape[0]):
+        assert rel_inf(host(f)[p], fo[p], e_last) <= tol, f"f pair {p}"
+        assert rel_inf(host(g)[p], go[p], e_last) <= tol, f"g pair {p}"
+    st = oracle.plan_stats(c["X"], c["Y"], c["a"], c["b"], fo, go, e_last)
+    np.testing.assert_allclose(host(cost), st["cost"], rtol=cost_tol, atol=0)
+    return f, g, fo, go
+
+
+# ------------------------------------------------------------ small, d = 3
+SMALL = [  # (B, n, m, weights, zero weights, eps, iters)
+    (1, 1, 1, "uniform", 0, [0.1], [3]),
+    (1, 7, 5, "dirichlet", 0, [0.05], [20]),
+    (1, 64, 64, "uniform", 0, [0.05], [10]),
+    (2, 100, 37, "dirichlet", 0, [0.03], [25]),
+    (3, 257, 300, "dirichlet", 2, [0.05], [15]),
+    (1, 1000, 1, "uniform", 0, [0.2], [4]),
+    (1, 1, 999, "dirichlet", 0, [0.2], [4]),
+    (2, 129, 1030, "dirichlet", 0, [1.0, 0.3, 0.1, 0.03], [3, 3, 3, 10]),
+    (1, 2000, 1500, "dirichlet", 0, [0.01], [30]),
+]
+
+
+@pytest.mark.parametrize("B,n,m,w,zw,eps,iters", SMALL)
+def test_potentials_d3_match_oracle(B, n, m, w, zw, eps, iters):
+    c = workloads.random_case(100 + n + m, B, n, m, 3, weights=w, zero_weights=zw)
+    check_potentials(c, eps, iters)
+
+
+def test_schedule_with_empty_stages_and_zero_iterations():
+    c = workloads.random_case(5, 1, 90, 70, 3, weights="dirichlet")
+    check_potentials(c, [0.5, 0.2, 0.05], [0, 6, 8])
+    f, g, cost = run_gpu(c, [0.05], [0])
+    assert torch.all(f == 0) and torch.all(g == 0)
+
+
+def test_translated_clouds_give_the_same_potentials():
+    # the cost is translation invariant; the GPU's attention form must stay accurate
+    c = workloads.random_case(8, 1, 300, 200, 3, weights="dirichlet")
+    check_potentials(c, [0.05], [20])
+    shifted = dict(c, X=(c["X"] + np.float32(3.0)), Y=(c["Y"] + np.float32(3.0)))
+    check_potentials(shifted, [0.05], [20])
+
+
+# ---------------------------------------------------------- feature path
+@pytest.mark.parametrize("dtype,d,n,m", [("f32", 8, 130, 77), ("f32", 64, 300, 257),
+                                          ("bf16", 64, 200, 333), ("bf16", 3, 65, 64),
+                                          ("f32", 128, 64, 100), ("bf16", 32, 1, 500)])
+def test_feature_potentials_match_oracle(dtype, d, n, m):
+    c = workloads.random_case(9 + d, 2, n, m, d, weights="dirichlet", dtype=dtype,
+                              spread=0.25)
+    check_potentials(c, [0.5, 0.1], [5, 10])
+
+
+# ---------------------------------------------------- warm start, determinism
+def test_warm_start_split_matches_single_run():
+    c = workloads.random_case(12, 2, 500, 400, 3, weights="dirichlet")
+    f1, g1, _ = run_gpu(c, [0.1, 0.03], [10, 10])
+    fa, ga, _ = run_gpu(c, [0.1], [10])
+    f2, g2, _ = run_gpu(c, [0.03], [10], f0=fa, g0=ga)
+    assert rel_inf(host(f2), host(f1), 0.03) < 1e-5
+    assert rel_inf(host(g2), host(g1), 0.03) < 1e-5
+
+
+def test_potentials_are_deterministic():
+    c = workloads.random_case(13, 3, 700, 650, 3, weights="dirichlet")
+    r1 = run_gpu(c, [0.02], [10])
+    r2 = run_gpu(c, [0.02], [10])
+    for a_, b_ in zip(r1, r2):
+        assert torch.equal(a_, b_)
+
+
+# ------------------------------------------------------------ sparse plan
+def compare_coo(got, ref, m, thr_val, band=1e-3, val_tol=1e-4):
+    """got/ref: (rows, cols, vals) of one pair.  Support equal except entries
+    within `band` (relative) of the threshold value; values agree on the rest."""
+    gk = got[0].astype(np.int64) * m + got[1]
+    rk = ref[0].astype(np.int64) * m + ref[1]
+    only_g = ~np.isin(gk, rk)
+    only_r = ~np.isin(rk, gk)
+    for v in np.concatenate([got[2][only_g], ref[2][only_r]]):
+        assert abs(v / thr_val - 1.0) <= band, f"value {v} vs threshold {thr_val}"
+    common, ig, ir = np.intersect1d(gk, rk, assume_unique=True, return_indices=True)
+    gv, rv = got[2][ig].astype(np.float64), ref[2][ir]
+    assert np.all(np.abs(gv - rv) <= val_tol * rv)
+    return len(common)
+
+
+def check_coo_given_potentials(c, eps, fo, go, pairs=None, thr=1e-8):
+    """Both sides get the oracle's potentials rounded to fp32."""
+    B = c["X"].shape[0]
+    pairs = range(B) if pairs is None else pairs
+    f32, g32 = fo.astype(np.float32), go.astype(np.float32)
+    X, Y = points(c)
+    rows, cols, vals, offs = sk.plan_coo(X, Y, dev(c["a"]), dev(c["b"]), dev(f32), dev(g32),
+                                         eps, thr)
+    rows, cols, vals, offs = (t.cpu().numpy() for t in (rows, cols, vals, offs))
+    assert offs[0] == 0 and np.all(np.diff(offs) >= 0) and offs[-1] == len(rows)
+    for p in pairs:
+        s = slice(offs[p], offs[p + 1])
+        # row-major order, no duplicates
+        key = rows[s].astype(np.int64) * c["Y"].shape[1] + cols[s]
+        assert np.all(np.diff(key) > 0)
+        ro, co, vo, oo = oracle.plan_coo(c["X"][p], c["Y"][p], c["a"][p], c["b"][p], f32[p],
+                                         g32[p], float(np.float32(eps)), thr)
+        thr_val = thr * np.max(vo)
+        compare_coo((rows[s], cols[s], vals[s]), (ro, co, vo), c["Y"].shape[1], thr_val)
+    return rows, cols, vals, offs
+
+
+@pytest.mark.parametrize("B,n,m,eps,thr", [(1, 33, 47, 0.02, 1e-8), (2, 300, 257, 0.01, 1e-8),
+                                           (3, 129, 64, 0.05, 1e-3), (1, 500, 700, 0.02, 1.0)])
+def test_coo_matches_oracle(B, n, m, eps, thr):
+    c = workloads.random_case(21 + n, B, n, m, 3, weights="dirichlet")
+    fo, go = oracle.potentials(c["X"], c["Y"], c["a"], c["b"], eps=np.float32([eps]),
+                               iters=[15])
+    check_coo_given_potentials(c, eps, fo, go, thr=thr)
+
+
+def test_coo_capacity_protocol():
+    c = workloads.random_case(31, 2, 200, 150, 3, weights="dirichlet")
+    fo, go = oracle.potentials(c["X"], c["Y"], c["a"], c["b"], eps=np.float32([0.05]),
+                               iters=[10])
+    X, Y = points(c)
+    args = (X, Y, dev(c["a"]), dev(c["b"]), dev(fo.astype(np.float32)),
+            dev(go.astype(np.float32)), 0.05, 1e-8)
+    with pytest.raises(sk.SinkhornError) as ei:
+        sk.plan_coo(*args, capacity=3)
+    assert ei.value.status == sk.SK_ERR_CAPACITY
+    rows, cols, vals, offs = sk.plan_coo(*args)
+    rows2, cols2, vals2, offs2 = sk.plan_coo(*args, capacity=rows.numel() + 5)
+    assert torch.equal(rows, rows2) and torch.equal(cols, cols2) and torch.equal(vals, vals2)
+    assert torch.equal(offs, offs2)
+
+
+# ------------------------------------------------------------ loss / grad
+def check_loss_grad_given_coo(c, rows, cols, vals, offs, tol=1e-5, pairs=None):
+    X, Y = points(c)
+    loss, dX = sk.loss_grad(X, Y, dev(rows.astype(np.int32)), dev(cols.astype(np.int32)),
+                            dev(vals.astype(np.float32)), dev(offs.astype(np.int64)))
+    lo, dXo = oracle.loss_grad(c["X"], c["Y"], rows, cols, vals.astype(np.float32), offs)
+    pairs = range(c["X"].shape[0]) if pairs is None else pairs
+    for p in pairs:
+        assert abs(host(loss)[p] - lo[p]) <= tol * abs(lo[p]) + 1e-30
+        assert rel_inf(host(dX)[p], dXo[p], 1e-30) <= tol
+    return loss, dX
+
+
+@pytest.mark.parametrize("B,n,m,d,dtype", [(2, 100, 80, 3, "f32"), (1, 257, 300, 3, "f32"),
+                                           (2, 70, 90, 64, "bf16"), (1, 40, 50, 8, "f32")])
+def test_loss_grad_matches_oracle(B, n, m, d, dtype):
+    c = workloads.random_case(41 + n, B, n, m, d, weights="dirichlet", dtype=dtype,
+                              spread=1.0 if d <= 8 else 0.25)
+    eps = 0.05
+    fo, go = oracle.potentials(c["X"], c["Y"], c["a"], c["b"], eps=np.float32([eps]),
+                               iters=[10])
+    rows, cols, vals, offs = oracle.plan_coo(c["X"], c["Y"], c["a"], c["b"], fo, go,
+                                             float(np.float32(eps)), 1e-6)
+    check_loss_grad_given_coo(c, rows, cols, vals, offs)
+
+
+def test_loss_grad_rows_without_entries_and_empty_pairs():
+    c = workloads.random_case(43, 3, 50, 40, 3, weights="dirichlet")
+    rows = np.array([0, 0, 7, 49, 3, 3, 3], dtype=np.int32)
+    cols = np.array([1, 39, 0, 5, 2, 8, 9], dtype=np.int32)
+    vals = np.array([0.1, 0.2, 0.3, 0.05, 0.5, 0.25, 0.125], dtype=np.float32)
+    offs = np.array([0, 4, 4, 7], dtype=np.int64)     # pair 1 has no entries
+    loss, dX = check_loss_grad_given_coo(c, rows, cols, vals, offs)
+    assert host(loss)[1] == 0.0 and np.all(host(dX)[1] == 0.0)
+    assert np.all(host(dX)[0, 1:7] == 0.0)
+
+
+def test_plan_chain_on_gpu_potentials():
+    # GPU potentials -> GPU plan -> GPU loss against the oracle's own chain
+    c = workloads.random_case(44, 2, 400, 350, 3, weights="dirichlet")
+    eps = [0.02]
+    f, g, _ = run_gpu(c, eps, [20])
+    X, Y = points(c)
+    rows, cols, vals, offs = sk.plan_coo(X, Y, dev(c["a"]), dev(c["b"]), f, g, eps[0], 1e-8)
+    loss, dX = sk.loss_grad(X, Y, rows, cols, vals, offs)
+    fo, go = oracle.potentials(c["X"], c["Y"], c["a"], c["b"], eps=np.float32(eps), iters=[20])
+    ro, co, vo, oo = oracle.plan_coo(c["X"], c["Y"], c["a"], c["b"], fo, go,
+                                     float(np.float32(eps[0])), 1e-8)
+    lo, dXo = oracle.loss_grad(c["X"], c["Y"], ro, co, vo, oo)
+    np.testing.assert_allclose(host(loss), lo, rtol=1e-4)
+    for p in range(2):
+        assert rel_inf(host(dX)[p], dXo[p]) <= 1e-4
+
+
+# ------------------------------------------------------------ workloads
+def golden(name):
+    path = os.path.join(GOLDEN, f"{name}.npz")
+    if not os.path.exists(path):
+        pytest.skip(f"no stored oracle values for {name}")
+    z = np.load(path)
+    return {k: z[k] for k in z.files}
+
+
+def load_workload(name):
+    w = workloads.make(name)
+    gold = golden(name)
+    s = sum(np.asarray(w[k], dtype=np.float64).sum() for k in ("X", "Y", "a", "b"))
+    assert s == gold["input_sum"], "input generator drifted from the stored oracle run"
+    return w, gold
+
+
+def check_workload_potentials(name, tol):
+    w, gold = load_workload(name)
+    f, g, cost = run_gpu(w, list(w["eps"]), list(w["iters"]))
+    e_last = float(w["eps"][-1])
+    for p in range(w["X"].shape[0]):
+        assert rel_inf(host(f)[p], gold["f"][p], e_last) <= tol, f"f pair {p}"
+        assert rel_inf(host(g)[p], gold["g"][p], e_last) <= tol, f"g pair {p}"
+    np.testing.assert_allclose(host(cost), gold["cost"], rtol=tol)
+    return w, gold, f, g
+
+
+def test_workload_pair_1k():
+    check_workload_potentials("pair-1k", 1e-4)
+
+
+@pytest.mark.parametrize("name,pairs", [("sphere-2k", [0, 31]), ("blobs-1k", [0, 1, 128, 255])])
+def test_workload_sparse_plan_and_loss(name, pairs):
+    w, gold, f, g = check_workload_potentials(name, 1e-4)
+    eps = float(w["eps"][-1])
+    # plan: both sides from the oracle's potentials (rounded to fp32), sampled pairs
+    check_coo_given_potentials(w, eps, gold["f"].astype(np.float64),
+                               gold["g"].astype(np.float64), pairs=pairs)
+    # full GPU chain against the oracle's chain, every pair
+    X, Y = points(w)
+    rows, cols, vals, offs = sk.plan_coo(X, Y, dev(w["a"]), dev(w["b"]), f, g, eps,
+                                         w["threshold"])
+    loss, dX = sk.loss_grad(X, Y, rows, cols, vals, offs)
+    np.testing.assert_allclose(host(loss), gold["loss"], rtol=1e-4)
+    for k, p in enumerate(gold["dX_pairs"]):
+        assert rel_inf(host(dX)[p], gold["dX"][k]) <= 1e-4
+
+
+def test_workload_gmm_64k():
+    check_workload_potentials("gmm-64k", 1e-4)
+
+
+def test_workload_feat_50k():
+    check_workload_potentials("feat-50k", 1e-2)
