@@ -1,0 +1,171 @@
+"""Benchmark of the streaming Sinkhorn hot path on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gmm-64k] [--no-cpu-baseline]
+
+One step is the whole workload's hot path on inputs already resident in HBM:
+pack, every annealed Sinkhorn half-iteration and the transport-cost pass
+(gmm-64k: 65536 x 65536 points, d = 3, eps 1.0 -> 0.01 over 10 stages of 20
+iterations).  Prints ONE JSON line with
+  value      B*n*m*iters / step time   (cost-entry updates per second)
+  roofline   the half-iteration kernel: entry evaluations per launch / its
+             average launch time (events on the library's stream, taken as the
+             difference between the full step and the same call with zero
+             iterations, divided by the number of half-iteration launches),
+             against the exp/FP32 ALU roofline of the chip
+  cpu_baseline  the fp64 oracle timed on one full iteration of the same
+             problem on this host's cores, scaled to updates per second.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X (gfx950) unit counts and clock
+N_CU = 256
+CLOCK_HZ = 2.4e9
+FP32_VECTOR_PEAK = 157.3e12        # flop/s (packed FP32 FMA)
+FLOPS_PER_EVAL_D3 = 9              # 3 mul + 3 add (score with bias) + max, subtract, accumulate
+EXP_LANES_PER_CLK_CU = 32          # v_exp_f32 issues at half the FMA rate (measured ~28.5)
+
+
+def alu_roofline_evals_per_s():
+    fp32 = FP32_VECTOR_PEAK / FLOPS_PER_EVAL_D3
+    exp = N_CU * CLOCK_HZ * EXP_LANES_PER_CLK_CU
+    return min(fp32, exp), fp32, exp
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=1)
+    p.add_argument("--workload", default="gmm-64k")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def cpu_baseline(w):
+    """Oracle (as it stands) on one full iteration of the workload at its final eps."""
+    import numpy as np
+    import oracle
+
+    X, Y, a, b = (w[k].astype(np.float64) for k in ("X", "Y", "a", "b"))
+    B, n, m = X.shape[0], X.shape[1], Y.shape[1]
+    t0 = time.perf_counter()
+    oracle.potentials(X, Y, a, b, eps=[float(w["eps"][-1])], iters=[1])
+    dt = time.perf_counter() - t0
+    return {"value": B * n * m / dt, "unit": "updates/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"1 full iteration (f- and g-update, {2 * B * n * m:.3g} entry "
+                      f"evaluations) of {w['name']} at eps={float(w['eps'][-1]):g}, fp64, "
+                      f"{dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU "
+              "split of the path is described in DESIGN.md, not run.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import sinkhorn_point_cloud_amd as sk
+    import workloads
+
+    w = workloads.make(args.workload)
+    dev = torch.device("cuda:0")
+    if w["dtype"] == "bf16":
+        X = torch.from_numpy(w["X_bits"].view(np.int16)).to(dev).view(torch.bfloat16)
+        Y = torch.from_numpy(w["Y_bits"].view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        X, Y = torch.from_numpy(w["X"]).to(dev), torch.from_numpy(w["Y"]).to(dev)
+    a, b = torch.from_numpy(w["a"]).to(dev), torch.from_numpy(w["b"]).to(dev)
+    B, n, d = X.shape
+    m = Y.shape[1]
+    eps = [float(e) for e in w["eps"]]
+    iters = [int(i) for i in w["iters"]]
+    total_iters = sum(iters)
+    f = torch.empty(B, n, device=dev)
+    g = torch.empty(B, m, device=dev)
+    cost = torch.empty(B, device=dev)
+    dt = sk.SK_F32 if w["dtype"] == "f32" else sk.SK_BF16
+    ws = torch.empty(sk.workspace_bytes(sk.SK_OP_POTENTIALS, B, n, m, d, dt), dtype=torch.uint8,
+                     device=dev)
+
+    def step(it=iters, with_cost=True):
+        sk.potentials(X, Y, a, b, eps=eps, iters=it, out=(f, g, cost if with_cost else None),
+                      cost=with_cost, workspace=ws)
+
+    def timed(fn, reps):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / reps
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    t_step = timed(step, args.steps)
+    wall = time.perf_counter() - t0
+    assert torch.isfinite(f).all() and torch.isfinite(g).all() and torch.isfinite(cost).all()
+
+    # fixed part of a step (pack + cost pass), the same call with zero iterations
+    zero = [0] * len(iters)
+    t_fixed = timed(lambda: step(zero, True), max(3, args.steps))
+    t_pack = timed(lambda: step(zero, False), max(3, args.steps))
+    launches = 2 * total_iters
+    t_launch = (t_step - t_fixed) / launches
+    evals_per_launch = B * n * m
+    achieved = evals_per_launch / t_launch
+    peak, fp32_bound, exp_bound = alu_roofline_evals_per_s()
+    serial = 1.0 / (1.0 / fp32_bound + 1.0 / exp_bound)
+
+    updates = B * n * m * total_iters
+    line = {
+        "metric": "Sinkhorn cost-entry updates/s (B*n*m*iters/s); % of exp/FP32 roofline",
+        "value": updates / t_step,
+        "unit": "updates/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": t_step * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w["dtype"],
+        "data": "synthetic",
+        "config": {"workload": w["name"], "B": B, "n": n, "m": m, "d": d,
+                   "eps": f"{eps[0]:g}->{eps[-1]:g} over {len(eps)} stage(s)",
+                   "iters": total_iters, "outputs": "potentials f, g and transport cost"},
+        "roofline": {"bound": "alu", "achieved": achieved / 1e12, "peak": peak / 1e12,
+                     "unit": "Teval/s", "frac": achieved / peak, "traffic": None,
+                     "kernel": "lse3_kernel (one half-iteration)" if (d == 3 and dt == 0)
+                     else "lseF_kernel (one half-iteration)",
+                     "launch_ms": t_launch * 1e3, "evals_per_launch": evals_per_launch,
+                     "serial_exp_fp32_peak": serial / 1e12,
+                     "frac_of_serial_peak": achieved / serial},
+        "phases_ms": {"step": t_step * 1e3, "pack": t_pack * 1e3,
+                      "cost_pass": (t_fixed - t_pack) * 1e3,
+                      "iterations": (t_step - t_fixed) * 1e3},
+        "potentials_updates_per_s": updates / (t_step - (t_fixed - t_pack)),
+        "wall_s_timed": wall,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -29,22 +29,6 @@ int hip_fail(hipError_t e, const char *where)
 constexpr int kMaxPoints = 1 << 24;
 constexpr int kPad = 64;
 
-// hat -> true potential, out = hat + ||x||^2
-template <typename T>
-__global__ void unhat_kernel(const T *__restrict__ X, int d, const float *__restrict__ hat,
-                             size_t count, float *__restrict__ out)
-{
-    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= count)
-        return;
-    float sq = 0.f;
-    for (int k = 0; k < d; ++k) {
-        const float v = Elem<T>::get(X, i * d + k);
-        sq = fmaf(v, v, sq);
-    }
-    out[i] = hat[i] + sq;
-}
-
 // Bump allocator over the caller's workspace (256-byte aligned pieces).
 struct Carve {
     char *base;
@@ -74,7 +58,7 @@ struct PotWs {
     // feature path
     float *xbias = nullptr, *ybias = nullptr;
     // both
-    float *fhat, *ghat, *l2a, *l2b;
+    float *l2a, *l2b;
     float2 *part;
     double *row_part;
 };
@@ -93,8 +77,6 @@ PotWs carve_potentials(Carve &c, int B, int n, int m, int d, int dtype)
         w.ybias = c.take<float>((size_t)B * mp);
         parts = std::max(lseF_partial_floats2(B, np, mp), lseF_partial_floats2(B, mp, np));
     }
-    w.fhat = c.take<float>((size_t)B * n);
-    w.ghat = c.take<float>((size_t)B * m);
     w.l2a = c.take<float>((size_t)B * n);
     w.l2b = c.take<float>((size_t)B * m);
     w.part = c.take<float2>(parts > 0 ? parts : 1);
@@ -143,19 +125,6 @@ size_t ws_size(int op, int B, int n, int m, int d, int dtype)
     else
         carve_loss(c, B, n);
     return c.off + 256;
-}
-
-hipError_t unhat(const void *X, int dtype, int d, const float *hat, size_t count, float *out,
-                 hipStream_t st)
-{
-    const unsigned blocks = (unsigned)((count + 255) / 256);
-    if (dtype == SK_BF16)
-        hipLaunchKernelGGL(unhat_kernel<uint16_t>, dim3(blocks), dim3(256), 0, st,
-                           (const uint16_t *)X, d, hat, count, out);
-    else
-        hipLaunchKernelGGL(unhat_kernel<float>, dim3(blocks), dim3(256), 0, st,
-                           (const float *)X, d, hat, count, out);
-    return hipGetLastError();
 }
 
 int check_ws(void *ws, size_t ws_bytes, size_t need)
@@ -249,21 +218,21 @@ int sinkhorn_potentials(const void *X, const void *Y, int dtype, const float *a,
             first = s;
             break;
         }
-    const float c0 = kLog2e / (first >= 0 ? eps[first] : 1.0f);
+    const double c0 = (double)scale_of(first >= 0 ? eps[first] : 1.0f);
     hipError_t e;
     const bool p3 = path3(dtype, d);
-    Side3 sx3{w.px, w.fhat, w.l2a, n, np}, sy3{w.py, w.ghat, w.l2b, m, mp};
-    SideF sxf{X, w.xbias, w.fhat, w.l2a, nullptr, n, np}, syf{Y, w.ybias, w.ghat, w.l2b, nullptr,
-                                                             m, mp};
+    // the caller's f and g are the state of the iteration
+    Side3 sx3{w.px, f, w.l2a, n, np}, sy3{w.py, g, w.l2b, m, mp};
+    SideF sxf{X, w.xbias, f, w.l2a, n, np}, syf{Y, w.ybias, g, w.l2b, m, mp};
     if (p3) {
-        if ((e = launch_pack3((const float *)X, a, f, warm, B, sx3, c0, st)))
+        if ((e = launch_pack3((const float *)X, a, warm, B, sx3, c0, st)))
             return hip_fail(e, "pack X");
-        if ((e = launch_pack3((const float *)Y, b, g, warm, B, sy3, c0, st)))
+        if ((e = launch_pack3((const float *)Y, b, warm, B, sy3, c0, st)))
             return hip_fail(e, "pack Y");
     } else {
-        if ((e = launch_packF(X, dtype, d, a, f, warm, B, sxf, c0, st)))
+        if ((e = launch_packF(X, dtype, d, a, warm, B, sxf, c0, st)))
             return hip_fail(e, "pack X");
-        if ((e = launch_packF(Y, dtype, d, b, g, warm, B, syf, c0, st)))
+        if ((e = launch_packF(Y, dtype, d, b, warm, B, syf, c0, st)))
             return hip_fail(e, "pack Y");
     }
     for (int s = 0; s < n_stages; ++s) {
@@ -289,10 +258,6 @@ int sinkhorn_potentials(const void *X, const void *Y, int dtype, const float *a,
             }
         }
     }
-    if ((e = unhat(X, dtype, d, w.fhat, (size_t)B * n, f, st)))
-        return hip_fail(e, "unhat f");
-    if ((e = unhat(Y, dtype, d, w.ghat, (size_t)B * m, g, st)))
-        return hip_fail(e, "unhat g");
     if (cost) {
         PlanArgs p{X, Y, dtype, d, B, n, m, f, g, a, b, 1.0 / (double)eps[n_stages - 1]};
         if ((e = launch_cost(p, w.row_part, cost, st)))

@@ -15,6 +15,12 @@ constexpr float kNeg = -1.0e30f;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr double kLog2eD = 1.4426950408889634;
+constexpr double kLn2D = 0.6931471805599453;
+
+// c = log2(e)/eps rounded to fp32 once; every use of c (scores, biases, the
+// conversion of a row's log-sum-exp back to a potential) takes this value.
+inline float scale_of(float eps) { return (float)(kLog2eD / (double)eps); }
 
 // Hardware base-2 exponential and logarithm (v_exp_f32 / v_log_f32).
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -86,13 +92,14 @@ inline int round_up(int a, int b) { return ceil_div(a, b) * b; }
 // Points of one side packed for the d = 3 streaming kernel: (x, y, z, bias).
 struct Side3 {
     float4 *pts;      // [B][n_pad] (x, y, z, bias for the opposite pass)
-    float *hat;       // [B][n]     hat potential (nats)
+    float *pot;       // [B][n]     potential of this side (the state; in/out)
     float *l2w;       // [B][n]     log2 of the weights (kNeg for 0)
     int n, n_pad;
 };
 
-hipError_t launch_pack3(const float *X, const float *w, const float *pot, int warm, int B,
-                        Side3 s, float c0, hipStream_t st);
+// Packs points and the initial bias; without warm start the potential is set to 0.
+hipError_t launch_pack3(const float *X, const float *w, int warm, int B, Side3 s, double c0,
+                        hipStream_t st);
 // One half-iteration, d = 3: q side rows, k side columns.
 hipError_t launch_lse3(Side3 q, Side3 k, int B, float eps, float eps_next, float2 *part,
                        int part_cap, hipStream_t st);
@@ -102,21 +109,16 @@ size_t lse3_partial_floats2(int B, int nq_pad, int nk_pad);
 struct SideF {
     const void *pts;  // [B][n][d] original points (fp32 or bf16)
     float *bias;      // [B][n_pad] bias for the opposite pass
-    float *hat;       // [B][n]
+    float *pot;       // [B][n] potential of this side (the state; in/out)
     float *l2w;       // [B][n]
-    float *sq;        // [B][n] squared norms
     int n, n_pad;
 };
-hipError_t launch_packF(const void *X, int dtype, int d, const float *w, const float *pot,
-                        int warm, int B, SideF s, float c0, hipStream_t st);
+hipError_t launch_packF(const void *X, int dtype, int d, const float *w, int warm, int B,
+                        SideF s, double c0, hipStream_t st);
 hipError_t launch_lseF(SideF q, SideF k, int dtype, int d, int B, float eps, float eps_next,
                        float2 *part, hipStream_t st);
 size_t lseF_partial_floats2(int B, int nq_pad, int nk_pad);
 bool lseF_supported(int dtype, int d);
-
-// hat -> true potential: out = hat + ||x||^2
-hipError_t launch_unhat(const void *X, int dtype, int d, const float *hat, int B, int n,
-                        float *out, hipStream_t st);
 
 // Plan evaluation passes, shared by the cost, max, count and emit steps.
 struct PlanArgs {

@@ -1,21 +1,28 @@
 // lse_d3.hip -- fused streaming half-iteration for 3-D point clouds (fp32).
 //
 // One launch computes, for every row i of the "query" side and every pair b,
-//     hat_i = -eps * LSE_j[(2 x_i . y_j + hat_j + eps log w_j) / eps]
-// i.e. the stabilised log-domain update in its biased dot-product form
+//     f_i = -eps * LSE_j[(g_j - ||x_i - y_j||^2)/eps + log w_j]
+// as the stabilised log-domain update in its biased dot-product form
 // (FlashSinkhorn summary, Methodologie 1, Propositie 1: Q = sqrt2 X, K = sqrt2 Y,
-// the row-broadcast bias is the opposite hat potential plus eps log w).  With
+// the row-broadcast bias is the opposite hat potential g - ||y||^2 plus
+// eps log w; the row's own ||x_i||^2 leaves the LSE and is added back).  With
 // rows = X this is the f-update, with rows = Y the g-update (the same kernel,
 // roles swapped).  The score matrix only exists tile by tile in registers
 // (Methodologie 2: no n x m matrix in memory, online max / sum-exp on chip,
 // one fused pass per update, query rows held stationary).
 //
 // Work is done in base 2: with c = log2(e)/eps,
-//     s_ij = (2c x_i) . y_j + beta_j,   beta_j = c hat_j + log2 w_j,
-//     hat_i = -(eps ln2) * log2 sum_j 2^(s_ij)
+//     s_ij = (2c x_i) . y_j + beta_j,   beta_j = c (g_j - ||y_j||^2) + log2 w_j,
+//     f_i  = ||x_i||^2 - (eps ln2) * log2 sum_j 2^(s_ij)
 // beta lives in the 4th lane of the packed key (x, y, z, beta), so one 16-byte
 // load brings a key and its bias.  Keys are read with wave-uniform addresses
 // (scalar loads, shared by all 64 lanes); each lane owns one query row.
+//
+// The state carried between passes is the true potential (f, g), not the hat
+// potential f - ||x||^2: when the clouds are far from the origin compared with
+// the size of the potentials, an fp32 hat potential would lose an ulp of
+// ||x||^2 on every pass.  Each row's result and the bias it hands to the
+// other pass are formed in fp64 (a few operations per row) and rounded once.
 //
 // Online log-sum-exp with a lazy maximum: each lane keeps (M, S) meaning
 // S * 2^M.  Scores are formed relative to M; only when a tile holds a value
@@ -41,10 +48,20 @@ __device__ __forceinline__ float score(float qx, float qy, float qz, float4 k, f
     return fmaf(qz, k.z, fmaf(qy, k.y, fmaf(qx, k.x, base)));
 }
 
-__global__ void pack3_kernel(const float *__restrict__ X, const float *__restrict__ w,
-                             const float *__restrict__ pot, int warm, int n, int n_pad,
-                             float4 *__restrict__ pts, float *__restrict__ hat,
-                             float *__restrict__ l2w, float c0)
+__device__ __forceinline__ float sq3(float x0, float x1, float x2)
+{
+    return fmaf(x2, x2, fmaf(x1, x1, x0 * x0));
+}
+
+// bias handed to the other pass: c (pot - ||x||^2) + log2 w, rounded once
+__device__ __forceinline__ float bias_of(double c, float pot, float sq, float l2w)
+{
+    return (float)fma(c, (double)pot - (double)sq, (double)l2w);
+}
+
+__global__ void pack3_kernel(const float *__restrict__ X, const float *__restrict__ w, int warm,
+                             int n, int n_pad, float4 *__restrict__ pts, float *__restrict__ pot,
+                             float *__restrict__ l2w, double c0)
 {
     const int b = blockIdx.y;
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -53,28 +70,42 @@ __global__ void pack3_kernel(const float *__restrict__ X, const float *__restric
     float4 out = make_float4(0.f, 0.f, 0.f, kNeg);
     if (i < n) {
         const float *x = X + ((size_t)b * n + i) * 3;
-        float x0 = x[0], x1 = x[1], x2 = x[2];
-        float sq = fmaf(x2, x2, fmaf(x1, x1, x0 * x0));
+        const float x0 = x[0], x1 = x[1], x2 = x[2];
         float lw;
         if (w) {
-            float wi = w[(size_t)b * n + i];
+            const float wi = w[(size_t)b * n + i];
             lw = wi > 0.f ? log2f(wi) : kNeg;
         } else {
             lw = -log2f((float)n);
         }
-        float h = (warm ? pot[(size_t)b * n + i] : 0.f) - sq;
-        hat[(size_t)b * n + i] = h;
-        l2w[(size_t)b * n + i] = lw;
-        out = make_float4(x0, x1, x2, fmaf(c0, h, lw));
+        const size_t k = (size_t)b * n + i;
+        if (!warm)
+            pot[k] = 0.f;
+        l2w[k] = lw;
+        out = make_float4(x0, x1, x2, lw == kNeg ? kNeg : bias_of(c0, pot[k], sq3(x0, x1, x2), lw));
     }
     pts[(size_t)b * n_pad + i] = out;
 }
 
+// Row result: true potential from the (M, S) state, and the bias of this row
+// for the other pass.
+__device__ __forceinline__ void finish_row(float4 *qpts, float *qpot, const float *ql2w,
+                                           size_t pt, size_t k, float4 p, float M, float S,
+                                           double eps_ln2, double c_next)
+{
+    const float sq = sq3(p.x, p.y, p.z);
+    const double lse2 = (double)M + (double)lg2(S);
+    const float f = (float)((double)sq - lse2 * eps_ln2);
+    qpot[k] = f;
+    const float lw = ql2w[k];
+    qpts[pt].w = lw == kNeg ? kNeg : bias_of(c_next, f, sq, lw);
+}
+
 // part == nullptr: single split, finalise in place.
 __global__ __launch_bounds__(kWaves *kWave) void lse3_kernel(
-    float4 *__restrict__ qpts, const float4 *__restrict__ kpts, float *__restrict__ qhat,
+    float4 *__restrict__ qpts, const float4 *__restrict__ kpts, float *__restrict__ qpot,
     const float *__restrict__ ql2w, float2 *__restrict__ part, int nq, int nq_pad,
-    int nk_pad, int tiles_per_split, float two_c, float neg_eps_ln2, float c_next)
+    int nk_pad, int tiles_per_split, float two_c, double eps_ln2, double c_next)
 {
     __shared__ float2 red[kWaves][kWave];
     const int b = blockIdx.z;
@@ -142,18 +173,15 @@ __global__ __launch_bounds__(kWaves *kWave) void lse3_kernel(
         part[((size_t)split * gridDim.z + b) * nq_pad + row] = make_float2(M, S);
         return;
     }
-    if (row < nq) {
-        const float h = (M + lg2(S)) * neg_eps_ln2;
-        const size_t i = (size_t)b * nq + row;
-        qhat[i] = h;
-        qpts[(size_t)b * nq_pad + row].w = fmaf(c_next, h, ql2w[i]);
-    }
+    if (row < nq)
+        finish_row(qpts, qpot, ql2w, (size_t)b * nq_pad + row, (size_t)b * nq + row, p, M, S,
+                   eps_ln2, c_next);
 }
 
-__global__ void lse3_finalize(float4 *__restrict__ qpts, float *__restrict__ qhat,
+__global__ void lse3_finalize(float4 *__restrict__ qpts, float *__restrict__ qpot,
                               const float *__restrict__ ql2w, const float2 *__restrict__ part,
-                              int B, int nq, int nq_pad, int splits, float neg_eps_ln2,
-                              float c_next)
+                              int B, int nq, int nq_pad, int splits, double eps_ln2,
+                              double c_next)
 {
     const int b = blockIdx.y;
     const int row = blockIdx.x * blockDim.x + threadIdx.x;
@@ -165,10 +193,8 @@ __global__ void lse3_finalize(float4 *__restrict__ qpts, float *__restrict__ qha
         const float2 o = part[((size_t)s * B + b) * nq_pad + row];
         lse_merge(M, S, o.x, o.y);
     }
-    const float h = (M + lg2(S)) * neg_eps_ln2;
-    const size_t i = (size_t)b * nq + row;
-    qhat[i] = h;
-    qpts[(size_t)b * nq_pad + row].w = fmaf(c_next, h, ql2w[i]);
+    const size_t pt = (size_t)b * nq_pad + row;
+    finish_row(qpts, qpot, ql2w, pt, (size_t)b * nq + row, qpts[pt], M, S, eps_ln2, c_next);
 }
 
 // Column splits so that a launch has about 4 work-groups per CU.
@@ -191,12 +217,12 @@ size_t lse3_partial_floats2(int B, int nq_pad, int nk_pad)
     return s > 1 ? (size_t)s * B * nq_pad : 0;
 }
 
-hipError_t launch_pack3(const float *X, const float *w, const float *pot, int warm, int B,
-                        Side3 s, float c0, hipStream_t st)
+hipError_t launch_pack3(const float *X, const float *w, int warm, int B, Side3 s, double c0,
+                        hipStream_t st)
 {
     dim3 grid(ceil_div(s.n_pad, 256), B);
-    hipLaunchKernelGGL(pack3_kernel, grid, dim3(256), 0, st, X, w, pot, warm, s.n, s.n_pad,
-                       s.pts, s.hat, s.l2w, c0);
+    hipLaunchKernelGGL(pack3_kernel, grid, dim3(256), 0, st, X, w, warm, s.n, s.n_pad, s.pts,
+                       s.pot, s.l2w, c0);
     return hipGetLastError();
 }
 
@@ -204,22 +230,23 @@ hipError_t launch_lse3(Side3 q, Side3 k, int B, float eps, float eps_next, float
                        int part_cap, hipStream_t st)
 {
     (void)part_cap;
-    const float c = kLog2e / eps;
-    const float c_next = kLog2e / eps_next;
-    const float neg_eps_ln2 = -eps * kLn2;
+    // one fp32 value of c = log2(e)/eps is used everywhere (scores, bias, result)
+    const float c = scale_of(eps);
+    const double c_next = (double)scale_of(eps_next);
+    const double eps_ln2 = 1.0 / (double)c;
     const int splits = lse3_splits(B, q.n_pad, k.n_pad);
     const int tiles = k.n_pad / kTile;
     const int tiles_per_split = ceil_div(tiles, splits);
     dim3 grid(q.n_pad / kWave, splits, B);
     hipLaunchKernelGGL(lse3_kernel, grid, dim3(kWaves * kWave), 0, st, q.pts,
-                       (const float4 *)k.pts, q.hat, (const float *)q.l2w,
+                       (const float4 *)k.pts, q.pot, (const float *)q.l2w,
                        splits > 1 ? part : nullptr, q.n, q.n_pad, k.n_pad, tiles_per_split,
-                       2.0f * c, neg_eps_ln2, c_next);
+                       2.0f * c, eps_ln2, c_next);
     if (splits > 1) {
         dim3 g2(ceil_div(q.n, 256), B);
-        hipLaunchKernelGGL(lse3_finalize, g2, dim3(256), 0, st, q.pts, q.hat,
+        hipLaunchKernelGGL(lse3_finalize, g2, dim3(256), 0, st, q.pts, q.pot,
                            (const float *)q.l2w, (const float2 *)part, B, q.n, q.n_pad, splits,
-                           neg_eps_ln2, c_next);
+                           eps_ln2, c_next);
     }
     return hipGetLastError();
 }

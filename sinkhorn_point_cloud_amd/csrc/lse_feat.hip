@@ -2,10 +2,11 @@
 // dimension d <= 128 (fp32 or bf16 points), computed on the vector ALUs.
 //
 // Same update as lse_d3.hip (FlashSinkhorn summary, Methodologie 1,
-// Propositie 1; streaming per Methodologie 2):
-//     hat_i = -eps * LSE_j[(2 x_i . y_j + hat_j + eps log w_j) / eps]
-// in base 2, s_ij = 2c (x_i . y_j) + beta_j with c = log2(e)/eps and
-// beta_j = c hat_j + log2 w_j kept in a separate bias array.
+// Propositie 1; streaming per Methodologie 2), in base 2:
+//     s_ij = 2c (x_i . y_j) + beta_j,  beta_j = c (g_j - ||y_j||^2) + log2 w_j,
+//     f_i  = ||x_i||^2 - (eps ln2) * log2 sum_j 2^(s_ij),   c = log2(e)/eps,
+// with beta in a separate bias array and the true potentials as the state
+// (row results and biases formed in fp64 and rounded once).
 //
 // Each lane owns one query row, held in registers as fp32.  A work-group of
 // 4 waves shares 64 rows; per step the group stages 4 tiles of kKeys keys in
@@ -21,11 +22,15 @@ constexpr int kKeys = 16;
 constexpr int kWaves = 4;
 constexpr float kLazy = 32.0f;
 
+__device__ __forceinline__ float bias_of(double c, float pot, float sq, float l2w)
+{
+    return l2w == kNeg ? kNeg : (float)fma(c, (double)pot - (double)sq, (double)l2w);
+}
+
 template <typename T>
 __global__ void packF_kernel(const T *__restrict__ X, int d, const float *__restrict__ w,
-                             const float *__restrict__ pot, int warm, int n, int n_pad,
-                             float *__restrict__ bias, float *__restrict__ hat,
-                             float *__restrict__ l2w, float c0)
+                             int warm, int n, int n_pad, float *__restrict__ bias,
+                             float *__restrict__ pot, float *__restrict__ l2w, double c0)
 {
     const int b = blockIdx.y;
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -48,18 +53,41 @@ __global__ void packF_kernel(const T *__restrict__ X, int d, const float *__rest
     } else {
         lw = -log2f((float)n);
     }
-    const float h = (warm ? pot[(size_t)b * n + i] : 0.f) - sq;
-    hat[(size_t)b * n + i] = h;
-    l2w[(size_t)b * n + i] = lw;
-    bias[(size_t)b * n_pad + i] = fmaf(c0, h, lw);
+    const size_t k = (size_t)b * n + i;
+    if (!warm)
+        pot[k] = 0.f;
+    l2w[k] = lw;
+    bias[(size_t)b * n_pad + i] = bias_of(c0, pot[k], sq, lw);
+}
+
+// squared norm of a row held in registers, summed in the order of packF_kernel
+template <int DP>
+__device__ __forceinline__ float row_sq(const float (&q)[DP], int d)
+{
+    float sq = 0.f;
+#pragma unroll
+    for (int k = 0; k < DP; ++k)
+        if (k < d)
+            sq = fmaf(q[k], q[k], sq);
+    return sq;
+}
+
+__device__ __forceinline__ void finish_row(float *qbias, float *qpot, const float *ql2w,
+                                           size_t pt, size_t k, float sq, float M, float S,
+                                           double eps_ln2, double c_next)
+{
+    const double lse2 = (double)M + (double)lg2(S);
+    const float f = (float)((double)sq - lse2 * eps_ln2);
+    qpot[k] = f;
+    qbias[pt] = bias_of(c_next, f, sq, ql2w[k]);
 }
 
 template <typename T, int DP>
 __global__ __launch_bounds__(kWaves *kWave) void lseF_kernel(
-    const T *__restrict__ qx_, float *__restrict__ qbias, float *__restrict__ qhat,
+    const T *__restrict__ qx_, float *__restrict__ qbias, float *__restrict__ qpot,
     const float *__restrict__ ql2w, const T *__restrict__ ky_, const float *__restrict__ kbias,
     float2 *__restrict__ part, int d, int nq, int nq_pad, int nk, int nk_pad,
-    int tiles_per_split, float two_c, float neg_eps_ln2, float c_next)
+    int tiles_per_split, float two_c, double eps_ln2, double c_next)
 {
     __shared__ float4 tile[kWaves][kKeys][DP / 4];
     __shared__ float2 red[kWaves][kWave];
@@ -152,18 +180,16 @@ __global__ __launch_bounds__(kWaves *kWave) void lseF_kernel(
         part[((size_t)split * gridDim.z + b) * nq_pad + row] = make_float2(M, S);
         return;
     }
-    if (row < nq) {
-        const float h = (M + lg2(S)) * neg_eps_ln2;
-        const size_t i = (size_t)b * nq + row;
-        qhat[i] = h;
-        qbias[(size_t)b * nq_pad + row] = fmaf(c_next, h, ql2w[i]);
-    }
+    if (row < nq)
+        finish_row(qbias, qpot, ql2w, (size_t)b * nq_pad + row, (size_t)b * nq + row,
+                   row_sq(q, d), M, S, eps_ln2, c_next);
 }
 
-__global__ void lseF_finalize(float *__restrict__ qbias, float *__restrict__ qhat,
-                              const float *__restrict__ ql2w, const float2 *__restrict__ part,
-                              int B, int nq, int nq_pad, int splits, float neg_eps_ln2,
-                              float c_next)
+template <typename T>
+__global__ void lseF_finalize(const T *__restrict__ qx_, int d, float *__restrict__ qbias,
+                              float *__restrict__ qpot, const float *__restrict__ ql2w,
+                              const float2 *__restrict__ part, int B, int nq, int nq_pad,
+                              int splits, double eps_ln2, double c_next)
 {
     const int b = blockIdx.y;
     const int row = blockIdx.x * blockDim.x + threadIdx.x;
@@ -175,10 +201,14 @@ __global__ void lseF_finalize(float *__restrict__ qbias, float *__restrict__ qha
         const float2 o = part[((size_t)s * B + b) * nq_pad + row];
         lse_merge(M, S, o.x, o.y);
     }
-    const float h = (M + lg2(S)) * neg_eps_ln2;
-    const size_t i = (size_t)b * nq + row;
-    qhat[i] = h;
-    qbias[(size_t)b * nq_pad + row] = fmaf(c_next, h, ql2w[i]);
+    const T *x = qx_ + ((size_t)b * nq + row) * d;
+    float sq = 0.f;
+    for (int k = 0; k < d; ++k) {
+        const float v = Elem<T>::get(x, k);
+        sq = fmaf(v, v, sq);
+    }
+    finish_row(qbias, qpot, ql2w, (size_t)b * nq_pad + row, (size_t)b * nq + row, sq, M, S,
+               eps_ln2, c_next);
 }
 
 int padded_dim(int d)
@@ -203,27 +233,27 @@ int lseF_splits(int B, int nq_pad, int nk_pad)
 }
 
 template <typename T, int DP>
-void launch_lseF_t(SideF q, SideF k, int d, int B, float two_c, float neg_eps_ln2,
-                   float c_next, float2 *part, hipStream_t st)
+void launch_lseF_t(SideF q, SideF k, int d, int B, float two_c, double eps_ln2,
+                   double c_next, float2 *part, hipStream_t st)
 {
     const int splits = lseF_splits(B, q.n_pad, k.n_pad);
     const int tiles = k.n_pad / kKeys;
     const int tps = ceil_div(tiles, splits);
     dim3 grid(q.n_pad / kWave, splits, B);
     hipLaunchKernelGGL((lseF_kernel<T, DP>), grid, dim3(kWaves * kWave), 0, st,
-                       (const T *)q.pts, q.bias, q.hat, (const float *)q.l2w,
+                       (const T *)q.pts, q.bias, q.pot, (const float *)q.l2w,
                        (const T *)k.pts, (const float *)k.bias, splits > 1 ? part : nullptr, d,
-                       q.n, q.n_pad, k.n, k.n_pad, tps, two_c, neg_eps_ln2, c_next);
+                       q.n, q.n_pad, k.n, k.n_pad, tps, two_c, eps_ln2, c_next);
     if (splits > 1) {
         dim3 g2(ceil_div(q.n, 256), B);
-        hipLaunchKernelGGL(lseF_finalize, g2, dim3(256), 0, st, q.bias, q.hat,
-                           (const float *)q.l2w, (const float2 *)part, B, q.n, q.n_pad, splits,
-                           neg_eps_ln2, c_next);
+        hipLaunchKernelGGL(lseF_finalize<T>, g2, dim3(256), 0, st, (const T *)q.pts, d, q.bias,
+                           q.pot, (const float *)q.l2w, (const float2 *)part, B, q.n, q.n_pad,
+                           splits, eps_ln2, c_next);
     }
 }
 
 template <typename T>
-void dispatch(SideF q, SideF k, int d, int B, float two_c, float ne, float cn, float2 *part,
+void dispatch(SideF q, SideF k, int d, int B, float two_c, double ne, double cn, float2 *part,
               hipStream_t st)
 {
     switch (padded_dim(d)) {
@@ -245,30 +275,30 @@ size_t lseF_partial_floats2(int B, int nq_pad, int nk_pad)
     return s > 1 ? (size_t)s * B * nq_pad : 0;
 }
 
-hipError_t launch_packF(const void *X, int dtype, int d, const float *w, const float *pot,
-                        int warm, int B, SideF s, float c0, hipStream_t st)
+hipError_t launch_packF(const void *X, int dtype, int d, const float *w, int warm, int B,
+                        SideF s, double c0, hipStream_t st)
 {
     dim3 grid(ceil_div(s.n_pad, 256), B);
     if (dtype == 1)
         hipLaunchKernelGGL(packF_kernel<uint16_t>, grid, dim3(256), 0, st,
-                           (const uint16_t *)X, d, w, pot, warm, s.n, s.n_pad, s.bias, s.hat,
-                           s.l2w, c0);
+                           (const uint16_t *)X, d, w, warm, s.n, s.n_pad, s.bias, s.pot, s.l2w,
+                           c0);
     else
         hipLaunchKernelGGL(packF_kernel<float>, grid, dim3(256), 0, st, (const float *)X, d, w,
-                           pot, warm, s.n, s.n_pad, s.bias, s.hat, s.l2w, c0);
+                           warm, s.n, s.n_pad, s.bias, s.pot, s.l2w, c0);
     return hipGetLastError();
 }
 
 hipError_t launch_lseF(SideF q, SideF k, int dtype, int d, int B, float eps, float eps_next,
                        float2 *part, hipStream_t st)
 {
-    const float c = kLog2e / eps;
-    const float c_next = kLog2e / eps_next;
-    const float neg_eps_ln2 = -eps * kLn2;
+    const float c = scale_of(eps);
+    const double c_next = (double)scale_of(eps_next);
+    const double eps_ln2 = 1.0 / (double)c;
     if (dtype == 1)
-        dispatch<uint16_t>(q, k, d, B, 2.0f * c, neg_eps_ln2, c_next, part, st);
+        dispatch<uint16_t>(q, k, d, B, 2.0f * c, eps_ln2, c_next, part, st);
     else
-        dispatch<float>(q, k, d, B, 2.0f * c, neg_eps_ln2, c_next, part, st);
+        dispatch<float>(q, k, d, B, 2.0f * c, eps_ln2, c_next, part, st);
     return hipGetLastError();
 }
 
