@@ -47,6 +47,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=1)
     p.add_argument("--workload", default="gmm-64k")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--valu-scores", action="store_true",
+                   help="d = 3: form scores on the vector ALUs (comparison)")
     return p.parse_args()
 
 
@@ -101,7 +103,7 @@ def main():
 
     def step(it=iters, with_cost=True):
         sk.potentials(X, Y, a, b, eps=eps, iters=it, out=(f, g, cost if with_cost else None),
-                      cost=with_cost, workspace=ws)
+                      cost=with_cost, workspace=ws, valu_scores=args.valu_scores)
 
     def timed(fn, reps):
         torch.cuda.synchronize()
@@ -151,7 +153,8 @@ def main():
                    "iters": total_iters, "outputs": "potentials f, g and transport cost"},
         "roofline": {"bound": "alu", "achieved": achieved / 1e12, "peak": peak / 1e12,
                      "unit": "Teval/s", "frac": achieved / peak, "traffic": None,
-                     "kernel": "lse3_kernel (one half-iteration)" if (d == 3 and dt == 0)
+                     "kernel": ("lse3_kernel" if args.valu_scores else "lse3m_kernel")
+                     + " (one half-iteration)" if (d == 3 and dt == 0)
                      else "lseF_kernel (one half-iteration)",
                      "launch_ms": t_launch * 1e3, "evals_per_launch": evals_per_launch,
                      "serial_exp_fp32_peak": serial / 1e12,

@@ -67,7 +67,10 @@ enum { SK_F32 = 0, SK_BF16 = 1 };
 enum { SK_OP_POTENTIALS = 0, SK_OP_PLAN_COO = 1, SK_OP_LOSS_GRAD = 2 };
 
 /* Flags of sinkhorn_potentials(). */
-#define SK_WARM_START 1u /* f and g hold starting potentials (resume) */
+#define SK_WARM_START 1u  /* f and g hold starting potentials (resume) */
+#define SK_VALU_SCORES 2u /* d = 3: form scores on the vector ALUs instead of the
+                             matrix cores (same results to fp32 rounding; slower
+                             on gfx950, kept for comparison) */
 
 /*
  * Supported shapes: B >= 1, 1 <= n, m <= 2^24, B*n and B*m <= 2^31, and

@@ -29,6 +29,7 @@ SK_OK, SK_ERR_INVALID_ARG, SK_ERR_UNSUPPORTED, SK_ERR_WORKSPACE, SK_ERR_CAPACITY
 SK_F32, SK_BF16 = 0, 1
 SK_OP_POTENTIALS, SK_OP_PLAN_COO, SK_OP_LOSS_GRAD = 0, 1, 2
 SK_WARM_START = 1
+SK_VALU_SCORES = 2
 
 EXPORTS = ("sinkhorn_workspace_bytes", "sinkhorn_potentials", "sinkhorn_plan_coo",
            "sinkhorn_loss_grad", "sinkhorn_status_string", "sinkhorn_last_error")
@@ -128,12 +129,14 @@ def _workspace(op, B, n, m, d, dt, device, workspace=None):
 
 
 def potentials(X, Y, a=None, b=None, eps=(0.05,), iters=(100,), f0=None, g0=None,
-               cost: bool = True, out=None, workspace=None):
+               cost: bool = True, out=None, workspace=None, valu_scores: bool = False):
     """Sinkhorn potentials over an eps schedule (one stage per entry of eps/iters).
 
     X [B,n,d], Y [B,m,d] (float32, or bfloat16), a [B,n], b [B,m] or None
     (uniform).  f0/g0 warm-start the run.  Returns (f [B,n], g [B,m], cost [B] or
-    None), all float32 on the device.  ``out`` = (f, g, cost) reuses buffers."""
+    None), all float32 on the device.  ``out`` = (f, g, cost) reuses buffers.
+    ``valu_scores`` forms the d = 3 scores on the vector ALUs instead of the
+    matrix cores."""
     lib = load_library()
     X, Y, dt = _points(X, Y)
     B, n, d = X.shape
@@ -150,7 +153,7 @@ def potentials(X, Y, a=None, b=None, eps=(0.05,), iters=(100,), f0=None, g0=None
         f = torch.empty(B, n, dtype=torch.float32, device=dev)
         g = torch.empty(B, m, dtype=torch.float32, device=dev)
         c = torch.empty(B, dtype=torch.float32, device=dev) if cost else None
-    flags = 0
+    flags = SK_VALU_SCORES if valu_scores else 0
     if (f0 is None) != (g0 is None):
         raise ValueError("warm start needs both f0 and g0")
     if f0 is not None:

@@ -25,6 +25,9 @@ ARCH = os.environ.get("SK_OFFLOAD_ARCH", "gfx950")
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC", "-Wall", "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs (gfx950 has one register file): no
+    # copies through the accumulation registers on every tile
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 

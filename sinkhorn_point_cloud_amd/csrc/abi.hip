@@ -54,7 +54,7 @@ bool supported(int dtype, int d) { return path3(dtype, d) || lseF_supported(dtyp
 
 struct PotWs {
     // d = 3 path
-    float4 *px = nullptr, *py = nullptr;
+    float4 *px = nullptr, *py = nullptr, *center = nullptr;
     // feature path
     float *xbias = nullptr, *ybias = nullptr;
     // both
@@ -71,6 +71,7 @@ PotWs carve_potentials(Carve &c, int B, int n, int m, int d, int dtype)
     if (path3(dtype, d)) {
         w.px = c.take<float4>((size_t)B * np);
         w.py = c.take<float4>((size_t)B * mp);
+        w.center = c.take<float4>(B);
         parts = std::max(lse3_partial_floats2(B, np, mp), lse3_partial_floats2(B, mp, np));
     } else {
         w.xbias = c.take<float>((size_t)B * np);
@@ -191,7 +192,7 @@ int sinkhorn_potentials(const void *X, const void *Y, int dtype, const float *a,
         return fail(SK_ERR_INVALID_ARG, "f and g must be non-NULL device pointers");
     if (n_stages < 0 || (n_stages > 0 && (!eps || !iters)))
         return fail(SK_ERR_INVALID_ARG, "n_stages=%d needs host arrays eps and iters", n_stages);
-    if (flags & ~SK_WARM_START)
+    if (flags & ~(SK_WARM_START | SK_VALU_SCORES))
         return fail(SK_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
     for (int s = 0; s < n_stages; ++s) {
         if (!(eps[s] > 0.f) || !isfinite(eps[s]))
@@ -209,6 +210,7 @@ int sinkhorn_potentials(const void *X, const void *Y, int dtype, const float *a,
     Carve c{(char *)ws};
     PotWs w = carve_potentials(c, B, n, m, d, dtype);
     const int warm = (flags & SK_WARM_START) ? 1 : 0;
+    const bool mfma = !(flags & SK_VALU_SCORES);
     const int np = round_up(n, kPad), mp = round_up(m, kPad);
 
     // eps of every half-iteration, in order
@@ -225,9 +227,11 @@ int sinkhorn_potentials(const void *X, const void *Y, int dtype, const float *a,
     Side3 sx3{w.px, f, w.l2a, n, np}, sy3{w.py, g, w.l2b, m, mp};
     SideF sxf{X, w.xbias, f, w.l2a, n, np}, syf{Y, w.ybias, g, w.l2b, m, mp};
     if (p3) {
-        if ((e = launch_pack3((const float *)X, a, warm, B, sx3, c0, st)))
+        if ((e = launch_center3((const float *)X, n, (const float *)Y, m, B, w.center, st)))
+            return hip_fail(e, "center");
+        if ((e = launch_pack3((const float *)X, a, warm, B, sx3, w.center, c0, st)))
             return hip_fail(e, "pack X");
-        if ((e = launch_pack3((const float *)Y, b, warm, B, sy3, c0, st)))
+        if ((e = launch_pack3((const float *)Y, b, warm, B, sy3, w.center, c0, st)))
             return hip_fail(e, "pack Y");
     } else {
         if ((e = launch_packF(X, dtype, d, a, warm, B, sxf, c0, st)))
@@ -246,9 +250,9 @@ int sinkhorn_potentials(const void *X, const void *Y, int dtype, const float *a,
                         break;
                     }
             if (p3) {
-                if ((e = launch_lse3(sx3, sy3, B, eps[s], eps[s], w.part, 0, st)))
+                if ((e = launch_lse3(sx3, sy3, B, eps[s], eps[s], w.part, mfma, st)))
                     return hip_fail(e, "f-update");
-                if ((e = launch_lse3(sy3, sx3, B, eps[s], eps_next, w.part, 0, st)))
+                if ((e = launch_lse3(sy3, sx3, B, eps[s], eps_next, w.part, mfma, st)))
                     return hip_fail(e, "g-update");
             } else {
                 if ((e = launch_lseF(sxf, syf, dtype, d, B, eps[s], eps[s], w.part, st)))

@@ -97,12 +97,17 @@ struct Side3 {
     int n, n_pad;
 };
 
-// Packs points and the initial bias; without warm start the potential is set to 0.
-hipError_t launch_pack3(const float *X, const float *w, int warm, int B, Side3 s, double c0,
-                        hipStream_t st);
-// One half-iteration, d = 3: q side rows, k side columns.
+// Per-pair center (bounding-box midpoint of both clouds) for the d = 3 path.
+hipError_t launch_center3(const float *X, int n, const float *Y, int m, int B, float4 *center,
+                          hipStream_t st);
+// Packs points relative to the pair's center, and the initial bias; without
+// warm start the potential is set to 0.
+hipError_t launch_pack3(const float *X, const float *w, int warm, int B, Side3 s,
+                        const float4 *center, double c0, hipStream_t st);
+// One half-iteration, d = 3: q side rows, k side columns; scores on the matrix
+// cores (mfma) or on the vector ALUs.
 hipError_t launch_lse3(Side3 q, Side3 k, int B, float eps, float eps_next, float2 *part,
-                       int part_cap, hipStream_t st);
+                       bool mfma, hipStream_t st);
 size_t lse3_partial_floats2(int B, int nq_pad, int nk_pad);
 
 // Generic-d feature path (fp32 or bf16 points, VALU).

@@ -59,8 +59,52 @@ __device__ __forceinline__ float bias_of(double c, float pot, float sq, float l2
     return (float)fma(c, (double)pot - (double)sq, (double)l2w);
 }
 
+// Center of each pair: midpoint of the bounding box of both clouds.  The
+// squared-Euclidean cost is unchanged by a common translation, so the packed
+// points are stored relative to it; this keeps ||x||^2 and 2 x . y, whose fp32
+// rounding the expanded score carries, as small as the clouds allow.
+__global__ __launch_bounds__(256) void center3_kernel(const float *__restrict__ X, int n,
+                                                      const float *__restrict__ Y, int m,
+                                                      float4 *__restrict__ center)
+{
+    __shared__ float lo[3][256], hi[3][256];
+    const int b = blockIdx.x, t = threadIdx.x;
+    float mn[3] = {INFINITY, INFINITY, INFINITY}, mx[3] = {-INFINITY, -INFINITY, -INFINITY};
+    for (int i = t; i < n + m; i += 256) {
+        const float *p = i < n ? X + ((size_t)b * n + i) * 3 : Y + ((size_t)b * m + i - n) * 3;
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            mn[k] = fminf(mn[k], p[k]);
+            mx[k] = fmaxf(mx[k], p[k]);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        lo[k][t] = mn[k];
+        hi[k][t] = mx[k];
+    }
+    __syncthreads();
+    for (int s = 128; s > 0; s >>= 1) {
+        if (t < s)
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                lo[k][t] = fminf(lo[k][t], lo[k][t + s]);
+                hi[k][t] = fmaxf(hi[k][t], hi[k][t + s]);
+            }
+        __syncthreads();
+    }
+    if (t == 0) {
+        float c[3];
+#pragma unroll
+        for (int k = 0; k < 3; ++k)
+            c[k] = isfinite(lo[k][0]) && isfinite(hi[k][0]) ? 0.5f * (lo[k][0] + hi[k][0]) : 0.f;
+        center[b] = make_float4(c[0], c[1], c[2], 0.f);
+    }
+}
+
 __global__ void pack3_kernel(const float *__restrict__ X, const float *__restrict__ w, int warm,
-                             int n, int n_pad, float4 *__restrict__ pts, float *__restrict__ pot,
+                             int n, int n_pad, const float4 *__restrict__ center,
+                             float4 *__restrict__ pts, float *__restrict__ pot,
                              float *__restrict__ l2w, double c0)
 {
     const int b = blockIdx.y;
@@ -70,7 +114,8 @@ __global__ void pack3_kernel(const float *__restrict__ X, const float *__restric
     float4 out = make_float4(0.f, 0.f, 0.f, kNeg);
     if (i < n) {
         const float *x = X + ((size_t)b * n + i) * 3;
-        const float x0 = x[0], x1 = x[1], x2 = x[2];
+        const float4 o = center[b];
+        const float x0 = x[0] - o.x, x1 = x[1] - o.y, x2 = x[2] - o.z;
         float lw;
         if (w) {
             const float wi = w[(size_t)b * n + i];
@@ -178,6 +223,166 @@ __global__ __launch_bounds__(kWaves *kWave) void lse3_kernel(
                    eps_ln2, c_next);
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-core variant.  The augmented score is a K = 4 contraction,
+//     s_ij - M = (2c x_i, 2c y_i, 2c z_i, 1) . (y_j, beta_j) + (-M),
+// Propositie 1's Q K^T plus its rank-one bias, so one v_mfma_f32_16x16x4_f32
+// per 16 x 16 block produces s - M with M riding in the accumulator input.
+// The vector ALUs are left with the exponential, the accumulation and a
+// per-tile check of the lazy maximum.
+//
+// Operand layout of v_mfma_f32_16x16x4_f32 (wave64): lane l supplies
+// A[l % 16][l / 16] and B[l / 16][l % 16]; it receives D[4 (l / 16) + r][l % 16]
+// in register r.  A wave covers 64 query rows as 4 groups of 16; per key tile
+// of 16 columns it issues 4 MFMAs.  Each (lane, group, register) keeps its own
+// (M, S) over the columns l % 16 + 16 t; the 16 lanes of a row merge at the end.
+// The accumulator input holds -M; +1e30 marks a state that has seen no key
+// yet, and the first key it sees is re-evaluated with a zero accumulator so
+// that M starts at an exact score.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kGroups = 4;        // 16-row groups per wave
+constexpr float kEmpty = 1.0e29f; // accumulator input above this: no key seen yet
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__global__ __launch_bounds__(kWaves *kWave) void lse3m_kernel(
+    float4 *__restrict__ qpts, const float *__restrict__ kflat, float *__restrict__ qpot,
+    const float *__restrict__ ql2w, float2 *__restrict__ part, int nq, int nq_pad,
+    int nk_pad, int tiles_per_split, float two_c, double eps_ln2, double c_next)
+{
+    __shared__ float2 red[kWaves][kWave];
+    const int b = blockIdx.z;
+    const int split = blockIdx.y;
+    const int lane = lane_id();
+    const int w = wave_id_uniform();
+    const int row0 = blockIdx.x * kWave;
+    const int kq = lane >> 4;      // operand k index this lane supplies / row quad it receives
+    const int c16 = lane & 15;     // operand row (A) or column (B) within a 16-block
+
+    float A[kGroups];
+    {
+        const float *qf = reinterpret_cast<const float *>(qpts + (size_t)b * nq_pad + row0);
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g)
+            A[g] = kq == 3 ? 1.0f : two_c * qf[(16 * g + c16) * 4 + kq];
+    }
+    f32x4 Cn[kGroups], S[kGroups];
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) {
+        Cn[g] = f32x4{-kNeg, -kNeg, -kNeg, -kNeg};
+        S[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    const float *kb = kflat + (size_t)b * nk_pad * 4;
+    const int n_tiles = nk_pad / kTile;
+    const int t_begin = split * tiles_per_split;
+    const int t_end = min(t_begin + tiles_per_split, n_tiles);
+
+    int t = t_begin + w;
+    // the key operand of the next tile is loaded one tile ahead; the clamped
+    // index keeps that load inside the pair's keys on the last tile
+    float Bv = kb[(min(t, n_tiles - 1) * kTile + c16) * 4 + kq];
+    for (; t < t_end; t += kWaves) {
+        const int tn = min(t + kWaves, t_end - 1);
+        const float Bn = kb[(tn * kTile + c16) * 4 + kq];
+        f32x4 D[kGroups];
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g)
+            D[g] = mfma4(A[g], Bv, Cn[g]);
+        float cm = D[0][0];
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                cm = fmaxf(cm, D[g][r]);
+        // The branch is taken by the whole wave (ballot): an MFMA ignores the
+        // execution mask and writes every lane, so it must never run with
+        // part of the wave switched off.
+        if (__ballot(cm > kLazy) != 0) {
+            // raise M where a score exceeds it by more than kLazy (by an integer,
+            // so the rescale of S is exact); states with no key yet restart from
+            // the exact score, read with a zero accumulator input
+            f32x4 Cx[kGroups];
+            uint32_t fresh = 0;
+#pragma unroll
+            for (int g = 0; g < kGroups; ++g)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float d = D[g][r], cn = Cn[g][r];
+                    float cx = cn;
+                    if (d > kLazy) {
+                        if (cn > kEmpty) {
+                            cx = 0.f;
+                            fresh |= 1u << (4 * g + r);
+                        } else {
+                            cx = cn - floorf(d);
+                            S[g][r] *= ex2(cx - cn);
+                        }
+                    }
+                    Cx[g][r] = cx;
+                }
+#pragma unroll
+            for (int g = 0; g < kGroups; ++g)
+                D[g] = mfma4(A[g], Bv, Cx[g]);
+#pragma unroll
+            for (int g = 0; g < kGroups; ++g)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (fresh & (1u << (4 * g + r))) {
+                        S[g][r] = 0.f;
+                        Cx[g][r] = -D[g][r];
+                        D[g][r] = 0.f;
+                    }
+#pragma unroll
+            for (int g = 0; g < kGroups; ++g)
+                Cn[g] = Cx[g];
+        }
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                S[g][r] += ex2(D[g][r]);
+        Bv = Bn;
+    }
+
+    // merge the 16 column partials of every row (lanes sharing kq), then the waves
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float M = -Cn[g][r], Sr = S[g][r];
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) {
+                const float M2 = __shfl_xor(M, off, kWave);
+                const float S2 = __shfl_xor(Sr, off, kWave);
+                lse_merge(M, Sr, M2, S2);
+            }
+            if (c16 == 0)
+                red[w][16 * g + 4 * kq + r] = make_float2(M, Sr);
+        }
+    __syncthreads();
+    if (w != 0)
+        return;
+    float2 st = red[0][lane];
+    float M = st.x, Sf = st.y;
+#pragma unroll
+    for (int v = 1; v < kWaves; ++v) {
+        const float2 o = red[v][lane];
+        lse_merge(M, Sf, o.x, o.y);
+    }
+    const int row = row0 + lane;
+    if (part) {
+        part[((size_t)split * gridDim.z + b) * nq_pad + row] = make_float2(M, Sf);
+        return;
+    }
+    if (row < nq)
+        finish_row(qpts, qpot, ql2w, (size_t)b * nq_pad + row, (size_t)b * nq + row,
+                   qpts[(size_t)b * nq_pad + row], M, Sf, eps_ln2, c_next);
+}
+
 __global__ void lse3_finalize(float4 *__restrict__ qpts, float *__restrict__ qpot,
                               const float *__restrict__ ql2w, const float2 *__restrict__ part,
                               int B, int nq, int nq_pad, int splits, double eps_ln2,
@@ -217,19 +422,25 @@ size_t lse3_partial_floats2(int B, int nq_pad, int nk_pad)
     return s > 1 ? (size_t)s * B * nq_pad : 0;
 }
 
-hipError_t launch_pack3(const float *X, const float *w, int warm, int B, Side3 s, double c0,
-                        hipStream_t st)
+hipError_t launch_center3(const float *X, int n, const float *Y, int m, int B, float4 *center,
+                          hipStream_t st)
+{
+    hipLaunchKernelGGL(center3_kernel, dim3(B), dim3(256), 0, st, X, n, Y, m, center);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack3(const float *X, const float *w, int warm, int B, Side3 s,
+                        const float4 *center, double c0, hipStream_t st)
 {
     dim3 grid(ceil_div(s.n_pad, 256), B);
-    hipLaunchKernelGGL(pack3_kernel, grid, dim3(256), 0, st, X, w, warm, s.n, s.n_pad, s.pts,
-                       s.pot, s.l2w, c0);
+    hipLaunchKernelGGL(pack3_kernel, grid, dim3(256), 0, st, X, w, warm, s.n, s.n_pad, center,
+                       s.pts, s.pot, s.l2w, c0);
     return hipGetLastError();
 }
 
 hipError_t launch_lse3(Side3 q, Side3 k, int B, float eps, float eps_next, float2 *part,
-                       int part_cap, hipStream_t st)
+                       bool mfma, hipStream_t st)
 {
-    (void)part_cap;
     // one fp32 value of c = log2(e)/eps is used everywhere (scores, bias, result)
     const float c = scale_of(eps);
     const double c_next = (double)scale_of(eps_next);
@@ -238,10 +449,16 @@ hipError_t launch_lse3(Side3 q, Side3 k, int B, float eps, float eps_next, float
     const int tiles = k.n_pad / kTile;
     const int tiles_per_split = ceil_div(tiles, splits);
     dim3 grid(q.n_pad / kWave, splits, B);
-    hipLaunchKernelGGL(lse3_kernel, grid, dim3(kWaves * kWave), 0, st, q.pts,
-                       (const float4 *)k.pts, q.pot, (const float *)q.l2w,
-                       splits > 1 ? part : nullptr, q.n, q.n_pad, k.n_pad, tiles_per_split,
-                       2.0f * c, eps_ln2, c_next);
+    if (mfma)
+        hipLaunchKernelGGL(lse3m_kernel, grid, dim3(kWaves * kWave), 0, st, q.pts,
+                           (const float *)k.pts, q.pot, (const float *)q.l2w,
+                           splits > 1 ? part : nullptr, q.n, q.n_pad, k.n_pad, tiles_per_split,
+                           2.0f * c, eps_ln2, c_next);
+    else
+        hipLaunchKernelGGL(lse3_kernel, grid, dim3(kWaves * kWave), 0, st, q.pts,
+                           (const float4 *)k.pts, q.pot, (const float *)q.l2w,
+                           splits > 1 ? part : nullptr, q.n, q.n_pad, k.n_pad, tiles_per_split,
+                           2.0f * c, eps_ln2, c_next);
     if (splits > 1) {
         dim3 g2(ceil_div(q.n, 256), B);
         hipLaunchKernelGGL(lse3_finalize, g2, dim3(256), 0, st, q.pts, q.pot,

@@ -53,9 +53,9 @@ def run_gpu(c, eps, iters, **kw):
     return f, g, cost
 
 
-def check_potentials(c, eps, iters, tol=1e-4, cost_tol=1e-4):
+def check_potentials(c, eps, iters, tol=1e-4, cost_tol=1e-4, **kw):
     eps32 = np.float32(eps)
-    f, g, cost = run_gpu(c, eps, iters)
+    f, g, cost = run_gpu(c, eps, iters, **kw)
     fo, go = oracle.potentials(c["X"], c["Y"], c["a"], c["b"], eps=eps32, iters=iters)
     e_last = float(eps32[-1])
     for p in range(c["X"].shape[0]):
@@ -80,10 +80,21 @@ SMALL = [  # (B, n, m, weights, zero weights, eps, iters)
 ]
 
 
+@pytest.mark.parametrize("scores", ["mfma", "valu"])
 @pytest.mark.parametrize("B,n,m,w,zw,eps,iters", SMALL)
-def test_potentials_d3_match_oracle(B, n, m, w, zw, eps, iters):
+def test_potentials_d3_match_oracle(B, n, m, w, zw, eps, iters, scores):
     c = workloads.random_case(100 + n + m, B, n, m, 3, weights=w, zero_weights=zw)
-    check_potentials(c, eps, iters)
+    check_potentials(c, eps, iters, valu_scores=scores == "valu")
+
+
+@pytest.mark.parametrize("scores", ["mfma", "valu"])
+def test_far_from_origin_and_huge_score_range(scores):
+    # clouds far from the origin at small eps: scores span thousands of log2
+    # units, so the running maximum is raised many times and the first keys
+    # seen are far below the row maximum
+    c = workloads.random_case(77, 2, 300, 333, 3, weights="dirichlet", spread=4.0)
+    c = dict(c, X=c["X"] + np.float32(10.0), Y=c["Y"] + np.float32(10.0))
+    check_potentials(c, [0.003], [5], valu_scores=scores == "valu")
 
 
 def test_schedule_with_empty_stages_and_zero_iterations():
@@ -121,12 +132,21 @@ def test_warm_start_split_matches_single_run():
     assert rel_inf(host(g2), host(g1), 0.03) < 1e-5
 
 
-def test_potentials_are_deterministic():
+@pytest.mark.parametrize("scores", ["mfma", "valu"])
+def test_potentials_are_deterministic(scores):
     c = workloads.random_case(13, 3, 700, 650, 3, weights="dirichlet")
-    r1 = run_gpu(c, [0.02], [10])
-    r2 = run_gpu(c, [0.02], [10])
+    r1 = run_gpu(c, [0.02], [10], valu_scores=scores == "valu")
+    r2 = run_gpu(c, [0.02], [10], valu_scores=scores == "valu")
     for a_, b_ in zip(r1, r2):
         assert torch.equal(a_, b_)
+
+
+def test_matrix_and_vector_score_paths_agree():
+    c = workloads.random_case(14, 2, 1000, 900, 3, weights="dirichlet")
+    f1, g1, c1 = run_gpu(c, [0.1, 0.02], [10, 10])
+    f2, g2, c2 = run_gpu(c, [0.1, 0.02], [10, 10], valu_scores=True)
+    assert rel_inf(host(f1), host(f2), 0.02) < 2e-5
+    assert rel_inf(host(g1), host(g2), 0.02) < 2e-5
 
 
 # ------------------------------------------------------------ sparse plan
