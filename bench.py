@@ -49,6 +49,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--valu-scores", action="store_true",
                    help="d = 3: form scores on the vector ALUs (comparison)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a plain 256 MiB device copy, so that HBM byte counters of "
+                        "a profiler run can be scaled by a kernel of known traffic")
     return p.parse_args()
 
 
@@ -165,6 +168,12 @@ def main():
         "potentials_updates_per_s": updates / (t_step - (t_fixed - t_pack)),
         "wall_s_timed": wall,
     }
+    if args.copy_calibration:
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        line["copy_calibration_bytes"] = {"read": src.numel() * 4, "write": dst.numel() * 4}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)

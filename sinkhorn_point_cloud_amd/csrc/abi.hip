@@ -54,13 +54,14 @@ bool supported(int dtype, int d) { return path3(dtype, d) || lseF_supported(dtyp
 
 struct PotWs {
     // d = 3 path
-    float4 *px = nullptr, *py = nullptr, *center = nullptr;
+    float4 *px = nullptr, *py = nullptr, *center = nullptr, *boxes = nullptr;
     // feature path
     float *xbias = nullptr, *ybias = nullptr;
     // both
     float *l2a, *l2b;
     float2 *part;
     double *row_part;
+    double *la, *lb;   // fp64 log-weights for the cost pass
 };
 
 PotWs carve_potentials(Carve &c, int B, int n, int m, int d, int dtype)
@@ -72,6 +73,7 @@ PotWs carve_potentials(Carve &c, int B, int n, int m, int d, int dtype)
         w.px = c.take<float4>((size_t)B * np);
         w.py = c.take<float4>((size_t)B * mp);
         w.center = c.take<float4>(B);
+        w.boxes = c.take<float4>((size_t)2 * B * center3_parts(n, m));
         parts = std::max(lse3_partial_floats2(B, np, mp), lse3_partial_floats2(B, mp, np));
     } else {
         w.xbias = c.take<float>((size_t)B * np);
@@ -82,18 +84,23 @@ PotWs carve_potentials(Carve &c, int B, int n, int m, int d, int dtype)
     w.l2b = c.take<float>((size_t)B * m);
     w.part = c.take<float2>(parts > 0 ? parts : 1);
     w.row_part = c.take<double>((size_t)B * n);
+    w.la = c.take<double>((size_t)B * n);
+    w.lb = c.take<double>((size_t)B * m);
     return w;
 }
 
 struct CooWs {
+    double *la, *lb;
     double *row_max, *pair_thr;
     int32_t *row_count;
     int64_t *row_off, *pair_tot;
 };
 
-CooWs carve_coo(Carve &c, int B, int n)
+CooWs carve_coo(Carve &c, int B, int n, int m)
 {
     CooWs w;
+    w.la = c.take<double>((size_t)B * n);
+    w.lb = c.take<double>((size_t)B * m);
     w.row_max = c.take<double>((size_t)B * n);
     w.pair_thr = c.take<double>(B);
     w.row_count = c.take<int32_t>((size_t)B * n);
@@ -122,7 +129,7 @@ size_t ws_size(int op, int B, int n, int m, int d, int dtype)
     if (op == SK_OP_POTENTIALS)
         carve_potentials(c, B, n, m, d, dtype);
     else if (op == SK_OP_PLAN_COO)
-        carve_coo(c, B, n);
+        carve_coo(c, B, n, m);
     else
         carve_loss(c, B, n);
     return c.off + 256;
@@ -227,7 +234,8 @@ int sinkhorn_potentials(const void *X, const void *Y, int dtype, const float *a,
     Side3 sx3{w.px, f, w.l2a, n, np}, sy3{w.py, g, w.l2b, m, mp};
     SideF sxf{X, w.xbias, f, w.l2a, n, np}, syf{Y, w.ybias, g, w.l2b, m, mp};
     if (p3) {
-        if ((e = launch_center3((const float *)X, n, (const float *)Y, m, B, w.center, st)))
+        if ((e = launch_center3((const float *)X, n, (const float *)Y, m, B, w.boxes, w.center,
+                                st)))
             return hip_fail(e, "center");
         if ((e = launch_pack3((const float *)X, a, warm, B, sx3, w.center, c0, st)))
             return hip_fail(e, "pack X");
@@ -263,7 +271,10 @@ int sinkhorn_potentials(const void *X, const void *Y, int dtype, const float *a,
         }
     }
     if (cost) {
-        PlanArgs p{X, Y, dtype, d, B, n, m, f, g, a, b, 1.0 / (double)eps[n_stages - 1]};
+        PlanArgs p{X, Y, dtype, d, B, n, m, f, g, w.la, w.lb, 1.0 / (double)eps[n_stages - 1]};
+        if ((e = launch_log_weights(a, B, n, w.la, st)) ||
+            (e = launch_log_weights(b, B, m, w.lb, st)))
+            return hip_fail(e, "log weights");
         if ((e = launch_cost(p, w.row_part, cost, st)))
             return hip_fail(e, "cost");
     }
@@ -295,9 +306,11 @@ int sinkhorn_plan_coo(const void *X, const void *Y, int dtype, const float *a, c
 
     hipStream_t st = (hipStream_t)stream;
     Carve c{(char *)ws};
-    CooWs w = carve_coo(c, B, n);
-    PlanArgs p{X, Y, dtype, d, B, n, m, f, g, a, b, 1.0 / (double)eps};
+    CooWs w = carve_coo(c, B, n, m);
+    PlanArgs p{X, Y, dtype, d, B, n, m, f, g, w.la, w.lb, 1.0 / (double)eps};
     hipError_t e;
+    if ((e = launch_log_weights(a, B, n, w.la, st)) || (e = launch_log_weights(b, B, m, w.lb, st)))
+        return hip_fail(e, "log weights");
     if ((e = launch_plan_max(p, w.row_max, w.pair_thr, log((double)rel_threshold), st)))
         return hip_fail(e, "plan max");
     if ((e = launch_plan_count(p, w.pair_thr, w.row_count, st)))

@@ -97,9 +97,11 @@ struct Side3 {
     int n, n_pad;
 };
 
-// Per-pair center (bounding-box midpoint of both clouds) for the d = 3 path.
-hipError_t launch_center3(const float *X, int n, const float *Y, int m, int B, float4 *center,
-                          hipStream_t st);
+// Per-pair center (bounding-box midpoint of both clouds) for the d = 3 path;
+// part holds center3_parts(n, m) * B partial boxes.
+int center3_parts(int n, int m);
+hipError_t launch_center3(const float *X, int n, const float *Y, int m, int B, float4 *part,
+                          float4 *center, hipStream_t st);
 // Packs points relative to the pair's center, and the initial bias; without
 // warm start the potential is set to 0.
 hipError_t launch_pack3(const float *X, const float *w, int warm, int B, Side3 s,
@@ -130,9 +132,11 @@ struct PlanArgs {
     const void *X, *Y;
     int dtype, d, B, n, m;
     const float *f, *g;      // true potentials
-    const float *a, *b;      // weights or NULL (uniform)
+    const double *la, *lb;   // natural log of the weights, [B][n] and [B][m] (-inf for 0)
     double inv_eps;
 };
+// log of the weights in fp64 (w == NULL: uniform 1/count)
+hipError_t launch_log_weights(const float *w, int B, int count, double *out, hipStream_t st);
 hipError_t launch_cost(const PlanArgs &p, double *row_part, float *cost, hipStream_t st);
 hipError_t launch_plan_max(const PlanArgs &p, double *row_max, double *pair_thr,
                            double log_rel_thr, hipStream_t st);

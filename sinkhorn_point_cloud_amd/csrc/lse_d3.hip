@@ -63,21 +63,12 @@ __device__ __forceinline__ float bias_of(double c, float pot, float sq, float l2
 // squared-Euclidean cost is unchanged by a common translation, so the packed
 // points are stored relative to it; this keeps ||x||^2 and 2 x . y, whose fp32
 // rounding the expanded score carries, as small as the clouds allow.
-__global__ __launch_bounds__(256) void center3_kernel(const float *__restrict__ X, int n,
-                                                      const float *__restrict__ Y, int m,
-                                                      float4 *__restrict__ center)
+constexpr int kCenterChunk = 8192;   // points per work-group of the partial boxes
+
+__device__ __forceinline__ void box_reduce(float (&mn)[3], float (&mx)[3])
 {
     __shared__ float lo[3][256], hi[3][256];
-    const int b = blockIdx.x, t = threadIdx.x;
-    float mn[3] = {INFINITY, INFINITY, INFINITY}, mx[3] = {-INFINITY, -INFINITY, -INFINITY};
-    for (int i = t; i < n + m; i += 256) {
-        const float *p = i < n ? X + ((size_t)b * n + i) * 3 : Y + ((size_t)b * m + i - n) * 3;
-#pragma unroll
-        for (int k = 0; k < 3; ++k) {
-            mn[k] = fminf(mn[k], p[k]);
-            mx[k] = fmaxf(mx[k], p[k]);
-        }
-    }
+    const int t = threadIdx.x;
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
         lo[k][t] = mn[k];
@@ -93,11 +84,59 @@ __global__ __launch_bounds__(256) void center3_kernel(const float *__restrict__ 
             }
         __syncthreads();
     }
-    if (t == 0) {
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        mn[k] = lo[k][0];
+        mx[k] = hi[k][0];
+    }
+}
+
+// Partial bounding boxes: work-group (c, b) covers points c*kCenterChunk ...
+// of the concatenation X_b, Y_b.  part[2 (b parts + c)] = (min, max).
+__global__ __launch_bounds__(256) void center3_parts_kernel(const float *__restrict__ X, int n,
+                                                            const float *__restrict__ Y, int m,
+                                                            float4 *__restrict__ part)
+{
+    const int b = blockIdx.y, c = blockIdx.x;
+    float mn[3] = {INFINITY, INFINITY, INFINITY}, mx[3] = {-INFINITY, -INFINITY, -INFINITY};
+    const int end = min(n + m, (c + 1) * kCenterChunk);
+    for (int i = c * kCenterChunk + threadIdx.x; i < end; i += 256) {
+        const float *p = i < n ? X + ((size_t)b * n + i) * 3 : Y + ((size_t)b * m + i - n) * 3;
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            mn[k] = fminf(mn[k], p[k]);
+            mx[k] = fmaxf(mx[k], p[k]);
+        }
+    }
+    box_reduce(mn, mx);
+    if (threadIdx.x == 0) {
+        const size_t o = 2 * ((size_t)b * gridDim.x + c);
+        part[o] = make_float4(mn[0], mn[1], mn[2], 0.f);
+        part[o + 1] = make_float4(mx[0], mx[1], mx[2], 0.f);
+    }
+}
+
+// Center of each pair: midpoint of the bounding box of both clouds.  The
+// squared-Euclidean cost is unchanged by a common translation, so the packed
+// points are stored relative to it; this keeps ||x||^2 and 2 x . y, whose fp32
+// rounding the expanded score carries, as small as the clouds allow.
+__global__ __launch_bounds__(256) void center3_kernel(const float4 *__restrict__ part, int parts,
+                                                     float4 *__restrict__ center)
+{
+    const int b = blockIdx.x;
+    float mn[3] = {INFINITY, INFINITY, INFINITY}, mx[3] = {-INFINITY, -INFINITY, -INFINITY};
+    for (int c = threadIdx.x; c < parts; c += 256) {
+        const float4 lo = part[2 * ((size_t)b * parts + c)];
+        const float4 hi = part[2 * ((size_t)b * parts + c) + 1];
+        mn[0] = fminf(mn[0], lo.x); mn[1] = fminf(mn[1], lo.y); mn[2] = fminf(mn[2], lo.z);
+        mx[0] = fmaxf(mx[0], hi.x); mx[1] = fmaxf(mx[1], hi.y); mx[2] = fmaxf(mx[2], hi.z);
+    }
+    box_reduce(mn, mx);
+    if (threadIdx.x == 0) {
         float c[3];
 #pragma unroll
         for (int k = 0; k < 3; ++k)
-            c[k] = isfinite(lo[k][0]) && isfinite(hi[k][0]) ? 0.5f * (lo[k][0] + hi[k][0]) : 0.f;
+            c[k] = isfinite(mn[k]) && isfinite(mx[k]) ? 0.5f * (mn[k] + mx[k]) : 0.f;
         center[b] = make_float4(c[0], c[1], c[2], 0.f);
     }
 }
@@ -249,12 +288,24 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c)
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// Shifted pass: every row streams against a fixed shift, the log-sum-exp of
+// its previous pass, M_i = c (||x_i||^2 - f_i).  Between passes potentials
+// move little, so 2^(s - M) stays in range and the loop is exponential plus
+// accumulation only.  The merged sum of each row is checked at the end: if any
+// row of the work-group left [2^-64, 2^100] (the shift was stale, e.g. on the
+// first pass or after a large change of eps), the whole group streams its
+// keys again with the lazy-maximum scheme below.  Either way the result is the
+// exact log-sum-exp to fp32 rounding.
+constexpr float kSumLo = 5.421010862e-20f;  // 2^-64
+constexpr float kSumHi = 1.2676506e30f;     // 2^100
+
 __global__ __launch_bounds__(kWaves *kWave) void lse3m_kernel(
     float4 *__restrict__ qpts, const float *__restrict__ kflat, float *__restrict__ qpot,
     const float *__restrict__ ql2w, float2 *__restrict__ part, int nq, int nq_pad,
     int nk_pad, int tiles_per_split, float two_c, double eps_ln2, double c_next)
 {
     __shared__ float2 red[kWaves][kWave];
+    __shared__ int redo;
     const int b = blockIdx.z;
     const int split = blockIdx.y;
     const int lane = lane_id();
@@ -263,24 +314,94 @@ __global__ __launch_bounds__(kWaves *kWave) void lse3m_kernel(
     const int kq = lane >> 4;      // operand k index this lane supplies / row quad it receives
     const int c16 = lane & 15;     // operand row (A) or column (B) within a 16-block
 
+    const float4 *qrow = qpts + (size_t)b * nq_pad + row0;
     float A[kGroups];
     {
-        const float *qf = reinterpret_cast<const float *>(qpts + (size_t)b * nq_pad + row0);
+        const float *qf = reinterpret_cast<const float *>(qrow);
 #pragma unroll
         for (int g = 0; g < kGroups; ++g)
             A[g] = kq == 3 ? 1.0f : two_c * qf[(16 * g + c16) * 4 + kq];
-    }
-    f32x4 Cn[kGroups], S[kGroups];
-#pragma unroll
-    for (int g = 0; g < kGroups; ++g) {
-        Cn[g] = f32x4{-kNeg, -kNeg, -kNeg, -kNeg};
-        S[g] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     const float *kb = kflat + (size_t)b * nk_pad * 4;
     const int n_tiles = nk_pad / kTile;
     const int t_begin = split * tiles_per_split;
     const int t_end = min(t_begin + tiles_per_split, n_tiles);
+    f32x4 Cn[kGroups], S[kGroups];
 
+    if (part == nullptr) {
+        // ---- shifted pass
+        const float c = 0.5f * two_c;
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int lr = 16 * g + 4 * kq + r;
+                const float4 p = qrow[lr];
+                const float f = row0 + lr < nq ? qpot[(size_t)b * nq + row0 + lr] : 0.f;
+                Cn[g][r] = -(c * (sq3(p.x, p.y, p.z) - f));
+                S[g][r] = 0.f;
+            }
+        // key operands are loaded two tiles ahead (clamped indices stay inside
+        // the pair); the scheduling barrier keeps each load ahead of its use
+        int t = t_begin + w;
+        const int last = max(t_end - 1, 0);
+        float B0 = kb[(min(t, last) * kTile + c16) * 4 + kq];
+        float B1 = kb[(min(t + kWaves, last) * kTile + c16) * 4 + kq];
+        for (; t < t_end; t += kWaves) {
+            const float B2 = kb[(min(t + 2 * kWaves, last) * kTile + c16) * 4 + kq];
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int g = 0; g < kGroups; ++g) {
+                const f32x4 D = mfma4(A[g], B0, Cn[g]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    S[g][r] += ex2(D[r]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            B0 = B1;
+            B1 = B2;
+        }
+        // every partial of a row has the same shift: the merge is a sum
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float Sr = S[g][r];
+#pragma unroll
+                for (int off = 1; off < 16; off <<= 1)
+                    Sr += __shfl_xor(Sr, off, kWave);
+                if (c16 == 0)
+                    red[w][16 * g + 4 * kq + r] = make_float2(-Cn[g][r], Sr);
+            }
+        if (threadIdx.x == 0)
+            redo = 0;
+        __syncthreads();
+        float Ssum = 0.f;
+        const float M = red[0][lane].x;
+        if (w == 0) {
+#pragma unroll
+            for (int v = 0; v < kWaves; ++v)
+                Ssum += red[v][lane].y;
+            if (row0 + lane < nq && !(Ssum >= kSumLo && Ssum <= kSumHi))
+                redo = 1;   // benign race: every writer stores 1 (padding rows never do)
+        }
+        __syncthreads();
+        if (!redo) {
+            const int row = row0 + lane;
+            if (w == 0 && row < nq)
+                finish_row(qpts, qpot, ql2w, (size_t)b * nq_pad + row, (size_t)b * nq + row,
+                           qpts[(size_t)b * nq_pad + row], M, Ssum, eps_ln2, c_next);
+            return;
+        }
+        __syncthreads();   // red is reused below
+    }
+
+    // ---- lazy-maximum pass
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) {
+        Cn[g] = f32x4{-kNeg, -kNeg, -kNeg, -kNeg};
+        S[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     int t = t_begin + w;
     // the key operand of the next tile is loaded one tile ahead; the clamped
     // index keeps that load inside the pair's keys on the last tile
@@ -422,10 +543,15 @@ size_t lse3_partial_floats2(int B, int nq_pad, int nk_pad)
     return s > 1 ? (size_t)s * B * nq_pad : 0;
 }
 
-hipError_t launch_center3(const float *X, int n, const float *Y, int m, int B, float4 *center,
-                          hipStream_t st)
+int center3_parts(int n, int m) { return ceil_div(n + m, kCenterChunk); }
+
+hipError_t launch_center3(const float *X, int n, const float *Y, int m, int B, float4 *part,
+                          float4 *center, hipStream_t st)
 {
-    hipLaunchKernelGGL(center3_kernel, dim3(B), dim3(256), 0, st, X, n, Y, m, center);
+    const int parts = center3_parts(n, m);
+    hipLaunchKernelGGL(center3_parts_kernel, dim3(parts, B), dim3(256), 0, st, X, n, Y, m, part);
+    hipLaunchKernelGGL(center3_kernel, dim3(B), dim3(256), 0, st, (const float4 *)part, parts,
+                       center);
     return hipGetLastError();
 }
 

@@ -42,12 +42,18 @@ __device__ __forceinline__ double sq_dist(const float (&x)[DP], const T *y, int 
     return s;
 }
 
-__device__ __forceinline__ double log_weight(const float *w, size_t i, int count)
+__global__ void log_weights_kernel(const float *__restrict__ w, int count, size_t total,
+                                   double *__restrict__ out)
 {
-    if (!w)
-        return -log((double)count);
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= total)
+        return;
+    if (!w) {
+        out[i] = -log((double)count);
+        return;
+    }
     const float v = w[i];
-    return v > 0.f ? log((double)v) : -INFINITY;
+    out[i] = v > 0.f ? log((double)v) : -INFINITY;
 }
 
 // log P_ij (nats) and C_ij for a row context and column j of one pair.  Written
@@ -70,7 +76,7 @@ __device__ void load_row(RowCtx<DP> &r, const PlanArgs &p, int b, int i)
     for (int k = 0; k < DP; ++k)
         r.x[k] = k < p.d ? Elem<T>::get(x, k) : 0.f;
     r.f = (double)p.f[(size_t)b * p.n + i];
-    r.la = log_weight(p.a, (size_t)b * p.n + i, p.n);
+    r.la = p.la[(size_t)b * p.n + i];
 }
 
 // mode 0: cost  (row sum of P C, double)   -> outd[row]
@@ -98,7 +104,7 @@ __global__ __launch_bounds__(kRowsPerGroup *kWave) void row_pass(PlanArgs p,
         const int j = j0 + lane;
         if (j < p.m) {
             double C;
-            const double lbj = log_weight(p.b, (size_t)b * p.m + j, p.m);
+            const double lbj = p.lb[(size_t)b * p.m + j];
             const double lp = log_plan<T, DP>(r, p, Yb, gb, lbj, j, &C);
             if (MODE == 0) {
                 const double P = (double)ex2((float)(lp * 1.4426950408889634));
@@ -257,7 +263,7 @@ __global__ __launch_bounds__(kRowsPerGroup *kWave) void emit_pass(
         double lp = 0.0;
         if (j < p.m) {
             double C;
-            const double lbj = log_weight(p.b, (size_t)b * p.m + j, p.m);
+            const double lbj = p.lb[(size_t)b * p.m + j];
             lp = log_plan<T, DP>(r, p, Yb, gb, lbj, j, &C);
             keep = lp >= t;
         }
@@ -302,6 +308,14 @@ void row_dispatch(const PlanArgs &p, const double *thr, double *outd, int32_t *o
 }
 
 }  // namespace
+
+hipError_t launch_log_weights(const float *w, int B, int count, double *out, hipStream_t st)
+{
+    const size_t total = (size_t)B * count;
+    hipLaunchKernelGGL(log_weights_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                       st, w, count, total, out);
+    return hipGetLastError();
+}
 
 hipError_t launch_cost(const PlanArgs &p, double *row_part, float *cost, hipStream_t st)
 {
