@@ -8,10 +8,10 @@ pack, every annealed Sinkhorn half-iteration and the transport-cost pass
 iterations).  Prints ONE JSON line with
   value      B*n*m*iters / step time   (cost-entry updates per second)
   roofline   the half-iteration kernel: entry evaluations per launch / its
-             average launch time (events on the library's stream, taken as the
-             difference between the full step and the same call with zero
-             iterations, divided by the number of half-iteration launches),
-             against the exp/FP32 ALU roofline of the chip
+             average launch time (events on the library's stream: the full step
+             minus the same step with every stage's iteration count halved,
+             divided by the difference in half-iteration launches), against the
+             exp/FP32 ALU roofline of the chip
   cpu_baseline  the fp64 oracle timed on one full iteration of the same
              problem on this host's cores, scaled to updates per second.
 """
@@ -34,10 +34,38 @@ FLOPS_PER_EVAL_D3 = 9              # 3 mul + 3 add (score with bias) + max, subt
 EXP_LANES_PER_CLK_CU = 32          # v_exp_f32 issues at half the FMA rate (measured ~28.5)
 
 
-def alu_roofline_evals_per_s():
-    fp32 = FP32_VECTOR_PEAK / FLOPS_PER_EVAL_D3
+BF16_MFMA_PEAK = 2.5e15            # flop/s, dense
+VECTOR_FLOPS_PER_EVAL_FEAT = 3     # per evaluation beside the dot product: bias fma + accumulate
+
+
+def roofline_evals_per_s(d):
+    """(peak, bound, fp32/vector bound, exp bound, matrix bound) in evaluations/s.
+    d = 3: min(FP32 vector / 9 flops, exp).  Feature clouds: the dot product's
+    2d flops on bf16 MFMA, the bias fma and accumulation on FP32 vector, exp."""
     exp = N_CU * CLOCK_HZ * EXP_LANES_PER_CLK_CU
-    return min(fp32, exp), fp32, exp
+    if d == 3:
+        fp32 = FP32_VECTOR_PEAK / FLOPS_PER_EVAL_D3
+        return min(fp32, exp), "alu", fp32, exp, None
+    fp32 = FP32_VECTOR_PEAK / VECTOR_FLOPS_PER_EVAL_FEAT
+    mfma = BF16_MFMA_PEAK / (2 * d)
+    peak = min(fp32, exp, mfma)
+    return peak, "mfma" if peak == mfma else "alu", fp32, exp, mfma
+
+
+def measured_traffic(kernel, workload, source):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    when there is none or the kernel's source has changed since it was taken."""
+    import glob
+    import hashlib
+
+    sha = hashlib.sha256(open(os.path.join(ROOT, source), "rb").read()).hexdigest()[:16]
+    for path in glob.glob(os.path.join(ROOT, "profiles", "traffic_*.md")):
+        for line in open(path):
+            parts = line.split()
+            if (len(parts) == 6 and parts[0] == "traffic_bytes_per_launch"
+                    and parts[1] == kernel and parts[2] == workload):
+                return float(parts[3]) if parts[5] == sha else None
+    return None
 
 
 def parse():
@@ -126,15 +154,16 @@ def main():
     wall = time.perf_counter() - t0
     assert torch.isfinite(f).all() and torch.isfinite(g).all() and torch.isfinite(cost).all()
 
-    # fixed part of a step (pack + cost pass), the same call with zero iterations
-    zero = [0] * len(iters)
-    t_fixed = timed(lambda: step(zero, True), max(3, args.steps))
-    t_pack = timed(lambda: step(zero, False), max(3, args.steps))
-    launches = 2 * total_iters
-    t_launch = (t_step - t_fixed) / launches
+    # the half-iteration kernel's launch time: the same step with every stage's
+    # iteration count halved (pack and cost pass unchanged), differenced
+    fewer = [max(1, i // 2) if i else 0 for i in iters]
+    t_fewer = timed(lambda: step(fewer, True), max(3, args.steps))
+    launches = 2 * (total_iters - sum(fewer))
+    t_launch = (t_step - t_fewer) / launches
+    t_iterations = t_launch * 2 * total_iters
     evals_per_launch = B * n * m
     achieved = evals_per_launch / t_launch
-    peak, fp32_bound, exp_bound = alu_roofline_evals_per_s()
+    peak, bound, fp32_bound, exp_bound, mfma_bound = roofline_evals_per_s(d)
     serial = 1.0 / (1.0 / fp32_bound + 1.0 / exp_bound)
 
     updates = B * n * m * total_iters
@@ -154,18 +183,22 @@ def main():
         "config": {"workload": w["name"], "B": B, "n": n, "m": m, "d": d,
                    "eps": f"{eps[0]:g}->{eps[-1]:g} over {len(eps)} stage(s)",
                    "iters": total_iters, "outputs": "potentials f, g and transport cost"},
-        "roofline": {"bound": "alu", "achieved": achieved / 1e12, "peak": peak / 1e12,
-                     "unit": "Teval/s", "frac": achieved / peak, "traffic": None,
+        "roofline": {"bound": bound, "achieved": achieved / 1e12, "peak": peak / 1e12,
+                     "unit": "Teval/s", "frac": achieved / peak,
+                     "traffic": measured_traffic("lse3m_kernel", w["name"],
+                                                 "sinkhorn_point_cloud_amd/csrc/lse_d3.hip")
+                     if (d == 3 and dt == 0 and not args.valu_scores) else None,
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                                     "scaled by a 256 MiB copy)",
                      "kernel": ("lse3_kernel" if args.valu_scores else "lse3m_kernel")
                      + " (one half-iteration)" if (d == 3 and dt == 0)
+                     else "lseFm_kernel (one half-iteration)" if dt == 1 and d % 32 == 0
                      else "lseF_kernel (one half-iteration)",
                      "launch_ms": t_launch * 1e3, "evals_per_launch": evals_per_launch,
                      "serial_exp_fp32_peak": serial / 1e12,
                      "frac_of_serial_peak": achieved / serial},
-        "phases_ms": {"step": t_step * 1e3, "pack": t_pack * 1e3,
-                      "cost_pass": (t_fixed - t_pack) * 1e3,
-                      "iterations": (t_step - t_fixed) * 1e3},
-        "potentials_updates_per_s": updates / (t_step - (t_fixed - t_pack)),
+        "phases_ms": {"step": t_step * 1e3, "iterations": t_iterations * 1e3,
+                      "pack_and_cost_pass": (t_step - t_iterations) * 1e3},
         "wall_s_timed": wall,
     }
     if args.copy_calibration:

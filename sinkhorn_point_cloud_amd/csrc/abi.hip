@@ -56,7 +56,8 @@ struct PotWs {
     // d = 3 path
     float4 *px = nullptr, *py = nullptr, *center = nullptr, *boxes = nullptr;
     // feature path
-    float *xbias = nullptr, *ybias = nullptr;
+    float *xbias = nullptr, *ybias = nullptr, *xsq = nullptr, *ysq = nullptr;
+    int *xredo = nullptr, *yredo = nullptr;
     // both
     float *l2a, *l2b;
     float2 *part;
@@ -78,6 +79,10 @@ PotWs carve_potentials(Carve &c, int B, int n, int m, int d, int dtype)
     } else {
         w.xbias = c.take<float>((size_t)B * np);
         w.ybias = c.take<float>((size_t)B * mp);
+        w.xsq = c.take<float>((size_t)B * n);
+        w.ysq = c.take<float>((size_t)B * m);
+        w.xredo = c.take<int>((size_t)B * (np / kPad));
+        w.yredo = c.take<int>((size_t)B * (mp / kPad));
         parts = std::max(lseF_partial_floats2(B, np, mp), lseF_partial_floats2(B, mp, np));
     }
     w.l2a = c.take<float>((size_t)B * n);
@@ -232,7 +237,8 @@ int sinkhorn_potentials(const void *X, const void *Y, int dtype, const float *a,
     const bool p3 = path3(dtype, d);
     // the caller's f and g are the state of the iteration
     Side3 sx3{w.px, f, w.l2a, n, np}, sy3{w.py, g, w.l2b, m, mp};
-    SideF sxf{X, w.xbias, f, w.l2a, n, np}, syf{Y, w.ybias, g, w.l2b, m, mp};
+    SideF sxf{X, w.xbias, f, w.l2a, w.xsq, w.xredo, n, np};
+    SideF syf{Y, w.ybias, g, w.l2b, w.ysq, w.yredo, m, mp};
     if (p3) {
         if ((e = launch_center3((const float *)X, n, (const float *)Y, m, B, w.boxes, w.center,
                                 st)))
@@ -270,7 +276,13 @@ int sinkhorn_potentials(const void *X, const void *Y, int dtype, const float *a,
             }
         }
     }
-    if (cost) {
+    if (cost && !p3 && iters[n_stages - 1] > 0 && lseF_matrix_cores(sxf, syf, dtype, d, B)) {
+        // the final passes left both biases at the last eps: stream the cost on the
+        // matrix cores like a half-iteration
+        if ((e = launch_costFm(sxf, syf, d, B, eps[n_stages - 1], w.row_part, st)) ||
+            (e = launch_row_sums(w.row_part, B, n, cost, st)))
+            return hip_fail(e, "cost");
+    } else if (cost) {
         PlanArgs p{X, Y, dtype, d, B, n, m, f, g, w.la, w.lb, 1.0 / (double)eps[n_stages - 1]};
         if ((e = launch_log_weights(a, B, n, w.la, st)) ||
             (e = launch_log_weights(b, B, m, w.lb, st)))

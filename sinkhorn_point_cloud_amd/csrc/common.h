@@ -118,6 +118,8 @@ struct SideF {
     float *bias;      // [B][n_pad] bias for the opposite pass
     float *pot;       // [B][n] potential of this side (the state; in/out)
     float *l2w;       // [B][n]
+    float *sq;        // [B][n] squared norms of the points
+    int *redo;        // [B][n_pad / 64] per-row-block fallback flags (matrix-core path)
     int n, n_pad;
 };
 hipError_t launch_packF(const void *X, int dtype, int d, const float *w, int warm, int B,
@@ -126,6 +128,13 @@ hipError_t launch_lseF(SideF q, SideF k, int dtype, int d, int B, float eps, flo
                        float2 *part, hipStream_t st);
 size_t lseF_partial_floats2(int B, int nq_pad, int nk_pad);
 bool lseF_supported(int dtype, int d);
+// true when both passes of this shape run on the matrix-core kernel
+bool lseF_matrix_cores(SideF q, SideF k, int dtype, int d, int B);
+// transport cost rows for the matrix-core feature path, from the biases of the
+// final passes (which must have run at eps)
+hipError_t launch_costFm(SideF x, SideF y, int d, int B, float eps, double *row_part,
+                         hipStream_t st);
+hipError_t launch_row_sums(const double *row_part, int B, int n, float *out, hipStream_t st);
 
 // Plan evaluation passes, shared by the cost, max, count and emit steps.
 struct PlanArgs {

@@ -30,7 +30,8 @@ __device__ __forceinline__ float bias_of(double c, float pot, float sq, float l2
 template <typename T>
 __global__ void packF_kernel(const T *__restrict__ X, int d, const float *__restrict__ w,
                              int warm, int n, int n_pad, float *__restrict__ bias,
-                             float *__restrict__ pot, float *__restrict__ l2w, double c0)
+                             float *__restrict__ pot, float *__restrict__ l2w,
+                             float *__restrict__ sqo, double c0)
 {
     const int b = blockIdx.y;
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -57,6 +58,7 @@ __global__ void packF_kernel(const T *__restrict__ X, int d, const float *__rest
     if (!warm)
         pot[k] = 0.f;
     l2w[k] = lw;
+    sqo[k] = sq;
     bias[(size_t)b * n_pad + i] = bias_of(c0, pot[k], sq, lw);
 }
 
@@ -86,9 +88,12 @@ template <typename T, int DP>
 __global__ __launch_bounds__(kWaves *kWave) void lseF_kernel(
     const T *__restrict__ qx_, float *__restrict__ qbias, float *__restrict__ qpot,
     const float *__restrict__ ql2w, const T *__restrict__ ky_, const float *__restrict__ kbias,
-    float2 *__restrict__ part, int d, int nq, int nq_pad, int nk, int nk_pad,
-    int tiles_per_split, float two_c, double eps_ln2, double c_next)
+    float2 *__restrict__ part, const int *__restrict__ only, int d, int nq, int nq_pad, int nk,
+    int nk_pad, int tiles_per_split, float two_c, double eps_ln2, double c_next)
 {
+    // only != nullptr: a fallback launch, work only on the row blocks flagged there
+    if (only && !only[blockIdx.z * gridDim.x + blockIdx.x])
+        return;
     __shared__ float4 tile[kWaves][kKeys][DP / 4];
     __shared__ float2 red[kWaves][kWave];
     const int b = blockIdx.z;
@@ -185,6 +190,245 @@ __global__ __launch_bounds__(kWaves *kWave) void lseF_kernel(
                    row_sq(q, d), M, S, eps_ln2, c_next);
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-core variant for bf16 features with d a multiple of 32 (the
+// high-dimensional workload).  The score's dot product x_i . y_j is a real
+// dense contraction: v_mfma_f32_16x16x32_bf16 multiplies bf16 inputs exactly
+// and accumulates in fp32, one instruction per 16 x 16 block and 32 dims.
+// Lane l supplies A[l % 16][8 (l / 16) + e] and B[8 (l / 16) + e][l % 16],
+// e = 0..7, and receives D[4 (l / 16) + r][l % 16] (layout checked with an
+// in-bounds probe).  The factor 2c is applied in fp32 after the product, never
+// to the bf16 inputs.
+//
+// Shifted streaming as in lse_d3.hip: row i streams against
+// M_i = c (||x_i||^2 - f_i), carried in the accumulator input as
+// -M_i / (2c) = -(||x_i||^2 - f_i) / 2, so one fma with the column bias gives
+// s_ij - M_i = 2c D_ij + beta_j.  A row block whose sum leaves [2^-64, 2^100]
+// is flagged and recomputed by the vector kernel in a second launch.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+constexpr int kGroups = 4;
+constexpr float kSumLo = 5.421010862e-20f;  // 2^-64
+constexpr float kSumHi = 1.2676506e30f;     // 2^100
+
+__device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t *p)
+{
+    const uint4 v = *reinterpret_cast<const uint4 *>(p);
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+template <int DK>
+__global__ __launch_bounds__(kWaves *kWave) void lseFm_kernel(
+    const uint16_t *__restrict__ qx_, float *__restrict__ qbias, float *__restrict__ qpot,
+    const float *__restrict__ ql2w, const float *__restrict__ qsq, int *__restrict__ redo_out,
+    const uint16_t *__restrict__ ky_, const float *__restrict__ kbias, int nq, int nq_pad,
+    int nk, int nk_pad, float two_c, double eps_ln2, double c_next)
+{
+    constexpr int d = 32 * DK;
+    __shared__ float2 red[kWaves][kWave];
+    const int b = blockIdx.z;
+    const int lane = lane_id();
+    const int w = wave_id_uniform();
+    const int row0 = blockIdx.x * kWave;
+    const int kq = lane >> 4;
+    const int c16 = lane & 15;
+
+    bf16x8 A[kGroups][DK];
+    f32x4 Cn[kGroups], S[kGroups];
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) {
+        const int ra = row0 + 16 * g + c16;      // row whose operand this lane supplies
+        const int rc = min(ra, nq - 1);
+#pragma unroll
+        for (int kb = 0; kb < DK; ++kb) {
+            bf16x8 v = load_bf16x8(qx_ + ((size_t)b * nq + rc) * d + 32 * kb + 8 * kq);
+            if (ra >= nq)
+                v = bf16x8{};
+            A[g][kb] = v;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int rr = row0 + 16 * g + 4 * kq + r;   // row whose results this lane holds
+            float sh = 0.f;
+            if (rr < nq) {
+                const size_t k = (size_t)b * nq + rr;
+                sh = -0.5f * (qsq[k] - qpot[k]);
+            }
+            Cn[g][r] = sh;
+            S[g][r] = 0.f;
+        }
+    }
+    const uint16_t *ky = ky_ + (size_t)b * nk * d;
+    const float *kb_ = kbias + (size_t)b * nk_pad;
+    const int n_tiles = nk_pad / kKeys;
+    auto key_ptr = [&](int t) {
+        const int j = min(t * kKeys + c16, nk - 1);    // padding keys carry bias -1e30
+        return ky + (size_t)j * d + 8 * kq;
+    };
+    int t = w;
+    const int last = n_tiles - 1;
+    bf16x8 B0[DK], B1[DK];
+    float b0 = kb_[min(t, last) * kKeys + c16], b1 = kb_[min(t + kWaves, last) * kKeys + c16];
+#pragma unroll
+    for (int kb = 0; kb < DK; ++kb) {
+        B0[kb] = load_bf16x8(key_ptr(min(t, last)) + 32 * kb);
+        B1[kb] = load_bf16x8(key_ptr(min(t + kWaves, last)) + 32 * kb);
+    }
+    for (; t < n_tiles; t += kWaves) {
+        const int t2 = min(t + 2 * kWaves, last);
+        bf16x8 B2[DK];
+#pragma unroll
+        for (int kb = 0; kb < DK; ++kb)
+            B2[kb] = load_bf16x8(key_ptr(t2) + 32 * kb);
+        const float b2 = kb_[t2 * kKeys + c16];
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g) {
+            f32x4 D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][0], B0[0], Cn[g], 0, 0, 0);
+#pragma unroll
+            for (int kb = 1; kb < DK; ++kb)
+                D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][kb], B0[kb], D, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                S[g][r] += ex2(fmaf(two_c, D[r], b0));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kb = 0; kb < DK; ++kb) {
+            B0[kb] = B1[kb];
+            B1[kb] = B2[kb];
+        }
+        b0 = b1;
+        b1 = b2;
+    }
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float Sr = S[g][r];
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1)
+                Sr += __shfl_xor(Sr, off, kWave);
+            if (c16 == 0)
+                red[w][16 * g + 4 * kq + r] = make_float2(Cn[g][r], Sr);
+        }
+    __syncthreads();
+    if (w != 0)
+        return;
+    float Ssum = 0.f;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v)
+        Ssum += red[v][lane].y;
+    const int row = row0 + lane;
+    const bool bad = row < nq && !(Ssum >= kSumLo && Ssum <= kSumHi);
+    // wave 0 alone decides for the block; the other waves have left
+    const int flag = __builtin_amdgcn_readfirstlane(__ballot(bad) != 0 ? 1 : 0);
+    if (lane == 0)
+        redo_out[b * gridDim.x + blockIdx.x] = flag;
+    if (flag || row >= nq)
+        return;
+    const size_t k = (size_t)b * nq + row;
+    const double sq = (double)qsq[k];
+    // effective shift: s - M = 2c (x.y + Cn) + beta, so M = -2c Cn
+    const double M = -2.0 * (0.5 * (double)two_c) * (double)red[0][lane].x;
+    const double lse2 = M + (double)lg2(Ssum);
+    const float f = (float)(sq - lse2 * eps_ln2);
+    qpot[k] = f;
+    qbias[(size_t)b * nq_pad + row] = bias_of(c_next, f, (float)sq, ql2w[k]);
+}
+
+// Transport cost for the bf16 matrix-core path, streamed like a half-
+// iteration: with both biases of the final passes (c (f - ||x||^2) + log2 a and
+// c (g - ||y||^2) + log2 b at the last eps),
+//     log2 P_ij = 2c x_i . y_j + beta_j + alpha_i,
+//     C_ij = ||x_i||^2 + ||y_j||^2 - 2 x_i . y_j,
+// and each row's sum_j P_ij C_ij goes to row_out (fp64) for a fixed-order
+// per-pair reduction.  No n x m quantity is stored.
+template <int DK>
+__global__ __launch_bounds__(kWaves *kWave) void costFm_kernel(
+    const uint16_t *__restrict__ X, const float *__restrict__ xbias, const float *__restrict__ xsq,
+    const uint16_t *__restrict__ Y, const float *__restrict__ ybias, const float *__restrict__ ysq,
+    int n, int n_pad, int m, int m_pad, float two_c, double *__restrict__ row_out)
+{
+    constexpr int d = 32 * DK;
+    __shared__ float red[kWaves][kWave];
+    const int b = blockIdx.z;
+    const int lane = lane_id();
+    const int w = wave_id_uniform();
+    const int row0 = blockIdx.x * kWave;
+    const int kq = lane >> 4;
+    const int c16 = lane & 15;
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+
+    bf16x8 A[kGroups][DK];
+    f32x4 al[kGroups], sqx[kGroups], acc[kGroups];
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) {
+        const int ra = row0 + 16 * g + c16;
+        const int rc = min(ra, n - 1);
+#pragma unroll
+        for (int kb = 0; kb < DK; ++kb) {
+            bf16x8 v = load_bf16x8(X + ((size_t)b * n + rc) * d + 32 * kb + 8 * kq);
+            if (ra >= n)
+                v = bf16x8{};
+            A[g][kb] = v;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int rr = row0 + 16 * g + 4 * kq + r;
+            al[g][r] = rr < n ? xbias[(size_t)b * n_pad + rr] : kNeg;
+            sqx[g][r] = rr < n ? xsq[(size_t)b * n + rr] : 0.f;
+            acc[g][r] = 0.f;
+        }
+    }
+    const uint16_t *yb = Y + (size_t)b * m * d;
+    const int n_tiles = m_pad / kKeys;
+    for (int t = w; t < n_tiles; t += kWaves) {
+        const int jr = t * kKeys + c16;
+        const int j = min(jr, m - 1);
+        bf16x8 Bv[DK];
+#pragma unroll
+        for (int kb = 0; kb < DK; ++kb)
+            Bv[kb] = load_bf16x8(yb + (size_t)j * d + 32 * kb + 8 * kq);
+        const float be = jr < m ? ybias[(size_t)b * m_pad + jr] : kNeg;
+        const float sy = ysq[(size_t)b * m + j];
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g) {
+            f32x4 D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][0], Bv[0], zero, 0, 0, 0);
+#pragma unroll
+            for (int kb = 1; kb < DK; ++kb)
+                D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][kb], Bv[kb], D, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float P = ex2(fmaf(two_c, D[r], be) + al[g][r]);
+                const float C = fmaf(-2.f, D[r], sqx[g][r] + sy);
+                acc[g][r] = fmaf(P, C, acc[g][r]);
+            }
+        }
+    }
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float v = acc[g][r];
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1)
+                v += __shfl_xor(v, off, kWave);
+            if (c16 == 0)
+                red[w][16 * g + 4 * kq + r] = v;
+        }
+    __syncthreads();
+    if (w != 0)
+        return;
+    double tot = 0.0;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v)
+        tot += (double)red[v][lane];
+    const int row = row0 + lane;
+    if (row < n)
+        row_out[(size_t)b * n + row] = tot;
+}
+
 template <typename T>
 __global__ void lseF_finalize(const T *__restrict__ qx_, int d, float *__restrict__ qbias,
                               float *__restrict__ qpot, const float *__restrict__ ql2w,
@@ -242,14 +486,41 @@ void launch_lseF_t(SideF q, SideF k, int d, int B, float two_c, double eps_ln2,
     dim3 grid(q.n_pad / kWave, splits, B);
     hipLaunchKernelGGL((lseF_kernel<T, DP>), grid, dim3(kWaves * kWave), 0, st,
                        (const T *)q.pts, q.bias, q.pot, (const float *)q.l2w,
-                       (const T *)k.pts, (const float *)k.bias, splits > 1 ? part : nullptr, d,
-                       q.n, q.n_pad, k.n, k.n_pad, tps, two_c, eps_ln2, c_next);
+                       (const T *)k.pts, (const float *)k.bias, splits > 1 ? part : nullptr,
+                       (const int *)nullptr, d, q.n, q.n_pad, k.n, k.n_pad, tps, two_c, eps_ln2,
+                       c_next);
     if (splits > 1) {
         dim3 g2(ceil_div(q.n, 256), B);
         hipLaunchKernelGGL(lseF_finalize<T>, g2, dim3(256), 0, st, (const T *)q.pts, d, q.bias,
                            q.pot, (const float *)q.l2w, (const float2 *)part, B, q.n, q.n_pad,
                            splits, eps_ln2, c_next);
     }
+}
+
+template <int DK>
+void launch_lseFm_t(SideF q, SideF k, int B, float two_c, double eps_ln2, double c_next,
+                    hipStream_t st)
+{
+    dim3 grid(q.n_pad / kWave, 1, B);
+    hipLaunchKernelGGL((lseFm_kernel<DK>), grid, dim3(kWaves * kWave), 0, st,
+                       (const uint16_t *)q.pts, q.bias, q.pot, (const float *)q.l2w,
+                       (const float *)q.sq, q.redo, (const uint16_t *)k.pts,
+                       (const float *)k.bias, q.n, q.n_pad, k.n, k.n_pad, two_c, eps_ln2, c_next);
+    // fallback for flagged row blocks: the vector kernel, same block shape
+    constexpr int DP = 32 * DK;
+    hipLaunchKernelGGL((lseF_kernel<uint16_t, DP>), grid, dim3(kWaves * kWave), 0, st,
+                       (const uint16_t *)q.pts, q.bias, q.pot, (const float *)q.l2w,
+                       (const uint16_t *)k.pts, (const float *)k.bias, (float2 *)nullptr,
+                       (const int *)q.redo, DP, q.n, q.n_pad, k.n, k.n_pad,
+                       k.n_pad / kKeys, two_c, eps_ln2, c_next);
+}
+
+// Matrix cores for bf16 with whole 32-dim blocks, 16-byte aligned rows (the
+// operands are read as 16-byte vectors) and at least 128 row blocks.
+bool use_matrix_cores(SideF q, SideF k, int dtype, int d, int B)
+{
+    const bool aligned = ((uintptr_t)q.pts % 16 == 0) && ((uintptr_t)k.pts % 16 == 0);
+    return dtype == 1 && d % 32 == 0 && d <= 128 && aligned && (long)B * (q.n_pad / kWave) >= 128;
 }
 
 template <typename T>
@@ -269,6 +540,31 @@ void dispatch(SideF q, SideF k, int d, int B, float two_c, double ne, double cn,
 
 bool lseF_supported(int dtype, int d) { return (dtype == 0 || dtype == 1) && padded_dim(d) > 0; }
 
+bool lseF_matrix_cores(SideF q, SideF k, int dtype, int d, int B)
+{
+    return use_matrix_cores(q, k, dtype, d, B) && use_matrix_cores(k, q, dtype, d, B);
+}
+
+hipError_t launch_costFm(SideF x, SideF y, int d, int B, float eps, double *row_part,
+                         hipStream_t st)
+{
+    const float two_c = 2.0f * scale_of(eps);
+    dim3 grid(x.n_pad / kWave, 1, B);
+#define SK_COSTFM(DK)                                                                      \
+    hipLaunchKernelGGL((costFm_kernel<DK>), grid, dim3(kWaves * kWave), 0, st,                 \
+                       (const uint16_t *)x.pts, (const float *)x.bias, (const float *)x.sq,     \
+                       (const uint16_t *)y.pts, (const float *)y.bias, (const float *)y.sq, x.n, \
+                       x.n_pad, y.n, y.n_pad, two_c, row_part)
+    switch (d / 32) {
+    case 1: SK_COSTFM(1); break;
+    case 2: SK_COSTFM(2); break;
+    case 3: SK_COSTFM(3); break;
+    default: SK_COSTFM(4); break;
+    }
+#undef SK_COSTFM
+    return hipGetLastError();
+}
+
 size_t lseF_partial_floats2(int B, int nq_pad, int nk_pad)
 {
     const int s = lseF_splits(B, nq_pad, nk_pad);
@@ -282,10 +578,10 @@ hipError_t launch_packF(const void *X, int dtype, int d, const float *w, int war
     if (dtype == 1)
         hipLaunchKernelGGL(packF_kernel<uint16_t>, grid, dim3(256), 0, st,
                            (const uint16_t *)X, d, w, warm, s.n, s.n_pad, s.bias, s.pot, s.l2w,
-                           c0);
+                           s.sq, c0);
     else
         hipLaunchKernelGGL(packF_kernel<float>, grid, dim3(256), 0, st, (const float *)X, d, w,
-                           warm, s.n, s.n_pad, s.bias, s.pot, s.l2w, c0);
+                           warm, s.n, s.n_pad, s.bias, s.pot, s.l2w, s.sq, c0);
     return hipGetLastError();
 }
 
@@ -295,7 +591,14 @@ hipError_t launch_lseF(SideF q, SideF k, int dtype, int d, int B, float eps, flo
     const float c = scale_of(eps);
     const double c_next = (double)scale_of(eps_next);
     const double eps_ln2 = 1.0 / (double)c;
-    if (dtype == 1)
+    if (use_matrix_cores(q, k, dtype, d, B)) {
+        switch (d / 32) {
+        case 1: launch_lseFm_t<1>(q, k, B, 2.0f * c, eps_ln2, c_next, st); break;
+        case 2: launch_lseFm_t<2>(q, k, B, 2.0f * c, eps_ln2, c_next, st); break;
+        case 3: launch_lseFm_t<3>(q, k, B, 2.0f * c, eps_ln2, c_next, st); break;
+        default: launch_lseFm_t<4>(q, k, B, 2.0f * c, eps_ln2, c_next, st); break;
+        }
+    } else if (dtype == 1)
         dispatch<uint16_t>(q, k, d, B, 2.0f * c, eps_ln2, c_next, part, st);
     else
         dispatch<float>(q, k, d, B, 2.0f * c, eps_ln2, c_next, part, st);

@@ -325,6 +325,13 @@ hipError_t launch_cost(const PlanArgs &p, double *row_part, float *cost, hipStre
     return hipGetLastError();
 }
 
+hipError_t launch_row_sums(const double *row_part, int B, int n, float *out, hipStream_t st)
+{
+    hipLaunchKernelGGL(pair_reduce<0>, dim3(B), dim3(256), 0, st, row_part, n, out,
+                       (double *)nullptr, 0.0);
+    return hipGetLastError();
+}
+
 hipError_t launch_plan_max(const PlanArgs &p, double *row_max, double *pair_thr,
                            double log_rel_thr, hipStream_t st)
 {

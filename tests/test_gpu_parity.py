@@ -122,6 +122,27 @@ def test_feature_potentials_match_oracle(dtype, d, n, m):
     check_potentials(c, [0.5, 0.1], [5, 10])
 
 
+@pytest.mark.parametrize("d,n,m", [(64, 8192, 1000), (32, 4100, 3000), (128, 8200, 700)])
+def test_feature_matrix_core_path_matches_oracle(d, n, m):
+    # bf16 with whole 32-dim blocks and >= 128 row blocks: the MFMA kernel
+    c = workloads.random_case(30 + d, 2, n, m, d, weights="dirichlet", dtype="bf16",
+                              spread=0.25)
+    check_potentials(c, [0.5, 0.05], [3, 4])
+
+
+def test_feature_matrix_core_fallback_on_stale_shift():
+    # warm start from potentials far off: every row block must take the fallback
+    c = workloads.random_case(35, 1, 8192, 900, 64, weights="uniform", dtype="bf16",
+                              spread=0.25)
+    f0 = np.full((1, 8192), 500.0, dtype=np.float32)
+    g0 = np.full((1, 900), -500.0, dtype=np.float32)
+    f, g, _ = run_gpu(c, [0.05], [2], f0=f0, g0=g0)
+    fo, go = oracle.potentials(c["X"], c["Y"], c["a"], c["b"], eps=np.float32([0.05]),
+                               iters=[2], f0=f0.astype(np.float64), g0=g0.astype(np.float64))
+    assert rel_inf(host(f), fo, 0.05) <= 1e-4
+    assert rel_inf(host(g), go, 0.05) <= 1e-4
+
+
 # ---------------------------------------------------- warm start, determinism
 def test_warm_start_split_matches_single_run():
     c = workloads.random_case(12, 2, 500, 400, 3, weights="dirichlet")
