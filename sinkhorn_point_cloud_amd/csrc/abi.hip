@@ -55,6 +55,7 @@ bool supported(int dtype, int d) { return path3(dtype, d) || lseF_supported(dtyp
 struct PotWs {
     // d = 3 path
     float4 *px = nullptr, *py = nullptr, *center = nullptr, *boxes = nullptr;
+    uint16_t *kxrec = nullptr, *kyrec = nullptr, *qxrec = nullptr, *qyrec = nullptr;
     // feature path
     float *xbias = nullptr, *ybias = nullptr, *xsq = nullptr, *ysq = nullptr;
     int *xredo = nullptr, *yredo = nullptr;
@@ -74,6 +75,10 @@ PotWs carve_potentials(Carve &c, int B, int n, int m, int d, int dtype)
         w.px = c.take<float4>((size_t)B * np);
         w.py = c.take<float4>((size_t)B * mp);
         w.center = c.take<float4>(B);
+        w.kxrec = c.take<uint16_t>((size_t)B * np * kRec);
+        w.kyrec = c.take<uint16_t>((size_t)B * mp * kRec);
+        w.qxrec = c.take<uint16_t>((size_t)B * np * kRec);
+        w.qyrec = c.take<uint16_t>((size_t)B * mp * kRec);
         w.boxes = c.take<float4>((size_t)2 * B * center3_parts(n, m));
         parts = std::max(lse3_partial_floats2(B, np, mp), lse3_partial_floats2(B, mp, np));
     } else {
@@ -236,7 +241,7 @@ int sinkhorn_potentials(const void *X, const void *Y, int dtype, const float *a,
     hipError_t e;
     const bool p3 = path3(dtype, d);
     // the caller's f and g are the state of the iteration
-    Side3 sx3{w.px, f, w.l2a, n, np}, sy3{w.py, g, w.l2b, m, mp};
+    Side3 sx3{w.px, f, w.l2a, w.kxrec, w.qxrec, n, np}, sy3{w.py, g, w.l2b, w.kyrec, w.qyrec, m, mp};
     SideF sxf{X, w.xbias, f, w.l2a, w.xsq, w.xredo, n, np};
     SideF syf{Y, w.ybias, g, w.l2b, w.ysq, w.yredo, m, mp};
     if (p3) {
@@ -254,6 +259,11 @@ int sinkhorn_potentials(const void *X, const void *Y, int dtype, const float *a,
             return hip_fail(e, "pack Y");
     }
     for (int s = 0; s < n_stages; ++s) {
+        if (p3 && mfma && iters[s] > 0) {
+            // query records carry 2c x, so they follow eps
+            if ((e = launch_qrec3(sx3, B, eps[s], st)) || (e = launch_qrec3(sy3, B, eps[s], st)))
+                return hip_fail(e, "query records");
+        }
         for (int it = 0; it < iters[s]; ++it) {
             // eps of the f-update that follows this g-update
             float eps_next = eps[s];

@@ -94,8 +94,14 @@ struct Side3 {
     float4 *pts;      // [B][n_pad] (x, y, z, bias for the opposite pass)
     float *pot;       // [B][n]     potential of this side (the state; in/out)
     float *l2w;       // [B][n]     log2 of the weights (kNeg for 0)
+    uint16_t *krec;   // [B][n_pad][32] bf16 key records (matrix-core path)
+    uint16_t *qrec;   // [B][n_pad][32] bf16 query records at the current eps
     int n, n_pad;
 };
+constexpr int kRec = 32;  // bf16 slots per record (one 16x16x32 MFMA k-range)
+
+// Query records of one side for the scale of eps (rebuilt when eps changes).
+hipError_t launch_qrec3(Side3 s, int B, float eps, hipStream_t st);
 
 // Per-pair center (bounding-box midpoint of both clouds) for the d = 3 path;
 // part holds center3_parts(n, m) * B partial boxes.

@@ -59,6 +59,95 @@ __device__ __forceinline__ float bias_of(double c, float pot, float sq, float l2
     return (float)fma(c, (double)pot - (double)sq, (double)l2w);
 }
 
+// ---- bf16 records for the matrix-core path --------------------------------
+// An fp32 value is the exact sum of three bf16 pieces (8 + 8 + 8 significant
+// bits, fp32's exponent range): v = v0 + v1 + v2.  Products of two bf16 pieces
+// are exact in the MFMA's fp32 accumulator, so
+//     q . y = sum_u sum_(a,b) q_u,a y_u,b     over (a,b) in kPairs
+// reproduces the fp32 dot product up to the dropped pieces of relative size
+// 2^-32 and the accumulator's fp32 rounding.  Record slots (one 16x16x32 MFMA
+// k-range): 6u + p holds piece kPairs[p] of coordinate u (query: q's piece a,
+// key: y's piece b); slots 20..22 hold the bias pieces (key) or 1 (query);
+// the rest are zero.
+__device__ __forceinline__ uint32_t bf16_bits(float v)   // round to nearest even
+{
+    const uint32_t u = __float_as_uint(v);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ float bf16_value(uint32_t h) { return __uint_as_float(h << 16); }
+
+__device__ __forceinline__ void split3(float v, uint32_t (&h)[3])
+{
+    h[0] = bf16_bits(v);
+    const float r1 = v - bf16_value(h[0]);
+    h[1] = bf16_bits(r1);
+    const float r2 = r1 - bf16_value(h[1]);
+    h[2] = bf16_bits(r2);
+}
+
+constexpr int kPairA[6] = {0, 0, 1, 0, 1, 2};   // query piece of pair p
+constexpr int kPairB[6] = {0, 1, 0, 2, 1, 0};   // key piece of pair p
+constexpr int kBiasSlot = 20;
+constexpr uint32_t kBf16One = 0x3F80u;
+
+__device__ __forceinline__ void store_record(uint16_t *rec, const uint32_t (&slot)[kRec])
+{
+    uint4 *dst = reinterpret_cast<uint4 *>(rec);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+        dst[c] = make_uint4(slot[8 * c] | slot[8 * c + 1] << 16, slot[8 * c + 2] | slot[8 * c + 3] << 16,
+                            slot[8 * c + 4] | slot[8 * c + 5] << 16, slot[8 * c + 6] | slot[8 * c + 7] << 16);
+}
+
+// bias pieces of a key record: one 8-byte store of slots 20..23
+__device__ __forceinline__ void store_key_bias(uint16_t *rec, float beta)
+{
+    uint32_t h[3];
+    split3(beta, h);
+    *reinterpret_cast<uint2 *>(rec + kBiasSlot) = make_uint2(h[0] | h[1] << 16, h[2]);
+}
+
+__device__ __forceinline__ void store_key_record(uint16_t *rec, float x0, float x1, float x2,
+                                                 float beta)
+{
+    uint32_t h[3][3], slot[kRec];
+    split3(x0, h[0]);
+    split3(x1, h[1]);
+    split3(x2, h[2]);
+#pragma unroll
+    for (int k = 0; k < kRec; ++k)
+        slot[k] = 0;
+#pragma unroll
+    for (int u = 0; u < 3; ++u)
+#pragma unroll
+        for (int p = 0; p < 6; ++p)
+            slot[6 * u + p] = h[u][kPairB[p]];
+    uint32_t hb[3];
+    split3(beta, hb);
+    slot[kBiasSlot] = hb[0];
+    slot[kBiasSlot + 1] = hb[1];
+    slot[kBiasSlot + 2] = hb[2];
+    store_record(rec, slot);
+}
+
+__device__ __forceinline__ void store_query_record(uint16_t *rec, float q0, float q1, float q2)
+{
+    uint32_t h[3][3], slot[kRec];
+    split3(q0, h[0]);
+    split3(q1, h[1]);
+    split3(q2, h[2]);
+#pragma unroll
+    for (int k = 0; k < kRec; ++k)
+        slot[k] = 0;
+#pragma unroll
+    for (int u = 0; u < 3; ++u)
+#pragma unroll
+        for (int p = 0; p < 6; ++p)
+            slot[6 * u + p] = h[u][kPairA[p]];
+    slot[kBiasSlot] = slot[kBiasSlot + 1] = slot[kBiasSlot + 2] = kBf16One;
+    store_record(rec, slot);
+}
+
 // Center of each pair: midpoint of the bounding box of both clouds.  The
 // squared-Euclidean cost is unchanged by a common translation, so the packed
 // points are stored relative to it; this keeps ||x||^2 and 2 x . y, whose fp32
@@ -144,7 +233,7 @@ __global__ __launch_bounds__(256) void center3_kernel(const float4 *__restrict__
 __global__ void pack3_kernel(const float *__restrict__ X, const float *__restrict__ w, int warm,
                              int n, int n_pad, const float4 *__restrict__ center,
                              float4 *__restrict__ pts, float *__restrict__ pot,
-                             float *__restrict__ l2w, double c0)
+                             float *__restrict__ l2w, uint16_t *__restrict__ krec, double c0)
 {
     const int b = blockIdx.y;
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -169,27 +258,43 @@ __global__ void pack3_kernel(const float *__restrict__ X, const float *__restric
         out = make_float4(x0, x1, x2, lw == kNeg ? kNeg : bias_of(c0, pot[k], sq3(x0, x1, x2), lw));
     }
     pts[(size_t)b * n_pad + i] = out;
+    store_key_record(krec + ((size_t)b * n_pad + i) * kRec, out.x, out.y, out.z, out.w);
+}
+
+// Query records at the scale c of the current eps: q = 2c (x, y, z).
+__global__ void qrec3_kernel(const float4 *__restrict__ pts, int n_pad, float two_c,
+                             uint16_t *__restrict__ qrec)
+{
+    const int b = blockIdx.y;
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n_pad)
+        return;
+    const size_t k = (size_t)b * n_pad + i;
+    const float4 p = pts[k];
+    store_query_record(qrec + k * kRec, two_c * p.x, two_c * p.y, two_c * p.z);
 }
 
 // Row result: true potential from the (M, S) state, and the bias of this row
 // for the other pass.
-__device__ __forceinline__ void finish_row(float4 *qpts, float *qpot, const float *ql2w,
-                                           size_t pt, size_t k, float4 p, float M, float S,
-                                           double eps_ln2, double c_next)
+__device__ __forceinline__ void finish_row(float4 *qpts, uint16_t *qkrec, float *qpot,
+                                           const float *ql2w, size_t pt, size_t k, float4 p,
+                                           float M, float S, double eps_ln2, double c_next)
 {
     const float sq = sq3(p.x, p.y, p.z);
     const double lse2 = (double)M + (double)lg2(S);
     const float f = (float)((double)sq - lse2 * eps_ln2);
     qpot[k] = f;
     const float lw = ql2w[k];
-    qpts[pt].w = lw == kNeg ? kNeg : bias_of(c_next, f, sq, lw);
+    const float beta = lw == kNeg ? kNeg : bias_of(c_next, f, sq, lw);
+    qpts[pt].w = beta;
+    store_key_bias(qkrec + pt * kRec, beta);
 }
 
 // part == nullptr: single split, finalise in place.
 __global__ __launch_bounds__(kWaves *kWave) void lse3_kernel(
-    float4 *__restrict__ qpts, const float4 *__restrict__ kpts, float *__restrict__ qpot,
-    const float *__restrict__ ql2w, float2 *__restrict__ part, int nq, int nq_pad,
-    int nk_pad, int tiles_per_split, float two_c, double eps_ln2, double c_next)
+    float4 *__restrict__ qpts, uint16_t *__restrict__ qkrec, const float4 *__restrict__ kpts,
+    float *__restrict__ qpot, const float *__restrict__ ql2w, float2 *__restrict__ part, int nq,
+    int nq_pad, int nk_pad, int tiles_per_split, float two_c, double eps_ln2, double c_next)
 {
     __shared__ float2 red[kWaves][kWave];
     const int b = blockIdx.z;
@@ -258,8 +363,8 @@ __global__ __launch_bounds__(kWaves *kWave) void lse3_kernel(
         return;
     }
     if (row < nq)
-        finish_row(qpts, qpot, ql2w, (size_t)b * nq_pad + row, (size_t)b * nq + row, p, M, S,
-                   eps_ln2, c_next);
+        finish_row(qpts, qkrec, qpot, ql2w, (size_t)b * nq_pad + row, (size_t)b * nq + row, p, M,
+                   S, eps_ln2, c_next);
 }
 
 // ---------------------------------------------------------------------------
@@ -279,13 +384,21 @@ __global__ __launch_bounds__(kWaves *kWave) void lse3_kernel(
 // yet, and the first key it sees is re-evaluated with a zero accumulator so
 // that M starts at an exact score.
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kGroups = 4;        // 16-row groups per wave
 constexpr float kEmpty = 1.0e29f; // accumulator input above this: no key seen yet
 
-__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c)
+__device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t *p)
 {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(p));
+}
+
+// D = A B + C over one 32-slot record range: the augmented score from the
+// bf16 pieces (exact products, fp32 accumulation)
+__device__ __forceinline__ f32x4 mfma4(bf16x8 a, bf16x8 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 // Shifted pass: every row streams against a fixed shift, the log-sum-exp of
@@ -300,9 +413,10 @@ constexpr float kSumLo = 5.421010862e-20f;  // 2^-64
 constexpr float kSumHi = 1.2676506e30f;     // 2^100
 
 __global__ __launch_bounds__(kWaves *kWave) void lse3m_kernel(
-    float4 *__restrict__ qpts, const float *__restrict__ kflat, float *__restrict__ qpot,
-    const float *__restrict__ ql2w, float2 *__restrict__ part, int nq, int nq_pad,
-    int nk_pad, int tiles_per_split, float two_c, double eps_ln2, double c_next)
+    float4 *__restrict__ qpts, uint16_t *__restrict__ qkrec, const uint16_t *__restrict__ qrec,
+    const uint16_t *__restrict__ krec, float *__restrict__ qpot, const float *__restrict__ ql2w,
+    float2 *__restrict__ part, int nq, int nq_pad, int nk_pad, int tiles_per_split, float two_c,
+    double eps_ln2, double c_next)
 {
     __shared__ float2 red[kWaves][kWave];
     __shared__ int redo;
@@ -315,14 +429,12 @@ __global__ __launch_bounds__(kWaves *kWave) void lse3m_kernel(
     const int c16 = lane & 15;     // operand row (A) or column (B) within a 16-block
 
     const float4 *qrow = qpts + (size_t)b * nq_pad + row0;
-    float A[kGroups];
-    {
-        const float *qf = reinterpret_cast<const float *>(qrow);
+    const int lane_off = c16 * kRec + 8 * kq;   // this lane's 8 slots of a record
+    bf16x8 A[kGroups];
 #pragma unroll
-        for (int g = 0; g < kGroups; ++g)
-            A[g] = kq == 3 ? 1.0f : two_c * qf[(16 * g + c16) * 4 + kq];
-    }
-    const float *kb = kflat + (size_t)b * nk_pad * 4;
+    for (int g = 0; g < kGroups; ++g)
+        A[g] = load_bf16x8(qrec + ((size_t)b * nq_pad + row0 + 16 * g) * kRec + lane_off);
+    const uint16_t *kb = krec + (size_t)b * nk_pad * kRec;
     const int n_tiles = nk_pad / kTile;
     const int t_begin = split * tiles_per_split;
     const int t_end = min(t_begin + tiles_per_split, n_tiles);
@@ -345,10 +457,11 @@ __global__ __launch_bounds__(kWaves *kWave) void lse3m_kernel(
         // the pair); the scheduling barrier keeps each load ahead of its use
         int t = t_begin + w;
         const int last = max(t_end - 1, 0);
-        float B0 = kb[(min(t, last) * kTile + c16) * 4 + kq];
-        float B1 = kb[(min(t + kWaves, last) * kTile + c16) * 4 + kq];
+        bf16x8 B0 = load_bf16x8(kb + (size_t)min(t, last) * kTile * kRec + lane_off);
+        bf16x8 B1 = load_bf16x8(kb + (size_t)min(t + kWaves, last) * kTile * kRec + lane_off);
         for (; t < t_end; t += kWaves) {
-            const float B2 = kb[(min(t + 2 * kWaves, last) * kTile + c16) * 4 + kq];
+            const bf16x8 B2 =
+                load_bf16x8(kb + (size_t)min(t + 2 * kWaves, last) * kTile * kRec + lane_off);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int g = 0; g < kGroups; ++g) {
@@ -389,7 +502,7 @@ __global__ __launch_bounds__(kWaves *kWave) void lse3m_kernel(
         if (!redo) {
             const int row = row0 + lane;
             if (w == 0 && row < nq)
-                finish_row(qpts, qpot, ql2w, (size_t)b * nq_pad + row, (size_t)b * nq + row,
+                finish_row(qpts, qkrec, qpot, ql2w, (size_t)b * nq_pad + row, (size_t)b * nq + row,
                            qpts[(size_t)b * nq_pad + row], M, Ssum, eps_ln2, c_next);
             return;
         }
@@ -405,10 +518,10 @@ __global__ __launch_bounds__(kWaves *kWave) void lse3m_kernel(
     int t = t_begin + w;
     // the key operand of the next tile is loaded one tile ahead; the clamped
     // index keeps that load inside the pair's keys on the last tile
-    float Bv = kb[(min(t, n_tiles - 1) * kTile + c16) * 4 + kq];
+    bf16x8 Bv = load_bf16x8(kb + (size_t)min(t, n_tiles - 1) * kTile * kRec + lane_off);
     for (; t < t_end; t += kWaves) {
         const int tn = min(t + kWaves, t_end - 1);
-        const float Bn = kb[(tn * kTile + c16) * 4 + kq];
+        const bf16x8 Bn = load_bf16x8(kb + (size_t)tn * kTile * kRec + lane_off);
         f32x4 D[kGroups];
 #pragma unroll
         for (int g = 0; g < kGroups; ++g)
@@ -500,11 +613,12 @@ __global__ __launch_bounds__(kWaves *kWave) void lse3m_kernel(
         return;
     }
     if (row < nq)
-        finish_row(qpts, qpot, ql2w, (size_t)b * nq_pad + row, (size_t)b * nq + row,
+        finish_row(qpts, qkrec, qpot, ql2w, (size_t)b * nq_pad + row, (size_t)b * nq + row,
                    qpts[(size_t)b * nq_pad + row], M, Sf, eps_ln2, c_next);
 }
 
-__global__ void lse3_finalize(float4 *__restrict__ qpts, float *__restrict__ qpot,
+__global__ void lse3_finalize(float4 *__restrict__ qpts, uint16_t *__restrict__ qkrec,
+                              float *__restrict__ qpot,
                               const float *__restrict__ ql2w, const float2 *__restrict__ part,
                               int B, int nq, int nq_pad, int splits, double eps_ln2,
                               double c_next)
@@ -520,7 +634,8 @@ __global__ void lse3_finalize(float4 *__restrict__ qpts, float *__restrict__ qpo
         lse_merge(M, S, o.x, o.y);
     }
     const size_t pt = (size_t)b * nq_pad + row;
-    finish_row(qpts, qpot, ql2w, pt, (size_t)b * nq + row, qpts[pt], M, S, eps_ln2, c_next);
+    finish_row(qpts, qkrec, qpot, ql2w, pt, (size_t)b * nq + row, qpts[pt], M, S, eps_ln2,
+               c_next);
 }
 
 // Column splits so that a launch has about 4 work-groups per CU.
@@ -560,7 +675,15 @@ hipError_t launch_pack3(const float *X, const float *w, int warm, int B, Side3 s
 {
     dim3 grid(ceil_div(s.n_pad, 256), B);
     hipLaunchKernelGGL(pack3_kernel, grid, dim3(256), 0, st, X, w, warm, s.n, s.n_pad, center,
-                       s.pts, s.pot, s.l2w, c0);
+                       s.pts, s.pot, s.l2w, s.krec, c0);
+    return hipGetLastError();
+}
+
+hipError_t launch_qrec3(Side3 s, int B, float eps, hipStream_t st)
+{
+    dim3 grid(ceil_div(s.n_pad, 256), B);
+    hipLaunchKernelGGL(qrec3_kernel, grid, dim3(256), 0, st, (const float4 *)s.pts, s.n_pad,
+                       2.0f * scale_of(eps), s.qrec);
     return hipGetLastError();
 }
 
@@ -576,18 +699,18 @@ hipError_t launch_lse3(Side3 q, Side3 k, int B, float eps, float eps_next, float
     const int tiles_per_split = ceil_div(tiles, splits);
     dim3 grid(q.n_pad / kWave, splits, B);
     if (mfma)
-        hipLaunchKernelGGL(lse3m_kernel, grid, dim3(kWaves * kWave), 0, st, q.pts,
-                           (const float *)k.pts, q.pot, (const float *)q.l2w,
-                           splits > 1 ? part : nullptr, q.n, q.n_pad, k.n_pad, tiles_per_split,
-                           2.0f * c, eps_ln2, c_next);
+        hipLaunchKernelGGL(lse3m_kernel, grid, dim3(kWaves * kWave), 0, st, q.pts, q.krec,
+                           (const uint16_t *)q.qrec, (const uint16_t *)k.krec, q.pot,
+                           (const float *)q.l2w, splits > 1 ? part : nullptr, q.n, q.n_pad,
+                           k.n_pad, tiles_per_split, 2.0f * c, eps_ln2, c_next);
     else
-        hipLaunchKernelGGL(lse3_kernel, grid, dim3(kWaves * kWave), 0, st, q.pts,
+        hipLaunchKernelGGL(lse3_kernel, grid, dim3(kWaves * kWave), 0, st, q.pts, q.krec,
                            (const float4 *)k.pts, q.pot, (const float *)q.l2w,
                            splits > 1 ? part : nullptr, q.n, q.n_pad, k.n_pad, tiles_per_split,
                            2.0f * c, eps_ln2, c_next);
     if (splits > 1) {
         dim3 g2(ceil_div(q.n, 256), B);
-        hipLaunchKernelGGL(lse3_finalize, g2, dim3(256), 0, st, q.pts, q.pot,
+        hipLaunchKernelGGL(lse3_finalize, g2, dim3(256), 0, st, q.pts, q.krec, q.pot,
                            (const float *)q.l2w, (const float2 *)part, B, q.n, q.n_pad, splits,
                            eps_ln2, c_next);
     }
