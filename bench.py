@@ -3,9 +3,10 @@
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gmm-64k] [--no-cpu-baseline]
 
 One step is the whole workload's hot path on inputs already resident in HBM:
-pack, every annealed Sinkhorn half-iteration and the transport-cost pass
+pack, every (annealed) Sinkhorn half-iteration, then the transport-cost pass
 (gmm-64k: 65536 x 65536 points, d = 3, eps 1.0 -> 0.01 over 10 stages of 20
-iterations).  Prints ONE JSON line with
+iterations; pair-1k; feat-50k) or, for the sparse-plan workloads (sphere-2k,
+blobs-1k), the thresholded COO plan and the loss and dL/dX computed from it.  Prints ONE JSON line with
   value      B*n*m*iters / step time   (cost-entry updates per second)
   roofline   the half-iteration kernel: entry evaluations per launch / its
              average launch time (events on the library's stream: the full step
@@ -132,9 +133,32 @@ def main():
     ws = torch.empty(sk.workspace_bytes(sk.SK_OP_POTENTIALS, B, n, m, d, dt), dtype=torch.uint8,
                      device=dev)
 
-    def step(it=iters, with_cost=True):
+    sparse = w["threshold"] is not None
+    with_cost_default = not sparse
+    coo = loss_out = None
+    if sparse:
+        # size the plan once (untimed); the timed steps reuse the buffers
+        sk.potentials(X, Y, a, b, eps=eps, iters=iters, out=(f, g, None), cost=False,
+                      workspace=ws)
+        r0, _, _, _ = sk.plan_coo(X, Y, a, b, f, g, eps[-1], w["threshold"])
+        cap = int(r0.numel() * 1.05) + 1024
+        coo = (torch.empty(cap, dtype=torch.int32, device=dev),
+               torch.empty(cap, dtype=torch.int32, device=dev),
+               torch.empty(cap, dtype=torch.float32, device=dev),
+               torch.empty(B + 1, dtype=torch.int64, device=dev))
+        coo_ws = torch.empty(sk.workspace_bytes(sk.SK_OP_PLAN_COO, B, n, m, d, dt),
+                             dtype=torch.uint8, device=dev)
+        lg_ws = torch.empty(sk.workspace_bytes(sk.SK_OP_LOSS_GRAD, B, n, m, d, dt),
+                            dtype=torch.uint8, device=dev)
+        loss_out = (torch.empty(B, device=dev), torch.empty(B, n, d, device=dev))
+
+    def step(it=iters, with_cost=with_cost_default):
         sk.potentials(X, Y, a, b, eps=eps, iters=it, out=(f, g, cost if with_cost else None),
                       cost=with_cost, workspace=ws, valu_scores=args.valu_scores)
+        if sparse:
+            rows, cols, vals, offs = sk.plan_coo(X, Y, a, b, f, g, eps[-1], w["threshold"],
+                                                 workspace=coo_ws, out=coo)
+            sk.loss_grad(X, Y, rows, cols, vals, offs, workspace=lg_ws, out=loss_out)
 
     def timed(fn, reps):
         torch.cuda.synchronize()
@@ -152,12 +176,13 @@ def main():
     t0 = time.perf_counter()
     t_step = timed(step, args.steps)
     wall = time.perf_counter() - t0
-    assert torch.isfinite(f).all() and torch.isfinite(g).all() and torch.isfinite(cost).all()
+    assert torch.isfinite(f).all() and torch.isfinite(g).all()
+    assert sparse or torch.isfinite(cost).all()
 
     # the half-iteration kernel's launch time: the same step with every stage's
     # iteration count halved (pack and cost pass unchanged), differenced
     fewer = [max(1, i // 2) if i else 0 for i in iters]
-    t_fewer = timed(lambda: step(fewer, True), max(3, args.steps))
+    t_fewer = timed(lambda: step(fewer), max(3, args.steps))
     launches = 2 * (total_iters - sum(fewer))
     t_launch = (t_step - t_fewer) / launches
     t_iterations = t_launch * 2 * total_iters
@@ -182,7 +207,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": w["name"], "B": B, "n": n, "m": m, "d": d,
                    "eps": f"{eps[0]:g}->{eps[-1]:g} over {len(eps)} stage(s)",
-                   "iters": total_iters, "outputs": "potentials f, g and transport cost"},
+                   "iters": total_iters,
+                   "outputs": ("potentials, COO plan at %g x max P per pair, loss and dL/dX"
+                               % w["threshold"]) if sparse
+                   else "potentials f, g and transport cost"},
         "roofline": {"bound": bound, "achieved": achieved / 1e12, "peak": peak / 1e12,
                      "unit": "Teval/s", "frac": achieved / peak,
                      "traffic": measured_traffic("lse3m_kernel", w["name"],
@@ -198,7 +226,8 @@ def main():
                      "serial_exp_fp32_peak": serial / 1e12,
                      "frac_of_serial_peak": achieved / serial},
         "phases_ms": {"step": t_step * 1e3, "iterations": t_iterations * 1e3,
-                      "pack_and_cost_pass": (t_step - t_iterations) * 1e3},
+                      ("pack_plan_and_loss" if sparse else "pack_and_cost_pass"):
+                      (t_step - t_iterations) * 1e3},
         "wall_s_timed": wall,
     }
     if args.copy_calibration:

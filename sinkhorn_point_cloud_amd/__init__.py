@@ -171,11 +171,13 @@ def potentials(X, Y, a=None, b=None, eps=(0.05,), iters=(100,), f0=None, g0=None
 
 
 def plan_coo(X, Y, a, b, f, g, eps: float, rel_threshold: float = 1e-8, capacity=None,
-             workspace=None):
+             workspace=None, out=None):
     """Thresholded sparse plan: (rows int32, cols int32, vals float32, pair_offsets int64[B+1]).
 
     With capacity=None the plan is counted first, then emitted into buffers of
-    exactly the right size (two calls of the C entry point)."""
+    exactly the right size (two calls of the C entry point).  ``out`` = (rows,
+    cols, vals, pair_offsets) reuses buffers; its length is the capacity, and
+    a plan that does not fit raises SinkhornError(SK_ERR_CAPACITY)."""
     lib = load_library()
     X, Y, dt = _points(X, Y)
     B, n, d = X.shape
@@ -185,8 +187,16 @@ def plan_coo(X, Y, a, b, f, g, eps: float, rel_threshold: float = 1e-8, capacity
     f = f.reshape(B, n).contiguous().float()
     g = g.reshape(B, m).contiguous().float()
     ws = _workspace(SK_OP_PLAN_COO, B, n, m, d, dt, dev, workspace)
-    offs = torch.empty(B + 1, dtype=torch.int64, device=dev)
     nnz = ctypes.c_int64(0)
+    if out is not None:
+        rows, cols, vals, offs = out
+        cap = rows.numel()
+    else:
+        offs = torch.empty(B + 1, dtype=torch.int64, device=dev)
+        cap = 0 if capacity is None else int(capacity)
+        rows = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+        cols = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+        vals = torch.empty(max(cap, 1), dtype=torch.float32, device=dev)
 
     def call(cap, rows, cols, vals):
         return lib.sinkhorn_plan_coo(_ptr(X), _ptr(Y), dt, _ptr(a), _ptr(b), B, n, m, d,
@@ -194,12 +204,8 @@ def plan_coo(X, Y, a, b, f, g, eps: float, rel_threshold: float = 1e-8, capacity
                                      _ptr(rows), _ptr(cols), _ptr(vals), _ptr(offs),
                                      ctypes.byref(nnz), _ptr(ws), ws.numel(), _stream())
 
-    cap = 0 if capacity is None else int(capacity)
-    rows = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
-    cols = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
-    vals = torch.empty(max(cap, 1), dtype=torch.float32, device=dev)
     rc = call(cap, rows, cols, vals)
-    if rc == SK_ERR_CAPACITY and capacity is None:
+    if rc == SK_ERR_CAPACITY and capacity is None and out is None:
         cap = int(nnz.value)
         rows = torch.empty(cap, dtype=torch.int32, device=dev)
         cols = torch.empty(cap, dtype=torch.int32, device=dev)
@@ -210,8 +216,10 @@ def plan_coo(X, Y, a, b, f, g, eps: float, rel_threshold: float = 1e-8, capacity
     return rows[:k], cols[:k], vals[:k], offs
 
 
-def loss_grad(X, Y, rows, cols, vals, pair_offsets, grad: bool = True, workspace=None):
-    """Loss [B] and dL/dX [B,n,d] (float32) on the stored support of a row-sorted COO plan."""
+def loss_grad(X, Y, rows, cols, vals, pair_offsets, grad: bool = True, workspace=None,
+              out=None):
+    """Loss [B] and dL/dX [B,n,d] (float32) on the stored support of a row-sorted COO plan.
+    ``out`` = (loss, dX) reuses buffers."""
     lib = load_library()
     X, Y, dt = _points(X, Y)
     B, n, d = X.shape
@@ -226,8 +234,11 @@ def loss_grad(X, Y, rows, cols, vals, pair_offsets, grad: bool = True, workspace
         rows = torch.zeros(1, dtype=torch.int32, device=dev)
         cols = torch.zeros(1, dtype=torch.int32, device=dev)
         vals = torch.zeros(1, dtype=torch.float32, device=dev)
-    loss = torch.empty(B, dtype=torch.float32, device=dev)
-    dX = torch.empty(B, n, d, dtype=torch.float32, device=dev) if grad else None
+    if out is not None:
+        loss, dX = out
+    else:
+        loss = torch.empty(B, dtype=torch.float32, device=dev)
+        dX = torch.empty(B, n, d, dtype=torch.float32, device=dev) if grad else None
     ws = _workspace(SK_OP_LOSS_GRAD, B, n, m, d, dt, dev, workspace)
     rc = lib.sinkhorn_loss_grad(_ptr(X), _ptr(Y), dt, B, n, m, d, _ptr(rows), _ptr(cols),
                                 _ptr(vals), _ptr(offs), _ptr(loss), _ptr(dX), _ptr(ws),

@@ -30,8 +30,8 @@
 // and S rescaled.  The result is the exact LSE up to fp32 rounding, because
 // LSE(z) = M + log2 sum 2^(z - M) for any M and no term exceeds 2^kLazy.
 //
-// A work-group = 4 waves on the same 64 rows, each streaming every 4th key
-// tile; the four (M, S) states merge through LDS.  When a batch has too few
+// A work-group = 8 waves on the same 64 rows, each streaming every 8th key
+// tile; the eight (M, S) states merge through LDS.  When a batch has too few
 // rows to fill the chip the key range is also split across work-groups and a
 // second small kernel merges the partial states.
 #include "common.h"
@@ -40,7 +40,7 @@ namespace sk {
 namespace {
 
 constexpr int kTile = 16;      // keys per tile (64 SGPRs)
-constexpr int kWaves = 4;      // waves per work-group, sharing rows
+constexpr int kWaves = 8;      // waves per work-group, sharing rows
 constexpr float kLazy = 32.0f; // terms may reach 2^kLazy before a rescale
 
 __device__ __forceinline__ float score(float qx, float qy, float qz, float4 k, float base)
@@ -453,26 +453,41 @@ __global__ __launch_bounds__(kWaves *kWave) void lse3m_kernel(
                 Cn[g][r] = -(c * (sq3(p.x, p.y, p.z) - f));
                 S[g][r] = 0.f;
             }
-        // key operands are loaded two tiles ahead (clamped indices stay inside
-        // the pair); the scheduling barrier keeps each load ahead of its use
-        int t = t_begin + w;
+        // Key operands are loaded two tiles ahead (clamped indices stay inside
+        // the pair); three register sets take turns, so no operand is copied,
+        // and the scheduling barriers keep each load ahead of its use.
         const int last = max(t_end - 1, 0);
-        bf16x8 B0 = load_bf16x8(kb + (size_t)min(t, last) * kTile * kRec + lane_off);
-        bf16x8 B1 = load_bf16x8(kb + (size_t)min(t + kWaves, last) * kTile * kRec + lane_off);
-        for (; t < t_end; t += kWaves) {
-            const bf16x8 B2 =
-                load_bf16x8(kb + (size_t)min(t + 2 * kWaves, last) * kTile * kRec + lane_off);
-            __builtin_amdgcn_sched_barrier(0);
+        auto key = [&](int t) {
+            return load_bf16x8(kb + (size_t)min(t, last) * kTile * kRec + lane_off);
+        };
+        auto tile = [&](const bf16x8 &Bt) {
 #pragma unroll
             for (int g = 0; g < kGroups; ++g) {
-                const f32x4 D = mfma4(A[g], B0, Cn[g]);
+                const f32x4 D = mfma4(A[g], Bt, Cn[g]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     S[g][r] += ex2(D[r]);
             }
+        };
+        int t = t_begin + w;
+        bf16x8 Ra = key(t), Rb = key(t + kWaves), Rc;
+        for (; t < t_end; t += 3 * kWaves) {
+            Rc = key(t + 2 * kWaves);
             __builtin_amdgcn_sched_barrier(0);
-            B0 = B1;
-            B1 = B2;
+            tile(Ra);
+            __builtin_amdgcn_sched_barrier(0);
+            if (t + kWaves >= t_end)
+                break;
+            Ra = key(t + 3 * kWaves);
+            __builtin_amdgcn_sched_barrier(0);
+            tile(Rb);
+            __builtin_amdgcn_sched_barrier(0);
+            if (t + 2 * kWaves >= t_end)
+                break;
+            Rb = key(t + 4 * kWaves);
+            __builtin_amdgcn_sched_barrier(0);
+            tile(Rc);
+            __builtin_amdgcn_sched_barrier(0);
         }
         // every partial of a row has the same shift: the merge is a sum
 #pragma unroll
