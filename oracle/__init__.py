@@ -39,6 +39,9 @@ PINS = {
     "plan_stats": "dense numpy enumeration; strong duality at convergence",
     "plan_coo": "dense numpy enumeration on small shapes",
     "loss_grad": "finite differences of the dual (envelope theorem); dense sums",
+    "dense_grad": "finite differences of the dual (envelope theorem); assignment limit of"
+                  " the projection at small eps; product-plan limit at large eps; row mass"
+                  " after an f-update; translation",
 }
 
 
@@ -75,6 +78,9 @@ def _load():
         lib.oracle_plan_coo.restype = i64
         lib.oracle_loss_grad.argtypes = [P, P, i32, i32, i32, i32, P, P, P, P, P, P]
         lib.oracle_loss_grad.restype = i32
+        lib.oracle_dense_grad.argtypes = [P, P, P, P, P, P, f64, i32, i32, i32, i32, P, i64,
+                                          P, P, P]
+        lib.oracle_dense_grad.restype = None
         _lib = lib
     return _lib
 
@@ -196,3 +202,30 @@ def loss_grad(X, Y, rows, cols, vals, pair_offsets):
     if rc != 0:
         raise ValueError("oracle_loss_grad: index out of range")
     return loss, dX
+
+
+def dense_grad(X, Y, a, b, f, g, eps, sel=None):
+    """Dense transport application at eps (X side): (r, dX, T).
+
+    r[k] = sum_j P_ij, dX[k] = sum_j 2 P_ij (x_i - y_j), T[k] = sum_j P_ij y_j / r[k]
+    for the rows listed in ``sel`` (flat indices p * n + i; None: all rows, shaped
+    [B,n] / [B,n,d]).  For the Y side pass (Y, X, b, a, g, f)."""
+    lib = _load()
+    X, Y, B, n, m, d = _shapes(X, Y)
+    a, b = _weights(a, B, n), _weights(b, B, m)
+    f, g = _d(f).reshape(B, n), _d(g).reshape(B, m)
+    if sel is None:
+        k = B * n
+        selp, cnt = None, 0
+    else:
+        s = np.ascontiguousarray(np.asarray(sel, dtype=np.int64))
+        assert s.min() >= 0 and s.max() < B * n
+        k, selp, cnt = s.size, _p(s), s.size
+    r = np.empty(k)
+    dX = np.empty((k, d))
+    T = np.empty((k, d))
+    lib.oracle_dense_grad(_p(X), _p(Y), _p(a), _p(b), _p(f), _p(g), float(eps), B, n, m, d,
+                          selp, cnt, _p(r), _p(dX), _p(T))
+    if sel is None:
+        return r.reshape(B, n), dX.reshape(B, n, d), T.reshape(B, n, d)
+    return r, dX, T

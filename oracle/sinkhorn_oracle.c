@@ -460,3 +460,73 @@ int oracle_loss_grad(const double *X, const double *Y, int B, int n, int m, int 
     }
     return 0;
 }
+
+/*
+ * Dense transport application at eps [FS Methodologie, "Toepassing van
+ * Transportmatrix": the barycentric projection and the gradient are weighted
+ * averages over the plan, streamed like the update].  For each selected row i
+ * of the X side of pair p, with P from the given potentials:
+ *   r_i  = sum_j P_ij                              (row mass)
+ *   dX_i = sum_j 2 P_ij (x_i - y_j)                (gradient of <P,C> in x_i,
+ *                                                   P held fixed)
+ *   T_i  = sum_j P_ij y_j / r_i                    (barycentric projection;
+ *                                                   0 where r_i = 0)
+ * Every sum is compensated and runs over j in order.  sel lists flat row
+ * indices p * n + i (NULL: all B * n rows in order); outputs are indexed by
+ * position in that list: r[k], dX[k][d], T[k][d] (any of them may be NULL).
+ * The Y side is the same call with the roles of (X, a, f) and (Y, b, g)
+ * exchanged, since log P is symmetric in them.
+ */
+void oracle_dense_grad(const double *X, const double *Y, const double *a, const double *b,
+                       const double *f, const double *g, double eps, int B, int n, int m, int d,
+                       const int64_t *sel, int64_t nsel, double *r, double *dX, double *T)
+{
+    const int64_t count = sel ? nsel : (int64_t)B * n;
+#pragma omp parallel
+    {
+        double *lb = (double *)malloc(sizeof(double) * (size_t)m);
+        acc_t *G = (acc_t *)malloc(sizeof(acc_t) * (size_t)d);
+        acc_t *V = (acc_t *)malloc(sizeof(acc_t) * (size_t)d);
+        int cur = -1;
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t k = 0; k < count; ++k) {
+            const int64_t flat = sel ? sel[k] : k;
+            const int p = (int)(flat / n), i = (int)(flat % n);
+            if (p != cur) {
+                log_weights(b + (size_t)p * m, m, lb);
+                cur = p;
+            }
+            const double *x = X + ((size_t)p * n + i) * d;
+            const double *Yp = Y + (size_t)p * m * d;
+            const double ai = a[(size_t)p * n + i];
+            const double lai = ai > 0.0 ? log(ai) : -INFINITY;
+            const double fi = f[(size_t)p * n + i];
+            acc_t mass = {0, 0};
+            for (int c = 0; c < d; ++c) {
+                G[c].s = G[c].c = 0.0;
+                V[c].s = V[c].c = 0.0;
+            }
+            for (int j = 0; j < m; ++j) {
+                const double *y = Yp + (size_t)j * d;
+                const double P = exp(log_plan(x, y, d, fi, g[(size_t)p * m + j], lai, lb[j], eps));
+                acc_add(&mass, P);
+                for (int c = 0; c < d; ++c) {
+                    acc_add(&G[c], 2.0 * P * (x[c] - y[c]));
+                    acc_add(&V[c], P * y[c]);
+                }
+            }
+            const double rm = acc_get(&mass);
+            if (r)
+                r[k] = rm;
+            for (int c = 0; c < d; ++c) {
+                if (dX)
+                    dX[(size_t)k * d + c] = acc_get(&G[c]);
+                if (T)
+                    T[(size_t)k * d + c] = rm > 0.0 ? acc_get(&V[c]) / rm : 0.0;
+            }
+        }
+        free(lb);
+        free(G);
+        free(V);
+    }
+}

@@ -66,6 +66,39 @@ __device__ __forceinline__ void lse_merge(float &M, float &S, float M2, float S2
     M = Mn;
 }
 
+// Reductions over each row of 16 lanes with DPP lane moves (no LDS traffic).
+// The four moves pair lanes i^1, i^2 (quad permutes), then 7-i within each
+// half row and 15-i within the row; after the four steps every lane of a row
+// holds the row's result.  All 64 lanes must be active.
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // row_half_mirror
+constexpr int kDppMirror = 0x140;     // row_mirror
+
+template <int Ctrl>
+__device__ __forceinline__ float dpp_move(float v)
+{
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), Ctrl, 0xF, 0xF, true));
+}
+
+__device__ __forceinline__ float row16_sum(float v)
+{
+    v += dpp_move<kDppXor1>(v);
+    v += dpp_move<kDppXor2>(v);
+    v += dpp_move<kDppHalfMirror>(v);
+    v += dpp_move<kDppMirror>(v);
+    return v;
+}
+
+__device__ __forceinline__ void row16_merge(float &M, float &S)
+{
+    lse_merge(M, S, dpp_move<kDppXor1>(M), dpp_move<kDppXor1>(S));
+    lse_merge(M, S, dpp_move<kDppXor2>(M), dpp_move<kDppXor2>(S));
+    lse_merge(M, S, dpp_move<kDppHalfMirror>(M), dpp_move<kDppHalfMirror>(S));
+    lse_merge(M, S, dpp_move<kDppMirror>(M), dpp_move<kDppMirror>(S));
+}
+
 __device__ __forceinline__ float bf16_to_float(uint16_t h)
 {
     return __uint_as_float(static_cast<uint32_t>(h) << 16);

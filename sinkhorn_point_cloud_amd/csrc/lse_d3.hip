@@ -205,10 +205,7 @@ __global__ __launch_bounds__(256) void center3_parts_kernel(const float *__restr
     }
 }
 
-// Center of each pair: midpoint of the bounding box of both clouds.  The
-// squared-Euclidean cost is unchanged by a common translation, so the packed
-// points are stored relative to it; this keeps ||x||^2 and 2 x . y, whose fp32
-// rounding the expanded score carries, as small as the clouds allow.
+// Merge of the partial boxes of each pair into its center.
 __global__ __launch_bounds__(256) void center3_kernel(const float4 *__restrict__ part, int parts,
                                                      float4 *__restrict__ center)
 {
@@ -368,21 +365,20 @@ __global__ __launch_bounds__(kWaves *kWave) void lse3_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Matrix-core variant.  The augmented score is a K = 4 contraction,
-//     s_ij - M = (2c x_i, 2c y_i, 2c z_i, 1) . (y_j, beta_j) + (-M),
-// Propositie 1's Q K^T plus its rank-one bias, so one v_mfma_f32_16x16x4_f32
-// per 16 x 16 block produces s - M with M riding in the accumulator input.
-// The vector ALUs are left with the exponential, the accumulation and a
-// per-tile check of the lazy maximum.
+// Matrix-core variant.  Score and bias are one contraction over the 32-slot
+// records: s_ij - M = qrec_i . krec_j + (-M), the bf16 pieces of 2c x_i against
+// those of y_j plus 1 against the pieces of beta_j.  One
+// v_mfma_f32_16x16x32_bf16 per 16 x 16 block produces s - M, with -M riding in
+// the accumulator input; the vector ALUs are left with the exponential and the
+// accumulation.
 //
-// Operand layout of v_mfma_f32_16x16x4_f32 (wave64): lane l supplies
-// A[l % 16][l / 16] and B[l / 16][l % 16]; it receives D[4 (l / 16) + r][l % 16]
-// in register r.  A wave covers 64 query rows as 4 groups of 16; per key tile
-// of 16 columns it issues 4 MFMAs.  Each (lane, group, register) keeps its own
-// (M, S) over the columns l % 16 + 16 t; the 16 lanes of a row merge at the end.
-// The accumulator input holds -M; +1e30 marks a state that has seen no key
-// yet, and the first key it sees is re-evaluated with a zero accumulator so
-// that M starts at an exact score.
+// Operand layout of v_mfma_f32_16x16x32_bf16 (wave64): lane l supplies
+// A[l % 16][8 (l / 16) + e] and B[8 (l / 16) + e][l % 16] for e = 0..7 and
+// receives D[4 (l / 16) + r][l % 16] in register r.  A wave covers 64 query
+// rows as 4 groups of 16; per key tile of 16 columns it issues 4 MFMAs.  Each
+// (lane, group, register) keeps its own (M, S) over the columns l % 16 + 16 t;
+// the 16 lanes of a row merge at the end with DPP moves, then the W waves of
+// the work-group (each streaming every W-th tile) merge through LDS.
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
@@ -407,18 +403,21 @@ __device__ __forceinline__ f32x4 mfma4(bf16x8 a, bf16x8 b, f32x4 c)
 // accumulation only.  The merged sum of each row is checked at the end: if any
 // row of the work-group left [2^-64, 2^100] (the shift was stale, e.g. on the
 // first pass or after a large change of eps), the whole group streams its
-// keys again with the lazy-maximum scheme below.  Either way the result is the
-// exact log-sum-exp to fp32 rounding.
+// keys again with the lazy-maximum scheme: the accumulator input holds -M,
+// +1e30 marks a state that has seen no key yet, and the first key it sees is
+// re-evaluated with a zero accumulator so that M starts at an exact score.
+// Either way the result is the exact log-sum-exp to fp32 rounding.
 constexpr float kSumLo = 5.421010862e-20f;  // 2^-64
 constexpr float kSumHi = 1.2676506e30f;     // 2^100
 
-__global__ __launch_bounds__(kWaves *kWave) void lse3m_kernel(
+template <int W>
+__global__ __launch_bounds__(W *kWave) void lse3m_kernel(
     float4 *__restrict__ qpts, uint16_t *__restrict__ qkrec, const uint16_t *__restrict__ qrec,
     const uint16_t *__restrict__ krec, float *__restrict__ qpot, const float *__restrict__ ql2w,
     float2 *__restrict__ part, int nq, int nq_pad, int nk_pad, int tiles_per_split, float two_c,
     double eps_ln2, double c_next)
 {
-    __shared__ float2 red[kWaves][kWave];
+    __shared__ float2 red[W][kWave];
     __shared__ int redo;
     const int b = blockIdx.z;
     const int split = blockIdx.y;
@@ -453,12 +452,17 @@ __global__ __launch_bounds__(kWaves *kWave) void lse3m_kernel(
                 Cn[g][r] = -(c * (sq3(p.x, p.y, p.z) - f));
                 S[g][r] = 0.f;
             }
-        // Key operands are loaded two tiles ahead (clamped indices stay inside
-        // the pair); three register sets take turns, so no operand is copied,
-        // and the scheduling barriers keep each load ahead of its use.
-        const int last = max(t_end - 1, 0);
-        auto key = [&](int t) {
-            return load_bf16x8(kb + (size_t)min(t, last) * kTile * kRec + lane_off);
+        // This wave takes tiles t_begin + w + k W, k = 0 .. cnt-1: the first
+        // cnt % 3 one by one, the rest in groups of three with no branch inside a
+        // group, so every key operand is loaded two tiles ahead of its use (the
+        // scheduling barriers keep each load in place; indices are clamped to the
+        // wave's last tile so that loads past the end stay inside the pair).
+        // Three register sets take turns, so no operand is copied.
+        const int first = t_begin + w;
+        const int cnt = first < t_end ? (t_end - first + W - 1) / W : 0;
+        const int last = first + (cnt > 0 ? cnt - 1 : 0) * W;
+        auto key = [&](int k) {
+            return load_bf16x8(kb + (size_t)min(first + k * W, last) * kTile * kRec + lane_off);
         };
         auto tile = [&](const bf16x8 &Bt) {
 #pragma unroll
@@ -469,35 +473,32 @@ __global__ __launch_bounds__(kWaves *kWave) void lse3m_kernel(
                     S[g][r] += ex2(D[r]);
             }
         };
-        int t = t_begin + w;
-        bf16x8 Ra = key(t), Rb = key(t + kWaves), Rc;
-        for (; t < t_end; t += 3 * kWaves) {
-            Rc = key(t + 2 * kWaves);
-            __builtin_amdgcn_sched_barrier(0);
-            tile(Ra);
-            __builtin_amdgcn_sched_barrier(0);
-            if (t + kWaves >= t_end)
-                break;
-            Ra = key(t + 3 * kWaves);
-            __builtin_amdgcn_sched_barrier(0);
-            tile(Rb);
-            __builtin_amdgcn_sched_barrier(0);
-            if (t + 2 * kWaves >= t_end)
-                break;
-            Rb = key(t + 4 * kWaves);
-            __builtin_amdgcn_sched_barrier(0);
-            tile(Rc);
-            __builtin_amdgcn_sched_barrier(0);
+        int k = 0;
+        for (; k < cnt % 3; ++k)
+            tile(key(k));
+        if (k < cnt) {
+            bf16x8 Ra = key(k), Rb = key(k + 1), Rc;
+            for (; k < cnt; k += 3) {
+                Rc = key(k + 2);
+                __builtin_amdgcn_sched_barrier(0);
+                tile(Ra);
+                __builtin_amdgcn_sched_barrier(0);
+                Ra = key(k + 3);
+                __builtin_amdgcn_sched_barrier(0);
+                tile(Rb);
+                __builtin_amdgcn_sched_barrier(0);
+                Rb = key(k + 4);
+                __builtin_amdgcn_sched_barrier(0);
+                tile(Rc);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
         // every partial of a row has the same shift: the merge is a sum
 #pragma unroll
         for (int g = 0; g < kGroups; ++g)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                float Sr = S[g][r];
-#pragma unroll
-                for (int off = 1; off < 16; off <<= 1)
-                    Sr += __shfl_xor(Sr, off, kWave);
+                const float Sr = row16_sum(S[g][r]);
                 if (c16 == 0)
                     red[w][16 * g + 4 * kq + r] = make_float2(-Cn[g][r], Sr);
             }
@@ -508,7 +509,7 @@ __global__ __launch_bounds__(kWaves *kWave) void lse3m_kernel(
         const float M = red[0][lane].x;
         if (w == 0) {
 #pragma unroll
-            for (int v = 0; v < kWaves; ++v)
+            for (int v = 0; v < W; ++v)
                 Ssum += red[v][lane].y;
             if (row0 + lane < nq && !(Ssum >= kSumLo && Ssum <= kSumHi))
                 redo = 1;   // benign race: every writer stores 1 (padding rows never do)
@@ -534,8 +535,8 @@ __global__ __launch_bounds__(kWaves *kWave) void lse3m_kernel(
     // the key operand of the next tile is loaded one tile ahead; the clamped
     // index keeps that load inside the pair's keys on the last tile
     bf16x8 Bv = load_bf16x8(kb + (size_t)min(t, n_tiles - 1) * kTile * kRec + lane_off);
-    for (; t < t_end; t += kWaves) {
-        const int tn = min(t + kWaves, t_end - 1);
+    for (; t < t_end; t += W) {
+        const int tn = min(t + W, t_end - 1);
         const bf16x8 Bn = load_bf16x8(kb + (size_t)tn * kTile * kRec + lane_off);
         f32x4 D[kGroups];
 #pragma unroll
@@ -603,12 +604,7 @@ __global__ __launch_bounds__(kWaves *kWave) void lse3m_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             float M = -Cn[g][r], Sr = S[g][r];
-#pragma unroll
-            for (int off = 1; off < 16; off <<= 1) {
-                const float M2 = __shfl_xor(M, off, kWave);
-                const float S2 = __shfl_xor(Sr, off, kWave);
-                lse_merge(M, Sr, M2, S2);
-            }
+            row16_merge(M, Sr);
             if (c16 == 0)
                 red[w][16 * g + 4 * kq + r] = make_float2(M, Sr);
         }
@@ -618,7 +614,7 @@ __global__ __launch_bounds__(kWaves *kWave) void lse3m_kernel(
     float2 st = red[0][lane];
     float M = st.x, Sf = st.y;
 #pragma unroll
-    for (int v = 1; v < kWaves; ++v) {
+    for (int v = 1; v < W; ++v) {
         const float2 o = red[v][lane];
         lse_merge(M, Sf, o.x, o.y);
     }
@@ -665,6 +661,32 @@ int lse3_splits(int B, int nq_pad, int nk_pad)
     return splits < 1 ? 1 : splits;
 }
 
+
+// Waves per work-group of the matrix-core pass.  Every wave pays a fixed cost
+// (query operands, shift, merge) besides its key tiles.  Long rows (512 tiles
+// or more per split) take 8 waves; shorter rows take the fewest waves that
+// still give about 4096 waves per launch (4 per SIMD), which spreads that
+// fixed cost over the most tiles.  Every wave gets at least 2 tiles.
+int lse3m_waves(long groups, int tiles_per_split)
+{
+    int w = 8;
+    if (tiles_per_split < 512)
+        while (w > 1 && groups * (w / 2) >= 4096)
+            w /= 2;
+    while (w > 1 && tiles_per_split < 2 * w)
+        w /= 2;
+    return w;
+}
+
+template <int W>
+void launch_lse3m_w(dim3 grid, hipStream_t st, Side3 q, Side3 k, float2 *part, int tiles_per_split,
+                    float two_c, double eps_ln2, double c_next)
+{
+    hipLaunchKernelGGL(lse3m_kernel<W>, grid, dim3(W * kWave), 0, st, q.pts, q.krec,
+                       (const uint16_t *)q.qrec, (const uint16_t *)k.krec, q.pot,
+                       (const float *)q.l2w, part, q.n, q.n_pad, k.n_pad, tiles_per_split, two_c,
+                       eps_ln2, c_next);
+}
 }  // namespace
 
 size_t lse3_partial_floats2(int B, int nq_pad, int nk_pad)
@@ -713,12 +735,15 @@ hipError_t launch_lse3(Side3 q, Side3 k, int B, float eps, float eps_next, float
     const int tiles = k.n_pad / kTile;
     const int tiles_per_split = ceil_div(tiles, splits);
     dim3 grid(q.n_pad / kWave, splits, B);
-    if (mfma)
-        hipLaunchKernelGGL(lse3m_kernel, grid, dim3(kWaves * kWave), 0, st, q.pts, q.krec,
-                           (const uint16_t *)q.qrec, (const uint16_t *)k.krec, q.pot,
-                           (const float *)q.l2w, splits > 1 ? part : nullptr, q.n, q.n_pad,
-                           k.n_pad, tiles_per_split, 2.0f * c, eps_ln2, c_next);
-    else
+    if (mfma) {
+        float2 *p = splits > 1 ? part : nullptr;
+        switch (lse3m_waves((long)B * splits * (q.n_pad / kWave), tiles_per_split)) {
+        case 1: launch_lse3m_w<1>(grid, st, q, k, p, tiles_per_split, 2.0f * c, eps_ln2, c_next); break;
+        case 2: launch_lse3m_w<2>(grid, st, q, k, p, tiles_per_split, 2.0f * c, eps_ln2, c_next); break;
+        case 4: launch_lse3m_w<4>(grid, st, q, k, p, tiles_per_split, 2.0f * c, eps_ln2, c_next); break;
+        default: launch_lse3m_w<8>(grid, st, q, k, p, tiles_per_split, 2.0f * c, eps_ln2, c_next); break;
+        }
+    } else
         hipLaunchKernelGGL(lse3_kernel, grid, dim3(kWaves * kWave), 0, st, q.pts, q.krec,
                            (const float4 *)k.pts, q.pot, (const float *)q.l2w,
                            splits > 1 ? part : nullptr, q.n, q.n_pad, k.n_pad, tiles_per_split,

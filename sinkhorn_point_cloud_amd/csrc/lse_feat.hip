@@ -305,10 +305,7 @@ __global__ __launch_bounds__(kWaves *kWave) void lseFm_kernel(
     for (int g = 0; g < kGroups; ++g)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            float Sr = S[g][r];
-#pragma unroll
-            for (int off = 1; off < 16; off <<= 1)
-                Sr += __shfl_xor(Sr, off, kWave);
+            const float Sr = row16_sum(S[g][r]);
             if (c16 == 0)
                 red[w][16 * g + 4 * kq + r] = make_float2(Cn[g][r], Sr);
         }
@@ -410,10 +407,7 @@ __global__ __launch_bounds__(kWaves *kWave) void costFm_kernel(
     for (int g = 0; g < kGroups; ++g)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            float v = acc[g][r];
-#pragma unroll
-            for (int off = 1; off < 16; off <<= 1)
-                v += __shfl_xor(v, off, kWave);
+            const float v = row16_sum(acc[g][r]);
             if (c16 == 0)
                 red[w][16 * g + 4 * kq + r] = v;
         }

@@ -321,3 +321,95 @@ def test_loss_grad_any_order_and_truncated_support():
     # rows without stored entries get a zero gradient
     empty = np.setdiff1d(np.arange(20), rows)
     assert np.all(dX[0, empty] == 0.0)
+
+
+# ------------------------------------------- dense gradient and projection
+def test_dense_gradient_is_envelope_derivative_both_sides():
+    # at convergence d OT_eps / d x_i = sum_j 2 P_ij (x_i - y_j), and the same for y_j
+    X, Y, a, b = _case(23, 9, 11)
+    eps, iters = 0.1, 3000
+
+    def ot_value(Xv, Yv):
+        f, g = oracle.potentials(Xv, Yv, a, b, eps=[eps], iters=[iters])
+        return float(a @ f + b @ g)
+
+    f, g = _converge(X, Y, a, b, eps, iters)
+    r, dX, T = oracle.dense_grad(X, Y, a, b, f, g, eps)
+    rY, dY, TY = oracle.dense_grad(Y, X, b, a, g, f, eps)
+    h = 1e-5
+    for side, P0, ref in (("x", X, dX[0]), ("y", Y, dY[0])):
+        fd = np.zeros_like(P0)
+        for i in range(P0.shape[0]):
+            for k in range(3):
+                Pp, Pm = P0.copy(), P0.copy()
+                Pp[i, k] += h
+                Pm[i, k] -= h
+                args_p = (Pp, Y) if side == "x" else (X, Pp)
+                args_m = (Pm, Y) if side == "x" else (X, Pm)
+                fd[i, k] = (ot_value(*args_p) - ot_value(*args_m)) / (2 * h)
+        np.testing.assert_allclose(ref, fd, rtol=1e-6, atol=1e-8)
+    # at convergence the row masses are the weights on both sides
+    np.testing.assert_allclose(r[0], a, rtol=1e-9)
+    np.testing.assert_allclose(rY[0], b, rtol=1e-9)
+
+
+def test_dense_row_mass_is_exact_after_an_f_update():
+    # f from one half-update against any g makes every row sum of P equal a_i
+    X, Y, a, b = _case(29, 40, 23)
+    eps = 0.04
+    g = np.random.default_rng(5).normal(scale=0.1, size=23)
+    f = oracle.half_update(X, Y, g, b, eps)
+    r, _, _ = oracle.dense_grad(X, Y, a, b, f, g, eps)
+    np.testing.assert_allclose(r[0], a, rtol=1e-13)
+
+
+def test_barycentric_projection_approaches_assignment_at_small_eps():
+    n = 7
+    X, Y, a, b = _case(61, n, n, weights="uniform")
+    C = _cost_matrix(X, Y)
+    rows, sigma = linear_sum_assignment(C)
+    eps = 1e-3
+    sched = list(np.geomspace(1.0, eps, 12)) + [eps]
+    f, g = oracle.potentials(X, Y, a, b, eps=sched, iters=[500] * 12 + [100000])
+    r, dX, T = oracle.dense_grad(X, Y, a, b, f, g, eps)
+    np.testing.assert_allclose(T[0], Y[sigma], atol=1e-4)
+    np.testing.assert_allclose(dX[0], 2.0 / n * (X - Y[sigma]), atol=1e-4)
+
+
+def test_projection_at_large_eps_is_the_weighted_mean():
+    # P -> a b^T: T_i -> sum_j b_j y_j and dX_i -> 2 a_i (x_i - ybar), up to O(1/eps)
+    X, Y, a, b = _case(67, 30, 40)
+    eps = 1e4
+    f, g = _converge(X, Y, a, b, eps, 20)
+    r, dX, T = oracle.dense_grad(X, Y, a, b, f, g, eps)
+    ybar = b @ Y
+    np.testing.assert_allclose(T[0], np.broadcast_to(ybar, T[0].shape), atol=1e-3)
+    np.testing.assert_allclose(dX[0], 2 * a[:, None] * (X - ybar), atol=1e-3 * np.abs(dX).max())
+
+
+def test_dense_grad_translation_and_subset():
+    X, Y, a, b = _case(71, 25, 31)
+    eps = 0.05
+    f, g = oracle.potentials(X, Y, a, b, eps=[eps], iters=[15])
+    r, dX, T = oracle.dense_grad(X, Y, a, b, f, g, eps)
+    t = np.array([4.0, -1.0, 2.5])
+    r2, dX2, T2 = oracle.dense_grad(X + t, Y + t, a, b, f, g, eps)   # plan unchanged
+    np.testing.assert_allclose(r2, r, rtol=1e-12)
+    np.testing.assert_allclose(dX2, dX, rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(T2, T + t, rtol=1e-12, atol=1e-12)
+    sel = [24, 3, 3, 0]
+    r3, dX3, T3 = oracle.dense_grad(X, Y, a, b, f, g, eps, sel=sel)
+    np.testing.assert_array_equal(r3, r[0, sel])
+    np.testing.assert_array_equal(dX3, dX[0, sel])
+    np.testing.assert_array_equal(T3, T[0, sel])
+
+
+def test_dense_grad_matches_full_support_coo_gradient():
+    X, Y, a, b = _case(73, 14, 19)
+    eps = 0.03
+    f, g = oracle.potentials(X, Y, a, b, eps=[eps], iters=[9])
+    rows, cols, vals, offs = oracle.plan_coo(X, Y, a, b, f, g, eps, rel_thr=1e-300)
+    assert len(rows) == 14 * 19
+    loss, dXc = oracle.loss_grad(X, Y, rows, cols, vals, offs)
+    r, dX, T = oracle.dense_grad(X, Y, a, b, f, g, eps)
+    np.testing.assert_allclose(dX, dXc, rtol=1e-12, atol=1e-15)
