@@ -230,6 +230,21 @@ def main():
                       (t_step - t_iterations) * 1e3},
         "wall_s_timed": wall,
     }
+    if not sparse:
+        # dense gradient and barycentric projection of both clouds at the final eps
+        # (one streamed pass per side); reported beside the step, not inside it
+        dg_ws = torch.empty(sk.workspace_bytes(sk.SK_OP_DENSE_GRAD, B, n, m, d, dt),
+                            dtype=torch.uint8, device=dev)
+        dg_out = (torch.empty(B, n, d, device=dev), torch.empty(B, n, d, device=dev),
+                  torch.empty(B, m, d, device=dev), torch.empty(B, m, d, device=dev))
+
+        def dense_grad():
+            sk.dense_grad(X, Y, a, b, f, g, eps[-1], workspace=dg_ws, out=dg_out)
+
+        dense_grad()
+        t_dg = timed(dense_grad, 2)
+        assert all(bool(torch.isfinite(t).all()) for t in dg_out)
+        line["phases_ms"]["dense_grad_and_projection_both_sides"] = t_dg * 1e3
     if args.copy_calibration:
         src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)

@@ -64,7 +64,7 @@ enum {
 enum { SK_F32 = 0, SK_BF16 = 1 };
 
 /* Operation ids for sinkhorn_workspace_bytes(). */
-enum { SK_OP_POTENTIALS = 0, SK_OP_PLAN_COO = 1, SK_OP_LOSS_GRAD = 2 };
+enum { SK_OP_POTENTIALS = 0, SK_OP_PLAN_COO = 1, SK_OP_LOSS_GRAD = 2, SK_OP_DENSE_GRAD = 3 };
 
 /* Flags of sinkhorn_potentials(). */
 #define SK_WARM_START 1u  /* f and g hold starting potentials (resume) */
@@ -155,6 +155,30 @@ int sinkhorn_loss_grad(const void *X, const void *Y, int dtype,
                        const int32_t *rows, const int32_t *cols, const float *vals,
                        const int64_t *pair_offsets, float *loss, float *dX,
                        void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Dense transport application: gradient and barycentric projection
+ * [FS Methodologie, "Toepassing van Transportmatrix": both are weighted
+ * averages over the plan, computed by streaming like the update, without
+ * storing the plan].
+ *
+ * With the plan of potentials f, g at eps (the P of sinkhorn_potentials'
+ * cost), for every point x_i of X and y_j of Y of each pair:
+ *     dX[p][i] = sum_j 2 P_ij (x_i - y_j)          (gradient of sum P C in x_i,
+ *     dY[p][j] = sum_i 2 P_ij (y_j - x_i)           P held fixed)
+ *     TX[p][i] = sum_j P_ij y_j / sum_j P_ij       (barycentric projection)
+ *     TY[p][j] = sum_i P_ij x_i / sum_i P_ij
+ * dX, TX are [B][n][d] and dY, TY [B][m][d], fp32; each may be NULL, and a side
+ * whose two outputs are both NULL is skipped.  A point whose row (column) of P
+ * has zero mass gets a zero gradient and a zero projection.  log P is
+ * evaluated in fp64 from the fp32 inputs, as for the sparse plan.
+ */
+int sinkhorn_dense_grad(const void *X, const void *Y, int dtype,
+                        const float *a, const float *b,
+                        int B, int n, int m, int d, float eps,
+                        const float *f, const float *g,
+                        float *dX, float *TX, float *dY, float *TY,
+                        void *ws, size_t ws_bytes, void *stream);
 
 /* Static text for a return code. */
 const char *sinkhorn_status_string(int status);

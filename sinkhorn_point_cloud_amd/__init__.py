@@ -27,12 +27,13 @@ _LIB_PATH = os.path.join(_HERE, "libsinkhorn_amd.so")
 SK_OK, SK_ERR_INVALID_ARG, SK_ERR_UNSUPPORTED, SK_ERR_WORKSPACE, SK_ERR_CAPACITY, SK_ERR_HIP = \
     range(6)
 SK_F32, SK_BF16 = 0, 1
-SK_OP_POTENTIALS, SK_OP_PLAN_COO, SK_OP_LOSS_GRAD = 0, 1, 2
+SK_OP_POTENTIALS, SK_OP_PLAN_COO, SK_OP_LOSS_GRAD, SK_OP_DENSE_GRAD = 0, 1, 2, 3
 SK_WARM_START = 1
 SK_VALU_SCORES = 2
 
 EXPORTS = ("sinkhorn_workspace_bytes", "sinkhorn_potentials", "sinkhorn_plan_coo",
-           "sinkhorn_loss_grad", "sinkhorn_status_string", "sinkhorn_last_error")
+           "sinkhorn_loss_grad", "sinkhorn_dense_grad", "sinkhorn_status_string",
+           "sinkhorn_last_error")
 
 
 class SinkhornError(RuntimeError):
@@ -68,6 +69,8 @@ def load_library():
     lib.sinkhorn_plan_coo.restype = I
     lib.sinkhorn_loss_grad.argtypes = [P, P, I, I, I, I, I, P, P, P, P, P, P, P, Z, P]
     lib.sinkhorn_loss_grad.restype = I
+    lib.sinkhorn_dense_grad.argtypes = [P, P, I, P, P, I, I, I, I, F, P, P, P, P, P, P, P, Z, P]
+    lib.sinkhorn_dense_grad.restype = I
     lib.sinkhorn_status_string.argtypes = [I]
     lib.sinkhorn_status_string.restype = ctypes.c_char_p
     lib.sinkhorn_last_error.argtypes = []
@@ -245,3 +248,32 @@ def loss_grad(X, Y, rows, cols, vals, pair_offsets, grad: bool = True, workspace
                                 ws.numel(), _stream())
     _check(rc)
     return loss, dX
+
+
+def dense_grad(X, Y, a, b, f, g, eps: float, sides: str = "xy", workspace=None, out=None):
+    """Dense transport application at eps: (dX, TX, dY, TY), float32.
+
+    dX[p,i] = sum_j 2 P_ij (x_i - y_j), TX[p,i] = sum_j P_ij y_j / sum_j P_ij, and
+    the same for the Y side; ``sides`` picks "x", "y" or "xy" (the others are
+    None).  ``out`` = (dX, TX, dY, TY) reuses buffers (entries may be None)."""
+    lib = load_library()
+    X, Y, dt = _points(X, Y)
+    B, n, d = X.shape
+    m = Y.shape[1]
+    dev = X.device
+    a, b = _weights(a, B, n, dev), _weights(b, B, m, dev)
+    f = f.reshape(B, n).contiguous().float()
+    g = g.reshape(B, m).contiguous().float()
+    if out is not None:
+        dX, TX, dY, TY = out
+    else:
+        def new(k, on):
+            return torch.empty(B, k, d, dtype=torch.float32, device=dev) if on else None
+        dX, TX = new(n, "x" in sides), new(n, "x" in sides)
+        dY, TY = new(m, "y" in sides), new(m, "y" in sides)
+    ws = _workspace(SK_OP_DENSE_GRAD, B, n, m, d, dt, dev, workspace)
+    rc = lib.sinkhorn_dense_grad(_ptr(X), _ptr(Y), dt, _ptr(a), _ptr(b), B, n, m, d, float(eps),
+                                 _ptr(f), _ptr(g), _ptr(dX), _ptr(TX), _ptr(dY), _ptr(TY),
+                                 _ptr(ws), ws.numel(), _stream())
+    _check(rc)
+    return dX, TX, dY, TY

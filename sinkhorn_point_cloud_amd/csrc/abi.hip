@@ -133,6 +133,18 @@ LossWs carve_loss(Carve &c, int B, int n)
     return w;
 }
 
+struct GradWs {
+    double *la, *lb;
+};
+
+GradWs carve_grad(Carve &c, int B, int n, int m)
+{
+    GradWs w;
+    w.la = c.take<double>((size_t)B * n);
+    w.lb = c.take<double>((size_t)B * m);
+    return w;
+}
+
 size_t ws_size(int op, int B, int n, int m, int d, int dtype)
 {
     Carve c{nullptr};
@@ -140,8 +152,10 @@ size_t ws_size(int op, int B, int n, int m, int d, int dtype)
         carve_potentials(c, B, n, m, d, dtype);
     else if (op == SK_OP_PLAN_COO)
         carve_coo(c, B, n, m);
-    else
+    else if (op == SK_OP_LOSS_GRAD)
         carve_loss(c, B, n);
+    else
+        carve_grad(c, B, n, m);
     return c.off + 256;
 }
 
@@ -175,7 +189,7 @@ extern "C" {
 
 size_t sinkhorn_workspace_bytes(int op, int B, int n, int m, int d, int dtype)
 {
-    if (op < SK_OP_POTENTIALS || op > SK_OP_LOSS_GRAD || !shape_ok(B, n, m, d) ||
+    if (op < SK_OP_POTENTIALS || op > SK_OP_DENSE_GRAD || !shape_ok(B, n, m, d) ||
         (dtype != SK_F32 && dtype != SK_BF16) || !supported(dtype, d))
         return 0;
     return ws_size(op, B, n, m, d, dtype);
@@ -375,6 +389,43 @@ int sinkhorn_loss_grad(const void *X, const void *Y, int dtype, int B, int n, in
                                     w.begin, w.end, w.row_loss, loss, dX, st);
     if (e)
         return hip_fail(e, "loss/grad");
+    return SK_OK;
+}
+
+int sinkhorn_dense_grad(const void *X, const void *Y, int dtype, const float *a, const float *b,
+                        int B, int n, int m, int d, float eps, const float *f, const float *g,
+                        float *dX, float *TX, float *dY, float *TY, void *ws, size_t ws_bytes,
+                        void *stream)
+{
+    g_err[0] = '\0';
+    int rc = check_common(X, Y, dtype, B, n, m, d);
+    if (rc)
+        return rc;
+    if (!f || !g)
+        return fail(SK_ERR_INVALID_ARG, "f and g must be non-NULL device pointers");
+    if (!(eps > 0.f) || !isfinite(eps))
+        return fail(SK_ERR_INVALID_ARG, "eps=%g must be finite and > 0", eps);
+    rc = check_ws(ws, ws_bytes, ws_size(SK_OP_DENSE_GRAD, B, n, m, d, dtype));
+    if (rc)
+        return rc;
+    hipStream_t st = (hipStream_t)stream;
+    Carve c{(char *)ws};
+    GradWs w = carve_grad(c, B, n, m);
+    hipError_t e;
+    if ((e = launch_log_weights(a, B, n, w.la, st)) || (e = launch_log_weights(b, B, m, w.lb, st)))
+        return hip_fail(e, "log weights");
+    const double inv_eps = 1.0 / (double)eps;
+    if (dX || TX) {
+        PlanArgs p{X, Y, dtype, d, B, n, m, f, g, w.la, w.lb, inv_eps};
+        if ((e = launch_dense_grad(p, dX, TX, st)))
+            return hip_fail(e, "dense gradient (X side)");
+    }
+    if (dY || TY) {
+        // log P is symmetric in (X, a, f) and (Y, b, g): the Y side is the same pass
+        PlanArgs p{Y, X, dtype, d, B, m, n, g, f, w.lb, w.la, inv_eps};
+        if ((e = launch_dense_grad(p, dY, TY, st)))
+            return hip_fail(e, "dense gradient (Y side)");
+    }
     return SK_OK;
 }
 

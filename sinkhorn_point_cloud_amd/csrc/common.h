@@ -195,6 +195,9 @@ hipError_t launch_plan_scan(const int32_t *row_count, int B, int n, int64_t *row
 hipError_t launch_plan_emit(const PlanArgs &p, const double *pair_thr, const int64_t *row_off,
                             const int32_t *row_count, int32_t *rows, int32_t *cols,
                             float *vals, hipStream_t st);
+// Dense gradient 2 sum_j P_ij (x_i - y_j) and barycentric projection
+// sum_j P_ij y_j / sum_j P_ij of every row of p.X (either output may be NULL).
+hipError_t launch_dense_grad(const PlanArgs &p, float *grad, float *proj, hipStream_t st);
 
 hipError_t launch_loss_grad(const void *X, const void *Y, int dtype, int d, int B, int n,
                             int m, const int32_t *rows, const int32_t *cols, const float *vals,

@@ -14,14 +14,24 @@
 // potentials; P itself is returned as fp32.  The count and emit passes call the
 // same evaluation on the same inputs, so their decisions agree bit for bit.
 //
-// Layout: one wave per row, lanes across columns (64 consecutive columns per
-// step), so every wave reads contiguous keys and writes contiguous COO slices.
+//   - the dense transport application (FlashSinkhorn summary, Methodologie,
+//     "Toepassing van Transportmatrix": the gradient and the barycentric
+//     projection are weighted averages over the plan, streamed like the
+//     update): per row r_i = sum_j P_ij, G_i = sum_j P_ij (x_i - y_j), giving
+//     dX_i = 2 G_i and T_i = sum_j P_ij y_j / r_i = x_i - G_i / r_i.
+//
+// Two traversals.  Passes that reduce each row to a few numbers (cost, max,
+// count, dense gradient) hold one row per lane, 64 rows per wave, and stream
+// the keys with wave-uniform addresses (scalar loads shared by the lanes);
+// the 4 waves of a work-group take every 4th key and merge in LDS.  The emit
+// pass holds one row per wave with lanes across 64 consecutive columns, so
+// each wave writes contiguous slices of the COO arrays.
 #include "common.h"
 
 namespace sk {
 namespace {
 
-constexpr int kRowsPerGroup = 4;  // one wave per row
+constexpr int kRowsPerGroup = 4;  // emit pass: one wave per row
 
 template <int DP> struct RowCtx {
     float x[DP];   // row point (exact fp32 value of the fp32 / bf16 input)
@@ -79,55 +89,97 @@ __device__ void load_row(RowCtx<DP> &r, const PlanArgs &p, int b, int i)
     r.la = p.la[(size_t)b * p.n + i];
 }
 
-// mode 0: cost  (row sum of P C, double)   -> outd[row]
-// mode 1: max   (row max of log P, double) -> outd[row]
-// mode 2: count (entries >= thr, int32)    -> outi[row]
+constexpr int kTileWaves = 4;   // waves of a tile_pass work-group, splitting the keys
+constexpr int kGradDims = 16;   // gradient components accumulated per launch (no spills)
+
+// mode 0: cost  (row sum of P C, double)          -> outd[row]
+// mode 1: max   (row max of log P, double)        -> outd[row]
+// mode 2: count (entries >= thr, int32)           -> outi[row]
+// mode 3: dense gradient for dims k0 .. k0+KC-1   -> grad, proj (fp32, [B][n][d])
 template <typename T, int DP, int MODE>
-__global__ __launch_bounds__(kRowsPerGroup *kWave) void row_pass(PlanArgs p,
-                                                                 const double *__restrict__ thr,
-                                                                 double *__restrict__ outd,
-                                                                 int32_t *__restrict__ outi)
+__global__ __launch_bounds__(kTileWaves *kWave) void tile_pass(
+    PlanArgs p, const double *__restrict__ thr, double *__restrict__ outd,
+    int32_t *__restrict__ outi, float *__restrict__ grad, float *__restrict__ proj, int k0)
 {
+    constexpr int KC = MODE == 3 ? (DP < kGradDims ? DP : kGradDims) : 1;
+    __shared__ double red[kTileWaves][kWave];
     const int b = blockIdx.y;
-    const int i = blockIdx.x * kRowsPerGroup + wave_id_uniform();
-    if (i >= p.n)
-        return;
+    const int w = wave_id_uniform();
     const int lane = lane_id();
+    const int i = blockIdx.x * kWave + lane;
+    const bool live = i < p.n;
     RowCtx<DP> r;
-    load_row<T, DP>(r, p, b, i);
+    load_row<T, DP>(r, p, b, live ? i : p.n - 1);
     const T *Yb = (const T *)p.Y + (size_t)b * p.m * p.d;
     const float *gb = p.g + (size_t)b * p.m;
+    const double *lbb = p.lb + (size_t)b * p.m;
     const double t = MODE == 2 ? thr[b] : 0.0;
     double acc = MODE == 1 ? -INFINITY : 0.0;
     int cnt = 0;
-    for (int j0 = 0; j0 < p.m; j0 += kWave) {
-        const int j = j0 + lane;
-        if (j < p.m) {
-            double C;
-            const double lbj = p.lb[(size_t)b * p.m + j];
-            const double lp = log_plan<T, DP>(r, p, Yb, gb, lbj, j, &C);
-            if (MODE == 0) {
-                const double P = (double)ex2((float)(lp * 1.4426950408889634));
-                acc = fma(P, C, acc);
-            } else if (MODE == 1) {
-                acc = fmax(acc, lp);
-            } else {
-                cnt += lp >= t ? 1 : 0;
-            }
+    double G[KC], xc[KC];   // gradient sums and this chunk's row coordinates
+    {
+        const T *x = (const T *)p.X + ((size_t)b * p.n + (live ? i : p.n - 1)) * p.d;
+#pragma unroll
+        for (int k = 0; k < KC; ++k) {
+            G[k] = 0.0;
+            xc[k] = MODE == 3 && k0 + k < p.d ? (double)Elem<T>::get(x, k0 + k) : 0.0;
         }
     }
-    if (MODE == 0) {
-        acc = wave_sum(acc);
-        if (lane == 0)
-            outd[(size_t)b * p.n + i] = acc;
-    } else if (MODE == 1) {
-        acc = wave_max(acc);
-        if (lane == 0)
-            outd[(size_t)b * p.n + i] = acc;
+#pragma unroll 4
+    for (int j = w; j < p.m; j += kTileWaves) {
+        double C;
+        const double lp = log_plan<T, DP>(r, p, Yb, gb, lbb[j], j, &C);
+        if (MODE == 0) {
+            const double P = (double)ex2((float)(lp * 1.4426950408889634));
+            acc = fma(P, C, acc);
+        } else if (MODE == 1) {
+            acc = fmax(acc, lp);
+        } else if (MODE == 2) {
+            cnt += lp >= t ? 1 : 0;
+        } else {
+            const double P = (double)ex2((float)(lp * 1.4426950408889634));
+            acc += P;
+            const T *y = Yb + (size_t)j * p.d;
+#pragma unroll
+            for (int k = 0; k < KC; ++k)
+                if (k0 + k < p.d)
+                    G[k] = fma(P, xc[k] - (double)Elem<T>::get(y, k0 + k), G[k]);
+        }
+    }
+    // merge the waves in a fixed order
+    auto merged = [&](double v, bool is_max) {
+        __syncthreads();
+        red[w][lane] = v;
+        __syncthreads();
+        double s = red[0][lane];
+#pragma unroll
+        for (int v2 = 1; v2 < kTileWaves; ++v2)
+            s = is_max ? fmax(s, red[v2][lane]) : s + red[v2][lane];
+        return s;
+    };
+    if (MODE == 2) {
+        const double tot = merged((double)cnt, false);
+        if (w == 0 && live)
+            outi[(size_t)b * p.n + i] = (int32_t)tot;
+    } else if (MODE != 3) {
+        const double tot = merged(acc, MODE == 1);
+        if (w == 0 && live)
+            outd[(size_t)b * p.n + i] = tot;
     } else {
-        cnt = wave_sum(cnt);
-        if (lane == 0)
-            outi[(size_t)b * p.n + i] = cnt;
+        const double mass = merged(acc, false);
+        const size_t o = ((size_t)b * p.n + i) * p.d;
+#pragma unroll
+        for (int k = 0; k < KC; ++k) {
+            if (k0 + k >= p.d)
+                break;
+            const double Gk = merged(G[k], false);
+            if (w == 0 && live) {
+                if (grad)
+                    grad[o + k0 + k] = (float)(2.0 * Gk);
+                if (proj)
+                    proj[o + k0 + k] = mass > 0.0 ? (float)(xc[k] - Gk / mass) : 0.f;
+            }
+        }
     }
 }
 
@@ -292,18 +344,21 @@ void with_dp(int d, F fn)
 }
 
 template <int MODE>
-void row_dispatch(const PlanArgs &p, const double *thr, double *outd, int32_t *outi,
-                  hipStream_t st)
+void tile_dispatch(const PlanArgs &p, const double *thr, double *outd, int32_t *outi,
+                   float *grad, float *proj, hipStream_t st)
 {
-    dim3 grid(ceil_div(p.n, kRowsPerGroup), p.B);
-    dim3 block(kRowsPerGroup * kWave);
+    dim3 grid(ceil_div(p.n, kWave), p.B);
+    dim3 block(kTileWaves * kWave);
     with_dp(p.d, [&]<int DP>() {
-        if (p.dtype == 1)
-            hipLaunchKernelGGL((row_pass<uint16_t, DP, MODE>), grid, block, 0, st, p, thr, outd,
-                               outi);
-        else
-            hipLaunchKernelGGL((row_pass<float, DP, MODE>), grid, block, 0, st, p, thr, outd,
-                               outi);
+        const int chunks = MODE == 3 ? ceil_div(p.d, kGradDims) : 1;
+        for (int c = 0; c < chunks; ++c) {
+            if (p.dtype == 1)
+                hipLaunchKernelGGL((tile_pass<uint16_t, DP, MODE>), grid, block, 0, st, p, thr,
+                                   outd, outi, grad, proj, c * kGradDims);
+            else
+                hipLaunchKernelGGL((tile_pass<float, DP, MODE>), grid, block, 0, st, p, thr,
+                                   outd, outi, grad, proj, c * kGradDims);
+        }
     });
 }
 
@@ -319,7 +374,7 @@ hipError_t launch_log_weights(const float *w, int B, int count, double *out, hip
 
 hipError_t launch_cost(const PlanArgs &p, double *row_part, float *cost, hipStream_t st)
 {
-    row_dispatch<0>(p, nullptr, row_part, nullptr, st);
+    tile_dispatch<0>(p, nullptr, row_part, nullptr, nullptr, nullptr, st);
     hipLaunchKernelGGL(pair_reduce<0>, dim3(p.B), dim3(256), 0, st, (const double *)row_part,
                        p.n, cost, (double *)nullptr, 0.0);
     return hipGetLastError();
@@ -335,7 +390,7 @@ hipError_t launch_row_sums(const double *row_part, int B, int n, float *out, hip
 hipError_t launch_plan_max(const PlanArgs &p, double *row_max, double *pair_thr,
                            double log_rel_thr, hipStream_t st)
 {
-    row_dispatch<1>(p, nullptr, row_max, nullptr, st);
+    tile_dispatch<1>(p, nullptr, row_max, nullptr, nullptr, nullptr, st);
     hipLaunchKernelGGL(pair_reduce<1>, dim3(p.B), dim3(256), 0, st, (const double *)row_max,
                        p.n, (float *)nullptr, pair_thr, log_rel_thr);
     return hipGetLastError();
@@ -344,7 +399,7 @@ hipError_t launch_plan_max(const PlanArgs &p, double *row_max, double *pair_thr,
 hipError_t launch_plan_count(const PlanArgs &p, const double *pair_thr, int32_t *row_count,
                              hipStream_t st)
 {
-    row_dispatch<2>(p, pair_thr, nullptr, row_count, st);
+    tile_dispatch<2>(p, pair_thr, nullptr, row_count, nullptr, nullptr, st);
     return hipGetLastError();
 }
 
@@ -373,6 +428,12 @@ hipError_t launch_plan_emit(const PlanArgs &p, const double *pair_thr, const int
             hipLaunchKernelGGL((emit_pass<float, DP>), grid, block, 0, st, p, pair_thr, row_off,
                                row_count, rows, cols, vals);
     });
+    return hipGetLastError();
+}
+
+hipError_t launch_dense_grad(const PlanArgs &p, float *grad, float *proj, hipStream_t st)
+{
+    tile_dispatch<3>(p, nullptr, nullptr, nullptr, grad, proj, st);
     return hipGetLastError();
 }
 

@@ -53,7 +53,7 @@ def test_status_strings(lib):
 
 def test_workspace_bytes(lib):
     ws = lib.sinkhorn_workspace_bytes
-    for op in (0, 1, 2):
+    for op in (0, 1, 2, 3):
         assert ws(op, 1, 1024, 1024, 3, 0) > 0
         assert ws(op, 2, 1024, 1024, 3, 0) > ws(op, 1, 1024, 1024, 3, 0)
         assert ws(op, 1, 4096, 1024, 3, 0) > ws(op, 1, 1024, 1024, 3, 0)
@@ -62,7 +62,8 @@ def test_workspace_bytes(lib):
     assert ws(0, 1, 10, 10, 3, 1) > 0                  # bf16 d=3: feature kernel
     assert ws(0, 1, 10, 10, 200, 0) == 0               # d > 128: no kernel
     assert ws(0, 0, 10, 10, 3, 0) == 0
-    assert ws(3, 1, 10, 10, 3, 0) == 0
+    assert ws(4, 1, 10, 10, 3, 0) == 0
+    assert ws(3, 1, 65536, 65536, 3, 0) < 4 << 20      # two fp64 log-weight vectors
     assert ws(0, 1, 1 << 25, 10, 3, 0) == 0
 
 
@@ -139,6 +140,27 @@ def test_loss_grad_rejects_bad_arguments(lib):
                                 _host(loss), None, DUMMY, 8, None)
     assert rc == sk.SK_ERR_WORKSPACE
     assert loss[0] == 5.0
+
+
+def _dgrad(lib, eps=0.1, f=DUMMY, g=DUMMY, d=3, ws=DUMMY, ws_bytes=1 << 40, out=DUMMY):
+    return lib.sinkhorn_dense_grad(DUMMY, DUMMY, 0, None, None, 1, 8, 9, d, eps, f, g, out,
+                                   None, None, None, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(eps=0.0), sk.SK_ERR_INVALID_ARG),
+    (dict(eps=float("inf")), sk.SK_ERR_INVALID_ARG),
+    (dict(f=None), sk.SK_ERR_INVALID_ARG),
+    (dict(g=None), sk.SK_ERR_INVALID_ARG),
+    (dict(d=129), sk.SK_ERR_UNSUPPORTED),
+    (dict(ws=None), sk.SK_ERR_WORKSPACE),
+    (dict(ws_bytes=64), sk.SK_ERR_WORKSPACE),
+])
+def test_dense_grad_rejects_bad_arguments_without_writing(lib, kw, code):
+    dX = np.full(8 * 3, 7.0, dtype=np.float32)
+    rc = _dgrad(lib, out=_host(dX), **kw)
+    assert rc == code, lib.sinkhorn_last_error()
+    assert np.all(dX == 7.0)
 
 
 def test_binding_refuses_cpu_tensors():

@@ -342,3 +342,99 @@ def test_workload_gmm_64k():
 
 def test_workload_feat_50k():
     check_workload_potentials("feat-50k", 1e-2)
+
+
+# ------------------------------------------------ dense gradient and projection
+def check_dense_grad(c, eps, fo, go, sel_x=None, sel_y=None, tol=1e-4):
+    """GPU dense_grad against the oracle, both from the same fp32 potentials."""
+    f32 = np.asarray(fo, dtype=np.float32)
+    g32 = np.asarray(go, dtype=np.float32)
+    X, Y = points(c)
+    dX, TX, dY, TY = sk.dense_grad(X, Y, dev(c["a"]), dev(c["b"]), dev(f32), dev(g32), eps)
+    torch.cuda.synchronize()
+    B, n, d = c["X"].shape
+    m = c["Y"].shape[1]
+    for side, P, Q, wp, wq, fp, gq, k, sel, dG, T in (
+            ("x", c["X"], c["Y"], c["a"], c["b"], f32, g32, n, sel_x, dX, TX),
+            ("y", c["Y"], c["X"], c["b"], c["a"], g32, f32, m, sel_y, dY, TY)):
+        r_o, dG_o, T_o = oracle.dense_grad(P, Q, wp, wq, fp.astype(np.float64),
+                                           gq.astype(np.float64), eps, sel=sel)
+        got_dG = host(dG).reshape(B * k, d)
+        got_T = host(T).reshape(B * k, d)
+        if sel is None:
+            dG_o, T_o = dG_o.reshape(B * k, d), T_o.reshape(B * k, d)
+        else:
+            got_dG, got_T = got_dG[sel], got_T[sel]
+        assert rel_inf(got_dG, dG_o) <= tol, f"gradient, {side} side"
+        # the projection is a point: compare against the cloud's extent
+        ext = max(np.abs(P).max(), np.abs(Q).max())
+        assert np.abs(got_T - T_o).max() / ext <= tol, f"projection, {side} side"
+    return dX, TX, dY, TY
+
+
+@pytest.mark.parametrize("B,n,m,d,dtype,w,eps", [
+    (1, 33, 47, 3, "f32", "uniform", 0.05),
+    (2, 300, 257, 3, "f32", "dirichlet", 0.01),
+    (1, 130, 77, 8, "f32", "dirichlet", 0.1),
+    (1, 200, 190, 64, "bf16", "uniform", 0.2),
+    (1, 90, 100, 100, "f32", "uniform", 0.5),
+])
+def test_dense_grad_matches_oracle(B, n, m, d, dtype, w, eps):
+    c = workloads.random_case(11, B, n, m, d, weights=w, dtype=dtype)
+    fo, go = oracle.potentials(c["X"], c["Y"], c["a"], c["b"], eps=[eps], iters=[20])
+    check_dense_grad(c, np.float32(eps), fo, go)
+
+
+def test_dense_grad_zero_mass_rows_and_single_side():
+    c = workloads.random_case(12, 1, 70, 50, 3, weights="dirichlet", zero_weights=4)
+    eps = np.float32(0.03)
+    fo, go = oracle.potentials(c["X"], c["Y"], c["a"], c["b"], eps=[eps], iters=[10])
+    dX, TX, dY, TY = check_dense_grad(c, eps, fo, go)
+    assert np.all(host(dX)[0, :4] == 0) and np.all(host(TX)[0, :4] == 0)
+    assert np.all(host(dY)[0, :4] == 0) and np.all(host(TY)[0, :4] == 0)
+    # one output or one side at a time gives the same values
+    X, Y = points(c)
+    f32, g32 = dev(fo.astype(np.float32)), dev(go.astype(np.float32))
+    a, b = dev(c["a"]), dev(c["b"])
+    only_dX = sk.dense_grad(X, Y, a, b, f32, g32, float(eps),
+                            out=(torch.empty_like(dX), None, None, None))
+    only_y = sk.dense_grad(X, Y, a, b, f32, g32, float(eps), sides="y")
+    torch.cuda.synchronize()
+    assert torch.equal(only_dX[0], dX) and only_dX[1] is None
+    assert only_y[0] is None and only_y[1] is None
+    assert torch.equal(only_y[2], dY) and torch.equal(only_y[3], TY)
+
+
+def test_dense_grad_agrees_with_full_support_coo_gradient():
+    c = workloads.random_case(13, 2, 120, 110, 3, weights="dirichlet")
+    eps = 0.05
+    fo, go = oracle.potentials(c["X"], c["Y"], c["a"], c["b"], eps=[eps], iters=[15])
+    X, Y = points(c)
+    f32, g32 = dev(fo.astype(np.float32)), dev(go.astype(np.float32))
+    a, b = dev(c["a"]), dev(c["b"])
+    rows, cols, vals, offs = sk.plan_coo(X, Y, a, b, f32, g32, eps, 1e-30)
+    _, dXc = sk.loss_grad(X, Y, rows, cols, vals, offs)
+    dX, _, _, _ = sk.dense_grad(X, Y, a, b, f32, g32, eps, sides="x")
+    for p in range(2):
+        assert rel_inf(host(dX)[p], host(dXc)[p]) <= 1e-5
+
+
+def test_workload_pair_1k_dense_grad():
+    w, gold = load_workload("pair-1k")
+    check_dense_grad(w, float(w["eps"][-1]), gold["f"], gold["g"])
+
+
+def test_workload_gmm_64k_dense_grad_sampled_rows():
+    w, gold = load_workload("gmm-64k")
+    rng = np.random.default_rng(1)
+    sel_x = np.sort(rng.choice(65536, 256, replace=False))
+    sel_y = np.sort(rng.choice(65536, 256, replace=False))
+    check_dense_grad(w, float(w["eps"][-1]), gold["f"], gold["g"], sel_x, sel_y)
+
+
+def test_workload_feat_50k_dense_grad_sampled_rows():
+    w, gold = load_workload("feat-50k")
+    rng = np.random.default_rng(2)
+    sel_x = np.sort(rng.choice(50000, 64, replace=False))
+    sel_y = np.sort(rng.choice(60000, 64, replace=False))
+    check_dense_grad(w, float(w["eps"][-1]), gold["f"], gold["g"], sel_x, sel_y, tol=1e-2)
