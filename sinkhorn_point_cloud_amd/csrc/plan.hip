@@ -38,13 +38,21 @@ template <int DP> struct RowCtx {
     double f, la;
 };
 
+// Whether component k exists: the DP = 3 instantiations serve d == 3 only, so
+// their loops carry no run-time test; wider ones pad d up to DP.
+template <int DP>
+__device__ __forceinline__ bool has_dim(int k, int d)
+{
+    return DP == 3 || k < d;
+}
+
 template <typename T, int DP>
 __device__ __forceinline__ double sq_dist(const float (&x)[DP], const T *y, int d)
 {
     double s = 0.0;
 #pragma unroll
     for (int k = 0; k < DP; ++k) {
-        if (k < d) {
+        if (has_dim<DP>(k, d)) {
             const double t = (double)x[k] - (double)Elem<T>::get(y, k);
             s = fma(t, t, s);
         }
@@ -84,7 +92,7 @@ __device__ void load_row(RowCtx<DP> &r, const PlanArgs &p, int b, int i)
     const T *x = (const T *)p.X + ((size_t)b * p.n + i) * p.d;
 #pragma unroll
     for (int k = 0; k < DP; ++k)
-        r.x[k] = k < p.d ? Elem<T>::get(x, k) : 0.f;
+        r.x[k] = has_dim<DP>(k, p.d) ? Elem<T>::get(x, k) : 0.f;
     r.f = (double)p.f[(size_t)b * p.n + i];
     r.la = p.la[(size_t)b * p.n + i];
 }
@@ -122,11 +130,10 @@ __global__ __launch_bounds__(kTileWaves *kWave) void tile_pass(
 #pragma unroll
         for (int k = 0; k < KC; ++k) {
             G[k] = 0.0;
-            xc[k] = MODE == 3 && k0 + k < p.d ? (double)Elem<T>::get(x, k0 + k) : 0.0;
+            xc[k] = MODE == 3 && has_dim<DP>(k0 + k, p.d) ? (double)Elem<T>::get(x, k0 + k) : 0.0;
         }
     }
-#pragma unroll 4
-    for (int j = w; j < p.m; j += kTileWaves) {
+    auto visit = [&](int j) {
         double C;
         const double lp = log_plan<T, DP>(r, p, Yb, gb, lbb[j], j, &C);
         if (MODE == 0) {
@@ -142,10 +149,22 @@ __global__ __launch_bounds__(kTileWaves *kWave) void tile_pass(
             const T *y = Yb + (size_t)j * p.d;
 #pragma unroll
             for (int k = 0; k < KC; ++k)
-                if (k0 + k < p.d)
+                if (has_dim<DP>(k0 + k, p.d))
                     G[k] = fma(P, xc[k] - (double)Elem<T>::get(y, k0 + k), G[k]);
         }
+    };
+    int j = w;
+    if constexpr (DP <= 4) {
+        // four keys per step, so that their loads are in flight together
+        for (; j + 3 * kTileWaves < p.m; j += 4 * kTileWaves) {
+            visit(j);
+            visit(j + kTileWaves);
+            visit(j + 2 * kTileWaves);
+            visit(j + 3 * kTileWaves);
+        }
     }
+    for (; j < p.m; j += kTileWaves)
+        visit(j);
     // merge the waves in a fixed order
     auto merged = [&](double v, bool is_max) {
         __syncthreads();
@@ -170,8 +189,8 @@ __global__ __launch_bounds__(kTileWaves *kWave) void tile_pass(
         const size_t o = ((size_t)b * p.n + i) * p.d;
 #pragma unroll
         for (int k = 0; k < KC; ++k) {
-            if (k0 + k >= p.d)
-                break;
+            if (!has_dim<DP>(k0 + k, p.d))   // uniform: every thread skips alike
+                continue;
             const double Gk = merged(G[k], false);
             if (w == 0 && live) {
                 if (grad)
@@ -335,7 +354,8 @@ __global__ __launch_bounds__(kRowsPerGroup *kWave) void emit_pass(
 template <typename F>
 void with_dp(int d, F fn)
 {
-    if (d <= 4) fn.template operator()<4>();
+    if (d == 3) fn.template operator()<3>();
+    else if (d <= 4) fn.template operator()<4>();
     else if (d <= 8) fn.template operator()<8>();
     else if (d <= 16) fn.template operator()<16>();
     else if (d <= 32) fn.template operator()<32>();
