@@ -135,13 +135,31 @@ LossWs carve_loss(Carve &c, int B, int n)
 
 struct GradWs {
     double *la, *lb;
+    // matrix-core path (bf16, d = 32 or 64)
+    float *xbias = nullptr, *ybias = nullptr, *xsq = nullptr, *ysq = nullptr;
+    float *l2a = nullptr, *l2b = nullptr;
+    uint16_t *xt = nullptr, *yt = nullptr;
+    int *xredo = nullptr, *yredo = nullptr;
 };
 
-GradWs carve_grad(Carve &c, int B, int n, int m)
+GradWs carve_grad(Carve &c, int B, int n, int m, int d, int dtype)
 {
     GradWs w;
     w.la = c.take<double>((size_t)B * n);
     w.lb = c.take<double>((size_t)B * m);
+    if (gradF_matrix_cores(dtype, d)) {
+        const int np = round_up(n, kPad), mp = round_up(m, kPad);
+        w.xbias = c.take<float>((size_t)B * np);
+        w.ybias = c.take<float>((size_t)B * mp);
+        w.xsq = c.take<float>((size_t)B * n);
+        w.ysq = c.take<float>((size_t)B * m);
+        w.l2a = c.take<float>((size_t)B * n);
+        w.l2b = c.take<float>((size_t)B * m);
+        w.xt = c.take<uint16_t>((size_t)B * d * np);
+        w.yt = c.take<uint16_t>((size_t)B * d * mp);
+        w.xredo = c.take<int>((size_t)B * (np / kPad));
+        w.yredo = c.take<int>((size_t)B * (mp / kPad));
+    }
     return w;
 }
 
@@ -155,7 +173,7 @@ size_t ws_size(int op, int B, int n, int m, int d, int dtype)
     else if (op == SK_OP_LOSS_GRAD)
         carve_loss(c, B, n);
     else
-        carve_grad(c, B, n, m);
+        carve_grad(c, B, n, m, d, dtype);
     return c.off + 256;
 }
 
@@ -410,22 +428,43 @@ int sinkhorn_dense_grad(const void *X, const void *Y, int dtype, const float *a,
         return rc;
     hipStream_t st = (hipStream_t)stream;
     Carve c{(char *)ws};
-    GradWs w = carve_grad(c, B, n, m);
+    GradWs w = carve_grad(c, B, n, m, d, dtype);
     hipError_t e;
     if ((e = launch_log_weights(a, B, n, w.la, st)) || (e = launch_log_weights(b, B, m, w.lb, st)))
         return hip_fail(e, "log weights");
     const double inv_eps = 1.0 / (double)eps;
-    if (dX || TX) {
-        PlanArgs p{X, Y, dtype, d, B, n, m, f, g, w.la, w.lb, inv_eps};
-        if ((e = launch_dense_grad(p, dX, TX, st)))
-            return hip_fail(e, "dense gradient (X side)");
+    const bool want_x = dX || TX, want_y = dY || TY;
+    // log P is symmetric in (X, a, f) and (Y, b, g): the Y side is the same pass
+    PlanArgs px{X, Y, dtype, d, B, n, m, f, g, w.la, w.lb, inv_eps};
+    PlanArgs py{Y, X, dtype, d, B, m, n, g, f, w.lb, w.la, inv_eps};
+    const bool aligned = (uintptr_t)X % 16 == 0 && (uintptr_t)Y % 16 == 0;
+    if (gradF_matrix_cores(dtype, d) && aligned) {
+        const int np = round_up(n, kPad), mp = round_up(m, kPad);
+        // potentials are only read (warm start): biases c (pot - ||.||^2) + log2 w at eps
+        SideF sx{X, w.xbias, const_cast<float *>(f), w.l2a, w.xsq, w.xredo, n, np};
+        SideF sy{Y, w.ybias, const_cast<float *>(g), w.l2b, w.ysq, w.yredo, m, mp};
+        const double c0 = (double)scale_of(eps);
+        if ((e = launch_packF(X, dtype, d, a, 1, B, sx, c0, st)) ||
+            (e = launch_packF(Y, dtype, d, b, 1, B, sy, c0, st)))
+            return hip_fail(e, "dense gradient: biases");
+        if (want_x) {
+            if ((e = launch_transpose_bf16(Y, B, m, mp, d, w.yt, st)) ||
+                (e = launch_gradFm(sx, a, sy, w.yt, d, B, eps, dX, TX, st)) ||
+                (e = launch_dense_grad(px, dX, TX, w.xredo, st)))
+                return hip_fail(e, "dense gradient (X side)");
+        }
+        if (want_y) {
+            if ((e = launch_transpose_bf16(X, B, n, np, d, w.xt, st)) ||
+                (e = launch_gradFm(sy, b, sx, w.xt, d, B, eps, dY, TY, st)) ||
+                (e = launch_dense_grad(py, dY, TY, w.yredo, st)))
+                return hip_fail(e, "dense gradient (Y side)");
+        }
+        return SK_OK;
     }
-    if (dY || TY) {
-        // log P is symmetric in (X, a, f) and (Y, b, g): the Y side is the same pass
-        PlanArgs p{Y, X, dtype, d, B, m, n, g, f, w.lb, w.la, inv_eps};
-        if ((e = launch_dense_grad(p, dY, TY, st)))
-            return hip_fail(e, "dense gradient (Y side)");
-    }
+    if (want_x && (e = launch_dense_grad(px, dX, TX, nullptr, st)))
+        return hip_fail(e, "dense gradient (X side)");
+    if (want_y && (e = launch_dense_grad(py, dY, TY, nullptr, st)))
+        return hip_fail(e, "dense gradient (Y side)");
     return SK_OK;
 }
 

@@ -196,8 +196,20 @@ hipError_t launch_plan_emit(const PlanArgs &p, const double *pair_thr, const int
                             const int32_t *row_count, int32_t *rows, int32_t *cols,
                             float *vals, hipStream_t st);
 // Dense gradient 2 sum_j P_ij (x_i - y_j) and barycentric projection
-// sum_j P_ij y_j / sum_j P_ij of every row of p.X (either output may be NULL).
-hipError_t launch_dense_grad(const PlanArgs &p, float *grad, float *proj, hipStream_t st);
+// sum_j P_ij y_j / sum_j P_ij of every row of p.X (either output may be NULL),
+// log P in fp64.  only != NULL: just the 64-row blocks flagged there.
+hipError_t launch_dense_grad(const PlanArgs &p, float *grad, float *proj, const int *only,
+                             hipStream_t st);
+// The same on the matrix cores for bf16 with d = 32 or 64: rows' side (points,
+// potential, squared norms; its redo array receives the per-block fallback
+// flags), row weights (NULL: uniform), and the key side's points, biases at
+// eps (from launch_packF with warm start) and transposed points [B][d][n_pad].
+bool gradF_matrix_cores(int dtype, int d);
+hipError_t launch_gradFm(const SideF &rows, const float *row_w, const SideF &keys,
+                         const uint16_t *keys_t, int d, int B, float eps, float *grad,
+                         float *proj, hipStream_t st);
+hipError_t launch_transpose_bf16(const void *X, int B, int n, int n_pad, int d, uint16_t *Xt,
+                                 hipStream_t st);
 
 hipError_t launch_loss_grad(const void *X, const void *Y, int dtype, int d, int B, int n,
                             int m, const int32_t *rows, const int32_t *cols, const float *vals,

@@ -107,8 +107,12 @@ constexpr int kGradDims = 16;   // gradient components accumulated per launch (n
 template <typename T, int DP, int MODE>
 __global__ __launch_bounds__(kTileWaves *kWave) void tile_pass(
     PlanArgs p, const double *__restrict__ thr, double *__restrict__ outd,
-    int32_t *__restrict__ outi, float *__restrict__ grad, float *__restrict__ proj, int k0)
+    int32_t *__restrict__ outi, float *__restrict__ grad, float *__restrict__ proj, int k0,
+    const int *__restrict__ only)
 {
+    // only != nullptr: redo just the row blocks flagged there
+    if (only && !only[blockIdx.y * gridDim.x + blockIdx.x])
+        return;
     constexpr int KC = MODE == 3 ? (DP < kGradDims ? DP : kGradDims) : 1;
     __shared__ double red[kTileWaves][kWave];
     const int b = blockIdx.y;
@@ -365,7 +369,7 @@ void with_dp(int d, F fn)
 
 template <int MODE>
 void tile_dispatch(const PlanArgs &p, const double *thr, double *outd, int32_t *outi,
-                   float *grad, float *proj, hipStream_t st)
+                   float *grad, float *proj, hipStream_t st, const int *only = nullptr)
 {
     dim3 grid(ceil_div(p.n, kWave), p.B);
     dim3 block(kTileWaves * kWave);
@@ -374,10 +378,10 @@ void tile_dispatch(const PlanArgs &p, const double *thr, double *outd, int32_t *
         for (int c = 0; c < chunks; ++c) {
             if (p.dtype == 1)
                 hipLaunchKernelGGL((tile_pass<uint16_t, DP, MODE>), grid, block, 0, st, p, thr,
-                                   outd, outi, grad, proj, c * kGradDims);
+                                   outd, outi, grad, proj, c * kGradDims, only);
             else
                 hipLaunchKernelGGL((tile_pass<float, DP, MODE>), grid, block, 0, st, p, thr,
-                                   outd, outi, grad, proj, c * kGradDims);
+                                   outd, outi, grad, proj, c * kGradDims, only);
         }
     });
 }
@@ -451,9 +455,10 @@ hipError_t launch_plan_emit(const PlanArgs &p, const double *pair_thr, const int
     return hipGetLastError();
 }
 
-hipError_t launch_dense_grad(const PlanArgs &p, float *grad, float *proj, hipStream_t st)
+hipError_t launch_dense_grad(const PlanArgs &p, float *grad, float *proj, const int *only,
+                             hipStream_t st)
 {
-    tile_dispatch<3>(p, nullptr, nullptr, nullptr, grad, proj, st);
+    tile_dispatch<3>(p, nullptr, nullptr, nullptr, grad, proj, st, only);
     return hipGetLastError();
 }
 
