@@ -53,13 +53,31 @@ def roofline_evals_per_s(d):
     return peak, "mfma" if peak == mfma else "alu", fp32, exp, mfma
 
 
-def measured_traffic(kernel, workload, source):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
-    when there is none or the kernel's source has changed since it was taken."""
-    import glob
+# sources whose change invalidates a kernel's committed traffic counters
+KERNEL_SOURCES = {
+    "lse3m_kernel": ("sinkhorn_point_cloud_amd/csrc/lse_d3.hip",
+                     "sinkhorn_point_cloud_amd/csrc/common.h"),
+    "lseFm_kernel": ("sinkhorn_point_cloud_amd/csrc/lse_feat.hip",
+                     "sinkhorn_point_cloud_amd/csrc/common.h"),
+}
+
+
+def source_hash(sources):
+    """First 16 hex digits of the sha256 of the kernel's source files, in order."""
     import hashlib
 
-    sha = hashlib.sha256(open(os.path.join(ROOT, source), "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for src in sources:
+        h.update(open(os.path.join(ROOT, src), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload, sources):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    when there is none or the kernel's sources have changed since it was taken."""
+    import glob
+
+    sha = source_hash(sources)
     for path in glob.glob(os.path.join(ROOT, "profiles", "traffic_*.md")):
         for line in open(path):
             parts = line.split()
@@ -191,6 +209,11 @@ def main():
     peak, bound, fp32_bound, exp_bound, mfma_bound = roofline_evals_per_s(d)
     serial = 1.0 / (1.0 / fp32_bound + 1.0 / exp_bound)
 
+    if d == 3 and dt == sk.SK_F32:
+        kernel = "lse3_kernel" if args.valu_scores else "lse3m_kernel"
+    else:
+        kernel = "lseFm_kernel" if dt == sk.SK_BF16 and d % 32 == 0 else "lseF_kernel"
+
     updates = B * n * m * total_iters
     line = {
         "metric": "Sinkhorn cost-entry updates/s (B*n*m*iters/s); % of exp/FP32 roofline",
@@ -213,15 +236,11 @@ def main():
                    else "potentials f, g and transport cost"},
         "roofline": {"bound": bound, "achieved": achieved / 1e12, "peak": peak / 1e12,
                      "unit": "Teval/s", "frac": achieved / peak,
-                     "traffic": measured_traffic("lse3m_kernel", w["name"],
-                                                 "sinkhorn_point_cloud_amd/csrc/lse_d3.hip")
-                     if (d == 3 and dt == 0 and not args.valu_scores) else None,
+                     "traffic": measured_traffic(kernel, w["name"], KERNEL_SOURCES[kernel])
+                     if kernel in KERNEL_SOURCES else None,
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
                                      "scaled by a 256 MiB copy)",
-                     "kernel": ("lse3_kernel" if args.valu_scores else "lse3m_kernel")
-                     + " (one half-iteration)" if (d == 3 and dt == 0)
-                     else "lseFm_kernel (one half-iteration)" if dt == 1 and d % 32 == 0
-                     else "lseF_kernel (one half-iteration)",
+                     "kernel": kernel + " (one half-iteration)",
                      "launch_ms": t_launch * 1e3, "evals_per_launch": evals_per_launch,
                      "serial_exp_fp32_peak": serial / 1e12,
                      "frac_of_serial_peak": achieved / serial},
