@@ -158,7 +158,7 @@ int sinkhorn_loss_grad(const void *X, const void *Y, int dtype,
 
 /*
  * Dense transport application: gradient and barycentric projection
- * [FS Methodologie, "Toepassing van Transportmatrix": both are weighted
+ * [FS Methodologie 3, "Toepassing van Transportmatrix": both are weighted
  * averages over the plan, computed by streaming like the update, without
  * storing the plan].
  *

@@ -462,7 +462,7 @@ int oracle_loss_grad(const double *X, const double *Y, int B, int n, int m, int 
 }
 
 /*
- * Dense transport application at eps [FS Methodologie, "Toepassing van
+ * Dense transport application at eps [FS Methodologie 3, "Toepassing van
  * Transportmatrix": the barycentric projection and the gradient are weighted
  * averages over the plan, streamed like the update].  For each selected row i
  * of the X side of pair p, with P from the given potentials:

@@ -1,7 +1,7 @@
 // grad_feat.hip -- dense gradient and barycentric projection for bf16 feature
 // clouds on the matrix cores (d = 32 or 64).
 //
-// The transport application of the FlashSinkhorn summary (Methodologie,
+// The transport application of the FlashSinkhorn summary (Methodologie 3,
 // "Toepassing van Transportmatrix": the gradient and the barycentric
 // projection are weighted averages over the plan, streamed like the update
 // without storing the plan).  With c = log2(e)/eps and the potentials f, g of

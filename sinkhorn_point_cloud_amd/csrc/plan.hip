@@ -14,7 +14,7 @@
 // potentials; P itself is returned as fp32.  The count and emit passes call the
 // same evaluation on the same inputs, so their decisions agree bit for bit.
 //
-//   - the dense transport application (FlashSinkhorn summary, Methodologie,
+//   - the dense transport application (FlashSinkhorn summary, Methodologie 3,
 //     "Toepassing van Transportmatrix": the gradient and the barycentric
 //     projection are weighted averages over the plan, streamed like the
 //     update): per row r_i = sum_j P_ij, G_i = sum_j P_ij (x_i - y_j), giving
