@@ -203,8 +203,18 @@ __global__ __launch_bounds__(kWaves *kWave) void lseF_kernel(
 // Shifted streaming as in lse_d3.hip: row i streams against
 // M_i = c (||x_i||^2 - f_i), carried in the accumulator input as
 // -M_i / (2c) = -(||x_i||^2 - f_i) / 2, so one fma with the column bias gives
-// s_ij - M_i = 2c D_ij + beta_j.  A row block whose sum leaves [2^-64, 2^100]
-// is flagged and recomputed by the vector kernel in a second launch.
+// s_ij - M_i = 2c D_ij + beta_j.  With one shift per row, partial sums over
+// key ranges simply add.
+//
+// Key stream shared by the waves of a work-group: each of its R waves owns 64
+// rows, and all R stream the same key tiles, staged in LDS (double buffered,
+// 64 keys a stage, loaded cooperatively with 16-byte accesses), so the chip
+// fetches each key tile once per R * 64 rows instead of once per 64; the key
+// range is split across work-groups to fill the chip.  Each wave writes the
+// partial sums of its rows; a finalize kernel adds the splits in a fixed
+// order, turns the sums into potentials and biases, and flags a 64-row block
+// whose sum left [2^-64, 2^100] (a stale shift), which the vector kernel then
+// recomputes in full.
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 constexpr int kGroups = 4;
@@ -217,19 +227,29 @@ __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t *p)
     return __builtin_bit_cast(bf16x8, v);
 }
 
+constexpr int kShareWaves = 8;   // waves (64-row blocks) sharing one key stream
+constexpr int kStageTiles = 8;   // key tiles per LDS stage (128 keys)
+
 template <int DK>
-__global__ __launch_bounds__(kWaves *kWave) void lseFm_kernel(
-    const uint16_t *__restrict__ qx_, float *__restrict__ qbias, float *__restrict__ qpot,
-    const float *__restrict__ ql2w, const float *__restrict__ qsq, int *__restrict__ redo_out,
-    const uint16_t *__restrict__ ky_, const float *__restrict__ kbias, int nq, int nq_pad,
-    int nk, int nk_pad, float two_c, double eps_ln2, double c_next)
+__global__ __launch_bounds__(kShareWaves *kWave) void lseFm_kernel(
+    const uint16_t *__restrict__ qx_, const float *__restrict__ qpot,
+    const float *__restrict__ qsq, const uint16_t *__restrict__ ky_,
+    const float *__restrict__ kbias, float *__restrict__ part, int nq, int nq_pad, int nk,
+    int nk_pad, int tiles_per_split, float two_c)
 {
     constexpr int d = 32 * DK;
-    __shared__ float2 red[kWaves][kWave];
+    constexpr int kStageKeys = kStageTiles * kKeys;
+    constexpr int kChunks = d / 8;            // 16-byte chunks per key
+    constexpr int kStride = kChunks + 1;      // padded key stride in LDS (bank spread)
+    constexpr int kTotal = kStageKeys * kChunks;   // 16-byte chunks per stage
+    constexpr int kLoads = (kTotal + kShareWaves * kWave - 1) / (kShareWaves * kWave);
+    __shared__ uint4 kbuf[2][kStageKeys * kStride];
+    __shared__ float bbuf[2][kStageKeys];
     const int b = blockIdx.z;
+    const int split = blockIdx.y;
     const int lane = lane_id();
     const int w = wave_id_uniform();
-    const int row0 = blockIdx.x * kWave;
+    const int row0 = (blockIdx.x * kShareWaves + w) * kWave;   // this wave's 64 rows
     const int kq = lane >> 4;
     const int c16 = lane & 15;
 
@@ -258,80 +278,125 @@ __global__ __launch_bounds__(kWaves *kWave) void lseFm_kernel(
             S[g][r] = 0.f;
         }
     }
-    const uint16_t *ky = ky_ + (size_t)b * nk * d;
+    const uint4 *ky = reinterpret_cast<const uint4 *>(ky_ + (size_t)b * nk * d);
     const float *kb_ = kbias + (size_t)b * nk_pad;
     const int n_tiles = nk_pad / kKeys;
-    auto key_ptr = [&](int t) {
-        const int j = min(t * kKeys + c16, nk - 1);    // padding keys carry bias -1e30
-        return ky + (size_t)j * d + 8 * kq;
-    };
-    int t = w;
-    const int last = n_tiles - 1;
-    bf16x8 B0[DK], B1[DK];
-    float b0 = kb_[min(t, last) * kKeys + c16], b1 = kb_[min(t + kWaves, last) * kKeys + c16];
-#pragma unroll
-    for (int kb = 0; kb < DK; ++kb) {
-        B0[kb] = load_bf16x8(key_ptr(min(t, last)) + 32 * kb);
-        B1[kb] = load_bf16x8(key_ptr(min(t + kWaves, last)) + 32 * kb);
+    const int t_begin = split * tiles_per_split;
+    const int t_end = min(t_begin + tiles_per_split, n_tiles);
+    const int n_stages = t_begin < t_end ? (t_end - t_begin + kStageTiles - 1) / kStageTiles : 0;
+
+    // cooperative stage load: chunk e = key * kChunks + part of the stage's keys;
+    // keys past the split's last tile get bias -1e30 (they add exactly 0), and
+    // their point index is clamped inside the pair.  A thread's chunks of the
+    // next stage are loaded into registers while the current stage is
+    // consumed, then written to the other LDS buffer.
+    const int e0 = threadIdx.x;
+    uint4 ld0, ld1, ld2, ld3;   // kLoads <= 4 of them are used
+    float lb = kNeg;
+#define SK_CHUNK(i_) (e0 + (i_) * kShareWaves * kWave)
+#define SK_LOAD(i_, v_)                                                                    \
+    if (kLoads > (i_) && SK_CHUNK(i_) < kTotal)                                            \
+        v_ = ky[(size_t)min(key0_ + SK_CHUNK(i_) / kChunks, nk - 1) * kChunks +            \
+                SK_CHUNK(i_) % kChunks]
+#define SK_PUT(buf_, i_, v_)                                                               \
+    if (kLoads > (i_) && SK_CHUNK(i_) < kTotal)                                            \
+        kbuf[buf_][(SK_CHUNK(i_) / kChunks) * kStride + SK_CHUNK(i_) % kChunks] = v_
+#define SK_FETCH(s_)                                                                       \
+    do {                                                                                   \
+        const int key0_ = (t_begin + (s_) * kStageTiles) * kKeys;                          \
+        SK_LOAD(0, ld0);                                                                   \
+        SK_LOAD(1, ld1);                                                                   \
+        SK_LOAD(2, ld2);                                                                   \
+        SK_LOAD(3, ld3);                                                                   \
+        if (e0 < kStageKeys)                                                               \
+            lb = key0_ + e0 < t_end * kKeys ? kb_[key0_ + e0] : kNeg;                      \
+    } while (0)
+#define SK_STASH(buf_)                                                                     \
+    do {                                                                                   \
+        SK_PUT(buf_, 0, ld0);                                                              \
+        SK_PUT(buf_, 1, ld1);                                                              \
+        SK_PUT(buf_, 2, ld2);                                                              \
+        SK_PUT(buf_, 3, ld3);                                                              \
+        if (e0 < kStageKeys)                                                               \
+            bbuf[buf_][e0] = lb;                                                           \
+    } while (0)
+    static_assert(kLoads <= 4, "at most four 16-byte chunks per thread and stage");
+    if (n_stages > 0) {
+        SK_FETCH(0);
+        SK_STASH(0);
     }
-    for (; t < n_tiles; t += kWaves) {
-        const int t2 = min(t + 2 * kWaves, last);
-        bf16x8 B2[DK];
+    __syncthreads();
+    for (int s = 0; s < n_stages; ++s) {
+        const int buf = s & 1;
+        if (s + 1 < n_stages)
+            SK_FETCH(s + 1);   // in flight while this stage is consumed
+#pragma unroll 1
+        for (int tt = 0; tt < kStageTiles; ++tt) {
+            bf16x8 Bv[DK];
 #pragma unroll
-        for (int kb = 0; kb < DK; ++kb)
-            B2[kb] = load_bf16x8(key_ptr(t2) + 32 * kb);
-        const float b2 = kb_[t2 * kKeys + c16];
-        __builtin_amdgcn_sched_barrier(0);
+            for (int kb = 0; kb < DK; ++kb)
+                Bv[kb] = __builtin_bit_cast(
+                    bf16x8, kbuf[buf][(tt * kKeys + c16) * kStride + 4 * kb + kq]);
+            const float be = bbuf[buf][tt * kKeys + c16];
 #pragma unroll
-        for (int g = 0; g < kGroups; ++g) {
-            f32x4 D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][0], B0[0], Cn[g], 0, 0, 0);
+            for (int g = 0; g < kGroups; ++g) {
+                f32x4 D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][0], Bv[0], Cn[g], 0, 0, 0);
 #pragma unroll
-            for (int kb = 1; kb < DK; ++kb)
-                D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][kb], B0[kb], D, 0, 0, 0);
+                for (int kb = 1; kb < DK; ++kb)
+                    D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][kb], Bv[kb], D, 0, 0, 0);
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                S[g][r] += ex2(fmaf(two_c, D[r], b0));
+                for (int r = 0; r < 4; ++r)
+                    S[g][r] += ex2(fmaf(two_c, D[r], be));
+            }
         }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int kb = 0; kb < DK; ++kb) {
-            B0[kb] = B1[kb];
-            B1[kb] = B2[kb];
-        }
-        b0 = b1;
-        b1 = b2;
+        if (s + 1 < n_stages)
+            SK_STASH(buf ^ 1);
+        __syncthreads();
     }
+#undef SK_FETCH
+#undef SK_STASH
+#undef SK_LOAD
+#undef SK_PUT
+#undef SK_CHUNK
 #pragma unroll
     for (int g = 0; g < kGroups; ++g)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const float Sr = row16_sum(S[g][r]);
-            if (c16 == 0)
-                red[w][16 * g + 4 * kq + r] = make_float2(Cn[g][r], Sr);
+            const int row = row0 + 16 * g + 4 * kq + r;
+            if (c16 == 0 && row < nq_pad)
+                part[((size_t)split * gridDim.z + b) * nq_pad + row] = Sr;
         }
-    __syncthreads();
-    if (w != 0)
-        return;
+}
+
+// Sum of the splits' partials per row (fixed order), potentials and biases; a
+// 64-row block with a sum out of range is flagged and left unchanged.
+__global__ __launch_bounds__(kWave) void lseFm_finalize(
+    float *__restrict__ qbias, float *__restrict__ qpot, const float *__restrict__ ql2w,
+    const float *__restrict__ qsq, const float *__restrict__ part, int *__restrict__ redo_out,
+    int B, int nq, int nq_pad, int splits, float two_c, double eps_ln2, double c_next)
+{
+    const int b = blockIdx.y;
+    const int row = blockIdx.x * kWave + lane_id();
     float Ssum = 0.f;
-#pragma unroll
-    for (int v = 0; v < kWaves; ++v)
-        Ssum += red[v][lane].y;
-    const int row = row0 + lane;
+    for (int s = 0; s < splits; ++s)
+        Ssum += part[((size_t)s * B + b) * nq_pad + row];
     const bool bad = row < nq && !(Ssum >= kSumLo && Ssum <= kSumHi);
-    // wave 0 alone decides for the block; the other waves have left
     const int flag = __builtin_amdgcn_readfirstlane(__ballot(bad) != 0 ? 1 : 0);
-    if (lane == 0)
+    if (lane_id() == 0)
         redo_out[b * gridDim.x + blockIdx.x] = flag;
     if (flag || row >= nq)
         return;
     const size_t k = (size_t)b * nq + row;
-    const double sq = (double)qsq[k];
-    // effective shift: s - M = 2c (x.y + Cn) + beta, so M = -2c Cn
-    const double M = -2.0 * (0.5 * (double)two_c) * (double)red[0][lane].x;
+    const float sqf = qsq[k];
+    const double sq = (double)sqf;
+    // the shift the partial kernels used: s - M = 2c (x.y + Cn) + beta, M = -2c Cn
+    const float Cn = -0.5f * (sqf - qpot[k]);
+    const double M = -2.0 * (0.5 * (double)two_c) * (double)Cn;
     const double lse2 = M + (double)lg2(Ssum);
     const float f = (float)(sq - lse2 * eps_ln2);
     qpot[k] = f;
-    qbias[(size_t)b * nq_pad + row] = bias_of(c_next, f, (float)sq, ql2w[k]);
+    qbias[(size_t)b * nq_pad + row] = bias_of(c_next, f, sqf, ql2w[k]);
 }
 
 // Transport cost for the bf16 matrix-core path, streamed like a half-
@@ -491,18 +556,39 @@ void launch_lseF_t(SideF q, SideF k, int d, int B, float two_c, double eps_ln2,
     }
 }
 
+// Key splits of the matrix-core pass: about as many waves as the chip holds at
+// once (4096: 4 per SIMD), rounded down so that the launch is one round, with
+// at least two stages of keys per split.
+int lseFm_splits(int B, int nq_pad, int nk_pad)
+{
+    const long groups = (long)B * ceil_div(nq_pad / kWave, kShareWaves);
+    const int tiles = nk_pad / kKeys;
+    int splits = (int)(4096 / kShareWaves / groups);
+    const int max_splits = tiles / (2 * kStageTiles);
+    if (splits > max_splits)
+        splits = max_splits;
+    return splits < 1 ? 1 : splits;
+}
+
 template <int DK>
 void launch_lseFm_t(SideF q, SideF k, int B, float two_c, double eps_ln2, double c_next,
-                    hipStream_t st)
+                    float *part, hipStream_t st)
 {
-    dim3 grid(q.n_pad / kWave, 1, B);
-    hipLaunchKernelGGL((lseFm_kernel<DK>), grid, dim3(kWaves * kWave), 0, st,
-                       (const uint16_t *)q.pts, q.bias, q.pot, (const float *)q.l2w,
-                       (const float *)q.sq, q.redo, (const uint16_t *)k.pts,
-                       (const float *)k.bias, q.n, q.n_pad, k.n, k.n_pad, two_c, eps_ln2, c_next);
-    // fallback for flagged row blocks: the vector kernel, same block shape
+    const int splits = lseFm_splits(B, q.n_pad, k.n_pad);
+    const int tps = ceil_div(k.n_pad / kKeys, splits);
+    dim3 grid(ceil_div(q.n_pad / kWave, kShareWaves), splits, B);
+    hipLaunchKernelGGL((lseFm_kernel<DK>), grid, dim3(kShareWaves * kWave), 0, st,
+                       (const uint16_t *)q.pts, (const float *)q.pot, (const float *)q.sq,
+                       (const uint16_t *)k.pts, (const float *)k.bias, part, q.n, q.n_pad, k.n,
+                       k.n_pad, tps, two_c);
+    dim3 g2(q.n_pad / kWave, B);
+    hipLaunchKernelGGL(lseFm_finalize, g2, dim3(kWave), 0, st, q.bias, q.pot,
+                       (const float *)q.l2w, (const float *)q.sq, (const float *)part, q.redo, B,
+                       q.n, q.n_pad, splits, two_c, eps_ln2, c_next);
+    // fallback for flagged row blocks: the vector kernel
     constexpr int DP = 32 * DK;
-    hipLaunchKernelGGL((lseF_kernel<uint16_t, DP>), grid, dim3(kWaves * kWave), 0, st,
+    dim3 g3(q.n_pad / kWave, 1, B);
+    hipLaunchKernelGGL((lseF_kernel<uint16_t, DP>), g3, dim3(kWaves * kWave), 0, st,
                        (const uint16_t *)q.pts, q.bias, q.pot, (const float *)q.l2w,
                        (const uint16_t *)k.pts, (const float *)k.bias, (float2 *)nullptr,
                        (const int *)q.redo, DP, q.n, q.n_pad, k.n, k.n_pad,
@@ -559,10 +645,14 @@ hipError_t launch_costFm(SideF x, SideF y, int d, int B, float eps, double *row_
     return hipGetLastError();
 }
 
+// float2 slots of partial-state workspace: the vector path's split (M, S) states
+// or the matrix-core path's split sums (one float each), whichever is larger
 size_t lseF_partial_floats2(int B, int nq_pad, int nk_pad)
 {
     const int s = lseF_splits(B, nq_pad, nk_pad);
-    return s > 1 ? (size_t)s * B * nq_pad : 0;
+    const size_t vec = s > 1 ? (size_t)s * B * nq_pad : 0;
+    const size_t mat = ((size_t)lseFm_splits(B, nq_pad, nk_pad) * B * nq_pad + 1) / 2;
+    return vec > mat ? vec : mat;
 }
 
 hipError_t launch_packF(const void *X, int dtype, int d, const float *w, int warm, int B,
@@ -587,10 +677,10 @@ hipError_t launch_lseF(SideF q, SideF k, int dtype, int d, int B, float eps, flo
     const double eps_ln2 = 1.0 / (double)c;
     if (use_matrix_cores(q, k, dtype, d, B)) {
         switch (d / 32) {
-        case 1: launch_lseFm_t<1>(q, k, B, 2.0f * c, eps_ln2, c_next, st); break;
-        case 2: launch_lseFm_t<2>(q, k, B, 2.0f * c, eps_ln2, c_next, st); break;
-        case 3: launch_lseFm_t<3>(q, k, B, 2.0f * c, eps_ln2, c_next, st); break;
-        default: launch_lseFm_t<4>(q, k, B, 2.0f * c, eps_ln2, c_next, st); break;
+        case 1: launch_lseFm_t<1>(q, k, B, 2.0f * c, eps_ln2, c_next, (float *)part, st); break;
+        case 2: launch_lseFm_t<2>(q, k, B, 2.0f * c, eps_ln2, c_next, (float *)part, st); break;
+        case 3: launch_lseFm_t<3>(q, k, B, 2.0f * c, eps_ln2, c_next, (float *)part, st); break;
+        default: launch_lseFm_t<4>(q, k, B, 2.0f * c, eps_ln2, c_next, (float *)part, st); break;
         }
     } else if (dtype == 1)
         dispatch<uint16_t>(q, k, d, B, 2.0f * c, eps_ln2, c_next, part, st);
