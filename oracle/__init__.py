@@ -39,6 +39,10 @@ PINS = {
     "plan_stats": "dense numpy enumeration; strong duality at convergence",
     "plan_coo": "dense numpy enumeration on small shapes",
     "loss_grad": "finite differences of the dual (envelope theorem); dense sums",
+    "normalize": "unit norms, direction and scale invariance; cosine cost matrix 2 - 2 x.y"
+                 " from numpy with scipy logsumexp for one update",
+    "normalize_backward": "finite differences of a function of the normalised points;"
+                          " orthogonality to the point",
     "dense_grad": "finite differences of the dual (envelope theorem); assignment limit of"
                   " the projection at small eps; product-plan limit at large eps; row mass"
                   " after an f-update; translation",
@@ -81,6 +85,10 @@ def _load():
         lib.oracle_dense_grad.argtypes = [P, P, P, P, P, P, f64, i32, i32, i32, i32, P, i64,
                                           P, P, P]
         lib.oracle_dense_grad.restype = None
+        lib.oracle_normalize.argtypes = [P, i64, i32, P, P]
+        lib.oracle_normalize.restype = None
+        lib.oracle_normalize_backward.argtypes = [P, P, P, i64, i32, P]
+        lib.oracle_normalize_backward.restype = None
         _lib = lib
     return _lib
 
@@ -229,3 +237,25 @@ def dense_grad(X, Y, a, b, f, g, eps, sel=None):
     if sel is None:
         return r.reshape(B, n), dX.reshape(B, n, d), T.reshape(B, n, d)
     return r, dX, T
+
+
+def normalize(X):
+    """(Xh, norms): points scaled to unit length (zero vectors stay 0), any leading shape."""
+    lib = _load()
+    X = _d(X)
+    d = X.shape[-1]
+    count = X.size // d
+    out = np.empty_like(X)
+    norms = np.empty(X.shape[:-1])
+    lib.oracle_normalize(_p(X), count, d, _p(out), _p(norms))
+    return out, norms
+
+
+def normalize_backward(Xh, norms, G):
+    """dX = (G - xh (xh . G)) / ||x||, the gradient through x -> x / ||x||."""
+    lib = _load()
+    Xh, norms, G = _d(Xh), _d(norms), _d(G)
+    d = Xh.shape[-1]
+    dX = np.empty_like(Xh)
+    lib.oracle_normalize_backward(_p(Xh), _p(norms), _p(G), Xh.size // d, d, _p(dX))
+    return dX

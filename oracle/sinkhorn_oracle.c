@@ -530,3 +530,43 @@ void oracle_dense_grad(const double *X, const double *Y, const double *a, const 
         free(V);
     }
 }
+
+/*
+ * Cosine cost on normalised vectors [FS Betekenis en Claims: the approach
+ * applies to the cosine distance after normalisation].  For unit vectors
+ * 2 - 2 xh . yh = ||xh - yh||^2, so the squared-Euclidean routines above give
+ * the cosine-cost problem on the normalised points.
+ *   out_i = x_i / ||x_i||, norms_i = ||x_i||   (out_i = 0 for a zero vector)
+ */
+void oracle_normalize(const double *X, int64_t count, int d, double *out, double *norms)
+{
+    for (int64_t i = 0; i < count; ++i) {
+        const double *x = X + (size_t)i * d;
+        double s = 0.0;
+        for (int k = 0; k < d; ++k)
+            s += x[k] * x[k];
+        const double r = sqrt(s);
+        norms[i] = r;
+        for (int k = 0; k < d; ++k)
+            out[(size_t)i * d + k] = r > 0.0 ? x[k] / r : 0.0;
+    }
+}
+
+/*
+ * Chain rule through the normalisation: with G the gradient with respect to
+ * the normalised point xh = x / ||x||,
+ *   dX_i = (G_i - xh_i (xh_i . G_i)) / ||x_i||     (0 for a zero vector),
+ * the Jacobian of x / ||x|| being (I - xh xh^T) / ||x||.
+ */
+void oracle_normalize_backward(const double *Xh, const double *norms, const double *G,
+                               int64_t count, int d, double *dX)
+{
+    for (int64_t i = 0; i < count; ++i) {
+        const double *xh = Xh + (size_t)i * d, *g = G + (size_t)i * d;
+        double dot = 0.0;
+        for (int k = 0; k < d; ++k)
+            dot += xh[k] * g[k];
+        for (int k = 0; k < d; ++k)
+            dX[(size_t)i * d + k] = norms[i] > 0.0 ? (g[k] - xh[k] * dot) / norms[i] : 0.0;
+    }
+}

@@ -75,7 +75,11 @@ __global__ void log_weights_kernel(const float *__restrict__ w, int count, size_
 }
 
 // log P_ij (nats) and C_ij for a row context and column j of one pair.  Written
-// with explicit fma so that every pass evaluates it with the same roundings.
+// with explicit fma so that every pass evaluates it with the same roundings,
+// and symmetric in the two sides (f_i + g_j, (x - y)^2 = (y - x)^2 and
+// log a_i + log b_j all round the same either way), so a pass over the plan
+// with the roles of X and Y exchanged sees bit-identical values: the sparse
+// plan of (Y, X) is exactly the transpose of that of (X, Y).
 template <typename T, int DP>
 __device__ __forceinline__ double log_plan(const RowCtx<DP> &r, const PlanArgs &p,
                                            const T *Yb, const float *gb, double lbj, int j,
@@ -83,7 +87,7 @@ __device__ __forceinline__ double log_plan(const RowCtx<DP> &r, const PlanArgs &
 {
     const double c = sq_dist<T, DP>(r.x, Yb + (size_t)j * p.d, p.d);
     *C = c;
-    return fma((r.f + (double)gb[j]) - c, p.inv_eps, r.la) + lbj;
+    return fma((r.f + (double)gb[j]) - c, p.inv_eps, r.la + lbj);
 }
 
 template <typename T, int DP>

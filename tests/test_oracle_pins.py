@@ -413,3 +413,85 @@ def test_dense_grad_matches_full_support_coo_gradient():
     loss, dXc = oracle.loss_grad(X, Y, rows, cols, vals, offs)
     r, dX, T = oracle.dense_grad(X, Y, a, b, f, g, eps)
     np.testing.assert_allclose(dX, dXc, rtol=1e-12, atol=1e-15)
+
+
+# ------------------------------------------ cosine cost on normalised vectors
+def test_normalize_gives_unit_vectors_along_the_input():
+    rng = np.random.default_rng(3)
+    X = rng.normal(size=(4, 30, 7))
+    X[1, 5] = 0.0
+    Xh, nr = oracle.normalize(X)
+    live = nr > 0
+    np.testing.assert_allclose(np.linalg.norm(Xh, axis=-1)[live], 1.0, rtol=1e-15)
+    np.testing.assert_array_equal(Xh[1, 5], 0.0)
+    np.testing.assert_allclose(Xh * nr[..., None], X, rtol=1e-14, atol=1e-15)
+    # scaling a point by a positive factor leaves its direction unchanged
+    Xh2, nr2 = oracle.normalize(X * 3.5)
+    np.testing.assert_allclose(Xh2, Xh, rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(nr2, 3.5 * nr, rtol=1e-14)
+
+
+def test_cosine_cost_update_matches_scipy_on_the_cosine_matrix():
+    # the squared-Euclidean update on normalised points is the update of the
+    # cosine cost 2 - 2 xh.yh, computed here directly with numpy and scipy
+    rng = np.random.default_rng(8)
+    X, Y = rng.normal(size=(40, 16)), rng.normal(size=(33, 16)) * 5.0
+    Xh, _ = oracle.normalize(X)
+    Yh, _ = oracle.normalize(Y)
+    g = rng.normal(scale=0.1, size=33)
+    b = rng.dirichlet(np.ones(33))
+    eps = 0.05
+    f = oracle.half_update(Xh, Yh, g, b, eps)
+    C = 2.0 - 2.0 * (X / np.linalg.norm(X, axis=1, keepdims=True)) @ \
+        (Y / np.linalg.norm(Y, axis=1, keepdims=True)).T
+    ref = -eps * logsumexp((g[None, :] - C) / eps, b=b[None, :], axis=1)
+    np.testing.assert_allclose(f, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_normalize_backward_is_the_derivative_of_the_normalisation():
+    rng = np.random.default_rng(9)
+    X = rng.normal(size=(6, 5))
+    W = rng.normal(size=(6, 5))
+    Xh, nr = oracle.normalize(X)
+    dX = oracle.normalize_backward(Xh, nr, W)      # d/dX of sum(W * X/||X||)
+    h = 1e-6
+    fd = np.zeros_like(X)
+    for i in range(6):
+        for k in range(5):
+            Xp, Xm = X.copy(), X.copy()
+            Xp[i, k] += h
+            Xm[i, k] -= h
+            fd[i, k] = ((W * oracle.normalize(Xp)[0]).sum()
+                        - (W * oracle.normalize(Xm)[0]).sum()) / (2 * h)
+    np.testing.assert_allclose(dX, fd, rtol=1e-7, atol=1e-9)
+    np.testing.assert_allclose((dX * X).sum(-1), 0.0, atol=1e-12)   # orthogonal to x
+
+
+def test_y_gradient_from_the_transposed_sparse_plan():
+    # the COO of (Y, X, b, a, g, f) is the transpose of that of (X, Y, a, b, f, g); its
+    # row-segment gradient is dL/dY = sum_i 2 P_ij (y_j - x_i), checked against finite
+    # differences of the converged dual in y
+    X, Y, a, b = _case(37, 10, 8)
+    eps, iters = 0.1, 3000
+    f, g = _converge(X, Y, a, b, eps, iters)
+    r1, c1, v1, o1 = oracle.plan_coo(X, Y, a, b, f, g, eps, rel_thr=1e-300)
+    r2, c2, v2, o2 = oracle.plan_coo(Y, X, b, a, g, f, eps, rel_thr=1e-300)
+    order = np.lexsort((r1, c1))        # CSR entries in column-major order
+    np.testing.assert_array_equal(r2, c1[order])
+    np.testing.assert_array_equal(c2, r1[order])
+    np.testing.assert_allclose(v2, v1[order], rtol=1e-14)
+    _, dY = oracle.loss_grad(Y, X, r2, c2, v2, o2)
+
+    def ot_value(Yv):
+        fv, gv = oracle.potentials(X, Yv, a, b, eps=[eps], iters=[iters])
+        return float(a @ fv + b @ gv)
+
+    h = 1e-5
+    fd = np.zeros_like(Y)
+    for j in range(Y.shape[0]):
+        for k in range(3):
+            Yp, Ym = Y.copy(), Y.copy()
+            Yp[j, k] += h
+            Ym[j, k] -= h
+            fd[j, k] = (ot_value(Yp) - ot_value(Ym)) / (2 * h)
+    np.testing.assert_allclose(dY[0], fd, rtol=1e-6, atol=1e-8)
