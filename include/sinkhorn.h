@@ -180,6 +180,26 @@ int sinkhorn_dense_grad(const void *X, const void *Y, int dtype,
                         float *dX, float *TX, float *dY, float *TY,
                         void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * Cosine cost on normalised vectors [FS Betekenis en Claims: the approach
+ * applies to the cosine distance after normalisation].  For unit vectors
+ * ||x^ - y^||^2 = 2 - 2 x^ . y^, so every entry point above, given the
+ * normalised points, computes under the cosine cost; a gradient they return
+ * (dX of sinkhorn_loss_grad or sinkhorn_dense_grad) is with respect to the
+ * normalised points and sinkhorn_normalize_backward carries it to the raw ones.
+ *
+ * sinkhorn_normalize: Xh[B][n][d] = x / ||x|| (fp32), norms[B][n] = ||x||
+ * (fp32), from X in `dtype` (SK_F32 or SK_BF16, any 1 <= d <= 4096); a zero
+ * vector gives Xh = 0 and norm 0.  Norm and quotient in fp64, rounded once.
+ * sinkhorn_normalize_backward: dX = (G - x^ (x^ . G)) / ||x|| for every point,
+ * from Xh and norms as written above and G[B][n][d] (fp32); 0 for a zero
+ * vector.  Both only enqueue work; no workspace.
+ */
+int sinkhorn_normalize(const void *X, int dtype, int B, int n, int d,
+                       float *Xh, float *norms, void *stream);
+int sinkhorn_normalize_backward(const float *Xh, const float *norms, const float *G,
+                                int B, int n, int d, float *dX, void *stream);
+
 /* Static text for a return code. */
 const char *sinkhorn_status_string(int status);
 

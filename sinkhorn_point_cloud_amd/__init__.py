@@ -32,8 +32,8 @@ SK_WARM_START = 1
 SK_VALU_SCORES = 2
 
 EXPORTS = ("sinkhorn_workspace_bytes", "sinkhorn_potentials", "sinkhorn_plan_coo",
-           "sinkhorn_loss_grad", "sinkhorn_dense_grad", "sinkhorn_status_string",
-           "sinkhorn_last_error")
+           "sinkhorn_loss_grad", "sinkhorn_dense_grad", "sinkhorn_normalize",
+           "sinkhorn_normalize_backward", "sinkhorn_status_string", "sinkhorn_last_error")
 
 
 class SinkhornError(RuntimeError):
@@ -71,6 +71,10 @@ def load_library():
     lib.sinkhorn_loss_grad.restype = I
     lib.sinkhorn_dense_grad.argtypes = [P, P, I, P, P, I, I, I, I, F, P, P, P, P, P, P, P, Z, P]
     lib.sinkhorn_dense_grad.restype = I
+    lib.sinkhorn_normalize.argtypes = [P, I, I, I, I, P, P, P]
+    lib.sinkhorn_normalize.restype = I
+    lib.sinkhorn_normalize_backward.argtypes = [P, P, P, I, I, I, P, P]
+    lib.sinkhorn_normalize_backward.restype = I
     lib.sinkhorn_status_string.argtypes = [I]
     lib.sinkhorn_status_string.restype = ctypes.c_char_p
     lib.sinkhorn_last_error.argtypes = []
@@ -277,3 +281,33 @@ def dense_grad(X, Y, a, b, f, g, eps: float, sides: str = "xy", workspace=None, 
                                  _ptr(ws), ws.numel(), _stream())
     _check(rc)
     return dX, TX, dY, TY
+
+
+def normalize(X):
+    """(Xh, norms): points of X [B,n,d] (fp32 or bf16) scaled to unit length, float32.
+    With the normalised clouds every other call works under the cosine cost."""
+    lib = load_library()
+    if not X.is_cuda:
+        raise ValueError("X must be a CUDA tensor")
+    X = X.contiguous()
+    if X.dim() == 2:
+        X = X[None]
+    dt = {torch.float32: SK_F32, torch.bfloat16: SK_BF16}.get(X.dtype)
+    if dt is None:
+        raise TypeError("X must be float32 or bfloat16")
+    B, n, d = X.shape
+    Xh = torch.empty(B, n, d, dtype=torch.float32, device=X.device)
+    norms = torch.empty(B, n, dtype=torch.float32, device=X.device)
+    _check(lib.sinkhorn_normalize(_ptr(X), dt, B, n, d, _ptr(Xh), _ptr(norms), _stream()))
+    return Xh, norms
+
+
+def normalize_backward(Xh, norms, G):
+    """Gradient with respect to the raw points from G, the gradient with respect to Xh."""
+    lib = load_library()
+    Xh, norms, G = Xh.contiguous(), norms.contiguous(), G.contiguous().float()
+    B, n, d = Xh.shape
+    dX = torch.empty_like(Xh)
+    _check(lib.sinkhorn_normalize_backward(_ptr(Xh), _ptr(norms), _ptr(G), B, n, d, _ptr(dX),
+                                           _stream()))
+    return dX

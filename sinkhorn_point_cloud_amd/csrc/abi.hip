@@ -27,6 +27,7 @@ int hip_fail(hipError_t e, const char *where)
 }
 
 constexpr int kMaxPoints = 1 << 24;
+constexpr int kMaxNormDim = 4096;   // dimensions accepted by the normalisation
 constexpr int kPad = 64;
 
 // Bump allocator over the caller's workspace (256-byte aligned pieces).
@@ -466,6 +467,32 @@ int sinkhorn_dense_grad(const void *X, const void *Y, int dtype, const float *a,
     if (want_y && (e = launch_dense_grad(py, dY, TY, nullptr, st)))
         return hip_fail(e, "dense gradient (Y side)");
     return SK_OK;
+}
+
+int sinkhorn_normalize(const void *X, int dtype, int B, int n, int d, float *Xh, float *norms,
+                       void *stream)
+{
+    g_err[0] = '\0';
+    if (!X || !Xh || !norms)
+        return fail(SK_ERR_INVALID_ARG, "X, Xh and norms must be non-NULL device pointers");
+    if (dtype != SK_F32 && dtype != SK_BF16)
+        return fail(SK_ERR_INVALID_ARG, "dtype %d is neither SK_F32 nor SK_BF16", dtype);
+    if (B < 1 || n < 1 || d < 1 || d > kMaxNormDim || (long long)B * n > (1ll << 31))
+        return fail(SK_ERR_INVALID_ARG, "bad sizes B=%d n=%d d=%d", B, n, d);
+    hipError_t e = launch_normalize(X, dtype, (long)B * n, d, Xh, norms, (hipStream_t)stream);
+    return e ? hip_fail(e, "normalize") : SK_OK;
+}
+
+int sinkhorn_normalize_backward(const float *Xh, const float *norms, const float *G, int B, int n,
+                                int d, float *dX, void *stream)
+{
+    g_err[0] = '\0';
+    if (!Xh || !norms || !G || !dX)
+        return fail(SK_ERR_INVALID_ARG, "Xh, norms, G and dX must be non-NULL device pointers");
+    if (B < 1 || n < 1 || d < 1 || d > kMaxNormDim || (long long)B * n > (1ll << 31))
+        return fail(SK_ERR_INVALID_ARG, "bad sizes B=%d n=%d d=%d", B, n, d);
+    hipError_t e = launch_normalize_backward(Xh, norms, G, (long)B * n, d, dX, (hipStream_t)stream);
+    return e ? hip_fail(e, "normalize backward") : SK_OK;
 }
 
 }  // extern "C"

@@ -210,6 +210,12 @@ hipError_t launch_gradFm(const SideF &rows, const float *row_w, const SideF &key
                          float *proj, hipStream_t st);
 hipError_t launch_transpose_bf16(const void *X, int B, int n, int n_pad, int d, uint16_t *Xt,
                                  hipStream_t st);
+// Cosine cost support: points to unit length (fp32 out, norms kept), and the
+// gradient through that map.
+hipError_t launch_normalize(const void *X, int dtype, long count, int d, float *Xh,
+                            float *norms, hipStream_t st);
+hipError_t launch_normalize_backward(const float *Xh, const float *norms, const float *G,
+                                     long count, int d, float *dX, hipStream_t st);
 
 hipError_t launch_loss_grad(const void *X, const void *Y, int dtype, int d, int B, int n,
                             int m, const int32_t *rows, const int32_t *cols, const float *vals,

@@ -163,6 +163,21 @@ def test_dense_grad_rejects_bad_arguments_without_writing(lib, kw, code):
     assert np.all(dX == 7.0)
 
 
+@pytest.mark.parametrize("kw", [dict(X=None), dict(dtype=3), dict(B=0), dict(d=0), dict(d=5000),
+                                dict(out=None)])
+def test_normalize_rejects_bad_arguments_without_writing(lib, kw):
+    args = dict(X=DUMMY, dtype=0, B=1, n=4, d=3, out=True)
+    args.update(kw)
+    xh = np.full(12, 3.0, dtype=np.float32)
+    nr = np.full(4, 3.0, dtype=np.float32)
+    rc = lib.sinkhorn_normalize(args["X"], args["dtype"], args["B"], args["n"], args["d"],
+                                _host(xh) if args["out"] else None, _host(nr), None)
+    assert rc == sk.SK_ERR_INVALID_ARG, lib.sinkhorn_last_error()
+    assert np.all(xh == 3.0) and np.all(nr == 3.0)
+    rc = lib.sinkhorn_normalize_backward(DUMMY, DUMMY, None, 1, 4, 3, _host(xh), None)
+    assert rc == sk.SK_ERR_INVALID_ARG and np.all(xh == 3.0)
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     X = torch.zeros(1, 4, 3)

@@ -467,3 +467,85 @@ def test_dense_grad_matrix_core_fallback_block():
     for rows, tol in ((slice(0, 64), 1e-3), (slice(64, 128), 1e-5), (slice(128, 200), 1e-3)):
         assert rel_inf(host(dX)[0, rows], dX_o[0, rows]) <= tol
         assert np.abs(host(TX)[0, rows] - T_o[0, rows]).max() <= tol
+
+
+# ------------------------------------------- cosine cost and the Y-side gradient
+@pytest.mark.parametrize("dtype,d", [("f32", 3), ("bf16", 64), ("f32", 300)])
+def test_normalize_and_backward_match_oracle(dtype, d):
+    c = workloads.random_case(15, 2, 70, 5, d, dtype=dtype, spread=4.0)
+    X = c["X"].copy()
+    X[0, 3] = 0.0                                   # a zero vector stays zero
+    Xd = dev(X) if dtype == "f32" else \
+        dev(workloads.bf16_round(X).view(np.int16)).view(torch.bfloat16)
+    Xh, nr = sk.normalize(Xd)
+    G = np.random.default_rng(2).normal(size=X.shape).astype(np.float32)
+    dX = sk.normalize_backward(Xh, nr, dev(G))
+    torch.cuda.synchronize()
+    Xh_o, nr_o = oracle.normalize(X)
+    np.testing.assert_allclose(host(Xh), Xh_o, rtol=0, atol=1e-7)
+    np.testing.assert_allclose(host(nr), nr_o, rtol=1e-7)
+    dX_o = oracle.normalize_backward(Xh_o, nr_o, G)
+    assert rel_inf(host(dX), dX_o) <= 1e-6
+    assert np.all(host(Xh)[0, 3] == 0) and np.all(host(dX)[0, 3] == 0)
+
+
+@pytest.mark.parametrize("d,eps", [(3, 0.02), (16, 0.05)])
+def test_cosine_cost_chain_matches_oracle(d, eps):
+    # raw clouds -> normalised -> potentials -> sparse plan -> loss and dL/dX with
+    # respect to the raw points, on both sides
+    c = workloads.random_case(16, 2, 150, 130, d, weights="dirichlet", spread=3.0)
+    X, Y, a, b = dev(c["X"]), dev(c["Y"]), dev(c["a"]), dev(c["b"])
+    Xh, nx = sk.normalize(X)
+    Yh, ny = sk.normalize(Y)
+    f, g, cost = sk.potentials(Xh, Yh, a, b, eps=[eps], iters=[25])
+    Xh_o, nx_o = oracle.normalize(c["X"])
+    Yh_o, ny_o = oracle.normalize(c["Y"])
+    fo, go = oracle.potentials(Xh_o, Yh_o, c["a"], c["b"], eps=[np.float32(eps)], iters=[25])
+    torch.cuda.synchronize()
+    for p in range(2):
+        assert rel_inf(host(f)[p], fo[p], eps) <= 1e-4
+        assert rel_inf(host(g)[p], go[p], eps) <= 1e-4
+    st = oracle.plan_stats(Xh_o, Yh_o, c["a"], c["b"], fo, go, float(np.float32(eps)))
+    np.testing.assert_allclose(host(cost), st["cost"], rtol=1e-4)
+    # sparse plan and gradients from the oracle's potentials, on both sides
+    f32, g32 = fo.astype(np.float32), go.astype(np.float32)
+    rows, cols, vals, offs = sk.plan_coo(Xh, Yh, a, b, dev(f32), dev(g32), eps, 1e-8)
+    loss, dXh = sk.loss_grad(Xh, Yh, rows, cols, vals, offs)
+    dX = sk.normalize_backward(Xh, nx, dXh)
+    torch.cuda.synchronize()
+    ro, co, vo, oo = oracle.plan_coo(Xh_o, Yh_o, c["a"], c["b"], f32.astype(np.float64),
+                                     g32.astype(np.float64), float(np.float32(eps)), 1e-8)
+    lo, dXh_o = oracle.loss_grad(Xh_o, Yh_o, ro, co, vo, oo)
+    dX_o = oracle.normalize_backward(Xh_o, nx_o, dXh_o)
+    np.testing.assert_allclose(host(loss), lo, rtol=1e-4)
+    for p in range(2):
+        assert rel_inf(host(dX)[p], dX_o[p]) <= 1e-4
+
+
+def test_transposed_sparse_plan_and_y_gradient():
+    c = workloads.random_case(17, 2, 260, 300, 3, weights="dirichlet")
+    eps = 0.02
+    fo, go = oracle.potentials(c["X"], c["Y"], c["a"], c["b"], eps=[eps], iters=[15])
+    X, Y, a, b = dev(c["X"]), dev(c["Y"]), dev(c["a"]), dev(c["b"])
+    f32, g32 = dev(fo.astype(np.float32)), dev(go.astype(np.float32))
+    r1, c1, v1, o1 = sk.plan_coo(X, Y, a, b, f32, g32, eps, 1e-8)
+    r2, c2, v2, o2 = sk.plan_coo(Y, X, b, a, g32, f32, eps, 1e-8)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    R1, C1, V1, O1 = (t.cpu().numpy() for t in (r1, c1, v1, o1))
+    R2, C2, V2 = (t.cpu().numpy() for t in (r2, c2, v2))
+    for p in range(2):
+        s1, s2 = slice(O1[p], O1[p + 1]), slice(O1[p], O1[p + 1])
+        order = np.lexsort((R1[s1], C1[s1]))
+        # exactly the transpose: same entries, bit-identical values
+        np.testing.assert_array_equal(R2[s2], C1[s1][order])
+        np.testing.assert_array_equal(C2[s2], R1[s1][order])
+        np.testing.assert_array_equal(V2[s2], V1[s1][order])
+    _, dY = sk.loss_grad(Y, X, r2, c2, v2, o2)
+    torch.cuda.synchronize()
+    ro, co, vo, oo = oracle.plan_coo(c["Y"], c["X"], c["b"], c["a"],
+                                     go.astype(np.float32).astype(np.float64),
+                                     fo.astype(np.float32).astype(np.float64), eps, 1e-8)
+    _, dY_o = oracle.loss_grad(c["Y"], c["X"], ro, co, vo, oo)
+    for p in range(2):
+        assert rel_inf(host(dY)[p], dY_o[p]) <= 1e-4
