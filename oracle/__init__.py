@@ -39,6 +39,9 @@ PINS = {
     "plan_stats": "dense numpy enumeration; strong duality at convergence",
     "plan_coo": "dense numpy enumeration on small shapes",
     "loss_grad": "finite differences of the dual (envelope theorem); dense sums",
+    "coo_normalize": "full support converges to the dense Sinkhorn plan; marginals at"
+                     " convergence; invariance to row and column scalings of the input;"
+                     " 2x2 closed form (cross-ratio kept)",
     "normalize": "unit norms, direction and scale invariance; cosine cost matrix 2 - 2 x.y"
                  " from numpy with scipy logsumexp for one update",
     "normalize_backward": "finite differences of a function of the normalised points;"
@@ -89,6 +92,8 @@ def _load():
         lib.oracle_normalize.restype = None
         lib.oracle_normalize_backward.argtypes = [P, P, P, i64, i32, P]
         lib.oracle_normalize_backward.restype = None
+        lib.oracle_coo_normalize.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, P]
+        lib.oracle_coo_normalize.restype = i32
         _lib = lib
     return _lib
 
@@ -259,3 +264,20 @@ def normalize_backward(Xh, norms, G):
     dX = np.empty_like(Xh)
     lib.oracle_normalize_backward(_p(Xh), _p(norms), _p(G), Xh.size // d, d, _p(dX))
     return dX
+
+
+def coo_normalize(rows, cols, vals, pair_offsets, a, b, n, m, iters):
+    """Sinkhorn normalisation of a COO plan on its support: (vals', err[B,2])."""
+    lib = _load()
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int32))
+    cols = np.ascontiguousarray(np.asarray(cols, dtype=np.int32))
+    vals = _d(vals).copy()
+    offs = np.ascontiguousarray(np.asarray(pair_offsets, dtype=np.int64))
+    B = offs.size - 1
+    a, b = _weights(a, B, n), _weights(b, B, m)
+    err = np.empty((B, 2))
+    rc = lib.oracle_coo_normalize(_p(rows), _p(cols), _p(vals), _p(offs), _p(a), _p(b), B, n, m,
+                                  int(iters), _p(err))
+    if rc != 0:
+        raise ValueError("oracle_coo_normalize: index out of range")
+    return vals, err

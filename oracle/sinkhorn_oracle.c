@@ -570,3 +570,96 @@ void oracle_normalize_backward(const double *Xh, const double *norms, const doub
             dX[(size_t)i * d + k] = norms[i] > 0.0 ? (g[k] - xh[k] * dot) / norms[i] : 0.0;
     }
 }
+
+/*
+ * Sinkhorn normalisation of a sparse plan on its stored support [AP Abstract,
+ * Innovation: Sinkhorn normalisation run directly in COO form].  For each pair
+ * p, with the entries k of the pair (any order, no duplicates) and
+ * lv_k = log vals_k, scalings alpha (rows) and beta (columns) start at 0 and
+ * each of `iters` rounds sets, in this order,
+ *   alpha_i = log a_i - LSE_{k in row i} (lv_k + beta_{col k})
+ *   beta_j  = log b_j - LSE_{k in col j} (lv_k + alpha_{row k})
+ * (a row or column with no entries, or whose LSE is -inf, keeps scaling 0);
+ * then vals_k <- exp(lv_k + alpha_{row k} + beta_{col k}).  Afterwards
+ * err[2p] = sum_i |row sum_i - a_i| and err[2p+1] = sum_j |col sum_j - b_j|
+ * over the rows and columns of the pair.  Returns 0, or -1 on an index out of
+ * range.
+ */
+int oracle_coo_normalize(const int32_t *rows, const int32_t *cols, double *vals,
+                         const int64_t *pair_offsets, const double *a, const double *b,
+                         int B, int n, int m, int iters, double *err)
+{
+    double *al = (double *)malloc(sizeof(double) * (size_t)n);
+    double *be = (double *)malloc(sizeof(double) * (size_t)m);
+    double *mx_r = (double *)malloc(sizeof(double) * (size_t)n);
+    double *sm_r = (double *)malloc(sizeof(double) * (size_t)n);
+    double *mx_c = (double *)malloc(sizeof(double) * (size_t)m);
+    double *sm_c = (double *)malloc(sizeof(double) * (size_t)m);
+    int rc = 0;
+    for (int p = 0; p < B && rc == 0; ++p) {
+        const int64_t k0 = pair_offsets[p], k1 = pair_offsets[p + 1];
+        const double *ap = a + (size_t)p * n, *bp = b + (size_t)p * m;
+        for (int64_t k = k0; k < k1; ++k)
+            if (rows[k] < 0 || rows[k] >= n || cols[k] < 0 || cols[k] >= m)
+                rc = -1;
+        if (rc)
+            break;
+        for (int i = 0; i < n; ++i)
+            al[i] = 0.0;
+        for (int j = 0; j < m; ++j)
+            be[j] = 0.0;
+        for (int it = 0; it < iters; ++it) {
+            /* rows */
+            for (int i = 0; i < n; ++i) {
+                mx_r[i] = -INFINITY;
+                sm_r[i] = 0.0;
+            }
+            for (int64_t k = k0; k < k1; ++k) {
+                const double z = log(vals[k]) + be[cols[k]];
+                if (z > mx_r[rows[k]])
+                    mx_r[rows[k]] = z;
+            }
+            for (int64_t k = k0; k < k1; ++k)
+                if (mx_r[rows[k]] > -INFINITY)
+                    sm_r[rows[k]] += exp(log(vals[k]) + be[cols[k]] - mx_r[rows[k]]);
+            for (int i = 0; i < n; ++i)
+                al[i] = mx_r[i] > -INFINITY ? log(ap[i]) - (mx_r[i] + log(sm_r[i])) : 0.0;
+            /* columns */
+            for (int j = 0; j < m; ++j) {
+                mx_c[j] = -INFINITY;
+                sm_c[j] = 0.0;
+            }
+            for (int64_t k = k0; k < k1; ++k) {
+                const double z = log(vals[k]) + al[rows[k]];
+                if (z > mx_c[cols[k]])
+                    mx_c[cols[k]] = z;
+            }
+            for (int64_t k = k0; k < k1; ++k)
+                if (mx_c[cols[k]] > -INFINITY)
+                    sm_c[cols[k]] += exp(log(vals[k]) + al[rows[k]] - mx_c[cols[k]]);
+            for (int j = 0; j < m; ++j)
+                be[j] = mx_c[j] > -INFINITY ? log(bp[j]) - (mx_c[j] + log(sm_c[j])) : 0.0;
+        }
+        for (int64_t k = k0; k < k1; ++k)
+            vals[k] = exp(log(vals[k]) + al[rows[k]] + be[cols[k]]);
+        if (err) {
+            for (int i = 0; i < n; ++i)
+                sm_r[i] = 0.0;
+            for (int j = 0; j < m; ++j)
+                sm_c[j] = 0.0;
+            for (int64_t k = k0; k < k1; ++k) {
+                sm_r[rows[k]] += vals[k];
+                sm_c[cols[k]] += vals[k];
+            }
+            double er = 0.0, ec = 0.0;
+            for (int i = 0; i < n; ++i)
+                er += fabs(sm_r[i] - ap[i]);
+            for (int j = 0; j < m; ++j)
+                ec += fabs(sm_c[j] - bp[j]);
+            err[2 * p] = er;
+            err[2 * p + 1] = ec;
+        }
+    }
+    free(al); free(be); free(mx_r); free(sm_r); free(mx_c); free(sm_c);
+    return rc;
+}

@@ -495,3 +495,53 @@ def test_y_gradient_from_the_transposed_sparse_plan():
             Ym[j, k] -= h
             fd[j, k] = (ot_value(Yp) - ot_value(Ym)) / (2 * h)
     np.testing.assert_allclose(dY[0], fd, rtol=1e-6, atol=1e-8)
+
+
+# ---------------------------------------- Sinkhorn normalisation in COO form
+def test_coo_normalisation_of_the_full_support_reaches_the_dense_solution():
+    # scaling the plan of early potentials on its full support converges to the
+    # unique plan with marginals a, b of the same Gibbs kernel: converged Sinkhorn
+    X, Y, a, b = _case(41, 18, 23)
+    eps = 0.1
+    f5, g5 = oracle.potentials(X, Y, a, b, eps=[eps], iters=[5])
+    rows, cols, vals, offs = oracle.plan_coo(X, Y, a, b, f5, g5, eps, rel_thr=1e-300)
+    assert len(rows) == 18 * 23
+    vn, err = oracle.coo_normalize(rows, cols, vals, offs, a, b, 18, 23, iters=3000)
+    assert err[0, 0] < 1e-12 and err[0, 1] < 1e-12
+    fc, gc = _converge(X, Y, a, b, eps, 3000)
+    _, _, vref, _ = oracle.plan_coo(X, Y, a, b, fc, gc, eps, rel_thr=1e-300)
+    np.testing.assert_allclose(vn, vref, rtol=1e-9)
+
+
+def test_coo_normalisation_ignores_row_and_column_scalings_of_its_input():
+    X, Y, a, b = _case(43, 30, 25)
+    eps = 0.03
+    f, g = oracle.potentials(X, Y, a, b, eps=[eps], iters=[8])
+    rows, cols, vals, offs = oracle.plan_coo(X, Y, a, b, f, g, eps, rel_thr=1e-6)
+    rng = np.random.default_rng(1)
+    ru, cv = rng.uniform(0.1, 10, 30), rng.uniform(0.1, 10, 25)
+    # the fixed point is unique on a support that admits the marginals
+    v1, e1 = oracle.coo_normalize(rows, cols, vals, offs, a, b, 30, 25, iters=3000)
+    v2, e2 = oracle.coo_normalize(rows, cols, vals * ru[rows] * cv[cols], offs, a, b, 30, 25,
+                                  iters=3000)
+    assert e1.max() < 1e-10 and e2.max() < 1e-10
+    np.testing.assert_allclose(v2, v1, rtol=1e-7)
+    # after a finite number of rounds the columns are exact (the last half-step)
+    _, e3 = oracle.coo_normalize(rows, cols, vals, offs, a, b, 30, 25, iters=3)
+    assert e3[0, 1] < 1e-13 < e3[0, 0]
+
+
+def test_coo_normalisation_two_by_two_closed_form():
+    # the scaled 2x2 matrix keeps the cross-ratio q11 q22 / (q12 q21) and has the
+    # marginals: with x = q11, x (1 - a1 - b1 + x) = rho (a1 - x)(b1 - x)
+    P = np.array([[0.3, 0.05], [0.2, 0.45]])
+    a, b = np.array([0.4, 0.6]), np.array([0.7, 0.3])
+    rows, cols = np.array([0, 0, 1, 1]), np.array([0, 1, 0, 1])
+    vn, err = oracle.coo_normalize(rows, cols, P.ravel(), [0, 4], a, b, 2, 2, iters=500)
+    rho = P[0, 0] * P[1, 1] / (P[0, 1] * P[1, 0])
+    A, B1 = a[0], b[0]
+    qa, qb, qc = 1 - rho, 1 - A - B1 + rho * (A + B1), -rho * A * B1
+    roots = np.roots([qa, qb, qc])
+    x = [r.real for r in roots if max(0, A + B1 - 1) < r.real < min(A, B1)][0]
+    ref = np.array([x, A - x, B1 - x, 1 - A - B1 + x])
+    np.testing.assert_allclose(vn, ref, rtol=1e-12)
