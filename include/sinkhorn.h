@@ -181,6 +181,36 @@ int sinkhorn_dense_grad(const void *X, const void *Y, int dtype,
                         void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * Sinkhorn normalisation of a sparse plan on its stored support [AP Abstract,
+ * Innovation: Sinkhorn normalisation run directly in COO form].
+ *
+ * rows/cols/vals/pair_offsets: a plan as sinkhorn_plan_coo writes it (per pair
+ * sorted by row, then column; B+1 offsets); t_rows/t_cols/t_pair_offsets: its
+ * transpose, i.e. the plan extracted with the roles of the clouds exchanged
+ * (sinkhorn_plan_coo(Y, X, b, a, g, f, ...)), which holds exactly the same
+ * entries because log P is evaluated symmetrically.  Per pair, with
+ * lv = log vals, row scalings alpha and column scalings beta start at 0 and
+ * each of `iters` rounds sets
+ *     alpha_i = log a_i - LSE_{k in row i}(lv_k + beta_{col k}),
+ *     beta_j  = log b_j - LSE_{k in col j}(lv_k + alpha_{row k})
+ * (0 for a row or column without a finite term); then
+ * vals_k <- exp(lv_k + alpha_{row k} + beta_{col k}) in place: column sums equal
+ * b, row sums approach a.  err [2B] (device, may be NULL) receives per pair
+ * sum_i |row sum - a_i| and sum_j |column sum - b_j| of the result.  a, b may
+ * be NULL (uniform).  Workspace: sinkhorn_coo_workspace_bytes(B, n, m, nnz).
+ * Synchronises twice on `stream` (entry counts, transpose check); a transpose
+ * that does not match the plan returns SK_ERR_INVALID_ARG with vals unchanged.
+ */
+size_t sinkhorn_coo_workspace_bytes(int B, int n, int m, int64_t nnz);
+int sinkhorn_coo_normalize(int B, int n, int m,
+                           const int32_t *rows, const int32_t *cols, float *vals,
+                           const int64_t *pair_offsets,
+                           const int32_t *t_rows, const int32_t *t_cols,
+                           const int64_t *t_pair_offsets,
+                           const float *a, const float *b, int iters, float *err,
+                           void *ws, size_t ws_bytes, void *stream);
+
+/*
  * Cosine cost on normalised vectors [FS Betekenis en Claims: the approach
  * applies to the cosine distance after normalisation].  For unit vectors
  * ||x^ - y^||^2 = 2 - 2 x^ . y^, so every entry point above, given the

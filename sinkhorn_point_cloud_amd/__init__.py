@@ -32,7 +32,8 @@ SK_WARM_START = 1
 SK_VALU_SCORES = 2
 
 EXPORTS = ("sinkhorn_workspace_bytes", "sinkhorn_potentials", "sinkhorn_plan_coo",
-           "sinkhorn_loss_grad", "sinkhorn_dense_grad", "sinkhorn_normalize",
+           "sinkhorn_loss_grad", "sinkhorn_dense_grad", "sinkhorn_coo_workspace_bytes",
+           "sinkhorn_coo_normalize", "sinkhorn_normalize",
            "sinkhorn_normalize_backward", "sinkhorn_status_string", "sinkhorn_last_error")
 
 
@@ -71,6 +72,10 @@ def load_library():
     lib.sinkhorn_loss_grad.restype = I
     lib.sinkhorn_dense_grad.argtypes = [P, P, I, P, P, I, I, I, I, F, P, P, P, P, P, P, P, Z, P]
     lib.sinkhorn_dense_grad.restype = I
+    lib.sinkhorn_coo_workspace_bytes.argtypes = [I, I, I, L]
+    lib.sinkhorn_coo_workspace_bytes.restype = Z
+    lib.sinkhorn_coo_normalize.argtypes = [I, I, I, P, P, P, P, P, P, P, P, P, I, P, P, Z, P]
+    lib.sinkhorn_coo_normalize.restype = I
     lib.sinkhorn_normalize.argtypes = [P, I, I, I, I, P, P, P]
     lib.sinkhorn_normalize.restype = I
     lib.sinkhorn_normalize_backward.argtypes = [P, P, P, I, I, I, P, P]
@@ -311,3 +316,33 @@ def normalize_backward(Xh, norms, G):
     _check(lib.sinkhorn_normalize_backward(_ptr(Xh), _ptr(norms), _ptr(G), B, n, d, _ptr(dX),
                                            _stream()))
     return dX
+
+
+def coo_normalize(plan, transpose, a, b, n, m, iters, err=True, workspace=None):
+    """Sinkhorn normalisation of a sparse plan on its support, in place.
+
+    plan = (rows, cols, vals, pair_offsets) as plan_coo returns it; transpose =
+    the plan of the exchanged clouds (plan_coo(Y, X, b, a, g, f, ...)), whose
+    (rows, cols, _, pair_offsets) are used.  Returns err [B,2] (float32:
+    sum |row sums - a| and sum |column sums - b| per pair) or None."""
+    lib = load_library()
+    rows, cols, vals, offs = plan
+    t_rows, t_cols, _, t_offs = transpose
+    B = offs.numel() - 1
+    dev = vals.device
+    a, b = _weights(a, B, n, dev), _weights(b, B, m, dev)
+    nnz = int(rows.numel())
+    if workspace is None:
+        workspace = torch.empty(lib.sinkhorn_coo_workspace_bytes(B, n, m, nnz), dtype=torch.uint8,
+                                device=dev)
+    e = torch.empty(B, 2, dtype=torch.float32, device=dev) if err else None
+    one = torch.zeros(1, dtype=torch.int32, device=dev)   # real pointers for an empty plan
+
+    def p(t):
+        return _ptr(t if t.numel() else one)
+
+    rc = lib.sinkhorn_coo_normalize(B, n, m, p(rows), p(cols), p(vals), _ptr(offs), p(t_rows),
+                                    p(t_cols), _ptr(t_offs), _ptr(a), _ptr(b), int(iters), _ptr(e),
+                                    _ptr(workspace), workspace.numel(), _stream())
+    _check(rc)
+    return e

@@ -164,6 +164,25 @@ GradWs carve_grad(Carve &c, int B, int n, int m, int d, int dtype)
     return w;
 }
 
+CooNormWs carve_coo_norm(Carve &c, int B, int n, int m, int64_t nnz)
+{
+    CooNormWs w;
+    w.rb = c.take<int64_t>((size_t)B * n);
+    w.re = c.take<int64_t>((size_t)B * n);
+    w.cb = c.take<int64_t>((size_t)B * m);
+    w.ce = c.take<int64_t>((size_t)B * m);
+    w.perm = c.take<int64_t>(nnz > 0 ? (size_t)nnz : 1);
+    w.lv = c.take<float>(nnz > 0 ? (size_t)nnz : 1);
+    w.al = c.take<double>((size_t)B * n);
+    w.la = c.take<double>((size_t)B * n);
+    w.be = c.take<double>((size_t)B * m);
+    w.lb = c.take<double>((size_t)B * m);
+    w.row_part = c.take<double>((size_t)B * n);
+    w.col_part = c.take<double>((size_t)B * m);
+    w.bad = c.take<int>(1);
+    return w;
+}
+
 size_t ws_size(int op, int B, int n, int m, int d, int dtype)
 {
     Carve c{nullptr};
@@ -466,6 +485,66 @@ int sinkhorn_dense_grad(const void *X, const void *Y, int dtype, const float *a,
         return hip_fail(e, "dense gradient (X side)");
     if (want_y && (e = launch_dense_grad(py, dY, TY, nullptr, st)))
         return hip_fail(e, "dense gradient (Y side)");
+    return SK_OK;
+}
+
+size_t sinkhorn_coo_workspace_bytes(int B, int n, int m, int64_t nnz)
+{
+    if (B < 1 || n < 1 || m < 1 || nnz < 0 || n > kMaxPoints || m > kMaxPoints ||
+        (long long)B * n > (1ll << 31) || (long long)B * m > (1ll << 31))
+        return 0;
+    Carve c{nullptr};
+    carve_coo_norm(c, B, n, m, nnz);
+    return c.off + 256;
+}
+
+int sinkhorn_coo_normalize(int B, int n, int m, const int32_t *rows, const int32_t *cols,
+                           float *vals, const int64_t *pair_offsets, const int32_t *t_rows,
+                           const int32_t *t_cols, const int64_t *t_pair_offsets, const float *a,
+                           const float *b, int iters, float *err, void *ws, size_t ws_bytes,
+                           void *stream)
+{
+    g_err[0] = '\0';
+    if (B < 1 || n < 1 || m < 1 || n > kMaxPoints || m > kMaxPoints ||
+        (long long)B * n > (1ll << 31) || (long long)B * m > (1ll << 31))
+        return fail(SK_ERR_INVALID_ARG, "bad sizes B=%d n=%d m=%d", B, n, m);
+    if (!rows || !cols || !vals || !pair_offsets || !t_rows || !t_cols || !t_pair_offsets)
+        return fail(SK_ERR_INVALID_ARG, "the plan, its transpose and both offset arrays must be "
+                                        "non-NULL device pointers");
+    if (iters < 0)
+        return fail(SK_ERR_INVALID_ARG, "iters=%d must be >= 0", iters);
+    hipStream_t st = (hipStream_t)stream;
+    int64_t tot[2] = {0, 0};
+    hipError_t e;
+    if ((e = hipMemcpyAsync(&tot[0], pair_offsets + B, sizeof(int64_t), hipMemcpyDeviceToHost,
+                            st)) ||
+        (e = hipMemcpyAsync(&tot[1], t_pair_offsets + B, sizeof(int64_t), hipMemcpyDeviceToHost,
+                            st)) ||
+        (e = hipStreamSynchronize(st)))
+        return hip_fail(e, "read entry counts");
+    if (tot[0] != tot[1] || tot[0] < 0)
+        return fail(SK_ERR_INVALID_ARG, "plan has %lld entries, its transpose %lld",
+                    (long long)tot[0], (long long)tot[1]);
+    const int64_t nnz = tot[0];
+    if (!ws || ws_bytes < sinkhorn_coo_workspace_bytes(B, n, m, nnz))
+        return fail(SK_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given",
+                    sinkhorn_coo_workspace_bytes(B, n, m, nnz), ws_bytes);
+    Carve c{(char *)ws};
+    CooNormWs w = carve_coo_norm(c, B, n, m, nnz);
+    if ((e = launch_log_weights(a, B, n, w.la, st)) || (e = launch_log_weights(b, B, m, w.lb, st)) ||
+        (e = launch_segment_bounds(rows, pair_offsets, B, n, w.rb, w.re, st)) ||
+        (e = launch_segment_bounds(t_rows, t_pair_offsets, B, m, w.cb, w.ce, st)) ||
+        (e = launch_coo_perm(cols, t_rows, t_cols, t_pair_offsets, B, n, m, w, st)))
+        return hip_fail(e, "coo normalisation set-up");
+    int bad = 0;
+    if ((e = hipMemcpyAsync(&bad, w.bad, sizeof bad, hipMemcpyDeviceToHost, st)) ||
+        (e = hipStreamSynchronize(st)))
+        return hip_fail(e, "read transpose check");
+    if (bad)
+        return fail(SK_ERR_INVALID_ARG, "%d entries of the transpose are not in the plan", bad);
+    if ((e = launch_coo_normalize(rows, cols, vals, pair_offsets, t_cols, B, n, m, nnz, iters, err,
+                                  a, b, w, st)))
+        return hip_fail(e, "coo normalisation");
     return SK_OK;
 }
 

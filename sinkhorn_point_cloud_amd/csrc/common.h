@@ -210,6 +210,27 @@ hipError_t launch_gradFm(const SideF &rows, const float *row_w, const SideF &key
                          float *proj, hipStream_t st);
 hipError_t launch_transpose_bf16(const void *X, int B, int n, int n_pad, int d, uint16_t *Xt,
                                  hipStream_t st);
+// Runs of equal keys in a key-sorted COO (per pair): begin/end [B][count], 0/0
+// for a key with no entries.
+hipError_t launch_segment_bounds(const int32_t *keys, const int64_t *pair_offsets, int B, int count,
+                                 int64_t *begin, int64_t *end, hipStream_t st);
+// Sinkhorn normalisation of a row-sorted COO plan on its support, given its
+// transpose (column-sorted).  Workspace pieces as carved by the ABI.
+struct CooNormWs {
+    int64_t *rb, *re, *cb, *ce;   // row runs of the plan, column runs of the transpose
+    int64_t *perm;                // transpose entry -> plan entry
+    float *lv;                    // log of the plan's values
+    double *al, *be, *la, *lb;    // scalings and log weights
+    double *row_part, *col_part;  // per-row / per-column marginal errors
+    int *bad;                     // transpose entries with no match in the plan
+};
+hipError_t launch_coo_perm(const int32_t *cols, const int32_t *t_rows, const int32_t *t_cols,
+                           const int64_t *t_offs, int B, int n, int m, const CooNormWs &w,
+                           hipStream_t st);
+hipError_t launch_coo_normalize(const int32_t *rows, const int32_t *cols, float *vals,
+                                const int64_t *offs, const int32_t *t_cols, int B, int n, int m,
+                                int64_t nnz, int iters, float *err, const float *a,
+                                const float *b, const CooNormWs &w, hipStream_t st);
 // Cosine cost support: points to unit length (fp32 out, norms kept), and the
 // gradient through that map.
 hipError_t launch_normalize(const void *X, int dtype, long count, int d, float *Xh,

@@ -140,6 +140,18 @@ void rows_dispatch(const void *X, const void *Y, int d, int B, int n, int m,
 
 }  // namespace
 
+hipError_t launch_segment_bounds(const int32_t *keys, const int64_t *pair_offsets, int B, int count,
+                                 int64_t *begin, int64_t *end, hipStream_t st)
+{
+    const size_t cnt = (size_t)B * count;
+    hipLaunchKernelGGL(fill_i64, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0, st, begin,
+                       cnt);
+    hipLaunchKernelGGL(fill_i64, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0, st, end, cnt);
+    hipLaunchKernelGGL(row_bounds, dim3(256, B), dim3(256), 0, st, keys, pair_offsets, count,
+                       begin, end);
+    return hipGetLastError();
+}
+
 hipError_t launch_loss_grad(const void *X, const void *Y, int dtype, int d, int B, int n,
                             int m, const int32_t *rows, const int32_t *cols, const float *vals,
                             const int64_t *pair_offsets, int64_t *row_begin,

@@ -178,6 +178,18 @@ def test_normalize_rejects_bad_arguments_without_writing(lib, kw):
     assert rc == sk.SK_ERR_INVALID_ARG and np.all(xh == 3.0)
 
 
+def test_coo_normalize_rejects_bad_arguments(lib):
+    assert lib.sinkhorn_coo_workspace_bytes(2, 100, 90, 5000) > 5000 * 12
+    assert lib.sinkhorn_coo_workspace_bytes(0, 100, 90, 5000) == 0
+    assert lib.sinkhorn_coo_workspace_bytes(1, 100, 90, -1) == 0
+    for B, n, m, it, null in ((0, 4, 4, 1, False), (1, 0, 4, 1, False), (1, 4, 4, -1, False),
+                              (1, 4, 4, 1, True)):
+        rc = lib.sinkhorn_coo_normalize(B, n, m, DUMMY, DUMMY, None if null else DUMMY, DUMMY,
+                                        DUMMY, DUMMY, DUMMY, None, None, it, None, DUMMY, 1 << 40,
+                                        None)
+        assert rc == sk.SK_ERR_INVALID_ARG, lib.sinkhorn_last_error()
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     X = torch.zeros(1, 4, 3)

@@ -549,3 +549,82 @@ def test_transposed_sparse_plan_and_y_gradient():
     _, dY_o = oracle.loss_grad(c["Y"], c["X"], ro, co, vo, oo)
     for p in range(2):
         assert rel_inf(host(dY)[p], dY_o[p]) <= 1e-4
+
+
+# --------------------------------------------- Sinkhorn normalisation in COO form
+def _coo_dev(coo):
+    rows, cols, vals, offs = coo
+    return (dev(rows.astype(np.int32)), dev(cols.astype(np.int32)),
+            dev(vals.astype(np.float32)), dev(offs.astype(np.int64)))
+
+
+@pytest.mark.parametrize("B,n,m,eps,thr,iters", [(1, 33, 47, 0.05, 1e-8, 1),
+                                                  (2, 300, 257, 0.01, 1e-8, 20),
+                                                  (3, 128, 200, 0.02, 1e-4, 200)])
+def test_coo_normalize_matches_oracle(B, n, m, eps, thr, iters):
+    # both sides normalise the oracle's plan (fp32 values), so the supports agree
+    c = workloads.random_case(18, B, n, m, 3, weights="dirichlet")
+    fo, go = oracle.potentials(c["X"], c["Y"], c["a"], c["b"], eps=[eps], iters=[10])
+    plan = oracle.plan_coo(c["X"], c["Y"], c["a"], c["b"], fo, go, eps, rel_thr=thr)
+    tr = oracle.plan_coo(c["Y"], c["X"], c["b"], c["a"], go, fo, eps, rel_thr=thr)
+    vals32 = plan[2].astype(np.float32)
+    v_o, err_o = oracle.coo_normalize(plan[0], plan[1], vals32.astype(np.float64), plan[3],
+                                      c["a"], c["b"], n, m, iters)
+    P = _coo_dev((plan[0], plan[1], vals32, plan[3]))
+    T = _coo_dev(tr)
+    err = sk.coo_normalize(P, T, dev(c["a"]), dev(c["b"]), n, m, iters)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(host(P[2]), v_o, rtol=1e-4, atol=0)
+    np.testing.assert_allclose(host(err), err_o, rtol=1e-3, atol=1e-6)
+
+
+def test_coo_normalize_gpu_chain_reaches_the_marginals():
+    c = workloads.random_case(19, 2, 400, 350, 3, weights="dirichlet")
+    eps = 0.02
+    X, Y, a, b = dev(c["X"]), dev(c["Y"]), dev(c["a"]), dev(c["b"])
+    f, g, _ = sk.potentials(X, Y, a, b, eps=[eps], iters=[10])
+    P = sk.plan_coo(X, Y, a, b, f, g, eps, 1e-8)
+    T = sk.plan_coo(Y, X, b, a, g, f, eps, 1e-8)
+    before = P[2].clone()
+    err = sk.coo_normalize(P, T, a, b, 400, 350, 300)
+    torch.cuda.synchronize()
+    e = host(err)
+    assert np.all(e[:, 1] < 1e-5) and np.all(e[:, 0] < 1e-4), e
+    # the column sums after the last half-step are b; the support is unchanged
+    assert P[2].shape == before.shape and bool((P[2] >= 0).all())
+
+
+def test_coo_normalize_rejects_a_mismatched_transpose():
+    c = workloads.random_case(20, 1, 64, 70, 3)
+    eps = 0.05
+    fo, go = oracle.potentials(c["X"], c["Y"], c["a"], c["b"], eps=[eps], iters=[5])
+    plan = oracle.plan_coo(c["X"], c["Y"], c["a"], c["b"], fo, go, eps, rel_thr=1e-3)
+    tr = list(oracle.plan_coo(c["Y"], c["X"], c["b"], c["a"], go, fo, eps, rel_thr=1e-3))
+    tr[1] = tr[1].copy()
+    tr[1][0] = (tr[1][0] + 1) % 64                  # one transposed entry points elsewhere
+    P, T = _coo_dev(plan), _coo_dev(tr)
+    before = P[2].clone()
+    with pytest.raises(sk.SinkhornError) as ex:
+        sk.coo_normalize(P, T, None, None, 64, 70, 5)
+    assert ex.value.status == sk.SK_ERR_INVALID_ARG
+    assert torch.equal(P[2], before)
+
+
+@pytest.mark.parametrize("name,pairs", [("sphere-2k", [0, 31]), ("blobs-1k", [0, 255])])
+def test_workload_coo_normalize_sampled_pairs(name, pairs):
+    w = workloads.make(name, pairs=pairs)
+    gold = golden(name)
+    eps = float(w["eps"][-1])
+    n, m = w["X"].shape[1], w["Y"].shape[1]
+    fo = gold["f"][pairs].astype(np.float32).astype(np.float64)
+    go = gold["g"][pairs].astype(np.float32).astype(np.float64)
+    plan = oracle.plan_coo(w["X"], w["Y"], w["a"], w["b"], fo, go, eps, rel_thr=w["threshold"])
+    tr = oracle.plan_coo(w["Y"], w["X"], w["b"], w["a"], go, fo, eps, rel_thr=w["threshold"])
+    vals32 = plan[2].astype(np.float32)
+    v_o, err_o = oracle.coo_normalize(plan[0], plan[1], vals32.astype(np.float64), plan[3],
+                                      w["a"], w["b"], n, m, 10)
+    P = _coo_dev((plan[0], plan[1], vals32, plan[3]))
+    err = sk.coo_normalize(P, _coo_dev(tr), dev(w["a"]), dev(w["b"]), n, m, 10)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(host(P[2]), v_o, rtol=1e-4, atol=0)
+    np.testing.assert_allclose(host(err), err_o, rtol=1e-3, atol=1e-6)
