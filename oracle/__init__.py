@@ -42,6 +42,7 @@ PINS = {
     "coo_normalize": "full support converges to the dense Sinkhorn plan; marginals at"
                      " convergence; invariance to row and column scalings of the input;"
                      " 2x2 closed form (cross-ratio kept)",
+    "hvp": "finite differences of the converged dense gradient; symmetry <U, HV> = <V, HU>",
     "normalize": "unit norms, direction and scale invariance; cosine cost matrix 2 - 2 x.y"
                  " from numpy with scipy logsumexp for one update",
     "normalize_backward": "finite differences of a function of the normalised points;"
@@ -94,6 +95,8 @@ def _load():
         lib.oracle_normalize_backward.restype = None
         lib.oracle_coo_normalize.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, P]
         lib.oracle_coo_normalize.restype = i32
+        lib.oracle_hvp.argtypes = [P, P, P, P, P, P, f64, i32, i32, i32, i32, P, P]
+        lib.oracle_hvp.restype = i32
         _lib = lib
     return _lib
 
@@ -281,3 +284,18 @@ def coo_normalize(rows, cols, vals, pair_offsets, a, b, n, m, iters):
     if rc != 0:
         raise ValueError("oracle_coo_normalize: index out of range")
     return vals, err
+
+
+def hvp(X, Y, a, b, f, g, eps, V):
+    """Hessian-vector product of the entropic OT value in X along V [B,n,d] (dense, small)."""
+    lib = _load()
+    X, Y, B, n, m, d = _shapes(X, Y)
+    a, b = _weights(a, B, n), _weights(b, B, m)
+    f, g = _d(f).reshape(B, n), _d(g).reshape(B, m)
+    V = _d(V).reshape(B, n, d)
+    HV = np.empty((B, n, d))
+    rc = lib.oracle_hvp(_p(X), _p(Y), _p(a), _p(b), _p(f), _p(g), float(eps), B, n, m, d, _p(V),
+                        _p(HV))
+    if rc != 0:
+        raise ValueError("oracle_hvp: system not positive definite")
+    return HV

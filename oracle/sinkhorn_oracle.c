@@ -663,3 +663,142 @@ int oracle_coo_normalize(const int32_t *rows, const int32_t *cols, double *vals,
     free(al); free(be); free(mx_r); free(sm_r); free(mx_c); free(sm_c);
     return rc;
 }
+
+/*
+ * Hessian-vector product of the entropic OT value in X [FS Methodologie 3,
+ * Hessiaan-Vector Producten], at the plan of the given potentials (meant to be
+ * converged):  HV = d/dt grad_X OT(X + t V) at t = 0, where
+ *   grad_i = sum_j 2 P_ij (x_i - y_j)          (the envelope gradient)
+ * and P moves with X through C and through the potentials, which keep the
+ * plan's marginals.  Differentiating P_ij = a_i b_j exp((f_i + g_j - C_ij)/eps):
+ *   dP_ij = P_ij (df_i + dg_j - dC_ij) / eps,   dC_ij = 2 (x_i - y_j) . v_i,
+ * and the marginals stay fixed, sum_j dP_ij = 0 and sum_i dP_ij = 0:
+ *   ma_i df_i + (P dg)_i = r_i = sum_j P_ij dC_ij,
+ *   (P^T df)_j + mb_j dg_j = c_j = sum_i P_ij dC_ij,
+ * with ma, mb the plan's row and column sums.  Eliminating df gives
+ *   (diag(mb) - P^T diag(1/ma) P) dg = c - P^T (r / ma),
+ * singular only along the constant vector (df + t, dg - t leave dP unchanged);
+ * here dg_0 = 0 fixes it and the rest is solved by Cholesky.  Then
+ *   HV_i = sum_j 2 dP_ij (x_i - y_j) + 2 ma_i v_i.
+ * Dense in n x m: for the small cases the tests use.  Returns 0, or -1 when a
+ * system is not positive definite.
+ */
+int oracle_hvp(const double *X, const double *Y, const double *a, const double *b,
+               const double *f, const double *g, double eps, int B, int n, int m, int d,
+               const double *V, double *HV)
+{
+    double *P = (double *)malloc(sizeof(double) * (size_t)n * m);
+    double *dC = (double *)malloc(sizeof(double) * (size_t)n * m);
+    double *S = (double *)malloc(sizeof(double) * (size_t)m * m);
+    double *ma = (double *)malloc(sizeof(double) * (size_t)n);
+    double *mb = (double *)malloc(sizeof(double) * (size_t)m);
+    double *r = (double *)malloc(sizeof(double) * (size_t)n);
+    double *c = (double *)malloc(sizeof(double) * (size_t)m);
+    double *rhs = (double *)malloc(sizeof(double) * (size_t)m);
+    double *dg = (double *)malloc(sizeof(double) * (size_t)m);
+    double *df = (double *)malloc(sizeof(double) * (size_t)n);
+    double *la = (double *)malloc(sizeof(double) * (size_t)n);
+    double *lb = (double *)malloc(sizeof(double) * (size_t)m);
+    int rc = 0;
+    for (int p = 0; p < B && rc == 0; ++p) {
+        const double *Xp = X + (size_t)p * n * d, *Yp = Y + (size_t)p * m * d;
+        const double *Vp = V + (size_t)p * n * d;
+        double *Hp = HV + (size_t)p * n * d;
+        log_weights(a + (size_t)p * n, n, la);
+        log_weights(b + (size_t)p * m, m, lb);
+        for (int i = 0; i < n; ++i) {
+            ma[i] = 0.0;
+            r[i] = 0.0;
+        }
+        for (int j = 0; j < m; ++j) {
+            mb[j] = 0.0;
+            c[j] = 0.0;
+        }
+        for (int i = 0; i < n; ++i)
+            for (int j = 0; j < m; ++j) {
+                const double *x = Xp + (size_t)i * d, *y = Yp + (size_t)j * d;
+                const double pij = exp(log_plan(x, y, d, f[(size_t)p * n + i],
+                                                g[(size_t)p * m + j], la[i], lb[j], eps));
+                double dot = 0.0;
+                for (int k = 0; k < d; ++k)
+                    dot += (x[k] - y[k]) * Vp[(size_t)i * d + k];
+                P[(size_t)i * m + j] = pij;
+                dC[(size_t)i * m + j] = 2.0 * dot;
+                ma[i] += pij;
+                mb[j] += pij;
+                r[i] += pij * 2.0 * dot;
+                c[j] += pij * 2.0 * dot;
+            }
+        /* S = diag(mb) - P^T diag(1/ma) P,  rhs = c - P^T (r / ma) */
+        for (int j = 0; j < m; ++j) {
+            double s = c[j];
+            for (int i = 0; i < n; ++i)
+                if (ma[i] > 0.0)
+                    s -= P[(size_t)i * m + j] * r[i] / ma[i];
+            rhs[j] = s;
+            for (int l = 0; l < m; ++l) {
+                double t = (j == l) ? mb[j] : 0.0;
+                for (int i = 0; i < n; ++i)
+                    if (ma[i] > 0.0)
+                        t -= P[(size_t)i * m + j] * P[(size_t)i * m + l] / ma[i];
+                S[(size_t)j * m + l] = t;
+            }
+        }
+        /* dg_0 = 0; Cholesky of S[1:,1:] */
+        const int q = m - 1;
+        dg[0] = 0.0;
+        for (int j = 0; j < q; ++j) {
+            for (int l = 0; l <= j; ++l) {
+                double s = S[(size_t)(j + 1) * m + (l + 1)];
+                for (int k = 0; k < l; ++k)
+                    s -= S[(size_t)(j + 1) * m + (k + 1)] * S[(size_t)(l + 1) * m + (k + 1)];
+                if (j == l) {
+                    if (!(s > 0.0)) {
+                        rc = -1;
+                        break;
+                    }
+                    S[(size_t)(j + 1) * m + (j + 1)] = sqrt(s);
+                } else {
+                    S[(size_t)(j + 1) * m + (l + 1)] = s / S[(size_t)(l + 1) * m + (l + 1)];
+                }
+            }
+            if (rc)
+                break;
+        }
+        if (rc)
+            break;
+        for (int j = 0; j < q; ++j) {   /* L y = rhs[1:] */
+            double s = rhs[j + 1];
+            for (int k = 0; k < j; ++k)
+                s -= S[(size_t)(j + 1) * m + (k + 1)] * dg[k + 1];
+            dg[j + 1] = s / S[(size_t)(j + 1) * m + (j + 1)];
+        }
+        for (int j = q - 1; j >= 0; --j) {   /* L^T dg = y */
+            double s = dg[j + 1];
+            for (int k = j + 1; k < q; ++k)
+                s -= S[(size_t)(k + 1) * m + (j + 1)] * dg[k + 1];
+            dg[j + 1] = s / S[(size_t)(j + 1) * m + (j + 1)];
+        }
+        for (int i = 0; i < n; ++i) {
+            double s = r[i];
+            for (int j = 0; j < m; ++j)
+                s -= P[(size_t)i * m + j] * dg[j];
+            df[i] = ma[i] > 0.0 ? s / ma[i] : 0.0;
+        }
+        for (int i = 0; i < n; ++i) {
+            const double *x = Xp + (size_t)i * d;
+            for (int k = 0; k < d; ++k)
+                Hp[(size_t)i * d + k] = 2.0 * ma[i] * Vp[(size_t)i * d + k];
+            for (int j = 0; j < m; ++j) {
+                const double *y = Yp + (size_t)j * d;
+                const double dp = P[(size_t)i * m + j] *
+                                  (df[i] + dg[j] - dC[(size_t)i * m + j]) / eps;
+                for (int k = 0; k < d; ++k)
+                    Hp[(size_t)i * d + k] += 2.0 * dp * (x[k] - y[k]);
+            }
+        }
+    }
+    free(P); free(dC); free(S); free(ma); free(mb); free(r); free(c); free(rhs); free(dg);
+    free(df); free(la); free(lb);
+    return rc;
+}

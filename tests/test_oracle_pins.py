@@ -545,3 +545,31 @@ def test_coo_normalisation_two_by_two_closed_form():
     x = [r.real for r in roots if max(0, A + B1 - 1) < r.real < min(A, B1)][0]
     ref = np.array([x, A - x, B1 - x, 1 - A - B1 + x])
     np.testing.assert_allclose(vn, ref, rtol=1e-12)
+
+
+# ---------------------------------------------------- Hessian-vector product
+def test_hvp_is_the_derivative_of_the_converged_gradient():
+    X, Y, a, b = _case(47, 9, 11)
+    eps, iters = 0.1, 3000
+    V = np.random.default_rng(4).normal(size=X.shape)
+
+    def grad(Xv):
+        f, g = oracle.potentials(Xv, Y, a, b, eps=[eps], iters=[iters])
+        return oracle.dense_grad(Xv, Y, a, b, f, g, eps)[1][0]
+
+    f, g = _converge(X, Y, a, b, eps, iters)
+    HV = oracle.hvp(X, Y, a, b, f, g, eps, V)[0]
+    h = 1e-5
+    fd = (grad(X + h * V) - grad(X - h * V)) / (2 * h)
+    np.testing.assert_allclose(HV, fd, rtol=1e-6, atol=1e-8 * np.abs(fd).max())
+
+
+def test_hvp_is_symmetric():
+    X, Y, a, b = _case(53, 12, 10, d=4)
+    eps = 0.05
+    f, g = _converge(X, Y, a, b, eps, 4000)
+    rng = np.random.default_rng(5)
+    U, V = rng.normal(size=X.shape), rng.normal(size=X.shape)
+    HU = oracle.hvp(X, Y, a, b, f, g, eps, U)[0]
+    HV = oracle.hvp(X, Y, a, b, f, g, eps, V)[0]
+    assert abs((U * HV).sum() - (V * HU).sum()) <= 1e-10 * np.abs(U * HV).sum()
