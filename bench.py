@@ -289,6 +289,19 @@ def main():
         t_dg = timed(dense_grad, 2)
         assert all(bool(torch.isfinite(t).all()) for t in dg_out)
         line["phases_ms"]["dense_grad_and_projection_both_sides"] = t_dg * 1e3
+        if d <= 16:
+            # Hessian-vector product in X along the gradient direction, 20 CG steps
+            hv_ws = torch.empty(sk.workspace_bytes(sk.SK_OP_HVP, B, n, m, d, dt),
+                                dtype=torch.uint8, device=dev)
+            V, HV = dg_out[0].clone(), torch.empty_like(dg_out[0])
+
+            def hvp():
+                sk.hvp(X, Y, a, b, f, g, eps[-1], V, cg_iters=20, workspace=hv_ws, out=HV)
+
+            hvp()
+            t_hv = timed(hvp, 1)
+            assert bool(torch.isfinite(HV).all())
+            line["phases_ms"]["hvp_20_cg_steps"] = t_hv * 1e3
     if args.copy_calibration:
         src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)

@@ -64,7 +64,13 @@ enum {
 enum { SK_F32 = 0, SK_BF16 = 1 };
 
 /* Operation ids for sinkhorn_workspace_bytes(). */
-enum { SK_OP_POTENTIALS = 0, SK_OP_PLAN_COO = 1, SK_OP_LOSS_GRAD = 2, SK_OP_DENSE_GRAD = 3 };
+enum {
+    SK_OP_POTENTIALS = 0,
+    SK_OP_PLAN_COO = 1,
+    SK_OP_LOSS_GRAD = 2,
+    SK_OP_DENSE_GRAD = 3,
+    SK_OP_HVP = 4
+};
 
 /* Flags of sinkhorn_potentials(). */
 #define SK_WARM_START 1u  /* f and g hold starting potentials (resume) */
@@ -179,6 +185,31 @@ int sinkhorn_dense_grad(const void *X, const void *Y, int dtype,
                         const float *f, const float *g,
                         float *dX, float *TX, float *dY, float *TY,
                         void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Hessian-vector product of the entropic OT value in X [FS Methodologie 3,
+ * Hessiaan-Vector Producten: transport-vector and transport-matrix products,
+ * O((n+m)d) memory].
+ *
+ * HV = d/dt grad_X OT(X + t V) at t = 0, grad_i = sum_j 2 P_ij (x_i - y_j),
+ * with P the plan of potentials f, g at eps (meant to be converged: the
+ * derivative keeps P's row and column sums fixed, as they are at the solution).
+ * The potentials' derivative solves a symmetric positive semidefinite m x m
+ * system, (diag(mb) - P^T diag(1/ma) P) dg = c - P^T (r/ma), by `cg_iters`
+ * conjugate-gradient steps from 0 (ma, mb: the plan's row and column sums;
+ * r_i, c_j: row and column sums of P_ij 2 (x_i - y_j).v_i); every product with
+ * P streams the plan with log P in fp64, nothing n x m is stored.
+ * V, HV: [B][n][d] fp32.  cg_residual [B] (device, may be NULL) receives the
+ * final conjugate-gradient residual relative to the right-hand side.
+ * Supported for d <= 16 (SK_ERR_UNSUPPORTED above); workspace
+ * sinkhorn_workspace_bytes(SK_OP_HVP, ...).
+ */
+int sinkhorn_hvp(const void *X, const void *Y, int dtype,
+                 const float *a, const float *b,
+                 int B, int n, int m, int d, float eps,
+                 const float *f, const float *g, const float *V,
+                 int cg_iters, float *HV, float *cg_residual,
+                 void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Sinkhorn normalisation of a sparse plan on its stored support [AP Abstract,

@@ -27,12 +27,13 @@ _LIB_PATH = os.path.join(_HERE, "libsinkhorn_amd.so")
 SK_OK, SK_ERR_INVALID_ARG, SK_ERR_UNSUPPORTED, SK_ERR_WORKSPACE, SK_ERR_CAPACITY, SK_ERR_HIP = \
     range(6)
 SK_F32, SK_BF16 = 0, 1
-SK_OP_POTENTIALS, SK_OP_PLAN_COO, SK_OP_LOSS_GRAD, SK_OP_DENSE_GRAD = 0, 1, 2, 3
+SK_OP_POTENTIALS, SK_OP_PLAN_COO, SK_OP_LOSS_GRAD, SK_OP_DENSE_GRAD, SK_OP_HVP = range(5)
 SK_WARM_START = 1
 SK_VALU_SCORES = 2
 
 EXPORTS = ("sinkhorn_workspace_bytes", "sinkhorn_potentials", "sinkhorn_plan_coo",
-           "sinkhorn_loss_grad", "sinkhorn_dense_grad", "sinkhorn_coo_workspace_bytes",
+           "sinkhorn_loss_grad", "sinkhorn_dense_grad", "sinkhorn_hvp",
+           "sinkhorn_coo_workspace_bytes",
            "sinkhorn_coo_normalize", "sinkhorn_normalize",
            "sinkhorn_normalize_backward", "sinkhorn_status_string", "sinkhorn_last_error")
 
@@ -72,6 +73,8 @@ def load_library():
     lib.sinkhorn_loss_grad.restype = I
     lib.sinkhorn_dense_grad.argtypes = [P, P, I, P, P, I, I, I, I, F, P, P, P, P, P, P, P, Z, P]
     lib.sinkhorn_dense_grad.restype = I
+    lib.sinkhorn_hvp.argtypes = [P, P, I, P, P, I, I, I, I, F, P, P, P, I, P, P, P, Z, P]
+    lib.sinkhorn_hvp.restype = I
     lib.sinkhorn_coo_workspace_bytes.argtypes = [I, I, I, L]
     lib.sinkhorn_coo_workspace_bytes.restype = Z
     lib.sinkhorn_coo_normalize.argtypes = [I, I, I, P, P, P, P, P, P, P, P, P, I, P, P, Z, P]
@@ -346,3 +349,26 @@ def coo_normalize(plan, transpose, a, b, n, m, iters, err=True, workspace=None):
                                     _ptr(workspace), workspace.numel(), _stream())
     _check(rc)
     return e
+
+
+def hvp(X, Y, a, b, f, g, eps: float, V, cg_iters: int = 100, workspace=None, out=None):
+    """(HV, cg_residual): Hessian-vector product of the entropic OT value in X along V
+    [B,n,d] (d <= 16), at the plan of potentials f, g; cg_residual [B] is the final
+    conjugate-gradient residual relative to the right-hand side."""
+    lib = load_library()
+    X, Y, dt = _points(X, Y)
+    B, n, d = X.shape
+    m = Y.shape[1]
+    dev = X.device
+    a, b = _weights(a, B, n, dev), _weights(b, B, m, dev)
+    f = f.reshape(B, n).contiguous().float()
+    g = g.reshape(B, m).contiguous().float()
+    V = V.reshape(B, n, d).contiguous().float()
+    HV = out if out is not None else torch.empty(B, n, d, dtype=torch.float32, device=dev)
+    res = torch.empty(B, dtype=torch.float32, device=dev)
+    ws = _workspace(SK_OP_HVP, B, n, m, d, dt, dev, workspace)
+    rc = lib.sinkhorn_hvp(_ptr(X), _ptr(Y), dt, _ptr(a), _ptr(b), B, n, m, d, float(eps), _ptr(f),
+                          _ptr(g), _ptr(V), int(cg_iters), _ptr(HV), _ptr(res), _ptr(ws),
+                          ws.numel(), _stream())
+    _check(rc)
+    return HV, res

@@ -183,6 +183,33 @@ CooNormWs carve_coo_norm(Carve &c, int B, int n, int m, int64_t nnz)
     return w;
 }
 
+constexpr int kMaxHvpDim = 16;
+
+HvpWs carve_hvp(Carve &c, int B, int n, int m, int d)
+{
+    HvpWs w;
+    const size_t Bn = (size_t)B * n, Bm = (size_t)B * m;
+    w.la = c.take<double>(Bn);
+    w.lb = c.take<double>(Bm);
+    w.ma = c.take<double>(Bn);
+    w.tv = c.take<double>(Bn);
+    w.ur = c.take<double>(Bn);
+    w.mur = c.take<double>(Bn);
+    w.D1 = c.take<double>(Bn * d);
+    w.Tv = c.take<double>(Bn * d);
+    w.Du = c.take<double>(Bn * d);
+    w.mb = c.take<double>(Bm);
+    w.muc = c.take<double>(Bm);
+    w.tw = c.take<double>(Bm);
+    w.rhs = c.take<double>(Bm);
+    w.x = c.take<double>(Bm);
+    w.res = c.take<double>(Bm);
+    w.dir = c.take<double>(Bm);
+    w.rr = c.take<double>(B);
+    w.rr0 = c.take<double>(B);
+    return w;
+}
+
 size_t ws_size(int op, int B, int n, int m, int d, int dtype)
 {
     Carve c{nullptr};
@@ -192,8 +219,10 @@ size_t ws_size(int op, int B, int n, int m, int d, int dtype)
         carve_coo(c, B, n, m);
     else if (op == SK_OP_LOSS_GRAD)
         carve_loss(c, B, n);
-    else
+    else if (op == SK_OP_DENSE_GRAD)
         carve_grad(c, B, n, m, d, dtype);
+    else
+        carve_hvp(c, B, n, m, d);
     return c.off + 256;
 }
 
@@ -227,7 +256,8 @@ extern "C" {
 
 size_t sinkhorn_workspace_bytes(int op, int B, int n, int m, int d, int dtype)
 {
-    if (op < SK_OP_POTENTIALS || op > SK_OP_DENSE_GRAD || !shape_ok(B, n, m, d) ||
+    if (op < SK_OP_POTENTIALS || op > SK_OP_HVP || !shape_ok(B, n, m, d) ||
+        (op == SK_OP_HVP && d > kMaxHvpDim) ||
         (dtype != SK_F32 && dtype != SK_BF16) || !supported(dtype, d))
         return 0;
     return ws_size(op, B, n, m, d, dtype);
@@ -485,6 +515,41 @@ int sinkhorn_dense_grad(const void *X, const void *Y, int dtype, const float *a,
         return hip_fail(e, "dense gradient (X side)");
     if (want_y && (e = launch_dense_grad(py, dY, TY, nullptr, st)))
         return hip_fail(e, "dense gradient (Y side)");
+    return SK_OK;
+}
+
+int sinkhorn_hvp(const void *X, const void *Y, int dtype, const float *a, const float *b, int B,
+                 int n, int m, int d, float eps, const float *f, const float *g, const float *V,
+                 int cg_iters, float *HV, float *cg_residual, void *ws, size_t ws_bytes,
+                 void *stream)
+{
+    g_err[0] = '\0';
+    int rc = check_common(X, Y, dtype, B, n, m, d);
+    if (rc)
+        return rc;
+    if (d > kMaxHvpDim)
+        return fail(SK_ERR_UNSUPPORTED, "Hessian-vector products need d <= %d (d=%d)", kMaxHvpDim,
+                    d);
+    if (!f || !g || !V || !HV)
+        return fail(SK_ERR_INVALID_ARG, "f, g, V and HV must be non-NULL device pointers");
+    if (!(eps > 0.f) || !isfinite(eps))
+        return fail(SK_ERR_INVALID_ARG, "eps=%g must be finite and > 0", eps);
+    if (cg_iters < 0)
+        return fail(SK_ERR_INVALID_ARG, "cg_iters=%d must be >= 0", cg_iters);
+    rc = check_ws(ws, ws_bytes, ws_size(SK_OP_HVP, B, n, m, d, dtype));
+    if (rc)
+        return rc;
+    hipStream_t st = (hipStream_t)stream;
+    Carve c{(char *)ws};
+    HvpWs w = carve_hvp(c, B, n, m, d);
+    hipError_t e;
+    if ((e = launch_log_weights(a, B, n, w.la, st)) || (e = launch_log_weights(b, B, m, w.lb, st)))
+        return hip_fail(e, "log weights");
+    const double inv_eps = 1.0 / (double)eps;
+    PlanArgs px{X, Y, dtype, d, B, n, m, f, g, w.la, w.lb, inv_eps};
+    PlanArgs py{Y, X, dtype, d, B, m, n, g, f, w.lb, w.la, inv_eps};
+    if ((e = launch_hvp(px, py, V, cg_iters, HV, cg_residual, w, st)))
+        return hip_fail(e, "Hessian-vector product");
     return SK_OK;
 }
 

@@ -231,6 +231,18 @@ hipError_t launch_coo_normalize(const int32_t *rows, const int32_t *cols, float 
                                 const int64_t *offs, const int32_t *t_cols, int B, int n, int m,
                                 int64_t nnz, int iters, float *err, const float *a,
                                 const float *b, const CooNormWs &w, hipStream_t st);
+// Hessian-vector product of the entropic OT value in X (d <= 16): px = plan
+// arguments with rows X, py the same with the roles exchanged.
+struct HvpWs {
+    double *la, *lb;                    // log weights
+    double *ma, *tv, *ur, *mur;         // [B][n]
+    double *D1, *Tv, *Du;               // [B][n][d]
+    double *mb, *muc, *tw, *rhs;        // [B][m]
+    double *x, *res, *dir;              // conjugate-gradient vectors [B][m]
+    double *rr, *rr0;                   // [B]
+};
+hipError_t launch_hvp(const PlanArgs &px, const PlanArgs &py, const float *V, int cg_iters,
+                      float *HV, float *cg_residual, const HvpWs &w, hipStream_t st);
 // Cosine cost support: points to unit length (fp32 out, norms kept), and the
 // gradient through that map.
 hipError_t launch_normalize(const void *X, int dtype, long count, int d, float *Xh,

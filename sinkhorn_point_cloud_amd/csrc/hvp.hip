@@ -1,0 +1,342 @@
+// hvp.hip -- streaming Hessian-vector product of the entropic OT value in X
+// (FlashSinkhorn summary, Methodologie 3, Hessiaan-Vector Producten: the HVP
+// as a sequence of transport-vector and transport-matrix products, working
+// memory O((n + m) d), neither the Hessian nor the plan stored).
+//
+// With the plan P of potentials f, g at eps (row sums ma, column sums mb) and a
+// direction V [n][d], dC_ij = 2 (x_i - y_j) . v_i and
+//     r_i = sum_j P_ij dC_ij = 2 tv_i,       c_j = sum_i P_ij dC_ij,
+// the potentials' derivatives solve (marginals held fixed)
+//     ma_i df_i + (P dg)_i = r_i,   (P^T df)_j + mb_j dg_j = c_j,
+// i.e. S dg = rhs with S = diag(mb) - P^T diag(1/ma) P (symmetric, positive
+// semidefinite, null space the constants) and rhs = c - P^T (r / ma), solved by
+// conjugate gradients from dg = 0 (which stays orthogonal to the null space);
+// then df = (r - P dg) / ma and
+//     HV_i = (2/eps) (df_i D1_i + Du_i - 2 Tv_i) + 2 ma_i v_i,
+// with D1_i = sum_j P_ij (x_i - y_j), Du_i = sum_j P_ij dg_j (x_i - y_j) and
+// Tv_i = sum_j P_ij ((x_i - y_j) . v_i)(x_i - y_j).
+//
+// Every sum over the plan is one streaming pass (transport_pass): one row per
+// lane, keys read with wave-uniform loads, log P in fp64 as in the other plan
+// passes; the four waves of a work-group split the keys and merge in LDS in a
+// fixed order.  Conjugate-gradient vectors and dot products are fp64; one
+// work-group per pair reduces in a fixed order.  Deterministic throughout.
+#include "plan_eval.h"
+
+namespace sk {
+namespace {
+
+constexpr int kHvpWaves = 4;
+enum : int { F_V = 1, F_U = 2, F_W = 4, F_D = 8 };
+
+// Per row i of p.X against the keys of p.Y:
+//   m0 = sum P;  mu = sum P u_j (F_U);  D1 = sum P (x - y), Du = sum P u_j (x - y) (F_D);
+//   tv = sum P (x - y).v_i, Tv = sum P ((x - y).v_i)(x - y) (F_V);  tw = sum P (x - y).w_j (F_W).
+template <typename T, int DP, int FL>
+__global__ __launch_bounds__(kHvpWaves *kWave) void transport_pass(
+    PlanArgs p, const float *__restrict__ v, const double *__restrict__ u,
+    const float *__restrict__ wk, double *__restrict__ o_m0, double *__restrict__ o_mu,
+    double *__restrict__ o_tv, double *__restrict__ o_tw, double *__restrict__ o_D1,
+    double *__restrict__ o_Du, double *__restrict__ o_Tv)
+{
+    __shared__ double red[kHvpWaves][kWave];
+    const int b = blockIdx.y;
+    const int w = wave_id_uniform();
+    const int lane = lane_id();
+    const int i = blockIdx.x * kWave + lane;
+    const bool live = i < p.n;
+    const int ic = live ? i : p.n - 1;
+    RowCtx<DP> r;
+    load_row<T, DP>(r, p, b, ic);
+    double vi[DP];
+#pragma unroll
+    for (int k = 0; k < DP; ++k)
+        vi[k] = (FL & F_V) && has_dim<DP>(k, p.d) ? (double)v[((size_t)b * p.n + ic) * p.d + k]
+                                                  : 0.0;
+    const T *Yb = (const T *)p.Y + (size_t)b * p.m * p.d;
+    const float *gb = p.g + (size_t)b * p.m;
+    const double *lbb = p.lb + (size_t)b * p.m;
+    double m0 = 0.0, mu = 0.0, tv = 0.0, tw = 0.0;
+    double D1[DP], Du[DP], Tv[DP];
+#pragma unroll
+    for (int k = 0; k < DP; ++k)
+        D1[k] = Du[k] = Tv[k] = 0.0;
+    for (int j = w; j < p.m; j += kHvpWaves) {
+        double C;
+        const double lp = log_plan<T, DP>(r, p, Yb, gb, lbb[j], j, &C);
+        const double P = (double)ex2((float)(lp * 1.4426950408889634));
+        const T *y = Yb + (size_t)j * p.d;
+        double diff[DP];
+#pragma unroll
+        for (int k = 0; k < DP; ++k)
+            diff[k] = has_dim<DP>(k, p.d) ? (double)r.x[k] - (double)Elem<T>::get(y, k) : 0.0;
+        m0 += P;
+        double uj = 0.0;
+        if (FL & F_U) {
+            uj = u[(size_t)b * p.m + j];
+            mu = fma(P, uj, mu);
+        }
+        if (FL & F_D) {
+#pragma unroll
+            for (int k = 0; k < DP; ++k) {
+                D1[k] = fma(P, diff[k], D1[k]);
+                if (FL & F_U)
+                    Du[k] = fma(P * uj, diff[k], Du[k]);
+            }
+        }
+        if (FL & F_V) {
+            double dv = 0.0;
+#pragma unroll
+            for (int k = 0; k < DP; ++k)
+                dv = fma(diff[k], vi[k], dv);
+            tv = fma(P, dv, tv);
+#pragma unroll
+            for (int k = 0; k < DP; ++k)
+                Tv[k] = fma(P * dv, diff[k], Tv[k]);
+        }
+        if (FL & F_W) {
+            const float *wj = wk + ((size_t)b * p.m + j) * p.d;
+            double dw = 0.0;
+#pragma unroll
+            for (int k = 0; k < DP; ++k)
+                if (has_dim<DP>(k, p.d))
+                    dw = fma(diff[k], (double)wj[k], dw);
+            tw = fma(P, dw, tw);
+        }
+    }
+    // merge the waves' partial sums in a fixed order, one quantity at a time
+    auto merged = [&](double val) {
+        __syncthreads();
+        red[w][lane] = val;
+        __syncthreads();
+        double s = red[0][lane];
+#pragma unroll
+        for (int v2 = 1; v2 < kHvpWaves; ++v2)
+            s += red[v2][lane];
+        return s;
+    };
+    const size_t ri = (size_t)b * p.n + i;
+    {
+        const double s = merged(m0);
+        if (w == 0 && live && o_m0)
+            o_m0[ri] = s;
+    }
+    if (FL & F_U) {
+        const double s = merged(mu);
+        if (w == 0 && live && o_mu)
+            o_mu[ri] = s;
+    }
+    if (FL & F_V) {
+        const double s = merged(tv);
+        if (w == 0 && live && o_tv)
+            o_tv[ri] = s;
+    }
+    if (FL & F_W) {
+        const double s = merged(tw);
+        if (w == 0 && live && o_tw)
+            o_tw[ri] = s;
+    }
+#pragma unroll
+    for (int k = 0; k < DP; ++k) {
+        if (!has_dim<DP>(k, p.d))   // uniform: every thread skips alike
+            continue;
+        if (FL & F_D) {
+            const double s = merged(D1[k]);
+            if (w == 0 && live && o_D1)
+                o_D1[ri * p.d + k] = s;
+            if (FL & F_U) {
+                const double s2 = merged(Du[k]);
+                if (w == 0 && live && o_Du)
+                    o_Du[ri * p.d + k] = s2;
+            }
+        }
+        if (FL & F_V) {
+            const double s = merged(Tv[k]);
+            if (w == 0 && live && o_Tv)
+                o_Tv[ri * p.d + k] = s;
+        }
+    }
+}
+
+// out_i = num_i / den_i (0 where den_i = 0), times scale
+__global__ void ratio_kernel(const double *__restrict__ num, const double *__restrict__ den,
+                             size_t count, double scale, double *__restrict__ out)
+{
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < count)
+        out[i] = den[i] > 0.0 ? scale * num[i] / den[i] : 0.0;
+}
+
+// rhs_j = -2 tw_j - mu_j  (c_j = -2 tw_j when the pass ran with rows Y, keys X)
+__global__ void rhs_kernel(const double *__restrict__ tw, const double *__restrict__ mu,
+                           size_t count, double *__restrict__ rhs)
+{
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < count)
+        rhs[i] = -2.0 * tw[i] - mu[i];
+}
+
+__device__ double block_sum(double v, double *sm)
+{
+    const int t = threadIdx.x;
+    sm[t] = v;
+    __syncthreads();
+    for (int s = 128; s > 0; s >>= 1) {
+        if (t < s)
+            sm[t] += sm[t + s];
+        __syncthreads();
+    }
+    const double r = sm[0];
+    __syncthreads();
+    return r;
+}
+
+// x = 0, res = rhs, dir = rhs, rr = rr0 = |rhs|^2 (one work-group per pair)
+__global__ __launch_bounds__(256) void cg_start(const double *__restrict__ rhs, int m,
+                                                double *__restrict__ x, double *__restrict__ res,
+                                                double *__restrict__ dir, double *__restrict__ rr,
+                                                double *__restrict__ rr0)
+{
+    __shared__ double sm[256];
+    const int b = blockIdx.x;
+    double acc = 0.0;
+    for (int j = threadIdx.x; j < m; j += 256) {
+        const size_t k = (size_t)b * m + j;
+        const double v = rhs[k];
+        x[k] = 0.0;
+        res[k] = v;
+        dir[k] = v;
+        acc = fma(v, v, acc);
+    }
+    const double s = block_sum(acc, sm);
+    if (threadIdx.x == 0) {
+        rr[b] = s;
+        rr0[b] = s;
+    }
+}
+
+// One conjugate-gradient step, with S dir = mb o dir - q2 (q2 = P^T((P dir)/ma)).
+__global__ __launch_bounds__(256) void cg_step(const double *__restrict__ mb,
+                                               const double *__restrict__ q2, int m,
+                                               double *__restrict__ x, double *__restrict__ res,
+                                               double *__restrict__ dir, double *__restrict__ rr)
+{
+    __shared__ double sm[256];
+    const int b = blockIdx.x;
+    double acc = 0.0;
+    for (int j = threadIdx.x; j < m; j += 256) {
+        const size_t k = (size_t)b * m + j;
+        const double q = fma(mb[k], dir[k], -q2[k]);
+        acc = fma(dir[k], q, acc);
+    }
+    const double pq = block_sum(acc, sm);
+    const double rr_old = rr[b];
+    const double alpha = pq > 0.0 ? rr_old / pq : 0.0;
+    acc = 0.0;
+    for (int j = threadIdx.x; j < m; j += 256) {
+        const size_t k = (size_t)b * m + j;
+        const double q = fma(mb[k], dir[k], -q2[k]);
+        x[k] = fma(alpha, dir[k], x[k]);
+        res[k] = fma(-alpha, q, res[k]);
+        acc = fma(res[k], res[k], acc);
+    }
+    const double rr_new = block_sum(acc, sm);
+    const double beta = rr_old > 0.0 ? rr_new / rr_old : 0.0;
+    for (int j = threadIdx.x; j < m; j += 256) {
+        const size_t k = (size_t)b * m + j;
+        dir[k] = fma(beta, dir[k], res[k]);
+    }
+    if (threadIdx.x == 0)
+        rr[b] = rr_new;
+}
+
+// HV_i = (2/eps)(df_i D1_i + Du_i - 2 Tv_i) + 2 ma_i v_i,  df_i = (2 tv_i - (P dg)_i) / ma_i
+__global__ void hv_kernel(const double *__restrict__ ma, const double *__restrict__ tv,
+                          const double *__restrict__ pdg, const double *__restrict__ D1,
+                          const double *__restrict__ Du, const double *__restrict__ Tv,
+                          const float *__restrict__ V, size_t rows, int d, double inv_eps,
+                          float *__restrict__ HV)
+{
+    const size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= rows * d)
+        return;
+    const size_t i = e / d;
+    const double df = ma[i] > 0.0 ? (2.0 * tv[i] - pdg[i]) / ma[i] : 0.0;
+    const double h = 2.0 * inv_eps * (df * D1[e] + Du[e] - 2.0 * Tv[e]) + 2.0 * ma[i] * (double)V[e];
+    HV[e] = (float)h;
+}
+
+__global__ void cg_report(const double *__restrict__ rr, const double *__restrict__ rr0, int B,
+                          float *__restrict__ out)
+{
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b < B)
+        out[b] = rr0[b] > 0.0 ? (float)sqrt(rr[b] / rr0[b]) : 0.f;
+}
+
+template <int FL>
+void pass(const PlanArgs &p, const float *v, const double *u, const float *wk, double *m0,
+          double *mu, double *tv, double *tw, double *D1, double *Du, double *Tv, hipStream_t st)
+{
+    dim3 grid(ceil_div(p.n, kWave), p.B), block(kHvpWaves * kWave);
+    auto go = [&]<int DP>() {
+        if (p.dtype == 1)
+            hipLaunchKernelGGL((transport_pass<uint16_t, DP, FL>), grid, block, 0, st, p, v, u, wk,
+                               m0, mu, tv, tw, D1, Du, Tv);
+        else
+            hipLaunchKernelGGL((transport_pass<float, DP, FL>), grid, block, 0, st, p, v, u, wk,
+                               m0, mu, tv, tw, D1, Du, Tv);
+    };
+    if (p.d == 3) go.template operator()<3>();
+    else if (p.d <= 4) go.template operator()<4>();
+    else if (p.d <= 8) go.template operator()<8>();
+    else go.template operator()<16>();
+}
+
+unsigned blocks_for(size_t count) { return (unsigned)((count + 255) / 256); }
+
+}  // namespace
+
+hipError_t launch_hvp(const PlanArgs &px, const PlanArgs &py, const float *V, int cg_iters,
+                      float *HV, float *cg_residual, const HvpWs &w, hipStream_t st)
+{
+    const int B = px.B, n = px.n, m = px.m, d = px.d;
+    const size_t Bn = (size_t)B * n, Bm = (size_t)B * m;
+    // rows X: ma, D1, tv, Tv
+    pass<F_V | F_D>(px, V, nullptr, nullptr, w.ma, nullptr, w.tv, nullptr, w.D1, nullptr, w.Tv,
+                    st);
+    // u_i = r_i / ma_i = 2 tv_i / ma_i; rows Y (keys X carry v): mb, P^T u, tw
+    hipLaunchKernelGGL(ratio_kernel, dim3(blocks_for(Bn)), dim3(256), 0, st,
+                       (const double *)w.tv, (const double *)w.ma, Bn, 2.0, w.ur);
+    pass<F_U | F_W>(py, nullptr, w.ur, V, w.mb, w.muc, nullptr, w.tw, nullptr, nullptr, nullptr,
+                    st);
+    hipLaunchKernelGGL(rhs_kernel, dim3(blocks_for(Bm)), dim3(256), 0, st, (const double *)w.tw,
+                       (const double *)w.muc, Bm, w.rhs);
+    hipLaunchKernelGGL(cg_start, dim3(B), dim3(256), 0, st, (const double *)w.rhs, m, w.x, w.res,
+                       w.dir, w.rr, w.rr0);
+    for (int it = 0; it < cg_iters; ++it) {
+        // q2 = P^T ((P dir) / ma)
+        pass<F_U>(px, nullptr, w.dir, nullptr, nullptr, w.mur, nullptr, nullptr, nullptr,
+                  nullptr, nullptr, st);
+        hipLaunchKernelGGL(ratio_kernel, dim3(blocks_for(Bn)), dim3(256), 0, st,
+                           (const double *)w.mur, (const double *)w.ma, Bn, 1.0, w.ur);
+        pass<F_U>(py, nullptr, w.ur, nullptr, nullptr, w.muc, nullptr, nullptr, nullptr, nullptr,
+                  nullptr, st);
+        hipLaunchKernelGGL(cg_step, dim3(B), dim3(256), 0, st, (const double *)w.mb,
+                           (const double *)w.muc, m, w.x, w.res, w.dir, w.rr);
+    }
+    // rows X with u = dg: P dg and Du
+    // (D1 comes out bit-identical to the first pass's and is simply rewritten)
+    pass<F_U | F_D>(px, nullptr, w.x, nullptr, nullptr, w.mur, nullptr, nullptr, w.D1, w.Du,
+                    nullptr, st);
+    hipLaunchKernelGGL(hv_kernel, dim3(blocks_for(Bn * d)), dim3(256), 0, st,
+                       (const double *)w.ma, (const double *)w.tv, (const double *)w.mur,
+                       (const double *)w.D1, (const double *)w.Du, (const double *)w.Tv, V, Bn, d,
+                       px.inv_eps, HV);
+    if (cg_residual)
+        hipLaunchKernelGGL(cg_report, dim3(blocks_for(B)), dim3(256), 0, st, (const double *)w.rr,
+                           (const double *)w.rr0, B, cg_residual);
+    return hipGetLastError();
+}
+
+}  // namespace sk

@@ -53,7 +53,7 @@ def test_status_strings(lib):
 
 def test_workspace_bytes(lib):
     ws = lib.sinkhorn_workspace_bytes
-    for op in (0, 1, 2, 3):
+    for op in (0, 1, 2, 3, 4):
         assert ws(op, 1, 1024, 1024, 3, 0) > 0
         assert ws(op, 2, 1024, 1024, 3, 0) > ws(op, 1, 1024, 1024, 3, 0)
         assert ws(op, 1, 4096, 1024, 3, 0) > ws(op, 1, 1024, 1024, 3, 0)
@@ -62,7 +62,7 @@ def test_workspace_bytes(lib):
     assert ws(0, 1, 10, 10, 3, 1) > 0                  # bf16 d=3: feature kernel
     assert ws(0, 1, 10, 10, 200, 0) == 0               # d > 128: no kernel
     assert ws(0, 0, 10, 10, 3, 0) == 0
-    assert ws(4, 1, 10, 10, 3, 0) == 0
+    assert ws(5, 1, 10, 10, 3, 0) == 0
     assert ws(3, 1, 65536, 65536, 3, 0) < 4 << 20      # two fp64 log-weight vectors
     assert ws(0, 1, 1 << 25, 10, 3, 0) == 0
 
@@ -176,6 +176,21 @@ def test_normalize_rejects_bad_arguments_without_writing(lib, kw):
     assert np.all(xh == 3.0) and np.all(nr == 3.0)
     rc = lib.sinkhorn_normalize_backward(DUMMY, DUMMY, None, 1, 4, 3, _host(xh), None)
     assert rc == sk.SK_ERR_INVALID_ARG and np.all(xh == 3.0)
+
+
+def test_hvp_rejects_bad_arguments_without_writing(lib):
+    assert lib.sinkhorn_workspace_bytes(4, 1, 100, 90, 3, 0) > 0
+    assert lib.sinkhorn_workspace_bytes(4, 1, 100, 90, 17, 0) == 0     # d > 16
+    hv = np.full(8 * 3, 2.0, dtype=np.float32)
+    for kw, code in ((dict(d=17), sk.SK_ERR_UNSUPPORTED), (dict(eps=0.0), sk.SK_ERR_INVALID_ARG),
+                     (dict(it=-1), sk.SK_ERR_INVALID_ARG), (dict(V=None), sk.SK_ERR_INVALID_ARG),
+                     (dict(ws=None), sk.SK_ERR_WORKSPACE)):
+        a = dict(d=3, eps=0.1, it=10, V=DUMMY, ws=DUMMY)
+        a.update(kw)
+        rc = lib.sinkhorn_hvp(DUMMY, DUMMY, 0, None, None, 1, 8, 9, a["d"], a["eps"], DUMMY, DUMMY,
+                              a["V"], a["it"], _host(hv), None, a["ws"], 1 << 40, None)
+        assert rc == code, (kw, lib.sinkhorn_last_error())
+    assert np.all(hv == 2.0)
 
 
 def test_coo_normalize_rejects_bad_arguments(lib):

@@ -628,3 +628,42 @@ def test_workload_coo_normalize_sampled_pairs(name, pairs):
     torch.cuda.synchronize()
     np.testing.assert_allclose(host(P[2]), v_o, rtol=1e-4, atol=0)
     np.testing.assert_allclose(host(err), err_o, rtol=1e-3, atol=1e-6)
+
+
+# ------------------------------------------------------- Hessian-vector product
+@pytest.mark.parametrize("B,n,m,d,dtype,eps", [(1, 40, 50, 3, "f32", 0.1),
+                                                (2, 120, 90, 3, "f32", 0.05),
+                                                (1, 64, 70, 8, "f32", 0.2),
+                                                (1, 50, 45, 16, "bf16", 0.5)])
+def test_hvp_matches_oracle(B, n, m, d, dtype, eps):
+    c = workloads.random_case(21, B, n, m, d, weights="dirichlet", dtype=dtype)
+    fo, go = oracle.potentials(c["X"], c["Y"], c["a"], c["b"], eps=[eps], iters=[2000])
+    f32, g32 = fo.astype(np.float32), go.astype(np.float32)
+    V = np.random.default_rng(3).normal(size=(B, n, d)).astype(np.float32)
+    X, Y = points(c)
+    HV, res = sk.hvp(X, Y, dev(c["a"]), dev(c["b"]), dev(f32), dev(g32), eps, dev(V),
+                     cg_iters=300)
+    torch.cuda.synchronize()
+    HVo = oracle.hvp(c["X"], c["Y"], c["a"], c["b"], f32.astype(np.float64),
+                     g32.astype(np.float64), np.float32(eps), V)
+    assert np.all(host(res) < 1e-4), host(res)
+    for p in range(B):
+        assert rel_inf(host(HV)[p], HVo[p]) <= 1e-4
+
+
+def test_hvp_is_linear_and_symmetric_on_gpu():
+    c = workloads.random_case(22, 1, 80, 60, 3, weights="dirichlet")
+    eps = 0.1
+    fo, go = oracle.potentials(c["X"], c["Y"], c["a"], c["b"], eps=[eps], iters=[2000])
+    X, Y, a, b = dev(c["X"]), dev(c["Y"]), dev(c["a"]), dev(c["b"])
+    f32, g32 = dev(fo.astype(np.float32)), dev(go.astype(np.float32))
+    rng = np.random.default_rng(6)
+    U = dev(rng.normal(size=(1, 80, 3)).astype(np.float32))
+    V = dev(rng.normal(size=(1, 80, 3)).astype(np.float32))
+    HU, _ = sk.hvp(X, Y, a, b, f32, g32, eps, U, cg_iters=200)
+    HV, _ = sk.hvp(X, Y, a, b, f32, g32, eps, V, cg_iters=200)
+    HW, _ = sk.hvp(X, Y, a, b, f32, g32, eps, 2.0 * U - V, cg_iters=200)
+    torch.cuda.synchronize()
+    hu, hv, hw, u, v = (host(t)[0] for t in (HU, HV, HW, U, V))
+    assert rel_inf(hw, 2.0 * hu - hv) <= 1e-5
+    assert abs((u * hv).sum() - (v * hu).sum()) <= 1e-5 * np.abs(u * hv).sum()
