@@ -77,6 +77,9 @@ SMALL = [  # (B, n, m, weights, zero weights, eps, iters)
     (1, 1, 999, "dirichlet", 0, [0.2], [4]),
     (2, 129, 1030, "dirichlet", 0, [1.0, 0.3, 0.1, 0.03], [3, 3, 3, 10]),
     (1, 2000, 1500, "dirichlet", 0, [0.01], [30]),
+    # few rows against long key ranges: the key range is split across work-groups
+    (1, 100, 12000, "dirichlet", 0, [0.05, 0.02], [4, 6]),
+    (2, 9000, 70, "uniform", 3, [0.03], [8]),
 ]
 
 
