@@ -256,10 +256,14 @@ static void acc_add(acc_t *a, double v)
 }
 static double acc_get(const acc_t *a) { return a->s + a->c; }
 
+/* log P_ij = (f_i + g_j - C_ij)/eps + log a_i + log b_j.  The two log weights
+ * are added to each other first, so every rounding is symmetric in the two
+ * sides and the plan of (Y, X) is exactly the transpose of the plan of (X, Y),
+ * values included. */
 static double log_plan(const double *x, const double *y, int d, double fi, double gj,
                        double lai, double lbj, double eps)
 {
-    return (fi + gj - sq_dist(x, y, d)) / eps + lai + lbj;
+    return (fi + gj - sq_dist(x, y, d)) / eps + (lai + lbj);
 }
 
 /*
