@@ -166,17 +166,15 @@ def main():
                torch.empty(B + 1, dtype=torch.int64, device=dev))
         coo_ws = torch.empty(sk.workspace_bytes(sk.SK_OP_PLAN_COO, B, n, m, d, dt),
                              dtype=torch.uint8, device=dev)
-        lg_ws = torch.empty(sk.workspace_bytes(sk.SK_OP_LOSS_GRAD, B, n, m, d, dt),
-                            dtype=torch.uint8, device=dev)
         loss_out = (torch.empty(B, device=dev), torch.empty(B, n, d, device=dev))
 
     def step(it=iters, with_cost=with_cost_default):
         sk.potentials(X, Y, a, b, eps=eps, iters=it, out=(f, g, cost if with_cost else None),
                       cost=with_cost, workspace=ws, valu_scores=args.valu_scores)
         if sparse:
-            rows, cols, vals, offs = sk.plan_coo(X, Y, a, b, f, g, eps[-1], w["threshold"],
-                                                 workspace=coo_ws, out=coo)
-            sk.loss_grad(X, Y, rows, cols, vals, offs, workspace=lg_ws, out=loss_out)
+            # the loss and dL/dX are accumulated while the plan is emitted
+            sk.plan_coo(X, Y, a, b, f, g, eps[-1], w["threshold"], workspace=coo_ws, out=coo,
+                        loss_out=loss_out)
 
     def timed(fn, reps):
         torch.cuda.synchronize()
@@ -233,7 +231,8 @@ def main():
                    "iters": total_iters,
                    "outputs": ("potentials, COO plan at %g x max P per pair, loss and dL/dX"
                                % w["threshold"]) if sparse
-                   else "potentials f, g and transport cost"},
+                   else "potentials f, g and transport cost",
+                   **({"plan_entries": int(coo[3][-1].item())} if sparse else {})},
         "roofline": {"bound": bound, "achieved": achieved / 1e12, "peak": peak / 1e12,
                      "unit": "Teval/s", "frac": achieved / peak,
                      "traffic": measured_traffic(kernel, w["name"], KERNEL_SOURCES[kernel])
@@ -262,10 +261,11 @@ def main():
                          out=(t_rows, t_cols, t_vals, t_offs))
         cn_ws = torch.empty(sk.load_library().sinkhorn_coo_workspace_bytes(B, n, m, rows.numel()),
                             dtype=torch.uint8, device=dev)
-        base = vals.clone()
+        base, t_base = vals.clone(), tr[2].clone()
 
         def normalise():
             vals.copy_(base)
+            tr[2].copy_(t_base)
             sk.coo_normalize((rows, cols, vals, offs), tr, a, b, n, m, 10, workspace=cn_ws)
 
         normalise()

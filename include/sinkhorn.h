@@ -136,15 +136,24 @@ int sinkhorn_potentials(const void *X, const void *Y, int dtype,
  * *nnz_total (HOST int64) always receives the number of kept entries.  If it
  * exceeds `capacity`, the call returns SK_ERR_CAPACITY after writing
  * pair_offsets and *nnz_total only; rows/cols/vals may be NULL when capacity
- * is 0.  This is the one entry point that waits on `stream`: it synchronises
- * once to read the count back.
+ * is 0.  The call synchronises `stream` once, to read the count back.
+ *
+ * loss [B] and dX [B][n][d] (fp32, device, each may be NULL) receive, in the
+ * same pass, the transport loss on the emitted support and its gradient in X
+ * with the plan held fixed [AP Abstract: gradients preserved on the stored
+ * support]:
+ *     loss[p] = sum_k vals_k ||x_{rows_k} - y_{cols_k}||^2,
+ *     dX[p][i] = sum_{k: rows_k = i} 2 vals_k (x_i - y_{cols_k}),
+ * i.e. what sinkhorn_loss_grad computes from the emitted plan, with the same
+ * per-entry arithmetic (the summation order differs, so the two agree to
+ * rounding).  Rows with no entry get a zero gradient.
  */
 int sinkhorn_plan_coo(const void *X, const void *Y, int dtype,
                       const float *a, const float *b,
                       int B, int n, int m, int d, float eps,
                       const float *f, const float *g, float rel_threshold,
                       int64_t capacity, int32_t *rows, int32_t *cols, float *vals,
-                      int64_t *pair_offsets, int64_t *nnz_total,
+                      int64_t *pair_offsets, float *loss, float *dX, int64_t *nnz_total,
                       void *ws, size_t ws_bytes, void *stream);
 
 /*
@@ -216,27 +225,30 @@ int sinkhorn_hvp(const void *X, const void *Y, int dtype,
  * Innovation: Sinkhorn normalisation run directly in COO form].
  *
  * rows/cols/vals/pair_offsets: a plan as sinkhorn_plan_coo writes it (per pair
- * sorted by row, then column; B+1 offsets); t_rows/t_cols/t_pair_offsets: its
- * transpose, i.e. the plan extracted with the roles of the clouds exchanged
- * (sinkhorn_plan_coo(Y, X, b, a, g, f, ...)), which holds exactly the same
- * entries because log P is evaluated symmetrically.  Per pair, with
- * lv = log vals, row scalings alpha and column scalings beta start at 0 and
- * each of `iters` rounds sets
+ * sorted by row, then column; B+1 offsets); t_rows/t_cols/t_vals/
+ * t_pair_offsets: its transpose, i.e. the plan extracted with the roles of the
+ * clouds exchanged (sinkhorn_plan_coo(Y, X, b, a, g, f, ...)), which holds
+ * exactly the same entries and values because log P is evaluated
+ * symmetrically.  Per pair, with lv = log vals, row scalings alpha and column
+ * scalings beta start at 0 and each of `iters` rounds sets
  *     alpha_i = log a_i - LSE_{k in row i}(lv_k + beta_{col k}),
  *     beta_j  = log b_j - LSE_{k in col j}(lv_k + alpha_{row k})
  * (0 for a row or column without a finite term); then
- * vals_k <- exp(lv_k + alpha_{row k} + beta_{col k}) in place: column sums equal
- * b, row sums approach a.  err [2B] (device, may be NULL) receives per pair
- * sum_i |row sum - a_i| and sum_j |column sum - b_j| of the result.  a, b may
- * be NULL (uniform).  Workspace: sinkhorn_coo_workspace_bytes(B, n, m, nnz).
- * Synchronises twice on `stream` (entry counts, transpose check); a transpose
- * that does not match the plan returns SK_ERR_INVALID_ARG with vals unchanged.
+ * vals_k <- exp(lv_k + alpha_{row k} + beta_{col k}) in place, in both the plan
+ * and the transpose (which stay each other's transpose bit for bit): column
+ * sums equal b, row sums approach a.  err [2B] (device, may be NULL) receives
+ * per pair sum_i |row sum - a_i| and sum_j |column sum - b_j| of the result.
+ * a, b may be NULL (uniform).  Workspace: sinkhorn_coo_workspace_bytes(B, n, m,
+ * nnz).  Synchronises twice on `stream` (entry counts, transpose check).  The
+ * transpose is checked per pair by entry count and by a 64-bit checksum of
+ * every entry's (row, column, value bits); a mismatch returns
+ * SK_ERR_INVALID_ARG with both value arrays unchanged.
  */
 size_t sinkhorn_coo_workspace_bytes(int B, int n, int m, int64_t nnz);
 int sinkhorn_coo_normalize(int B, int n, int m,
                            const int32_t *rows, const int32_t *cols, float *vals,
                            const int64_t *pair_offsets,
-                           const int32_t *t_rows, const int32_t *t_cols,
+                           const int32_t *t_rows, const int32_t *t_cols, float *t_vals,
                            const int64_t *t_pair_offsets,
                            const float *a, const float *b, int iters, float *err,
                            void *ws, size_t ws_bytes, void *stream);

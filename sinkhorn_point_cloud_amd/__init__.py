@@ -67,7 +67,7 @@ def load_library():
     lib.sinkhorn_potentials.argtypes = [P, P, I, P, P, I, I, I, I, P, P, I, U, P, P, P, P, Z, P]
     lib.sinkhorn_potentials.restype = I
     lib.sinkhorn_plan_coo.argtypes = [P, P, I, P, P, I, I, I, I, F, P, P, F, L, P, P, P, P, P,
-                                      P, Z, P]
+                                      P, P, P, Z, P]
     lib.sinkhorn_plan_coo.restype = I
     lib.sinkhorn_loss_grad.argtypes = [P, P, I, I, I, I, I, P, P, P, P, P, P, P, Z, P]
     lib.sinkhorn_loss_grad.restype = I
@@ -77,7 +77,7 @@ def load_library():
     lib.sinkhorn_hvp.restype = I
     lib.sinkhorn_coo_workspace_bytes.argtypes = [I, I, I, L]
     lib.sinkhorn_coo_workspace_bytes.restype = Z
-    lib.sinkhorn_coo_normalize.argtypes = [I, I, I, P, P, P, P, P, P, P, P, P, I, P, P, Z, P]
+    lib.sinkhorn_coo_normalize.argtypes = [I, I, I, P, P, P, P, P, P, P, P, P, P, I, P, P, Z, P]
     lib.sinkhorn_coo_normalize.restype = I
     lib.sinkhorn_normalize.argtypes = [P, I, I, I, I, P, P, P]
     lib.sinkhorn_normalize.restype = I
@@ -186,13 +186,16 @@ def potentials(X, Y, a=None, b=None, eps=(0.05,), iters=(100,), f0=None, g0=None
 
 
 def plan_coo(X, Y, a, b, f, g, eps: float, rel_threshold: float = 1e-8, capacity=None,
-             workspace=None, out=None):
+             workspace=None, out=None, loss_out=None):
     """Thresholded sparse plan: (rows int32, cols int32, vals float32, pair_offsets int64[B+1]).
 
     With capacity=None the plan is counted first, then emitted into buffers of
     exactly the right size (two calls of the C entry point).  ``out`` = (rows,
     cols, vals, pair_offsets) reuses buffers; its length is the capacity, and
-    a plan that does not fit raises SinkhornError(SK_ERR_CAPACITY)."""
+    a plan that does not fit raises SinkhornError(SK_ERR_CAPACITY).
+    ``loss_out`` = (loss [B], dX [B,n,d]) float32 tensors (either may be None)
+    receive the loss on the emitted support and its gradient in X, computed
+    during the emission."""
     lib = load_library()
     X, Y, dt = _points(X, Y)
     B, n, d = X.shape
@@ -202,6 +205,12 @@ def plan_coo(X, Y, a, b, f, g, eps: float, rel_threshold: float = 1e-8, capacity
     f = f.reshape(B, n).contiguous().float()
     g = g.reshape(B, m).contiguous().float()
     ws = _workspace(SK_OP_PLAN_COO, B, n, m, d, dt, dev, workspace)
+    loss, dX = loss_out if loss_out is not None else (None, None)
+    for t, shape in ((loss, (B,)), (dX, (B, n, d))):
+        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != shape
+                              or not t.is_contiguous() or t.device != dev):
+            raise ValueError(f"loss_out tensors must be contiguous float32 of shape {shape} "
+                             f"on {dev}")
     nnz = ctypes.c_int64(0)
     if out is not None:
         rows, cols, vals, offs = out
@@ -216,8 +225,8 @@ def plan_coo(X, Y, a, b, f, g, eps: float, rel_threshold: float = 1e-8, capacity
     def call(cap, rows, cols, vals):
         return lib.sinkhorn_plan_coo(_ptr(X), _ptr(Y), dt, _ptr(a), _ptr(b), B, n, m, d,
                                      float(eps), _ptr(f), _ptr(g), float(rel_threshold), cap,
-                                     _ptr(rows), _ptr(cols), _ptr(vals), _ptr(offs),
-                                     ctypes.byref(nnz), _ptr(ws), ws.numel(), _stream())
+                                     _ptr(rows), _ptr(cols), _ptr(vals), _ptr(offs), _ptr(loss),
+                                     _ptr(dX), ctypes.byref(nnz), _ptr(ws), ws.numel(), _stream())
 
     rc = call(cap, rows, cols, vals)
     if rc == SK_ERR_CAPACITY and capacity is None and out is None:
@@ -325,12 +334,13 @@ def coo_normalize(plan, transpose, a, b, n, m, iters, err=True, workspace=None):
     """Sinkhorn normalisation of a sparse plan on its support, in place.
 
     plan = (rows, cols, vals, pair_offsets) as plan_coo returns it; transpose =
-    the plan of the exchanged clouds (plan_coo(Y, X, b, a, g, f, ...)), whose
-    (rows, cols, _, pair_offsets) are used.  Returns err [B,2] (float32:
-    sum |row sums - a| and sum |column sums - b| per pair) or None."""
+    the plan of the exchanged clouds (plan_coo(Y, X, b, a, g, f, ...)), which
+    must hold the same entries and values; both value arrays are rescaled in
+    place.  Returns err [B,2] (float32: sum |row sums - a| and
+    sum |column sums - b| per pair) or None."""
     lib = load_library()
     rows, cols, vals, offs = plan
-    t_rows, t_cols, _, t_offs = transpose
+    t_rows, t_cols, t_vals, t_offs = transpose
     B = offs.numel() - 1
     dev = vals.device
     a, b = _weights(a, B, n, dev), _weights(b, B, m, dev)
@@ -345,8 +355,9 @@ def coo_normalize(plan, transpose, a, b, n, m, iters, err=True, workspace=None):
         return _ptr(t if t.numel() else one)
 
     rc = lib.sinkhorn_coo_normalize(B, n, m, p(rows), p(cols), p(vals), _ptr(offs), p(t_rows),
-                                    p(t_cols), _ptr(t_offs), _ptr(a), _ptr(b), int(iters), _ptr(e),
-                                    _ptr(workspace), workspace.numel(), _stream())
+                                    p(t_cols), p(t_vals), _ptr(t_offs), _ptr(a), _ptr(b),
+                                    int(iters), _ptr(e), _ptr(workspace), workspace.numel(),
+                                    _stream())
     _check(rc)
     return e
 

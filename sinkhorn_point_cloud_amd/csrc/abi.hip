@@ -171,14 +171,15 @@ CooNormWs carve_coo_norm(Carve &c, int B, int n, int m, int64_t nnz)
     w.re = c.take<int64_t>((size_t)B * n);
     w.cb = c.take<int64_t>((size_t)B * m);
     w.ce = c.take<int64_t>((size_t)B * m);
-    w.perm = c.take<int64_t>(nnz > 0 ? (size_t)nnz : 1);
     w.lv = c.take<float>(nnz > 0 ? (size_t)nnz : 1);
+    w.lvt = c.take<float>(nnz > 0 ? (size_t)nnz : 1);
     w.al = c.take<double>((size_t)B * n);
     w.la = c.take<double>((size_t)B * n);
     w.be = c.take<double>((size_t)B * m);
     w.lb = c.take<double>((size_t)B * m);
     w.row_part = c.take<double>((size_t)B * n);
     w.col_part = c.take<double>((size_t)B * m);
+    w.sums = c.take<uint64_t>((size_t)2 * B);
     w.bad = c.take<int>(1);
     return w;
 }
@@ -388,8 +389,8 @@ int sinkhorn_potentials(const void *X, const void *Y, int dtype, const float *a,
 int sinkhorn_plan_coo(const void *X, const void *Y, int dtype, const float *a, const float *b,
                       int B, int n, int m, int d, float eps, const float *f, const float *g,
                       float rel_threshold, int64_t capacity, int32_t *rows, int32_t *cols,
-                      float *vals, int64_t *pair_offsets, int64_t *nnz_total, void *ws,
-                      size_t ws_bytes, void *stream)
+                      float *vals, int64_t *pair_offsets, float *loss, float *dX,
+                      int64_t *nnz_total, void *ws, size_t ws_bytes, void *stream)
 {
     g_err[0] = '\0';
     int rc = check_common(X, Y, dtype, B, n, m, d);
@@ -430,8 +431,10 @@ int sinkhorn_plan_coo(const void *X, const void *Y, int dtype, const float *a, c
     if (total > capacity)
         return fail(SK_ERR_CAPACITY, "sparse plan has %lld entries, capacity is %lld",
                     (long long)total, (long long)capacity);
-    if (total > 0 &&
-        (e = launch_plan_emit(p, w.pair_thr, w.row_off, w.row_count, rows, cols, vals, st)))
+    // row_max is free once the threshold is known: it takes the per-row loss
+    if ((total > 0 || loss || dX) &&
+        (e = launch_plan_emit(p, w.pair_thr, w.row_off, w.row_count, rows, cols, vals, w.row_max,
+                              loss, dX, st)))
         return hip_fail(e, "plan emit");
     return SK_OK;
 }
@@ -565,15 +568,16 @@ size_t sinkhorn_coo_workspace_bytes(int B, int n, int m, int64_t nnz)
 
 int sinkhorn_coo_normalize(int B, int n, int m, const int32_t *rows, const int32_t *cols,
                            float *vals, const int64_t *pair_offsets, const int32_t *t_rows,
-                           const int32_t *t_cols, const int64_t *t_pair_offsets, const float *a,
-                           const float *b, int iters, float *err, void *ws, size_t ws_bytes,
-                           void *stream)
+                           const int32_t *t_cols, float *t_vals, const int64_t *t_pair_offsets,
+                           const float *a, const float *b, int iters, float *err, void *ws,
+                           size_t ws_bytes, void *stream)
 {
     g_err[0] = '\0';
     if (B < 1 || n < 1 || m < 1 || n > kMaxPoints || m > kMaxPoints ||
         (long long)B * n > (1ll << 31) || (long long)B * m > (1ll << 31))
         return fail(SK_ERR_INVALID_ARG, "bad sizes B=%d n=%d m=%d", B, n, m);
-    if (!rows || !cols || !vals || !pair_offsets || !t_rows || !t_cols || !t_pair_offsets)
+    if (!rows || !cols || !vals || !pair_offsets || !t_rows || !t_cols || !t_vals ||
+        !t_pair_offsets)
         return fail(SK_ERR_INVALID_ARG, "the plan, its transpose and both offset arrays must be "
                                         "non-NULL device pointers");
     if (iters < 0)
@@ -599,16 +603,18 @@ int sinkhorn_coo_normalize(int B, int n, int m, const int32_t *rows, const int32
     if ((e = launch_log_weights(a, B, n, w.la, st)) || (e = launch_log_weights(b, B, m, w.lb, st)) ||
         (e = launch_segment_bounds(rows, pair_offsets, B, n, w.rb, w.re, st)) ||
         (e = launch_segment_bounds(t_rows, t_pair_offsets, B, m, w.cb, w.ce, st)) ||
-        (e = launch_coo_perm(cols, t_rows, t_cols, t_pair_offsets, B, n, m, w, st)))
+        (e = launch_coo_check(rows, cols, vals, pair_offsets, t_rows, t_cols, t_vals,
+                              t_pair_offsets, B, w, st)))
         return hip_fail(e, "coo normalisation set-up");
     int bad = 0;
     if ((e = hipMemcpyAsync(&bad, w.bad, sizeof bad, hipMemcpyDeviceToHost, st)) ||
         (e = hipStreamSynchronize(st)))
         return hip_fail(e, "read transpose check");
     if (bad)
-        return fail(SK_ERR_INVALID_ARG, "%d entries of the transpose are not in the plan", bad);
-    if ((e = launch_coo_normalize(rows, cols, vals, pair_offsets, t_cols, B, n, m, nnz, iters, err,
-                                  a, b, w, st)))
+        return fail(SK_ERR_INVALID_ARG,
+                    "the transpose does not hold the plan's entries and values in %d pair(s)", bad);
+    if ((e = launch_coo_normalize(rows, cols, vals, pair_offsets, t_rows, t_cols, t_vals,
+                                  t_pair_offsets, B, n, m, nnz, iters, err, a, b, w, st)))
         return hip_fail(e, "coo normalisation");
     return SK_OK;
 }

@@ -192,9 +192,13 @@ hipError_t launch_plan_count(const PlanArgs &p, const double *pair_thr, int32_t 
                              hipStream_t st);
 hipError_t launch_plan_scan(const int32_t *row_count, int B, int n, int64_t *row_off,
                             int64_t *pair_offsets, int64_t *pair_tot, hipStream_t st);
+// Emission of the counted entries; with loss / dX (either may be NULL) also the
+// loss per pair and its gradient in X on the emitted support (row_loss: [B][n]
+// scratch, needed with loss).
 hipError_t launch_plan_emit(const PlanArgs &p, const double *pair_thr, const int64_t *row_off,
                             const int32_t *row_count, int32_t *rows, int32_t *cols,
-                            float *vals, hipStream_t st);
+                            float *vals, double *row_loss, float *loss, float *dX,
+                            hipStream_t st);
 // Dense gradient 2 sum_j P_ij (x_i - y_j) and barycentric projection
 // sum_j P_ij y_j / sum_j P_ij of every row of p.X (either output may be NULL),
 // log P in fp64.  only != NULL: just the 64-row blocks flagged there.
@@ -210,25 +214,30 @@ hipError_t launch_gradFm(const SideF &rows, const float *row_w, const SideF &key
                          float *proj, hipStream_t st);
 hipError_t launch_transpose_bf16(const void *X, int B, int n, int n_pad, int d, uint16_t *Xt,
                                  hipStream_t st);
-// Runs of equal keys in a key-sorted COO (per pair): begin/end [B][count], 0/0
-// for a key with no entries.
+// Runs of equal keys in a key-sorted COO (per pair), by binary search:
+// begin/end [B][count]; a key with no entries gets an empty run.
 hipError_t launch_segment_bounds(const int32_t *keys, const int64_t *pair_offsets, int B, int count,
                                  int64_t *begin, int64_t *end, hipStream_t st);
 // Sinkhorn normalisation of a row-sorted COO plan on its support, given its
-// transpose (column-sorted).  Workspace pieces as carved by the ABI.
+// transpose (column-sorted, the same entries and values).  Workspace pieces as
+// carved by the ABI.
 struct CooNormWs {
     int64_t *rb, *re, *cb, *ce;   // row runs of the plan, column runs of the transpose
-    int64_t *perm;                // transpose entry -> plan entry
-    float *lv;                    // log of the plan's values
+    float *lv, *lvt;              // log of the values of the plan and of the transpose
     double *al, *be, *la, *lb;    // scalings and log weights
     double *row_part, *col_part;  // per-row / per-column marginal errors
-    int *bad;                     // transpose entries with no match in the plan
+    uint64_t *sums;               // [2][B] entry checksums of the plan and the transpose
+    int *bad;                     // pairs whose transpose does not match the plan
 };
-hipError_t launch_coo_perm(const int32_t *cols, const int32_t *t_rows, const int32_t *t_cols,
-                           const int64_t *t_offs, int B, int n, int m, const CooNormWs &w,
-                           hipStream_t st);
+// Checks the transpose against the plan (per pair: entry counts and a checksum
+// of every entry's (row, column, value bits)); *w.bad = mismatching pairs.
+hipError_t launch_coo_check(const int32_t *rows, const int32_t *cols, const float *vals,
+                            const int64_t *offs, const int32_t *t_rows, const int32_t *t_cols,
+                            const float *t_vals, const int64_t *t_offs, int B, const CooNormWs &w,
+                            hipStream_t st);
 hipError_t launch_coo_normalize(const int32_t *rows, const int32_t *cols, float *vals,
-                                const int64_t *offs, const int32_t *t_cols, int B, int n, int m,
+                                const int64_t *offs, const int32_t *t_rows, const int32_t *t_cols,
+                                float *t_vals, const int64_t *t_offs, int B, int n, int m,
                                 int64_t nnz, int iters, float *err, const float *a,
                                 const float *b, const CooNormWs &w, hipStream_t st);
 // Hessian-vector product of the entropic OT value in X (d <= 16): px = plan

@@ -12,9 +12,14 @@
 //
 // Rows are runs of the row-sorted plan; columns are runs of its transpose (the
 // plan extracted with the roles of the clouds exchanged, which the symmetric
-// evaluation of log P makes entry-for-entry identical), mapped back to plan
-// entries once by binary search inside each row.  One wave reduces one row or
-// one column in a fixed order: no atomics on values, deterministic results.
+// evaluation of log P makes entry-for-entry identical, values included).  Row
+// updates read the plan, column updates read the transpose, and both are
+// rescaled in place with the same arithmetic, so they stay each other's
+// transpose bit for bit.  The transpose is checked first: per pair, the entry
+// counts and a checksum (the sum mod 2^64 of a 64-bit mix of each entry's row,
+// column and value bits, independent of the order) must agree.  One wave
+// reduces one row or one column in a fixed order: no atomics on values,
+// deterministic results.
 #include "common.h"
 
 namespace sk {
@@ -22,43 +27,71 @@ namespace {
 
 constexpr int kSegsPerGroup = 4;   // one wave per row or column
 
-__device__ __forceinline__ double wave_sum_d(double v)
+// SplitMix64 finaliser (Steele, Lea and Flood, "Fast splittable pseudorandom
+// number generators", 2014): a bijective 64-bit mix
+__device__ __forceinline__ uint64_t mix64(uint64_t z)
 {
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1)
-        v += __shfl_xor(v, off, kWave);
-    return v;
+    z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+    z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+    return z ^ (z >> 31);
 }
 
-// perm[q] = plan entry holding (t_cols[q], t_rows[q]), or -1 (counted in *bad)
-__global__ void perm_kernel(const int32_t *__restrict__ cols, const int32_t *__restrict__ t_rows,
-                            const int32_t *__restrict__ t_cols, const int64_t *__restrict__ t_offs,
-                            int n, int m, const int64_t *__restrict__ rb,
-                            const int64_t *__restrict__ re, int64_t *__restrict__ perm,
-                            int *__restrict__ bad)
+// sums[b] += sum over the pair's entries of mix(row, col, value bits), where
+// (ri, ci) are the entry's row and column in the plan's orientation
+__global__ __launch_bounds__(256) void checksum_kernel(const int32_t *__restrict__ ri,
+                                                       const int32_t *__restrict__ ci,
+                                                       const float *__restrict__ v,
+                                                       const int64_t *__restrict__ offs,
+                                                       uint64_t *__restrict__ sums)
 {
+    __shared__ uint64_t part[256 / kWave];
     const int b = blockIdx.y;
-    const int64_t lo = t_offs[b], hi = t_offs[b + 1];
-    for (int64_t q = lo + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < hi;
-         q += (int64_t)gridDim.x * blockDim.x) {
-        const int j = t_rows[q], i = t_cols[q];
-        int64_t found = -1;
-        if (i >= 0 && i < n && j >= 0 && j < m) {
-            int64_t l = rb[(size_t)b * n + i], h = re[(size_t)b * n + i];
-            while (l < h) {   // first entry of row i with column >= j
-                const int64_t mid = l + (h - l) / 2;
-                if (cols[mid] < j)
-                    l = mid + 1;
-                else
-                    h = mid;
-            }
-            if (l < re[(size_t)b * n + i] && cols[l] == j)
-                found = l;
-        }
-        perm[q] = found;
-        if (found < 0)
-            atomicAdd(bad, 1);
+    const int64_t lo = offs[b], hi = offs[b + 1];
+    uint64_t acc = 0;
+    for (int64_t k = lo + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < hi;
+         k += (int64_t)gridDim.x * blockDim.x) {
+        const uint64_t rc = ((uint64_t)(uint32_t)ri[k] << 32) | (uint32_t)ci[k];
+        acc += mix64(rc ^ mix64((uint64_t)__float_as_uint(v[k]) + 0x9e3779b97f4a7c15ull));
     }
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1)
+        acc += __shfl_xor(acc, off, kWave);
+    if (lane_id() == 0)
+        part[threadIdx.x / kWave] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint64_t t = 0;
+        for (int w = 0; w < 256 / kWave; ++w)
+            t += part[w];
+        atomicAdd((unsigned long long *)&sums[b], (unsigned long long)t);
+    }
+}
+
+// *bad = number of pairs whose entry counts or checksums differ
+__global__ __launch_bounds__(256) void compare_kernel(const int64_t *__restrict__ offs,
+                                                      const int64_t *__restrict__ t_offs,
+                                                      const uint64_t *__restrict__ sums, int B,
+                                                      int *__restrict__ bad)
+{
+    __shared__ int cnt;
+    if (threadIdx.x == 0)
+        cnt = 0;
+    __syncthreads();
+    int mine = 0;
+    for (int b = threadIdx.x; b < B; b += 256)
+        mine += (offs[b + 1] - offs[b] != t_offs[b + 1] - t_offs[b]) || (sums[b] != sums[B + b]);
+    if (mine)
+        atomicAdd(&cnt, mine);
+    __syncthreads();
+    if (threadIdx.x == 0)
+        *bad = cnt;
+}
+
+__global__ void zero_u64(uint64_t *__restrict__ p, int count)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < count)
+        p[i] = 0;
 }
 
 __global__ void log_kernel(const float *__restrict__ vals, int64_t nnz, float *__restrict__ lv)
@@ -68,16 +101,14 @@ __global__ void log_kernel(const float *__restrict__ vals, int64_t nnz, float *_
         lv[k] = logf(vals[k]);
 }
 
-// One scaling update per segment (row of the plan or column of its transpose):
-// out_s = lw_s - LSE over the segment of (lv_k + other_{partner}).
-// ROW: entries k = begin..end of the plan, partner = cols[k];
-// COL: entries q = begin..end of the transpose, k = perm[q], partner = t_cols[q].
-template <bool ROW>
+// One scaling update per segment (a row of the plan or a row of the transpose,
+// i.e. a column of the plan): out_s = lw_s - LSE over the segment's entries k
+// of (lv_k + other_{partner_k}).
 __global__ __launch_bounds__(kSegsPerGroup *kWave) void scale_pass(
     const int64_t *__restrict__ sb, const int64_t *__restrict__ se,
-    const int32_t *__restrict__ partner, const int64_t *__restrict__ perm,
-    const float *__restrict__ lv, const double *__restrict__ other, int count,
-    int other_count, const double *__restrict__ lw, double *__restrict__ out)
+    const int32_t *__restrict__ partner, const float *__restrict__ lv,
+    const double *__restrict__ other, int count, int other_count, const double *__restrict__ lw,
+    double *__restrict__ out)
 {
     const int b = blockIdx.y;
     const int s = blockIdx.x * kSegsPerGroup + wave_id_uniform();
@@ -88,24 +119,31 @@ __global__ __launch_bounds__(kSegsPerGroup *kWave) void scale_pass(
     const int64_t lo = sb[si], hi = se[si];
     const double *ob = other + (size_t)b * other_count;
     auto term = [&](int64_t q) -> double {
-        const int64_t k = ROW ? q : perm[q];
         const int p = partner[q];
-        if (k < 0 || p < 0 || p >= other_count)
+        if (p < 0 || p >= other_count)
             return -INFINITY;
-        return (double)lv[k] + ob[p];
+        return (double)lv[q] + ob[p];
     };
     // one pass: each lane keeps (M, S) meaning S e^M over its entries, raising M
     // when a larger term arrives; lanes merge in a fixed order
     double M = -INFINITY, S = 0.0;
-    for (int64_t q = lo + lane; q < hi; q += kWave) {
-        const double z = term(q);
+    auto add = [&](double z) {
         if (z > M) {
             S = S * (double)expf((float)(M - z)) + 1.0;
             M = z;
         } else if (z > -INFINITY) {
             S += (double)expf((float)(z - M));
         }
+    };
+    // two entries per lane and step (loaded before either is used), in order
+    int64_t q = lo + lane;
+    for (; q + kWave < hi; q += 2 * kWave) {
+        const double z0 = term(q), z1 = term(q + kWave);
+        add(z0);
+        add(z1);
     }
+    if (q < hi)
+        add(term(q));
 #pragma unroll
     for (int off = kWave / 2; off > 0; off >>= 1) {
         const double M2 = __shfl_xor(M, off, kWave), S2 = __shfl_xor(S, off, kWave);
@@ -119,7 +157,10 @@ __global__ __launch_bounds__(kSegsPerGroup *kWave) void scale_pass(
         out[si] = M > -INFINITY ? lw[si] - (M + log(S)) : 0.0;
 }
 
-__global__ void apply_kernel(const int32_t *__restrict__ rows, const int32_t *__restrict__ cols,
+// vals_k <- exp(lv_k + alpha_{ri_k} + beta_{ci_k}) with (ri, ci) the entry's row
+// and column in the plan's orientation (the same sum, in the same order, for
+// the plan and for its transpose)
+__global__ void apply_kernel(const int32_t *__restrict__ ri, const int32_t *__restrict__ ci,
                              const int64_t *__restrict__ offs, int n, int m,
                              const float *__restrict__ lv, const double *__restrict__ al,
                              const double *__restrict__ be, float *__restrict__ vals)
@@ -128,7 +169,7 @@ __global__ void apply_kernel(const int32_t *__restrict__ rows, const int32_t *__
     const int64_t lo = offs[b], hi = offs[b + 1];
     for (int64_t k = lo + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < hi;
          k += (int64_t)gridDim.x * blockDim.x) {
-        const int i = rows[k], j = cols[k];
+        const int i = ri[k], j = ci[k];
         if (i < 0 || i >= n || j < 0 || j >= m)
             continue;
         const double z = (double)lv[k] + al[(size_t)b * n + i] + be[(size_t)b * m + j];
@@ -136,12 +177,10 @@ __global__ void apply_kernel(const int32_t *__restrict__ rows, const int32_t *__
     }
 }
 
-// |sum of the segment's values - weight| per row or column
-template <bool ROW>
+// |sum of the segment's values - weight| per row (of the plan or of the transpose)
 __global__ __launch_bounds__(kSegsPerGroup *kWave) void marginal_pass(
-    const int64_t *__restrict__ sb, const int64_t *__restrict__ se,
-    const int64_t *__restrict__ perm, const float *__restrict__ vals, int count,
-    const float *__restrict__ w, double *__restrict__ part)
+    const int64_t *__restrict__ sb, const int64_t *__restrict__ se, const float *__restrict__ vals,
+    int count, const float *__restrict__ w, double *__restrict__ part)
 {
     const int b = blockIdx.y;
     const int s = blockIdx.x * kSegsPerGroup + wave_id_uniform();
@@ -150,12 +189,9 @@ __global__ __launch_bounds__(kSegsPerGroup *kWave) void marginal_pass(
     const int lane = lane_id();
     const size_t si = (size_t)b * count + s;
     double acc = 0.0;
-    for (int64_t q = sb[si] + lane; q < se[si]; q += kWave) {
-        const int64_t k = ROW ? q : perm[q];
-        if (k >= 0)
-            acc += (double)vals[k];
-    }
-    acc = wave_sum_d(acc);
+    for (int64_t q = sb[si] + lane; q < se[si]; q += kWave)
+        acc += (double)vals[q];
+    acc = wave_sum(acc);
     if (lane == 0)
         part[si] = fabs(acc - (w ? (double)w[si] : 1.0 / (double)count));
 }
@@ -186,56 +222,60 @@ __global__ void zero_f64(double *__restrict__ p, size_t count)
         p[i] = 0.0;
 }
 
-__global__ void zero_i32(int *__restrict__ p)
-{
-    if (threadIdx.x == 0 && blockIdx.x == 0)
-        *p = 0;
-}
-
 }  // namespace
 
-hipError_t launch_coo_perm(const int32_t *cols, const int32_t *t_rows, const int32_t *t_cols,
-                           const int64_t *t_offs, int B, int n, int m, const CooNormWs &w,
-                           hipStream_t st)
+hipError_t launch_coo_check(const int32_t *rows, const int32_t *cols, const float *vals,
+                            const int64_t *offs, const int32_t *t_rows, const int32_t *t_cols,
+                            const float *t_vals, const int64_t *t_offs, int B, const CooNormWs &w,
+                            hipStream_t st)
 {
-    hipLaunchKernelGGL(zero_i32, dim3(1), dim3(64), 0, st, w.bad);
-    hipLaunchKernelGGL(perm_kernel, dim3(256, B), dim3(256), 0, st, cols, t_rows, t_cols, t_offs,
-                       n, m, (const int64_t *)w.rb, (const int64_t *)w.re, w.perm, w.bad);
+    hipLaunchKernelGGL(zero_u64, dim3(ceil_div(2 * B, 256)), dim3(256), 0, st, w.sums, 2 * B);
+    hipLaunchKernelGGL(checksum_kernel, dim3(64, B), dim3(256), 0, st, rows, cols, vals, offs,
+                       w.sums);
+    // the transpose's entry (row j, column i) is the plan's (i, j)
+    hipLaunchKernelGGL(checksum_kernel, dim3(64, B), dim3(256), 0, st, t_cols, t_rows, t_vals,
+                       t_offs, w.sums + B);
+    hipLaunchKernelGGL(compare_kernel, dim3(1), dim3(256), 0, st, offs, t_offs,
+                       (const uint64_t *)w.sums, B, w.bad);
     return hipGetLastError();
 }
 
 hipError_t launch_coo_normalize(const int32_t *rows, const int32_t *cols, float *vals,
-                                const int64_t *offs, const int32_t *t_cols, int B, int n, int m,
+                                const int64_t *offs, const int32_t *t_rows, const int32_t *t_cols,
+                                float *t_vals, const int64_t *t_offs, int B, int n, int m,
                                 int64_t nnz, int iters, float *err, const float *a,
                                 const float *b, const CooNormWs &w, hipStream_t st)
 {
     const unsigned nb = (unsigned)((nnz + 255) / 256);
-    if (nnz > 0)
+    if (nnz > 0) {
         hipLaunchKernelGGL(log_kernel, dim3(nb), dim3(256), 0, st, (const float *)vals, nnz, w.lv);
+        hipLaunchKernelGGL(log_kernel, dim3(nb), dim3(256), 0, st, (const float *)t_vals, nnz,
+                           w.lvt);
+    }
     const size_t cn = (size_t)B * m;
     hipLaunchKernelGGL(zero_f64, dim3((unsigned)((cn + 255) / 256)), dim3(256), 0, st, w.be, cn);
     const dim3 gr(ceil_div(n, kSegsPerGroup), B), gc(ceil_div(m, kSegsPerGroup), B);
     const dim3 blk(kSegsPerGroup * kWave);
     for (int it = 0; it < iters; ++it) {
-        hipLaunchKernelGGL(scale_pass<true>, gr, blk, 0, st, (const int64_t *)w.rb,
-                           (const int64_t *)w.re, cols, (const int64_t *)nullptr,
-                           (const float *)w.lv, (const double *)w.be, n, m,
+        hipLaunchKernelGGL(scale_pass, gr, blk, 0, st, (const int64_t *)w.rb, (const int64_t *)w.re,
+                           cols, (const float *)w.lv, (const double *)w.be, n, m,
                            (const double *)w.la, w.al);
-        hipLaunchKernelGGL(scale_pass<false>, gc, blk, 0, st, (const int64_t *)w.cb,
-                           (const int64_t *)w.ce, t_cols, (const int64_t *)w.perm,
-                           (const float *)w.lv, (const double *)w.al, m, n,
+        hipLaunchKernelGGL(scale_pass, gc, blk, 0, st, (const int64_t *)w.cb, (const int64_t *)w.ce,
+                           t_cols, (const float *)w.lvt, (const double *)w.al, m, n,
                            (const double *)w.lb, w.be);
     }
-    if (iters > 0)
+    if (iters > 0) {
         hipLaunchKernelGGL(apply_kernel, dim3(256, B), dim3(256), 0, st, rows, cols, offs, n, m,
                            (const float *)w.lv, (const double *)w.al, (const double *)w.be, vals);
+        hipLaunchKernelGGL(apply_kernel, dim3(256, B), dim3(256), 0, st, t_cols, t_rows, t_offs, n,
+                           m, (const float *)w.lvt, (const double *)w.al, (const double *)w.be,
+                           t_vals);
+    }
     if (err) {
-        hipLaunchKernelGGL(marginal_pass<true>, gr, blk, 0, st, (const int64_t *)w.rb,
-                           (const int64_t *)w.re, (const int64_t *)nullptr, (const float *)vals, n,
-                           a, w.row_part);
-        hipLaunchKernelGGL(marginal_pass<false>, gc, blk, 0, st, (const int64_t *)w.cb,
-                           (const int64_t *)w.ce, (const int64_t *)w.perm, (const float *)vals, m,
-                           b, w.col_part);
+        hipLaunchKernelGGL(marginal_pass, gr, blk, 0, st, (const int64_t *)w.rb,
+                           (const int64_t *)w.re, (const float *)vals, n, a, w.row_part);
+        hipLaunchKernelGGL(marginal_pass, gc, blk, 0, st, (const int64_t *)w.cb,
+                           (const int64_t *)w.ce, (const float *)t_vals, m, b, w.col_part);
         hipLaunchKernelGGL(pair_err, dim3(B), dim3(256), 0, st, (const double *)w.row_part, n,
                            err, 0);
         hipLaunchKernelGGL(pair_err, dim3(B), dim3(256), 0, st, (const double *)w.col_part, m,

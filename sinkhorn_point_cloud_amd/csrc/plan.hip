@@ -25,7 +25,8 @@
 // the keys with wave-uniform addresses (scalar loads shared by the lanes);
 // the 4 waves of a work-group take every 4th key and merge in LDS.  The emit
 // pass holds one row per wave with lanes across 64 consecutive columns, so
-// each wave writes contiguous slices of the COO arrays.
+// each wave writes contiguous slices of the COO arrays; for d <= 4 the
+// columns are staged in LDS once per work-group of 32 rows.
 #include "plan_eval.h"
 
 namespace sk {
@@ -264,11 +265,14 @@ __global__ __launch_bounds__(256) void row_offsets_scan(const int32_t *__restric
     }
 }
 
-template <typename T, int DP>
+// LG: also accumulate the loss and its gradient in x over the emitted entries
+// (loss_term on the value as stored), one row per wave: row_loss [B][n] and
+// dX [B][n][d] (either may be NULL).
+template <typename T, int DP, bool LG>
 __global__ __launch_bounds__(kRowsPerGroup *kWave) void emit_pass(
     PlanArgs p, const double *__restrict__ thr, const int64_t *__restrict__ row_off,
     const int32_t *__restrict__ row_cnt, int32_t *__restrict__ rows, int32_t *__restrict__ cols,
-    float *__restrict__ vals)
+    float *__restrict__ vals, double *__restrict__ row_loss, float *__restrict__ dX)
 {
     const int b = blockIdx.y;
     const int i = blockIdx.x * kRowsPerGroup + wave_id_uniform();
@@ -283,26 +287,163 @@ __global__ __launch_bounds__(kRowsPerGroup *kWave) void emit_pass(
     int64_t pos = row_off[(size_t)b * p.n + i];
     const int64_t end = pos + row_cnt[(size_t)b * p.n + i];
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int j0 = 0; j0 < p.m; j0 += kWave) {
+    double loss = 0.0;
+    float gr[DP];
+#pragma unroll
+    for (int c = 0; c < DP; ++c)
+        gr[c] = 0.f;
+    for (int j0 = 0; j0 < p.m && pos < end; j0 += kWave) {
         const int j = j0 + lane;
         bool keep = false;
         double lp = 0.0;
+        float y[DP];
         if (j < p.m) {
+            const T *yp = Yb + (size_t)j * p.d;
+#pragma unroll
+            for (int k = 0; k < DP; ++k)
+                y[k] = has_dim<DP>(k, p.d) ? Elem<T>::get(yp, k) : 0.f;
             double C;
-            const double lbj = p.lb[(size_t)b * p.m + j];
-            lp = log_plan<T, DP>(r, p, Yb, gb, lbj, j, &C);
+            lp = log_plan_at<DP>(r, y, gb[j], p.lb[(size_t)b * p.m + j], p.inv_eps, p.d, &C);
             keep = lp >= t;
         }
         const uint64_t mask = __ballot(keep);
         if (keep) {
             const int64_t k = pos + __popcll(mask & below);
             if (k < end) {   // always true: count and emit make identical decisions
+                const float P = ex2((float)(lp * 1.4426950408889634));
                 rows[k] = i;
                 cols[k] = j;
-                vals[k] = ex2((float)(lp * 1.4426950408889634));
+                vals[k] = P;
+                if (LG)
+                    loss_term<DP>(r.x, y, p.d, P, loss, gr);
             }
         }
         pos += __popcll(mask);
+    }
+    if (LG) {
+        const size_t ri = (size_t)b * p.n + i;
+        loss = wave_sum(loss);
+        if (row_loss && lane == 0)
+            row_loss[ri] = loss;
+        if (dX) {
+#pragma unroll
+            for (int c = 0; c < DP; ++c) {
+                if (has_dim<DP>(c, p.d)) {
+                    const float v = wave_sum(gr[c]);
+                    if (lane == 0)
+                        dX[ri * p.d + c] = v;
+                }
+            }
+        }
+    }
+}
+
+// Emit pass for small d with the keys staged in LDS: a work-group of
+// kEmitWaves waves takes kEmitRows consecutive rows of one pair (a wave per row
+// at a time, lanes across 64 consecutive columns, as above) and shares one
+// staged copy of each chunk of kEmitChunk columns (point components as fp32,
+// g_j, log b_j), so the column data is read from memory once per work-group
+// instead of once per row.  The evaluation is log_plan_at on the same values
+// as the count pass, so the decisions agree bit for bit.
+constexpr int kEmitWaves = 8, kEmitRows = 32, kEmitChunk = 1024;
+
+template <typename T, int DP, bool LG>
+__global__ __launch_bounds__(kEmitWaves *kWave) void emit_staged(
+    PlanArgs p, const double *__restrict__ thr, const int64_t *__restrict__ row_off,
+    const int32_t *__restrict__ row_cnt, int32_t *__restrict__ rows, int32_t *__restrict__ cols,
+    float *__restrict__ vals, double *__restrict__ row_loss, float *__restrict__ dX)
+{
+    static_assert(DP <= 4, "staged emit holds at most 4 components per column");
+    constexpr int kRowsPerWave = kEmitRows / kEmitWaves;
+    __shared__ float ys[DP][kEmitChunk];
+    __shared__ float gs[kEmitChunk];
+    __shared__ double lbs[kEmitChunk];
+    const int b = blockIdx.y;
+    const int wave = wave_id_uniform(), lane = lane_id();
+    const int i0 = blockIdx.x * kEmitRows + wave * kRowsPerWave;
+    const T *Yb = (const T *)p.Y + (size_t)b * p.m * p.d;
+    const float *gb = p.g + (size_t)b * p.m;
+    const double *lbb = p.lb + (size_t)b * p.m;
+    const double t = thr[b];
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    RowCtx<DP> r[kRowsPerWave];
+    int64_t pos[kRowsPerWave], end[kRowsPerWave];
+    double loss[kRowsPerWave];
+    float gr[kRowsPerWave][DP];
+#pragma unroll
+    for (int q = 0; q < kRowsPerWave; ++q) {
+        const int i = min(i0 + q, p.n - 1);   // rows past n are loaded but never emitted
+        load_row<T, DP>(r[q], p, b, i);
+        pos[q] = row_off[(size_t)b * p.n + i];
+        end[q] = i0 + q < p.n ? pos[q] + row_cnt[(size_t)b * p.n + i] : pos[q];
+        loss[q] = 0.0;
+#pragma unroll
+        for (int c = 0; c < DP; ++c)
+            gr[q][c] = 0.f;
+    }
+    for (int c0 = 0; c0 < p.m; c0 += kEmitChunk) {
+        const int kc = min(kEmitChunk, p.m - c0);
+        __syncthreads();   // the previous chunk is no longer read
+        for (int j = threadIdx.x; j < kc; j += kEmitWaves * kWave) {
+            const T *yp = Yb + (size_t)(c0 + j) * p.d;
+#pragma unroll
+            for (int k = 0; k < DP; ++k)
+                ys[k][j] = has_dim<DP>(k, p.d) ? Elem<T>::get(yp, k) : 0.f;
+            gs[j] = gb[c0 + j];
+            lbs[j] = lbb[c0 + j];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < kRowsPerWave; ++q) {
+            for (int j0 = 0; j0 < kc && pos[q] < end[q]; j0 += kWave) {   // wave-uniform
+                const int j = j0 + lane;
+                bool keep = false;
+                double lp = 0.0;
+                float y[DP];
+                if (j < kc) {
+#pragma unroll
+                    for (int k = 0; k < DP; ++k)
+                        y[k] = ys[k][j];
+                    double C;
+                    lp = log_plan_at<DP>(r[q], y, gs[j], lbs[j], p.inv_eps, p.d, &C);
+                    keep = lp >= t;
+                }
+                const uint64_t mask = __ballot(keep);
+                if (keep) {
+                    const int64_t k = pos[q] + __popcll(mask & below);
+                    if (k < end[q]) {   // always true: count and emit make identical decisions
+                        const float P = ex2((float)(lp * 1.4426950408889634));
+                        rows[k] = i0 + q;
+                        cols[k] = c0 + j;
+                        vals[k] = P;
+                        if (LG)
+                            loss_term<DP>(r[q].x, y, p.d, P, loss[q], gr[q]);
+                    }
+                }
+                pos[q] += __popcll(mask);
+            }
+        }
+    }
+    if (LG) {
+#pragma unroll
+        for (int q = 0; q < kRowsPerWave; ++q) {
+            if (i0 + q >= p.n)
+                break;
+            const size_t ri = (size_t)b * p.n + i0 + q;
+            const double l = wave_sum(loss[q]);
+            if (row_loss && lane == 0)
+                row_loss[ri] = l;
+            if (dX) {
+#pragma unroll
+                for (int c = 0; c < DP; ++c) {
+                    if (has_dim<DP>(c, p.d)) {
+                        const float v = wave_sum(gr[q][c]);
+                        if (lane == 0)
+                            dX[ri * p.d + c] = v;
+                    }
+                }
+            }
+        }
     }
 }
 
@@ -391,18 +532,41 @@ hipError_t launch_plan_scan(const int32_t *row_count, int B, int n, int64_t *row
 
 hipError_t launch_plan_emit(const PlanArgs &p, const double *pair_thr, const int64_t *row_off,
                             const int32_t *row_count, int32_t *rows, int32_t *cols,
-                            float *vals, hipStream_t st)
+                            float *vals, double *row_loss, float *loss, float *dX, hipStream_t st)
 {
-    dim3 grid(ceil_div(p.n, kRowsPerGroup), p.B);
-    dim3 block(kRowsPerGroup * kWave);
-    with_dp(p.d, [&]<int DP>() {
-        if (p.dtype == 1)
-            hipLaunchKernelGGL((emit_pass<uint16_t, DP>), grid, block, 0, st, p, pair_thr,
-                               row_off, row_count, rows, cols, vals);
+    const bool lg = loss || dX;
+    double *rl = loss ? row_loss : nullptr;
+    if (p.d <= 4) {
+        const dim3 grid(ceil_div(p.n, kEmitRows), p.B), block(kEmitWaves * kWave);
+        auto go = [&]<int DP, bool LG>() {
+            if (p.dtype == 1)
+                hipLaunchKernelGGL((emit_staged<uint16_t, DP, LG>), grid, block, 0, st, p,
+                                   pair_thr, row_off, row_count, rows, cols, vals, rl, dX);
+            else
+                hipLaunchKernelGGL((emit_staged<float, DP, LG>), grid, block, 0, st, p, pair_thr,
+                                   row_off, row_count, rows, cols, vals, rl, dX);
+        };
+        if (p.d == 3)
+            lg ? go.template operator()<3, true>() : go.template operator()<3, false>();
         else
-            hipLaunchKernelGGL((emit_pass<float, DP>), grid, block, 0, st, p, pair_thr, row_off,
-                               row_count, rows, cols, vals);
-    });
+            lg ? go.template operator()<4, true>() : go.template operator()<4, false>();
+    } else {
+        const dim3 grid(ceil_div(p.n, kRowsPerGroup), p.B), block(kRowsPerGroup * kWave);
+        auto go = [&]<int DP, bool LG>() {
+            if (p.dtype == 1)
+                hipLaunchKernelGGL((emit_pass<uint16_t, DP, LG>), grid, block, 0, st, p, pair_thr,
+                                   row_off, row_count, rows, cols, vals, rl, dX);
+            else
+                hipLaunchKernelGGL((emit_pass<float, DP, LG>), grid, block, 0, st, p, pair_thr,
+                                   row_off, row_count, rows, cols, vals, rl, dX);
+        };
+        with_dp(p.d, [&]<int DP>() {
+            lg ? go.template operator()<DP, true>() : go.template operator()<DP, false>();
+        });
+    }
+    if (loss)
+        hipLaunchKernelGGL(pair_reduce<0>, dim3(p.B), dim3(256), 0, st, (const double *)row_loss,
+                           p.n, loss, (double *)nullptr, 0.0);
     return hipGetLastError();
 }
 

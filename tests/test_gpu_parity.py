@@ -273,6 +273,22 @@ def test_loss_grad_rows_without_entries_and_empty_pairs():
     assert np.all(host(dX)[0, 1:7] == 0.0)
 
 
+def fused_plan_loss(X, Y, a, b, f, g, eps, thr):
+    """plan_coo with the loss and dL/dX accumulated during the emission, checked
+    against loss_grad on the emitted plan (same per-entry arithmetic, another
+    summation order: agreement to a few fp32 roundings)."""
+    B, n, d = X.shape
+    loss = torch.full((B,), 7.0, device=X.device)
+    dX = torch.full((B, n, d), 7.0, device=X.device)
+    plan = sk.plan_coo(X, Y, a, b, f, g, eps, thr, loss_out=(loss, dX))
+    l2, dX2 = sk.loss_grad(X, Y, *plan)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(host(loss), host(l2), rtol=1e-5, atol=1e-30)
+    for p in range(B):
+        assert rel_inf(host(dX)[p], host(dX2)[p], 1e-30) <= 1e-5
+    return plan, loss, dX
+
+
 def test_plan_chain_on_gpu_potentials():
     # GPU potentials -> GPU plan -> GPU loss against the oracle's own chain
     c = workloads.random_case(44, 2, 400, 350, 3, weights="dirichlet")
@@ -281,13 +297,61 @@ def test_plan_chain_on_gpu_potentials():
     X, Y = points(c)
     rows, cols, vals, offs = sk.plan_coo(X, Y, dev(c["a"]), dev(c["b"]), f, g, eps[0], 1e-8)
     loss, dX = sk.loss_grad(X, Y, rows, cols, vals, offs)
+    _, loss_f, dX_f = fused_plan_loss(X, Y, dev(c["a"]), dev(c["b"]), f, g, eps[0], 1e-8)
     fo, go = oracle.potentials(c["X"], c["Y"], c["a"], c["b"], eps=np.float32(eps), iters=[20])
     ro, co, vo, oo = oracle.plan_coo(c["X"], c["Y"], c["a"], c["b"], fo, go,
                                      float(np.float32(eps[0])), 1e-8)
     lo, dXo = oracle.loss_grad(c["X"], c["Y"], ro, co, vo, oo)
+    for l_gpu, dX_gpu in ((loss, dX), (loss_f, dX_f)):
+        np.testing.assert_allclose(host(l_gpu), lo, rtol=1e-4)
+        for p in range(2):
+            assert rel_inf(host(dX_gpu)[p], dXo[p]) <= 1e-4
+
+
+@pytest.mark.parametrize("B,n,m,d,dtype,thr", [(2, 150, 1300, 3, "f32", 1e-8),
+                                               (1, 97, 80, 4, "bf16", 1e-3),
+                                               (2, 70, 90, 8, "f32", 1e-6),
+                                               (1, 60, 75, 64, "bf16", 1e-4),
+                                               (2, 50, 40, 3, "f32", 1.0)])
+def test_fused_loss_matches_oracle(B, n, m, d, dtype, thr):
+    # m = 1300 spans two LDS chunks of the staged emission; d = 8 and 64 take the
+    # unstaged one; thr = 1 keeps only each pair's largest entry, so nearly every
+    # row has no entry and must get a zero gradient
+    c = workloads.random_case(47 + d, B, n, m, d, weights="dirichlet", dtype=dtype,
+                              spread=1.0 if d <= 8 else 0.25)
+    eps = 0.05
+    fo, go = oracle.potentials(c["X"], c["Y"], c["a"], c["b"], eps=np.float32([eps]),
+                               iters=[10])
+    f32, g32 = fo.astype(np.float32), go.astype(np.float32)
+    X, Y = points(c)
+    (rows, cols, vals, offs), loss, dX = fused_plan_loss(X, Y, dev(c["a"]), dev(c["b"]),
+                                                         dev(f32), dev(g32), eps, thr)
+    # the oracle's chain from the same fp32 potentials (entries within the
+    # threshold band that one side keeps and the other drops weigh ~1e-8 of the max)
+    ro, co, vo, oo = oracle.plan_coo(c["X"], c["Y"], c["a"], c["b"], f32, g32,
+                                     float(np.float32(eps)), thr)
+    lo, dXo = oracle.loss_grad(c["X"], c["Y"], ro, co, vo.astype(np.float32), oo)
     np.testing.assert_allclose(host(loss), lo, rtol=1e-4)
-    for p in range(2):
-        assert rel_inf(host(dX)[p], dXo[p]) <= 1e-4
+    for p in range(B):
+        assert rel_inf(host(dX)[p], dXo[p], 1e-30) <= 1e-4
+    if thr == 1.0:
+        for p in range(B):
+            empty = np.setdiff1d(np.arange(n), ro[oo[p]:oo[p + 1]])
+            assert len(empty) >= n - 2 and np.all(host(dX)[p][empty] == 0.0)
+
+
+def test_fused_loss_untouched_when_the_plan_does_not_fit():
+    c = workloads.random_case(48, 1, 64, 60, 3)
+    fo, go = oracle.potentials(c["X"], c["Y"], c["a"], c["b"], eps=np.float32([0.05]),
+                               iters=[5])
+    X, Y = points(c)
+    loss = torch.full((1,), 7.0, device=X.device)
+    dX = torch.full((1, 64, 3), 7.0, device=X.device)
+    with pytest.raises(sk.SinkhornError) as ei:
+        sk.plan_coo(X, Y, None, None, dev(fo.astype(np.float32)), dev(go.astype(np.float32)),
+                    0.05, 1e-8, capacity=3, loss_out=(loss, dX))
+    assert ei.value.status == sk.SK_ERR_CAPACITY
+    assert bool((loss == 7.0).all()) and bool((dX == 7.0).all())
 
 
 # ------------------------------------------------------------ workloads
@@ -334,9 +398,11 @@ def test_workload_sparse_plan_and_loss(name, pairs):
     rows, cols, vals, offs = sk.plan_coo(X, Y, dev(w["a"]), dev(w["b"]), f, g, eps,
                                          w["threshold"])
     loss, dX = sk.loss_grad(X, Y, rows, cols, vals, offs)
-    np.testing.assert_allclose(host(loss), gold["loss"], rtol=1e-4)
-    for k, p in enumerate(gold["dX_pairs"]):
-        assert rel_inf(host(dX)[p], gold["dX"][k]) <= 1e-4
+    _, loss_f, dX_f = fused_plan_loss(X, Y, dev(w["a"]), dev(w["b"]), f, g, eps, w["threshold"])
+    for l_gpu, dX_gpu in ((loss, dX), (loss_f, dX_f)):
+        np.testing.assert_allclose(host(l_gpu), gold["loss"], rtol=1e-4)
+        for k, p in enumerate(gold["dX_pairs"]):
+            assert rel_inf(host(dX_gpu)[p], gold["dX"][k]) <= 1e-4
 
 
 def test_workload_gmm_64k():
@@ -579,6 +645,20 @@ def test_coo_normalize_matches_oracle(B, n, m, eps, thr, iters):
     torch.cuda.synchronize()
     np.testing.assert_allclose(host(P[2]), v_o, rtol=1e-4, atol=0)
     np.testing.assert_allclose(host(err), err_o, rtol=1e-3, atol=1e-6)
+    _assert_transposes(P, T, B)
+
+
+def _assert_transposes(P, T, B):
+    """T holds P's entries and values, bit for bit, in column-major order."""
+    r1, c1, v1, o1 = (host(t) for t in P)
+    r2, c2, v2, o2 = (host(t) for t in T)
+    for p in range(B):
+        s1 = slice(int(o1[p]), int(o1[p + 1]))
+        s2 = slice(int(o2[p]), int(o2[p + 1]))
+        order = np.lexsort((r1[s1], c1[s1]))
+        np.testing.assert_array_equal(r2[s2], c1[s1][order])
+        np.testing.assert_array_equal(c2[s2], r1[s1][order])
+        np.testing.assert_array_equal(v2[s2], v1[s1][order])
 
 
 def test_coo_normalize_gpu_chain_reaches_the_marginals():
@@ -588,6 +668,7 @@ def test_coo_normalize_gpu_chain_reaches_the_marginals():
     f, g, _ = sk.potentials(X, Y, a, b, eps=[eps], iters=[10])
     P = sk.plan_coo(X, Y, a, b, f, g, eps, 1e-8)
     T = sk.plan_coo(Y, X, b, a, g, f, eps, 1e-8)
+    _assert_transposes(P, T, 2)   # the two extractions agree before normalisation
     before = P[2].clone()
     err = sk.coo_normalize(P, T, a, b, 400, 350, 300)
     torch.cuda.synchronize()
@@ -595,6 +676,7 @@ def test_coo_normalize_gpu_chain_reaches_the_marginals():
     assert np.all(e[:, 1] < 1e-5) and np.all(e[:, 0] < 1e-4), e
     # the column sums after the last half-step are b; the support is unchanged
     assert P[2].shape == before.shape and bool((P[2] >= 0).all())
+    _assert_transposes(P, T, 2)   # and after it
 
 
 def test_coo_normalize_rejects_a_mismatched_transpose():
@@ -603,14 +685,17 @@ def test_coo_normalize_rejects_a_mismatched_transpose():
     fo, go = oracle.potentials(c["X"], c["Y"], c["a"], c["b"], eps=[eps], iters=[5])
     plan = oracle.plan_coo(c["X"], c["Y"], c["a"], c["b"], fo, go, eps, rel_thr=1e-3)
     tr = list(oracle.plan_coo(c["Y"], c["X"], c["b"], c["a"], go, fo, eps, rel_thr=1e-3))
-    tr[1] = tr[1].copy()
-    tr[1][0] = (tr[1][0] + 1) % 64                  # one transposed entry points elsewhere
-    P, T = _coo_dev(plan), _coo_dev(tr)
-    before = P[2].clone()
-    with pytest.raises(sk.SinkhornError) as ex:
-        sk.coo_normalize(P, T, None, None, 64, 70, 5)
-    assert ex.value.status == sk.SK_ERR_INVALID_ARG
-    assert torch.equal(P[2], before)
+    bad_col = [tr[0], tr[1].copy(), tr[2], tr[3]]
+    bad_col[1][0] = (bad_col[1][0] + 1) % 64        # one transposed entry points elsewhere
+    bad_val = [tr[0], tr[1], tr[2].astype(np.float32), tr[3]]
+    bad_val[2][len(bad_val[2]) // 2] *= 1.5         # one transposed value differs
+    for t in (bad_col, bad_val):
+        P, T = _coo_dev(plan), _coo_dev(t)
+        before, t_before = P[2].clone(), T[2].clone()
+        with pytest.raises(sk.SinkhornError) as ex:
+            sk.coo_normalize(P, T, None, None, 64, 70, 5)
+        assert ex.value.status == sk.SK_ERR_INVALID_ARG
+        assert torch.equal(P[2], before) and torch.equal(T[2], t_before)
 
 
 @pytest.mark.parametrize("name,pairs", [("sphere-2k", [0, 31]), ("blobs-1k", [0, 255])])
@@ -627,10 +712,12 @@ def test_workload_coo_normalize_sampled_pairs(name, pairs):
     v_o, err_o = oracle.coo_normalize(plan[0], plan[1], vals32.astype(np.float64), plan[3],
                                       w["a"], w["b"], n, m, 10)
     P = _coo_dev((plan[0], plan[1], vals32, plan[3]))
-    err = sk.coo_normalize(P, _coo_dev(tr), dev(w["a"]), dev(w["b"]), n, m, 10)
+    T = _coo_dev(tr)
+    err = sk.coo_normalize(P, T, dev(w["a"]), dev(w["b"]), n, m, 10)
     torch.cuda.synchronize()
     np.testing.assert_allclose(host(P[2]), v_o, rtol=1e-4, atol=0)
     np.testing.assert_allclose(host(err), err_o, rtol=1e-3, atol=1e-6)
+    _assert_transposes(P, T, len(pairs))
 
 
 # ------------------------------------------------------- Hessian-vector product
