@@ -100,6 +100,44 @@ def test_far_from_origin_and_huge_score_range(scores):
     check_potentials(c, [0.003], [5], valu_scores=scores == "valu")
 
 
+@pytest.mark.parametrize("n,m", [(1 << 24, 64), (64, 1 << 24)])
+def test_largest_cloud_per_pair(n, m):
+    # 2^24 points on one side (the largest the boundary accepts) against 64 on the
+    # other: the long side's half-update splits its key range across work-groups
+    c = workloads.random_case(501, 1, n, m, 3, weights="dirichlet")
+    check_potentials(c, [0.1], [1])
+
+
+def test_coincident_clouds_closed_form():
+    # every x_i = p and every y_j = q: C_ij = |p - q|^2 = c for all (i, j), so from
+    # g = 0 the first f-update gives f = c, the g-update gives g = 0, and the plan
+    # is a (x) b: cost c, every entry kept, loss c, dX_i = 2 a_i (p - q)
+    n, m = 300, 200
+    p = np.float32([0.3, -0.2, 0.5])
+    q = np.float32([-0.1, 0.4, 0.2])
+    X = np.broadcast_to(p, (1, n, 3)).copy()
+    Y = np.broadcast_to(q, (1, m, 3)).copy()
+    c = float(((p.astype(np.float64) - q.astype(np.float64)) ** 2).sum())
+    a = np.full((1, n), 1.0 / n, dtype=np.float32)
+    b = np.full((1, m), 1.0 / m, dtype=np.float32)
+    eps = 0.05
+    for valu in (False, True):
+        f, g, cost = sk.potentials(dev(X), dev(Y), dev(a), dev(b), eps=[eps], iters=[5],
+                                   valu_scores=valu)
+        assert np.abs(host(f) - c).max() <= 1e-4 * max(c, eps)
+        assert np.abs(host(g)).max() <= 1e-4 * max(c, eps)
+        assert abs(host(cost)[0] - c) <= 1e-4 * c
+    loss = torch.empty(1, device=f.device)
+    dX = torch.empty(1, n, 3, device=f.device)
+    rows, cols, vals, offs = sk.plan_coo(dev(X), dev(Y), dev(a), dev(b), f, g, eps, 1e-8,
+                                         loss_out=(loss, dX))
+    assert int(offs[-1]) == n * m
+    np.testing.assert_allclose(host(vals), 1.0 / (n * m), rtol=1e-4)
+    assert abs(host(loss)[0] - c) <= 1e-4 * c
+    ref = 2.0 * (p.astype(np.float64) - q.astype(np.float64)) / n
+    np.testing.assert_allclose(host(dX)[0], np.broadcast_to(ref, (n, 3)), rtol=1e-4)
+
+
 def test_schedule_with_empty_stages_and_zero_iterations():
     c = workloads.random_case(5, 1, 90, 70, 3, weights="dirichlet")
     check_potentials(c, [0.5, 0.2, 0.05], [0, 6, 8])
