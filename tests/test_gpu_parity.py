@@ -795,3 +795,36 @@ def test_hvp_is_linear_and_symmetric_on_gpu():
     hu, hv, hw, u, v = (host(t)[0] for t in (HU, HV, HW, U, V))
     assert rel_inf(hw, 2.0 * hu - hv) <= 1e-5
     assert abs((u * hv).sum() - (v * hu).sum()) <= 1e-5 * np.abs(u * hv).sum()
+
+
+# ------------------------------------------------- property-based random shapes
+from hypothesis import HealthCheck, given, settings, strategies as st  # noqa: E402
+
+
+@settings(max_examples=40, deadline=None, derandomize=True, database=None,
+          suppress_health_check=[HealthCheck.too_slow, HealthCheck.function_scoped_fixture])
+@given(B=st.integers(1, 4), n=st.integers(1, 300), m=st.integers(1, 300),
+       kind=st.sampled_from([(3, "f32"), (3, "bf16"), (64, "f32"), (64, "bf16")]),
+       weights=st.sampled_from(["uniform", "dirichlet"]),
+       eps=st.sampled_from([0.02, 0.05, 0.2]), iters=st.integers(1, 12),
+       seed=st.integers(0, 1 << 16))
+def test_random_shapes_match_oracle(B, n, m, kind, weights, eps, iters, seed):
+    d, dtype = kind
+    print(f"case B={B} n={n} m={m} d={d} {dtype} {weights} eps={eps} iters={iters} "
+          f"seed={seed}", flush=True)
+    c = workloads.random_case(1000 + seed, B, n, m, d, weights=weights, dtype=dtype,
+                              spread=1.0 if d == 3 else 0.25)
+    _, _, fo, go = check_potentials(c, [eps], [iters])
+    if d == 3:
+        # sparse plan and fused loss from the oracle's potentials (rounded to fp32)
+        check_coo_given_potentials(c, eps, fo, go)
+        f32, g32 = fo.astype(np.float32), go.astype(np.float32)
+        X, Y = points(c)
+        _, loss, dX = fused_plan_loss(X, Y, dev(c["a"]), dev(c["b"]), dev(f32), dev(g32), eps,
+                                      1e-8)
+        ro, co, vo, oo = oracle.plan_coo(c["X"], c["Y"], c["a"], c["b"], f32, g32,
+                                         float(np.float32(eps)), 1e-8)
+        lo, dXo = oracle.loss_grad(c["X"], c["Y"], ro, co, vo.astype(np.float32), oo)
+        np.testing.assert_allclose(host(loss), lo, rtol=1e-4)
+        for p in range(B):
+            assert rel_inf(host(dX)[p], dXo[p], 1e-30) <= 1e-4
