@@ -30,7 +30,8 @@
  *     pinned memory and keeps no state between calls, apart from a
  *     thread-local error message.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
- *     and returns without waiting, except sinkhorn_plan_coo (see there).
+ *     and returns without waiting, except sinkhorn_plan_coo and
+ *     sinkhorn_coo_normalize, which read counts back (see there).
  *     Calls are reentrant; two calls that share a workspace must not overlap.
  *   - Arguments are checked before anything is launched.  On an error no
  *     output buffer is written and the return value says why; the message
