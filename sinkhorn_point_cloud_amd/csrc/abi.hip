@@ -27,6 +27,7 @@ int hip_fail(hipError_t e, const char *where)
 }
 
 constexpr int kMaxPoints = 1 << 24;
+constexpr int kMaxPairs = 65535;     // pairs index a grid dimension (y or z), at most 65535
 constexpr int kMaxNormDim = 4096;   // dimensions accepted by the normalisation
 constexpr int kPad = 64;
 
@@ -45,8 +46,8 @@ struct Carve {
 
 bool shape_ok(int B, int n, int m, int d)
 {
-    return B >= 1 && n >= 1 && m >= 1 && d >= 1 && n <= kMaxPoints && m <= kMaxPoints &&
-           (long long)B * n <= (1ll << 31) && (long long)B * m <= (1ll << 31);
+    return B >= 1 && B <= kMaxPairs && n >= 1 && m >= 1 && d >= 1 && n <= kMaxPoints &&
+           m <= kMaxPoints && (long long)B * n <= (1ll << 31) && (long long)B * m <= (1ll << 31);
 }
 
 bool path3(int dtype, int d) { return dtype == SK_F32 && d == 3; }
@@ -558,7 +559,7 @@ int sinkhorn_hvp(const void *X, const void *Y, int dtype, const float *a, const 
 
 size_t sinkhorn_coo_workspace_bytes(int B, int n, int m, int64_t nnz)
 {
-    if (B < 1 || n < 1 || m < 1 || nnz < 0 || n > kMaxPoints || m > kMaxPoints ||
+    if (B < 1 || B > kMaxPairs || n < 1 || m < 1 || nnz < 0 || n > kMaxPoints || m > kMaxPoints ||
         (long long)B * n > (1ll << 31) || (long long)B * m > (1ll << 31))
         return 0;
     Carve c{nullptr};
@@ -573,7 +574,7 @@ int sinkhorn_coo_normalize(int B, int n, int m, const int32_t *rows, const int32
                            size_t ws_bytes, void *stream)
 {
     g_err[0] = '\0';
-    if (B < 1 || n < 1 || m < 1 || n > kMaxPoints || m > kMaxPoints ||
+    if (B < 1 || B > kMaxPairs || n < 1 || m < 1 || n > kMaxPoints || m > kMaxPoints ||
         (long long)B * n > (1ll << 31) || (long long)B * m > (1ll << 31))
         return fail(SK_ERR_INVALID_ARG, "bad sizes B=%d n=%d m=%d", B, n, m);
     if (!rows || !cols || !vals || !pair_offsets || !t_rows || !t_cols || !t_vals ||

@@ -65,6 +65,7 @@ def test_workspace_bytes(lib):
     assert ws(5, 1, 10, 10, 3, 0) == 0
     assert ws(3, 1, 65536, 65536, 3, 0) < 4 << 20      # two fp64 log-weight vectors
     assert ws(0, 1, 1 << 25, 10, 3, 0) == 0
+    assert ws(0, 65535, 4, 4, 3, 0) > 0 and ws(0, 65536, 4, 4, 3, 0) == 0
 
 
 DUMMY = ctypes.c_void_p(16)   # never dereferenced: validation fails first
@@ -86,6 +87,7 @@ def _pot(lib, X=DUMMY, Y=DUMMY, dtype=0, B=1, n=8, m=9, d=3, eps=(0.1,), iters=(
 @pytest.mark.parametrize("kw,code", [
     (dict(X=None), sk.SK_ERR_INVALID_ARG),
     (dict(B=0), sk.SK_ERR_INVALID_ARG),
+    (dict(B=65536, n=4, m=4), sk.SK_ERR_INVALID_ARG),   # pairs index a grid dimension
     (dict(n=0), sk.SK_ERR_INVALID_ARG),
     (dict(m=-1), sk.SK_ERR_INVALID_ARG),
     (dict(dtype=7), sk.SK_ERR_INVALID_ARG),

@@ -108,6 +108,28 @@ def test_largest_cloud_per_pair(n, m):
     check_potentials(c, [0.1], [1])
 
 
+def test_most_pairs_per_call():
+    # 65535 pairs (the largest batch the boundary accepts) of small clouds: every
+    # per-pair grid dimension at its limit, potentials, plan and fused loss
+    B, n, m = 65535, 5, 3
+    c = workloads.random_case(502, B, n, m, 3, weights="dirichlet")
+    eps = 0.05
+    _, _, fo, go = check_potentials(c, [eps], [3])
+    # plan and loss on both sides from the oracle's potentials rounded to fp32
+    f32, g32 = fo.astype(np.float32), go.astype(np.float32)
+    X, Y = points(c)
+    loss = torch.empty(B, device=X.device)
+    dX = torch.empty(B, n, 3, device=X.device)
+    rows, cols, vals, offs = sk.plan_coo(X, Y, dev(c["a"]), dev(c["b"]), dev(f32), dev(g32), eps,
+                                         1e-8, loss_out=(loss, dX))
+    ro, co, vo, oo = oracle.plan_coo(c["X"], c["Y"], c["a"], c["b"], f32, g32,
+                                     float(np.float32(eps)), 1e-8)
+    lo, dXo = oracle.loss_grad(c["X"], c["Y"], ro, co, vo.astype(np.float32), oo)
+    assert abs(int(offs[-1]) - int(oo[-1])) <= 1e-4 * int(oo[-1])
+    np.testing.assert_allclose(host(loss), lo, rtol=1e-4)
+    assert rel_inf(host(dX), dXo) <= 1e-4
+
+
 def test_coincident_clouds_closed_form():
     # every x_i = p and every y_j = q: C_ij = |p - q|^2 = c for all (i, j), so from
     # g = 0 the first f-update gives f = c, the g-update gives g = 0, and the plan
