@@ -461,8 +461,17 @@ __global__ __launch_bounds__(W *kWave) void lse3m_kernel(
         const int first = t_begin + w;
         const int cnt = first < t_end ? (t_end - first + W - 1) / W : 0;
         const int last = first + (cnt > 0 ? cnt - 1 : 0) * W;
+        // key operands through a buffer resource: the tile offset rides in an
+        // SGPR (soffset), the lane's offset is a constant VGPR, so no vector
+        // address arithmetic per tile
+        const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)kb, (short)0, nk_pad * kRec * (int)sizeof(uint16_t), 0x00020000);
+        const int voff = lane_off * (int)sizeof(uint16_t);
         auto key = [&](int k) {
-            return load_bf16x8(kb + (size_t)min(first + k * W, last) * kTile * kRec + lane_off);
+            const int t = min(first + k * W, last);
+            return __builtin_bit_cast(
+                bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                            krs, voff, t * (kTile * kRec * (int)sizeof(uint16_t)), 0));
         };
         auto tile = [&](const bf16x8 &Bt) {
 #pragma unroll
@@ -669,12 +678,12 @@ int lse3_splits(int B, int nq_pad, int nk_pad)
 
 // Waves per work-group of the matrix-core pass.  Every wave pays a fixed cost
 // (query operands, shift, merge) besides its key tiles.  Long rows (512 tiles
-// or more per split) take 8 waves; shorter rows take the fewest waves that
-// still give about 4096 waves per launch (4 per SIMD), which spreads that
+// or more per split) take 8 waves; shorter rows take at most 4, and the fewest
+// that still give about 4096 waves per launch (4 per SIMD), which spreads that
 // fixed cost over the most tiles.  Every wave gets at least 2 tiles.
 int lse3m_waves(long groups, int tiles_per_split)
 {
-    int w = 8;
+    int w = tiles_per_split >= 512 ? 8 : 4;
     if (tiles_per_split < 512)
         while (w > 1 && groups * (w / 2) >= 4096)
             w /= 2;
