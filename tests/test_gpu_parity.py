@@ -850,3 +850,63 @@ def test_random_shapes_match_oracle(B, n, m, kind, weights, eps, iters, seed):
         np.testing.assert_allclose(host(loss), lo, rtol=1e-4)
         for p in range(B):
             assert rel_inf(host(dX)[p], dXo[p], 1e-30) <= 1e-4
+
+
+# ------------------------------------------------------- streams and graph capture
+def test_work_follows_the_callers_stream():
+    # inputs produced on a side stream and every call issued there: the results
+    # equal those of the default stream (nothing runs on another stream)
+    c = workloads.random_case(61, 3, 500, 400, 3, weights="dirichlet")
+    eps = 0.03
+    X0, Y0 = points(c)
+    a0, b0 = dev(c["a"]), dev(c["b"])
+    f0, g0, cost0 = sk.potentials(X0, Y0, a0, b0, eps=[eps], iters=[20])
+    loss0 = torch.empty(3, device=X0.device)
+    dX0 = torch.empty(3, 500, 3, device=X0.device)
+    plan0 = sk.plan_coo(X0, Y0, a0, b0, f0, g0, eps, 1e-8, loss_out=(loss0, dX0))
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        X, Y = X0 * 1.0, Y0 * 1.0          # produced on s
+        a, b = a0 * 1.0, b0 * 1.0
+        f, g, cost = sk.potentials(X, Y, a, b, eps=[eps], iters=[20])
+        loss = torch.empty(3, device=X.device)
+        dX = torch.empty(3, 500, 3, device=X.device)
+        plan = sk.plan_coo(X, Y, a, b, f, g, eps, 1e-8, loss_out=(loss, dX))
+    s.synchronize()
+    for u, v in ((f, f0), (g, g0), (cost, cost0), (loss, loss0), (dX, dX0)):
+        assert torch.equal(u, v)
+    for u, v in zip(plan, plan0):
+        assert torch.equal(u, v)
+
+
+def test_potentials_replay_from_a_captured_graph():
+    # the potentials entry point launches kernels only (no allocation, copy or
+    # wait), so a caller can capture it; every replay equals the eager result
+    c = workloads.random_case(62, 2, 700, 600, 3, weights="dirichlet")
+    X, Y = points(c)
+    a, b = dev(c["a"]), dev(c["b"])
+    B, n, m = 2, 700, 600
+    ws = torch.empty(sk.workspace_bytes(sk.SK_OP_POTENTIALS, B, n, m, 3, sk.SK_F32),
+                     dtype=torch.uint8, device=X.device)
+    out = (torch.empty(B, n, device=X.device), torch.empty(B, m, device=X.device),
+           torch.empty(B, device=X.device))
+    sched = dict(eps=[0.3, 0.05, 0.02], iters=[3, 5, 10])
+    sk.potentials(X, Y, a, b, out=out, workspace=ws, **sched)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in out]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            sk.potentials(X, Y, a, b, out=out, workspace=ws, **sched)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in out:
+            t.fill_(float("nan"))          # eager work between the replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for t, r in zip(out, ref):
+            assert torch.equal(t, r), f"replay {rep}"
