@@ -32,12 +32,15 @@ constexpr int kMaxNormDim = 4096;   // dimensions accepted by the normalisation
 constexpr int kPad = 64;
 
 // Bump allocator over the caller's workspace (256-byte aligned pieces).
+// Pieces of the caller's workspace, each at a 256-byte aligned address (the
+// sizes add 256 bytes of slack for a workspace that starts unaligned).
 struct Carve {
     char *base;
     size_t off = 0;
     template <typename T> T *take(size_t count)
     {
-        off = (off + 255) & ~(size_t)255;
+        const uintptr_t at = (uintptr_t)base + off;
+        off += (((at + 255) & ~(uintptr_t)255) - at);
         T *p = base ? reinterpret_cast<T *>(base + off) : nullptr;
         off += count * sizeof(T);
         return p;
@@ -66,6 +69,7 @@ struct PotWs {
     float2 *part;
     double *row_part;
     double *la, *lb;   // fp64 log-weights for the cost pass
+    KeyD *kd = nullptr;   // d = 3: fp64 keys of the cost pass
 };
 
 PotWs carve_potentials(Carve &c, int B, int n, int m, int d, int dtype)
@@ -98,6 +102,8 @@ PotWs carve_potentials(Carve &c, int B, int n, int m, int d, int dtype)
     w.row_part = c.take<double>((size_t)B * n);
     w.la = c.take<double>((size_t)B * n);
     w.lb = c.take<double>((size_t)B * m);
+    if (d == 3)
+        w.kd = c.take<KeyD>((size_t)B * m);
     return w;
 }
 
@@ -106,9 +112,10 @@ struct CooWs {
     double *row_max, *pair_thr;
     int32_t *row_count;
     int64_t *row_off, *pair_tot;
+    KeyD *kd = nullptr;   // d = 3: fp64 keys of the max and count passes
 };
 
-CooWs carve_coo(Carve &c, int B, int n, int m)
+CooWs carve_coo(Carve &c, int B, int n, int m, int d)
 {
     CooWs w;
     w.la = c.take<double>((size_t)B * n);
@@ -118,6 +125,8 @@ CooWs carve_coo(Carve &c, int B, int n, int m)
     w.row_count = c.take<int32_t>((size_t)B * n);
     w.row_off = c.take<int64_t>((size_t)B * n);
     w.pair_tot = c.take<int64_t>(B);
+    if (d == 3)
+        w.kd = c.take<KeyD>((size_t)B * m);
     return w;
 }
 
@@ -137,6 +146,7 @@ LossWs carve_loss(Carve &c, int B, int n)
 
 struct GradWs {
     double *la, *lb;
+    KeyD *kdx = nullptr, *kdy = nullptr;   // d = 3: fp64 keys of the two sides
     // matrix-core path (bf16, d = 32 or 64)
     float *xbias = nullptr, *ybias = nullptr, *xsq = nullptr, *ysq = nullptr;
     float *l2a = nullptr, *l2b = nullptr;
@@ -149,6 +159,10 @@ GradWs carve_grad(Carve &c, int B, int n, int m, int d, int dtype)
     GradWs w;
     w.la = c.take<double>((size_t)B * n);
     w.lb = c.take<double>((size_t)B * m);
+    if (d == 3) {
+        w.kdx = c.take<KeyD>((size_t)B * n);
+        w.kdy = c.take<KeyD>((size_t)B * m);
+    }
     if (gradF_matrix_cores(dtype, d)) {
         const int np = round_up(n, kPad), mp = round_up(m, kPad);
         w.xbias = c.take<float>((size_t)B * np);
@@ -209,6 +223,10 @@ HvpWs carve_hvp(Carve &c, int B, int n, int m, int d)
     w.dir = c.take<double>(Bm);
     w.rr = c.take<double>(B);
     w.rr0 = c.take<double>(B);
+    if (d == 3) {
+        w.kdx = c.take<KeyD>(Bn);
+        w.kdy = c.take<KeyD>(Bm);
+    }
     return w;
 }
 
@@ -218,7 +236,7 @@ size_t ws_size(int op, int B, int n, int m, int d, int dtype)
     if (op == SK_OP_POTENTIALS)
         carve_potentials(c, B, n, m, d, dtype);
     else if (op == SK_OP_PLAN_COO)
-        carve_coo(c, B, n, m);
+        carve_coo(c, B, n, m, d);
     else if (op == SK_OP_LOSS_GRAD)
         carve_loss(c, B, n);
     else if (op == SK_OP_DENSE_GRAD)
@@ -377,9 +395,10 @@ int sinkhorn_potentials(const void *X, const void *Y, int dtype, const float *a,
             (e = launch_row_sums(w.row_part, B, n, cost, st)))
             return hip_fail(e, "cost");
     } else if (cost) {
-        PlanArgs p{X, Y, dtype, d, B, n, m, f, g, w.la, w.lb, 1.0 / (double)eps[n_stages - 1]};
+        PlanArgs p{X, Y, dtype, d, B, n, m, f, g, w.la, w.lb, 1.0 / (double)eps[n_stages - 1], w.kd};
         if ((e = launch_log_weights(a, B, n, w.la, st)) ||
-            (e = launch_log_weights(b, B, m, w.lb, st)))
+            (e = launch_log_weights(b, B, m, w.lb, st)) ||
+            (w.kd && (e = launch_keys_d3(Y, dtype, g, B, m, w.kd, st))))
             return hip_fail(e, "log weights");
         if ((e = launch_cost(p, w.row_part, cost, st)))
             return hip_fail(e, "cost");
@@ -412,10 +431,11 @@ int sinkhorn_plan_coo(const void *X, const void *Y, int dtype, const float *a, c
 
     hipStream_t st = (hipStream_t)stream;
     Carve c{(char *)ws};
-    CooWs w = carve_coo(c, B, n, m);
-    PlanArgs p{X, Y, dtype, d, B, n, m, f, g, w.la, w.lb, 1.0 / (double)eps};
+    CooWs w = carve_coo(c, B, n, m, d);
+    PlanArgs p{X, Y, dtype, d, B, n, m, f, g, w.la, w.lb, 1.0 / (double)eps, w.kd};
     hipError_t e;
-    if ((e = launch_log_weights(a, B, n, w.la, st)) || (e = launch_log_weights(b, B, m, w.lb, st)))
+    if ((e = launch_log_weights(a, B, n, w.la, st)) || (e = launch_log_weights(b, B, m, w.lb, st)) ||
+        (w.kd && (e = launch_keys_d3(Y, dtype, g, B, m, w.kd, st))))
         return hip_fail(e, "log weights");
     if ((e = launch_plan_max(p, w.row_max, w.pair_thr, log((double)rel_threshold), st)))
         return hip_fail(e, "plan max");
@@ -489,8 +509,11 @@ int sinkhorn_dense_grad(const void *X, const void *Y, int dtype, const float *a,
     const double inv_eps = 1.0 / (double)eps;
     const bool want_x = dX || TX, want_y = dY || TY;
     // log P is symmetric in (X, a, f) and (Y, b, g): the Y side is the same pass
-    PlanArgs px{X, Y, dtype, d, B, n, m, f, g, w.la, w.lb, inv_eps};
-    PlanArgs py{Y, X, dtype, d, B, m, n, g, f, w.lb, w.la, inv_eps};
+    PlanArgs px{X, Y, dtype, d, B, n, m, f, g, w.la, w.lb, inv_eps, w.kdy};
+    PlanArgs py{Y, X, dtype, d, B, m, n, g, f, w.lb, w.la, inv_eps, w.kdx};
+    if ((want_x && w.kdy && (e = launch_keys_d3(Y, dtype, g, B, m, w.kdy, st))) ||
+        (want_y && w.kdx && (e = launch_keys_d3(X, dtype, f, B, n, w.kdx, st))))
+        return hip_fail(e, "dense gradient: keys");
     const bool aligned = (uintptr_t)X % 16 == 0 && (uintptr_t)Y % 16 == 0;
     if (gradF_matrix_cores(dtype, d) && aligned) {
         const int np = round_up(n, kPad), mp = round_up(m, kPad);
@@ -550,8 +573,11 @@ int sinkhorn_hvp(const void *X, const void *Y, int dtype, const float *a, const 
     if ((e = launch_log_weights(a, B, n, w.la, st)) || (e = launch_log_weights(b, B, m, w.lb, st)))
         return hip_fail(e, "log weights");
     const double inv_eps = 1.0 / (double)eps;
-    PlanArgs px{X, Y, dtype, d, B, n, m, f, g, w.la, w.lb, inv_eps};
-    PlanArgs py{Y, X, dtype, d, B, m, n, g, f, w.lb, w.la, inv_eps};
+    PlanArgs px{X, Y, dtype, d, B, n, m, f, g, w.la, w.lb, inv_eps, w.kdy};
+    PlanArgs py{Y, X, dtype, d, B, m, n, g, f, w.lb, w.la, inv_eps, w.kdx};
+    if (w.kdx && ((e = launch_keys_d3(Y, dtype, g, B, m, w.kdy, st)) ||
+                  (e = launch_keys_d3(X, dtype, f, B, n, w.kdx, st))))
+        return hip_fail(e, "Hessian-vector product: keys");
     if ((e = launch_hvp(px, py, V, cg_iters, HV, cg_residual, w, st)))
         return hip_fail(e, "Hessian-vector product");
     return SK_OK;

@@ -175,6 +175,13 @@ hipError_t launch_costFm(SideF x, SideF y, int d, int B, float eps, double *row_
                          hipStream_t st);
 hipError_t launch_row_sums(const double *row_part, int B, int n, float *out, hipStream_t st);
 
+// One key of a d = 3 plan pass as fp64: point components and potential (exact
+// conversions of the inputs), 32 bytes.
+struct alignas(32) KeyD {
+    double y[3];
+    double g;
+};
+
 // Plan evaluation passes, shared by the cost, max, count and emit steps.
 struct PlanArgs {
     const void *X, *Y;
@@ -182,7 +189,11 @@ struct PlanArgs {
     const float *f, *g;      // true potentials
     const double *la, *lb;   // natural log of the weights, [B][n] and [B][m] (-inf for 0)
     double inv_eps;
+    const KeyD *kd = nullptr;   // d = 3: the keys (Y, g) as KeyD [B][m], or NULL
 };
+// KeyD records of the keys (Y [B][m][3], g [B][m]) of a d = 3 pass.
+hipError_t launch_keys_d3(const void *Y, int dtype, const float *g, int B, int m, KeyD *out,
+                          hipStream_t st);
 // log of the weights in fp64 (w == NULL: uniform 1/count)
 hipError_t launch_log_weights(const float *w, int B, int count, double *out, hipStream_t st);
 hipError_t launch_cost(const PlanArgs &p, double *row_part, float *cost, hipStream_t st);
@@ -249,6 +260,7 @@ struct HvpWs {
     double *mb, *muc, *tw, *rhs;        // [B][m]
     double *x, *res, *dir;              // conjugate-gradient vectors [B][m]
     double *rr, *rr0;                   // [B]
+    KeyD *kdx = nullptr, *kdy = nullptr;   // d = 3: fp64 keys of the two sides
 };
 hipError_t launch_hvp(const PlanArgs &px, const PlanArgs &py, const float *V, int cg_iters,
                       float *HV, float *cg_residual, const HvpWs &w, hipStream_t st);

@@ -32,7 +32,7 @@ enum : int { F_V = 1, F_U = 2, F_W = 4, F_D = 8 };
 // Per row i of p.X against the keys of p.Y:
 //   m0 = sum P;  mu = sum P u_j (F_U);  D1 = sum P (x - y), Du = sum P u_j (x - y) (F_D);
 //   tv = sum P (x - y).v_i, Tv = sum P ((x - y).v_i)(x - y) (F_V);  tw = sum P (x - y).w_j (F_W).
-template <typename T, int DP, int FL>
+template <typename T, int DP, int FL, bool KD>
 __global__ __launch_bounds__(kHvpWaves *kWave) void transport_pass(
     PlanArgs p, const float *__restrict__ v, const double *__restrict__ u,
     const float *__restrict__ wk, double *__restrict__ o_m0, double *__restrict__ o_mu,
@@ -56,20 +56,18 @@ __global__ __launch_bounds__(kHvpWaves *kWave) void transport_pass(
     const T *Yb = (const T *)p.Y + (size_t)b * p.m * p.d;
     const float *gb = p.g + (size_t)b * p.m;
     const double *lbb = p.lb + (size_t)b * p.m;
+    const KeyD *kdb = p.kd ? p.kd + (size_t)b * p.m : nullptr;
     double m0 = 0.0, mu = 0.0, tv = 0.0, tw = 0.0;
     double D1[DP], Du[DP], Tv[DP];
 #pragma unroll
     for (int k = 0; k < DP; ++k)
         D1[k] = Du[k] = Tv[k] = 0.0;
-    for (int j = w; j < p.m; j += kHvpWaves) {
-        double C;
-        const double lp = log_plan<T, DP>(r, p, Yb, gb, lbb[j], j, &C);
+    auto visit = [&](int j) {
+        double C, diff[DP];
+        KeyVals<DP> kv;
+        load_key<T, DP, KD>(kv, p, Yb, gb, kdb, j);
+        const double lp = log_plan_kv<DP>(r, kv, lbb[j], p.inv_eps, p.d, &C, diff);
         const double P = (double)ex2((float)(lp * 1.4426950408889634));
-        const T *y = Yb + (size_t)j * p.d;
-        double diff[DP];
-#pragma unroll
-        for (int k = 0; k < DP; ++k)
-            diff[k] = has_dim<DP>(k, p.d) ? (double)r.x[k] - (double)Elem<T>::get(y, k) : 0.0;
         m0 += P;
         double uj = 0.0;
         if (FL & F_U) {
@@ -103,7 +101,20 @@ __global__ __launch_bounds__(kHvpWaves *kWave) void transport_pass(
                     dw = fma(diff[k], (double)wj[k], dw);
             tw = fma(P, dw, tw);
         }
+    };
+    int j = w;
+    if constexpr (DP <= 4) {
+        // four keys per step, so that their loads are in flight together (the
+        // sums still take the keys in order)
+        for (; j + 3 * kHvpWaves < p.m; j += 4 * kHvpWaves) {
+            visit(j);
+            visit(j + kHvpWaves);
+            visit(j + 2 * kHvpWaves);
+            visit(j + 3 * kHvpWaves);
+        }
     }
+    for (; j < p.m; j += kHvpWaves)
+        visit(j);
     // merge the waves' partial sums in a fixed order, one quantity at a time
     auto merged = [&](double val) {
         __syncthreads();
@@ -279,15 +290,16 @@ void pass(const PlanArgs &p, const float *v, const double *u, const float *wk, d
           double *mu, double *tv, double *tw, double *D1, double *Du, double *Tv, hipStream_t st)
 {
     dim3 grid(ceil_div(p.n, kWave), p.B), block(kHvpWaves * kWave);
-    auto go = [&]<int DP>() {
+    auto go = [&]<int DP, bool KD = false>() {
         if (p.dtype == 1)
-            hipLaunchKernelGGL((transport_pass<uint16_t, DP, FL>), grid, block, 0, st, p, v, u, wk,
-                               m0, mu, tv, tw, D1, Du, Tv);
+            hipLaunchKernelGGL((transport_pass<uint16_t, DP, FL, KD>), grid, block, 0, st, p, v, u,
+                               wk, m0, mu, tv, tw, D1, Du, Tv);
         else
-            hipLaunchKernelGGL((transport_pass<float, DP, FL>), grid, block, 0, st, p, v, u, wk,
+            hipLaunchKernelGGL((transport_pass<float, DP, FL, KD>), grid, block, 0, st, p, v, u, wk,
                                m0, mu, tv, tw, D1, Du, Tv);
     };
-    if (p.d == 3) go.template operator()<3>();
+    if (p.d == 3 && p.kd) go.template operator()<3, true>();
+    else if (p.d == 3) go.template operator()<3>();
     else if (p.d <= 4) go.template operator()<4>();
     else if (p.d <= 8) go.template operator()<8>();
     else go.template operator()<16>();

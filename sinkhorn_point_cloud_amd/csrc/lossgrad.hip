@@ -74,11 +74,7 @@ __global__ __launch_bounds__(kRowsPerGroup *kWave) void loss_grad_rows(
         const int j = cols[k];
         if (j < 0 || j >= m)
             return;
-        float y[DP];
-#pragma unroll
-        for (int c = 0; c < DP; ++c)
-            y[c] = has(c) ? Elem<T>::get(Yb, (size_t)j * d + c) : 0.f;
-        loss_term<DP>(x, y, d, vals[k], loss, gr);
+        loss_term_at<T, DP>(x, Yb + (size_t)j * d, d, vals[k], loss, gr);
     };
     // two entries per lane and step keep more loads in flight
     int64_t k = k0 + lane;
@@ -151,7 +147,7 @@ __global__ __launch_bounds__(kStagedWaves *kWave) void loss_grad_staged(
 #pragma unroll
             for (int c = 0; c < DP; ++c)
                 y[c] = ys[(size_t)c * m + j];
-            loss_term<DP>(x, y, d, vals[k], loss, gr);
+            loss_term_xy<DP>(x, y, d, vals[k], loss, gr);
         };
         int64_t k = k0 + lane;
         for (; k + kWave < k1; k += 2 * kWave) {

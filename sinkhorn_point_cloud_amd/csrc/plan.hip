@@ -56,7 +56,7 @@ constexpr int kGradDims = 16;   // gradient components accumulated per launch (n
 // mode 1: max   (row max of log P, double)        -> outd[row]
 // mode 2: count (entries >= thr, int32)           -> outi[row]
 // mode 3: dense gradient for dims k0 .. k0+KC-1   -> grad, proj (fp32, [B][n][d])
-template <typename T, int DP, int MODE>
+template <typename T, int DP, int MODE, bool KD>
 __global__ __launch_bounds__(kTileWaves *kWave) void tile_pass(
     PlanArgs p, const double *__restrict__ thr, double *__restrict__ outd,
     int32_t *__restrict__ outi, float *__restrict__ grad, float *__restrict__ proj, int k0,
@@ -77,6 +77,7 @@ __global__ __launch_bounds__(kTileWaves *kWave) void tile_pass(
     const T *Yb = (const T *)p.Y + (size_t)b * p.m * p.d;
     const float *gb = p.g + (size_t)b * p.m;
     const double *lbb = p.lb + (size_t)b * p.m;
+    const KeyD *kdb = p.kd ? p.kd + (size_t)b * p.m : nullptr;
     const double t = MODE == 2 ? thr[b] : 0.0;
     double acc = MODE == 1 ? -INFINITY : 0.0;
     int cnt = 0;
@@ -89,9 +90,20 @@ __global__ __launch_bounds__(kTileWaves *kWave) void tile_pass(
             xc[k] = MODE == 3 && has_dim<DP>(k0 + k, p.d) ? (double)Elem<T>::get(x, k0 + k) : 0.0;
         }
     }
+    // narrow points: the key's values in registers (from KeyD records for d = 3),
+    // and whole-row gradients (one chunk) reuse the evaluation's differences
+    constexpr bool kRegs = DP <= kKeyRegDims;
+    constexpr bool kDiff = kRegs && MODE == 3 && KC == DP;
     auto visit = [&](int j) {
-        double C;
-        const double lp = log_plan<T, DP>(r, p, Yb, gb, lbb[j], j, &C);
+        double C, lp;
+        double diff[kDiff ? DP : 1];
+        if constexpr (kRegs) {
+            KeyVals<DP> kv;
+            load_key<T, DP, KD>(kv, p, Yb, gb, kdb, j);
+            lp = log_plan_kv<DP>(r, kv, lbb[j], p.inv_eps, p.d, &C, kDiff ? diff : nullptr);
+        } else {
+            lp = log_plan<T, DP>(r, p, Yb, gb, lbb[j], j, &C);
+        }
         if (MODE == 0) {
             const double P = (double)ex2((float)(lp * 1.4426950408889634));
             acc = fma(P, C, acc);
@@ -102,11 +114,18 @@ __global__ __launch_bounds__(kTileWaves *kWave) void tile_pass(
         } else {
             const double P = (double)ex2((float)(lp * 1.4426950408889634));
             acc += P;
-            const T *y = Yb + (size_t)j * p.d;
+            if constexpr (kDiff) {
 #pragma unroll
-            for (int k = 0; k < KC; ++k)
-                if (has_dim<DP>(k0 + k, p.d))
-                    G[k] = fma(P, xc[k] - (double)Elem<T>::get(y, k0 + k), G[k]);
+                for (int k = 0; k < KC; ++k)
+                    if (has_dim<DP>(k, p.d))
+                        G[k] = fma(P, diff[k], G[k]);
+            } else {
+                const T *y = Yb + (size_t)j * p.d;
+#pragma unroll
+                for (int k = 0; k < KC; ++k)
+                    if (has_dim<DP>(k0 + k, p.d))
+                        G[k] = fma(P, xc[k] - (double)Elem<T>::get(y, k0 + k), G[k]);
+            }
         }
     };
     int j = w;
@@ -295,15 +314,9 @@ __global__ __launch_bounds__(kRowsPerGroup *kWave) void emit_pass(
     for (int j0 = 0; j0 < p.m && pos < end; j0 += kWave) {
         const int j = j0 + lane;
         bool keep = false;
-        double lp = 0.0;
-        float y[DP];
+        double lp = 0.0, C = 0.0;
         if (j < p.m) {
-            const T *yp = Yb + (size_t)j * p.d;
-#pragma unroll
-            for (int k = 0; k < DP; ++k)
-                y[k] = has_dim<DP>(k, p.d) ? Elem<T>::get(yp, k) : 0.f;
-            double C;
-            lp = log_plan_at<DP>(r, y, gb[j], p.lb[(size_t)b * p.m + j], p.inv_eps, p.d, &C);
+            lp = log_plan<T, DP>(r, p, Yb, gb, p.lb[(size_t)b * p.m + j], j, &C);
             keep = lp >= t;
         }
         const uint64_t mask = __ballot(keep);
@@ -314,8 +327,8 @@ __global__ __launch_bounds__(kRowsPerGroup *kWave) void emit_pass(
                 rows[k] = i;
                 cols[k] = j;
                 vals[k] = P;
-                if (LG)
-                    loss_term<DP>(r.x, y, p.d, P, loss, gr);
+                if constexpr (LG)   // differences recomputed: no per-entry array for wide rows
+                    loss_term_at<T, DP>(r.x, Yb + (size_t)j * p.d, p.d, P, loss, gr);
             }
         }
         pos += __popcll(mask);
@@ -341,10 +354,10 @@ __global__ __launch_bounds__(kRowsPerGroup *kWave) void emit_pass(
 // Emit pass for small d with the keys staged in LDS: a work-group of
 // kEmitWaves waves takes kEmitRows consecutive rows of one pair (a wave per row
 // at a time, lanes across 64 consecutive columns, as above) and shares one
-// staged copy of each chunk of kEmitChunk columns (point components as fp32,
-// g_j, log b_j), so the column data is read from memory once per work-group
-// instead of once per row.  The evaluation is log_plan_at on the same values
-// as the count pass, so the decisions agree bit for bit.
+// staged copy of each chunk of kEmitChunk columns (point components and g_j as
+// fp64, log b_j), so the column data is read and converted once per work-group
+// instead of once per row.  The evaluation is log_plan_kv on the same values as
+// the count pass, so the decisions agree bit for bit.
 constexpr int kEmitWaves = 8, kEmitRows = 32, kEmitChunk = 1024;
 
 template <typename T, int DP, bool LG>
@@ -355,8 +368,8 @@ __global__ __launch_bounds__(kEmitWaves *kWave) void emit_staged(
 {
     static_assert(DP <= 4, "staged emit holds at most 4 components per column");
     constexpr int kRowsPerWave = kEmitRows / kEmitWaves;
-    __shared__ float ys[DP][kEmitChunk];
-    __shared__ float gs[kEmitChunk];
+    __shared__ double ys[DP][kEmitChunk];
+    __shared__ double gs[kEmitChunk];
     __shared__ double lbs[kEmitChunk];
     const int b = blockIdx.y;
     const int wave = wave_id_uniform(), lane = lane_id();
@@ -385,11 +398,12 @@ __global__ __launch_bounds__(kEmitWaves *kWave) void emit_staged(
         const int kc = min(kEmitChunk, p.m - c0);
         __syncthreads();   // the previous chunk is no longer read
         for (int j = threadIdx.x; j < kc; j += kEmitWaves * kWave) {
-            const T *yp = Yb + (size_t)(c0 + j) * p.d;
+            KeyVals<DP> kv;
+            load_key<T, DP, false>(kv, p, Yb, gb, nullptr, c0 + j);
 #pragma unroll
             for (int k = 0; k < DP; ++k)
-                ys[k][j] = has_dim<DP>(k, p.d) ? Elem<T>::get(yp, k) : 0.f;
-            gs[j] = gb[c0 + j];
+                ys[k][j] = kv.y[k];
+            gs[j] = kv.g;
             lbs[j] = lbb[c0 + j];
         }
         __syncthreads();
@@ -398,14 +412,16 @@ __global__ __launch_bounds__(kEmitWaves *kWave) void emit_staged(
             for (int j0 = 0; j0 < kc && pos[q] < end[q]; j0 += kWave) {   // wave-uniform
                 const int j = j0 + lane;
                 bool keep = false;
-                double lp = 0.0;
-                float y[DP];
+                double lp = 0.0, C = 0.0;
+                double diff[LG ? DP : 1];
                 if (j < kc) {
+                    KeyVals<DP> kv;
 #pragma unroll
                     for (int k = 0; k < DP; ++k)
-                        y[k] = ys[k][j];
-                    double C;
-                    lp = log_plan_at<DP>(r[q], y, gs[j], lbs[j], p.inv_eps, p.d, &C);
+                        kv.y[k] = ys[k][j];
+                    kv.g = gs[j];
+                    lp = log_plan_kv<DP>(r[q], kv, lbs[j], p.inv_eps, p.d, &C,
+                                         LG ? diff : nullptr);
                     keep = lp >= t;
                 }
                 const uint64_t mask = __ballot(keep);
@@ -416,8 +432,8 @@ __global__ __launch_bounds__(kEmitWaves *kWave) void emit_staged(
                         rows[k] = i0 + q;
                         cols[k] = c0 + j;
                         vals[k] = P;
-                        if (LG)
-                            loss_term<DP>(r[q].x, y, p.d, P, loss[q], gr[q]);
+                        if constexpr (LG)
+                            loss_term<DP>(diff, C, p.d, P, loss[q], gr[q]);
                     }
                 }
                 pos[q] += __popcll(mask);
@@ -447,6 +463,21 @@ __global__ __launch_bounds__(kEmitWaves *kWave) void emit_staged(
     }
 }
 
+template <typename T>
+__global__ void keys_d3_kernel(const T *__restrict__ Y, const float *__restrict__ g, size_t count,
+                               KeyD *__restrict__ out)
+{
+    const size_t k = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (k >= count)
+        return;
+    KeyD r;
+#pragma unroll
+    for (int c = 0; c < 3; ++c)
+        r.y[c] = (double)Elem<T>::get(Y, 3 * k + c);
+    r.g = (double)g[k];
+    out[k] = r;
+}
+
 template <typename F>
 void with_dp(int d, F fn)
 {
@@ -467,18 +498,41 @@ void tile_dispatch(const PlanArgs &p, const double *thr, double *outd, int32_t *
     dim3 block(kTileWaves * kWave);
     with_dp(p.d, [&]<int DP>() {
         const int chunks = MODE == 3 ? ceil_div(p.d, kGradDims) : 1;
-        for (int c = 0; c < chunks; ++c) {
-            if (p.dtype == 1)
-                hipLaunchKernelGGL((tile_pass<uint16_t, DP, MODE>), grid, block, 0, st, p, thr,
-                                   outd, outi, grad, proj, c * kGradDims, only);
-            else
-                hipLaunchKernelGGL((tile_pass<float, DP, MODE>), grid, block, 0, st, p, thr,
-                                   outd, outi, grad, proj, c * kGradDims, only);
+        auto go = [&]<bool KD>() {
+            for (int c = 0; c < chunks; ++c) {
+                if (p.dtype == 1)
+                    hipLaunchKernelGGL((tile_pass<uint16_t, DP, MODE, KD>), grid, block, 0, st, p,
+                                       thr, outd, outi, grad, proj, c * kGradDims, only);
+                else
+                    hipLaunchKernelGGL((tile_pass<float, DP, MODE, KD>), grid, block, 0, st, p,
+                                       thr, outd, outi, grad, proj, c * kGradDims, only);
+            }
+        };
+        if constexpr (DP == 3) {
+            if (p.kd) {
+                go.template operator()<true>();
+                return;
+            }
         }
+        go.template operator()<false>();
     });
 }
 
 }  // namespace
+
+hipError_t launch_keys_d3(const void *Y, int dtype, const float *g, int B, int m, KeyD *out,
+                          hipStream_t st)
+{
+    const size_t count = (size_t)B * m;
+    const dim3 grid((unsigned)((count + 255) / 256));
+    if (dtype == 1)
+        hipLaunchKernelGGL(keys_d3_kernel<uint16_t>, grid, dim3(256), 0, st, (const uint16_t *)Y,
+                           g, count, out);
+    else
+        hipLaunchKernelGGL(keys_d3_kernel<float>, grid, dim3(256), 0, st, (const float *)Y, g,
+                           count, out);
+    return hipGetLastError();
+}
 
 hipError_t launch_log_weights(const float *w, int B, int count, double *out, hipStream_t st)
 {

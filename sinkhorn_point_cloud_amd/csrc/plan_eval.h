@@ -4,6 +4,13 @@
 // (cost, sparse plan, dense gradient, transport products of the Hessian-vector
 // product) so that all of them see the same values; and the per-entry loss
 // term shared by the loss pass and the emission of the sparse plan.
+//
+// Every pass reads a key (column j) as fp64 values: its point components and
+// g_j, exact conversions of the inputs.  For d = 3 they come precomputed
+// (KeyD, one 32-byte record per key, written by launch_keys_d3), so that a pass
+// whose lanes share the key reads them with scalar loads and spends no vector
+// instruction on conversions; otherwise they are converted where they are read.
+// The values, and so every result, are the same either way.
 #pragma once
 #include "common.h"
 
@@ -23,71 +30,141 @@ __device__ __forceinline__ bool has_dim(int k, int d)
     return DP == 3 || k < d;
 }
 
-// ||x - y||^2 in fp64 from the fp32 components (exact conversions), in
-// component order
+// A key's point components and potential as fp64 (components past d are 0).
+template <int DP> struct KeyVals {
+    double y[DP];
+    double g;
+};
+
+// Key j of one pair: from its KeyD record (KD: DP = 3 with records present; a
+// compile-time choice, so that the loop around it has no branch) or converted
+// from the inputs.
+template <typename T, int DP, bool KD>
+__device__ __forceinline__ void load_key(KeyVals<DP> &kv, const PlanArgs &p, const T *Yb,
+                                         const float *gb, const KeyD *kdb, int j)
+{
+    if constexpr (KD) {
+        static_assert(DP == 3, "KeyD records hold three components");
+        const KeyD k = kdb[j];
+        kv.y[0] = k.y[0];
+        kv.y[1] = k.y[1];
+        kv.y[2] = k.y[2];
+        kv.g = k.g;
+        return;
+    }
+    const T *yp = Yb + (size_t)j * p.d;
+#pragma unroll
+    for (int k = 0; k < DP; ++k)
+        kv.y[k] = has_dim<DP>(k, p.d) ? (double)Elem<T>::get(yp, k) : 0.0;
+    kv.g = (double)gb[j];
+}
+
+// log P_ij (nats) from the row context and the key's values; *C receives
+// C_ij = sum_k (x_k - y_k)^2 (differences exact in fp64, summed with fma in
+// component order).  Written with explicit fma so that every pass evaluates it
+// with the same roundings, and symmetric in the two sides (f_i + g_j,
+// (x - y)^2 = (y - x)^2 and log a_i + log b_j all round the same either way),
+// so a pass over the plan with the roles of X and Y exchanged sees
+// bit-identical values: the sparse plan of (Y, X) is exactly the transpose of
+// that of (X, Y).  With diff != nullptr the differences x_k - y_k are returned
+// too (callers with DP <= 16 only: they live in registers).
 template <int DP>
-__device__ __forceinline__ double sq_dist(const float (&x)[DP], const float (&y)[DP], int d)
+__device__ __forceinline__ double log_plan_kv(const RowCtx<DP> &r, const KeyVals<DP> &kv,
+                                              double lbj, double inv_eps, int d, double *C,
+                                              double *diff = nullptr)
 {
     double s = 0.0;
 #pragma unroll
     for (int k = 0; k < DP; ++k) {
         if (has_dim<DP>(k, d)) {
-            const double t = (double)x[k] - (double)y[k];
+            const double t = (double)r.x[k] - kv.y[k];
             s = fma(t, t, s);
+            if (diff)
+                diff[k] = t;
+        } else if (diff) {
+            diff[k] = 0.0;
         }
     }
-    return s;
+    *C = s;
+    return fma((r.f + kv.g) - s, inv_eps, r.la + lbj);
 }
 
-// log P_ij (nats) and C_ij from the row context and the column's values (its
-// point's components as fp32, g_j, log b_j).  Written with explicit fma so
-// that every pass evaluates it with the same roundings, and symmetric in the
-// two sides (f_i + g_j, (x - y)^2 = (y - x)^2 and log a_i + log b_j all round
-// the same either way), so a pass over the plan with the roles of X and Y
-// exchanged sees bit-identical values: the sparse plan of (Y, X) is exactly
-// the transpose of that of (X, Y).
-template <int DP>
-__device__ __forceinline__ double log_plan_at(const RowCtx<DP> &r, const float (&y)[DP], float gj,
-                                              double lbj, double inv_eps, int d, double *C)
-{
-    const double c = sq_dist<DP>(r.x, y, d);
-    *C = c;
-    return fma((r.f + (double)gj) - c, inv_eps, r.la + lbj);
-}
-
-// the same for column j of one pair, read from global memory
+// the same for column j of one pair, its components read from global memory
+// one at a time (no per-entry array: for wide points)
 template <typename T, int DP>
 __device__ __forceinline__ double log_plan(const RowCtx<DP> &r, const PlanArgs &p,
                                            const T *Yb, const float *gb, double lbj, int j,
                                            double *C)
 {
     const T *yp = Yb + (size_t)j * p.d;
-    float y[DP];
+    double s = 0.0;
 #pragma unroll
-    for (int k = 0; k < DP; ++k)
-        y[k] = has_dim<DP>(k, p.d) ? Elem<T>::get(yp, k) : 0.f;
-    return log_plan_at<DP>(r, y, gb[j], lbj, p.inv_eps, p.d, C);
+    for (int k = 0; k < DP; ++k) {
+        if (has_dim<DP>(k, p.d)) {
+            const double t = (double)r.x[k] - (double)Elem<T>::get(yp, k);
+            s = fma(t, t, s);
+        }
+    }
+    *C = s;
+    return fma((r.f + (double)gb[j]) - s, p.inv_eps, r.la + lbj);
 }
+
+// Points up to this width keep a key's values (and differences) in registers;
+// wider ones stream their components.
+constexpr int kKeyRegDims = 16;
 
 // One stored entry's share of the transport loss and of its gradient in x:
 //     loss += P ||x - y||^2,   gr += 2 P (x - y)
-// with x - y formed in fp32 and the squared distance summed in fp64.  The loss
-// pass over a stored plan and the emission that computes the loss on the fly
-// both call this, so they agree per entry (only the summation order differs).
+// from the exact fp64 differences diff = x - y and their squared norm C (as
+// log_plan_kv returns them); the gradient accumulates in fp32.  The loss pass
+// over a stored plan and the emission that computes the loss on the fly both
+// call this, so they agree per entry (only the summation order differs).
 template <int DP>
-__device__ __forceinline__ void loss_term(const float (&x)[DP], const float (&y)[DP], int d,
-                                          float P, double &loss, float (&gr)[DP])
+__device__ __forceinline__ void loss_term(const double (&diff)[DP], double C, int d, float P,
+                                          double &loss, float (&gr)[DP])
 {
-    double C = 0.0;
+#pragma unroll
+    for (int c = 0; c < DP; ++c)
+        if (has_dim<DP>(c, d))
+            gr[c] = fmaf(2.0f * P, (float)diff[c], gr[c]);
+    loss = fma((double)P, C, loss);
+}
+
+// The same from the row point and the key's point components (fp32 values),
+// for callers without the differences at hand: identical per-entry arithmetic
+// (each difference exact in fp64, squares summed with fma in component order).
+template <int DP>
+__device__ __forceinline__ void loss_term_xy(const float (&x)[DP], const float (&y)[DP], int d,
+                                             float P, double &loss, float (&gr)[DP])
+{
+    double s = 0.0;
 #pragma unroll
     for (int c = 0; c < DP; ++c) {
         if (has_dim<DP>(c, d)) {
-            const float t = x[c] - y[c];
-            C = fma((double)t, (double)t, C);
-            gr[c] = fmaf(2.0f * P, t, gr[c]);
+            const double t = (double)x[c] - (double)y[c];
+            s = fma(t, t, s);
+            gr[c] = fmaf(2.0f * P, (float)t, gr[c]);
         }
     }
-    loss = fma((double)P, C, loss);
+    loss = fma((double)P, s, loss);
+}
+
+// The same with the key's components read from memory one at a time (no
+// per-entry array, for wide points).
+template <typename T, int DP>
+__device__ __forceinline__ void loss_term_at(const float (&x)[DP], const T *yp, int d, float P,
+                                             double &loss, float (&gr)[DP])
+{
+    double s = 0.0;
+#pragma unroll
+    for (int c = 0; c < DP; ++c) {
+        if (has_dim<DP>(c, d)) {
+            const double t = (double)x[c] - (double)Elem<T>::get(yp, c);
+            s = fma(t, t, s);
+            gr[c] = fmaf(2.0f * P, (float)t, gr[c]);
+        }
+    }
+    loss = fma((double)P, s, loss);
 }
 
 template <typename T, int DP>

@@ -63,7 +63,7 @@ def test_workspace_bytes(lib):
     assert ws(0, 1, 10, 10, 200, 0) == 0               # d > 128: no kernel
     assert ws(0, 0, 10, 10, 3, 0) == 0
     assert ws(5, 1, 10, 10, 3, 0) == 0
-    assert ws(3, 1, 65536, 65536, 3, 0) < 4 << 20      # two fp64 log-weight vectors
+    assert ws(3, 1, 65536, 65536, 3, 0) < 6 << 20      # fp64 log weights and keys, O(n + m)
     assert ws(0, 1, 1 << 25, 10, 3, 0) == 0
     assert ws(0, 65535, 4, 4, 3, 0) > 0 and ws(0, 65536, 4, 4, 3, 0) == 0
 
