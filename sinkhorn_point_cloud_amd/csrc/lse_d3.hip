@@ -14,9 +14,12 @@
 // Work is done in base 2: with c = log2(e)/eps,
 //     s_ij = (2c x_i) . y_j + beta_j,   beta_j = c (g_j - ||y_j||^2) + log2 w_j,
 //     f_i  = ||x_i||^2 - (eps ln2) * log2 sum_j 2^(s_ij)
-// beta lives in the 4th lane of the packed key (x, y, z, beta), so one 16-byte
-// load brings a key and its bias.  Keys are read with wave-uniform addresses
-// (scalar loads, shared by all 64 lanes); each lane owns one query row.
+// Two kernels compute it.  The default one (lse3m_kernel, below) forms s on
+// the matrix cores from exact bf16 splits of the fp32 operands and streams each
+// row against a fixed shift; the vector one (lse3_kernel, behind
+// SK_VALU_SCORES) forms s with fp32 FMAs from packed keys (x, y, z, beta) read
+// with wave-uniform addresses, one query row per lane, and keeps a lazy online
+// maximum.  Both give the exact LSE up to fp32 rounding.
 //
 // The state carried between passes is the true potential (f, g), not the hat
 // potential f - ||x||^2: when the clouds are far from the origin compared with
@@ -24,16 +27,16 @@
 // ||x||^2 on every pass.  Each row's result and the bias it hands to the
 // other pass are formed in fp64 (a few operations per row) and rounded once.
 //
-// Online log-sum-exp with a lazy maximum: each lane keeps (M, S) meaning
+// Online log-sum-exp with a lazy maximum: each state keeps (M, S) meaning
 // S * 2^M.  Scores are formed relative to M; only when a tile holds a value
 // more than kLazy above M is the tile re-evaluated against the new maximum
 // and S rescaled.  The result is the exact LSE up to fp32 rounding, because
 // LSE(z) = M + log2 sum 2^(z - M) for any M and no term exceeds 2^kLazy.
 //
-// A work-group = 8 waves on the same 64 rows, each streaming every 8th key
-// tile; the eight (M, S) states merge through LDS.  When a batch has too few
-// rows to fill the chip the key range is also split across work-groups and a
-// second small kernel merges the partial states.
+// A work-group holds W waves on the same 64 rows, each streaming every W-th key
+// tile; their states merge at the end.  When a batch has too few rows to fill
+// the chip the key range is also split across work-groups and a second small
+// kernel merges the partial states.
 #include "common.h"
 
 namespace sk {
