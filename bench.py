@@ -208,7 +208,13 @@ def main():
     serial = 1.0 / (1.0 / fp32_bound + 1.0 / exp_bound)
 
     if d == 3 and dt == sk.SK_F32:
-        kernel = "lse3_kernel" if args.valu_scores else "lse3m_kernel"
+        # the library runs whole stages per pair in one launch when the batch has at
+        # least one pair per compute unit and both padded clouds hold <= 8192 points
+        pad = lambda k: (k + 63) // 64 * 64
+        pairwise = (B >= torch.cuda.get_device_properties(dev).multi_processor_count
+                    and pad(n) <= 8192 and pad(m) <= 8192)
+        kernel = ("lse3_kernel" if args.valu_scores else
+                  "lse3p_kernel" if pairwise else "lse3m_kernel")
     else:
         kernel = "lseFm_kernel" if dt == sk.SK_BF16 and d % 32 == 0 else "lseF_kernel"
 
@@ -239,7 +245,8 @@ def main():
                      if kernel in KERNEL_SOURCES else None,
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
                                      "scaled by a 256 MiB copy)",
-                     "kernel": kernel + " (one half-iteration)",
+                     "kernel": kernel + (" (one half-iteration of a per-pair stage launch)"
+                                         if kernel == "lse3p_kernel" else " (one half-iteration)"),
                      "launch_ms": t_launch * 1e3, "evals_per_launch": evals_per_launch,
                      "serial_exp_fp32_peak": serial / 1e12,
                      "frac_of_serial_peak": achieved / serial},

@@ -342,6 +342,7 @@ int sinkhorn_potentials(const void *X, const void *Y, int dtype, const float *a,
     const double c0 = (double)scale_of(first >= 0 ? eps[first] : 1.0f);
     hipError_t e;
     const bool p3 = path3(dtype, d);
+    const bool pairwise = p3 && mfma && lse3_pairwise(B, np, mp);
     // the caller's f and g are the state of the iteration
     Side3 sx3{w.px, f, w.l2a, w.kxrec, w.qxrec, n, np}, sy3{w.py, g, w.l2b, w.kyrec, w.qyrec, m, mp};
     SideF sxf{X, w.xbias, f, w.l2a, w.xsq, w.xredo, n, np};
@@ -365,6 +366,17 @@ int sinkhorn_potentials(const void *X, const void *Y, int dtype, const float *a,
             // query records carry 2c x, so they follow eps
             if ((e = launch_qrec3(sx3, B, eps[s], st)) || (e = launch_qrec3(sy3, B, eps[s], st)))
                 return hip_fail(e, "query records");
+        }
+        if (p3 && mfma && iters[s] > 0 && pairwise) {
+            float eps_next = eps[s];   // eps of the f-update after the stage's last g-update
+            for (int t = s + 1; t < n_stages; ++t)
+                if (iters[t] > 0) {
+                    eps_next = eps[t];
+                    break;
+                }
+            if ((e = launch_lse3_pairwise(sx3, sy3, B, eps[s], iters[s], eps_next, st)))
+                return hip_fail(e, "iterations");
+            continue;
         }
         for (int it = 0; it < iters[s]; ++it) {
             // eps of the f-update that follows this g-update

@@ -413,139 +413,77 @@ __device__ __forceinline__ f32x4 mfma4(bf16x8 a, bf16x8 b, f32x4 c)
 constexpr float kSumLo = 5.421010862e-20f;  // 2^-64
 constexpr float kSumHi = 1.2676506e30f;     // 2^100
 
+// Shifted stream of one wave: key tiles first, first + W, ... (cnt of them)
+// against the wave's 64 rows, accumulated into S with the shift in Cn.  The
+// first cnt % 3 tiles go one by one, the rest in groups of three with no
+// branch inside a group, so every key operand is loaded two tiles ahead of its
+// use (the scheduling barriers keep each load in place; indices are clamped to
+// the wave's last tile so that loads past the end stay inside the pair).  Three
+// register sets take turns, so no operand is copied.  Key operands come through
+// a buffer resource: the tile offset rides in an SGPR (soffset), the lane's
+// offset is a constant VGPR, so there is no vector address arithmetic per tile.
 template <int W>
-__global__ __launch_bounds__(W *kWave) void lse3m_kernel(
-    float4 *__restrict__ qpts, uint16_t *__restrict__ qkrec, const uint16_t *__restrict__ qrec,
-    const uint16_t *__restrict__ krec, float *__restrict__ qpot, const float *__restrict__ ql2w,
-    float2 *__restrict__ part, int nq, int nq_pad, int nk_pad, int tiles_per_split, float two_c,
-    double eps_ln2, double c_next)
+__device__ __forceinline__ void shifted_stream(const bf16x8 (&A)[kGroups],
+                                               const f32x4 (&Cn)[kGroups], f32x4 (&S)[kGroups],
+                                               const uint16_t *kb, int nk_pad, int lane_off,
+                                               int first, int cnt)
 {
-    __shared__ float2 red[W][kWave];
-    __shared__ int redo;
-    const int b = blockIdx.z;
-    const int split = blockIdx.y;
-    const int lane = lane_id();
-    const int w = wave_id_uniform();
-    const int row0 = blockIdx.x * kWave;
-    const int kq = lane >> 4;      // operand k index this lane supplies / row quad it receives
-    const int c16 = lane & 15;     // operand row (A) or column (B) within a 16-block
-
-    const float4 *qrow = qpts + (size_t)b * nq_pad + row0;
-    const int lane_off = c16 * kRec + 8 * kq;   // this lane's 8 slots of a record
-    bf16x8 A[kGroups];
+    const int last = first + (cnt > 0 ? cnt - 1 : 0) * W;
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)kb, (short)0, nk_pad * kRec * (int)sizeof(uint16_t), 0x00020000);
+    const int voff = lane_off * (int)sizeof(uint16_t);
+    auto key = [&](int k) {
+        const int t = min(first + k * W, last);
+        return __builtin_bit_cast(
+            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                        krs, voff, t * (kTile * kRec * (int)sizeof(uint16_t)), 0));
+    };
+    auto tile = [&](const bf16x8 &Bt) {
 #pragma unroll
-    for (int g = 0; g < kGroups; ++g)
-        A[g] = load_bf16x8(qrec + ((size_t)b * nq_pad + row0 + 16 * g) * kRec + lane_off);
-    const uint16_t *kb = krec + (size_t)b * nk_pad * kRec;
-    const int n_tiles = nk_pad / kTile;
-    const int t_begin = split * tiles_per_split;
-    const int t_end = min(t_begin + tiles_per_split, n_tiles);
-    f32x4 Cn[kGroups], S[kGroups];
-
-    if (part == nullptr) {
-        // ---- shifted pass
-        const float c = 0.5f * two_c;
+        for (int g = 0; g < kGroups; ++g) {
+            const f32x4 D = mfma4(A[g], Bt, Cn[g]);
 #pragma unroll
-        for (int g = 0; g < kGroups; ++g)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int lr = 16 * g + 4 * kq + r;
-                const float4 p = qrow[lr];
-                const float f = row0 + lr < nq ? qpot[(size_t)b * nq + row0 + lr] : 0.f;
-                Cn[g][r] = -(c * (sq3(p.x, p.y, p.z) - f));
-                S[g][r] = 0.f;
-            }
-        // This wave takes tiles t_begin + w + k W, k = 0 .. cnt-1: the first
-        // cnt % 3 one by one, the rest in groups of three with no branch inside a
-        // group, so every key operand is loaded two tiles ahead of its use (the
-        // scheduling barriers keep each load in place; indices are clamped to the
-        // wave's last tile so that loads past the end stay inside the pair).
-        // Three register sets take turns, so no operand is copied.
-        const int first = t_begin + w;
-        const int cnt = first < t_end ? (t_end - first + W - 1) / W : 0;
-        const int last = first + (cnt > 0 ? cnt - 1 : 0) * W;
-        // key operands through a buffer resource: the tile offset rides in an
-        // SGPR (soffset), the lane's offset is a constant VGPR, so no vector
-        // address arithmetic per tile
-        const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)kb, (short)0, nk_pad * kRec * (int)sizeof(uint16_t), 0x00020000);
-        const int voff = lane_off * (int)sizeof(uint16_t);
-        auto key = [&](int k) {
-            const int t = min(first + k * W, last);
-            return __builtin_bit_cast(
-                bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                            krs, voff, t * (kTile * kRec * (int)sizeof(uint16_t)), 0));
-        };
-        auto tile = [&](const bf16x8 &Bt) {
-#pragma unroll
-            for (int g = 0; g < kGroups; ++g) {
-                const f32x4 D = mfma4(A[g], Bt, Cn[g]);
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    S[g][r] += ex2(D[r]);
-            }
-        };
-        int k = 0;
-        for (; k < cnt % 3; ++k)
-            tile(key(k));
-        if (k < cnt) {
-            bf16x8 Ra = key(k), Rb = key(k + 1), Rc;
-            for (; k < cnt; k += 3) {
-                Rc = key(k + 2);
-                __builtin_amdgcn_sched_barrier(0);
-                tile(Ra);
-                __builtin_amdgcn_sched_barrier(0);
-                Ra = key(k + 3);
-                __builtin_amdgcn_sched_barrier(0);
-                tile(Rb);
-                __builtin_amdgcn_sched_barrier(0);
-                Rb = key(k + 4);
-                __builtin_amdgcn_sched_barrier(0);
-                tile(Rc);
-                __builtin_amdgcn_sched_barrier(0);
-            }
+            for (int r = 0; r < 4; ++r)
+                S[g][r] += ex2(D[r]);
         }
-        // every partial of a row has the same shift: the merge is a sum
-#pragma unroll
-        for (int g = 0; g < kGroups; ++g)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float Sr = row16_sum(S[g][r]);
-                if (c16 == 0)
-                    red[w][16 * g + 4 * kq + r] = make_float2(-Cn[g][r], Sr);
-            }
-        if (threadIdx.x == 0)
-            redo = 0;
-        __syncthreads();
-        float Ssum = 0.f;
-        const float M = red[0][lane].x;
-        if (w == 0) {
-#pragma unroll
-            for (int v = 0; v < W; ++v)
-                Ssum += red[v][lane].y;
-            if (row0 + lane < nq && !(Ssum >= kSumLo && Ssum <= kSumHi))
-                redo = 1;   // benign race: every writer stores 1 (padding rows never do)
+    };
+    int k = 0;
+    for (; k < cnt % 3; ++k)
+        tile(key(k));
+    if (k < cnt) {
+        bf16x8 Ra = key(k), Rb = key(k + 1), Rc;
+        for (; k < cnt; k += 3) {
+            Rc = key(k + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            tile(Ra);
+            __builtin_amdgcn_sched_barrier(0);
+            Ra = key(k + 3);
+            __builtin_amdgcn_sched_barrier(0);
+            tile(Rb);
+            __builtin_amdgcn_sched_barrier(0);
+            Rb = key(k + 4);
+            __builtin_amdgcn_sched_barrier(0);
+            tile(Rc);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        __syncthreads();
-        if (!redo) {
-            const int row = row0 + lane;
-            if (w == 0 && row < nq)
-                finish_row(qpts, qkrec, qpot, ql2w, (size_t)b * nq_pad + row, (size_t)b * nq + row,
-                           qpts[(size_t)b * nq_pad + row], M, Ssum, eps_ln2, c_next);
-            return;
-        }
-        __syncthreads();   // red is reused below
     }
+}
 
-    // ---- lazy-maximum pass
+// Lazy-maximum stream of one wave: key tiles t0, t0 + W, ... below t_end into
+// the (M, S) states, M carried as -Cn (+1e30 marks a state that has seen no key
+// yet).  The key operand of the next tile is loaded one tile ahead; the clamped
+// index keeps that load inside the pair's keys on the last tile.
+template <int W>
+__device__ __forceinline__ void lazy_stream(const bf16x8 (&A)[kGroups], f32x4 (&Cn)[kGroups],
+                                            f32x4 (&S)[kGroups], const uint16_t *kb, int lane_off,
+                                            int t0, int t_end, int n_tiles)
+{
 #pragma unroll
     for (int g = 0; g < kGroups; ++g) {
         Cn[g] = f32x4{-kNeg, -kNeg, -kNeg, -kNeg};
         S[g] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    int t = t_begin + w;
-    // the key operand of the next tile is loaded one tile ahead; the clamped
-    // index keeps that load inside the pair's keys on the last tile
+    int t = t0;
     bf16x8 Bv = load_bf16x8(kb + (size_t)min(t, n_tiles - 1) * kTile * kRec + lane_off);
     for (; t < t_end; t += W) {
         const int tn = min(t + W, t_end - 1);
@@ -609,6 +547,98 @@ __global__ __launch_bounds__(W *kWave) void lse3m_kernel(
                 S[g][r] += ex2(D[g][r]);
         Bv = Bn;
     }
+}
+
+// Query operands of a wave's 64 rows and their shifts M_i = c (||x_i||^2 - f_i),
+// carried as -M in the accumulator input.
+__device__ __forceinline__ void load_rows(bf16x8 (&A)[kGroups], f32x4 (&Cn)[kGroups],
+                                          f32x4 (&S)[kGroups], const float4 *qrow,
+                                          const uint16_t *qrec_rows, const float *qpot_b, int nq,
+                                          int row0, int lane_off, int kq, float c)
+{
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g)
+        A[g] = load_bf16x8(qrec_rows + (size_t)(16 * g) * kRec + lane_off);
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int lr = 16 * g + 4 * kq + r;
+            const float4 p = qrow[lr];
+            const float f = row0 + lr < nq ? qpot_b[row0 + lr] : 0.f;
+            Cn[g][r] = -(c * (sq3(p.x, p.y, p.z) - f));
+            S[g][r] = 0.f;
+        }
+}
+
+template <int W>
+__global__ __launch_bounds__(W *kWave) void lse3m_kernel(
+    float4 *__restrict__ qpts, uint16_t *__restrict__ qkrec, const uint16_t *__restrict__ qrec,
+    const uint16_t *__restrict__ krec, float *__restrict__ qpot, const float *__restrict__ ql2w,
+    float2 *__restrict__ part, int nq, int nq_pad, int nk_pad, int tiles_per_split, float two_c,
+    double eps_ln2, double c_next)
+{
+    __shared__ float2 red[W][kWave];
+    __shared__ int redo;
+    const int b = blockIdx.z;
+    const int split = blockIdx.y;
+    const int lane = lane_id();
+    const int w = wave_id_uniform();
+    const int row0 = blockIdx.x * kWave;
+    const int kq = lane >> 4;      // operand k index this lane supplies / row quad it receives
+    const int c16 = lane & 15;     // operand row (A) or column (B) within a 16-block
+
+    const float4 *qrow = qpts + (size_t)b * nq_pad + row0;
+    const int lane_off = c16 * kRec + 8 * kq;   // this lane's 8 slots of a record
+    const uint16_t *qrec_rows = qrec + ((size_t)b * nq_pad + row0) * kRec;
+    const uint16_t *kb = krec + (size_t)b * nk_pad * kRec;
+    const int n_tiles = nk_pad / kTile;
+    const int t_begin = split * tiles_per_split;
+    const int t_end = min(t_begin + tiles_per_split, n_tiles);
+    bf16x8 A[kGroups];
+    f32x4 Cn[kGroups], S[kGroups];
+    load_rows(A, Cn, S, qrow, qrec_rows, qpot + (size_t)b * nq, nq, row0, lane_off, kq,
+              0.5f * two_c);
+
+    if (part == nullptr) {
+        // ---- shifted pass: this wave takes tiles t_begin + w + k W
+        const int first = t_begin + w;
+        shifted_stream<W>(A, Cn, S, kb, nk_pad, lane_off, first,
+                          first < t_end ? (t_end - first + W - 1) / W : 0);
+        // every partial of a row has the same shift: the merge is a sum
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float Sr = row16_sum(S[g][r]);
+                if (c16 == 0)
+                    red[w][16 * g + 4 * kq + r] = make_float2(-Cn[g][r], Sr);
+            }
+        if (threadIdx.x == 0)
+            redo = 0;
+        __syncthreads();
+        float Ssum = 0.f;
+        const float M = red[0][lane].x;
+        if (w == 0) {
+#pragma unroll
+            for (int v = 0; v < W; ++v)
+                Ssum += red[v][lane].y;
+            if (row0 + lane < nq && !(Ssum >= kSumLo && Ssum <= kSumHi))
+                redo = 1;   // benign race: every writer stores 1 (padding rows never do)
+        }
+        __syncthreads();
+        if (!redo) {
+            const int row = row0 + lane;
+            if (w == 0 && row < nq)
+                finish_row(qpts, qkrec, qpot, ql2w, (size_t)b * nq_pad + row, (size_t)b * nq + row,
+                           qpts[(size_t)b * nq_pad + row], M, Ssum, eps_ln2, c_next);
+            return;
+        }
+        __syncthreads();   // red is reused below
+    }
+
+    // ---- lazy-maximum pass
+    lazy_stream<W>(A, Cn, S, kb, lane_off, t_begin + w, t_end, n_tiles);
 
     // merge the 16 column partials of every row (lanes sharing kq), then the waves
 #pragma unroll
@@ -638,6 +668,89 @@ __global__ __launch_bounds__(W *kWave) void lse3m_kernel(
     if (row < nq)
         finish_row(qpts, qkrec, qpot, ql2w, (size_t)b * nq_pad + row, (size_t)b * nq + row,
                    qpts[(size_t)b * nq_pad + row], M, Sf, eps_ln2, c_next);
+}
+
+// ---------------------------------------------------------------------------
+// Persistent pass per pair, for batches of at least as many pairs as the chip
+// has compute units: one work-group of kPairWaves waves owns one pair and runs
+// every iteration of a stage in one launch.  Each wave takes whole 64-row
+// blocks (all keys, the shifted stream with the lazy-maximum stream as its
+// fallback when a row's sum leaves the range), finishes its rows, and the
+// work-group synchronises between the f- and the g-update.  Everything a pass
+// reads from the other side was written by this work-group, so the barrier is
+// the only synchronisation; the per-launch cost of the other path (a launch
+// and the fill and drain of the chip for every half-iteration) is paid once
+// per stage.  The arithmetic per row is that of lse3m_kernel<1>.
+constexpr int kPairWaves = 16;
+
+// One wave: rows row0 .. row0 + 63 of pair b on side q against all keys of side k.
+__device__ __forceinline__ void wave_rows(const Side3 &q, const Side3 &k, int b, int row0,
+                                          float two_c, double eps_ln2, double c_next,
+                                          float2 *red)
+{
+    const int lane = lane_id();
+    const int kq = lane >> 4, c16 = lane & 15;
+    const int lane_off = c16 * kRec + 8 * kq;
+    const float4 *qrow = q.pts + (size_t)b * q.n_pad + row0;
+    const uint16_t *qrec_rows = q.qrec + ((size_t)b * q.n_pad + row0) * kRec;
+    const uint16_t *kb = k.krec + (size_t)b * k.n_pad * kRec;
+    const int n_tiles = k.n_pad / kTile;
+    bf16x8 A[kGroups];
+    f32x4 Cn[kGroups], S[kGroups];
+    load_rows(A, Cn, S, qrow, qrec_rows, q.pot + (size_t)b * q.n, q.n, row0, lane_off, kq,
+              0.5f * two_c);
+    shifted_stream<1>(A, Cn, S, kb, k.n_pad, lane_off, 0, n_tiles);
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float Sr = row16_sum(S[g][r]);
+            if (c16 == 0)
+                red[16 * g + 4 * kq + r] = make_float2(-Cn[g][r], Sr);
+        }
+    __builtin_amdgcn_wave_barrier();
+    float M = red[lane].x, Sf = red[lane].y;
+    const int row = row0 + lane;
+    const bool bad = row < q.n && !(Sf >= kSumLo && Sf <= kSumHi);
+    if (__ballot(bad) != 0) {   // the whole wave: it owns every row of the block
+        lazy_stream<1>(A, Cn, S, kb, lane_off, 0, n_tiles, n_tiles);
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float Mr = -Cn[g][r], Sr = S[g][r];
+                row16_merge(Mr, Sr);
+                if (c16 == 0)
+                    red[16 * g + 4 * kq + r] = make_float2(Mr, Sr);
+            }
+        __builtin_amdgcn_wave_barrier();
+        M = red[lane].x;
+        Sf = red[lane].y;
+    }
+    if (row < q.n)
+        finish_row(q.pts, q.krec, q.pot, q.l2w, (size_t)b * q.n_pad + row, (size_t)b * q.n + row,
+                   q.pts[(size_t)b * q.n_pad + row], M, Sf, eps_ln2, c_next);
+    __builtin_amdgcn_wave_barrier();   // red is reused by the next block
+}
+
+__global__ __launch_bounds__(kPairWaves *kWave) void lse3p_kernel(Side3 x, Side3 y, int iters,
+                                                                  float two_c, double eps_ln2,
+                                                                  double c_next_last)
+{
+    __shared__ float2 red[kPairWaves][kWave];
+    const int b = blockIdx.x;
+    const int w = wave_id_uniform();
+    const double c_same = 0.5 * (double)two_c;
+    for (int it = 0; it < iters; ++it) {
+        for (int rb = w; rb < x.n_pad / kWave; rb += kPairWaves)
+            wave_rows(x, y, b, rb * kWave, two_c, eps_ln2, c_same, red[w]);
+        __syncthreads();   // f and the X-side biases are complete
+        const double cn = it + 1 < iters ? c_same : c_next_last;
+        for (int rb = w; rb < y.n_pad / kWave; rb += kPairWaves)
+            wave_rows(y, x, b, rb * kWave, two_c, eps_ln2, cn, red[w]);
+        __syncthreads();   // g and the Y-side biases are complete
+    }
 }
 
 __global__ void lse3_finalize(float4 *__restrict__ qpts, uint16_t *__restrict__ qkrec,
@@ -738,6 +851,24 @@ hipError_t launch_qrec3(Side3 s, int B, float eps, hipStream_t st)
     dim3 grid(ceil_div(s.n_pad, 256), B);
     hipLaunchKernelGGL(qrec3_kernel, grid, dim3(256), 0, st, (const float4 *)s.pts, s.n_pad,
                        2.0f * scale_of(eps), s.qrec);
+    return hipGetLastError();
+}
+
+bool lse3_pairwise(int B, int n_pad, int m_pad)
+{
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return false;
+    return B >= cus && n_pad <= kPairMaxPoints && m_pad <= kPairMaxPoints;
+}
+
+hipError_t launch_lse3_pairwise(Side3 x, Side3 y, int B, float eps, int iters, float eps_next,
+                                hipStream_t st)
+{
+    const float c = scale_of(eps);
+    hipLaunchKernelGGL(lse3p_kernel, dim3(B), dim3(kPairWaves * kWave), 0, st, x, y, iters,
+                       2.0f * c, 1.0 / (double)c, (double)scale_of(eps_next));
     return hipGetLastError();
 }
 

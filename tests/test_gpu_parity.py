@@ -160,6 +160,32 @@ def test_coincident_clouds_closed_form():
     np.testing.assert_allclose(host(dX)[0], np.broadcast_to(ref, (n, 3)), rtol=1e-4)
 
 
+@pytest.mark.parametrize("scores", ["mfma", "valu"])
+def test_batch_of_many_pairs(scores):
+    # at least as many pairs as compute units: the matrix-core path runs each
+    # stage per pair in one launch (several 64-row blocks per side, ragged
+    # sizes, zero weights, two stages); the vector path is the usual one
+    c = workloads.random_case(503, 260, 300, 200, 3, weights="dirichlet", zero_weights=2)
+    check_potentials(c, [0.2, 0.03], [4, 12], valu_scores=scores == "valu")
+
+
+def test_batch_of_many_pairs_from_a_stale_start():
+    # warm start from potentials far from the solution: every row block of the
+    # per-pair launch takes the lazy-maximum stream on its first pass
+    c = workloads.random_case(504, 256, 130, 140, 3, weights="uniform")
+    X, Y = points(c)
+    eps = 0.02
+    f0 = np.full((256, 130), 40.0, dtype=np.float32)
+    g0 = np.full((256, 140), -35.0, dtype=np.float32)
+    f, g, _ = sk.potentials(X, Y, dev(c["a"]), dev(c["b"]), eps=[eps], iters=[6],
+                            f0=dev(f0), g0=dev(g0))
+    fo, go = oracle.potentials(c["X"], c["Y"], c["a"], c["b"], eps=np.float32([eps]), iters=[6],
+                               f0=f0.astype(np.float64), g0=g0.astype(np.float64))
+    for p in (0, 77, 255):
+        assert rel_inf(host(f)[p], fo[p], eps) <= 1e-4
+        assert rel_inf(host(g)[p], go[p], eps) <= 1e-4
+
+
 def test_schedule_with_empty_stages_and_zero_iterations():
     c = workloads.random_case(5, 1, 90, 70, 3, weights="dirichlet")
     check_potentials(c, [0.5, 0.2, 0.05], [0, 6, 8])
