@@ -153,7 +153,7 @@ def main():
 
     sparse = w["threshold"] is not None
     with_cost_default = not sparse
-    coo = loss_out = None
+    coo = loss_out = nnz_dev = None
     if sparse:
         # size the plan once (untimed); the timed steps reuse the buffers
         sk.potentials(X, Y, a, b, eps=eps, iters=iters, out=(f, g, None), cost=False,
@@ -167,14 +167,16 @@ def main():
         coo_ws = torch.empty(sk.workspace_bytes(sk.SK_OP_PLAN_COO, B, n, m, d, dt),
                              dtype=torch.uint8, device=dev)
         loss_out = (torch.empty(B, device=dev), torch.empty(B, n, d, device=dev))
+        nnz_dev = torch.empty(1, dtype=torch.int64, device=dev)
 
     def step(it=iters, with_cost=with_cost_default):
         sk.potentials(X, Y, a, b, eps=eps, iters=it, out=(f, g, cost if with_cost else None),
                       cost=with_cost, workspace=ws, valu_scores=args.valu_scores)
         if sparse:
-            # the loss and dL/dX are accumulated while the plan is emitted
-            sk.plan_coo(X, Y, a, b, f, g, eps[-1], w["threshold"], workspace=coo_ws, out=coo,
-                        loss_out=loss_out)
+            # the loss and dL/dX are accumulated while the plan is emitted; no host
+            # wait inside the step (the count is checked against the capacity after)
+            sk.plan_coo_async(X, Y, a, b, f, g, eps[-1], w["threshold"], coo, loss_out=loss_out,
+                              workspace=coo_ws, nnz=nnz_dev)
 
     def timed(fn, reps):
         torch.cuda.synchronize()
@@ -194,6 +196,7 @@ def main():
     wall = time.perf_counter() - t0
     assert torch.isfinite(f).all() and torch.isfinite(g).all()
     assert sparse or torch.isfinite(cost).all()
+    assert not sparse or int(nnz_dev) <= coo[0].numel(), "plan outgrew its buffers"
 
     # the half-iteration kernel's launch time: the same step with every stage's
     # iteration count halved (pack and cost pass unchanged), differenced

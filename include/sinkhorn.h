@@ -31,7 +31,8 @@
  *     thread-local error message.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
  *     and returns without waiting, except sinkhorn_plan_coo and
- *     sinkhorn_coo_normalize, which read counts back (see there).
+ *     sinkhorn_coo_normalize, which read counts back (see there;
+ *     sinkhorn_plan_coo_async is the plan without the wait).
  *     Calls are reentrant; two calls that share a workspace must not overlap.
  *   - Arguments are checked before anything is launched.  On an error no
  *     output buffer is written and the return value says why; the message
@@ -156,6 +157,24 @@ int sinkhorn_plan_coo(const void *X, const void *Y, int dtype,
                       int64_t capacity, int32_t *rows, int32_t *cols, float *vals,
                       int64_t *pair_offsets, float *loss, float *dX, int64_t *nnz_total,
                       void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * The same plan (and optional loss / dX) without waiting on `stream`, for
+ * callers that keep the host out of the loop (graph capture, training loops).
+ * capacity >= 1 with rows/cols/vals of that many entries.  *nnz_device (DEVICE
+ * int64) receives the number of kept entries and pair_offsets is written as
+ * above.  If the count exceeds capacity nothing else is written: rows, cols,
+ * vals, loss and dX keep their contents, so the caller must check
+ * *nnz_device <= capacity before reading them (and call again with more room).
+ * Launches kernels only (no copy, wait or memset).
+ */
+int sinkhorn_plan_coo_async(const void *X, const void *Y, int dtype,
+                            const float *a, const float *b,
+                            int B, int n, int m, int d, float eps,
+                            const float *f, const float *g, float rel_threshold,
+                            int64_t capacity, int32_t *rows, int32_t *cols, float *vals,
+                            int64_t *pair_offsets, float *loss, float *dX, int64_t *nnz_device,
+                            void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Loss and gradient on the stored support [AP Abstract] (plan held fixed):

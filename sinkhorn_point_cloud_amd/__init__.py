@@ -34,7 +34,7 @@ SK_VALU_SCORES = 2
 EXPORTS = ("sinkhorn_workspace_bytes", "sinkhorn_potentials", "sinkhorn_plan_coo",
            "sinkhorn_loss_grad", "sinkhorn_dense_grad", "sinkhorn_hvp",
            "sinkhorn_coo_workspace_bytes",
-           "sinkhorn_coo_normalize", "sinkhorn_normalize",
+           "sinkhorn_coo_normalize", "sinkhorn_normalize", "sinkhorn_plan_coo_async",
            "sinkhorn_normalize_backward", "sinkhorn_status_string", "sinkhorn_last_error")
 
 
@@ -69,6 +69,9 @@ def load_library():
     lib.sinkhorn_plan_coo.argtypes = [P, P, I, P, P, I, I, I, I, F, P, P, F, L, P, P, P, P, P,
                                       P, P, P, Z, P]
     lib.sinkhorn_plan_coo.restype = I
+    lib.sinkhorn_plan_coo_async.argtypes = [P, P, I, P, P, I, I, I, I, F, P, P, F, L, P, P, P, P,
+                                            P, P, P, P, Z, P]
+    lib.sinkhorn_plan_coo_async.restype = I
     lib.sinkhorn_loss_grad.argtypes = [P, P, I, I, I, I, I, P, P, P, P, P, P, P, Z, P]
     lib.sinkhorn_loss_grad.restype = I
     lib.sinkhorn_dense_grad.argtypes = [P, P, I, P, P, I, I, I, I, F, P, P, P, P, P, P, P, Z, P]
@@ -238,6 +241,34 @@ def plan_coo(X, Y, a, b, f, g, eps: float, rel_threshold: float = 1e-8, capacity
     _check(rc)
     k = int(nnz.value)
     return rows[:k], cols[:k], vals[:k], offs
+
+
+def plan_coo_async(X, Y, a, b, f, g, eps: float, rel_threshold: float, out, loss_out=None,
+                   workspace=None, nnz=None):
+    """The thresholded plan into ``out`` = (rows, cols, vals, pair_offsets) without
+    waiting on the stream (capturable).  Returns ``nnz`` (int64 [1] on the device): the
+    number of kept entries.  If it exceeds len(rows), only pair_offsets and nnz are
+    written, so check nnz <= len(rows) before using rows/cols/vals or ``loss_out``."""
+    lib = load_library()
+    X, Y, dt = _points(X, Y)
+    B, n, d = X.shape
+    m = Y.shape[1]
+    dev = X.device
+    a, b = _weights(a, B, n, dev), _weights(b, B, m, dev)
+    f = f.reshape(B, n).contiguous().float()
+    g = g.reshape(B, m).contiguous().float()
+    ws = _workspace(SK_OP_PLAN_COO, B, n, m, d, dt, dev, workspace)
+    loss, dX = loss_out if loss_out is not None else (None, None)
+    rows, cols, vals, offs = out
+    if nnz is None:
+        nnz = torch.empty(1, dtype=torch.int64, device=dev)
+    rc = lib.sinkhorn_plan_coo_async(_ptr(X), _ptr(Y), dt, _ptr(a), _ptr(b), B, n, m, d,
+                                     float(eps), _ptr(f), _ptr(g), float(rel_threshold),
+                                     rows.numel(), _ptr(rows), _ptr(cols), _ptr(vals), _ptr(offs),
+                                     _ptr(loss), _ptr(dX), _ptr(nnz), _ptr(ws), ws.numel(),
+                                     _stream())
+    _check(rc)
+    return nnz
 
 
 def loss_grad(X, Y, rows, cols, vals, pair_offsets, grad: bool = True, workspace=None,

@@ -467,7 +467,50 @@ int sinkhorn_plan_coo(const void *X, const void *Y, int dtype, const float *a, c
     // row_max is free once the threshold is known: it takes the per-row loss
     if ((total > 0 || loss || dX) &&
         (e = launch_plan_emit(p, w.pair_thr, w.row_off, w.row_count, rows, cols, vals, w.row_max,
-                              loss, dX, st)))
+                              loss, dX, nullptr, 0, st)))
+        return hip_fail(e, "plan emit");
+    return SK_OK;
+}
+
+int sinkhorn_plan_coo_async(const void *X, const void *Y, int dtype, const float *a,
+                            const float *b, int B, int n, int m, int d, float eps, const float *f,
+                            const float *g, float rel_threshold, int64_t capacity, int32_t *rows,
+                            int32_t *cols, float *vals, int64_t *pair_offsets, float *loss,
+                            float *dX, int64_t *nnz_device, void *ws, size_t ws_bytes,
+                            void *stream)
+{
+    g_err[0] = '\0';
+    int rc = check_common(X, Y, dtype, B, n, m, d);
+    if (rc)
+        return rc;
+    if (!f || !g || !pair_offsets || !nnz_device)
+        return fail(SK_ERR_INVALID_ARG, "f, g, pair_offsets and nnz_device must be non-NULL");
+    if (!(eps > 0.f) || !isfinite(eps))
+        return fail(SK_ERR_INVALID_ARG, "eps=%g must be finite and > 0", eps);
+    if (!(rel_threshold > 0.f && rel_threshold <= 1.f))
+        return fail(SK_ERR_INVALID_ARG, "rel_threshold=%g must be in (0, 1]", rel_threshold);
+    if (capacity < 1 || !rows || !cols || !vals)
+        return fail(SK_ERR_INVALID_ARG, "capacity=%lld must be >= 1 with rows, cols and vals",
+                    (long long)capacity);
+    rc = check_ws(ws, ws_bytes, ws_size(SK_OP_PLAN_COO, B, n, m, d, dtype));
+    if (rc)
+        return rc;
+
+    hipStream_t st = (hipStream_t)stream;
+    Carve c{(char *)ws};
+    CooWs w = carve_coo(c, B, n, m, d);
+    PlanArgs p{X, Y, dtype, d, B, n, m, f, g, w.la, w.lb, 1.0 / (double)eps, w.kd};
+    hipError_t e;
+    if ((e = launch_log_weights(a, B, n, w.la, st)) || (e = launch_log_weights(b, B, m, w.lb, st)) ||
+        (w.kd && (e = launch_keys_d3(Y, dtype, g, B, m, w.kd, st))))
+        return hip_fail(e, "log weights");
+    if ((e = launch_plan_max(p, w.row_max, w.pair_thr, log((double)rel_threshold), st)) ||
+        (e = launch_plan_count(p, w.pair_thr, w.row_count, st)) ||
+        (e = launch_plan_scan(w.row_count, B, n, w.row_off, pair_offsets, w.pair_tot, st)) ||
+        (e = launch_copy_total(pair_offsets + B, nnz_device, st)))
+        return hip_fail(e, "plan count");
+    if ((e = launch_plan_emit(p, w.pair_thr, w.row_off, w.row_count, rows, cols, vals, w.row_max,
+                              loss, dX, pair_offsets + B, capacity, st)))
         return hip_fail(e, "plan emit");
     return SK_OK;
 }

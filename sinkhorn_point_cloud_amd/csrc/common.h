@@ -214,10 +214,14 @@ hipError_t launch_plan_scan(const int32_t *row_count, int B, int n, int64_t *row
 // Emission of the counted entries; with loss / dX (either may be NULL) also the
 // loss per pair and its gradient in X on the emitted support (row_loss: [B][n]
 // scratch, needed with loss).
+// gate != NULL: every kernel first reads *gate (the plan's entry count, on the
+// device) and writes nothing if it exceeds gate_cap.
 hipError_t launch_plan_emit(const PlanArgs &p, const double *pair_thr, const int64_t *row_off,
                             const int32_t *row_count, int32_t *rows, int32_t *cols,
                             float *vals, double *row_loss, float *loss, float *dX,
-                            hipStream_t st);
+                            const int64_t *gate, int64_t gate_cap, hipStream_t st);
+// *dst = *src on the device (one int64)
+hipError_t launch_copy_total(const int64_t *src, int64_t *dst, hipStream_t st);
 // Dense gradient 2 sum_j P_ij (x_i - y_j) and barycentric projection
 // sum_j P_ij y_j / sum_j P_ij of every row of p.X (either output may be NULL),
 // log P in fp64.  only != NULL: just the 64-row blocks flagged there.

@@ -549,16 +549,21 @@ __device__ __forceinline__ void lazy_stream(const bf16x8 (&A)[kGroups], f32x4 (&
     }
 }
 
-// Query operands of a wave's 64 rows and their shifts M_i = c (||x_i||^2 - f_i),
-// carried as -M in the accumulator input.
-__device__ __forceinline__ void load_rows(bf16x8 (&A)[kGroups], f32x4 (&Cn)[kGroups],
-                                          f32x4 (&S)[kGroups], const float4 *qrow,
-                                          const uint16_t *qrec_rows, const float *qpot_b, int nq,
-                                          int row0, int lane_off, int kq, float c)
+// Query operands of a wave's 64 rows.
+__device__ __forceinline__ void load_rows(bf16x8 (&A)[kGroups], const uint16_t *qrec_rows,
+                                          int lane_off)
 {
 #pragma unroll
     for (int g = 0; g < kGroups; ++g)
         A[g] = load_bf16x8(qrec_rows + (size_t)(16 * g) * kRec + lane_off);
+}
+
+// Their shifts M_i = c (||x_i||^2 - f_i), carried as -M in the accumulator
+// input, and empty sums.
+__device__ __forceinline__ void load_shifts(f32x4 (&Cn)[kGroups], f32x4 (&S)[kGroups],
+                                            const float4 *qrow, const float *qpot_b, int nq,
+                                            int row0, int kq, float c)
+{
 #pragma unroll
     for (int g = 0; g < kGroups; ++g)
 #pragma unroll
@@ -597,11 +602,11 @@ __global__ __launch_bounds__(W *kWave) void lse3m_kernel(
     const int t_end = min(t_begin + tiles_per_split, n_tiles);
     bf16x8 A[kGroups];
     f32x4 Cn[kGroups], S[kGroups];
-    load_rows(A, Cn, S, qrow, qrec_rows, qpot + (size_t)b * nq, nq, row0, lane_off, kq,
-              0.5f * two_c);
+    load_rows(A, qrec_rows, lane_off);
 
     if (part == nullptr) {
         // ---- shifted pass: this wave takes tiles t_begin + w + k W
+        load_shifts(Cn, S, qrow, qpot + (size_t)b * nq, nq, row0, kq, 0.5f * two_c);
         const int first = t_begin + w;
         shifted_stream<W>(A, Cn, S, kb, nk_pad, lane_off, first,
                           first < t_end ? (t_end - first + W - 1) / W : 0);
@@ -697,8 +702,8 @@ __device__ __forceinline__ void wave_rows(const Side3 &q, const Side3 &k, int b,
     const int n_tiles = k.n_pad / kTile;
     bf16x8 A[kGroups];
     f32x4 Cn[kGroups], S[kGroups];
-    load_rows(A, Cn, S, qrow, qrec_rows, q.pot + (size_t)b * q.n, q.n, row0, lane_off, kq,
-              0.5f * two_c);
+    load_rows(A, qrec_rows, lane_off);
+    load_shifts(Cn, S, qrow, q.pot + (size_t)b * q.n, q.n, row0, kq, 0.5f * two_c);
     shifted_stream<1>(A, Cn, S, kb, k.n_pad, lane_off, 0, n_tiles);
 #pragma unroll
     for (int g = 0; g < kGroups; ++g)

@@ -179,12 +179,17 @@ __global__ __launch_bounds__(kTileWaves *kWave) void tile_pass(
 
 // Per-pair reduction of row values in a fixed order (deterministic).
 // mode 0: sum -> float out[b];  mode 1: max + add -> double out[b]
+// gate != nullptr: write nothing unless *gate <= gate_cap (a plan that fit)
 template <int MODE>
 __global__ __launch_bounds__(256) void pair_reduce(const double *__restrict__ rowv, int n,
                                                    float *__restrict__ outf,
-                                                   double *__restrict__ outd, double add)
+                                                   double *__restrict__ outd, double add,
+                                                   const int64_t *__restrict__ gate,
+                                                   int64_t gate_cap)
 {
     __shared__ double sm[256];
+    if (gate && *gate > gate_cap)
+        return;
     const int b = blockIdx.x;
     double acc = MODE == 0 ? 0.0 : -INFINITY;
     for (int i = threadIdx.x; i < n; i += 256) {
@@ -291,8 +296,11 @@ template <typename T, int DP, bool LG>
 __global__ __launch_bounds__(kRowsPerGroup *kWave) void emit_pass(
     PlanArgs p, const double *__restrict__ thr, const int64_t *__restrict__ row_off,
     const int32_t *__restrict__ row_cnt, int32_t *__restrict__ rows, int32_t *__restrict__ cols,
-    float *__restrict__ vals, double *__restrict__ row_loss, float *__restrict__ dX)
+    float *__restrict__ vals, double *__restrict__ row_loss, float *__restrict__ dX,
+    const int64_t *__restrict__ gate, int64_t gate_cap)
 {
+    if (gate && *gate > gate_cap)
+        return;   // the plan does not fit: nothing is written
     const int b = blockIdx.y;
     const int i = blockIdx.x * kRowsPerGroup + wave_id_uniform();
     if (i >= p.n)
@@ -364,8 +372,11 @@ template <typename T, int DP, bool LG>
 __global__ __launch_bounds__(kEmitWaves *kWave) void emit_staged(
     PlanArgs p, const double *__restrict__ thr, const int64_t *__restrict__ row_off,
     const int32_t *__restrict__ row_cnt, int32_t *__restrict__ rows, int32_t *__restrict__ cols,
-    float *__restrict__ vals, double *__restrict__ row_loss, float *__restrict__ dX)
+    float *__restrict__ vals, double *__restrict__ row_loss, float *__restrict__ dX,
+    const int64_t *__restrict__ gate, int64_t gate_cap)
 {
+    if (gate && *gate > gate_cap)
+        return;   // the plan does not fit: nothing is written
     static_assert(DP <= 4, "staged emit holds at most 4 components per column");
     constexpr int kRowsPerWave = kEmitRows / kEmitWaves;
     __shared__ double ys[DP][kEmitChunk];
@@ -546,14 +557,14 @@ hipError_t launch_cost(const PlanArgs &p, double *row_part, float *cost, hipStre
 {
     tile_dispatch<0>(p, nullptr, row_part, nullptr, nullptr, nullptr, st);
     hipLaunchKernelGGL(pair_reduce<0>, dim3(p.B), dim3(256), 0, st, (const double *)row_part,
-                       p.n, cost, (double *)nullptr, 0.0);
+                       p.n, cost, (double *)nullptr, 0.0, (const int64_t *)nullptr, (int64_t)0);
     return hipGetLastError();
 }
 
 hipError_t launch_row_sums(const double *row_part, int B, int n, float *out, hipStream_t st)
 {
     hipLaunchKernelGGL(pair_reduce<0>, dim3(B), dim3(256), 0, st, row_part, n, out,
-                       (double *)nullptr, 0.0);
+                       (double *)nullptr, 0.0, (const int64_t *)nullptr, (int64_t)0);
     return hipGetLastError();
 }
 
@@ -562,7 +573,8 @@ hipError_t launch_plan_max(const PlanArgs &p, double *row_max, double *pair_thr,
 {
     tile_dispatch<1>(p, nullptr, row_max, nullptr, nullptr, nullptr, st);
     hipLaunchKernelGGL(pair_reduce<1>, dim3(p.B), dim3(256), 0, st, (const double *)row_max,
-                       p.n, (float *)nullptr, pair_thr, log_rel_thr);
+                       p.n, (float *)nullptr, pair_thr, log_rel_thr, (const int64_t *)nullptr,
+                       (int64_t)0);
     return hipGetLastError();
 }
 
@@ -586,7 +598,8 @@ hipError_t launch_plan_scan(const int32_t *row_count, int B, int n, int64_t *row
 
 hipError_t launch_plan_emit(const PlanArgs &p, const double *pair_thr, const int64_t *row_off,
                             const int32_t *row_count, int32_t *rows, int32_t *cols,
-                            float *vals, double *row_loss, float *loss, float *dX, hipStream_t st)
+                            float *vals, double *row_loss, float *loss, float *dX,
+                            const int64_t *gate, int64_t gate_cap, hipStream_t st)
 {
     const bool lg = loss || dX;
     double *rl = loss ? row_loss : nullptr;
@@ -595,10 +608,10 @@ hipError_t launch_plan_emit(const PlanArgs &p, const double *pair_thr, const int
         auto go = [&]<int DP, bool LG>() {
             if (p.dtype == 1)
                 hipLaunchKernelGGL((emit_staged<uint16_t, DP, LG>), grid, block, 0, st, p,
-                                   pair_thr, row_off, row_count, rows, cols, vals, rl, dX);
+                                   pair_thr, row_off, row_count, rows, cols, vals, rl, dX, gate, gate_cap);
             else
                 hipLaunchKernelGGL((emit_staged<float, DP, LG>), grid, block, 0, st, p, pair_thr,
-                                   row_off, row_count, rows, cols, vals, rl, dX);
+                                   row_off, row_count, rows, cols, vals, rl, dX, gate, gate_cap);
         };
         if (p.d == 3)
             lg ? go.template operator()<3, true>() : go.template operator()<3, false>();
@@ -609,10 +622,10 @@ hipError_t launch_plan_emit(const PlanArgs &p, const double *pair_thr, const int
         auto go = [&]<int DP, bool LG>() {
             if (p.dtype == 1)
                 hipLaunchKernelGGL((emit_pass<uint16_t, DP, LG>), grid, block, 0, st, p, pair_thr,
-                                   row_off, row_count, rows, cols, vals, rl, dX);
+                                   row_off, row_count, rows, cols, vals, rl, dX, gate, gate_cap);
             else
                 hipLaunchKernelGGL((emit_pass<float, DP, LG>), grid, block, 0, st, p, pair_thr,
-                                   row_off, row_count, rows, cols, vals, rl, dX);
+                                   row_off, row_count, rows, cols, vals, rl, dX, gate, gate_cap);
         };
         with_dp(p.d, [&]<int DP>() {
             lg ? go.template operator()<DP, true>() : go.template operator()<DP, false>();
@@ -620,7 +633,21 @@ hipError_t launch_plan_emit(const PlanArgs &p, const double *pair_thr, const int
     }
     if (loss)
         hipLaunchKernelGGL(pair_reduce<0>, dim3(p.B), dim3(256), 0, st, (const double *)row_loss,
-                           p.n, loss, (double *)nullptr, 0.0);
+                           p.n, loss, (double *)nullptr, 0.0, gate, gate_cap);
+    return hipGetLastError();
+}
+
+namespace {
+__global__ void copy_total(const int64_t *__restrict__ src, int64_t *__restrict__ dst)
+{
+    if (threadIdx.x == 0 && blockIdx.x == 0)
+        *dst = *src;
+}
+}  // namespace
+
+hipError_t launch_copy_total(const int64_t *src, int64_t *dst, hipStream_t st)
+{
+    hipLaunchKernelGGL(copy_total, dim3(1), dim3(64), 0, st, src, dst);
     return hipGetLastError();
 }
 

@@ -119,6 +119,18 @@ def _coo(lib, eps=0.1, thr=1e-8, capacity=10, rows=DUMMY, offs=DUMMY, nnz=True, 
     return rc, n_out.value
 
 
+def _coo_async(lib, eps=0.1, thr=1e-8, capacity=10, rows=DUMMY, nnz=DUMMY):
+    return lib.sinkhorn_plan_coo_async(DUMMY, DUMMY, 0, None, None, 1, 8, 9, 3, eps, DUMMY, DUMMY,
+                                       thr, capacity, rows, DUMMY, DUMMY, DUMMY, None, None, nnz,
+                                       DUMMY, 1 << 40, None)
+
+
+@pytest.mark.parametrize("kw", [dict(eps=0.0), dict(thr=2.0), dict(capacity=0),
+                                dict(capacity=-3), dict(rows=None), dict(nnz=None)])
+def test_plan_coo_async_rejects_bad_arguments(lib, kw):
+    assert _coo_async(lib, **kw) == sk.SK_ERR_INVALID_ARG, lib.sinkhorn_last_error()
+
+
 @pytest.mark.parametrize("kw", [dict(eps=0.0), dict(eps=-1.0), dict(thr=0.0), dict(thr=1.5),
                                 dict(capacity=-1), dict(rows=None), dict(offs=None),
                                 dict(nnz=False)])

@@ -936,3 +936,86 @@ def test_potentials_replay_from_a_captured_graph():
         torch.cuda.synchronize()
         for t, r in zip(out, ref):
             assert torch.equal(t, r), f"replay {rep}"
+
+
+def _plan_buffers(cap, B, n, dev_):
+    return ((torch.full((cap,), -5, dtype=torch.int32, device=dev_),
+             torch.full((cap,), -5, dtype=torch.int32, device=dev_),
+             torch.full((cap,), -5.0, dtype=torch.float32, device=dev_),
+             torch.full((B + 1,), -5, dtype=torch.int64, device=dev_)),
+            (torch.full((B,), -5.0, device=dev_), torch.full((B, n, 3), -5.0, device=dev_)))
+
+
+def test_plan_without_waiting_equals_the_waiting_plan():
+    c = workloads.random_case(63, 3, 400, 350, 3, weights="dirichlet")
+    X, Y = points(c)
+    a, b = dev(c["a"]), dev(c["b"])
+    eps = 0.02
+    f, g, _ = sk.potentials(X, Y, a, b, eps=[eps], iters=[15])
+    loss = torch.empty(3, device=X.device)
+    dX = torch.empty(3, 400, 3, device=X.device)
+    ref = sk.plan_coo(X, Y, a, b, f, g, eps, 1e-8, loss_out=(loss, dX))
+    total = int(ref[3][-1])
+    # room to spare: the same plan, loss and gradient, bit for bit
+    out, lo = _plan_buffers(total + 100, 3, 400, X.device)
+    nnz = sk.plan_coo_async(X, Y, a, b, f, g, eps, 1e-8, out, loss_out=lo)
+    torch.cuda.synchronize()
+    assert int(nnz) == total
+    for u, v in zip(out[:3], ref[:3]):
+        assert torch.equal(u[:total], v)
+    assert torch.equal(out[3], ref[3]) and torch.equal(lo[0], loss) and torch.equal(lo[1], dX)
+    # one entry short: the count and the offsets are written, nothing else
+    out, lo = _plan_buffers(total - 1, 3, 400, X.device)
+    nnz = sk.plan_coo_async(X, Y, a, b, f, g, eps, 1e-8, out, loss_out=lo)
+    torch.cuda.synchronize()
+    assert int(nnz) == total and torch.equal(out[3], ref[3])
+    for t in list(out[:3]) + list(lo):
+        assert bool((t == -5).all())
+
+
+def test_forward_and_gradient_replay_from_a_captured_graph():
+    # potentials, the sparse plan and its loss and gradient with no host wait:
+    # the whole step is captured once and replayed
+    c = workloads.random_case(64, 4, 300, 280, 3, weights="dirichlet")
+    X, Y = points(c)
+    a, b = dev(c["a"]), dev(c["b"])
+    B, n, m = 4, 300, 280
+    eps = 0.03
+    ws = torch.empty(sk.workspace_bytes(sk.SK_OP_POTENTIALS, B, n, m, 3, sk.SK_F32),
+                     dtype=torch.uint8, device=X.device)
+    cws = torch.empty(sk.workspace_bytes(sk.SK_OP_PLAN_COO, B, n, m, 3, sk.SK_F32),
+                      dtype=torch.uint8, device=X.device)
+    pot = (torch.empty(B, n, device=X.device), torch.empty(B, m, device=X.device), None)
+    out, lo = _plan_buffers(B * n * m, B, n, X.device)
+    nnz = torch.empty(1, dtype=torch.int64, device=X.device)
+
+    def step():
+        sk.potentials(X, Y, a, b, eps=[eps], iters=[12], cost=False, out=pot, workspace=ws)
+        sk.plan_coo_async(X, Y, a, b, pot[0], pot[1], eps, 1e-8, out, loss_out=lo,
+                          workspace=cws, nnz=nnz)
+
+    step()
+    torch.cuda.synchronize()
+    total = int(nnz)
+    assert total <= B * n * m
+
+    def results():   # the written part of every output
+        return list(pot[:2]) + [t[:total] for t in out[:3]] + [out[3]] + list(lo) + [nnz]
+
+    ref = [t.clone() for t in results()]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in list(pot[:2]) + list(lo):
+            t.fill_(float("nan"))
+        out[2].fill_(-1.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for t, r in zip(results(), ref):
+            assert torch.equal(t, r), f"replay {rep}"
