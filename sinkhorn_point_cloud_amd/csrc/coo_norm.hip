@@ -125,7 +125,7 @@ __global__ __launch_bounds__(kSegsPerGroup *kWave) void scale_pass(
         return (double)lv[q] + ob[p];
     };
     // one pass: each lane keeps (M, S) meaning S e^M over its entries, raising M
-    // when a larger term arrives; lanes merge in a fixed order
+    // when a larger term arrives
     double M = -INFINITY, S = 0.0;
     auto add = [&](double z) {
         if (z > M) {
@@ -144,17 +144,16 @@ __global__ __launch_bounds__(kSegsPerGroup *kWave) void scale_pass(
     }
     if (q < hi)
         add(term(q));
+    // merge the lanes: the segment's maximum, each lane's sum rescaled to it once,
+    // then one sum (fixed order)
+    double Mw = M;
 #pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) {
-        const double M2 = __shfl_xor(M, off, kWave), S2 = __shfl_xor(S, off, kWave);
-        const double Mn = fmax(M, M2);
-        if (Mn > -INFINITY)
-            S = (M > -INFINITY ? S * (double)expf((float)(M - Mn)) : 0.0) +
-                (M2 > -INFINITY ? S2 * (double)expf((float)(M2 - Mn)) : 0.0);
-        M = Mn;
-    }
+    for (int off = kWave / 2; off > 0; off >>= 1)
+        Mw = fmax(Mw, __shfl_xor(Mw, off, kWave));
+    S = M > -INFINITY ? S * (double)expf((float)(M - Mw)) : 0.0;
+    S = wave_sum(S);
     if (lane == 0)
-        out[si] = M > -INFINITY ? lw[si] - (M + log(S)) : 0.0;
+        out[si] = Mw > -INFINITY ? lw[si] - (Mw + log(S)) : 0.0;
 }
 
 // vals_k <- exp(lv_k + alpha_{ri_k} + beta_{ci_k}) with (ri, ci) the entry's row
