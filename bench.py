@@ -102,28 +102,28 @@ def parse():
     return p.parse_args()
 
 
-def cpu_baseline(w):
-    """Oracle (as it stands) on one full iteration of the workload at its final eps."""
+def cpu_baseline(w, iters=2):
+    """Oracle (as it stands) on `iters` full iterations of the workload at its final eps."""
     import numpy as np
     import oracle
 
     X, Y, a, b = (w[k].astype(np.float64) for k in ("X", "Y", "a", "b"))
     B, n, m = X.shape[0], X.shape[1], Y.shape[1]
     t0 = time.perf_counter()
-    oracle.potentials(X, Y, a, b, eps=[float(w["eps"][-1])], iters=[1])
+    oracle.potentials(X, Y, a, b, eps=[float(w["eps"][-1])], iters=[iters])
     dt = time.perf_counter() - t0
-    return {"value": B * n * m / dt, "unit": "updates/s", "cores": oracle.num_threads(),
+    return {"value": B * n * m * iters / dt, "unit": "updates/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"1 full iteration (f- and g-update, {2 * B * n * m:.3g} entry "
-                      f"evaluations) of {w['name']} at eps={float(w['eps'][-1]):g}, fp64, "
+            "sample": f"{iters} full iterations (f- and g-updates, {2 * iters * B * n * m:.3g} "
+                      f"entry evaluations) of {w['name']} at eps={float(w['eps'][-1]):g}, fp64, "
                       f"{dt:.2f} s"}
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU "
-              "split of the path is described in DESIGN.md, not run.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); splitting the path "
+              "across GPUs is designed, not built.", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
