@@ -161,11 +161,13 @@ def test_coincident_clouds_closed_form():
 
 
 @pytest.mark.parametrize("scores", ["mfma", "valu"])
-def test_batch_of_many_pairs(scores):
+@pytest.mark.parametrize("B,n,m", [(260, 300, 200), (256, 1100, 70)])
+def test_batch_of_many_pairs(scores, B, n, m):
     # at least as many pairs as compute units: the matrix-core path runs each
-    # stage per pair in one launch (several 64-row blocks per side, ragged
-    # sizes, zero weights, two stages); the vector path is the usual one
-    c = workloads.random_case(503, 260, 300, 200, 3, weights="dirichlet", zero_weights=2)
+    # stage per pair in one launch (several 64-row blocks per side, more blocks
+    # than waves on one side, ragged sizes, zero weights, two stages); the
+    # vector path is the usual one
+    c = workloads.random_case(503 + n, B, n, m, 3, weights="dirichlet", zero_weights=2)
     check_potentials(c, [0.2, 0.03], [4, 12], valu_scores=scores == "valu")
 
 
