@@ -244,6 +244,14 @@ def test_warm_start_split_matches_single_run():
     assert rel_inf(host(g2), host(g1), 0.03) < 1e-5
 
 
+def test_per_pair_launch_is_deterministic():
+    c = workloads.random_case(66, 256, 200, 150, 3, weights="dirichlet")
+    r1 = run_gpu(c, [0.3, 0.02], [3, 8])
+    r2 = run_gpu(c, [0.3, 0.02], [3, 8])
+    for u, v in zip(r1, r2):
+        assert torch.equal(u, v)
+
+
 @pytest.mark.parametrize("scores", ["mfma", "valu"])
 def test_potentials_are_deterministic(scores):
     c = workloads.random_case(13, 3, 700, 650, 3, weights="dirichlet")
@@ -747,6 +755,48 @@ def _assert_transposes(P, T, B):
         np.testing.assert_array_equal(r2[s2], c1[s1][order])
         np.testing.assert_array_equal(c2[s2], r1[s1][order])
         np.testing.assert_array_equal(v2[s2], v1[s1][order])
+
+
+def test_coo_normalize_degenerate_support():
+    # a row with no entry, a stored zero, a zero row weight and a column reached
+    # only through that row: scalings of empty rows and columns stay 0, a zero
+    # weight empties its row, and both sides agree with the oracle
+    B, n, m = 2, 6, 5
+    rng = np.random.default_rng(65)
+    rows, cols, vals, offs = [], [], [], [0]
+    for p in range(B):
+        for i in range(n):
+            if i == 2:
+                continue                                  # row 2: no entry
+            for j in sorted(rng.choice(m, size=rng.integers(1, m + 1), replace=False)):
+                if p == 1 and j == 4 and i != 0:
+                    continue                              # column 4 of pair 1 only via row 0
+                rows.append(i)
+                cols.append(j)
+                vals.append(0.0 if (i, j) == (3, 1) else rng.random() + 0.05)
+        offs.append(len(rows))
+    rows, cols = np.array(rows, dtype=np.int32), np.array(cols, dtype=np.int32)
+    vals, offs = np.array(vals, dtype=np.float32), np.array(offs, dtype=np.int64)
+    a = rng.dirichlet(np.ones(n), size=B).astype(np.float32)
+    a[1, 0] = 0.0                                         # zero weight on row 0 of pair 1
+    b = rng.dirichlet(np.ones(m), size=B).astype(np.float32)
+    # the transpose: the same entries in column-major order
+    t_rows, t_cols, t_vals = [], [], []
+    for p in range(B):
+        s_ = slice(offs[p], offs[p + 1])
+        order = np.lexsort((rows[s_], cols[s_]))
+        t_rows.append(cols[s_][order])
+        t_cols.append(rows[s_][order])
+        t_vals.append(vals[s_][order])
+    T = _coo_dev((np.concatenate(t_rows), np.concatenate(t_cols), np.concatenate(t_vals), offs))
+    P = _coo_dev((rows, cols, vals, offs))
+    v_o, err_o = oracle.coo_normalize(rows, cols, vals.astype(np.float64), offs, a, b, n, m, 25)
+    err = sk.coo_normalize(P, T, dev(a), dev(b), n, m, 25)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(host(P[2]), v_o, rtol=1e-4, atol=1e-30)
+    np.testing.assert_allclose(host(err), err_o, rtol=1e-3, atol=1e-6)
+    assert host(P[2])[(rows == 3) & (cols == 1)].max() == 0.0
+    _assert_transposes(P, T, B)
 
 
 def test_coo_normalize_gpu_chain_reaches_the_marginals():
