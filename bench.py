@@ -210,7 +210,7 @@ def main():
     peak, bound, fp32_bound, exp_bound, mfma_bound = roofline_evals_per_s(d)
     serial = 1.0 / (1.0 / fp32_bound + 1.0 / exp_bound)
 
-    if d == 3 and dt == sk.SK_F32:
+    if d == 3:
         # the library runs whole stages per pair in one launch when the batch has at
         # least one pair per compute unit and both padded clouds hold <= 8192 points
         pad = lambda k: (k + 63) // 64 * 64

@@ -82,7 +82,7 @@ enum {
 
 /*
  * Supported shapes: 1 <= B <= 65535, 1 <= n, m <= 2^24, B*n and B*m <= 2^31, and
- *   dtype SK_F32 with d == 3             (3-D point-cloud kernel), or
+ *   d == 3, dtype SK_F32 or SK_BF16       (3-D point-cloud kernel), or
  *   dtype SK_F32 or SK_BF16, 1 <= d <= 128 (feature kernel; d is padded with
  *                                          zeros to the next of 8,16,32,64,128).
  * Anything else returns SK_ERR_UNSUPPORTED.

@@ -53,7 +53,7 @@ bool shape_ok(int B, int n, int m, int d)
            m <= kMaxPoints && (long long)B * n <= (1ll << 31) && (long long)B * m <= (1ll << 31);
 }
 
-bool path3(int dtype, int d) { return dtype == SK_F32 && d == 3; }
+bool path3(int dtype, int d) { return (dtype == SK_F32 || dtype == SK_BF16) && d == 3; }
 
 bool supported(int dtype, int d) { return path3(dtype, d) || lseF_supported(dtype, d); }
 
@@ -348,12 +348,11 @@ int sinkhorn_potentials(const void *X, const void *Y, int dtype, const float *a,
     SideF sxf{X, w.xbias, f, w.l2a, w.xsq, w.xredo, n, np};
     SideF syf{Y, w.ybias, g, w.l2b, w.ysq, w.yredo, m, mp};
     if (p3) {
-        if ((e = launch_center3((const float *)X, n, (const float *)Y, m, B, w.boxes, w.center,
-                                st)))
+        if ((e = launch_center3(X, dtype, n, Y, m, B, w.boxes, w.center, st)))
             return hip_fail(e, "center");
-        if ((e = launch_pack3((const float *)X, a, warm, B, sx3, w.center, c0, st)))
+        if ((e = launch_pack3(X, dtype, a, warm, B, sx3, w.center, c0, st)))
             return hip_fail(e, "pack X");
-        if ((e = launch_pack3((const float *)Y, b, warm, B, sy3, w.center, c0, st)))
+        if ((e = launch_pack3(Y, dtype, b, warm, B, sy3, w.center, c0, st)))
             return hip_fail(e, "pack Y");
     } else {
         if ((e = launch_packF(X, dtype, d, a, warm, B, sxf, c0, st)))

@@ -147,11 +147,11 @@ hipError_t launch_lse3_pairwise(Side3 x, Side3 y, int B, float eps, int iters, f
 // Per-pair center (bounding-box midpoint of both clouds) for the d = 3 path;
 // part holds center3_parts(n, m) * B partial boxes.
 int center3_parts(int n, int m);
-hipError_t launch_center3(const float *X, int n, const float *Y, int m, int B, float4 *part,
-                          float4 *center, hipStream_t st);
+hipError_t launch_center3(const void *X, int dtype, int n, const void *Y, int m, int B,
+                          float4 *part, float4 *center, hipStream_t st);
 // Packs points relative to the pair's center, and the initial bias; without
 // warm start the potential is set to 0.
-hipError_t launch_pack3(const float *X, const float *w, int warm, int B, Side3 s,
+hipError_t launch_pack3(const void *X, int dtype, const float *w, int warm, int B, Side3 s,
                         const float4 *center, double c0, hipStream_t st);
 // One half-iteration, d = 3: q side rows, k side columns; scores on the matrix
 // cores (mfma) or on the vector ALUs.

@@ -1,4 +1,5 @@
-// lse_d3.hip -- fused streaming half-iteration for 3-D point clouds (fp32).
+// lse_d3.hip -- fused streaming half-iteration for 3-D point clouds (fp32 or bf16
+// coordinates, computed in fp32).
 //
 // One launch computes, for every row i of the "query" side and every pair b,
 //     f_i = -eps * LSE_j[(g_j - ||x_i - y_j||^2)/eps + log w_j]
@@ -185,19 +186,21 @@ __device__ __forceinline__ void box_reduce(float (&mn)[3], float (&mx)[3])
 
 // Partial bounding boxes: work-group (c, b) covers points c*kCenterChunk ...
 // of the concatenation X_b, Y_b.  part[2 (b parts + c)] = (min, max).
-__global__ __launch_bounds__(256) void center3_parts_kernel(const float *__restrict__ X, int n,
-                                                            const float *__restrict__ Y, int m,
+template <typename T>
+__global__ __launch_bounds__(256) void center3_parts_kernel(const T *__restrict__ X, int n,
+                                                            const T *__restrict__ Y, int m,
                                                             float4 *__restrict__ part)
 {
     const int b = blockIdx.y, c = blockIdx.x;
     float mn[3] = {INFINITY, INFINITY, INFINITY}, mx[3] = {-INFINITY, -INFINITY, -INFINITY};
     const int end = min(n + m, (c + 1) * kCenterChunk);
     for (int i = c * kCenterChunk + threadIdx.x; i < end; i += 256) {
-        const float *p = i < n ? X + ((size_t)b * n + i) * 3 : Y + ((size_t)b * m + i - n) * 3;
+        const T *p = i < n ? X + ((size_t)b * n + i) * 3 : Y + ((size_t)b * m + i - n) * 3;
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
-            mn[k] = fminf(mn[k], p[k]);
-            mx[k] = fmaxf(mx[k], p[k]);
+            const float v = Elem<T>::get(p, k);
+            mn[k] = fminf(mn[k], v);
+            mx[k] = fmaxf(mx[k], v);
         }
     }
     box_reduce(mn, mx);
@@ -230,7 +233,8 @@ __global__ __launch_bounds__(256) void center3_kernel(const float4 *__restrict__
     }
 }
 
-__global__ void pack3_kernel(const float *__restrict__ X, const float *__restrict__ w, int warm,
+template <typename T>
+__global__ void pack3_kernel(const T *__restrict__ X, const float *__restrict__ w, int warm,
                              int n, int n_pad, const float4 *__restrict__ center,
                              float4 *__restrict__ pts, float *__restrict__ pot,
                              float *__restrict__ l2w, uint16_t *__restrict__ krec, double c0)
@@ -241,9 +245,10 @@ __global__ void pack3_kernel(const float *__restrict__ X, const float *__restric
         return;
     float4 out = make_float4(0.f, 0.f, 0.f, kNeg);
     if (i < n) {
-        const float *x = X + ((size_t)b * n + i) * 3;
+        const T *x = X + ((size_t)b * n + i) * 3;
         const float4 o = center[b];
-        const float x0 = x[0] - o.x, x1 = x[1] - o.y, x2 = x[2] - o.z;
+        const float x0 = Elem<T>::get(x, 0) - o.x, x1 = Elem<T>::get(x, 1) - o.y,
+                    x2 = Elem<T>::get(x, 2) - o.z;
         float lw;
         if (w) {
             const float wi = w[(size_t)b * n + i];
@@ -832,22 +837,32 @@ size_t lse3_partial_floats2(int B, int nq_pad, int nk_pad)
 
 int center3_parts(int n, int m) { return ceil_div(n + m, kCenterChunk); }
 
-hipError_t launch_center3(const float *X, int n, const float *Y, int m, int B, float4 *part,
+hipError_t launch_center3(const void *X, int dtype, int n, const void *Y, int m, int B,
+                          float4 *part,
                           float4 *center, hipStream_t st)
 {
     const int parts = center3_parts(n, m);
-    hipLaunchKernelGGL(center3_parts_kernel, dim3(parts, B), dim3(256), 0, st, X, n, Y, m, part);
+    if (dtype == 1)
+        hipLaunchKernelGGL(center3_parts_kernel<uint16_t>, dim3(parts, B), dim3(256), 0, st,
+                           (const uint16_t *)X, n, (const uint16_t *)Y, m, part);
+    else
+        hipLaunchKernelGGL(center3_parts_kernel<float>, dim3(parts, B), dim3(256), 0, st,
+                           (const float *)X, n, (const float *)Y, m, part);
     hipLaunchKernelGGL(center3_kernel, dim3(B), dim3(256), 0, st, (const float4 *)part, parts,
                        center);
     return hipGetLastError();
 }
 
-hipError_t launch_pack3(const float *X, const float *w, int warm, int B, Side3 s,
+hipError_t launch_pack3(const void *X, int dtype, const float *w, int warm, int B, Side3 s,
                         const float4 *center, double c0, hipStream_t st)
 {
     dim3 grid(ceil_div(s.n_pad, 256), B);
-    hipLaunchKernelGGL(pack3_kernel, grid, dim3(256), 0, st, X, w, warm, s.n, s.n_pad, center,
-                       s.pts, s.pot, s.l2w, s.krec, c0);
+    if (dtype == 1)
+        hipLaunchKernelGGL(pack3_kernel<uint16_t>, grid, dim3(256), 0, st, (const uint16_t *)X, w,
+                           warm, s.n, s.n_pad, center, s.pts, s.pot, s.l2w, s.krec, c0);
+    else
+        hipLaunchKernelGGL(pack3_kernel<float>, grid, dim3(256), 0, st, (const float *)X, w, warm,
+                           s.n, s.n_pad, center, s.pts, s.pot, s.l2w, s.krec, c0);
     return hipGetLastError();
 }
 
