@@ -91,6 +91,17 @@ def test_potentials_d3_match_oracle(B, n, m, w, zw, eps, iters, scores):
 
 
 @pytest.mark.parametrize("scores", ["mfma", "valu"])
+@pytest.mark.parametrize("B,n,m,eps,iters", [(2, 300, 257, [0.05], [15]),
+                                             (1, 100, 12000, [0.05, 0.02], [4, 6]),
+                                             (256, 200, 150, [0.2, 0.03], [3, 8])])
+def test_bf16_point_clouds_match_oracle(scores, B, n, m, eps, iters):
+    # bf16 coordinates on the 3-D path: one launch per half-iteration, split key
+    # ranges, and per-pair stage launches (the oracle takes the same bf16 values)
+    c = workloads.random_case(600 + n, B, n, m, 3, weights="dirichlet", dtype="bf16")
+    check_potentials(c, eps, iters, valu_scores=scores == "valu")
+
+
+@pytest.mark.parametrize("scores", ["mfma", "valu"])
 def test_far_from_origin_and_huge_score_range(scores):
     # clouds far from the origin at small eps: scores span thousands of log2
     # units, so the running maximum is raised many times and the first keys
