@@ -8,11 +8,12 @@ pack, every (annealed) Sinkhorn half-iteration, then the transport-cost pass
 iterations; pair-1k; feat-50k) or, for the sparse-plan workloads (sphere-2k,
 blobs-1k), the thresholded COO plan and the loss and dL/dX computed from it.  Prints ONE JSON line with
   value      B*n*m*iters / step time   (cost-entry updates per second)
-  roofline   the half-iteration kernel: entry evaluations per launch / its
-             average launch time (events on the library's stream: the full step
-             minus the same step with every stage's iteration count halved,
-             divided by the difference in half-iteration launches), against the
-             exp/FP32 ALU roofline of the chip
+  roofline   the dominant kernel: entry evaluations per launch / its average
+             launch time (events on the library's stream: a potentials call with
+             the workload's schedule minus the same call with every iteration
+             count 0, divided by the launches the iterations make -- one per
+             half-iteration, or one per stage for the per-pair launch), against
+             the exp/FP32 ALU roofline of the chip (matrix cores for bf16 features)
   cpu_baseline  the fp64 oracle timed on one full iteration of the same
              problem on this host's cores, scaled to updates per second.
 """
@@ -188,9 +189,18 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / 1e3 / reps
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    def warm(fn, calls, seconds):
+        # untimed calls until both counts are reached: the GPU's clocks ramp up over
+        # the first tens of milliseconds of sustained work (a kernel runs 10-15%
+        # slower right after an idle gap), and the timed region should see them settled
+        torch.cuda.synchronize()
+        t0, k = time.perf_counter(), 0
+        while k < calls or time.perf_counter() - t0 < seconds:
+            fn()
+            k += 1
+            torch.cuda.synchronize()
+
+    warm(step, args.warmup, 0.25)
     t0 = time.perf_counter()
     t_step = timed(step, args.steps)
     wall = time.perf_counter() - t0
@@ -198,28 +208,39 @@ def main():
     assert sparse or torch.isfinite(cost).all()
     assert not sparse or int(nnz_dev) <= coo[0].numel(), "plan outgrew its buffers"
 
-    # the half-iteration kernel's launch time: the same step with every stage's
-    # iteration count halved (pack and cost pass unchanged), differenced
-    fewer = [max(1, i // 2) if i else 0 for i in iters]
-    t_fewer = timed(lambda: step(fewer), max(3, args.steps))
-    launches = 2 * (total_iters - sum(fewer))
-    t_launch = (t_step - t_fewer) / launches
-    t_iterations = t_launch * 2 * total_iters
-    evals_per_launch = B * n * m
-    achieved = evals_per_launch / t_launch
-    peak, bound, fp32_bound, exp_bound, mfma_bound = roofline_evals_per_s(d)
-    serial = 1.0 / (1.0 / fp32_bound + 1.0 / exp_bound)
-
     if d == 3:
         # the library runs whole stages per pair in one launch when the batch has at
         # least one pair per compute unit and both padded clouds hold <= 8192 points
         pad = lambda k: (k + 63) // 64 * 64
-        pairwise = (B >= torch.cuda.get_device_properties(dev).multi_processor_count
+        pairwise = (not args.valu_scores
+                    and B >= torch.cuda.get_device_properties(dev).multi_processor_count
                     and pad(n) <= 8192 and pad(m) <= 8192)
         kernel = ("lse3_kernel" if args.valu_scores else
                   "lse3p_kernel" if pairwise else "lse3m_kernel")
     else:
+        pairwise = False
         kernel = "lseFm_kernel" if dt == sk.SK_BF16 and d % 32 == 0 else "lseF_kernel"
+
+    # the dominant kernel's average launch: one potentials call (no cost pass, no
+    # plan) less the same call with every iteration count 0 (centering and packing
+    # only), over the launches its iterations make: one per half-iteration, or one
+    # per stage for the per-pair launch.  The difference also holds the query
+    # records built once per stage (two small launches).
+    def potentials_only(it):
+        sk.potentials(X, Y, a, b, eps=eps, iters=it, out=(f, g, None), cost=False,
+                      workspace=ws, valu_scores=args.valu_scores)
+
+    reps = max(3, args.steps)
+    warm(lambda: potentials_only(iters), 1, 0.1)
+    t_iterations = (timed(lambda: potentials_only(iters), reps)
+                    - timed(lambda: potentials_only([0] * len(iters)), reps))
+    potentials_only(iters)   # the converged potentials again, for the phases below
+    launches = sum(1 for i in iters if i) if pairwise else 2 * total_iters
+    t_launch = t_iterations / launches
+    evals_per_launch = 2 * B * n * m * total_iters / launches
+    achieved = evals_per_launch / t_launch
+    peak, bound, fp32_bound, exp_bound, mfma_bound = roofline_evals_per_s(d)
+    serial = 1.0 / (1.0 / fp32_bound + 1.0 / exp_bound)
 
     updates = B * n * m * total_iters
     line = {
@@ -248,8 +269,9 @@ def main():
                      if kernel in KERNEL_SOURCES else None,
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
                                      "scaled by a 256 MiB copy)",
-                     "kernel": kernel + (" (one half-iteration of a per-pair stage launch)"
-                                         if kernel == "lse3p_kernel" else " (one half-iteration)"),
+                     "kernel": kernel + (" (one launch: a stage of %d iterations for every pair)"
+                                         % (total_iters // launches) if pairwise
+                                         else " (one launch: a half-iteration)"),
                      "launch_ms": t_launch * 1e3, "evals_per_launch": evals_per_launch,
                      "serial_exp_fp32_peak": serial / 1e12,
                      "frac_of_serial_peak": achieved / serial},

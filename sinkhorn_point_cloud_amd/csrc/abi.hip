@@ -63,6 +63,7 @@ struct PotWs {
     uint16_t *kxrec = nullptr, *kyrec = nullptr, *qxrec = nullptr, *qyrec = nullptr;
     // feature path
     float *xbias = nullptr, *ybias = nullptr, *xsq = nullptr, *ysq = nullptr;
+    // both: per 64-row block marks of rows to recompute
     int *xredo = nullptr, *yredo = nullptr;
     // both
     float *l2a, *l2b;
@@ -86,6 +87,8 @@ PotWs carve_potentials(Carve &c, int B, int n, int m, int d, int dtype)
         w.qxrec = c.take<uint16_t>((size_t)B * np * kRec);
         w.qyrec = c.take<uint16_t>((size_t)B * mp * kRec);
         w.boxes = c.take<float4>((size_t)2 * B * center3_parts(n, m));
+        w.xredo = c.take<int>((size_t)B * (np / kPad));
+        w.yredo = c.take<int>((size_t)B * (mp / kPad));
         parts = std::max(lse3_partial_floats2(B, np, mp), lse3_partial_floats2(B, mp, np));
     } else {
         w.xbias = c.take<float>((size_t)B * np);
@@ -344,7 +347,8 @@ int sinkhorn_potentials(const void *X, const void *Y, int dtype, const float *a,
     const bool p3 = path3(dtype, d);
     const bool pairwise = p3 && mfma && lse3_pairwise(B, np, mp);
     // the caller's f and g are the state of the iteration
-    Side3 sx3{w.px, f, w.l2a, w.kxrec, w.qxrec, n, np}, sy3{w.py, g, w.l2b, w.kyrec, w.qyrec, m, mp};
+    Side3 sx3{w.px, f, w.l2a, w.kxrec, w.qxrec, n, np, w.xredo};
+    Side3 sy3{w.py, g, w.l2b, w.kyrec, w.qyrec, m, mp, w.yredo};
     SideF sxf{X, w.xbias, f, w.l2a, w.xsq, w.xredo, n, np};
     SideF syf{Y, w.ybias, g, w.l2b, w.ysq, w.yredo, m, mp};
     if (p3) {
@@ -373,7 +377,8 @@ int sinkhorn_potentials(const void *X, const void *Y, int dtype, const float *a,
                     eps_next = eps[t];
                     break;
                 }
-            if ((e = launch_lse3_pairwise(sx3, sy3, B, eps[s], iters[s], eps_next, st)))
+            const bool cold = !warm && s == first;
+            if ((e = launch_lse3_pairwise(sx3, sy3, B, eps[s], iters[s], eps_next, cold, st)))
                 return hip_fail(e, "iterations");
             continue;
         }

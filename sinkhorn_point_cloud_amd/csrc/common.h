@@ -130,6 +130,7 @@ struct Side3 {
     uint16_t *krec;   // [B][n_pad][32] bf16 key records (matrix-core path)
     uint16_t *qrec;   // [B][n_pad][32] bf16 query records at the current eps
     int n, n_pad;
+    int *redo = nullptr;   // [B][n_pad / 64] row blocks to recompute after a split merge
 };
 constexpr int kRec = 32;  // bf16 slots per record (one 16x16x32 MFMA k-range)
 
@@ -138,11 +139,12 @@ hipError_t launch_qrec3(Side3 s, int B, float eps, hipStream_t st);
 // Whole stages per pair in one launch (matrix-core scores): used when the batch
 // has at least as many pairs as the device has compute units and each cloud has
 // at most kPairMaxPoints points (padded).  Runs `iters` iterations at eps; the
-// last g-update hands the f-update biases at eps_next.
+// last g-update hands the f-update biases at eps_next.  cold: the potentials
+// are the zeros of a cold start (the first f- and g-update take exact shifts).
 constexpr int kPairMaxPoints = 8192;
 bool lse3_pairwise(int B, int n_pad, int m_pad);
 hipError_t launch_lse3_pairwise(Side3 x, Side3 y, int B, float eps, int iters, float eps_next,
-                                hipStream_t st);
+                                bool cold, hipStream_t st);
 
 // Per-pair center (bounding-box midpoint of both clouds) for the d = 3 path;
 // part holds center3_parts(n, m) * B partial boxes.

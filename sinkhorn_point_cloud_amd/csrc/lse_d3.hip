@@ -37,7 +37,9 @@
 // A work-group holds W waves on the same 64 rows, each streaming every W-th key
 // tile; their states merge at the end.  When a batch has too few rows to fill
 // the chip the key range is also split across work-groups and a second small
-// kernel merges the partial states.
+// kernel merges the partial states; on the matrix-core path a third launch
+// recomputes, with exact shifts, the row blocks whose merged sums left the
+// range (it returns at once for every other block).
 #include "common.h"
 
 namespace sk {
@@ -391,7 +393,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kGroups = 4;        // 16-row groups per wave
-constexpr float kEmpty = 1.0e29f; // accumulator input above this: no key seen yet
 
 __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t *p)
 {
@@ -409,17 +410,20 @@ __device__ __forceinline__ f32x4 mfma4(bf16x8 a, bf16x8 b, f32x4 c)
 // its previous pass, M_i = c (||x_i||^2 - f_i).  Between passes potentials
 // move little, so 2^(s - M) stays in range and the loop is exponential plus
 // accumulation only.  The merged sum of each row is checked at the end: if any
-// row of the work-group left [2^-64, 2^100] (the shift was stale, e.g. on the
-// first pass or after a large change of eps), the whole group streams its
-// keys again with the lazy-maximum scheme: the accumulator input holds -M,
-// +1e30 marks a state that has seen no key yet, and the first key it sees is
-// re-evaluated with a zero accumulator so that M starts at an exact score.
-// Either way the result is the exact log-sum-exp to fp32 rounding.
+// row of a 64-row block left [2^-64, 2^100] (the shift was stale, e.g. on the
+// first pass or after a large change of eps), the block's shifts are made
+// exact: a pass over the same keys takes every row's maximum of s - M, M moves
+// up by it, and the shifted pass runs again, now with terms of at most 1 and a
+// sum in [1, keys].  Either way the result is the exact log-sum-exp to fp32
+// rounding.
 constexpr float kSumLo = 5.421010862e-20f;  // 2^-64
 constexpr float kSumHi = 1.2676506e30f;     // 2^100
 
-// Shifted stream of one wave: key tiles first, first + W, ... (cnt of them)
-// against the wave's 64 rows, accumulated into S with the shift in Cn.  The
+// Stream of one wave: key tiles first, first + W, ... (cnt of them) against the
+// wave's 64 rows with the shift in Cn, accumulated into S as a sum of 2^(s - M)
+// (the shifted pass) or as the maximum of s - M (kMax, the pass that makes a
+// stale shift exact; the same tiles, operands and MFMAs, so the maximum is
+// taken over exactly the values the following shifted pass exponentiates).  The
 // first cnt % 3 tiles go one by one, the rest in groups of three with no
 // branch inside a group, so every key operand is loaded two tiles ahead of its
 // use (the scheduling barriers keep each load in place; indices are clamped to
@@ -427,11 +431,10 @@ constexpr float kSumHi = 1.2676506e30f;     // 2^100
 // register sets take turns, so no operand is copied.  Key operands come through
 // a buffer resource: the tile offset rides in an SGPR (soffset), the lane's
 // offset is a constant VGPR, so there is no vector address arithmetic per tile.
-template <int W>
-__device__ __forceinline__ void shifted_stream(const bf16x8 (&A)[kGroups],
-                                               const f32x4 (&Cn)[kGroups], f32x4 (&S)[kGroups],
-                                               const uint16_t *kb, int nk_pad, int lane_off,
-                                               int first, int cnt)
+template <int W, bool kMax>
+__device__ __forceinline__ void key_stream(const bf16x8 (&A)[kGroups], const f32x4 (&Cn)[kGroups],
+                                           f32x4 (&S)[kGroups], const uint16_t *kb, int nk_pad,
+                                           int lane_off, int first, int cnt)
 {
     const int last = first + (cnt > 0 ? cnt - 1 : 0) * W;
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
@@ -449,7 +452,7 @@ __device__ __forceinline__ void shifted_stream(const bf16x8 (&A)[kGroups],
             const f32x4 D = mfma4(A[g], Bt, Cn[g]);
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                S[g][r] += ex2(D[r]);
+                S[g][r] = kMax ? fmaxf(S[g][r], D[r]) : S[g][r] + ex2(D[r]);
         }
     };
     int k = 0;
@@ -479,79 +482,12 @@ __device__ __forceinline__ void shifted_stream(const bf16x8 (&A)[kGroups],
 // yet).  The key operand of the next tile is loaded one tile ahead; the clamped
 // index keeps that load inside the pair's keys on the last tile.
 template <int W>
-__device__ __forceinline__ void lazy_stream(const bf16x8 (&A)[kGroups], f32x4 (&Cn)[kGroups],
-                                            f32x4 (&S)[kGroups], const uint16_t *kb, int lane_off,
-                                            int t0, int t_end, int n_tiles)
+__device__ __forceinline__ void shifted_stream(const bf16x8 (&A)[kGroups],
+                                               const f32x4 (&Cn)[kGroups], f32x4 (&S)[kGroups],
+                                               const uint16_t *kb, int nk_pad, int lane_off,
+                                               int first, int cnt)
 {
-#pragma unroll
-    for (int g = 0; g < kGroups; ++g) {
-        Cn[g] = f32x4{-kNeg, -kNeg, -kNeg, -kNeg};
-        S[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    int t = t0;
-    bf16x8 Bv = load_bf16x8(kb + (size_t)min(t, n_tiles - 1) * kTile * kRec + lane_off);
-    for (; t < t_end; t += W) {
-        const int tn = min(t + W, t_end - 1);
-        const bf16x8 Bn = load_bf16x8(kb + (size_t)tn * kTile * kRec + lane_off);
-        f32x4 D[kGroups];
-#pragma unroll
-        for (int g = 0; g < kGroups; ++g)
-            D[g] = mfma4(A[g], Bv, Cn[g]);
-        float cm = D[0][0];
-#pragma unroll
-        for (int g = 0; g < kGroups; ++g)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                cm = fmaxf(cm, D[g][r]);
-        // The branch is taken by the whole wave (ballot): an MFMA ignores the
-        // execution mask and writes every lane, so it must never run with
-        // part of the wave switched off.
-        if (__ballot(cm > kLazy) != 0) {
-            // raise M where a score exceeds it by more than kLazy (by an integer,
-            // so the rescale of S is exact); states with no key yet restart from
-            // the exact score, read with a zero accumulator input
-            f32x4 Cx[kGroups];
-            uint32_t fresh = 0;
-#pragma unroll
-            for (int g = 0; g < kGroups; ++g)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float d = D[g][r], cn = Cn[g][r];
-                    float cx = cn;
-                    if (d > kLazy) {
-                        if (cn > kEmpty) {
-                            cx = 0.f;
-                            fresh |= 1u << (4 * g + r);
-                        } else {
-                            cx = cn - floorf(d);
-                            S[g][r] *= ex2(cx - cn);
-                        }
-                    }
-                    Cx[g][r] = cx;
-                }
-#pragma unroll
-            for (int g = 0; g < kGroups; ++g)
-                D[g] = mfma4(A[g], Bv, Cx[g]);
-#pragma unroll
-            for (int g = 0; g < kGroups; ++g)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (fresh & (1u << (4 * g + r))) {
-                        S[g][r] = 0.f;
-                        Cx[g][r] = -D[g][r];
-                        D[g][r] = 0.f;
-                    }
-#pragma unroll
-            for (int g = 0; g < kGroups; ++g)
-                Cn[g] = Cx[g];
-        }
-#pragma unroll
-        for (int g = 0; g < kGroups; ++g)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                S[g][r] += ex2(D[g][r]);
-        Bv = Bn;
-    }
+    key_stream<W, false>(A, Cn, S, kb, nk_pad, lane_off, first, cnt);
 }
 
 // Query operands of a wave's 64 rows.
@@ -581,16 +517,98 @@ __device__ __forceinline__ void load_shifts(f32x4 (&Cn)[kGroups], f32x4 (&S)[kGr
         }
 }
 
+__device__ __forceinline__ float row16_max(float v)
+{
+    v = fmaxf(v, dpp_move<kDppXor1>(v));
+    v = fmaxf(v, dpp_move<kDppXor2>(v));
+    v = fmaxf(v, dpp_move<kDppHalfMirror>(v));
+    v = fmaxf(v, dpp_move<kDppMirror>(v));
+    return v;
+}
+
+// Row sums of one wave's states, with the row's shift, into red_w[row].
+__device__ __forceinline__ void wave_sums(const f32x4 (&Cn)[kGroups], const f32x4 (&S)[kGroups],
+                                          float2 *red_w, int kq, int c16)
+{
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float Sr = row16_sum(S[g][r]);
+            if (c16 == 0)
+                red_w[16 * g + 4 * kq + r] = make_float2(-Cn[g][r], Sr);
+        }
+}
+
+// Makes the shifts of a 64-row block exact: the maximum of s - M over the
+// block's keys (each wave its tiles, merged over the W waves through red) is
+// added to every row's M, and S is emptied for the shifted pass that follows.
+// With W > 1 every wave of the work-group must call it.
+template <int W>
+__device__ __forceinline__ void exact_shifts(const bf16x8 (&A)[kGroups], f32x4 (&Cn)[kGroups],
+                                             f32x4 (&S)[kGroups], const uint16_t *kb, int nk_pad,
+                                             int lane_off, int first, int cnt,
+                                             float2 (*red)[kWave], int w, int kq, int c16)
+{
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g)
+        S[g] = f32x4{kNeg, kNeg, kNeg, kNeg};
+    key_stream<W, true>(A, Cn, S, kb, nk_pad, lane_off, first, cnt);
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            S[g][r] = row16_max(S[g][r]);
+    if constexpr (W > 1) {
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (c16 == 0)
+                    red[w][16 * g + 4 * kq + r].x = S[g][r];
+        __syncthreads();
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int lr = 16 * g + 4 * kq + r;
+                float mx = red[0][lr].x;
+#pragma unroll
+                for (int v = 1; v < W; ++v)
+                    mx = fmaxf(mx, red[v][lr].x);
+                S[g][r] = mx;
+            }
+        __syncthreads();   // red is written again by the caller
+    }
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            Cn[g][r] -= S[g][r];
+            S[g][r] = 0.f;
+        }
+}
+
+// One work-group: 64 query rows of pair b, W waves, key tiles of split
+// blockIdx.y.  Three uses:
+//   part == nullptr, redo == nullptr: all keys; shifted pass, made exact where
+//     a row left the range; finishes the rows.
+//   part != nullptr: the split's keys with the rows' shifts; writes the partial
+//     (M, S) of every row (no range check: the merge checks the whole row).
+//   redo != nullptr (repair, after the merge of split partials): only blocks
+//     marked in redo; exact shifts over all keys, then the shifted pass.
 template <int W>
 __global__ __launch_bounds__(W *kWave) void lse3m_kernel(
     float4 *__restrict__ qpts, uint16_t *__restrict__ qkrec, const uint16_t *__restrict__ qrec,
     const uint16_t *__restrict__ krec, float *__restrict__ qpot, const float *__restrict__ ql2w,
-    float2 *__restrict__ part, int nq, int nq_pad, int nk_pad, int tiles_per_split, float two_c,
-    double eps_ln2, double c_next)
+    float2 *__restrict__ part, const int *__restrict__ redo, int nq, int nq_pad, int nk_pad,
+    int tiles_per_split, float two_c, double eps_ln2, double c_next)
 {
     __shared__ float2 red[W][kWave];
-    __shared__ int redo;
+    __shared__ int stale;
     const int b = blockIdx.z;
+    if (redo && !redo[(size_t)b * (nq_pad / kWave) + blockIdx.x])
+        return;   // the whole work-group: this block was finished by the merge
     const int split = blockIdx.y;
     const int lane = lane_id();
     const int w = wave_id_uniform();
@@ -605,27 +623,20 @@ __global__ __launch_bounds__(W *kWave) void lse3m_kernel(
     const int n_tiles = nk_pad / kTile;
     const int t_begin = split * tiles_per_split;
     const int t_end = min(t_begin + tiles_per_split, n_tiles);
+    const int first = t_begin + w;   // this wave takes tiles first + k W
+    const int cnt = first < t_end ? (t_end - first + W - 1) / W : 0;
     bf16x8 A[kGroups];
     f32x4 Cn[kGroups], S[kGroups];
     load_rows(A, qrec_rows, lane_off);
+    load_shifts(Cn, S, qrow, qpot + (size_t)b * nq, nq, row0, kq, 0.5f * two_c);
+    const int row = row0 + lane;
 
-    if (part == nullptr) {
-        // ---- shifted pass: this wave takes tiles t_begin + w + k W
-        load_shifts(Cn, S, qrow, qpot + (size_t)b * nq, nq, row0, kq, 0.5f * two_c);
-        const int first = t_begin + w;
-        shifted_stream<W>(A, Cn, S, kb, nk_pad, lane_off, first,
-                          first < t_end ? (t_end - first + W - 1) / W : 0);
+    if (redo == nullptr) {
+        shifted_stream<W>(A, Cn, S, kb, nk_pad, lane_off, first, cnt);
         // every partial of a row has the same shift: the merge is a sum
-#pragma unroll
-        for (int g = 0; g < kGroups; ++g)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float Sr = row16_sum(S[g][r]);
-                if (c16 == 0)
-                    red[w][16 * g + 4 * kq + r] = make_float2(-Cn[g][r], Sr);
-            }
+        wave_sums(Cn, S, red[w], kq, c16);
         if (threadIdx.x == 0)
-            redo = 0;
+            stale = 0;
         __syncthreads();
         float Ssum = 0.f;
         const float M = red[0][lane].x;
@@ -633,51 +644,35 @@ __global__ __launch_bounds__(W *kWave) void lse3m_kernel(
 #pragma unroll
             for (int v = 0; v < W; ++v)
                 Ssum += red[v][lane].y;
-            if (row0 + lane < nq && !(Ssum >= kSumLo && Ssum <= kSumHi))
-                redo = 1;   // benign race: every writer stores 1 (padding rows never do)
+            if (part)
+                part[((size_t)split * gridDim.z + b) * nq_pad + row] = make_float2(M, Ssum);
+            else if (row < nq && !(Ssum >= kSumLo && Ssum <= kSumHi))
+                stale = 1;   // benign race: every writer stores 1 (padding rows never do)
         }
+        if (part)
+            return;
         __syncthreads();
-        if (!redo) {
-            const int row = row0 + lane;
+        if (!stale) {
             if (w == 0 && row < nq)
-                finish_row(qpts, qkrec, qpot, ql2w, (size_t)b * nq_pad + row, (size_t)b * nq + row,
-                           qpts[(size_t)b * nq_pad + row], M, Ssum, eps_ln2, c_next);
+                finish_row(qpts, qkrec, qpot, ql2w, (size_t)b * nq_pad + row,
+                           (size_t)b * nq + row, qpts[(size_t)b * nq_pad + row], M, Ssum,
+                           eps_ln2, c_next);
             return;
         }
-        __syncthreads();   // red is reused below
     }
 
-    // ---- lazy-maximum pass
-    lazy_stream<W>(A, Cn, S, kb, lane_off, t_begin + w, t_end, n_tiles);
-
-    // merge the 16 column partials of every row (lanes sharing kq), then the waves
-#pragma unroll
-    for (int g = 0; g < kGroups; ++g)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            float M = -Cn[g][r], Sr = S[g][r];
-            row16_merge(M, Sr);
-            if (c16 == 0)
-                red[w][16 * g + 4 * kq + r] = make_float2(M, Sr);
-        }
+    exact_shifts<W>(A, Cn, S, kb, nk_pad, lane_off, first, cnt, red, w, kq, c16);
+    shifted_stream<W>(A, Cn, S, kb, nk_pad, lane_off, first, cnt);
+    wave_sums(Cn, S, red[w], kq, c16);
     __syncthreads();
-    if (w != 0)
+    if (w != 0 || row >= nq)
         return;
-    float2 st = red[0][lane];
-    float M = st.x, Sf = st.y;
+    float Ssum = 0.f;
 #pragma unroll
-    for (int v = 1; v < W; ++v) {
-        const float2 o = red[v][lane];
-        lse_merge(M, Sf, o.x, o.y);
-    }
-    const int row = row0 + lane;
-    if (part) {
-        part[((size_t)split * gridDim.z + b) * nq_pad + row] = make_float2(M, Sf);
-        return;
-    }
-    if (row < nq)
-        finish_row(qpts, qkrec, qpot, ql2w, (size_t)b * nq_pad + row, (size_t)b * nq + row,
-                   qpts[(size_t)b * nq_pad + row], M, Sf, eps_ln2, c_next);
+    for (int v = 0; v < W; ++v)
+        Ssum += red[v][lane].y;
+    finish_row(qpts, qkrec, qpot, ql2w, (size_t)b * nq_pad + row, (size_t)b * nq + row,
+               qpts[(size_t)b * nq_pad + row], red[0][lane].x, Ssum, eps_ln2, c_next);
 }
 
 // ---------------------------------------------------------------------------
@@ -694,9 +689,12 @@ __global__ __launch_bounds__(W *kWave) void lse3m_kernel(
 constexpr int kPairWaves = 16;
 
 // One wave: rows row0 .. row0 + 63 of pair b on side q against all keys of side k.
+// With stale set (the first updates of a cold start, where the potentials
+// are zeros and most pairs' shifts are far off) the shifts are made exact
+// before the first shifted pass instead of after a failed one.
 __device__ __forceinline__ void wave_rows(const Side3 &q, const Side3 &k, int b, int row0,
                                           float two_c, double eps_ln2, double c_next,
-                                          float2 *red)
+                                          float2 *red, bool stale)
 {
     const int lane = lane_id();
     const int kq = lane >> 4, c16 = lane & 15;
@@ -709,31 +707,23 @@ __device__ __forceinline__ void wave_rows(const Side3 &q, const Side3 &k, int b,
     f32x4 Cn[kGroups], S[kGroups];
     load_rows(A, qrec_rows, lane_off);
     load_shifts(Cn, S, qrow, q.pot + (size_t)b * q.n, q.n, row0, kq, 0.5f * two_c);
-    shifted_stream<1>(A, Cn, S, kb, k.n_pad, lane_off, 0, n_tiles);
-#pragma unroll
-    for (int g = 0; g < kGroups; ++g)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float Sr = row16_sum(S[g][r]);
-            if (c16 == 0)
-                red[16 * g + 4 * kq + r] = make_float2(-Cn[g][r], Sr);
-        }
-    __builtin_amdgcn_wave_barrier();
-    float M = red[lane].x, Sf = red[lane].y;
+    float M = 0.f, Sf = 0.f;
     const int row = row0 + lane;
-    const bool bad = row < q.n && !(Sf >= kSumLo && Sf <= kSumHi);
-    if (__ballot(bad) != 0) {   // the whole wave: it owns every row of the block
-        lazy_stream<1>(A, Cn, S, kb, lane_off, 0, n_tiles, n_tiles);
+    if (!stale) {
+        shifted_stream<1>(A, Cn, S, kb, k.n_pad, lane_off, 0, n_tiles);
+        wave_sums(Cn, S, red, kq, c16);
         __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int g = 0; g < kGroups; ++g)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float Mr = -Cn[g][r], Sr = S[g][r];
-                row16_merge(Mr, Sr);
-                if (c16 == 0)
-                    red[16 * g + 4 * kq + r] = make_float2(Mr, Sr);
-            }
+        M = red[lane].x;
+        Sf = red[lane].y;
+        // the whole wave decides: it owns every row of the block
+        stale = __ballot(row < q.n && !(Sf >= kSumLo && Sf <= kSumHi)) != 0;
+        __builtin_amdgcn_wave_barrier();   // red is written again below
+    }
+    if (stale) {
+        exact_shifts<1>(A, Cn, S, kb, k.n_pad, lane_off, 0, n_tiles, nullptr, 0, kq, c16);
+        shifted_stream<1>(A, Cn, S, kb, k.n_pad, lane_off, 0, n_tiles);
+        __builtin_amdgcn_wave_barrier();
+        wave_sums(Cn, S, red, kq, c16);
         __builtin_amdgcn_wave_barrier();
         M = red[lane].x;
         Sf = red[lane].y;
@@ -746,48 +736,64 @@ __device__ __forceinline__ void wave_rows(const Side3 &q, const Side3 &k, int b,
 
 __global__ __launch_bounds__(kPairWaves *kWave) void lse3p_kernel(Side3 x, Side3 y, int iters,
                                                                   float two_c, double eps_ln2,
-                                                                  double c_next_last)
+                                                                  double c_next_last, int cold)
 {
     __shared__ float2 red[kPairWaves][kWave];
     const int b = blockIdx.x;
     const int w = wave_id_uniform();
     const double c_same = 0.5 * (double)two_c;
     for (int it = 0; it < iters; ++it) {
+        const bool stale = cold && it == 0;
         for (int rb = w; rb < x.n_pad / kWave; rb += kPairWaves)
-            wave_rows(x, y, b, rb * kWave, two_c, eps_ln2, c_same, red[w]);
+            wave_rows(x, y, b, rb * kWave, two_c, eps_ln2, c_same, red[w], stale);
         __syncthreads();   // f and the X-side biases are complete
         const double cn = it + 1 < iters ? c_same : c_next_last;
         for (int rb = w; rb < y.n_pad / kWave; rb += kPairWaves)
-            wave_rows(y, x, b, rb * kWave, two_c, eps_ln2, cn, red[w]);
+            wave_rows(y, x, b, rb * kWave, two_c, eps_ln2, cn, red[w], stale);
         __syncthreads();   // g and the Y-side biases are complete
     }
 }
 
+// Merge of the split partials of every row.  Matrix-core partials of a row
+// share one shift (vector-pass partials are exact states), so the merge is a
+// sum.  With redo, a row whose merged sum left [2^-64, 2^100] is not finished;
+// its 64-row block is marked (every block's mark is written on every pass) and
+// the repair launch of lse3m_kernel recomputes it with exact shifts.
 __global__ void lse3_finalize(float4 *__restrict__ qpts, uint16_t *__restrict__ qkrec,
                               float *__restrict__ qpot,
                               const float *__restrict__ ql2w, const float2 *__restrict__ part,
-                              int B, int nq, int nq_pad, int splits, double eps_ln2,
-                              double c_next)
+                              int *__restrict__ redo, int B, int nq, int nq_pad, int splits,
+                              double eps_ln2, double c_next)
 {
     const int b = blockIdx.y;
-    const int row = blockIdx.x * blockDim.x + threadIdx.x;
-    if (row >= nq)
-        return;
-    float2 s0 = part[(size_t)b * nq_pad + row];
-    float M = s0.x, S = s0.y;
-    for (int s = 1; s < splits; ++s) {
-        const float2 o = part[((size_t)s * B + b) * nq_pad + row];
-        lse_merge(M, S, o.x, o.y);
+    const int row = blockIdx.x * blockDim.x + threadIdx.x;   // blockDim: whole waves
+    bool bad = false;
+    if (row < nq) {
+        float2 s0 = part[(size_t)b * nq_pad + row];
+        float M = s0.x, S = s0.y;
+        for (int s = 1; s < splits; ++s) {
+            const float2 o = part[((size_t)s * B + b) * nq_pad + row];
+            lse_merge(M, S, o.x, o.y);
+        }
+        bad = redo && !(S >= kSumLo && S <= kSumHi);
+        const size_t pt = (size_t)b * nq_pad + row;
+        if (!bad)
+            finish_row(qpts, qkrec, qpot, ql2w, pt, (size_t)b * nq + row, qpts[pt], M, S,
+                       eps_ln2, c_next);
     }
-    const size_t pt = (size_t)b * nq_pad + row;
-    finish_row(qpts, qkrec, qpot, ql2w, pt, (size_t)b * nq + row, qpts[pt], M, S, eps_ln2,
-               c_next);
+    if (redo) {
+        const bool any = __ballot(bad) != 0;
+        const int rb = row / kWave;
+        if (lane_id() == 0 && rb < nq_pad / kWave)
+            redo[(size_t)b * (nq_pad / kWave) + rb] = any ? 1 : 0;
+    }
 }
 
 // Column splits so that a launch has about 4 work-groups per CU.  A split costs
-// a second (merge) kernel and gives up the shifted pass, so rows of at most
-// 64 tiles per wave are never split: there the launch is latency-bound and one
-// kernel is faster (pair-1k: 6.8 instead of 10.6 us per half-iteration).
+// two more launches (the merge and the repair of stale blocks), so rows of at
+// most 64 tiles per wave are never split: there the launch is latency-bound and
+// one kernel is as fast or faster (one pair of 4096 points: 8% slower split;
+// four pairs of 8192: 13% slower; one pair of 8192: 5% faster).
 int lse3_splits(int B, int nq_pad, int nk_pad)
 {
     const long groups = (long)B * (nq_pad / kWave);
@@ -819,13 +825,25 @@ int lse3m_waves(long groups, int tiles_per_split)
 }
 
 template <int W>
-void launch_lse3m_w(dim3 grid, hipStream_t st, Side3 q, Side3 k, float2 *part, int tiles_per_split,
-                    float two_c, double eps_ln2, double c_next)
+void launch_lse3m_w(dim3 grid, hipStream_t st, Side3 q, Side3 k, float2 *part, const int *redo,
+                    int tiles_per_split, float two_c, double eps_ln2, double c_next)
 {
     hipLaunchKernelGGL(lse3m_kernel<W>, grid, dim3(W * kWave), 0, st, q.pts, q.krec,
                        (const uint16_t *)q.qrec, (const uint16_t *)k.krec, q.pot,
-                       (const float *)q.l2w, part, q.n, q.n_pad, k.n_pad, tiles_per_split, two_c,
-                       eps_ln2, c_next);
+                       (const float *)q.l2w, part, redo, q.n, q.n_pad, k.n_pad, tiles_per_split,
+                       two_c, eps_ln2, c_next);
+}
+
+void launch_lse3m(dim3 grid, hipStream_t st, Side3 q, Side3 k, float2 *part, const int *redo,
+                  int tiles_per_split, float two_c, double eps_ln2, double c_next)
+{
+    const long groups = (long)grid.x * grid.y * grid.z;
+    switch (lse3m_waves(groups, tiles_per_split)) {
+    case 1: launch_lse3m_w<1>(grid, st, q, k, part, redo, tiles_per_split, two_c, eps_ln2, c_next); break;
+    case 2: launch_lse3m_w<2>(grid, st, q, k, part, redo, tiles_per_split, two_c, eps_ln2, c_next); break;
+    case 4: launch_lse3m_w<4>(grid, st, q, k, part, redo, tiles_per_split, two_c, eps_ln2, c_next); break;
+    default: launch_lse3m_w<8>(grid, st, q, k, part, redo, tiles_per_split, two_c, eps_ln2, c_next); break;
+    }
 }
 }  // namespace
 
@@ -884,11 +902,11 @@ bool lse3_pairwise(int B, int n_pad, int m_pad)
 }
 
 hipError_t launch_lse3_pairwise(Side3 x, Side3 y, int B, float eps, int iters, float eps_next,
-                                hipStream_t st)
+                                bool cold, hipStream_t st)
 {
     const float c = scale_of(eps);
     hipLaunchKernelGGL(lse3p_kernel, dim3(B), dim3(kPairWaves * kWave), 0, st, x, y, iters,
-                       2.0f * c, 1.0 / (double)c, (double)scale_of(eps_next));
+                       2.0f * c, 1.0 / (double)c, (double)scale_of(eps_next), cold ? 1 : 0);
     return hipGetLastError();
 }
 
@@ -903,24 +921,23 @@ hipError_t launch_lse3(Side3 q, Side3 k, int B, float eps, float eps_next, float
     const int tiles = k.n_pad / kTile;
     const int tiles_per_split = ceil_div(tiles, splits);
     dim3 grid(q.n_pad / kWave, splits, B);
-    if (mfma) {
-        float2 *p = splits > 1 ? part : nullptr;
-        switch (lse3m_waves((long)B * splits * (q.n_pad / kWave), tiles_per_split)) {
-        case 1: launch_lse3m_w<1>(grid, st, q, k, p, tiles_per_split, 2.0f * c, eps_ln2, c_next); break;
-        case 2: launch_lse3m_w<2>(grid, st, q, k, p, tiles_per_split, 2.0f * c, eps_ln2, c_next); break;
-        case 4: launch_lse3m_w<4>(grid, st, q, k, p, tiles_per_split, 2.0f * c, eps_ln2, c_next); break;
-        default: launch_lse3m_w<8>(grid, st, q, k, p, tiles_per_split, 2.0f * c, eps_ln2, c_next); break;
-        }
-    } else
+    if (mfma)
+        launch_lse3m(grid, st, q, k, splits > 1 ? part : nullptr, nullptr, tiles_per_split,
+                     2.0f * c, eps_ln2, c_next);
+    else
         hipLaunchKernelGGL(lse3_kernel, grid, dim3(kWaves * kWave), 0, st, q.pts, q.krec,
                            (const float4 *)k.pts, q.pot, (const float *)q.l2w,
                            splits > 1 ? part : nullptr, q.n, q.n_pad, k.n_pad, tiles_per_split,
                            2.0f * c, eps_ln2, c_next);
     if (splits > 1) {
+        int *redo = mfma ? q.redo : nullptr;
         dim3 g2(ceil_div(q.n, 256), B);
         hipLaunchKernelGGL(lse3_finalize, g2, dim3(256), 0, st, q.pts, q.krec, q.pot,
-                           (const float *)q.l2w, (const float2 *)part, B, q.n, q.n_pad, splits,
-                           eps_ln2, c_next);
+                           (const float *)q.l2w, (const float2 *)part, redo, B, q.n, q.n_pad,
+                           splits, eps_ln2, c_next);
+        if (redo)   // rows whose merged sum left the range, with exact shifts over all keys
+            launch_lse3m(dim3(q.n_pad / kWave, 1, B), st, q, k, nullptr, redo, tiles, 2.0f * c,
+                         eps_ln2, c_next);
     }
     return hipGetLastError();
 }

@@ -104,11 +104,27 @@ def test_bf16_point_clouds_match_oracle(scores, B, n, m, eps, iters):
 @pytest.mark.parametrize("scores", ["mfma", "valu"])
 def test_far_from_origin_and_huge_score_range(scores):
     # clouds far from the origin at small eps: scores span thousands of log2
-    # units, so the running maximum is raised many times and the first keys
-    # seen are far below the row maximum
+    # units, so the first pass's shifts are far off and every block takes the
+    # exact-shift pass (the vector path raises its running maximum many times,
+    # and the first keys it sees are far below the row maximum)
     c = workloads.random_case(77, 2, 300, 333, 3, weights="dirichlet", spread=4.0)
     c = dict(c, X=c["X"] + np.float32(10.0), Y=c["Y"] + np.float32(10.0))
     check_potentials(c, [0.003], [5], valu_scores=scores == "valu")
+
+
+@pytest.mark.parametrize("B,n,m,eps,iters", [
+    # a short side against a long key range split across work-groups: on the
+    # first pass every merged row of the f-update is out of range, and the
+    # repair launch recomputes its blocks with exact shifts
+    (1, 300, 20000, [0.003], [5]),
+    # a mid-size pair, both updates split, under a schedule whose eps jumps
+    # leave the shifts of some blocks stale
+    (1, 12000, 11000, [1.0, 0.1, 0.01, 0.003], [2, 2, 2, 3]),
+])
+def test_split_key_ranges_with_stale_shifts(B, n, m, eps, iters):
+    c = workloads.random_case(91 + n, B, n, m, 3, weights="dirichlet", spread=4.0)
+    c = dict(c, X=c["X"] + np.float32(10.0), Y=c["Y"] + np.float32(10.0))
+    check_potentials(c, eps, iters)
 
 
 @pytest.mark.parametrize("n,m", [(1 << 24, 64), (64, 1 << 24)])
