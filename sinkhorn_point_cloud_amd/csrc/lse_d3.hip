@@ -679,8 +679,8 @@ __global__ __launch_bounds__(W *kWave) void lse3m_kernel(
 // Persistent pass per pair, for batches of at least as many pairs as the chip
 // has compute units: one work-group of kPairWaves waves owns one pair and runs
 // every iteration of a stage in one launch.  Each wave takes whole 64-row
-// blocks (all keys, the shifted stream with the lazy-maximum stream as its
-// fallback when a row's sum leaves the range), finishes its rows, and the
+// blocks (all keys, the shifted stream, made exact and streamed again when a
+// row's sum leaves the range), finishes its rows, and the
 // work-group synchronises between the f- and the g-update.  Everything a pass
 // reads from the other side was written by this work-group, so the barrier is
 // the only synchronisation; the per-launch cost of the other path (a launch

@@ -200,7 +200,8 @@ def test_batch_of_many_pairs(scores, B, n, m):
 
 def test_batch_of_many_pairs_from_a_stale_start():
     # warm start from potentials far from the solution: every row block of the
-    # per-pair launch takes the lazy-maximum stream on its first pass
+    # per-pair launch finds its shifts stale on the first pass and makes them
+    # exact (a warm start never skips the first shifted pass)
     c = workloads.random_case(504, 256, 130, 140, 3, weights="uniform")
     X, Y = points(c)
     eps = 0.02
