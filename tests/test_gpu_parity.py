@@ -986,18 +986,29 @@ def test_work_follows_the_callers_stream():
         assert torch.equal(u, v)
 
 
-def test_potentials_replay_from_a_captured_graph():
+@pytest.mark.parametrize("shape", ["batch", "split_keys_stale", "per_pair_stages"])
+def test_potentials_replay_from_a_captured_graph(shape):
     # the potentials entry point launches kernels only (no allocation, copy or
-    # wait), so a caller can capture it; every replay equals the eager result
-    c = workloads.random_case(62, 2, 700, 600, 3, weights="dirichlet")
+    # wait), so a caller can capture it; every replay equals the eager result.
+    # Shapes: one launch per half-iteration; split key ranges whose merged rows
+    # go stale (merge marks and repair launch inside the graph); whole stages
+    # per pair (cold start with exact shifts)
+    if shape == "batch":
+        B, n, m, seed, sched = 2, 700, 600, 62, dict(eps=[0.3, 0.05, 0.02], iters=[3, 5, 10])
+        c = workloads.random_case(seed, B, n, m, 3, weights="dirichlet")
+    elif shape == "split_keys_stale":
+        B, n, m, seed, sched = 1, 300, 20000, 64, dict(eps=[0.05, 0.003], iters=[2, 3])
+        c = workloads.random_case(seed, B, n, m, 3, weights="dirichlet", spread=4.0)
+        c = dict(c, X=c["X"] + np.float32(10.0), Y=c["Y"] + np.float32(10.0))
+    else:
+        B, n, m, seed, sched = 256, 130, 140, 65, dict(eps=[0.1, 0.02], iters=[2, 4])
+        c = workloads.random_case(seed, B, n, m, 3, weights="dirichlet")
     X, Y = points(c)
     a, b = dev(c["a"]), dev(c["b"])
-    B, n, m = 2, 700, 600
     ws = torch.empty(sk.workspace_bytes(sk.SK_OP_POTENTIALS, B, n, m, 3, sk.SK_F32),
                      dtype=torch.uint8, device=X.device)
     out = (torch.empty(B, n, device=X.device), torch.empty(B, m, device=X.device),
            torch.empty(B, device=X.device))
-    sched = dict(eps=[0.3, 0.05, 0.02], iters=[3, 5, 10])
     sk.potentials(X, Y, a, b, out=out, workspace=ws, **sched)
     torch.cuda.synchronize()
     ref = [t.clone() for t in out]
