@@ -80,6 +80,9 @@ SMALL = [  # (B, n, m, weights, zero weights, eps, iters)
     # few rows against long key ranges: the key range is split across work-groups
     (1, 100, 12000, "dirichlet", 0, [0.05, 0.02], [4, 6]),
     (2, 9000, 70, "uniform", 3, [0.03], [8]),
+    # the first 3000 points of each cloud weigh nothing: whole key splits of the
+    # f-update hold only masked keys
+    (1, 3200, 12000, "dirichlet", 3000, [0.05], [5]),
 ]
 
 
