@@ -40,6 +40,8 @@
  *   - Inputs are not scanned for NaN/Inf: NaN in gives NaN out.
  *   - Weights must be >= 0.  A zero weight removes that point from the other
  *     side's log-sum-exp (log 0 = -inf); its own potential stays defined.
+ *     Each cloud of a pair needs at least one positive weight (the weights
+ *     are not scanned: a cloud of zero mass gives meaningless potentials).
  *     a and b may be NULL, meaning uniform weights 1/n and 1/m.
  */
 #ifndef SINKHORN_H
