@@ -124,8 +124,31 @@ __global__ __launch_bounds__(kSegsPerGroup *kWave) void scale_pass(
             return -INFINITY;
         return (double)lv[q] + ob[p];
     };
-    // one pass: each lane keeps (M, S) meaning S e^M over its entries, raising M
-    // when a larger term arrives
+    // Shifted pass: the segment's previous scaling puts its log-sum-exp near
+    // M = lw - out (every scaling starts at 0), so the terms are summed against
+    // that fixed shift, with no maximum per entry.  A sum outside [2^-40, 2^60]
+    // (the shift was stale), a segment of zero weight or an empty one takes
+    // the online form below instead.
+    const double Msh = lw[si] - out[si];
+    if (isfinite(Msh)) {   // wave-uniform
+        double Ssh = 0.0;
+        int64_t q = lo + lane;
+        for (; q + kWave < hi; q += 2 * kWave) {
+            const double z0 = term(q), z1 = term(q + kWave);
+            Ssh += (double)expf((float)(z0 - Msh));
+            Ssh += (double)expf((float)(z1 - Msh));
+        }
+        if (q < hi)
+            Ssh += (double)expf((float)(term(q) - Msh));
+        Ssh = wave_sum(Ssh);
+        if (Ssh >= 0x1p-40 && Ssh <= 0x1p60) {
+            if (lane == 0)
+                out[si] = lw[si] - (Msh + log(Ssh));
+            return;
+        }
+    }
+    // online form: each lane keeps (M, S) meaning S e^M over its entries, raising
+    // M when a larger term arrives
     double M = -INFINITY, S = 0.0;
     auto add = [&](double z) {
         if (z > M) {
@@ -252,7 +275,9 @@ hipError_t launch_coo_normalize(const int32_t *rows, const int32_t *cols, float 
                            w.lvt);
     }
     const size_t cn = (size_t)B * m;
+    const size_t rn = (size_t)B * n;
     hipLaunchKernelGGL(zero_f64, dim3((unsigned)((cn + 255) / 256)), dim3(256), 0, st, w.be, cn);
+    hipLaunchKernelGGL(zero_f64, dim3((unsigned)((rn + 255) / 256)), dim3(256), 0, st, w.al, rn);
     const dim3 gr(ceil_div(n, kSegsPerGroup), B), gc(ceil_div(m, kSegsPerGroup), B);
     const dim3 blk(kSegsPerGroup * kWave);
     for (int it = 0; it < iters; ++it) {
