@@ -58,6 +58,8 @@ def roofline_evals_per_s(d):
 KERNEL_SOURCES = {
     "lse3m_kernel": ("sinkhorn_point_cloud_amd/csrc/lse_d3.hip",
                      "sinkhorn_point_cloud_amd/csrc/common.h"),
+    "lse3p_kernel": ("sinkhorn_point_cloud_amd/csrc/lse_d3.hip",
+                     "sinkhorn_point_cloud_amd/csrc/common.h"),
     "lseFm_kernel": ("sinkhorn_point_cloud_amd/csrc/lse_feat.hip",
                      "sinkhorn_point_cloud_amd/csrc/common.h"),
 }
