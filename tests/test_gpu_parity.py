@@ -226,6 +226,16 @@ def test_schedule_with_empty_stages_and_zero_iterations():
     assert torch.all(f == 0) and torch.all(g == 0)
 
 
+@pytest.mark.parametrize("B,n,m", [(256, 130, 140), (1, 300, 20000)])
+def test_empty_stages_on_per_pair_and_split_launches(B, n, m):
+    # empty stages before, between and after others: the cold start's exact
+    # shifts belong to the first stage that runs, and each stage hands the next
+    # running stage's eps to its last g-update (per-pair stage launches; split
+    # key ranges with merge marks and repair)
+    c = workloads.random_case(506 + B, B, n, m, 3, weights="dirichlet", spread=2.0)
+    check_potentials(c, [1.0, 0.1, 0.05, 0.03, 0.02], [0, 3, 0, 4, 0])
+
+
 def test_translated_clouds_give_the_same_potentials():
     # the cost is translation invariant; the GPU's attention form must stay accurate
     c = workloads.random_case(8, 1, 300, 200, 3, weights="dirichlet")
