@@ -104,6 +104,28 @@ __global__ void log_kernel(const float *__restrict__ vals, int64_t nnz, float *_
 // One scaling update per segment (a row of the plan or a row of the transpose,
 // i.e. a column of the plan): out_s = lw_s - LSE over the segment's entries k
 // of (lv_k + other_{partner_k}).
+// Two segments per wave, kSegLanes lanes each: a row holds a few hundred
+// entries, so the per-segment work (the shift, the reductions, the logarithm)
+// is a large share, and two segments share those instructions.
+constexpr int kSegLanes = 32;
+
+// Sum and maximum over the kSegLanes lanes of a segment (butterfly, fixed order).
+__device__ __forceinline__ double seg_sum(double v)
+{
+#pragma unroll
+    for (int off = kSegLanes / 2; off > 0; off >>= 1)
+        v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+__device__ __forceinline__ double seg_max(double v)
+{
+#pragma unroll
+    for (int off = kSegLanes / 2; off > 0; off >>= 1)
+        v = fmax(v, __shfl_xor(v, off, kWave));
+    return v;
+}
+
 __global__ __launch_bounds__(kSegsPerGroup *kWave) void scale_pass(
     const int64_t *__restrict__ sb, const int64_t *__restrict__ se,
     const int32_t *__restrict__ partner, const float *__restrict__ lv,
@@ -111,10 +133,12 @@ __global__ __launch_bounds__(kSegsPerGroup *kWave) void scale_pass(
     double *__restrict__ out)
 {
     const int b = blockIdx.y;
-    const int s = blockIdx.x * kSegsPerGroup + wave_id_uniform();
-    if (s >= count)
-        return;
     const int lane = lane_id();
+    const int sl = lane % kSegLanes;   // lane within the segment
+    const int s = (blockIdx.x * kSegsPerGroup + wave_id_uniform()) * (kWave / kSegLanes) +
+                  lane / kSegLanes;
+    if (s >= count)
+        return;   // whole segments: the shuffles below stay inside a segment's lanes
     const size_t si = (size_t)b * count + s;
     const int64_t lo = sb[si], hi = se[si];
     const double *ob = other + (size_t)b * other_count;
@@ -130,19 +154,19 @@ __global__ __launch_bounds__(kSegsPerGroup *kWave) void scale_pass(
     // (the shift was stale), a segment of zero weight or an empty one takes
     // the online form below instead.
     const double Msh = lw[si] - out[si];
-    if (isfinite(Msh)) {   // wave-uniform
+    if (isfinite(Msh)) {   // uniform over the segment
         double Ssh = 0.0;
-        int64_t q = lo + lane;
-        for (; q + kWave < hi; q += 2 * kWave) {
-            const double z0 = term(q), z1 = term(q + kWave);
+        int64_t q = lo + sl;
+        for (; q + kSegLanes < hi; q += 2 * kSegLanes) {
+            const double z0 = term(q), z1 = term(q + kSegLanes);
             Ssh += (double)expf((float)(z0 - Msh));
             Ssh += (double)expf((float)(z1 - Msh));
         }
         if (q < hi)
             Ssh += (double)expf((float)(term(q) - Msh));
-        Ssh = wave_sum(Ssh);
+        Ssh = seg_sum(Ssh);
         if (Ssh >= 0x1p-40 && Ssh <= 0x1p60) {
-            if (lane == 0)
+            if (sl == 0)
                 out[si] = lw[si] - (Msh + log(Ssh));
             return;
         }
@@ -159,9 +183,9 @@ __global__ __launch_bounds__(kSegsPerGroup *kWave) void scale_pass(
         }
     };
     // two entries per lane and step (loaded before either is used), in order
-    int64_t q = lo + lane;
-    for (; q + kWave < hi; q += 2 * kWave) {
-        const double z0 = term(q), z1 = term(q + kWave);
+    int64_t q = lo + sl;
+    for (; q + kSegLanes < hi; q += 2 * kSegLanes) {
+        const double z0 = term(q), z1 = term(q + kSegLanes);
         add(z0);
         add(z1);
     }
@@ -169,13 +193,10 @@ __global__ __launch_bounds__(kSegsPerGroup *kWave) void scale_pass(
         add(term(q));
     // merge the lanes: the segment's maximum, each lane's sum rescaled to it once,
     // then one sum (fixed order)
-    double Mw = M;
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1)
-        Mw = fmax(Mw, __shfl_xor(Mw, off, kWave));
+    const double Mw = seg_max(M);
     S = M > -INFINITY ? S * (double)expf((float)(M - Mw)) : 0.0;
-    S = wave_sum(S);
-    if (lane == 0)
+    S = seg_sum(S);
+    if (sl == 0)
         out[si] = Mw > -INFINITY ? lw[si] - (Mw + log(S)) : 0.0;
 }
 
@@ -279,12 +300,14 @@ hipError_t launch_coo_normalize(const int32_t *rows, const int32_t *cols, float 
     hipLaunchKernelGGL(zero_f64, dim3((unsigned)((cn + 255) / 256)), dim3(256), 0, st, w.be, cn);
     hipLaunchKernelGGL(zero_f64, dim3((unsigned)((rn + 255) / 256)), dim3(256), 0, st, w.al, rn);
     const dim3 gr(ceil_div(n, kSegsPerGroup), B), gc(ceil_div(m, kSegsPerGroup), B);
+    constexpr int kScaleSegs = kSegsPerGroup * (kWave / kSegLanes);   // segments per group
+    const dim3 grs(ceil_div(n, kScaleSegs), B), gcs(ceil_div(m, kScaleSegs), B);
     const dim3 blk(kSegsPerGroup * kWave);
     for (int it = 0; it < iters; ++it) {
-        hipLaunchKernelGGL(scale_pass, gr, blk, 0, st, (const int64_t *)w.rb, (const int64_t *)w.re,
+        hipLaunchKernelGGL(scale_pass, grs, blk, 0, st, (const int64_t *)w.rb, (const int64_t *)w.re,
                            cols, (const float *)w.lv, (const double *)w.be, n, m,
                            (const double *)w.la, w.al);
-        hipLaunchKernelGGL(scale_pass, gc, blk, 0, st, (const int64_t *)w.cb, (const int64_t *)w.ce,
+        hipLaunchKernelGGL(scale_pass, gcs, blk, 0, st, (const int64_t *)w.cb, (const int64_t *)w.ce,
                            t_cols, (const float *)w.lvt, (const double *)w.al, m, n,
                            (const double *)w.lb, w.be);
     }
