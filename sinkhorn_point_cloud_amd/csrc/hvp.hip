@@ -27,6 +27,7 @@ namespace sk {
 namespace {
 
 constexpr int kHvpWaves = 4;
+constexpr int kHvpStage = 512;   // d = 3 key-side values staged in LDS per step
 enum : int { F_V = 1, F_U = 2, F_W = 4, F_D = 8 };
 
 // Per row i of p.X against the keys of p.Y:
@@ -62,16 +63,36 @@ __global__ __launch_bounds__(kHvpWaves *kWave) void transport_pass(
 #pragma unroll
     for (int k = 0; k < DP; ++k)
         D1[k] = Du[k] = Tv[k] = 0.0;
-    auto visit = [&](int j) {
+    // d = 3: the key side's values (fp64 record, log weight, u_j, w_j) pass through
+    // LDS a stage at a time and every lane of a wave reads the same key
+    __shared__ KeyD kst[KD ? kHvpStage : 1];
+    __shared__ double lbst[KD ? kHvpStage : 1];
+    __shared__ double ust[KD && (FL & F_U) ? kHvpStage : 1];
+    __shared__ float wst[KD && (FL & F_W) ? 3 * kHvpStage : 1];
+    auto visit = [&](int j, int js) {
         double C, diff[DP];
         KeyVals<DP> kv;
-        load_key<T, DP, KD>(kv, p, Yb, gb, kdb, j);
-        const double lp = log_plan_kv<DP>(r, kv, lbb[j], p.inv_eps, p.d, &C, diff);
+        double lbj;
+        if constexpr (KD) {
+            const KeyD kr = kst[js];
+#pragma unroll
+            for (int k = 0; k < DP; ++k)
+                kv.y[k] = kr.y[k];
+            kv.g = kr.g;
+            lbj = lbst[js];
+        } else {
+            load_key<T, DP, KD>(kv, p, Yb, gb, kdb, j);
+            lbj = lbb[j];
+        }
+        const double lp = log_plan_kv<DP>(r, kv, lbj, p.inv_eps, p.d, &C, diff);
         const double P = (double)ex2((float)(lp * 1.4426950408889634));
         m0 += P;
         double uj = 0.0;
         if (FL & F_U) {
-            uj = u[(size_t)b * p.m + j];
+            if constexpr (KD)
+                uj = ust[js];
+            else
+                uj = u[(size_t)b * p.m + j];
             mu = fma(P, uj, mu);
         }
         if (FL & F_D) {
@@ -93,7 +114,7 @@ __global__ __launch_bounds__(kHvpWaves *kWave) void transport_pass(
                 Tv[k] = fma(P * dv, diff[k], Tv[k]);
         }
         if (FL & F_W) {
-            const float *wj = wk + ((size_t)b * p.m + j) * p.d;
+            const float *wj = KD ? wst + 3 * js : wk + ((size_t)b * p.m + j) * p.d;
             double dw = 0.0;
 #pragma unroll
             for (int k = 0; k < DP; ++k)
@@ -102,19 +123,49 @@ __global__ __launch_bounds__(kHvpWaves *kWave) void transport_pass(
             tw = fma(P, dw, tw);
         }
     };
-    int j = w;
-    if constexpr (DP <= 4) {
-        // four keys per step, so that their loads are in flight together (the
-        // sums still take the keys in order)
-        for (; j + 3 * kHvpWaves < p.m; j += 4 * kHvpWaves) {
-            visit(j);
-            visit(j + kHvpWaves);
-            visit(j + 2 * kHvpWaves);
-            visit(j + 3 * kHvpWaves);
+    if constexpr (KD) {
+        for (int c0 = 0; c0 < p.m; c0 += kHvpStage) {
+            const int kc = min(kHvpStage, p.m - c0);
+            __syncthreads();   // the previous stage is no longer read
+            for (int e = threadIdx.x; e < kc; e += kHvpWaves * kWave) {
+                kst[e] = kdb[c0 + e];
+                lbst[e] = lbb[c0 + e];
+                if constexpr ((FL & F_U) != 0)
+                    ust[e] = u[(size_t)b * p.m + c0 + e];
+                if constexpr ((FL & F_W) != 0) {
+                    const float *wj = wk + ((size_t)b * p.m + c0 + e) * 3;
+                    wst[3 * e] = wj[0];
+                    wst[3 * e + 1] = wj[1];
+                    wst[3 * e + 2] = wj[2];
+                }
+            }
+            __syncthreads();
+            int js = w;
+            // four keys per step; the sums still take the keys in order
+            for (; js + 3 * kHvpWaves < kc; js += 4 * kHvpWaves) {
+                visit(c0 + js, js);
+                visit(c0 + js + kHvpWaves, js + kHvpWaves);
+                visit(c0 + js + 2 * kHvpWaves, js + 2 * kHvpWaves);
+                visit(c0 + js + 3 * kHvpWaves, js + 3 * kHvpWaves);
+            }
+            for (; js < kc; js += kHvpWaves)
+                visit(c0 + js, js);
         }
+    } else {
+        int j = w;
+        if constexpr (DP <= 4) {
+            // four keys per step, so that their loads are in flight together (the
+            // sums still take the keys in order)
+            for (; j + 3 * kHvpWaves < p.m; j += 4 * kHvpWaves) {
+                visit(j, 0);
+                visit(j + kHvpWaves, 0);
+                visit(j + 2 * kHvpWaves, 0);
+                visit(j + 3 * kHvpWaves, 0);
+            }
+        }
+        for (; j < p.m; j += kHvpWaves)
+            visit(j, 0);
     }
-    for (; j < p.m; j += kHvpWaves)
-        visit(j);
     // merge the waves' partial sums in a fixed order, one quantity at a time
     auto merged = [&](double val) {
         __syncthreads();

@@ -50,6 +50,7 @@ __global__ void log_weights_kernel(const float *__restrict__ w, int count, size_
 
 
 constexpr int kTileWaves = 4;   // waves of a tile_pass work-group, splitting the keys
+constexpr int kKeyStage = 512;  // d = 3 key records staged in LDS per step (20 KB)
 constexpr int kGradDims = 16;   // gradient components accumulated per launch (no spills)
 
 // mode 0: cost  (row sum of P C, double)          -> outd[row]
@@ -94,10 +95,21 @@ __global__ __launch_bounds__(kTileWaves *kWave) void tile_pass(
     // and whole-row gradients (one chunk) reuse the evaluation's differences
     constexpr bool kRegs = DP <= kKeyRegDims;
     constexpr bool kDiff = kRegs && MODE == 3 && KC == DP;
-    auto visit = [&](int j) {
+    __shared__ KeyD kst[KD ? kKeyStage : 1];
+    __shared__ double lbst[KD ? kKeyStage : 1];
+    auto visit = [&](int j, int js) {
         double C, lp;
         double diff[kDiff ? DP : 1];
-        if constexpr (kRegs) {
+        if constexpr (KD) {
+            // staged in LDS: every lane of the wave reads the same record
+            const KeyD kr = kst[js];
+            KeyVals<DP> kv;
+#pragma unroll
+            for (int k = 0; k < DP; ++k)
+                kv.y[k] = kr.y[k];
+            kv.g = kr.g;
+            lp = log_plan_kv<DP>(r, kv, lbst[js], p.inv_eps, p.d, &C, kDiff ? diff : nullptr);
+        } else if constexpr (kRegs) {
             KeyVals<DP> kv;
             load_key<T, DP, KD>(kv, p, Yb, gb, kdb, j);
             lp = log_plan_kv<DP>(r, kv, lbb[j], p.inv_eps, p.d, &C, kDiff ? diff : nullptr);
@@ -128,18 +140,40 @@ __global__ __launch_bounds__(kTileWaves *kWave) void tile_pass(
             }
         }
     };
-    int j = w;
-    if constexpr (DP <= 4) {
-        // four keys per step, so that their loads are in flight together
-        for (; j + 3 * kTileWaves < p.m; j += 4 * kTileWaves) {
-            visit(j);
-            visit(j + kTileWaves);
-            visit(j + 2 * kTileWaves);
-            visit(j + 3 * kTileWaves);
+    if constexpr (KD) {
+        // d = 3: the pair's fp64 key records pass through LDS a stage at a time
+        for (int c0 = 0; c0 < p.m; c0 += kKeyStage) {
+            const int kc = min(kKeyStage, p.m - c0);
+            __syncthreads();   // the previous stage is no longer read
+            for (int e = threadIdx.x; e < kc; e += kTileWaves * kWave) {
+                kst[e] = kdb[c0 + e];
+                lbst[e] = lbb[c0 + e];
+            }
+            __syncthreads();
+            int js = w;
+            for (; js + 3 * kTileWaves < kc; js += 4 * kTileWaves) {
+                visit(c0 + js, js);
+                visit(c0 + js + kTileWaves, js + kTileWaves);
+                visit(c0 + js + 2 * kTileWaves, js + 2 * kTileWaves);
+                visit(c0 + js + 3 * kTileWaves, js + 3 * kTileWaves);
+            }
+            for (; js < kc; js += kTileWaves)
+                visit(c0 + js, js);
         }
+    } else {
+        int j = w;
+        if constexpr (DP <= 4) {
+            // four keys per step, so that their loads are in flight together
+            for (; j + 3 * kTileWaves < p.m; j += 4 * kTileWaves) {
+                visit(j, 0);
+                visit(j + kTileWaves, 0);
+                visit(j + 2 * kTileWaves, 0);
+                visit(j + 3 * kTileWaves, 0);
+            }
+        }
+        for (; j < p.m; j += kTileWaves)
+            visit(j, 0);
     }
-    for (; j < p.m; j += kTileWaves)
-        visit(j);
     // merge the waves in a fixed order
     auto merged = [&](double v, bool is_max) {
         __syncthreads();
