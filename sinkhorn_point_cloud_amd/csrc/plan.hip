@@ -21,9 +21,11 @@
 //     dX_i = 2 G_i and T_i = sum_j P_ij y_j / r_i = x_i - G_i / r_i.
 //
 // Two traversals.  Passes that reduce each row to a few numbers (cost, max,
-// count, dense gradient) hold one row per lane, 64 rows per wave, and stream
-// the keys with wave-uniform addresses (scalar loads shared by the lanes);
-// the 4 waves of a work-group take every 4th key and merge in LDS.  The emit
+// count, dense gradient) hold one row per lane, 64 rows per wave, and take the
+// keys one at a time, the same key in every lane: for d = 3 the work-group
+// stages the keys' fp64 records in LDS and the lanes read them with broadcast
+// loads, otherwise they read them with wave-uniform (scalar) loads; the 4
+// waves of a work-group take every 4th key and merge in LDS.  The emit
 // pass holds one row per wave with lanes across 64 consecutive columns, so
 // each wave writes contiguous slices of the COO arrays; for d <= 4 the
 // columns are staged in LDS once per work-group of 32 rows.
@@ -91,7 +93,8 @@ __global__ __launch_bounds__(kTileWaves *kWave) void tile_pass(
             xc[k] = MODE == 3 && has_dim<DP>(k0 + k, p.d) ? (double)Elem<T>::get(x, k0 + k) : 0.0;
         }
     }
-    // narrow points: the key's values in registers (from KeyD records for d = 3),
+    // narrow points: the key's values in registers (from the staged KeyD records
+    // for d = 3),
     // and whole-row gradients (one chunk) reuse the evaluation's differences
     constexpr bool kRegs = DP <= kKeyRegDims;
     constexpr bool kDiff = kRegs && MODE == 3 && KC == DP;

@@ -8,8 +8,9 @@
 // Every pass reads a key (column j) as fp64 values: its point components and
 // g_j, exact conversions of the inputs.  For d = 3 they come precomputed
 // (KeyD, one 32-byte record per key, written by launch_keys_d3), so that a pass
-// whose lanes share the key reads them with scalar loads and spends no vector
-// instruction on conversions; otherwise they are converted where they are read.
+// whose lanes share the key reads them whole (staged in LDS, or with scalar
+// loads) and spends no vector instruction on conversions; otherwise they are
+// converted where they are read.
 // The values, and so every result, are the same either way.
 #pragma once
 #include "common.h"
