@@ -94,8 +94,8 @@ __global__ __launch_bounds__(kTileWaves *kWave) void tile_pass(
         }
     }
     // narrow points: the key's values in registers (from the staged KeyD records
-    // for d = 3),
-    // and whole-row gradients (one chunk) reuse the evaluation's differences
+    // for d = 3), and whole-row gradients (one chunk) reuse the evaluation's
+    // differences
     constexpr bool kRegs = DP <= kKeyRegDims;
     constexpr bool kDiff = kRegs && MODE == 3 && KC == DP;
     __shared__ KeyD kst[KD ? kKeyStage : 1];
