@@ -393,6 +393,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kGroups = 4;        // 16-row groups per wave
+constexpr unsigned kXcds = 8;     // XCDs (each with its own L2) the dispatcher deals to in turn
 
 __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t *p)
 {
@@ -616,13 +617,28 @@ __global__ __launch_bounds__(W *kWave) void lse3m_kernel(
 {
     __shared__ float2 red[W][kWave];
     __shared__ int stale;
-    const int b = blockIdx.z;
-    if (redo && !redo[(size_t)b * (nq_pad / kWave) + blockIdx.x])
+    // XCD-aware placement for batches: the dispatcher deals work-groups to the
+    // XCDs in turn, so the linear id is remapped to give each XCD a contiguous
+    // run of (row block, split, pair) and keep a pair's key records in one L2
+    // (one pair: every XCD needs its keys anyway, and the launch stays as is)
+    int bx = blockIdx.x, split = blockIdx.y, b = blockIdx.z;
+    {
+        const unsigned gx = gridDim.x, gy = gridDim.y;
+        const unsigned total = gx * gy * gridDim.z;   // B n_pad / 64 * splits < 2^31
+        if (gridDim.z > 1 && total % kXcds == 0) {
+            unsigned L = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+            L = (L % kXcds) * (total / kXcds) + L / kXcds;
+            bx = (int)(L % gx);
+            L /= gx;
+            split = (int)(L % gy);
+            b = (int)(L / gy);
+        }
+    }
+    if (redo && !redo[(size_t)b * (nq_pad / kWave) + bx])
         return;   // the whole work-group: this block was finished by the merge
-    const int split = blockIdx.y;
     const int lane = lane_id();
     const int w = wave_id_uniform();
-    const int row0 = blockIdx.x * kWave;
+    const int row0 = bx * kWave;
     const int kq = lane >> 4;      // operand k index this lane supplies / row quad it receives
     const int c16 = lane & 15;     // operand row (A) or column (B) within a 16-block
 
