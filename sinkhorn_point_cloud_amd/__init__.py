@@ -18,7 +18,8 @@ import os
 
 import torch
 
-__all__ = ["SinkhornError", "potentials", "plan_coo", "loss_grad", "workspace_bytes",
+__all__ = ["SinkhornError", "potentials", "plan_coo", "loss_grad",
+           "workspace_bytes",
            "library_path", "load_library"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -31,7 +32,8 @@ SK_OP_POTENTIALS, SK_OP_PLAN_COO, SK_OP_LOSS_GRAD, SK_OP_DENSE_GRAD, SK_OP_HVP =
 SK_WARM_START = 1
 SK_VALU_SCORES = 2
 
-EXPORTS = ("sinkhorn_workspace_bytes", "sinkhorn_potentials", "sinkhorn_plan_coo",
+EXPORTS = ("sinkhorn_workspace_bytes", "sinkhorn_potentials",
+           "sinkhorn_plan_coo",
            "sinkhorn_loss_grad", "sinkhorn_dense_grad", "sinkhorn_hvp",
            "sinkhorn_coo_workspace_bytes",
            "sinkhorn_coo_normalize", "sinkhorn_normalize", "sinkhorn_plan_coo_async",
@@ -133,6 +135,34 @@ def _weights(w, B, k, device):
     return w.reshape(B, k).contiguous()
 
 
+def _check_out(items, dtype, device, what):
+    """Refuses caller-provided output tensors that the C ABI would write out of
+    bounds or with the wrong layout: each (tensor or None, shape) must have that
+    exact shape, the dtype, C-contiguous layout and the device."""
+    for t, shape in items:
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{what}: expected a tensor, got {type(t).__name__}")
+        if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous() \
+                or t.device != device:
+            raise ValueError(f"{what}: need a contiguous {dtype} tensor of shape {tuple(shape)} "
+                             f"on {device}, got {t.dtype} {tuple(t.shape)} "
+                             f"{'contiguous' if t.is_contiguous() else 'strided'} on {t.device}")
+
+
+def _check_plan_out(rows, cols, vals, offs, B, device):
+    """A sparse plan's buffers: rows, cols int32 and vals float32 of one common
+    length (the capacity), offs int64 of B + 1 entries, all contiguous on device."""
+    for t in (rows, cols, vals, offs):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"plan buffers must be tensors, got {type(t).__name__}")
+    cap = rows.numel()
+    _check_out(((rows, (cap,)), (cols, (cap,))), torch.int32, device, "plan rows/cols")
+    _check_out(((vals, (cap,)),), torch.float32, device, "plan vals")
+    _check_out(((offs, (B + 1,)),), torch.int64, device, "plan pair_offsets")
+
+
 def workspace_bytes(op: int, B: int, n: int, m: int, d: int, dtype: int) -> int:
     return int(load_library().sinkhorn_workspace_bytes(op, B, n, m, d, dtype))
 
@@ -167,6 +197,9 @@ def potentials(X, Y, a=None, b=None, eps=(0.05,), iters=(100,), f0=None, g0=None
         raise ValueError("eps and iters need one entry per stage")
     if out is not None:
         f, g, c = out
+        if f is None or g is None:
+            raise ValueError("out needs f and g tensors")
+        _check_out(((f, (B, n)), (g, (B, m)), (c, (B,))), torch.float32, dev, "out")
     else:
         f = torch.empty(B, n, dtype=torch.float32, device=dev)
         g = torch.empty(B, m, dtype=torch.float32, device=dev)
@@ -209,14 +242,11 @@ def plan_coo(X, Y, a, b, f, g, eps: float, rel_threshold: float = 1e-8, capacity
     g = g.reshape(B, m).contiguous().float()
     ws = _workspace(SK_OP_PLAN_COO, B, n, m, d, dt, dev, workspace)
     loss, dX = loss_out if loss_out is not None else (None, None)
-    for t, shape in ((loss, (B,)), (dX, (B, n, d))):
-        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != shape
-                              or not t.is_contiguous() or t.device != dev):
-            raise ValueError(f"loss_out tensors must be contiguous float32 of shape {shape} "
-                             f"on {dev}")
+    _check_out(((loss, (B,)), (dX, (B, n, d))), torch.float32, dev, "loss_out")
     nnz = ctypes.c_int64(0)
     if out is not None:
         rows, cols, vals, offs = out
+        _check_plan_out(rows, cols, vals, offs, B, dev)
         cap = rows.numel()
     else:
         offs = torch.empty(B + 1, dtype=torch.int64, device=dev)
@@ -259,9 +289,14 @@ def plan_coo_async(X, Y, a, b, f, g, eps: float, rel_threshold: float, out, loss
     g = g.reshape(B, m).contiguous().float()
     ws = _workspace(SK_OP_PLAN_COO, B, n, m, d, dt, dev, workspace)
     loss, dX = loss_out if loss_out is not None else (None, None)
+    _check_out(((loss, (B,)), (dX, (B, n, d))), torch.float32, dev, "loss_out")
     rows, cols, vals, offs = out
+    _check_plan_out(rows, cols, vals, offs, B, dev)
+    if rows.numel() < 1:
+        raise ValueError("out needs a capacity of at least one entry")
     if nnz is None:
         nnz = torch.empty(1, dtype=torch.int64, device=dev)
+    _check_out(((nnz, (1,)),), torch.int64, dev, "nnz")
     rc = lib.sinkhorn_plan_coo_async(_ptr(X), _ptr(Y), dt, _ptr(a), _ptr(b), B, n, m, d,
                                      float(eps), _ptr(f), _ptr(g), float(rel_threshold),
                                      rows.numel(), _ptr(rows), _ptr(cols), _ptr(vals), _ptr(offs),
@@ -285,12 +320,17 @@ def loss_grad(X, Y, rows, cols, vals, pair_offsets, grad: bool = True, workspace
     if rows.dtype != torch.int32 or cols.dtype != torch.int32 or vals.dtype != torch.float32 \
             or offs.dtype != torch.int64 or offs.numel() != B + 1:
         raise TypeError("rows/cols int32, vals float32, pair_offsets int64[B+1]")
+    if not (rows.numel() == cols.numel() == vals.numel()):
+        raise ValueError("rows, cols and vals must have the same length (the offsets index them)")
     if rows.numel() == 0:   # the C ABI wants real pointers even for an empty plan
         rows = torch.zeros(1, dtype=torch.int32, device=dev)
         cols = torch.zeros(1, dtype=torch.int32, device=dev)
         vals = torch.zeros(1, dtype=torch.float32, device=dev)
     if out is not None:
         loss, dX = out
+        if loss is None:
+            raise ValueError("out needs a loss tensor")
+        _check_out(((loss, (B,)), (dX, (B, n, d))), torch.float32, dev, "out")
     else:
         loss = torch.empty(B, dtype=torch.float32, device=dev)
         dX = torch.empty(B, n, d, dtype=torch.float32, device=dev) if grad else None
@@ -318,6 +358,8 @@ def dense_grad(X, Y, a, b, f, g, eps: float, sides: str = "xy", workspace=None, 
     g = g.reshape(B, m).contiguous().float()
     if out is not None:
         dX, TX, dY, TY = out
+        _check_out(((dX, (B, n, d)), (TX, (B, n, d)), (dY, (B, m, d)), (TY, (B, m, d))),
+                   torch.float32, dev, "out")
     else:
         def new(k, on):
             return torch.empty(B, k, d, dtype=torch.float32, device=dev) if on else None
@@ -374,6 +416,13 @@ def coo_normalize(plan, transpose, a, b, n, m, iters, err=True, workspace=None):
     t_rows, t_cols, t_vals, t_offs = transpose
     B = offs.numel() - 1
     dev = vals.device
+    # both value arrays are rewritten in place through their pointers: refuse
+    # buffers of the wrong dtype, layout, device or length before the call
+    _check_plan_out(rows, cols, vals, offs, B, dev)
+    _check_plan_out(t_rows, t_cols, t_vals, t_offs, B, dev)
+    for what, o, k in (("plan", offs, rows.numel()), ("transpose", t_offs, t_rows.numel())):
+        if int(o[-1]) > k:   # this call reads the counts back anyway
+            raise ValueError(f"{what}: pair_offsets end at {int(o[-1])}, beyond its {k} entries")
     a, b = _weights(a, B, n, dev), _weights(b, B, m, dev)
     nnz = int(rows.numel())
     if workspace is None:
@@ -406,6 +455,8 @@ def hvp(X, Y, a, b, f, g, eps: float, V, cg_iters: int = 100, workspace=None, ou
     f = f.reshape(B, n).contiguous().float()
     g = g.reshape(B, m).contiguous().float()
     V = V.reshape(B, n, d).contiguous().float()
+    if out is not None:
+        _check_out(((out, (B, n, d)),), torch.float32, dev, "out")
     HV = out if out is not None else torch.empty(B, n, d, dtype=torch.float32, device=dev)
     res = torch.empty(B, dtype=torch.float32, device=dev)
     ws = _workspace(SK_OP_HVP, B, n, m, d, dt, dev, workspace)

@@ -236,3 +236,41 @@ def test_product_package_does_not_reach_the_oracle():
                                      text), fn
     out = os.popen(f"ldd {sk.library_path()}").read()
     assert "oracle" not in out
+
+
+def test_out_buffer_checks_refuse_what_the_abi_would_misuse():
+    # the binding checks every caller-provided output before its pointer reaches
+    # the C ABI: dtype, exact shape, contiguous layout, device
+    import torch
+    cpu = torch.device("cpu")
+    good = torch.zeros(2, 5, dtype=torch.float32)
+    sk._check_out(((good, (2, 5)), (None, (3,))), torch.float32, cpu, "out")
+    bad = [torch.zeros(2, 5, dtype=torch.float64),             # dtype
+           torch.zeros(2, 6, dtype=torch.float32),             # shape
+           torch.zeros(10, dtype=torch.float32),               # same size, wrong shape
+           torch.zeros(5, 2, dtype=torch.float32).t(),         # strided
+           ]
+    for t in bad:
+        with pytest.raises(ValueError):
+            sk._check_out(((t, (2, 5)),), torch.float32, cpu, "out")
+    with pytest.raises(TypeError):
+        sk._check_out(((np.zeros((2, 5), np.float32), (2, 5)),), torch.float32, cpu, "out")
+    with pytest.raises(ValueError):   # wrong device
+        sk._check_out(((good, (2, 5)),), torch.float32, torch.device("meta"), "out")
+
+
+def test_plan_buffer_checks():
+    import torch
+    cpu = torch.device("cpu")
+    i32 = lambda k: torch.zeros(k, dtype=torch.int32)
+    f32 = lambda k: torch.zeros(k, dtype=torch.float32)
+    i64 = lambda k: torch.zeros(k, dtype=torch.int64)
+    sk._check_plan_out(i32(10), i32(10), f32(10), i64(3), 2, cpu)
+    for args in ((i32(10), i32(9), f32(10), i64(3)),        # cols shorter than rows
+                 (i32(10), i32(10), f32(8), i64(3)),        # vals shorter
+                 (i32(10), i32(10), f32(10), i64(2)),       # offsets not B + 1
+                 (i32(10), i64(10), f32(10), i64(3)),       # cols int64
+                 (i32(10), i32(10), i32(10), i64(3)),       # vals int32
+                 (i32(10), i32(10), f32(20)[::2], i64(3))):  # strided vals
+        with pytest.raises(ValueError):
+            sk._check_plan_out(*args, 2, cpu)

@@ -1123,3 +1123,56 @@ def test_forward_and_gradient_replay_from_a_captured_graph():
         torch.cuda.synchronize()
         for t, r in zip(results(), ref):
             assert torch.equal(t, r), f"replay {rep}"
+
+
+def test_binding_refuses_bad_output_buffers_before_the_call():
+    # each public function checks caller-provided outputs (dtype, exact shape,
+    # contiguous layout, device) before a pointer reaches the C ABI; the
+    # refused call leaves the buffers untouched
+    c = workloads.random_case(90, 2, 40, 30, 3)
+    X, Y = points(c)
+    a, b = dev(c["a"]), dev(c["b"])
+    d0 = X.device
+    f, g, _ = sk.potentials(X, Y, a, b, eps=[0.1], iters=[2])
+    torch.cuda.synchronize()
+    sentinel = torch.full((2, 40), 5.0, device=d0)
+    with pytest.raises(ValueError):   # f of the wrong shape
+        sk.potentials(X, Y, a, b, eps=[0.1], iters=[2],
+                      out=(torch.empty(2, 41, device=d0), torch.empty(2, 30, device=d0), None))
+    with pytest.raises(ValueError):   # strided g
+        sk.potentials(X, Y, a, b, eps=[0.1], iters=[2],
+                      out=(sentinel, torch.empty(30, 2, device=d0).t(), None))
+    assert bool((sentinel == 5.0).all())
+    cap = 100
+    with pytest.raises(ValueError):   # cols shorter than rows
+        sk.plan_coo(X, Y, a, b, f, g, 0.1, 1e-8,
+                    out=(torch.empty(cap, dtype=torch.int32, device=d0),
+                         torch.empty(cap - 1, dtype=torch.int32, device=d0),
+                         torch.empty(cap, device=d0), torch.empty(3, dtype=torch.int64, device=d0)))
+    with pytest.raises(ValueError):   # nnz of the wrong dtype
+        sk.plan_coo_async(X, Y, a, b, f, g, 0.1, 1e-8,
+                          out=(torch.empty(cap, dtype=torch.int32, device=d0),
+                               torch.empty(cap, dtype=torch.int32, device=d0),
+                               torch.empty(cap, device=d0),
+                               torch.empty(3, dtype=torch.int64, device=d0)),
+                          nnz=torch.empty(1, dtype=torch.int32, device=d0))
+    with pytest.raises(ValueError):   # loss_out dX of the wrong shape
+        sk.plan_coo(X, Y, a, b, f, g, 0.1, 1e-8,
+                    loss_out=(None, torch.empty(2, 40, 4, device=d0)))
+    rows, cols, vals, offs = sk.plan_coo(X, Y, a, b, f, g, 0.1, 1e-8)
+    with pytest.raises(ValueError):   # float64 loss
+        sk.loss_grad(X, Y, rows, cols, vals, offs,
+                     out=(torch.empty(2, dtype=torch.float64, device=d0), None))
+    with pytest.raises(ValueError):   # vals shorter than rows
+        sk.loss_grad(X, Y, rows, cols, vals[:-1], offs)
+    with pytest.raises(ValueError):   # strided dY
+        sk.dense_grad(X, Y, a, b, f, g, 0.1,
+                      out=(None, None, torch.empty(2, 3, 30, device=d0).transpose(1, 2), None))
+    with pytest.raises(ValueError):   # HV of the wrong shape
+        sk.hvp(X, Y, a, b, f, g, 0.1, torch.zeros(2, 40, 3, device=d0), cg_iters=2,
+               out=torch.empty(2, 40, 2, device=d0))
+    with pytest.raises(ValueError):   # offsets that run past the plan's entries
+        bad_offs = offs.clone()
+        bad_offs[-1] = rows.numel() + 5
+        sk.coo_normalize((rows, cols, vals.clone(), bad_offs), (rows, cols, vals.clone(), offs),
+                         a, b, 40, 30, 2)
