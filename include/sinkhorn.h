@@ -127,6 +127,34 @@ int sinkhorn_potentials(const void *X, const void *Y, int dtype,
                         void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * The same potentials with no workspace argument and no allocation, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  The caller passes inputs
+ * and outputs as for sinkhorn_potentials; the workspace is a device array of
+ * SK_NOALLOC_SCRATCH_BYTES bytes inside the library's code object, one copy per
+ * GPU, held until the process ends.  Its address is resolved once per device,
+ * on that device's first call (the current device; `stream` must belong to
+ * it), so make the first call of each device outside any graph capture.
+ *
+ * Sizes whose workspace (sinkhorn_workspace_bytes(SK_OP_POTENTIALS, ...)) is
+ * above SK_NOALLOC_SCRATCH_BYTES return SK_ERR_WORKSPACE with nothing written
+ * (one pair of 65536 x 65536 points at d = 3 needs about 22 MiB; 256 pairs of
+ * 1024 x 1024, 88 MiB).  The call allocates nothing (no hipMalloc or
+ * allocating library routine) and launches the kernels of sinkhorn_potentials,
+ * with the same results.  All calls on one GPU share its array: two calls that
+ * overlap on one GPU (other streams, other threads) race and give undefined
+ * results, so the caller must serialise them.  The array's contents need no
+ * initialisation and are undefined after a call.
+ */
+#define SK_NOALLOC_SCRATCH_BYTES ((size_t)96 << 20)
+int sinkhorn_potentials_noalloc(const void *X, const void *Y, int dtype,
+                                const float *a, const float *b,
+                                int B, int n, int m, int d,
+                                const float *eps, const int *iters, int n_stages,
+                                unsigned flags, float *f, float *g, float *cost,
+                                void *stream);
+
+/*
  * Thresholded sparse plan in COO form [AP Abstract, Innovation].
  *
  * From potentials f, g at eps (as returned by sinkhorn_potentials), keeps per

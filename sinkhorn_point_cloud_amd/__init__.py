@@ -18,7 +18,7 @@ import os
 
 import torch
 
-__all__ = ["SinkhornError", "potentials", "plan_coo", "loss_grad",
+__all__ = ["SinkhornError", "potentials", "potentials_noalloc", "plan_coo", "loss_grad",
            "workspace_bytes",
            "library_path", "load_library"]
 
@@ -31,8 +31,9 @@ SK_F32, SK_BF16 = 0, 1
 SK_OP_POTENTIALS, SK_OP_PLAN_COO, SK_OP_LOSS_GRAD, SK_OP_DENSE_GRAD, SK_OP_HVP = range(5)
 SK_WARM_START = 1
 SK_VALU_SCORES = 2
+SK_NOALLOC_SCRATCH_BYTES = 96 << 20   # the static scratch of sinkhorn_potentials_noalloc
 
-EXPORTS = ("sinkhorn_workspace_bytes", "sinkhorn_potentials",
+EXPORTS = ("sinkhorn_workspace_bytes", "sinkhorn_potentials", "sinkhorn_potentials_noalloc",
            "sinkhorn_plan_coo",
            "sinkhorn_loss_grad", "sinkhorn_dense_grad", "sinkhorn_hvp",
            "sinkhorn_coo_workspace_bytes",
@@ -68,6 +69,8 @@ def load_library():
     lib.sinkhorn_workspace_bytes.restype = Z
     lib.sinkhorn_potentials.argtypes = [P, P, I, P, P, I, I, I, I, P, P, I, U, P, P, P, P, Z, P]
     lib.sinkhorn_potentials.restype = I
+    lib.sinkhorn_potentials_noalloc.argtypes = [P, P, I, P, P, I, I, I, I, P, P, I, U, P, P, P, P]
+    lib.sinkhorn_potentials_noalloc.restype = I
     lib.sinkhorn_plan_coo.argtypes = [P, P, I, P, P, I, I, I, I, F, P, P, F, L, P, P, P, P, P,
                                       P, P, P, Z, P]
     lib.sinkhorn_plan_coo.restype = I
@@ -219,6 +222,42 @@ def potentials(X, Y, a=None, b=None, eps=(0.05,), iters=(100,), f0=None, g0=None
                                  ws.numel(), _stream())
     _check(rc)
     return f, g, c
+
+
+def potentials_noalloc(X, Y, a, b, eps, iters, out, warm_start: bool = False,
+                       valu_scores: bool = False):
+    """Sinkhorn potentials through sinkhorn_potentials_noalloc: no workspace, nothing
+    allocated.  ``out`` = (f [B,n], g [B,m], cost [B] or None), float32 contiguous
+    tensors on X's device; with ``warm_start`` f and g hold the starting potentials.
+    X, Y, a and b must already be contiguous (float32 weights of [B,n], [B,m] or
+    None), so that no copy is made.  Returns ``out``."""
+    lib = load_library()
+    if X.dim() != 3 or Y.dim() != 3 or not (X.is_contiguous() and Y.is_contiguous()):
+        raise ValueError("X and Y must be contiguous [B,n,d] and [B,m,d] tensors")
+    X, Y, dt = _points(X, Y)
+    B, n, d = X.shape
+    m = Y.shape[1]
+    dev = X.device
+    for w, k, name in ((a, n, "a"), (b, m, "b")):
+        if w is not None and (w.dtype != torch.float32 or w.numel() != B * k
+                              or not w.is_contiguous() or w.device != dev):
+            raise ValueError(f"{name} must be a contiguous float32 tensor of {B * k} entries "
+                             f"on {dev}")
+    f, g, c = out
+    _check_out(((f, (B, n)), (g, (B, m)), (c, (B,))), torch.float32, dev, "out")
+    if f is None or g is None:
+        raise ValueError("out needs f and g")
+    eps_l = [float(e) for e in (eps if hasattr(eps, "__len__") else [eps])]
+    it_l = [int(i) for i in (iters if hasattr(iters, "__len__") else [iters])]
+    if len(eps_l) != len(it_l):
+        raise ValueError("eps and iters need one entry per stage")
+    flags = (SK_WARM_START if warm_start else 0) | (SK_VALU_SCORES if valu_scores else 0)
+    eps_a = (ctypes.c_float * max(1, len(eps_l)))(*eps_l)
+    it_a = (ctypes.c_int * max(1, len(it_l)))(*it_l)
+    _check(lib.sinkhorn_potentials_noalloc(_ptr(X), _ptr(Y), dt, _ptr(a), _ptr(b), B, n, m, d,
+                                           eps_a, it_a, len(eps_l), flags, _ptr(f), _ptr(g),
+                                           _ptr(c), _stream()))
+    return out
 
 
 def plan_coo(X, Y, a, b, f, g, eps: float, rel_threshold: float = 1e-8, capacity=None,

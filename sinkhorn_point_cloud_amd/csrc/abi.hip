@@ -7,6 +7,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 namespace sk {
 namespace {
 
@@ -270,43 +272,11 @@ int check_common(const void *X, const void *Y, int dtype, int B, int n, int m, i
     return SK_OK;
 }
 
-}  // namespace
-}  // namespace sk
-
-using namespace sk;
-
-extern "C" {
-
-size_t sinkhorn_workspace_bytes(int op, int B, int n, int m, int d, int dtype)
+// Argument checks of the potentials entry points (no HIP call).
+int check_potentials(const void *X, const void *Y, int dtype, int B, int n, int m, int d,
+                     const float *eps, const int *iters, int n_stages, unsigned flags,
+                     const float *f, const float *g, const float *cost)
 {
-    if (op < SK_OP_POTENTIALS || op > SK_OP_HVP || !shape_ok(B, n, m, d) ||
-        (op == SK_OP_HVP && d > kMaxHvpDim) ||
-        (dtype != SK_F32 && dtype != SK_BF16) || !supported(dtype, d))
-        return 0;
-    return ws_size(op, B, n, m, d, dtype);
-}
-
-const char *sinkhorn_status_string(int s)
-{
-    switch (s) {
-    case SK_OK: return "ok";
-    case SK_ERR_INVALID_ARG: return "invalid argument";
-    case SK_ERR_UNSUPPORTED: return "unsupported dtype/dimension";
-    case SK_ERR_WORKSPACE: return "workspace missing or too small";
-    case SK_ERR_CAPACITY: return "sparse plan exceeds capacity";
-    case SK_ERR_HIP: return "HIP runtime error";
-    default: return "unknown status";
-    }
-}
-
-const char *sinkhorn_last_error(void) { return g_err; }
-
-int sinkhorn_potentials(const void *X, const void *Y, int dtype, const float *a, const float *b,
-                        int B, int n, int m, int d, const float *eps, const int *iters,
-                        int n_stages, unsigned flags, float *f, float *g, float *cost, void *ws,
-                        size_t ws_bytes, void *stream)
-{
-    g_err[0] = '\0';
     int rc = check_common(X, Y, dtype, B, n, m, d);
     if (rc)
         return rc;
@@ -324,10 +294,14 @@ int sinkhorn_potentials(const void *X, const void *Y, int dtype, const float *a,
     }
     if (cost && n_stages == 0)
         return fail(SK_ERR_INVALID_ARG, "cost needs an eps (n_stages >= 1)");
-    rc = check_ws(ws, ws_bytes, ws_size(SK_OP_POTENTIALS, B, n, m, d, dtype));
-    if (rc)
-        return rc;
+    return SK_OK;
+}
 
+// The eps-annealing driver over a workspace of ws_size(SK_OP_POTENTIALS, ...) bytes.
+int run_potentials(const void *X, const void *Y, int dtype, const float *a, const float *b,
+                   int B, int n, int m, int d, const float *eps, const int *iters, int n_stages,
+                   unsigned flags, float *f, float *g, float *cost, void *ws, void *stream)
+{
     hipStream_t st = (hipStream_t)stream;
     Carve c{(char *)ws};
     PotWs w = carve_potentials(c, B, n, m, d, dtype);
@@ -420,6 +394,121 @@ int sinkhorn_potentials(const void *X, const void *Y, int dtype, const float *a,
             return hip_fail(e, "cost");
     }
     return SK_OK;
+}
+
+// Workspace of sinkhorn_potentials_noalloc: a device array that lives in the
+// library's code object, one copy per GPU the library runs on, held until the
+// process ends.  Host code never uses the name `scratch` as an address (on the
+// host it is only a stand-in for the symbol): the device address of each GPU's
+// copy is resolved once, with that GPU current, and kept in g_scratch.
+constexpr size_t kScratchBytes = SK_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices] = {};
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+// Device address of the current GPU's copy of `scratch`.
+int scratch_address(void *stream, void **out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    if (stream) {
+        hipDevice_t sdev = 0;
+        if ((e = hipStreamGetDevice((hipStream_t)stream, &sdev)) != hipSuccess)
+            return hip_fail(e, "hipStreamGetDevice");
+        if ((int)sdev != dev)
+            return fail(SK_ERR_INVALID_ARG, "stream belongs to device %d, the current device is %d",
+                        (int)sdev, dev);
+    }
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(SK_ERR_UNSUPPORTED, "device index %d beyond %d", dev, kMaxDevices - 1);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *p = nullptr;
+        if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess)
+            return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p)
+            return fail(SK_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return SK_OK;
+}
+
+}  // namespace
+}  // namespace sk
+
+using namespace sk;
+
+extern "C" {
+
+size_t sinkhorn_workspace_bytes(int op, int B, int n, int m, int d, int dtype)
+{
+    if (op < SK_OP_POTENTIALS || op > SK_OP_HVP || !shape_ok(B, n, m, d) ||
+        (op == SK_OP_HVP && d > kMaxHvpDim) ||
+        (dtype != SK_F32 && dtype != SK_BF16) || !supported(dtype, d))
+        return 0;
+    return ws_size(op, B, n, m, d, dtype);
+}
+
+const char *sinkhorn_status_string(int s)
+{
+    switch (s) {
+    case SK_OK: return "ok";
+    case SK_ERR_INVALID_ARG: return "invalid argument";
+    case SK_ERR_UNSUPPORTED: return "unsupported dtype/dimension";
+    case SK_ERR_WORKSPACE: return "workspace missing or too small";
+    case SK_ERR_CAPACITY: return "sparse plan exceeds capacity";
+    case SK_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+const char *sinkhorn_last_error(void) { return g_err; }
+
+int sinkhorn_potentials(const void *X, const void *Y, int dtype, const float *a, const float *b,
+                        int B, int n, int m, int d, const float *eps, const int *iters,
+                        int n_stages, unsigned flags, float *f, float *g, float *cost, void *ws,
+                        size_t ws_bytes, void *stream)
+{
+    g_err[0] = '\0';
+    int rc = check_potentials(X, Y, dtype, B, n, m, d, eps, iters, n_stages, flags, f, g, cost);
+    if (rc)
+        return rc;
+    rc = check_ws(ws, ws_bytes, ws_size(SK_OP_POTENTIALS, B, n, m, d, dtype));
+    if (rc)
+        return rc;
+    return run_potentials(X, Y, dtype, a, b, B, n, m, d, eps, iters, n_stages, flags, f, g, cost,
+                          ws, stream);
+}
+
+int sinkhorn_potentials_noalloc(const void *X, const void *Y, int dtype, const float *a,
+                                const float *b, int B, int n, int m, int d, const float *eps,
+                                const int *iters, int n_stages, unsigned flags, float *f,
+                                float *g, float *cost, void *stream)
+{
+    g_err[0] = '\0';
+    int rc = check_potentials(X, Y, dtype, B, n, m, d, eps, iters, n_stages, flags, f, g, cost);
+    if (rc)
+        return rc;
+    const size_t need = ws_size(SK_OP_POTENTIALS, B, n, m, d, dtype);
+    if (need > kScratchBytes)
+        return fail(SK_ERR_WORKSPACE,
+                    "these sizes need %zu bytes of scratch, the static scratch holds %zu "
+                    "(use sinkhorn_potentials with a workspace)",
+                    need, kScratchBytes);
+    void *ws = nullptr;
+    if ((rc = scratch_address(stream, &ws)))
+        return rc;
+    return run_potentials(X, Y, dtype, a, b, B, n, m, d, eps, iters, n_stages, flags, f, g, cost,
+                          ws, stream);
 }
 
 int sinkhorn_plan_coo(const void *X, const void *Y, int dtype, const float *a, const float *b,

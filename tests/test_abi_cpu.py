@@ -238,6 +238,35 @@ def test_product_package_does_not_reach_the_oracle():
     assert "oracle" not in out
 
 
+def test_noalloc_potentials_rejects_before_any_device_call(lib):
+    # argument checks and the scratch limit come before the first HIP call
+    f = np.full(8, 123.0, dtype=np.float32)
+    g = np.full(9, 456.0, dtype=np.float32)
+    e = (ctypes.c_float * 1)(0.1)
+    it = (ctypes.c_int * 1)(3)
+
+    def call(B=1, n=8, m=9, d=3, dtype=0, X=DUMMY, flags=0):
+        return lib.sinkhorn_potentials_noalloc(X, DUMMY, dtype, None, None, B, n, m, d, e, it,
+                                               1, flags, _host(f), _host(g), None, None)
+
+    assert call(X=None) == sk.SK_ERR_INVALID_ARG
+    assert call(flags=8) == sk.SK_ERR_INVALID_ARG
+    assert call(d=129) == sk.SK_ERR_UNSUPPORTED
+    # 256 pairs of 2048 x 2048: more workspace than the static scratch holds
+    assert lib.sinkhorn_workspace_bytes(0, 256, 2048, 2048, 3, 0) > sk.SK_NOALLOC_SCRATCH_BYTES
+    assert call(B=256, n=2048, m=2048) == sk.SK_ERR_WORKSPACE
+    assert b"static scratch" in lib.sinkhorn_last_error()
+    # one pair of 65536 x 65536 fits
+    assert lib.sinkhorn_workspace_bytes(0, 1, 65536, 65536, 3, 0) <= sk.SK_NOALLOC_SCRATCH_BYTES
+    assert np.all(f == 123.0) and np.all(g == 456.0)
+
+
+def test_header_states_the_noalloc_scratch_size():
+    text = open(HEADER).read()
+    assert "#define SK_NOALLOC_SCRATCH_BYTES ((size_t)96 << 20)" in text
+    assert sk.SK_NOALLOC_SCRATCH_BYTES == 96 << 20
+
+
 def test_out_buffer_checks_refuse_what_the_abi_would_misuse():
     # the binding checks every caller-provided output before its pointer reaches
     # the C ABI: dtype, exact shape, contiguous layout, device
