@@ -282,16 +282,15 @@ __global__ void qrec3_kernel(const float4 *__restrict__ pts, int n_pad, float tw
 }
 
 // Row result: true potential from the (M, S) state, and the bias of this row
-// for the other pass.
-__device__ __forceinline__ void finish_row(float4 *qpts, uint16_t *qkrec, float *qpot,
-                                           const float *ql2w, size_t pt, size_t k, float4 p,
-                                           float M, float S, double eps_ln2, double c_next)
+// for the other pass (lw: the row's log2 weight).
+__device__ __forceinline__ void finish_row(float4 *qpts, uint16_t *qkrec, float *qpot, float lw,
+                                           size_t pt, size_t k, float4 p, float M, float S,
+                                           double eps_ln2, double c_next)
 {
     const float sq = sq3(p.x, p.y, p.z);
     const double lse2 = (double)M + (double)lg2(S);
     const float f = (float)((double)sq - lse2 * eps_ln2);
     qpot[k] = f;
-    const float lw = ql2w[k];
     const float beta = lw == kNeg ? kNeg : bias_of(c_next, f, sq, lw);
     qpts[pt].w = beta;
     store_key_bias(qkrec + pt * kRec, beta);
@@ -370,8 +369,8 @@ __global__ __launch_bounds__(kWaves *kWave) void lse3_kernel(
         return;
     }
     if (row < nq)
-        finish_row(qpts, qkrec, qpot, ql2w, (size_t)b * nq_pad + row, (size_t)b * nq + row, p, M,
-                   S, eps_ln2, c_next);
+        finish_row(qpts, qkrec, qpot, ql2w[(size_t)b * nq + row], (size_t)b * nq_pad + row,
+                   (size_t)b * nq + row, p, M, S, eps_ln2, c_next);
 }
 
 // ---------------------------------------------------------------------------
@@ -432,9 +431,9 @@ constexpr float kSumHi = 1.2676506e30f;     // 2^100
 // register sets take turns, so no operand is copied.  Key operands come through
 // a buffer resource: the tile offset rides in an SGPR (soffset), the lane's
 // offset is a constant VGPR, so there is no vector address arithmetic per tile.
-template <int W, bool kMax>
-__device__ __forceinline__ void key_stream(const bf16x8 (&A)[kGroups], const f32x4 (&Cn)[kGroups],
-                                           f32x4 (&S)[kGroups], const uint16_t *kb, int nk_pad,
+template <int W, bool kMax, int G = kGroups>
+__device__ __forceinline__ void key_stream(const bf16x8 (&A)[G], const f32x4 (&Cn)[G],
+                                           f32x4 (&S)[G], const uint16_t *kb, int nk_pad,
                                            int lane_off, int first, int cnt)
 {
     const int last = first + (cnt > 0 ? cnt - 1 : 0) * W;
@@ -452,18 +451,18 @@ __device__ __forceinline__ void key_stream(const bf16x8 (&A)[kGroups], const f32
     // gmm-64k 1.3% faster).  The per-pair launch (W = 1) keeps the interleaved
     // order: at its 128-register limit the grouped one spills.
     auto tile = [&](const bf16x8 &Bt) {
-        f32x4 D[kGroups];
+        f32x4 D[G];
 #pragma unroll
-        for (int g = 0; g < kGroups; ++g)
+        for (int g = 0; g < G; ++g)
             D[g] = mfma4(A[g], Bt, Cn[g]);
 #pragma unroll
-        for (int g = 0; g < kGroups; ++g)
+        for (int g = 0; g < G; ++g)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 S[g][r] = kMax ? fmaxf(S[g][r], D[g][r]) : S[g][r] + ex2(D[g][r]);
         if constexpr (W > 1) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);   // the MFMAs
-            __builtin_amdgcn_sched_group_barrier(0x002, 32, 0);  // then the vector work
+            __builtin_amdgcn_sched_group_barrier(0x008, G, 0);       // the MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x002, 8 * G, 0);   // then the vector work
         }
     };
     int k = 0;
@@ -492,32 +491,31 @@ __device__ __forceinline__ void key_stream(const bf16x8 (&A)[kGroups], const f32
 // the (M, S) states, M carried as -Cn (+1e30 marks a state that has seen no key
 // yet).  The key operand of the next tile is loaded one tile ahead; the clamped
 // index keeps that load inside the pair's keys on the last tile.
-template <int W>
-__device__ __forceinline__ void shifted_stream(const bf16x8 (&A)[kGroups],
-                                               const f32x4 (&Cn)[kGroups], f32x4 (&S)[kGroups],
-                                               const uint16_t *kb, int nk_pad, int lane_off,
-                                               int first, int cnt)
+template <int W, int G = kGroups>
+__device__ __forceinline__ void shifted_stream(const bf16x8 (&A)[G], const f32x4 (&Cn)[G],
+                                               f32x4 (&S)[G], const uint16_t *kb, int nk_pad,
+                                               int lane_off, int first, int cnt)
 {
-    key_stream<W, false>(A, Cn, S, kb, nk_pad, lane_off, first, cnt);
+    key_stream<W, false, G>(A, Cn, S, kb, nk_pad, lane_off, first, cnt);
 }
 
-// Query operands of a wave's 64 rows.
-__device__ __forceinline__ void load_rows(bf16x8 (&A)[kGroups], const uint16_t *qrec_rows,
-                                          int lane_off)
+// Query operands of a wave's 16 G rows.
+template <int G = kGroups>
+__device__ __forceinline__ void load_rows(bf16x8 (&A)[G], const uint16_t *qrec_rows, int lane_off)
 {
 #pragma unroll
-    for (int g = 0; g < kGroups; ++g)
+    for (int g = 0; g < G; ++g)
         A[g] = load_bf16x8(qrec_rows + (size_t)(16 * g) * kRec + lane_off);
 }
 
 // Their shifts M_i = c (||x_i||^2 - f_i), carried as -M in the accumulator
 // input, and empty sums.
-__device__ __forceinline__ void load_shifts(f32x4 (&Cn)[kGroups], f32x4 (&S)[kGroups],
-                                            const float4 *qrow, const float *qpot_b, int nq,
-                                            int row0, int kq, float c)
+template <int G = kGroups>
+__device__ __forceinline__ void load_shifts(f32x4 (&Cn)[G], f32x4 (&S)[G], const float4 *qrow,
+                                            const float *qpot_b, int nq, int row0, int kq, float c)
 {
 #pragma unroll
-    for (int g = 0; g < kGroups; ++g)
+    for (int g = 0; g < G; ++g)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int lr = 16 * g + 4 * kq + r;
@@ -538,11 +536,12 @@ __device__ __forceinline__ float row16_max(float v)
 }
 
 // Row sums of one wave's states, with the row's shift, into red_w[row].
-__device__ __forceinline__ void wave_sums(const f32x4 (&Cn)[kGroups], const f32x4 (&S)[kGroups],
+template <int G = kGroups>
+__device__ __forceinline__ void wave_sums(const f32x4 (&Cn)[G], const f32x4 (&S)[G],
                                           float2 *red_w, int kq, int c16)
 {
 #pragma unroll
-    for (int g = 0; g < kGroups; ++g)
+    for (int g = 0; g < G; ++g)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const float Sr = row16_sum(S[g][r]);
@@ -555,31 +554,31 @@ __device__ __forceinline__ void wave_sums(const f32x4 (&Cn)[kGroups], const f32x
 // block's keys (each wave its tiles, merged over the W waves through red) is
 // added to every row's M, and S is emptied for the shifted pass that follows.
 // With W > 1 every wave of the work-group must call it.
-template <int W>
-__device__ __forceinline__ void exact_shifts(const bf16x8 (&A)[kGroups], f32x4 (&Cn)[kGroups],
-                                             f32x4 (&S)[kGroups], const uint16_t *kb, int nk_pad,
-                                             int lane_off, int first, int cnt,
-                                             float2 (*red)[kWave], int w, int kq, int c16)
+template <int W, int G = kGroups>
+__device__ __forceinline__ void exact_shifts(const bf16x8 (&A)[G], f32x4 (&Cn)[G], f32x4 (&S)[G],
+                                             const uint16_t *kb, int nk_pad, int lane_off,
+                                             int first, int cnt, float2 (*red)[kWave], int w,
+                                             int kq, int c16)
 {
 #pragma unroll
-    for (int g = 0; g < kGroups; ++g)
+    for (int g = 0; g < G; ++g)
         S[g] = f32x4{kNeg, kNeg, kNeg, kNeg};
-    key_stream<W, true>(A, Cn, S, kb, nk_pad, lane_off, first, cnt);
+    key_stream<W, true, G>(A, Cn, S, kb, nk_pad, lane_off, first, cnt);
 #pragma unroll
-    for (int g = 0; g < kGroups; ++g)
+    for (int g = 0; g < G; ++g)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             S[g][r] = row16_max(S[g][r]);
     if constexpr (W > 1) {
 #pragma unroll
-        for (int g = 0; g < kGroups; ++g)
+        for (int g = 0; g < G; ++g)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 if (c16 == 0)
                     red[w][16 * g + 4 * kq + r].x = S[g][r];
         __syncthreads();
 #pragma unroll
-        for (int g = 0; g < kGroups; ++g)
+        for (int g = 0; g < G; ++g)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int lr = 16 * g + 4 * kq + r;
@@ -592,7 +591,7 @@ __device__ __forceinline__ void exact_shifts(const bf16x8 (&A)[kGroups], f32x4 (
         __syncthreads();   // red is written again by the caller
     }
 #pragma unroll
-    for (int g = 0; g < kGroups; ++g)
+    for (int g = 0; g < G; ++g)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             Cn[g][r] -= S[g][r];
@@ -600,15 +599,17 @@ __device__ __forceinline__ void exact_shifts(const bf16x8 (&A)[kGroups], f32x4 (
         }
 }
 
-// One work-group: 64 query rows of pair b, W waves, key tiles of split
-// blockIdx.y.  Three uses:
+// One work-group: 16 G query rows of pair b (G = 4: one 64-row block; G = 1:
+// 16 rows, for launches with too few 64-row blocks to spread over the chip),
+// W waves, key tiles of split blockIdx.y.  Three uses (the last two with
+// G = 4 only):
 //   part == nullptr, redo == nullptr: all keys; shifted pass, made exact where
 //     a row left the range; finishes the rows.
 //   part != nullptr: the split's keys with the rows' shifts; writes the partial
 //     (M, S) of every row (no range check: the merge checks the whole row).
 //   redo != nullptr (repair, after the merge of split partials): only blocks
 //     marked in redo; exact shifts over all keys, then the shifted pass.
-template <int W>
+template <int W, int G>
 __global__ __launch_bounds__(W *kWave) void lse3m_kernel(
     float4 *__restrict__ qpts, uint16_t *__restrict__ qkrec, const uint16_t *__restrict__ qrec,
     const uint16_t *__restrict__ krec, float *__restrict__ qpot, const float *__restrict__ ql2w,
@@ -636,9 +637,11 @@ __global__ __launch_bounds__(W *kWave) void lse3m_kernel(
     }
     if (redo && !redo[(size_t)b * (nq_pad / kWave) + bx])
         return;   // the whole work-group: this block was finished by the merge
+    static_assert(G == kGroups || G == 1, "a work-group holds 64 or 16 rows");
+    constexpr int R = 16 * G;      // rows of the work-group
     const int lane = lane_id();
     const int w = wave_id_uniform();
-    const int row0 = bx * kWave;
+    const int row0 = bx * R;
     const int kq = lane >> 4;      // operand k index this lane supplies / row quad it receives
     const int c16 = lane & 15;     // operand row (A) or column (B) within a 16-block
 
@@ -651,16 +654,25 @@ __global__ __launch_bounds__(W *kWave) void lse3m_kernel(
     const int t_end = min(t_begin + tiles_per_split, n_tiles);
     const int first = t_begin + w;   // this wave takes tiles first + k W
     const int cnt = first < t_end ? (t_end - first + W - 1) / W : 0;
-    bf16x8 A[kGroups];
-    f32x4 Cn[kGroups], S[kGroups];
-    load_rows(A, qrec_rows, lane_off);
-    load_shifts(Cn, S, qrow, qpot + (size_t)b * nq, nq, row0, kq, 0.5f * two_c);
+    bf16x8 A[G];
+    f32x4 Cn[G], S[G];
+    load_rows<G>(A, qrec_rows, lane_off);
+    load_shifts<G>(Cn, S, qrow, qpot + (size_t)b * nq, nq, row0, kq, 0.5f * two_c);
     const int row = row0 + lane;
+    const bool mine = lane < R && row < nq;   // lane of wave 0 that finishes a row
+    // the finishing lanes fetch their row's point and log2 weight now, off the
+    // path that follows the merge
+    float4 prow = make_float4(0.f, 0.f, 0.f, 0.f);
+    float lw = 0.f;
+    if (w == 0 && mine) {
+        prow = qpts[(size_t)b * nq_pad + row];
+        lw = ql2w[(size_t)b * nq + row];
+    }
 
     if (redo == nullptr) {
-        shifted_stream<W>(A, Cn, S, kb, nk_pad, lane_off, first, cnt);
+        shifted_stream<W, G>(A, Cn, S, kb, nk_pad, lane_off, first, cnt);
         // every partial of a row has the same shift: the merge is a sum
-        wave_sums(Cn, S, red[w], kq, c16);
+        wave_sums<G>(Cn, S, red[w], kq, c16);
         if (threadIdx.x == 0)
             stale = 0;
         __syncthreads();
@@ -672,33 +684,32 @@ __global__ __launch_bounds__(W *kWave) void lse3m_kernel(
                 Ssum += red[v][lane].y;
             if (part)
                 part[((size_t)split * gridDim.z + b) * nq_pad + row] = make_float2(M, Ssum);
-            else if (row < nq && !(Ssum >= kSumLo && Ssum <= kSumHi))
+            else if (mine && !(Ssum >= kSumLo && Ssum <= kSumHi))
                 stale = 1;   // benign race: every writer stores 1 (padding rows never do)
         }
         if (part)
             return;
         __syncthreads();
         if (!stale) {
-            if (w == 0 && row < nq)
-                finish_row(qpts, qkrec, qpot, ql2w, (size_t)b * nq_pad + row,
-                           (size_t)b * nq + row, qpts[(size_t)b * nq_pad + row], M, Ssum,
-                           eps_ln2, c_next);
+            if (w == 0 && mine)
+                finish_row(qpts, qkrec, qpot, lw, (size_t)b * nq_pad + row, (size_t)b * nq + row,
+                           prow, M, Ssum, eps_ln2, c_next);
             return;
         }
     }
 
-    exact_shifts<W>(A, Cn, S, kb, nk_pad, lane_off, first, cnt, red, w, kq, c16);
-    shifted_stream<W>(A, Cn, S, kb, nk_pad, lane_off, first, cnt);
-    wave_sums(Cn, S, red[w], kq, c16);
+    exact_shifts<W, G>(A, Cn, S, kb, nk_pad, lane_off, first, cnt, red, w, kq, c16);
+    shifted_stream<W, G>(A, Cn, S, kb, nk_pad, lane_off, first, cnt);
+    wave_sums<G>(Cn, S, red[w], kq, c16);
     __syncthreads();
-    if (w != 0 || row >= nq)
+    if (w != 0 || !mine)
         return;
     float Ssum = 0.f;
 #pragma unroll
     for (int v = 0; v < W; ++v)
         Ssum += red[v][lane].y;
-    finish_row(qpts, qkrec, qpot, ql2w, (size_t)b * nq_pad + row, (size_t)b * nq + row,
-               qpts[(size_t)b * nq_pad + row], red[0][lane].x, Ssum, eps_ln2, c_next);
+    finish_row(qpts, qkrec, qpot, lw, (size_t)b * nq_pad + row, (size_t)b * nq + row, prow,
+               red[0][lane].x, Ssum, eps_ln2, c_next);
 }
 
 // ---------------------------------------------------------------------------
@@ -711,7 +722,7 @@ __global__ __launch_bounds__(W *kWave) void lse3m_kernel(
 // reads from the other side was written by this work-group, so the barrier is
 // the only synchronisation; the per-launch cost of the other path (a launch
 // and the fill and drain of the chip for every half-iteration) is paid once
-// per stage.  The arithmetic per row is that of lse3m_kernel<1>.
+// per stage.  The arithmetic per row is that of lse3m_kernel<1, 4>.
 constexpr int kPairWaves = 16;
 
 // One wave: rows row0 .. row0 + 63 of pair b on side q against all keys of side k.
@@ -755,8 +766,9 @@ __device__ __forceinline__ void wave_rows(const Side3 &q, const Side3 &k, int b,
         Sf = red[lane].y;
     }
     if (row < q.n)
-        finish_row(q.pts, q.krec, q.pot, q.l2w, (size_t)b * q.n_pad + row, (size_t)b * q.n + row,
-                   q.pts[(size_t)b * q.n_pad + row], M, Sf, eps_ln2, c_next);
+        finish_row(q.pts, q.krec, q.pot, q.l2w[(size_t)b * q.n + row], (size_t)b * q.n_pad + row,
+                   (size_t)b * q.n + row, q.pts[(size_t)b * q.n_pad + row], M, Sf, eps_ln2,
+                   c_next);
     __builtin_amdgcn_wave_barrier();   // red is reused by the next block
 }
 
@@ -804,8 +816,8 @@ __global__ void lse3_finalize(float4 *__restrict__ qpts, uint16_t *__restrict__ 
         bad = redo && !(S >= kSumLo && S <= kSumHi);
         const size_t pt = (size_t)b * nq_pad + row;
         if (!bad)
-            finish_row(qpts, qkrec, qpot, ql2w, pt, (size_t)b * nq + row, qpts[pt], M, S,
-                       eps_ln2, c_next);
+            finish_row(qpts, qkrec, qpot, ql2w[(size_t)b * nq + row], pt, (size_t)b * nq + row,
+                       qpts[pt], M, S, eps_ln2, c_next);
     }
     if (redo) {
         const bool any = __ballot(bad) != 0;
@@ -850,25 +862,42 @@ int lse3m_waves(long groups, int tiles_per_split)
     return w;
 }
 
-template <int W>
+// A launch of fewer 64-row blocks than a quarter of the compute units (a single
+// small pair: 16 blocks for 1024 points) uses 16-row work-groups of
+// kSmallWaves waves instead, four times as many, so that more compute units
+// share the pass; every wave keeps at least 2 tiles.
+constexpr int kSmallWaves = 8;
+bool lse3m_small(long groups, int tiles_per_split)
+{
+    return groups * 4 <= 256 && tiles_per_split >= 2 * kSmallWaves;
+}
+
+template <int W, int G>
 void launch_lse3m_w(dim3 grid, hipStream_t st, Side3 q, Side3 k, float2 *part, const int *redo,
                     int tiles_per_split, float two_c, double eps_ln2, double c_next)
 {
-    hipLaunchKernelGGL(lse3m_kernel<W>, grid, dim3(W * kWave), 0, st, q.pts, q.krec,
+    hipLaunchKernelGGL((lse3m_kernel<W, G>), grid, dim3(W * kWave), 0, st, q.pts, q.krec,
                        (const uint16_t *)q.qrec, (const uint16_t *)k.krec, q.pot,
                        (const float *)q.l2w, part, redo, q.n, q.n_pad, k.n_pad, tiles_per_split,
                        two_c, eps_ln2, c_next);
 }
 
+// grid.x counts 64-row blocks; with 16-row work-groups it is multiplied by 4
 void launch_lse3m(dim3 grid, hipStream_t st, Side3 q, Side3 k, float2 *part, const int *redo,
                   int tiles_per_split, float two_c, double eps_ln2, double c_next)
 {
     const long groups = (long)grid.x * grid.y * grid.z;
+    if (!part && !redo && lse3m_small(groups, tiles_per_split)) {
+        const dim3 g16(grid.x * 4, grid.y, grid.z);
+        launch_lse3m_w<kSmallWaves, 1>(g16, st, q, k, part, redo, tiles_per_split, two_c,
+                                        eps_ln2, c_next);
+        return;
+    }
     switch (lse3m_waves(groups, tiles_per_split)) {
-    case 1: launch_lse3m_w<1>(grid, st, q, k, part, redo, tiles_per_split, two_c, eps_ln2, c_next); break;
-    case 2: launch_lse3m_w<2>(grid, st, q, k, part, redo, tiles_per_split, two_c, eps_ln2, c_next); break;
-    case 4: launch_lse3m_w<4>(grid, st, q, k, part, redo, tiles_per_split, two_c, eps_ln2, c_next); break;
-    default: launch_lse3m_w<8>(grid, st, q, k, part, redo, tiles_per_split, two_c, eps_ln2, c_next); break;
+    case 1: launch_lse3m_w<1, kGroups>(grid, st, q, k, part, redo, tiles_per_split, two_c, eps_ln2, c_next); break;
+    case 2: launch_lse3m_w<2, kGroups>(grid, st, q, k, part, redo, tiles_per_split, two_c, eps_ln2, c_next); break;
+    case 4: launch_lse3m_w<4, kGroups>(grid, st, q, k, part, redo, tiles_per_split, two_c, eps_ln2, c_next); break;
+    default: launch_lse3m_w<8, kGroups>(grid, st, q, k, part, redo, tiles_per_split, two_c, eps_ln2, c_next); break;
     }
 }
 }  // namespace
