@@ -13,9 +13,14 @@ blobs-1k), the thresholded COO plan and the loss and dL/dX computed from it.  Pr
              the workload's schedule minus the same call with every iteration
              count 0, divided by the launches the iterations make -- one per
              half-iteration, or one per stage for the per-pair launch), against
-             the exp/FP32 ALU roofline of the chip (matrix cores for bf16 features)
-  cpu_baseline  the fp64 oracle timed on one full iteration of the same
-             problem on this host's cores, scaled to updates per second.
+             the chip's exp issue bound (one exponential per entry; the d = 3
+             scores run on the matrix cores) or, for bf16 features, the matrix
+             cores; beside it the metric's min(FP32, exp) roofline and the
+             kernel's own instruction-issue floor
+  cpu_baseline  the fp64 oracle timed on two full iterations of the same
+             problem on this host's cores, scaled to updates per second, with
+             the cached time of the oracle's full run.
+  --rates    adds the chip's measured instruction rates and clock (probe kernels).
 """
 from __future__ import annotations
 
@@ -30,28 +35,56 @@ sys.path.insert(0, ROOT)
 
 # MI355X (gfx950) unit counts and clock
 N_CU = 256
+N_SIMD = 4 * N_CU
 CLOCK_HZ = 2.4e9
 FP32_VECTOR_PEAK = 157.3e12        # flop/s (packed FP32 FMA)
-FLOPS_PER_EVAL_D3 = 9              # 3 mul + 3 add (score with bias) + max, subtract, accumulate
-EXP_LANES_PER_CLK_CU = 32          # v_exp_f32 issues at half the FMA rate (measured ~28.5)
-
-
 BF16_MFMA_PEAK = 2.5e15            # flop/s, dense
-VECTOR_FLOPS_PER_EVAL_FEAT = 3     # per evaluation beside the dot product: bias fma + accumulate
+FLOPS_PER_EVAL_D3 = 9              # 3 mul + 3 add (score with bias) + max, subtract, accumulate
+# Issue cost, in SIMD cycles, of one wave64 instruction (rates probe, profiles/rates_mi355x.md:
+# v_exp_f32 at 32 lanes per compute unit per clock, v_add/v_fma_f32 at 64, an MFMA takes
+# 4 cycles of the issue port and 16 of the matrix core for 16x16x32 bf16)
+EXP_LANES_PER_CLK_CU = 32
+CYC_EXP, CYC_VALU, CYC_MFMA_ISSUE = 8, 4, 4
+
+# Instructions per wave per 16-key tile (64 rows x 16 keys = 1024 entries) of each
+# streaming kernel: (MFMAs, exponentials, other vector instructions)
+TILE_MIX = {
+    "lse3m_kernel": (4, 16, 16),       # score + bias on the matrix cores; exp, add
+    "lse3p_kernel": (4, 16, 16),
+    "lse3_kernel": (0, 16, 16 * 4),    # vector scores: 3 fma + add per entry (lazy max aside)
+    "lseFm_kernel": (8, 16, 32),       # two 32-dim MFMAs per group; scale-and-bias fma, add
+    "lseF_kernel": (0, 16, 16 * 66),   # vector dot products of 64 dims
+}
 
 
-def roofline_evals_per_s(d):
-    """(peak, bound, fp32/vector bound, exp bound, matrix bound) in evaluations/s.
-    d = 3: min(FP32 vector / 9 flops, exp).  Feature clouds: the dot product's
-    2d flops on bf16 MFMA, the bias fma and accumulation on FP32 vector, exp."""
+def issue_floor_evals_per_s(kernel):
+    """Entry evaluations per second if every SIMD issued the kernel's tile mix
+    back to back at the nominal clock (the kernel's own instruction-issue bound)."""
+    mfma, exp, other = TILE_MIX[kernel]
+    cycles = mfma * CYC_MFMA_ISSUE + exp * CYC_EXP + other * CYC_VALU
+    return N_SIMD * CLOCK_HZ * 1024 / cycles
+
+
+def roofline_evals_per_s(d, kernel):
+    """(peak, bound, basis, algorithmic min(FP32, exp) bound) in evaluations/s.
+    Every entry needs one exponential, so the exp issue rate bounds every design:
+    256 CUs x 32 lanes x 2.4 GHz.  d = 3 with scores on the matrix cores: the vector
+    ALUs keep only the exponential and the accumulation, so the exp bound is the peak
+    (the 9 FP32 flops of the algorithmic count run on the matrix cores).  d = 3 with
+    vector scores: min(FP32 vector / 9 flops, exp).  bf16 features: min(MFMA dense
+    bf16 / 2d flops, exp)."""
     exp = N_CU * CLOCK_HZ * EXP_LANES_PER_CLK_CU
+    fp32 = FP32_VECTOR_PEAK / FLOPS_PER_EVAL_D3
+    algo = min(fp32, exp)
+    if d == 3 and kernel in ("lse3m_kernel", "lse3p_kernel"):
+        return exp, "alu", ("exp issue: 256 CUs x 32 v_exp_f32 lanes/clk x 2.4 GHz, one exp per "
+                            "entry (score and bias on the matrix cores)"), algo
     if d == 3:
-        fp32 = FP32_VECTOR_PEAK / FLOPS_PER_EVAL_D3
-        return min(fp32, exp), "alu", fp32, exp, None
-    fp32 = FP32_VECTOR_PEAK / VECTOR_FLOPS_PER_EVAL_FEAT
+        return algo, "alu", "min(FP32 157.3 TFLOP/s / 9 flops, exp issue)", algo
     mfma = BF16_MFMA_PEAK / (2 * d)
-    peak = min(fp32, exp, mfma)
-    return peak, "mfma" if peak == mfma else "alu", fp32, exp, mfma
+    peak = min(mfma, exp)
+    return peak, "mfma" if peak == mfma else "alu", (
+        f"min(bf16 MFMA 2.5 PFLOP/s / {2 * d} flops, exp issue)"), algo
 
 
 # sources whose change invalidates a kernel's committed traffic counters
@@ -90,6 +123,72 @@ def measured_traffic(kernel, workload, sources):
     return None
 
 
+PROBE_KINDS = (  # kind: (name, per wave per iteration: {instruction: count})
+    (0, "exp", {"v_exp_f32": 16}),
+    (1, "fma", {"v_fma_f32": 16}),
+    (2, "exp_add", {"v_exp_f32": 16, "v_add_f32": 16}),
+    (3, "mfma", {"v_mfma_f32_16x16x32_bf16": 4}),
+    (4, "d3_tile", {"v_mfma_f32_16x16x32_bf16": 4, "v_exp_f32": 16, "v_add_f32": 16}),
+    (5, "fma_f64", {"v_fma_f64": 16}),
+    (6, "feature_tile", {"v_mfma_f32_16x16x32_bf16": 8, "v_fma_f32": 16, "v_exp_f32": 16,
+                         "v_add_f32": 16}),
+    (7, "mfma32", {"v_mfma_f32_32x32x16_bf16": 2}),
+    (8, "feature_tile_32x32", {"v_mfma_f32_32x32x16_bf16": 4, "v_fma_f32": 16, "v_exp_f32": 16,
+                               "v_add_f32": 16}),
+)
+
+
+def measure_rates(dev, blocks_per_cu=8, target_s=0.02):
+    """Instruction rates of the chip from the library's probe kernels: per mix, the
+    shader clock under load (core-clock counter over the constant-rate wall clock)
+    and the rate per compute unit per clock of each instruction it issues."""
+    import ctypes
+
+    import torch
+
+    import sinkhorn_point_cloud_amd as sk
+
+    lib = sk.load_library()
+    lib.sinkhorn_probe_rates.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_void_p]
+    lib.sinkhorn_probe_rates.restype = ctypes.c_int
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    blocks = cus * blocks_per_cu
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    clocks = torch.empty(blocks * 4, dtype=torch.int64, device=dev)
+    hz = ctypes.c_double(0.0)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    out = {"compute_units": cus, "work_groups": blocks, "waves_per_simd": blocks_per_cu}
+
+    def run(kind, iters):
+        rc = lib.sinkhorn_probe_rates(kind, blocks, iters, ctypes.c_void_p(sink.data_ptr()),
+                                      ctypes.c_void_p(clocks.data_ptr()), ctypes.byref(hz),
+                                      stream)
+        assert rc == 0, f"rate probe {kind}: status {rc}"
+        torch.cuda.synchronize()
+        c = clocks.view(blocks, 4).cpu().numpy().astype("float64")
+        wall = (c[:, 3].max() - c[:, 2].min()) / hz.value     # first start to last end
+        sclk = (c[:, 1] - c[:, 0]).sum() / (c[:, 3] - c[:, 2]).sum() * hz.value
+        return wall, sclk
+
+    for kind, name, mix in PROBE_KINDS:
+        iters = 256
+        run(kind, iters)
+        wall, _ = run(kind, iters)
+        iters = max(256, int(iters * target_s / max(wall, 1e-6)))
+        wall, sclk = run(kind, iters)
+        waves = blocks * 4
+        rec = {"iters": iters, "seconds": wall, "sclk_ghz": sclk / 1e9}
+        for ins, cnt in mix.items():
+            per_cu_clk = waves * iters * cnt * 64 / (wall * sclk * cus)   # lanes
+            rec[ins + "_lanes_per_clk_cu"] = per_cu_clk
+        cycles = wall * sclk * cus * 4 / (waves * iters)   # SIMD cycles per wave-iteration
+        rec["simd_cycles_per_wave_iteration"] = cycles
+        out[name] = rec
+    return out
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -99,14 +198,34 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--valu-scores", action="store_true",
                    help="d = 3: form scores on the vector ALUs (comparison)")
+    p.add_argument("--graph", action="store_true",
+                   help="capture one step in a HIP graph and time its replays (the remedy for "
+                        "launch-bound shapes; the potentials after the timed replays are "
+                        "checked against an eager step)")
+    p.add_argument("--rates", action="store_true",
+                   help="also measure the chip's instruction rates with the library's probe "
+                        "kernels (exp, FMA, MFMA, the d = 3 tile mix, fp64 FMA) and the clock")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 256 MiB device copy, so that HBM byte counters of "
                         "a profiler run can be scaled by a kernel of known traffic")
     return p.parse_args()
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(w, iters=2):
-    """Oracle (as it stands) on `iters` full iterations of the workload at its final eps."""
+    """Oracle (as it stands) on `iters` full iterations of the workload at its final eps,
+    beside the cached time of the oracle's full run of the same workload (written by
+    tests/golden/make_golden.py, on the host and thread count stored with it)."""
     import numpy as np
     import oracle
 
@@ -115,11 +234,21 @@ def cpu_baseline(w, iters=2):
     t0 = time.perf_counter()
     oracle.potentials(X, Y, a, b, eps=[float(w["eps"][-1])], iters=[iters])
     dt = time.perf_counter() - t0
-    return {"value": B * n * m * iters / dt, "unit": "updates/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"{iters} full iterations (f- and g-updates, {2 * iters * B * n * m:.3g} "
-                      f"entry evaluations) of {w['name']} at eps={float(w['eps'][-1]):g}, fp64, "
-                      f"{dt:.2f} s"}
+    out = {"value": B * n * m * iters / dt, "unit": "updates/s", "cores": oracle.num_threads(),
+           "kind": "oracle", "cpu_model": cpu_model(),
+           "logical_cpus_visible": len(os.sched_getaffinity(0)),
+           "sample": f"{iters} full iterations (f- and g-updates, {2 * iters * B * n * m:.3g} "
+                     f"entry evaluations) of {w['name']} at eps={float(w['eps'][-1]):g}, fp64, "
+                     f"{dt:.2f} s (extrapolated rate)"}
+    gold = os.path.join(ROOT, "tests", "golden", f"{w['name']}.npz")
+    if os.path.exists(gold):
+        z = np.load(gold)
+        total = B * n * m * int(np.sum(w["iters"]))
+        out["cached_full_run"] = {"seconds": float(z["seconds"]), "threads": int(z["threads"]),
+                                  "value": total / float(z["seconds"]), "unit": "updates/s",
+                                  "note": "the oracle's full schedule, timed once when the "
+                                          "expected values were written (build container)"}
+    return out
 
 
 def main():
@@ -202,10 +331,26 @@ def main():
             k += 1
             torch.cuda.synchronize()
 
-    warm(step, args.warmup, 0.25)
+    run_step = step
+    if args.graph:
+        # one eager step for reference, then the same step captured once and replayed
+        warm(step, 1, 0.0)
+        ref = [t.clone() for t in (f, g)]
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                step()
+        torch.cuda.synchronize()
+        run_step = graph.replay
+    warm(run_step, args.warmup, 0.25)
     t0 = time.perf_counter()
-    t_step = timed(step, args.steps)
+    t_step = timed(run_step, args.steps)
     wall = time.perf_counter() - t0
+    if args.graph:
+        for t, r in zip((f, g), ref):
+            assert torch.equal(t, r), "graph replay differs from the eager step"
     assert torch.isfinite(f).all() and torch.isfinite(g).all()
     assert sparse or torch.isfinite(cost).all()
     assert not sparse or int(nnz_dev) <= coo[0].numel(), "plan outgrew its buffers"
@@ -241,8 +386,8 @@ def main():
     t_launch = t_iterations / launches
     evals_per_launch = 2 * B * n * m * total_iters / launches
     achieved = evals_per_launch / t_launch
-    peak, bound, fp32_bound, exp_bound, mfma_bound = roofline_evals_per_s(d)
-    serial = 1.0 / (1.0 / fp32_bound + 1.0 / exp_bound)
+    peak, bound, basis, algo = roofline_evals_per_s(d, kernel)
+    floor = issue_floor_evals_per_s(kernel)
 
     updates = B * n * m * total_iters
     line = {
@@ -261,6 +406,7 @@ def main():
         "config": {"workload": w["name"], "B": B, "n": n, "m": m, "d": d,
                    "eps": f"{eps[0]:g}->{eps[-1]:g} over {len(eps)} stage(s)",
                    "iters": total_iters,
+                   "launch": "hip graph replay of the step" if args.graph else "eager",
                    "outputs": ("potentials, COO plan at %g x max P per pair, loss and dL/dX"
                                % w["threshold"]) if sparse
                    else "potentials f, g and transport cost",
@@ -275,8 +421,13 @@ def main():
                                          % (total_iters // launches) if pairwise
                                          else " (one launch: a half-iteration)"),
                      "launch_ms": t_launch * 1e3, "evals_per_launch": evals_per_launch,
-                     "serial_exp_fp32_peak": serial / 1e12,
-                     "frac_of_serial_peak": achieved / serial},
+                     "peak_basis": basis,
+                     # the metric's exp/FP32 roofline: min(FP32 vector / 9 flops, exp issue)
+                     "exp_fp32_roofline": algo / 1e12, "frac_of_exp_fp32_roofline": achieved / algo,
+                     # the kernel's own instruction-issue bound: its per-tile mix of MFMAs,
+                     # exponentials and other vector instructions issued back to back
+                     "issue_floor": floor / 1e12, "frac_of_issue_floor": achieved / floor,
+                     "tile_mix_mfma_exp_other": list(TILE_MIX[kernel])},
         "phases_ms": {"step": t_step * 1e3, "iterations": t_iterations * 1e3,
                       ("pack_plan_and_loss" if sparse else "pack_and_cost_pass"):
                       (t_step - t_iterations) * 1e3},
@@ -336,6 +487,8 @@ def main():
             t_hv = timed(hvp, 1)
             assert bool(torch.isfinite(HV).all())
             line["phases_ms"]["hvp_20_cg_steps"] = t_hv * 1e3
+    if args.rates:
+        line["measured_rates"] = measure_rates(dev)
     if args.copy_calibration:
         src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)

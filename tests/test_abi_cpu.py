@@ -15,6 +15,7 @@ import sinkhorn_point_cloud_amd as sk
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "sinkhorn.h")
+PROBE_HEADER = os.path.join(ROOT, "include", "sinkhorn_probe.h")
 
 
 @pytest.fixture(scope="module")
@@ -303,3 +304,21 @@ def test_plan_buffer_checks():
                  (i32(10), i32(10), f32(20)[::2], i64(3))):  # strided vals
         with pytest.raises(ValueError):
             sk._check_plan_out(*args, 2, cpu)
+
+
+def test_rate_probe_is_declared_exported_and_checks_arguments(lib):
+    text = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
+    assert re.findall(r"\b(sinkhorn_\w+)\s*\(", text) == ["sinkhorn_probe_rates"]
+    out = os.popen(f"nm -D --defined-only {sk.library_path()}").read()
+    assert re.search(r"\bT sinkhorn_probe_rates$", out, flags=re.M)
+    f = lib.sinkhorn_probe_rates
+    f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_void_p]
+    hz = ctypes.c_double(0.0)
+    # argument checks come before any device call
+    assert f(9, 8, 10, DUMMY, DUMMY, ctypes.byref(hz), None) == 1
+    assert f(-1, 8, 10, DUMMY, DUMMY, ctypes.byref(hz), None) == 1
+    assert f(0, 0, 10, DUMMY, DUMMY, ctypes.byref(hz), None) == 1
+    assert f(0, 8, 0, DUMMY, DUMMY, ctypes.byref(hz), None) == 1
+    assert f(0, 8, 10, None, DUMMY, ctypes.byref(hz), None) == 1
+    assert f(0, 8, 10, DUMMY, DUMMY, None, None) == 1
