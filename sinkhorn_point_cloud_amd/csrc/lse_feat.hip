@@ -1,5 +1,6 @@
 // lse_feat.hip -- fused streaming half-iteration for feature clouds of
-// dimension d <= 128 (fp32 or bf16 points), computed on the vector ALUs.
+// dimension d <= 128 (fp32 or bf16 points): a vector-ALU kernel for any such d,
+// and, for bf16 points with d a multiple of 32, a matrix-core kernel (below).
 //
 // Same update as lse_d3.hip (FlashSinkhorn summary, Methodologie 1,
 // Propositie 1; streaming per Methodologie 2), in base 2:
@@ -8,8 +9,8 @@
 // with beta in a separate bias array and the true potentials as the state
 // (row results and biases formed in fp64 and rounded once).
 //
-// Each lane owns one query row, held in registers as fp32.  A work-group of
-// 4 waves shares 64 rows; per step the group stages 4 tiles of kKeys keys in
+// Vector kernel: each lane owns one query row, held in registers as fp32.  A
+// work-group of 4 waves shares 64 rows; per step the group stages 4 tiles of kKeys keys in
 // LDS (bf16 widened to fp32 on the way), each wave then streams its own tile
 // with broadcast LDS reads.  The online (M, S) state with a lazy maximum is
 // the one described in lse_d3.hip.
@@ -84,23 +85,20 @@ __device__ __forceinline__ void finish_row(float *qbias, float *qpot, const floa
     qbias[pt] = bias_of(c_next, f, sq, ql2w[k]);
 }
 
+// One 64-row block rb of pair b (of B), the keys of split `split`, with the
+// kWaves waves of the calling work-group (every one must call it).
 template <typename T, int DP>
-__global__ __launch_bounds__(kWaves *kWave) void lseF_kernel(
+__device__ __forceinline__ void lseF_block(
     const T *__restrict__ qx_, float *__restrict__ qbias, float *__restrict__ qpot,
     const float *__restrict__ ql2w, const T *__restrict__ ky_, const float *__restrict__ kbias,
-    float2 *__restrict__ part, const int *__restrict__ only, int d, int nq, int nq_pad, int nk,
-    int nk_pad, int tiles_per_split, float two_c, double eps_ln2, double c_next)
+    float2 *__restrict__ part, int rb, int split, int b, int B, int d, int nq, int nq_pad,
+    int nk, int nk_pad, int tiles_per_split, float two_c, double eps_ln2, double c_next)
 {
-    // only != nullptr: a fallback launch, work only on the row blocks flagged there
-    if (only && !only[blockIdx.z * gridDim.x + blockIdx.x])
-        return;
     __shared__ float4 tile[kWaves][kKeys][DP / 4];
     __shared__ float2 red[kWaves][kWave];
-    const int b = blockIdx.z;
-    const int split = blockIdx.y;
     const int lane = lane_id();
     const int w = wave_id_uniform();
-    const int row = blockIdx.x * kWave + lane;
+    const int row = rb * kWave + lane;
 
     float q[DP];
     {
@@ -182,12 +180,24 @@ __global__ __launch_bounds__(kWaves *kWave) void lseF_kernel(
         lse_merge(M, S, o.x, o.y);
     }
     if (part) {
-        part[((size_t)split * gridDim.z + b) * nq_pad + row] = make_float2(M, S);
+        part[((size_t)split * B + b) * nq_pad + row] = make_float2(M, S);
         return;
     }
     if (row < nq)
         finish_row(qbias, qpot, ql2w, (size_t)b * nq_pad + row, (size_t)b * nq + row,
                    row_sq(q, d), M, S, eps_ln2, c_next);
+}
+
+template <typename T, int DP>
+__global__ __launch_bounds__(kWaves *kWave) void lseF_kernel(
+    const T *__restrict__ qx_, float *__restrict__ qbias, float *__restrict__ qpot,
+    const float *__restrict__ ql2w, const T *__restrict__ ky_, const float *__restrict__ kbias,
+    float2 *__restrict__ part, int d, int nq, int nq_pad, int nk, int nk_pad,
+    int tiles_per_split, float two_c, double eps_ln2, double c_next)
+{
+    lseF_block<T, DP>(qx_, qbias, qpot, ql2w, ky_, kbias, part, blockIdx.x, blockIdx.y,
+                      blockIdx.z, gridDim.z, d, nq, nq_pad, nk, nk_pad, tiles_per_split, two_c,
+                      eps_ln2, c_next);
 }
 
 // ---------------------------------------------------------------------------
@@ -198,7 +208,9 @@ __global__ __launch_bounds__(kWaves *kWave) void lseF_kernel(
 // Lane l supplies A[l % 16][8 (l / 16) + e] and B[8 (l / 16) + e][l % 16],
 // e = 0..7, and receives D[4 (l / 16) + r][l % 16] (layout checked with an
 // in-bounds probe).  The factor 2c is applied in fp32 after the product, never
-// to the bf16 inputs.
+// to the bf16 inputs.  (32 x 32 x 16 blocks, half the matrix instructions per
+// entry, were measured slower: 495 against 466 us per feat-50k half-iteration;
+// a wave then covers 32 rows, which doubles the LDS reads per entry.)
 //
 // Shifted streaming as in lse_d3.hip: row i streams against
 // M_i = c (||x_i||^2 - f_i), carried in the accumulator input as
@@ -206,15 +218,23 @@ __global__ __launch_bounds__(kWaves *kWave) void lseF_kernel(
 // s_ij - M_i = 2c D_ij + beta_j.  With one shift per row, partial sums over
 // key ranges simply add.
 //
-// Key stream shared by the waves of a work-group: each of its R waves owns 64
-// rows, and all R stream the same key tiles, staged in LDS (double buffered,
-// 64 keys a stage, loaded cooperatively with 16-byte accesses), so the chip
-// fetches each key tile once per R * 64 rows instead of once per 64; the key
-// range is split across work-groups to fill the chip.  Each wave writes the
-// partial sums of its rows; a finalize kernel adds the splits in a fixed
-// order, turns the sums into potentials and biases, and flags a 64-row block
-// whose sum left [2^-64, 2^100] (a stale shift), which the vector kernel then
-// recomputes in full.
+// Work partition (stream-K): a work-group of 16 waves owns 1024 consecutive rows
+// (a row group; each wave 64 rows as four 16-row groups), and the key tiles of every row group are
+// laid end to end, pair by pair, into one range of units (row group, 16-key
+// tile).  A launch has a fixed number of work-groups (one per compute unit, 4
+// waves per SIMD, or one per row group when there are more row groups), and
+// work-group w takes
+// the units [w U / P, (w + 1) U / P): equal shares, so every compute unit
+// finishes together, whatever the row and key counts.  A share spans at most
+// two row groups; for each it writes the partial sums of its rows to slot
+// (w, 0) or (w, 1).  The keys of a share stream through LDS (double buffered,
+// 256 keys a stage, loaded cooperatively with 16-byte accesses) and the 16
+// waves read them from there, so each key tile is fetched once per 1024 rows
+// (16 waves: 1% faster than two work-groups of 8 per compute unit).  The finalize kernel adds, for every row, the
+// partials of the work-groups that cover its row group in increasing order
+// (a fixed order: the result does not depend on timing), turns the sums into
+// potentials and biases, and recomputes on the vector ALUs, in the same
+// launch, a 64-row block whose sum left [2^-64, 2^100] (a stale shift).
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 constexpr int kGroups = 4;
@@ -227,165 +247,224 @@ __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t *p)
     return __builtin_bit_cast(bf16x8, v);
 }
 
-constexpr int kShareWaves = 8;   // waves (64-row blocks) sharing one key stream
-constexpr int kStageTiles = 8;   // key tiles per LDS stage (128 keys)
+constexpr int kSWaves = 16;                     // waves per work-group
+constexpr int kSRows = 16 * kGroups;            // rows per wave
+constexpr int kSGroupRows = kSWaves * kSRows;   // rows per row group (work-group)
+constexpr int kSKeys = 16;                      // keys per tile
+constexpr int kSStageTiles = 16;                // tiles per LDS stage (256 keys)
+constexpr int kSSlots = 256;                    // work-groups per launch: 1 per compute unit
 
-template <int DK>
-__global__ __launch_bounds__(kShareWaves *kWave) void lseFm_kernel(
-    const uint16_t *__restrict__ qx_, const float *__restrict__ qpot,
-    const float *__restrict__ qsq, const uint16_t *__restrict__ ky_,
-    const float *__restrict__ kbias, float *__restrict__ part, int nq, int nq_pad, int nk,
-    int nk_pad, int tiles_per_split, float two_c)
+// The stream-K partition of one pass: G row groups (B pairs x RG each), T
+// tiles per row, U = G T units, P work-groups.
+struct Part {
+    int RG, T, P;
+    long long U;
+};
+
+// First unit of work-group w (w = P gives U).  When P T == U (one work-group
+// per row group) the shares are whole row groups.
+__device__ __forceinline__ long long share_lo(int w, const Part &pt)
 {
-    constexpr int d = 32 * DK;
-    constexpr int kStageKeys = kStageTiles * kKeys;
-    constexpr int kChunks = d / 8;            // 16-byte chunks per key
-    constexpr int kStride = kChunks + 1;      // padded key stride in LDS (bank spread)
-    constexpr int kTotal = kStageKeys * kChunks;   // 16-byte chunks per stage
-    constexpr int kLoads = (kTotal + kShareWaves * kWave - 1) / (kShareWaves * kWave);
-    __shared__ uint4 kbuf[2][kStageKeys * kStride];
-    __shared__ float bbuf[2][kStageKeys];
-    const int b = blockIdx.z;
-    const int split = blockIdx.y;
-    const int lane = lane_id();
-    const int w = wave_id_uniform();
-    const int row0 = (blockIdx.x * kShareWaves + w) * kWave;   // this wave's 64 rows
-    const int kq = lane >> 4;
-    const int c16 = lane & 15;
-
-    bf16x8 A[kGroups][DK];
-    f32x4 Cn[kGroups], S[kGroups];
-#pragma unroll
-    for (int g = 0; g < kGroups; ++g) {
-        const int ra = row0 + 16 * g + c16;      // row whose operand this lane supplies
-        const int rc = min(ra, nq - 1);
-#pragma unroll
-        for (int kb = 0; kb < DK; ++kb) {
-            bf16x8 v = load_bf16x8(qx_ + ((size_t)b * nq + rc) * d + 32 * kb + 8 * kq);
-            if (ra >= nq)
-                v = bf16x8{};
-            A[g][kb] = v;
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int rr = row0 + 16 * g + 4 * kq + r;   // row whose results this lane holds
-            float sh = 0.f;
-            if (rr < nq) {
-                const size_t k = (size_t)b * nq + rr;
-                sh = -0.5f * (qsq[k] - qpot[k]);
-            }
-            Cn[g][r] = sh;
-            S[g][r] = 0.f;
-        }
-    }
-    const uint4 *ky = reinterpret_cast<const uint4 *>(ky_ + (size_t)b * nk * d);
-    const float *kb_ = kbias + (size_t)b * nk_pad;
-    const int n_tiles = nk_pad / kKeys;
-    const int t_begin = split * tiles_per_split;
-    const int t_end = min(t_begin + tiles_per_split, n_tiles);
-    const int n_stages = t_begin < t_end ? (t_end - t_begin + kStageTiles - 1) / kStageTiles : 0;
-
-    // cooperative stage load: chunk e = key * kChunks + part of the stage's keys;
-    // keys past the split's last tile get bias -1e30 (they add exactly 0), and
-    // their point index is clamped inside the pair.  A thread's chunks of the
-    // next stage are loaded into registers while the current stage is
-    // consumed, then written to the other LDS buffer.
-    const int e0 = threadIdx.x;
-    uint4 ld0, ld1, ld2, ld3;   // kLoads <= 4 of them are used
-    float lb = kNeg;
-#define SK_CHUNK(i_) (e0 + (i_) * kShareWaves * kWave)
-#define SK_LOAD(i_, v_)                                                                    \
-    if (kLoads > (i_) && SK_CHUNK(i_) < kTotal)                                            \
-        v_ = ky[(size_t)min(key0_ + SK_CHUNK(i_) / kChunks, nk - 1) * kChunks +            \
-                SK_CHUNK(i_) % kChunks]
-#define SK_PUT(buf_, i_, v_)                                                               \
-    if (kLoads > (i_) && SK_CHUNK(i_) < kTotal)                                            \
-        kbuf[buf_][(SK_CHUNK(i_) / kChunks) * kStride + SK_CHUNK(i_) % kChunks] = v_
-#define SK_FETCH(s_)                                                                       \
-    do {                                                                                   \
-        const int key0_ = (t_begin + (s_) * kStageTiles) * kKeys;                          \
-        SK_LOAD(0, ld0);                                                                   \
-        SK_LOAD(1, ld1);                                                                   \
-        SK_LOAD(2, ld2);                                                                   \
-        SK_LOAD(3, ld3);                                                                   \
-        if (e0 < kStageKeys)                                                               \
-            lb = key0_ + e0 < t_end * kKeys ? kb_[key0_ + e0] : kNeg;                      \
-    } while (0)
-#define SK_STASH(buf_)                                                                     \
-    do {                                                                                   \
-        SK_PUT(buf_, 0, ld0);                                                              \
-        SK_PUT(buf_, 1, ld1);                                                              \
-        SK_PUT(buf_, 2, ld2);                                                              \
-        SK_PUT(buf_, 3, ld3);                                                              \
-        if (e0 < kStageKeys)                                                               \
-            bbuf[buf_][e0] = lb;                                                           \
-    } while (0)
-    static_assert(kLoads <= 4, "at most four 16-byte chunks per thread and stage");
-    if (n_stages > 0) {
-        SK_FETCH(0);
-        SK_STASH(0);
-    }
-    __syncthreads();
-    for (int s = 0; s < n_stages; ++s) {
-        const int buf = s & 1;
-        if (s + 1 < n_stages)
-            SK_FETCH(s + 1);   // in flight while this stage is consumed
-#pragma unroll 1
-        for (int tt = 0; tt < kStageTiles; ++tt) {
-            bf16x8 Bv[DK];
-#pragma unroll
-            for (int kb = 0; kb < DK; ++kb)
-                Bv[kb] = __builtin_bit_cast(
-                    bf16x8, kbuf[buf][(tt * kKeys + c16) * kStride + 4 * kb + kq]);
-            const float be = bbuf[buf][tt * kKeys + c16];
-#pragma unroll
-            for (int g = 0; g < kGroups; ++g) {
-                f32x4 D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][0], Bv[0], Cn[g], 0, 0, 0);
-#pragma unroll
-                for (int kb = 1; kb < DK; ++kb)
-                    D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][kb], Bv[kb], D, 0, 0, 0);
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    S[g][r] += ex2(fmaf(two_c, D[r], be));
-            }
-        }
-        if (s + 1 < n_stages)
-            SK_STASH(buf ^ 1);
-        __syncthreads();
-    }
-#undef SK_FETCH
-#undef SK_STASH
-#undef SK_LOAD
-#undef SK_PUT
-#undef SK_CHUNK
-#pragma unroll
-    for (int g = 0; g < kGroups; ++g)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float Sr = row16_sum(S[g][r]);
-            const int row = row0 + 16 * g + 4 * kq + r;
-            if (c16 == 0 && row < nq_pad)
-                part[((size_t)split * gridDim.z + b) * nq_pad + row] = Sr;
-        }
+    return pt.U == (long long)pt.P * pt.T ? (long long)w * pt.T : (long long)w * pt.U / pt.P;
 }
 
-// Sum of the splits' partials per row (fixed order), potentials and biases; a
-// 64-row block with a sum out of range is flagged and left unchanged.
-__global__ __launch_bounds__(kWave) void lseFm_finalize(
-    float *__restrict__ qbias, float *__restrict__ qpot, const float *__restrict__ ql2w,
-    const float *__restrict__ qsq, const float *__restrict__ part, int *__restrict__ redo_out,
-    int B, int nq, int nq_pad, int splits, float two_c, double eps_ln2, double c_next)
+// The work-group whose share holds unit u (the largest w with share_lo(w) <= u).
+__device__ __forceinline__ int share_of(long long u, const Part &pt)
 {
+    if (pt.U == (long long)pt.P * pt.T)
+        return (int)(u / pt.T);
+    return (int)(((u + 1) * pt.P - 1) / pt.U);
+}
+
+template <int DK>
+__global__ __launch_bounds__(kSWaves *kWave) void lseFs_kernel(
+    const uint16_t *__restrict__ qx_, const float *__restrict__ qpot,
+    const float *__restrict__ qsq, const uint16_t *__restrict__ ky_,
+    const float *__restrict__ kbias, float *__restrict__ part, int nq, int nk, int nk_pad,
+    Part pt, float two_c)
+{
+    constexpr int d = 32 * DK;
+    constexpr int kStageKeys = kSStageTiles * kSKeys;   // 256
+    constexpr int kChunks = d / 8;                      // 16-byte chunks per key
+    constexpr int kStride = kChunks + 1;                // padded key stride in LDS (bank spread)
+    constexpr int kTotal = kStageKeys * kChunks;        // 16-byte chunks per stage
+    constexpr int kThreads = kSWaves * kWave;
+    constexpr int kLoads = kTotal / kThreads;        // 16-byte chunks per thread and stage
+    static_assert(kTotal % kThreads == 0 && kLoads <= 4, "whole chunks per thread");
+    __shared__ uint4 kbuf[2][kStageKeys * kStride];
+    __shared__ float bbuf[2][kStageKeys];
+    const int wg = blockIdx.x;
+    const int lane = lane_id();
+    const int w = wave_id_uniform();
+    const int kq = lane >> 4;      // operand k index this lane supplies / row quad it receives
+    const int c16 = lane & 15;     // operand row (A) or column (B) within a 16-block
+    const int e0 = threadIdx.x;
+
+    const long long u_end = share_lo(wg + 1, pt);
+    long long u = share_lo(wg, pt);
+    for (int seg = 0; u < u_end && seg < 2; ++seg) {   // a share spans <= 2 row groups
+        const long long gb = u / pt.T;                    // pair-major row group
+        const long long g_end = (gb + 1) * pt.T;
+        const int t0 = (int)(u - gb * pt.T);
+        const int t1 = (int)((u_end < g_end ? u_end : g_end) - gb * pt.T);
+        u = u_end < g_end ? u_end : g_end;
+        const int b = (int)(gb / pt.RG);
+        const int row0 = (int)(gb % pt.RG) * kSGroupRows + w * kSRows;   // this wave's rows
+        const bool live = row0 < nq;   // wave-uniform: a wave past the last row only loads
+
+        bf16x8 A[kGroups][DK];
+        f32x4 Cn[kGroups], S[kGroups];
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g) {
+            const int ra = row0 + 16 * g + c16;      // row whose operand this lane supplies
+            const int rc = min(ra, nq - 1);
+#pragma unroll
+            for (int kb = 0; kb < DK; ++kb) {
+                bf16x8 v = load_bf16x8(qx_ + ((size_t)b * nq + rc) * d + 32 * kb + 8 * kq);
+                if (ra >= nq)
+                    v = bf16x8{};
+                A[g][kb] = v;
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int rr = row0 + 16 * g + 4 * kq + r;   // row whose results this lane holds
+                float sh = 0.f;
+                if (rr < nq) {
+                    const size_t k = (size_t)b * nq + rr;
+                    sh = -0.5f * (qsq[k] - qpot[k]);
+                }
+                Cn[g][r] = sh;
+                S[g][r] = 0.f;
+            }
+        }
+        const uint4 *ky = reinterpret_cast<const uint4 *>(ky_ + (size_t)b * nk * d);
+        const float *kb_ = kbias + (size_t)b * nk_pad;
+        const int n_stages = (t1 - t0 + kSStageTiles - 1) / kSStageTiles;
+
+        // cooperative stage load: chunk e of the stage is part e % kChunks of its
+        // key e / kChunks; keys past the share's last tile get bias -1e30 (they
+        // add exactly 0) and their point index is clamped inside the pair.  A
+        // thread's chunks of the next stage are loaded into registers while the
+        // current stage is consumed, then written to the other LDS buffer.
+        uint4 ld0, ld1, ld2, ld3;   // the first kLoads of them are used
+        float lb = kNeg;
+        auto fetch = [&](int s) {
+            const int key0 = (t0 + s * kSStageTiles) * kSKeys;
+            auto one = [&](int i) {
+                const int e = e0 + i * kThreads;
+                return ky[(size_t)min(key0 + e / kChunks, nk - 1) * kChunks + e % kChunks];
+            };
+            ld0 = one(0);
+            if constexpr (kLoads > 1)
+                ld1 = one(1);
+            if constexpr (kLoads > 2)
+                ld2 = one(2);
+            if constexpr (kLoads > 3)
+                ld3 = one(3);
+            if (e0 < kStageKeys)
+                lb = key0 + e0 < t1 * kSKeys ? kb_[key0 + e0] : kNeg;
+        };
+        auto stash = [&](int buf) {
+            auto one = [&](int i, const uint4 &v) {
+                const int e = e0 + i * kThreads;
+                kbuf[buf][(e / kChunks) * kStride + e % kChunks] = v;
+            };
+            one(0, ld0);
+            if constexpr (kLoads > 1)
+                one(1, ld1);
+            if constexpr (kLoads > 2)
+                one(2, ld2);
+            if constexpr (kLoads > 3)
+                one(3, ld3);
+            if (e0 < kStageKeys)
+                bbuf[buf][e0] = lb;
+        };
+        fetch(0);
+        stash(0);
+        __syncthreads();
+        for (int s = 0; s < n_stages; ++s) {
+            const int buf = s & 1;
+            if (s + 1 < n_stages)
+                fetch(s + 1);   // in flight while this stage is consumed
+            if (live) {
+#pragma unroll 1
+                for (int tt = 0; tt < kSStageTiles; ++tt) {
+                    bf16x8 Bv[DK];
+#pragma unroll
+                    for (int kb = 0; kb < DK; ++kb)
+                        Bv[kb] = __builtin_bit_cast(
+                            bf16x8, kbuf[buf][(tt * kSKeys + c16) * kStride + 4 * kb + kq]);
+                    const float be = bbuf[buf][tt * kSKeys + c16];
+#pragma unroll
+                    for (int g = 0; g < kGroups; ++g) {
+                        f32x4 D =
+                            __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][0], Bv[0], Cn[g], 0, 0, 0);
+#pragma unroll
+                        for (int kb = 1; kb < DK; ++kb)
+                            D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][kb], Bv[kb], D, 0, 0,
+                                                                        0);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            S[g][r] += ex2(fmaf(two_c, D[r], be));
+                    }
+                }
+            }
+            if (s + 1 < n_stages)
+                stash(buf ^ 1);
+            __syncthreads();
+        }
+        // row sums: each of the 16 lanes of a row holds one key column
+        float *out = part + ((size_t)wg * 2 + seg) * kSGroupRows + w * kSRows;
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float v = row16_sum(S[g][r]);
+                if (c16 == 0 && live)
+                    out[16 * g + 4 * kq + r] = v;
+            }
+    }
+}
+
+// Sum of the partials of every row (fixed order), potentials and biases; a
+// 64-row block with a sum out of range is recomputed by the work-group's waves
+// on the vector ALUs with an online maximum over all keys.
+template <int DP>
+__global__ __launch_bounds__(kWaves *kWave) void lseFs_finalize(
+    const uint16_t *__restrict__ qx_, float *__restrict__ qbias, float *__restrict__ qpot,
+    const float *__restrict__ ql2w, const float *__restrict__ qsq,
+    const uint16_t *__restrict__ ky_, const float *__restrict__ kbias,
+    const float *__restrict__ part, int B, int d, int nq, int nq_pad, int nk, int nk_pad,
+    Part pt, float two_c, double eps_ln2, double c_next)
+{
+    __shared__ int stale;
     const int b = blockIdx.y;
     const int row = blockIdx.x * kWave + lane_id();
+    const int w = wave_id_uniform();
     float Ssum = 0.f;
-    for (int s = 0; s < splits; ++s)
-        Ssum += part[((size_t)s * B + b) * nq_pad + row];
-    const bool bad = row < nq && !(Ssum >= kSumLo && Ssum <= kSumHi);
-    const int flag = __builtin_amdgcn_readfirstlane(__ballot(bad) != 0 ? 1 : 0);
-    if (lane_id() == 0)
-        redo_out[b * gridDim.x + blockIdx.x] = flag;
-    if (flag || row >= nq)
+    if (w == 0) {
+        if (row < nq) {
+            const long long gb = (long long)b * pt.RG + row / kSGroupRows;
+            const int rr = row % kSGroupRows;
+            const int w0 = share_of(gb * pt.T, pt), w1 = share_of(gb * pt.T + pt.T - 1, pt);
+            for (int v = w0; v <= w1; ++v) {
+                const int seg = share_lo(v, pt) / pt.T == gb ? 0 : 1;
+                Ssum += part[((size_t)v * 2 + seg) * kSGroupRows + rr];
+            }
+        }
+        const bool bad = row < nq && !(Ssum >= kSumLo && Ssum <= kSumHi);
+        const int flag = __builtin_amdgcn_readfirstlane(__ballot(bad) != 0 ? 1 : 0);
+        if (lane_id() == 0)
+            stale = flag;
+    }
+    __syncthreads();
+    if (stale) {
+        lseF_block<uint16_t, DP>(qx_, qbias, qpot, ql2w, ky_, kbias, nullptr, blockIdx.x, 0, b,
+                                 B, d, nq, nq_pad, nk, nk_pad, nk_pad / kKeys, two_c, eps_ln2,
+                                 c_next);
+        return;
+    }
+    if (w != 0 || row >= nq)
         return;
     const size_t k = (size_t)b * nq + row;
     const float sqf = qsq[k];
@@ -545,9 +624,8 @@ void launch_lseF_t(SideF q, SideF k, int d, int B, float two_c, double eps_ln2,
     dim3 grid(q.n_pad / kWave, splits, B);
     hipLaunchKernelGGL((lseF_kernel<T, DP>), grid, dim3(kWaves * kWave), 0, st,
                        (const T *)q.pts, q.bias, q.pot, (const float *)q.l2w,
-                       (const T *)k.pts, (const float *)k.bias, splits > 1 ? part : nullptr,
-                       (const int *)nullptr, d, q.n, q.n_pad, k.n, k.n_pad, tps, two_c, eps_ln2,
-                       c_next);
+                       (const T *)k.pts, (const float *)k.bias, splits > 1 ? part : nullptr, d,
+                       q.n, q.n_pad, k.n, k.n_pad, tps, two_c, eps_ln2, c_next);
     if (splits > 1) {
         dim3 g2(ceil_div(q.n, 256), B);
         hipLaunchKernelGGL(lseF_finalize<T>, g2, dim3(256), 0, st, (const T *)q.pts, d, q.bias,
@@ -556,43 +634,41 @@ void launch_lseF_t(SideF q, SideF k, int d, int B, float two_c, double eps_ln2,
     }
 }
 
-// Key splits of the matrix-core pass: about as many waves as the chip holds at
-// once (4096: 4 per SIMD), rounded down so that the launch is one round, with
-// at least two stages of keys per split.
-int lseFm_splits(int B, int nq_pad, int nk_pad)
+// Stream-K partition of a matrix-core pass: 1024-row groups of every pair,
+// 16-key tiles; one work-group per compute unit, or one per row group when
+// there are more row groups (then a share never spans more than two groups:
+// every share is at most one row group long).  At least 16 tiles per share.
+Part lseFs_part(int B, int nq_pad, int nk_pad)
 {
-    const long groups = (long)B * ceil_div(nq_pad / kWave, kShareWaves);
-    const int tiles = nk_pad / kKeys;
-    int splits = (int)(4096 / kShareWaves / groups);
-    const int max_splits = tiles / (2 * kStageTiles);
-    if (splits > max_splits)
-        splits = max_splits;
-    return splits < 1 ? 1 : splits;
+    Part pt;
+    pt.RG = ceil_div(nq_pad, kSGroupRows);
+    pt.T = nk_pad / kSKeys;
+    const long long G = (long long)B * pt.RG;
+    pt.U = G * pt.T;
+    long long P = pt.U / 16;
+    if (P > kSSlots)
+        P = kSSlots;
+    if (P < G)
+        P = G;
+    pt.P = (int)P;
+    return pt;
 }
 
 template <int DK>
-void launch_lseFm_t(SideF q, SideF k, int B, float two_c, double eps_ln2, double c_next,
+void launch_lseFs_t(SideF q, SideF k, int B, float two_c, double eps_ln2, double c_next,
                     float *part, hipStream_t st)
 {
-    const int splits = lseFm_splits(B, q.n_pad, k.n_pad);
-    const int tps = ceil_div(k.n_pad / kKeys, splits);
-    dim3 grid(ceil_div(q.n_pad / kWave, kShareWaves), splits, B);
-    hipLaunchKernelGGL((lseFm_kernel<DK>), grid, dim3(kShareWaves * kWave), 0, st,
+    const Part pt = lseFs_part(B, q.n_pad, k.n_pad);
+    hipLaunchKernelGGL((lseFs_kernel<DK>), dim3(pt.P), dim3(kSWaves * kWave), 0, st,
                        (const uint16_t *)q.pts, (const float *)q.pot, (const float *)q.sq,
-                       (const uint16_t *)k.pts, (const float *)k.bias, part, q.n, q.n_pad, k.n,
-                       k.n_pad, tps, two_c);
-    dim3 g2(q.n_pad / kWave, B);
-    hipLaunchKernelGGL(lseFm_finalize, g2, dim3(kWave), 0, st, q.bias, q.pot,
-                       (const float *)q.l2w, (const float *)q.sq, (const float *)part, q.redo, B,
-                       q.n, q.n_pad, splits, two_c, eps_ln2, c_next);
-    // fallback for flagged row blocks: the vector kernel
+                       (const uint16_t *)k.pts, (const float *)k.bias, part, q.n, k.n, k.n_pad,
+                       pt, two_c);
     constexpr int DP = 32 * DK;
-    dim3 g3(q.n_pad / kWave, 1, B);
-    hipLaunchKernelGGL((lseF_kernel<uint16_t, DP>), g3, dim3(kWaves * kWave), 0, st,
-                       (const uint16_t *)q.pts, q.bias, q.pot, (const float *)q.l2w,
-                       (const uint16_t *)k.pts, (const float *)k.bias, (float2 *)nullptr,
-                       (const int *)q.redo, DP, q.n, q.n_pad, k.n, k.n_pad,
-                       k.n_pad / kKeys, two_c, eps_ln2, c_next);
+    hipLaunchKernelGGL((lseFs_finalize<DP>), dim3(q.n_pad / kWave, B), dim3(kWaves * kWave), 0,
+                       st, (const uint16_t *)q.pts, q.bias, q.pot, (const float *)q.l2w,
+                       (const float *)q.sq, (const uint16_t *)k.pts, (const float *)k.bias,
+                       (const float *)part, B, DP, q.n, q.n_pad, k.n, k.n_pad, pt, two_c,
+                       eps_ln2, c_next);
 }
 
 // Matrix cores for bf16 with whole 32-dim blocks, 16-byte aligned rows (the
@@ -651,7 +727,7 @@ size_t lseF_partial_floats2(int B, int nq_pad, int nk_pad)
 {
     const int s = lseF_splits(B, nq_pad, nk_pad);
     const size_t vec = s > 1 ? (size_t)s * B * nq_pad : 0;
-    const size_t mat = ((size_t)lseFm_splits(B, nq_pad, nk_pad) * B * nq_pad + 1) / 2;
+    const size_t mat = (size_t)lseFs_part(B, nq_pad, nk_pad).P * kSGroupRows;   // 2 floats each
     return vec > mat ? vec : mat;
 }
 
@@ -677,10 +753,10 @@ hipError_t launch_lseF(SideF q, SideF k, int dtype, int d, int B, float eps, flo
     const double eps_ln2 = 1.0 / (double)c;
     if (use_matrix_cores(q, k, dtype, d, B)) {
         switch (d / 32) {
-        case 1: launch_lseFm_t<1>(q, k, B, 2.0f * c, eps_ln2, c_next, (float *)part, st); break;
-        case 2: launch_lseFm_t<2>(q, k, B, 2.0f * c, eps_ln2, c_next, (float *)part, st); break;
-        case 3: launch_lseFm_t<3>(q, k, B, 2.0f * c, eps_ln2, c_next, (float *)part, st); break;
-        default: launch_lseFm_t<4>(q, k, B, 2.0f * c, eps_ln2, c_next, (float *)part, st); break;
+        case 1: launch_lseFs_t<1>(q, k, B, 2.0f * c, eps_ln2, c_next, (float *)part, st); break;
+        case 2: launch_lseFs_t<2>(q, k, B, 2.0f * c, eps_ln2, c_next, (float *)part, st); break;
+        case 3: launch_lseFs_t<3>(q, k, B, 2.0f * c, eps_ln2, c_next, (float *)part, st); break;
+        default: launch_lseFs_t<4>(q, k, B, 2.0f * c, eps_ln2, c_next, (float *)part, st); break;
         }
     } else if (dtype == 1)
         dispatch<uint16_t>(q, k, d, B, 2.0f * c, eps_ln2, c_next, part, st);
