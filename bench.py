@@ -40,29 +40,32 @@ CLOCK_HZ = 2.4e9
 FP32_VECTOR_PEAK = 157.3e12        # flop/s (packed FP32 FMA)
 BF16_MFMA_PEAK = 2.5e15            # flop/s, dense
 FLOPS_PER_EVAL_D3 = 9              # 3 mul + 3 add (score with bias) + max, subtract, accumulate
-# Issue cost, in SIMD cycles, of one wave64 instruction (rates probe, profiles/rates_mi355x.md:
-# v_exp_f32 at 32 lanes per compute unit per clock, v_add/v_fma_f32 at 64, an MFMA takes
-# 4 cycles of the issue port and 16 of the matrix core for 16x16x32 bf16)
+# v_exp_f32 issues at a quarter of the FP32 lane rate: 128 FMA lanes per compute unit
+# per clock (157.3 TFLOP/s / 256 CUs / 2.4 GHz / 2), 32 exponential lanes (the rate
+# probe measures 29.2 and 112; profiles/rates_mi355x.md)
 EXP_LANES_PER_CLK_CU = 32
-CYC_EXP, CYC_VALU, CYC_MFMA_ISSUE = 8, 4, 4
 
-# Instructions per wave per 16-key tile (64 rows x 16 keys = 1024 entries) of each
-# streaming kernel: (MFMAs, exponentials, other vector instructions)
-TILE_MIX = {
-    "lse3m_kernel": (4, 16, 16),       # score + bias on the matrix cores; exp, add
-    "lse3p_kernel": (4, 16, 16),
-    "lse3_kernel": (0, 16, 16 * 4),    # vector scores: 3 fma + add per entry (lazy max aside)
-    "lseFm_kernel": (8, 16, 32),       # two 32-dim MFMAs per group; scale-and-bias fma, add
-    "lseF_kernel": (0, 16, 16 * 66),   # vector dot products of 64 dims
+# SIMD cycles per wave and 16-key tile (64 rows x 16 keys = 1024 entries) of each
+# streaming kernel's instruction mix, measured by the rate probe on the mix itself
+# (profiles/rates_mi355x.md): the d = 3 tile, 4 MFMA + 16 exp + 16 add on their
+# outputs, 220; the d = 64 bf16 feature tile, 8 MFMA + 16 fma + 16 exp + 16 add, 314.
+# The vector kernels' mixes are priced with the probe's single-instruction costs
+# (exp 8.8 cycles, fp32 add or fma 2.3).
+TILE_CYCLES = {
+    "lse3m_kernel": 220.0,
+    "lse3p_kernel": 220.0,
+    "lseFs_kernel": 314.0,
+    "lse3_kernel": 16 * 8.8 + 64 * 2.3,        # 3 fma + 1 add per entry on top of the exp
+    "lseF_kernel": 16 * 8.8 + 16 * 66 * 2.3,   # 64-dim dot products on the vector ALUs
 }
+TILE_PROBE = {"lse3m_kernel": "d3_tile", "lse3p_kernel": "d3_tile",
+              "lseFs_kernel": "feature_tile"}
 
 
-def issue_floor_evals_per_s(kernel):
-    """Entry evaluations per second if every SIMD issued the kernel's tile mix
-    back to back at the nominal clock (the kernel's own instruction-issue bound)."""
-    mfma, exp, other = TILE_MIX[kernel]
-    cycles = mfma * CYC_MFMA_ISSUE + exp * CYC_EXP + other * CYC_VALU
-    return N_SIMD * CLOCK_HZ * 1024 / cycles
+def issue_floor_evals_per_s(kernel, cycles=None):
+    """Entry evaluations per second if every SIMD issued the kernel's tile mix back
+    to back at the nominal clock (the kernel's own instruction-issue bound)."""
+    return N_SIMD * CLOCK_HZ * 1024 / (cycles or TILE_CYCLES[kernel])
 
 
 def roofline_evals_per_s(d, kernel):
@@ -93,7 +96,7 @@ KERNEL_SOURCES = {
                      "sinkhorn_point_cloud_amd/csrc/common.h"),
     "lse3p_kernel": ("sinkhorn_point_cloud_amd/csrc/lse_d3.hip",
                      "sinkhorn_point_cloud_amd/csrc/common.h"),
-    "lseFm_kernel": ("sinkhorn_point_cloud_amd/csrc/lse_feat.hip",
+    "lseFs_kernel": ("sinkhorn_point_cloud_amd/csrc/lse_feat.hip",
                      "sinkhorn_point_cloud_amd/csrc/common.h"),
 }
 
@@ -366,7 +369,7 @@ def main():
                   "lse3p_kernel" if pairwise else "lse3m_kernel")
     else:
         pairwise = False
-        kernel = "lseFm_kernel" if dt == sk.SK_BF16 and d % 32 == 0 else "lseF_kernel"
+        kernel = "lseFs_kernel" if dt == sk.SK_BF16 and d % 32 == 0 else "lseF_kernel"
 
     # the dominant kernel's average launch: one potentials call (no cost pass, no
     # plan) less the same call with every iteration count 0 (centering and packing
@@ -427,7 +430,7 @@ def main():
                      # the kernel's own instruction-issue bound: its per-tile mix of MFMAs,
                      # exponentials and other vector instructions issued back to back
                      "issue_floor": floor / 1e12, "frac_of_issue_floor": achieved / floor,
-                     "tile_mix_mfma_exp_other": list(TILE_MIX[kernel])},
+                     "tile_cycles": TILE_CYCLES[kernel]},
         "phases_ms": {"step": t_step * 1e3, "iterations": t_iterations * 1e3,
                       ("pack_plan_and_loss" if sparse else "pack_and_cost_pass"):
                       (t_step - t_iterations) * 1e3},
@@ -488,7 +491,13 @@ def main():
             assert bool(torch.isfinite(HV).all())
             line["phases_ms"]["hvp_20_cg_steps"] = t_hv * 1e3
     if args.rates:
-        line["measured_rates"] = measure_rates(dev)
+        rates = measure_rates(dev)
+        line["measured_rates"] = rates
+        if kernel in TILE_PROBE:
+            cyc = rates[TILE_PROBE[kernel]]["simd_cycles_per_wave_iteration"]
+            live = issue_floor_evals_per_s(kernel, cyc)
+            line["roofline"]["issue_floor_live_probe"] = live / 1e12
+            line["roofline"]["frac_of_issue_floor_live_probe"] = achieved / live
     if args.copy_calibration:
         src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)

@@ -20,17 +20,16 @@ def test_exp_issue_bound_and_issue_floors():
     # ... and the metric's min(FP32 / 9 flops, exp) stays reported beside it
     assert algo == pytest.approx(min(157.3e12 / 9, exp))
     # bf16 features: MFMA 2.5 PFLOP/s over 2d flops, just below the exp bound at d = 64
-    peak, bound, _, _ = bench.roofline_evals_per_s(64, "lseFm_kernel")
+    peak, bound, _, _ = bench.roofline_evals_per_s(64, "lseFs_kernel")
     assert bound == "mfma" and peak == pytest.approx(2.5e15 / 128)
-    # each kernel's issue floor counts one 8-cycle exponential per 64 entries at least,
-    # so it never exceeds the exp bound; the d = 3 tile (4 MFMA + 16 exp + 16 add)
-    # is 208 cycles per 1024 entries
-    for k in bench.TILE_MIX:
+    # each kernel's issue floor (its measured tile mix) is below the exp bound; the
+    # d = 3 tile costs 220 SIMD cycles per 1024 entries, the d = 64 feature tile 314
+    for k in bench.TILE_CYCLES:
         assert bench.issue_floor_evals_per_s(k) < exp
     assert bench.issue_floor_evals_per_s("lse3m_kernel") == pytest.approx(
-        1024 * 2.4e9 * 1024 / 208)
-    assert bench.issue_floor_evals_per_s("lseFm_kernel") == pytest.approx(
-        1024 * 2.4e9 * 1024 / 288)
+        1024 * 2.4e9 * 1024 / 220)
+    assert bench.issue_floor_evals_per_s("lseFs_kernel") == pytest.approx(
+        1024 * 2.4e9 * 1024 / 314)
 
 
 def test_more_than_one_gpu_exits_with_a_message():
