@@ -282,10 +282,10 @@ __global__ void qrec3_kernel(const float4 *__restrict__ pts, int n_pad, float tw
 }
 
 // Row result: true potential from the (M, S) state, and the bias of this row
-// for the other pass (lw: the row's log2 weight).
-__device__ __forceinline__ void finish_row(float4 *qpts, uint16_t *qkrec, float *qpot, float lw,
-                                           size_t pt, size_t k, float4 p, float M, float S,
-                                           double eps_ln2, double c_next)
+// for the other pass (lw: the row's log2 weight), which is returned.
+__device__ __forceinline__ float finish_row(float4 *qpts, uint16_t *qkrec, float *qpot, float lw,
+                                            size_t pt, size_t k, float4 p, float M, float S,
+                                            double eps_ln2, double c_next)
 {
     const float sq = sq3(p.x, p.y, p.z);
     const double lse2 = (double)M + (double)lg2(S);
@@ -294,6 +294,7 @@ __device__ __forceinline__ void finish_row(float4 *qpts, uint16_t *qkrec, float 
     const float beta = lw == kNeg ? kNeg : bias_of(c_next, f, sq, lw);
     qpts[pt].w = beta;
     store_key_bias(qkrec + pt * kRec, beta);
+    return beta;
 }
 
 // part == nullptr: single split, finalise in place.
@@ -419,6 +420,22 @@ __device__ __forceinline__ f32x4 mfma4(bf16x8 a, bf16x8 b, f32x4 c)
 constexpr float kSumLo = 5.421010862e-20f;  // 2^-64
 constexpr float kSumHi = 1.2676506e30f;     // 2^100
 
+// LDS copy of a side's key records (per-pair launch, clouds of at most
+// kLdsMaxPoints points): record r's four 16-byte chunks at 16-byte index 4 r
+// + (c ^ ((r >> 1) & 3)).  A tile read has lane (kq, c16) take chunk kq of
+// record 16 t + c16; the XOR spreads the 8 lanes that share kq over all banks
+// (record stride 64 bytes alone would map pairs of them onto the same banks).
+constexpr int kLdsMaxPoints = 1024;
+__device__ __forceinline__ int lds_chunk(int r, int c) { return 4 * r + (c ^ ((r >> 1) & 3)); }
+
+// Bias pieces of record r in the LDS copy (slots 20..23 = chunk 2, bytes 8..15).
+__device__ __forceinline__ void store_key_bias_lds(uint4 *lds, int r, float beta)
+{
+    uint32_t h[3];
+    split3(beta, h);
+    reinterpret_cast<uint2 *>(&lds[lds_chunk(r, 2)])[1] = make_uint2(h[0] | h[1] << 16, h[2]);
+}
+
 // Stream of one wave: key tiles first, first + W, ... (cnt of them) against the
 // wave's 64 rows with the shift in Cn, accumulated into S as a sum of 2^(s - M)
 // (the shifted pass) or as the maximum of s - M (kMax, the pass that makes a
@@ -431,20 +448,27 @@ constexpr float kSumHi = 1.2676506e30f;     // 2^100
 // register sets take turns, so no operand is copied.  Key operands come through
 // a buffer resource: the tile offset rides in an SGPR (soffset), the lane's
 // offset is a constant VGPR, so there is no vector address arithmetic per tile.
-template <int W, bool kMax, int G = kGroups>
+// With kLds the key records come from a copy in LDS instead (lds: the pair's
+// records in the layout of lds_chunk), the same operands in the same order.
+template <int W, bool kMax, int G = kGroups, bool kLds = false>
 __device__ __forceinline__ void key_stream(const bf16x8 (&A)[G], const f32x4 (&Cn)[G],
                                            f32x4 (&S)[G], const uint16_t *kb, int nk_pad,
-                                           int lane_off, int first, int cnt)
+                                           int lane_off, int first, int cnt,
+                                           const uint4 *lds = nullptr)
 {
     const int last = first + (cnt > 0 ? cnt - 1 : 0) * W;
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
         (void *)kb, (short)0, nk_pad * kRec * (int)sizeof(uint16_t), 0x00020000);
     const int voff = lane_off * (int)sizeof(uint16_t);
+    const int lane_rec = lane_id() & 15, lane_chunk = lane_id() >> 4;
     auto key = [&](int k) {
         const int t = min(first + k * W, last);
-        return __builtin_bit_cast(
-            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                        krs, voff, t * (kTile * kRec * (int)sizeof(uint16_t)), 0));
+        if constexpr (kLds)
+            return __builtin_bit_cast(bf16x8, lds[lds_chunk(t * kTile + lane_rec, lane_chunk)]);
+        else
+            return __builtin_bit_cast(
+                bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                            krs, voff, t * (kTile * kRec * (int)sizeof(uint16_t)), 0));
     };
     // With W > 1 the four MFMAs of a tile are issued together ahead of its
     // exponentials (one wait on the first result instead of one per group;
@@ -491,12 +515,13 @@ __device__ __forceinline__ void key_stream(const bf16x8 (&A)[G], const f32x4 (&C
 // the (M, S) states, M carried as -Cn (+1e30 marks a state that has seen no key
 // yet).  The key operand of the next tile is loaded one tile ahead; the clamped
 // index keeps that load inside the pair's keys on the last tile.
-template <int W, int G = kGroups>
+template <int W, int G = kGroups, bool kLds = false>
 __device__ __forceinline__ void shifted_stream(const bf16x8 (&A)[G], const f32x4 (&Cn)[G],
                                                f32x4 (&S)[G], const uint16_t *kb, int nk_pad,
-                                               int lane_off, int first, int cnt)
+                                               int lane_off, int first, int cnt,
+                                               const uint4 *lds = nullptr)
 {
-    key_stream<W, false, G>(A, Cn, S, kb, nk_pad, lane_off, first, cnt);
+    key_stream<W, false, G, kLds>(A, Cn, S, kb, nk_pad, lane_off, first, cnt, lds);
 }
 
 // Query operands of a wave's 16 G rows.
@@ -554,16 +579,16 @@ __device__ __forceinline__ void wave_sums(const f32x4 (&Cn)[G], const f32x4 (&S)
 // block's keys (each wave its tiles, merged over the W waves through red) is
 // added to every row's M, and S is emptied for the shifted pass that follows.
 // With W > 1 every wave of the work-group must call it.
-template <int W, int G = kGroups>
+template <int W, int G = kGroups, bool kLds = false>
 __device__ __forceinline__ void exact_shifts(const bf16x8 (&A)[G], f32x4 (&Cn)[G], f32x4 (&S)[G],
                                              const uint16_t *kb, int nk_pad, int lane_off,
                                              int first, int cnt, float2 (*red)[kWave], int w,
-                                             int kq, int c16)
+                                             int kq, int c16, const uint4 *lds = nullptr)
 {
 #pragma unroll
     for (int g = 0; g < G; ++g)
         S[g] = f32x4{kNeg, kNeg, kNeg, kNeg};
-    key_stream<W, true, G>(A, Cn, S, kb, nk_pad, lane_off, first, cnt);
+    key_stream<W, true, G, kLds>(A, Cn, S, kb, nk_pad, lane_off, first, cnt, lds);
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
@@ -728,10 +753,14 @@ constexpr int kPairWaves = 16;
 // One wave: rows row0 .. row0 + 63 of pair b on side q against all keys of side k.
 // With stale set (the first updates of a cold start, where the potentials
 // are zeros and most pairs' shifts are far off) the shifts are made exact
-// before the first shifted pass instead of after a failed one.
+// before the first shifted pass instead of after a failed one.  With kLds the
+// keys' records are read from their LDS copy k_lds, and each finished row
+// writes its new bias pieces to the LDS copy of its own side, q_lds, as well.
+template <bool kLds>
 __device__ __forceinline__ void wave_rows(const Side3 &q, const Side3 &k, int b, int row0,
                                           float two_c, double eps_ln2, double c_next,
-                                          float2 *red, bool stale)
+                                          float2 *red, bool stale, const uint4 *k_lds,
+                                          uint4 *q_lds)
 {
     const int lane = lane_id();
     const int kq = lane >> 4, c16 = lane & 15;
@@ -747,7 +776,7 @@ __device__ __forceinline__ void wave_rows(const Side3 &q, const Side3 &k, int b,
     float M = 0.f, Sf = 0.f;
     const int row = row0 + lane;
     if (!stale) {
-        shifted_stream<1>(A, Cn, S, kb, k.n_pad, lane_off, 0, n_tiles);
+        shifted_stream<1, kGroups, kLds>(A, Cn, S, kb, k.n_pad, lane_off, 0, n_tiles, k_lds);
         wave_sums(Cn, S, red, kq, c16);
         __builtin_amdgcn_wave_barrier();
         M = red[lane].x;
@@ -757,37 +786,61 @@ __device__ __forceinline__ void wave_rows(const Side3 &q, const Side3 &k, int b,
         __builtin_amdgcn_wave_barrier();   // red is written again below
     }
     if (stale) {
-        exact_shifts<1>(A, Cn, S, kb, k.n_pad, lane_off, 0, n_tiles, nullptr, 0, kq, c16);
-        shifted_stream<1>(A, Cn, S, kb, k.n_pad, lane_off, 0, n_tiles);
+        exact_shifts<1, kGroups, kLds>(A, Cn, S, kb, k.n_pad, lane_off, 0, n_tiles, nullptr, 0,
+                                       kq, c16, k_lds);
+        shifted_stream<1, kGroups, kLds>(A, Cn, S, kb, k.n_pad, lane_off, 0, n_tiles, k_lds);
         __builtin_amdgcn_wave_barrier();
         wave_sums(Cn, S, red, kq, c16);
         __builtin_amdgcn_wave_barrier();
         M = red[lane].x;
         Sf = red[lane].y;
     }
-    if (row < q.n)
-        finish_row(q.pts, q.krec, q.pot, q.l2w[(size_t)b * q.n + row], (size_t)b * q.n_pad + row,
-                   (size_t)b * q.n + row, q.pts[(size_t)b * q.n_pad + row], M, Sf, eps_ln2,
-                   c_next);
+    if (row < q.n) {
+        const float beta = finish_row(q.pts, q.krec, q.pot, q.l2w[(size_t)b * q.n + row],
+                                      (size_t)b * q.n_pad + row, (size_t)b * q.n + row,
+                                      q.pts[(size_t)b * q.n_pad + row], M, Sf, eps_ln2, c_next);
+        if constexpr (kLds)
+            store_key_bias_lds(q_lds, row, beta);
+    }
     __builtin_amdgcn_wave_barrier();   // red is reused by the next block
 }
 
+// kLds (both clouds of at most kLdsMaxPoints points): the key records of both
+// sides are copied into LDS once per launch (128 KB), and the passes read
+// their keys from there; between passes only the bias pieces of the records
+// change, and the rows that produce them write them to the copy as well.
+template <bool kLds>
 __global__ __launch_bounds__(kPairWaves *kWave) void lse3p_kernel(Side3 x, Side3 y, int iters,
                                                                   float two_c, double eps_ln2,
                                                                   double c_next_last, int cold)
 {
     __shared__ float2 red[kPairWaves][kWave];
+    __shared__ uint4 recs[2][kLds ? kLdsMaxPoints * kRec / 8 : 1];   // unused without kLds
     const int b = blockIdx.x;
     const int w = wave_id_uniform();
     const double c_same = 0.5 * (double)two_c;
+    if constexpr (kLds) {
+        const Side3 *side[2] = {&x, &y};
+#pragma unroll
+        for (int sd = 0; sd < 2; ++sd) {
+            const uint4 *src =
+                reinterpret_cast<const uint4 *>(side[sd]->krec + (size_t)b * side[sd]->n_pad * kRec);
+            const int chunks = side[sd]->n_pad * (kRec / 8);   // n_pad <= kLdsMaxPoints
+            for (int e = threadIdx.x; e < chunks; e += kPairWaves * kWave)
+                recs[sd][lds_chunk(e >> 2, e & 3)] = src[e];
+        }
+        __syncthreads();
+    }
     for (int it = 0; it < iters; ++it) {
         const bool stale = cold && it == 0;
         for (int rb = w; rb < x.n_pad / kWave; rb += kPairWaves)
-            wave_rows(x, y, b, rb * kWave, two_c, eps_ln2, c_same, red[w], stale);
+            wave_rows<kLds>(x, y, b, rb * kWave, two_c, eps_ln2, c_same, red[w], stale, recs[1],
+                            recs[0]);
         __syncthreads();   // f and the X-side biases are complete
         const double cn = it + 1 < iters ? c_same : c_next_last;
         for (int rb = w; rb < y.n_pad / kWave; rb += kPairWaves)
-            wave_rows(y, x, b, rb * kWave, two_c, eps_ln2, cn, red[w], stale);
+            wave_rows<kLds>(y, x, b, rb * kWave, two_c, eps_ln2, cn, red[w], stale, recs[0],
+                            recs[1]);
         __syncthreads();   // g and the Y-side biases are complete
     }
 }
@@ -960,8 +1013,14 @@ hipError_t launch_lse3_pairwise(Side3 x, Side3 y, int B, float eps, int iters, f
                                 bool cold, hipStream_t st)
 {
     const float c = scale_of(eps);
-    hipLaunchKernelGGL(lse3p_kernel, dim3(B), dim3(kPairWaves * kWave), 0, st, x, y, iters,
-                       2.0f * c, 1.0 / (double)c, (double)scale_of(eps_next), cold ? 1 : 0);
+    if (x.n_pad <= kLdsMaxPoints && y.n_pad <= kLdsMaxPoints)
+        hipLaunchKernelGGL(lse3p_kernel<true>, dim3(B), dim3(kPairWaves * kWave), 0, st, x, y,
+                           iters, 2.0f * c, 1.0 / (double)c, (double)scale_of(eps_next),
+                           cold ? 1 : 0);
+    else
+        hipLaunchKernelGGL(lse3p_kernel<false>, dim3(B), dim3(kPairWaves * kWave), 0, st, x, y,
+                           iters, 2.0f * c, 1.0 / (double)c, (double)scale_of(eps_next),
+                           cold ? 1 : 0);
     return hipGetLastError();
 }
 
