@@ -130,6 +130,18 @@ def test_split_key_ranges_with_stale_shifts(B, n, m, eps, iters):
     check_potentials(c, eps, iters)
 
 
+def test_split_keys_with_xcd_placement_and_repair():
+    # 4 pairs of 128 rows against 20000 keys: 2 row blocks x 78 key splits x 4 pairs =
+    # 624 work-groups (a multiple of 8, so batches are placed XCD by XCD), far from
+    # the origin at a small eps, so merged rows go stale and the repair launch
+    # (8 work-groups, also placed by XCD) recomputes them; twice, bit for bit
+    c = workloads.random_case(83, 4, 128, 20000, 3, weights="dirichlet", spread=4.0)
+    c = dict(c, X=c["X"] + np.float32(10.0), Y=c["Y"] + np.float32(10.0))
+    f1, g1, _, _ = check_potentials(c, [0.003], [3])
+    f2, g2, _ = run_gpu(c, [0.003], [3])
+    assert torch.equal(f1, f2) and torch.equal(g1, g2)
+
+
 @pytest.mark.parametrize("n,m", [(1 << 24, 64), (64, 1 << 24)])
 def test_largest_cloud_per_pair(n, m):
     # 2^24 points on one side (the largest the boundary accepts) against 64 on the
@@ -155,7 +167,9 @@ def test_most_pairs_per_call():
     ro, co, vo, oo = oracle.plan_coo(c["X"], c["Y"], c["a"], c["b"], f32, g32,
                                      float(np.float32(eps)), 1e-8)
     lo, dXo = oracle.loss_grad(c["X"], c["Y"], ro, co, vo.astype(np.float32), oo)
-    assert abs(int(offs[-1]) - int(oo[-1])) <= 1e-4 * int(oo[-1])
+    # the support of every pair, not only the total count
+    got = tuple(t.cpu().numpy() for t in (rows, cols, vals, offs))
+    compare_coo_all_pairs(got, (ro, co, vo, oo), n, m)
     np.testing.assert_allclose(host(loss), lo, rtol=1e-4)
     assert rel_inf(host(dX), dXo) <= 1e-4
 
@@ -324,6 +338,32 @@ def compare_coo(got, ref, m, thr_val, band=1e-3, val_tol=1e-4):
     gv, rv = got[2][ig].astype(np.float64), ref[2][ir]
     assert np.all(np.abs(gv - rv) <= val_tol * rv)
     return len(common)
+
+
+def compare_coo_all_pairs(got, ref, n, m, thr=1e-8, band=1e-3, val_tol=1e-4):
+    """got/ref: (rows, cols, vals, pair_offsets) of a whole batch.  Per pair, the
+    supports are equal except entries within `band` (relative) of that pair's
+    threshold value, and every pair's entries are in strictly increasing
+    (row, column) order; values agree on the common support."""
+    def keys(rows, cols, offs):
+        pair = np.repeat(np.arange(len(offs) - 1, dtype=np.int64), np.diff(offs))
+        return pair, (pair * n + rows.astype(np.int64)) * m + cols
+    gp, gk = keys(*got[:2], got[3])
+    rp, rk = keys(*ref[:2], ref[3])
+    assert np.all(np.diff(gk) > 0), "entries out of (pair, row, column) order"
+    B = len(ref[3]) - 1
+    vmax = np.zeros(B)
+    nonempty = np.diff(ref[3]) > 0
+    vmax[nonempty] = np.maximum.reduceat(ref[2], ref[3][:-1][nonempty])
+    thr_val = thr * vmax
+    only_g = ~np.isin(gk, rk)
+    only_r = ~np.isin(rk, gk)
+    for v, pp in ((got[2][only_g], gp[only_g]), (ref[2][only_r], rp[only_r])):
+        assert np.all(np.abs(v / thr_val[pp] - 1.0) <= band), "support differs off the threshold"
+    common, ig, ir = np.intersect1d(gk, rk, assume_unique=True, return_indices=True)
+    gv, rv = got[2][ig].astype(np.float64), ref[2][ir].astype(np.float64)
+    assert np.all(np.abs(gv - rv) <= val_tol * rv)
+    return len(common), int(only_g.sum()), int(only_r.sum())
 
 
 def check_coo_given_potentials(c, eps, fo, go, pairs=None, thr=1e-8):
@@ -523,13 +563,26 @@ def test_workload_pair_1k():
     check_workload_potentials("pair-1k", 1e-4)
 
 
-@pytest.mark.parametrize("name,pairs", [("sphere-2k", [0, 31]), ("blobs-1k", [0, 1, 128, 255])])
+@pytest.mark.parametrize("name,pairs", [("sphere-2k", list(range(32))),
+                                        ("blobs-1k", sorted(set(range(0, 256, 4)) | {1, 255}))])
 def test_workload_sparse_plan_and_loss(name, pairs):
     w, gold, f, g = check_workload_potentials(name, 1e-4)
     eps = float(w["eps"][-1])
-    # plan: both sides from the oracle's potentials (rounded to fp32), sampled pairs
-    check_coo_given_potentials(w, eps, gold["f"].astype(np.float64),
-                               gold["g"].astype(np.float64), pairs=pairs)
+    # plan: both sides from the oracle's potentials (rounded to fp32): support,
+    # order and values on every sphere-2k pair and 66 of the 256 blobs-1k pairs
+    f32, g32 = gold["f"].astype(np.float32), gold["g"].astype(np.float32)
+    rows, cols, vals, offs = check_coo_given_potentials(
+        w, eps, f32.astype(np.float64), g32.astype(np.float64), pairs=pairs)
+    # loss and dL/dX of the same pairs: the GPU on its plan, the oracle on its own
+    X, Y = points(w)
+    loss, dX = sk.loss_grad(X, Y, dev(rows), dev(cols), dev(vals), dev(offs))
+    loss, dX = host(loss), host(dX)
+    for p in pairs:
+        ro, co, vo, oo = oracle.plan_coo(w["X"][p], w["Y"][p], w["a"][p], w["b"][p], f32[p],
+                                         g32[p], float(np.float32(eps)), w["threshold"])
+        lo, dXo = oracle.loss_grad(w["X"][p], w["Y"][p], ro, co, vo.astype(np.float32), oo)
+        assert abs(loss[p] - lo[0]) <= 1e-4 * abs(lo[0]), f"loss pair {p}"
+        assert rel_inf(dX[p], dXo[0]) <= 1e-4, f"dX pair {p}"
     # full GPU chain against the oracle's chain, every pair
     X, Y = points(w)
     rows, cols, vals, offs = sk.plan_coo(X, Y, dev(w["a"]), dev(w["b"]), f, g, eps,
