@@ -30,6 +30,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "sinkhorn_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# tests/test_oracle_mutations.py only: load this build (a deliberately broken
+# copy of the oracle) instead, to check that the pins catch the mistake
+_LIB_OVERRIDE = os.environ.get("SK_ORACLE_LIB")
 
 PINS = {
     "half_update": "scipy logsumexp; brute-force assignment; 2x2 closed form; marginals",
@@ -69,8 +72,11 @@ _lib = None
 def _load():
     global _lib
     if _lib is None:
-        build()
-        lib = ctypes.CDLL(_LIB)
+        if _LIB_OVERRIDE:
+            lib = ctypes.CDLL(_LIB_OVERRIDE)
+        else:
+            build()
+            lib = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
         i32, i64, f64 = ctypes.c_int, ctypes.c_int64, ctypes.c_double
         lib.oracle_num_threads.restype = i32

@@ -70,8 +70,12 @@ __device__ __forceinline__ float bias_of(double c, float pot, float sq, float l2
 // bits, fp32's exponent range): v = v0 + v1 + v2.  Products of two bf16 pieces
 // are exact in the MFMA's fp32 accumulator, so
 //     q . y = sum_u sum_(a,b) q_u,a y_u,b     over (a,b) in kPairs
-// reproduces the fp32 dot product up to the dropped pieces of relative size
-// 2^-32 and the accumulator's fp32 rounding.  Record slots (one 16x16x32 MFMA
+// reproduces the fp32 dot product up to the accumulator's fp32 rounding and
+// the dropped products of pieces (a, b) with a + b > 2.  With round-to-nearest
+// pieces |v1| <= 2^-8 |v| and |v2| <= 2^-16 |v|, so (1, 2) and (2, 1) are each
+// at most 2^-24 |q_u y_u| and (2, 2) 2^-32 |q_u y_u|: a score error of at most
+// about 2^-23 sum_u |q_u y_u|, the size of one fp32 rounding of the products
+// (the vector path's fp32 FMAs round at 2^-24 per operation).  Record slots (one 16x16x32 MFMA
 // k-range): 6u + p holds piece kPairs[p] of coordinate u (query: q's piece a,
 // key: y's piece b); slots 20..22 hold the bias pieces (key) or 1 (query);
 // the rest are zero.
