@@ -682,7 +682,10 @@ int oracle_coo_normalize(const int32_t *rows, const int32_t *cols, double *vals,
  * with ma, mb the plan's row and column sums.  Eliminating df gives
  *   (diag(mb) - P^T diag(1/ma) P) dg = c - P^T (r / ma),
  * singular only along the constant vector (df + t, dg - t leave dP unchanged);
- * here dg_0 = 0 fixes it and the rest is solved by Cholesky.  Then
+ * here dg = 0 on the first column with plan mass fixes it and the rest is solved
+ * by Cholesky.  A column without plan mass (zero weight: its row and column of
+ * the system are 0) keeps dg = 0 and stays out of the solve; it enters nothing
+ * else, as P is 0 on it.  Then
  *   HV_i = sum_j 2 dP_ij (x_i - y_j) + 2 ma_i v_i.
  * Dense in n x m: for the small cases the tests use.  Returns 0, or -1 when a
  * system is not positive definite.
@@ -703,6 +706,7 @@ int oracle_hvp(const double *X, const double *Y, const double *a, const double *
     double *df = (double *)malloc(sizeof(double) * (size_t)n);
     double *la = (double *)malloc(sizeof(double) * (size_t)n);
     double *lb = (double *)malloc(sizeof(double) * (size_t)m);
+    int *idx = (int *)malloc(sizeof(int) * (size_t)m);
     int rc = 0;
     for (int p = 0; p < B && rc == 0; ++p) {
         const double *Xp = X + (size_t)p * n * d, *Yp = Y + (size_t)p * m * d;
@@ -748,40 +752,50 @@ int oracle_hvp(const double *X, const double *Y, const double *a, const double *
                 S[(size_t)j * m + l] = t;
             }
         }
-        /* dg_0 = 0; Cholesky of S[1:,1:] */
-        const int q = m - 1;
-        dg[0] = 0.0;
-        for (int j = 0; j < q; ++j) {
+        /* dg = 0 on the pinned column and on columns without mass; Cholesky of
+           S over the other columns (idx) */
+        int q = 0, pin = -1;
+        for (int j = 0; j < m; ++j) {
+            dg[j] = 0.0;
+            if (mb[j] > 0.0) {
+                if (pin < 0)
+                    pin = j;
+                else
+                    idx[q++] = j;
+            }
+        }
+        for (int j = 0; j < q && rc == 0; ++j) {
+            const size_t rj = (size_t)idx[j] * m;
             for (int l = 0; l <= j; ++l) {
-                double s = S[(size_t)(j + 1) * m + (l + 1)];
+                const size_t rl = (size_t)idx[l] * m;
+                double s = S[rj + idx[l]];
                 for (int k = 0; k < l; ++k)
-                    s -= S[(size_t)(j + 1) * m + (k + 1)] * S[(size_t)(l + 1) * m + (k + 1)];
+                    s -= S[rj + idx[k]] * S[rl + idx[k]];
                 if (j == l) {
                     if (!(s > 0.0)) {
                         rc = -1;
                         break;
                     }
-                    S[(size_t)(j + 1) * m + (j + 1)] = sqrt(s);
+                    S[rj + idx[j]] = sqrt(s);
                 } else {
-                    S[(size_t)(j + 1) * m + (l + 1)] = s / S[(size_t)(l + 1) * m + (l + 1)];
+                    S[rj + idx[l]] = s / S[rl + idx[l]];
                 }
             }
-            if (rc)
-                break;
         }
         if (rc)
             break;
-        for (int j = 0; j < q; ++j) {   /* L y = rhs[1:] */
-            double s = rhs[j + 1];
+        for (int j = 0; j < q; ++j) {   /* L y = rhs */
+            const size_t rj = (size_t)idx[j] * m;
+            double s = rhs[idx[j]];
             for (int k = 0; k < j; ++k)
-                s -= S[(size_t)(j + 1) * m + (k + 1)] * dg[k + 1];
-            dg[j + 1] = s / S[(size_t)(j + 1) * m + (j + 1)];
+                s -= S[rj + idx[k]] * dg[idx[k]];
+            dg[idx[j]] = s / S[rj + idx[j]];
         }
         for (int j = q - 1; j >= 0; --j) {   /* L^T dg = y */
-            double s = dg[j + 1];
+            double s = dg[idx[j]];
             for (int k = j + 1; k < q; ++k)
-                s -= S[(size_t)(k + 1) * m + (j + 1)] * dg[k + 1];
-            dg[j + 1] = s / S[(size_t)(j + 1) * m + (j + 1)];
+                s -= S[(size_t)idx[k] * m + idx[j]] * dg[idx[k]];
+            dg[idx[j]] = s / S[(size_t)idx[j] * m + idx[j]];
         }
         for (int i = 0; i < n; ++i) {
             double s = r[i];
@@ -803,6 +817,6 @@ int oracle_hvp(const double *X, const double *Y, const double *a, const double *
         }
     }
     free(P); free(dC); free(S); free(ma); free(mb); free(r); free(c); free(rhs); free(dg);
-    free(df); free(la); free(lb);
+    free(df); free(la); free(lb); free(idx);
     return rc;
 }

@@ -60,6 +60,9 @@ MUTATIONS = [
     ("Hessian-vector product with a halved row term",
      "r[i] += pij * 2.0 * dot;",
      "r[i] += pij * dot;"),
+    ("Hessian-vector product with columns of no mass kept in the solve",
+     "            if (mb[j] > 0.0) {\n                if (pin < 0)",
+     "            if (mb[j] >= 0.0) {\n                if (pin < 0)"),
 ]
 
 

@@ -574,3 +574,20 @@ def test_hvp_is_symmetric():
     HU = oracle.hvp(X, Y, a, b, f, g, eps, U)[0]
     HV = oracle.hvp(X, Y, a, b, f, g, eps, V)[0]
     assert abs((U * HV).sum() - (V * HU).sum()) <= 1e-10 * np.abs(U * HV).sum()
+
+
+def test_hvp_zero_weight_points_are_absent_points():
+    # a point of weight 0 carries no plan mass: the HVP of the other rows equals
+    # that of the problem without the point, and the row of weight 0 gets 0
+    X, Y, a, b = _case(59, 10, 9, d=3)
+    a[3], b[[0, 5]] = 0.0, 0.0
+    a, b = a / a.sum(), b / b.sum()
+    eps = 0.1
+    f, g = _converge(X, Y, a, b, eps, 3000)
+    V = np.random.default_rng(6).normal(size=X.shape)
+    HV = oracle.hvp(X, Y, a, b, f, g, eps, V)[0]
+    kx, ky = np.arange(10) != 3, ~np.isin(np.arange(9), [0, 5])
+    f, g = np.ravel(f), np.ravel(g)
+    HVr = oracle.hvp(X[kx], Y[ky], a[kx], b[ky], f[kx], g[ky], eps, V[kx])[0]
+    assert np.all(HV[3] == 0.0)
+    np.testing.assert_allclose(HV[kx], HVr, rtol=1e-9, atol=1e-12 * np.abs(HVr).max())
