@@ -477,10 +477,11 @@ def main():
         t_dg = timed(dense_grad, 2)
         assert all(bool(torch.isfinite(t).all()) for t in dg_out)
         line["phases_ms"]["dense_grad_and_projection_both_sides"] = t_dg * 1e3
-        if d <= 16:
+        hv_bytes = sk.workspace_bytes(sk.SK_OP_HVP, B, n, m, d, dt)
+        if hv_bytes > 0:
             # Hessian-vector product in X along the gradient direction, 20 CG steps
-            hv_ws = torch.empty(sk.workspace_bytes(sk.SK_OP_HVP, B, n, m, d, dt),
-                                dtype=torch.uint8, device=dev)
+            # (fp64 plan passes for d <= 16, matrix-core passes for bf16 d = 32 / 64)
+            hv_ws = torch.empty(hv_bytes, dtype=torch.uint8, device=dev)
             V, HV = dg_out[0].clone(), torch.empty_like(dg_out[0])
 
             def hvp():

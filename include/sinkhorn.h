@@ -257,11 +257,17 @@ int sinkhorn_dense_grad(const void *X, const void *Y, int dtype,
  * system, (diag(mb) - P^T diag(1/ma) P) dg = c - P^T (r/ma), by `cg_iters`
  * conjugate-gradient steps from 0 (ma, mb: the plan's row and column sums;
  * r_i, c_j: row and column sums of P_ij 2 (x_i - y_j).v_i); every product with
- * P streams the plan with log P in fp64, nothing n x m is stored.
+ * P streams the plan, nothing n x m is stored.
  * V, HV: [B][n][d] fp32.  cg_residual [B] (device, may be NULL) receives the
  * final conjugate-gradient residual relative to the right-hand side.
- * Supported for d <= 16 (SK_ERR_UNSUPPORTED above); workspace
- * sinkhorn_workspace_bytes(SK_OP_HVP, ...).
+ * Supported for d <= 16 (log P in fp64, either dtype) and for bf16 points with
+ * d = 32 or 64 (SK_ERR_UNSUPPORTED otherwise).  The bf16 d = 32/64 path runs
+ * every plan product on the matrix cores: plan entries from fp32 scores as in
+ * the dense gradient, the direction V in two bf16 pieces (16 bits), fp32 sums;
+ * it needs X and Y at 16-byte aligned addresses (SK_ERR_INVALID_ARG) and
+ * potentials near the solution: a pair with a positive-weight row whose plan
+ * mass, divided by its weight, falls outside [2^-64, 2^100] gets NaN in HV and
+ * cg_residual.  Workspace sinkhorn_workspace_bytes(SK_OP_HVP, ...).
  */
 int sinkhorn_hvp(const void *X, const void *Y, int dtype,
                  const float *a, const float *b,

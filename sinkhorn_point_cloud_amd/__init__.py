@@ -483,8 +483,10 @@ def coo_normalize(plan, transpose, a, b, n, m, iters, err=True, workspace=None):
 
 def hvp(X, Y, a, b, f, g, eps: float, V, cg_iters: int = 100, workspace=None, out=None):
     """(HV, cg_residual): Hessian-vector product of the entropic OT value in X along V
-    [B,n,d] (d <= 16), at the plan of potentials f, g; cg_residual [B] is the final
-    conjugate-gradient residual relative to the right-hand side."""
+    [B,n,d] (d <= 16, or bf16 points with d = 32 or 64 on the matrix cores), at the
+    plan of potentials f, g; cg_residual [B] is the final conjugate-gradient residual
+    relative to the right-hand side (NaN, with HV, for a pair whose potentials are
+    too far from a solution for the matrix-core path)."""
     lib = load_library()
     X, Y, dt = _points(X, Y)
     B, n, d = X.shape

@@ -31,7 +31,6 @@ int hip_fail(hipError_t e, const char *where)
 constexpr int kMaxPoints = 1 << 24;
 constexpr int kMaxPairs = 65535;     // pairs index a grid dimension (y or z), at most 65535
 constexpr int kMaxNormDim = 4096;   // dimensions accepted by the normalisation
-constexpr int kPad = 64;
 
 // Bump allocator over the caller's workspace (256-byte aligned pieces).
 // Pieces of the caller's workspace, each at a 256-byte aligned address (the
@@ -235,6 +234,53 @@ HvpWs carve_hvp(Carve &c, int B, int n, int m, int d)
     return w;
 }
 
+HvpFeatWs carve_hvp_feat(Carve &c, int B, int n, int m, int d)
+{
+    HvpFeatWs w;
+    const int np = round_up(n, kPad), mp = round_up(m, kPad);
+    const size_t Bn = (size_t)B * n, Bm = (size_t)B * m, Bnp = (size_t)B * np,
+                 Bmp = (size_t)B * mp;
+    const HvpFeatSizes z = hvp_feat_sizes(B, n, m, d);
+    w.y.pts = nullptr;
+    w.y.bias = c.take<float>(Bmp);
+    w.y.pot = nullptr;
+    w.y.l2w = c.take<float>(Bm);
+    w.y.sq = c.take<float>(Bm);
+    w.y.redo = nullptr;
+    w.y.n = m;
+    w.y.n_pad = mp;
+    w.yt = c.take<uint16_t>(Bmp * d);
+    w.h = c.take<float>(Bnp);
+    w.wa = c.take<float>(Bnp);
+    w.wu = c.take<float>(Bnp);
+    w.wt = c.take<float>(Bnp);
+    w.vh = c.take<uint16_t>(Bnp * d);
+    w.vl = c.take<uint16_t>(Bnp * d);
+    w.vth = c.take<uint16_t>(Bnp * d);
+    w.vtl = c.take<uint16_t>(Bnp * d);
+    w.u32 = c.take<float>(Bmp);
+    w.x32 = c.take<float>(Bmp);
+    w.part_r = c.take<float>(z.part_r);
+    w.part_rv = c.take<float>(z.part_rv);
+    w.part_rq = c.take<float>(z.part_rv);
+    w.part_c = c.take<float>(z.part_c);
+    w.part_cv = c.take<float>(z.part_cv);
+    w.mrow = c.take<double>(Bn);
+    w.ma = c.take<double>(Bn);
+    w.tv = c.take<double>(Bn);
+    w.D1 = c.take<double>(Bn * d);
+    w.Tv = c.take<double>(Bn * d);
+    w.mb = c.take<double>(Bm);
+    w.rhs = c.take<double>(Bm);
+    w.x = c.take<double>(Bm);
+    w.res = c.take<double>(Bm);
+    w.dir = c.take<double>(Bm);
+    w.rr = c.take<double>(B);
+    w.rr0 = c.take<double>(B);
+    w.bad = c.take<int>(B);
+    return w;
+}
+
 size_t ws_size(int op, int B, int n, int m, int d, int dtype)
 {
     Carve c{nullptr};
@@ -246,6 +292,8 @@ size_t ws_size(int op, int B, int n, int m, int d, int dtype)
         carve_loss(c, B, n);
     else if (op == SK_OP_DENSE_GRAD)
         carve_grad(c, B, n, m, d, dtype);
+    else if (hvp_matrix_cores(dtype, d))
+        carve_hvp_feat(c, B, n, m, d);
     else
         carve_hvp(c, B, n, m, d);
     return c.off + 256;
@@ -452,7 +500,7 @@ extern "C" {
 size_t sinkhorn_workspace_bytes(int op, int B, int n, int m, int d, int dtype)
 {
     if (op < SK_OP_POTENTIALS || op > SK_OP_HVP || !shape_ok(B, n, m, d) ||
-        (op == SK_OP_HVP && d > kMaxHvpDim) ||
+        (op == SK_OP_HVP && d > kMaxHvpDim && !hvp_matrix_cores(dtype, d)) ||
         (dtype != SK_F32 && dtype != SK_BF16) || !supported(dtype, d))
         return 0;
     return ws_size(op, B, n, m, d, dtype);
@@ -702,8 +750,16 @@ int sinkhorn_hvp(const void *X, const void *Y, int dtype, const float *a, const 
     int rc = check_common(X, Y, dtype, B, n, m, d);
     if (rc)
         return rc;
-    if (d > kMaxHvpDim)
-        return fail(SK_ERR_UNSUPPORTED, "Hessian-vector products need d <= %d (d=%d)", kMaxHvpDim,
+    const bool mfma = hvp_matrix_cores(dtype, d);
+    if (d > kMaxHvpDim && !mfma)
+        return fail(SK_ERR_UNSUPPORTED,
+                    "Hessian-vector products need d <= %d, or bf16 points with d = 32 or 64 "
+                    "(d=%d)",
+                    kMaxHvpDim, d);
+    if (mfma && ((uintptr_t)X % 16 != 0 || (uintptr_t)Y % 16 != 0))
+        return fail(SK_ERR_INVALID_ARG,
+                    "Hessian-vector products of bf16 points with d = %d need X and Y at "
+                    "16-byte aligned addresses",
                     d);
     if (!f || !g || !V || !HV)
         return fail(SK_ERR_INVALID_ARG, "f, g, V and HV must be non-NULL device pointers");
@@ -716,8 +772,15 @@ int sinkhorn_hvp(const void *X, const void *Y, int dtype, const float *a, const 
         return rc;
     hipStream_t st = (hipStream_t)stream;
     Carve c{(char *)ws};
-    HvpWs w = carve_hvp(c, B, n, m, d);
     hipError_t e;
+    if (mfma) {
+        HvpFeatWs w = carve_hvp_feat(c, B, n, m, d);
+        if ((e = launch_hvp_feat(X, Y, a, b, f, g, V, B, n, m, d, eps, cg_iters, HV, cg_residual,
+                                 w, st)))
+            return hip_fail(e, "Hessian-vector product (matrix cores)");
+        return SK_OK;
+    }
+    HvpWs w = carve_hvp(c, B, n, m, d);
     if ((e = launch_log_weights(a, B, n, w.la, st)) || (e = launch_log_weights(b, B, m, w.lb, st)))
         return hip_fail(e, "log weights");
     const double inv_eps = 1.0 / (double)eps;

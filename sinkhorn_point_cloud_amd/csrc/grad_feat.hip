@@ -24,16 +24,12 @@
 //     two bf16 pieces, hi + lo, which keep 16 of its bits.  The B operand
 //     (keys 4 (l / 16) + e, dim l % 16 of a 16-dim block) is one 8-byte load
 //     from a transposed copy of the keys, Yt[d][m_pad].
-// Lane layouts of both instructions were checked with in-bounds probes:
-// 16x16x32: A[l % 16][8 (l / 16) + e], B[8 (l / 16) + e][l % 16]; 16x16x16:
-// A[l % 16][4 (l / 16) + e], B[4 (l / 16) + e][l % 16]; both give
-// D[4 (l / 16) + r][l % 16] in register r.
 //
 // A work-group is 4 waves on 64 rows, each wave taking every 4th key tile; the
 // waves merge in LDS in a fixed order.  A row block with a row whose mass
 // falls outside [2^-64, 2^100] (potentials far from solving these weights) is
 // flagged; the fp64 plan pass redoes it.
-#include "common.h"
+#include "mfma_bf16.h"
 
 namespace sk {
 namespace {
@@ -43,33 +39,6 @@ constexpr int kKeysG = 16;
 constexpr int kGroupsG = 4;
 constexpr float kMassLo = 5.421010862e-20f;  // 2^-64
 constexpr float kMassHi = 1.2676506e30f;     // 2^100
-
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ bf16x8 load8(const uint16_t *p)
-{
-    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(p));
-}
-
-__device__ __forceinline__ i16x4 load4(const uint16_t *p)
-{
-    return __builtin_bit_cast(i16x4, *reinterpret_cast<const uint2 *>(p));
-}
-
-// four fp32 values -> hi and lo bf16 pieces (round to nearest even, the
-// hardware conversion), v ~ hi + lo to 16 bits
-__device__ __forceinline__ void split2(const float (&v)[4], i16x4 &hi, i16x4 &lo)
-{
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const __bf16 h = (__bf16)v[e];
-        const __bf16 l = (__bf16)(v[e] - (float)h);
-        hi[e] = __builtin_bit_cast(short, h);
-        lo[e] = __builtin_bit_cast(short, l);
-    }
-}
 
 template <int DK>
 __global__ __launch_bounds__(kWavesG *kWave) void gradFm_kernel(

@@ -21,6 +21,8 @@
 // passes; the four waves of a work-group split the keys and merge in LDS in a
 // fixed order.  Conjugate-gradient vectors and dot products are fp64; one
 // work-group per pair reduces in a fixed order.  Deterministic throughout.
+// bf16 clouds with d = 32 or 64 take the matrix-core passes of hvp_feat.hip,
+// which share the conjugate-gradient kernels below.
 #include "plan_eval.h"
 
 namespace sk {
@@ -253,21 +255,35 @@ __device__ double block_sum(double v, double *sm)
     return r;
 }
 
-// x = 0, res = rhs, dir = rhs, rr = rr0 = |rhs|^2 (one work-group per pair)
+// x = 0, res = rhs, dir = rhs, rr = rr0 = |rhs|^2 (one work-group per pair);
+// x32 / dir32 (if given, [B][m_pad]) receive fp32 copies of x and dir.  With
+// project, rhs is first taken orthogonal to the constants (S's null space).
 __global__ __launch_bounds__(256) void cg_start(const double *__restrict__ rhs, int m,
                                                 double *__restrict__ x, double *__restrict__ res,
                                                 double *__restrict__ dir, double *__restrict__ rr,
-                                                double *__restrict__ rr0)
+                                                double *__restrict__ rr0, float *__restrict__ x32,
+                                                float *__restrict__ dir32, int m_pad, int project)
 {
     __shared__ double sm[256];
     const int b = blockIdx.x;
+    double mean = 0.0;
+    if (project) {
+        double acc = 0.0;
+        for (int j = threadIdx.x; j < m; j += 256)
+            acc += rhs[(size_t)b * m + j];
+        mean = block_sum(acc, sm) / (double)m;
+    }
     double acc = 0.0;
     for (int j = threadIdx.x; j < m; j += 256) {
         const size_t k = (size_t)b * m + j;
-        const double v = rhs[k];
+        const double v = rhs[k] - mean;
         x[k] = 0.0;
         res[k] = v;
         dir[k] = v;
+        if (dir32) {
+            x32[(size_t)b * m_pad + j] = 0.f;
+            dir32[(size_t)b * m_pad + j] = (float)v;
+        }
         acc = fma(v, v, acc);
     }
     const double s = block_sum(acc, sm);
@@ -277,36 +293,78 @@ __global__ __launch_bounds__(256) void cg_start(const double *__restrict__ rhs, 
     }
 }
 
+// q2_j of pair b: the fp64 vector, or the sum of S fp32 partials [S][B][m_pad]
+// added in split order
+__device__ __forceinline__ double q2_at(const double *q2, const float *part, int S, int B,
+                                        int m, int m_pad, int b, int j)
+{
+    if (!part)
+        return q2[(size_t)b * m + j];
+    double s = 0.0;
+    for (int p = 0; p < S; ++p)
+        s += (double)part[((size_t)p * B + b) * m_pad + j];
+    return s;
+}
+
 // One conjugate-gradient step, with S dir = mb o dir - q2 (q2 = P^T((P dir)/ma)).
+// A pair whose residual has reached stop2 * rr0 (squared) is left as it is.  With
+// project, the new residual is taken orthogonal to the constants, so that
+// rounding does not feed S's null space (which does not change HV: a constant
+// added to dg moves df by minus that constant and the two uses cancel).
 __global__ __launch_bounds__(256) void cg_step(const double *__restrict__ mb,
-                                               const double *__restrict__ q2, int m,
-                                               double *__restrict__ x, double *__restrict__ res,
-                                               double *__restrict__ dir, double *__restrict__ rr)
+                                               const double *__restrict__ q2,
+                                               const float *__restrict__ q2_part, int S, int B,
+                                               int m, int m_pad, double *__restrict__ x,
+                                               double *__restrict__ res, double *__restrict__ dir,
+                                               double *__restrict__ rr,
+                                               const double *__restrict__ rr0, double stop2,
+                                               int project, float *__restrict__ x32,
+                                               float *__restrict__ dir32)
 {
     __shared__ double sm[256];
     const int b = blockIdx.x;
+    const double rr_old = rr[b];
+    if (!(rr_old > stop2 * rr0[b]))   // uniform over the work-group
+        return;
     double acc = 0.0;
     for (int j = threadIdx.x; j < m; j += 256) {
         const size_t k = (size_t)b * m + j;
-        const double q = fma(mb[k], dir[k], -q2[k]);
+        const double q = fma(mb[k], dir[k], -q2_at(q2, q2_part, S, B, m, m_pad, b, j));
         acc = fma(dir[k], q, acc);
     }
     const double pq = block_sum(acc, sm);
-    const double rr_old = rr[b];
     const double alpha = pq > 0.0 ? rr_old / pq : 0.0;
     acc = 0.0;
+    double rsum = 0.0;
     for (int j = threadIdx.x; j < m; j += 256) {
         const size_t k = (size_t)b * m + j;
-        const double q = fma(mb[k], dir[k], -q2[k]);
+        const double q = fma(mb[k], dir[k], -q2_at(q2, q2_part, S, B, m, m_pad, b, j));
         x[k] = fma(alpha, dir[k], x[k]);
-        res[k] = fma(-alpha, q, res[k]);
-        acc = fma(res[k], res[k], acc);
+        const double r = fma(-alpha, q, res[k]);
+        res[k] = r;
+        acc = fma(r, r, acc);
+        rsum += r;
     }
-    const double rr_new = block_sum(acc, sm);
+    double rr_new;
+    if (project) {
+        const double mean = block_sum(rsum, sm) / (double)m;
+        acc = 0.0;
+        for (int j = threadIdx.x; j < m; j += 256) {
+            const size_t k = (size_t)b * m + j;
+            const double r = res[k] - mean;
+            res[k] = r;
+            acc = fma(r, r, acc);
+        }
+    }
+    rr_new = block_sum(acc, sm);
     const double beta = rr_old > 0.0 ? rr_new / rr_old : 0.0;
     for (int j = threadIdx.x; j < m; j += 256) {
         const size_t k = (size_t)b * m + j;
         dir[k] = fma(beta, dir[k], res[k]);
+        if (dir32) {
+            x32[(size_t)b * m_pad + j] = (float)x[k];
+            dir32[(size_t)b * m_pad + j] = (float)dir[k];
+        }
     }
     if (threadIdx.x == 0)
         rr[b] = rr_new;
@@ -328,12 +386,14 @@ __global__ void hv_kernel(const double *__restrict__ ma, const double *__restric
     HV[e] = (float)h;
 }
 
-__global__ void cg_report(const double *__restrict__ rr, const double *__restrict__ rr0, int B,
-                          float *__restrict__ out)
+// sqrt(rr / rr0) per pair; NaN for a pair marked in bad (if given)
+__global__ void cg_report(const double *__restrict__ rr, const double *__restrict__ rr0,
+                          const int *__restrict__ bad, int B, float *__restrict__ out)
 {
     const int b = blockIdx.x * blockDim.x + threadIdx.x;
     if (b < B)
-        out[b] = rr0[b] > 0.0 ? (float)sqrt(rr[b] / rr0[b]) : 0.f;
+        out[b] = bad && bad[b] ? __builtin_nanf("")
+                               : rr0[b] > 0.0 ? (float)sqrt(rr[b] / rr0[b]) : 0.f;
 }
 
 template <int FL>
@@ -376,7 +436,7 @@ hipError_t launch_hvp(const PlanArgs &px, const PlanArgs &py, const float *V, in
     hipLaunchKernelGGL(rhs_kernel, dim3(blocks_for(Bm)), dim3(256), 0, st, (const double *)w.tw,
                        (const double *)w.muc, Bm, w.rhs);
     hipLaunchKernelGGL(cg_start, dim3(B), dim3(256), 0, st, (const double *)w.rhs, m, w.x, w.res,
-                       w.dir, w.rr, w.rr0);
+                       w.dir, w.rr, w.rr0, nullptr, nullptr, m, 0);
     for (int it = 0; it < cg_iters; ++it) {
         // q2 = P^T ((P dir) / ma)
         pass<F_U>(px, nullptr, w.dir, nullptr, nullptr, w.mur, nullptr, nullptr, nullptr,
@@ -386,7 +446,8 @@ hipError_t launch_hvp(const PlanArgs &px, const PlanArgs &py, const float *V, in
         pass<F_U>(py, nullptr, w.ur, nullptr, nullptr, w.muc, nullptr, nullptr, nullptr, nullptr,
                   nullptr, st);
         hipLaunchKernelGGL(cg_step, dim3(B), dim3(256), 0, st, (const double *)w.mb,
-                           (const double *)w.muc, m, w.x, w.res, w.dir, w.rr);
+                           (const double *)w.muc, nullptr, 0, B, m, m, w.x, w.res, w.dir, w.rr,
+                           (const double *)w.rr0, 0.0, 0, nullptr, nullptr);
     }
     // rows X with u = dg: P dg and Du
     // (D1 comes out bit-identical to the first pass's and is simply rewritten)
@@ -398,7 +459,33 @@ hipError_t launch_hvp(const PlanArgs &px, const PlanArgs &py, const float *V, in
                        px.inv_eps, HV);
     if (cg_residual)
         hipLaunchKernelGGL(cg_report, dim3(blocks_for(B)), dim3(256), 0, st, (const double *)w.rr,
-                           (const double *)w.rr0, B, cg_residual);
+                           (const double *)w.rr0, nullptr, B, cg_residual);
+    return hipGetLastError();
+}
+
+hipError_t launch_cg_start(const double *rhs, int B, int m, double *x, double *res, double *dir,
+                           double *rr, double *rr0, float *x32, float *dir32, int m_pad,
+                           bool project, hipStream_t st)
+{
+    hipLaunchKernelGGL(cg_start, dim3(B), dim3(256), 0, st, rhs, m, x, res, dir, rr, rr0, x32,
+                       dir32, m_pad, project ? 1 : 0);
+    return hipGetLastError();
+}
+
+hipError_t launch_cg_step(const double *mb, const double *q2, const float *q2_part, int S,
+                          int m_pad, int B, int m, double *x, double *res, double *dir,
+                          double *rr, const double *rr0, double stop2, bool project, float *x32,
+                          float *dir32, hipStream_t st)
+{
+    hipLaunchKernelGGL(cg_step, dim3(B), dim3(256), 0, st, mb, q2, q2_part, S, B, m, m_pad, x,
+                       res, dir, rr, rr0, stop2, project ? 1 : 0, x32, dir32);
+    return hipGetLastError();
+}
+
+hipError_t launch_cg_report(const double *rr, const double *rr0, const int *bad, int B,
+                            float *out, hipStream_t st)
+{
+    hipLaunchKernelGGL(cg_report, dim3(blocks_for(B)), dim3(256), 0, st, rr, rr0, bad, B, out);
     return hipGetLastError();
 }
 

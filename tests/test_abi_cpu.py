@@ -208,6 +208,23 @@ def test_hvp_rejects_bad_arguments_without_writing(lib):
     assert np.all(hv == 2.0)
 
 
+def test_hvp_matrix_core_shapes_and_alignment(lib):
+    # bf16 with d = 32 or 64 runs on the matrix cores; other d > 16 stay unsupported
+    assert lib.sinkhorn_workspace_bytes(4, 1, 100, 90, 64, 1) > 0
+    assert lib.sinkhorn_workspace_bytes(4, 1, 100, 90, 32, 1) > 0
+    assert lib.sinkhorn_workspace_bytes(4, 1, 100, 90, 64, 0) == 0
+    assert lib.sinkhorn_workspace_bytes(4, 1, 100, 90, 48, 1) == 0
+    hv = np.full(8 * 64, 2.0, dtype=np.float32)
+    odd = ctypes.c_void_p(24)   # 8 mod 16
+    for X, Y, d, code in ((odd, DUMMY, 64, sk.SK_ERR_INVALID_ARG),
+                          (DUMMY, odd, 32, sk.SK_ERR_INVALID_ARG),
+                          (DUMMY, DUMMY, 48, sk.SK_ERR_UNSUPPORTED)):
+        rc = lib.sinkhorn_hvp(X, Y, 1, None, None, 1, 8, 9, d, 0.1, DUMMY, DUMMY, DUMMY, 10,
+                              _host(hv), None, DUMMY, 1 << 40, None)
+        assert rc == code, (d, lib.sinkhorn_last_error())
+    assert np.all(hv == 2.0)
+
+
 def test_coo_normalize_rejects_bad_arguments(lib):
     assert lib.sinkhorn_coo_workspace_bytes(2, 100, 90, 5000) > 5000 * 8   # two logs per entry
     assert lib.sinkhorn_coo_workspace_bytes(0, 100, 90, 5000) == 0

@@ -953,12 +953,20 @@ def test_workload_coo_normalize_sampled_pairs(name, pairs):
 
 
 # ------------------------------------------------------- Hessian-vector product
-@pytest.mark.parametrize("B,n,m,d,dtype,eps", [(1, 40, 50, 3, "f32", 0.1),
-                                                (2, 120, 90, 3, "f32", 0.05),
-                                                (1, 64, 70, 8, "f32", 0.2),
-                                                (1, 50, 45, 16, "bf16", 0.5)])
-def test_hvp_matches_oracle(B, n, m, d, dtype, eps):
-    c = workloads.random_case(21, B, n, m, d, weights="dirichlet", dtype=dtype)
+# bf16 with d = 32 / 64 runs on the matrix cores: fp32 plan entries (exponent
+# bound ln2 * 2c * max|x.y| * 2^-24, under 1e-5 here), the direction in two bf16
+# pieces (2^-17) and fp32 sums, all below the 1e-4 held for the fp64 path.
+@pytest.mark.parametrize("B,n,m,d,dtype,eps,zw", [(1, 40, 50, 3, "f32", 0.1, 0),
+                                                  (2, 120, 90, 3, "f32", 0.05, 0),
+                                                  (1, 64, 70, 8, "f32", 0.2, 0),
+                                                  (1, 50, 45, 16, "bf16", 0.5, 0),
+                                                  (1, 50, 45, 64, "bf16", 0.5, 0),
+                                                  (2, 70, 90, 32, "bf16", 1.0, 0),
+                                                  (1, 150, 170, 64, "bf16", 0.5, 0),
+                                                  (2, 20, 600, 64, "bf16", 1.0, 0),
+                                                  (1, 97, 81, 64, "bf16", 0.5, 3)])
+def test_hvp_matches_oracle(B, n, m, d, dtype, eps, zw):
+    c = workloads.random_case(21, B, n, m, d, weights="dirichlet", dtype=dtype, zero_weights=zw)
     fo, go = oracle.potentials(c["X"], c["Y"], c["a"], c["b"], eps=[eps], iters=[2000])
     f32, g32 = fo.astype(np.float32), go.astype(np.float32)
     V = np.random.default_rng(3).normal(size=(B, n, d)).astype(np.float32)
@@ -971,6 +979,70 @@ def test_hvp_matches_oracle(B, n, m, d, dtype, eps):
     assert np.all(host(res) < 1e-4), host(res)
     for p in range(B):
         assert rel_inf(host(HV)[p], HVo[p]) <= 1e-4
+
+
+def hvp_case(seed, B, n, m, d, eps, iters=2000, dtype="bf16"):
+    c = workloads.random_case(seed, B, n, m, d, weights="dirichlet", dtype=dtype)
+    fo, go = oracle.potentials(c["X"], c["Y"], c["a"], c["b"], eps=[eps], iters=[iters])
+    X, Y = points(c)
+    return c, X, Y, dev(c["a"]), dev(c["b"]), dev(fo.astype(np.float32)), dev(go.astype(np.float32))
+
+
+def test_hvp_matrix_cores_symmetric_linear_and_deterministic():
+    c, X, Y, a, b, f, g = hvp_case(23, 2, 300, 260, 64, 0.5)
+    rng = np.random.default_rng(8)
+    U = dev(rng.normal(size=(2, 300, 64)).astype(np.float32))
+    V = dev(rng.normal(size=(2, 300, 64)).astype(np.float32))
+    HU, ru = sk.hvp(X, Y, a, b, f, g, 0.5, U, cg_iters=200)
+    HV, rv = sk.hvp(X, Y, a, b, f, g, 0.5, V, cg_iters=200)
+    HW, _ = sk.hvp(X, Y, a, b, f, g, 0.5, 2.0 * U - V, cg_iters=200)
+    HV2, rv2 = sk.hvp(X, Y, a, b, f, g, 0.5, V, cg_iters=200)
+    torch.cuda.synchronize()
+    assert torch.equal(HV, HV2) and torch.equal(rv, rv2)
+    assert np.all(host(ru) < 1e-4) and np.all(host(rv) < 1e-4)
+    for p in range(2):
+        hu, hv, hw, u, v = (host(t)[p] for t in (HU, HV, HW, U, V))
+        assert rel_inf(hw, 2.0 * hu - hv) <= 1e-4
+        assert abs((u * hv).sum() - (v * hu).sum()) <= 1e-4 * np.abs(u * hv).sum()
+
+
+def test_hvp_matrix_cores_far_potentials_give_nan():
+    # zero potentials at a small eps put every row's plan mass far below 2^-64 of
+    # its weight: the matrix-core path marks the pair and returns NaN
+    c = workloads.random_case(24, 2, 60, 70, 64, weights="uniform", dtype="bf16")
+    X, Y = points(c)
+    eps = 0.01
+    f = torch.zeros(2, 60, device="cuda")
+    g = torch.zeros(2, 70, device="cuda")
+    V = torch.ones(2, 60, 64, device="cuda")
+    HV, res = sk.hvp(X, Y, dev(c["a"]), dev(c["b"]), f, g, eps, V, cg_iters=3)
+    torch.cuda.synchronize()
+    assert torch.isnan(HV).all() and torch.isnan(res).all()
+
+
+def test_workload_feat_50k_hvp_properties():
+    # full size: the plan is n x m = 3e9 entries, beyond the oracle's dense HVP;
+    # properties that hold at any size stand in (symmetry of u.Hv, linearity,
+    # CG convergence, finiteness), on the stored potentials
+    w, gold = load_workload("feat-50k")
+    X, Y = points(w)
+    a, b = dev(w["a"]), dev(w["b"])
+    f, g = dev(gold["f"].astype(np.float32)), dev(gold["g"].astype(np.float32))
+    eps = float(w["eps"][-1])
+    rng = np.random.default_rng(9)
+    U = dev((rng.normal(size=(1, 50000, 64)) / 8).astype(np.float32))
+    V = dev((rng.normal(size=(1, 50000, 64)) / 8).astype(np.float32))
+    HU, ru = sk.hvp(X, Y, a, b, f, g, eps, U, cg_iters=60)
+    HV, rv = sk.hvp(X, Y, a, b, f, g, eps, V, cg_iters=60)
+    HW, rw = sk.hvp(X, Y, a, b, f, g, eps, U + V, cg_iters=60)
+    torch.cuda.synchronize()
+    print("feat-50k hvp residuals", host(ru), host(rv), host(rw), flush=True)
+    for t in (HU, HV, HW):
+        assert bool(torch.isfinite(t).all())
+    assert np.all(host(ru) < 1e-3) and np.all(host(rv) < 1e-3)
+    hu, hv, hw, u, v = (host(t)[0].astype(np.float64) for t in (HU, HV, HW, U, V))
+    assert rel_inf(hw, hu + hv) <= 1e-3
+    assert abs((u * hv).sum() - (v * hu).sum()) <= 1e-3 * np.abs(u * hv).sum()
 
 
 def test_hvp_is_linear_and_symmetric_on_gpu():
