@@ -237,7 +237,7 @@ HvpWs carve_hvp(Carve &c, int B, int n, int m, int d)
 HvpFeatWs carve_hvp_feat(Carve &c, int B, int n, int m, int d)
 {
     HvpFeatWs w;
-    const int np = round_up(n, kPad), mp = round_up(m, kPad);
+    const int np = round_up(n, kHvpPad), mp = round_up(m, kHvpPad);
     const size_t Bn = (size_t)B * n, Bm = (size_t)B * m, Bnp = (size_t)B * np,
                  Bmp = (size_t)B * mp;
     const HvpFeatSizes z = hvp_feat_sizes(B, n, m, d);
@@ -275,8 +275,12 @@ HvpFeatWs carve_hvp_feat(Carve &c, int B, int n, int m, int d)
     w.x = c.take<double>(Bm);
     w.res = c.take<double>(Bm);
     w.dir = c.take<double>(Bm);
-    w.rr = c.take<double>(B);
+    w.rr = c.take<double>((size_t)2 * B);
     w.rr0 = c.take<double>(B);
+    const size_t nred = (size_t)B * cg_wide_blocks(m);
+    w.red_pq = c.take<double>(nred);
+    w.red_s = c.take<double>(nred);
+    w.red_q = c.take<double>(nred);
     w.bad = c.take<int>(B);
     return w;
 }

@@ -296,13 +296,26 @@ hipError_t launch_cg_step(const double *mb, const double *q2, const float *q2_pa
                           float *dir32, hipStream_t st);
 hipError_t launch_cg_report(const double *rr, const double *rr0, const int *bad, int B,
                             float *out, hipStream_t st);
+// The CG step spread over cg_wide_blocks(m) work-groups per pair (three
+// launches), for q2 as S fp32 partials: q [B][m] scratch, red_* [B][blocks]
+// scratch; reads rr_cur [B], writes rr_next [B].
+int cg_wide_blocks(int m);
+hipError_t launch_cg_step_wide(const double *mb, const float *q2_part, int S, int m_pad, int B,
+                               int m, double *x, double *res, double *dir, double *q,
+                               const double *rr_cur, double *rr_next, const double *rr0,
+                               double stop2, bool project, double *red_pq, double *red_s,
+                               double *red_q, float *x32, float *dir32, hipStream_t st);
 // The same product on the matrix cores for bf16 with d = 32 or 64 (X, Y 16-byte
 // aligned).  Passes are split over S work-group columns of tps 16-point tiles.
+// Point counts are padded to kHvpPad there.
+constexpr int kHvpPad = 512;
 bool hvp_matrix_cores(int dtype, int d);
 struct HvpSplit {
     int S, tps;
 };
-HvpSplit hvp_split(int blocks, int tiles);
+// `blocks` work-groups' worth of points (all pairs) against `tiles` streamed
+// 16-point tiles, aiming at `target` work-groups: S splits of tps tiles.
+HvpSplit hvp_split(int blocks, int tiles, int target);
 struct HvpFeatSizes {
     size_t part_r, part_rv, part_c, part_cv;   // floats of the partial-sum buffers
 };
@@ -317,8 +330,9 @@ struct HvpFeatWs {
     float *part_r, *part_rv, *part_rq;   // row-pass partial sums
     float *part_c, *part_cv;             // column-pass partial sums
     double *mrow, *ma, *tv, *D1, *Tv;    // [B][n], [B][n][d]
-    double *mb, *rhs, *x, *res, *dir;    // [B][m]
-    double *rr, *rr0;                    // [B]
+    double *mb, *rhs, *x, *res, *dir;    // [B][m] (rhs doubles as the CG step's q)
+    double *rr, *rr0;                    // [2][B], [B]
+    double *red_pq, *red_s, *red_q;      // [B][cg_wide_blocks(m)]
     int *bad;                            // [B] pairs outside the path's range
 };
 hipError_t launch_hvp_feat(const void *X, const void *Y, const float *a, const float *b,

@@ -370,6 +370,134 @@ __global__ __launch_bounds__(256) void cg_step(const double *__restrict__ mb,
         rr[b] = rr_new;
 }
 
+// Wide conjugate-gradient step: many work-groups per pair, kCgChunk entries each,
+// three launches.  A work-group adds the others' partial sums itself, in block
+// order, so every work-group holds the same value and results are
+// deterministic.  rr holds two slots per pair: step k reads slot k % 2 and
+// writes the other; a pair whose residual has reached stop2 rr0 is left alone
+// (its slot is carried over).
+constexpr int kCgChunk = 1024;
+
+__device__ double sum_parts(const double *__restrict__ p, int count, double *sm)
+{
+    double a = 0.0;
+    for (int k = threadIdx.x; k < count; k += 256)
+        a += p[k];
+    return block_sum(a, sm);
+}
+
+__device__ __forceinline__ bool cg_active(const double *rr_cur, const double *rr0, double stop2,
+                                          int b)
+{
+    return rr_cur[b] > stop2 * rr0[b];
+}
+
+// q = mb o dir - q2 (q2 from S fp32 partials), and the blocks' dir.q
+__global__ __launch_bounds__(256) void cg_wide_q(const double *__restrict__ mb,
+                                                 const float *__restrict__ part, int S, int B,
+                                                 int m, int m_pad, const double *__restrict__ dir,
+                                                 double *__restrict__ q,
+                                                 const double *__restrict__ rr_cur,
+                                                 const double *__restrict__ rr0, double stop2,
+                                                 double *__restrict__ red_pq)
+{
+    __shared__ double sm[256];
+    const int b = blockIdx.y, blk = blockIdx.x, nblk = gridDim.x;
+    if (!cg_active(rr_cur, rr0, stop2, b))
+        return;
+    const int j1 = min(m, (blk + 1) * kCgChunk);
+    double acc = 0.0;
+    for (int j = blk * kCgChunk + threadIdx.x; j < j1; j += 256) {
+        const size_t k = (size_t)b * m + j;
+        double q2 = 0.0;
+        for (int p = 0; p < S; ++p)
+            q2 += (double)part[((size_t)p * B + b) * m_pad + j];
+        const double v = fma(mb[k], dir[k], -q2);
+        q[k] = v;
+        acc = fma(dir[k], v, acc);
+    }
+    const double s = block_sum(acc, sm);
+    if (threadIdx.x == 0)
+        red_pq[(size_t)b * nblk + blk] = s;
+}
+
+// x += alpha dir, res -= alpha q; the blocks' sum and sum of squares of res
+__global__ __launch_bounds__(256) void cg_wide_x(int m, double *__restrict__ x,
+                                                 double *__restrict__ res,
+                                                 const double *__restrict__ dir,
+                                                 const double *__restrict__ q,
+                                                 const double *__restrict__ rr_cur,
+                                                 const double *__restrict__ rr0, double stop2,
+                                                 const double *__restrict__ red_pq,
+                                                 double *__restrict__ red_s,
+                                                 double *__restrict__ red_q)
+{
+    __shared__ double sm[256];
+    const int b = blockIdx.y, blk = blockIdx.x, nblk = gridDim.x;
+    if (!cg_active(rr_cur, rr0, stop2, b))
+        return;
+    const double pq = sum_parts(red_pq + (size_t)b * nblk, nblk, sm);
+    const double alpha = pq > 0.0 ? rr_cur[b] / pq : 0.0;
+    const int j1 = min(m, (blk + 1) * kCgChunk);
+    double rs = 0.0, rq = 0.0;
+    for (int j = blk * kCgChunk + threadIdx.x; j < j1; j += 256) {
+        const size_t k = (size_t)b * m + j;
+        x[k] = fma(alpha, dir[k], x[k]);
+        const double r = fma(-alpha, q[k], res[k]);
+        res[k] = r;
+        rs += r;
+        rq = fma(r, r, rq);
+    }
+    const double s1 = block_sum(rs, sm);
+    const double s2 = block_sum(rq, sm);
+    if (threadIdx.x == 0) {
+        red_s[(size_t)b * nblk + blk] = s1;
+        red_q[(size_t)b * nblk + blk] = s2;
+    }
+}
+
+// res taken orthogonal to the constants (project), beta, dir = res + beta dir,
+// fp32 copies of x and dir, and the next residual slot
+__global__ __launch_bounds__(256) void cg_wide_dir(int m, int m_pad, int project,
+                                                   const double *__restrict__ x,
+                                                   double *__restrict__ res,
+                                                   double *__restrict__ dir,
+                                                   const double *__restrict__ rr_cur,
+                                                   double *__restrict__ rr_next,
+                                                   const double *__restrict__ rr0, double stop2,
+                                                   const double *__restrict__ red_s,
+                                                   const double *__restrict__ red_q,
+                                                   float *__restrict__ x32,
+                                                   float *__restrict__ dir32)
+{
+    __shared__ double sm[256];
+    const int b = blockIdx.y, blk = blockIdx.x, nblk = gridDim.x;
+    const bool lead = blk == 0 && threadIdx.x == 0;
+    if (!cg_active(rr_cur, rr0, stop2, b)) {
+        if (lead)
+            rr_next[b] = rr_cur[b];
+        return;
+    }
+    const double rs = sum_parts(red_s + (size_t)b * nblk, nblk, sm);
+    const double rq = sum_parts(red_q + (size_t)b * nblk, nblk, sm);
+    const double mean = project ? rs / (double)m : 0.0;
+    // sum (r - mean)^2 = sum r^2 - m mean^2
+    const double rr_new = fmax(rq - (double)m * mean * mean, 0.0);
+    const double beta = rr_cur[b] > 0.0 ? rr_new / rr_cur[b] : 0.0;
+    const int j1 = min(m, (blk + 1) * kCgChunk);
+    for (int j = blk * kCgChunk + threadIdx.x; j < j1; j += 256) {
+        const size_t k = (size_t)b * m + j;
+        const double r = res[k] - mean;
+        res[k] = r;
+        const double dn = fma(beta, dir[k], r);
+        dir[k] = dn;
+        x32[(size_t)b * m_pad + j] = (float)x[k];
+        dir32[(size_t)b * m_pad + j] = (float)dn;
+    }
+    if (lead)
+        rr_next[b] = rr_new;
+}
+
 // HV_i = (2/eps)(df_i D1_i + Du_i - 2 Tv_i) + 2 ma_i v_i,  df_i = (2 tv_i - (P dg)_i) / ma_i
 __global__ void hv_kernel(const double *__restrict__ ma, const double *__restrict__ tv,
                           const double *__restrict__ pdg, const double *__restrict__ D1,
@@ -479,6 +607,26 @@ hipError_t launch_cg_step(const double *mb, const double *q2, const float *q2_pa
 {
     hipLaunchKernelGGL(cg_step, dim3(B), dim3(256), 0, st, mb, q2, q2_part, S, B, m, m_pad, x,
                        res, dir, rr, rr0, stop2, project ? 1 : 0, x32, dir32);
+    return hipGetLastError();
+}
+
+int cg_wide_blocks(int m) { return ceil_div(m, kCgChunk); }
+
+hipError_t launch_cg_step_wide(const double *mb, const float *q2_part, int S, int m_pad, int B,
+                               int m, double *x, double *res, double *dir, double *q,
+                               const double *rr_cur, double *rr_next, const double *rr0,
+                               double stop2, bool project, double *red_pq, double *red_s,
+                               double *red_q, float *x32, float *dir32, hipStream_t st)
+{
+    const dim3 grid(cg_wide_blocks(m), B), block(256);
+    hipLaunchKernelGGL(cg_wide_q, grid, block, 0, st, mb, q2_part, S, B, m, m_pad,
+                       (const double *)dir, q, rr_cur, rr0, stop2, red_pq);
+    hipLaunchKernelGGL(cg_wide_x, grid, block, 0, st, m, x, res, (const double *)dir,
+                       (const double *)q, rr_cur, rr0, stop2, (const double *)red_pq, red_s,
+                       red_q);
+    hipLaunchKernelGGL(cg_wide_dir, grid, block, 0, st, m, m_pad, project ? 1 : 0,
+                       (const double *)x, res, dir, rr_cur, rr_next, rr0, stop2,
+                       (const double *)red_s, (const double *)red_q, x32, dir32);
     return hipGetLastError();
 }
 

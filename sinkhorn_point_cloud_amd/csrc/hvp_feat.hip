@@ -50,15 +50,24 @@ constexpr int kWavesH = 4;
 constexpr int kKeysH = 16;   // keys (or rows) per streamed tile
 constexpr float kMassLoH = 5.421010862e-20f;   // 2^-64
 constexpr float kMassHiH = 1.2676506e30f;      // 2^100
-constexpr int kGroupsCg = 4;      // 16-point groups per work-group, CG passes
+constexpr int kGroupsCg = 8;      // 16-point groups per wave, CG passes
 constexpr int kGroupsRows1 = 2;   // the first row pass (three products)
 constexpr int kGroupsOther = 4;   // the first column pass and the final row pass
-constexpr int kTargetGroups = 2048;
+// work-groups a pass aims for: the CG passes (scalar partials) split finely, the
+// passes with d-vector partials less so
+constexpr int kTargetCg = 8192;
+constexpr int kTargetVec = 2048;
 // Relative CG residual at which the solve stops: the plan products carry fp32
 // rounding (2^-24 relative), and past about 2^-20 further steps only move the
 // iterate along that rounding.
 constexpr double kCgStop = 9.5367431640625e-07;   // 2^-20
-constexpr int kMaxSplits = 32;
+constexpr int kMaxSplits = 64;
+
+// every work-group's points lie inside the padded arrays
+static_assert(kHvpPad % (kWavesH * 16 * kGroupsCg) == 0 &&
+                  kHvpPad % (kWavesH * 16 * kGroupsRows1) == 0 &&
+                  kHvpPad % (kWavesH * 16 * kGroupsOther) == 0,
+              "padding must hold whole work-groups");
 
 enum : int { kRowsCg = 0, kRowsFirst = 1, kRowsFinal = 2 };
 enum : int { kColsCg = 0, kColsFirst = 1 };
@@ -72,10 +81,11 @@ __device__ __forceinline__ f32x4 score(const bf16x8 (&A)[2], const bf16x8 (&Bm)[
     return D;
 }
 
-// Rows pass over row block blockIdx.x (16 G rows), the key tiles of split
-// blockIdx.y, pair blockIdx.z.  The four waves take every fourth tile of the
-// split.  part_s [S][B][n_pad]: m_i (first) or e_i; part_v [S][B][n_pad][d]: O_i
-// (first) or W_i (final); part_q: Q_i (first).
+// Rows pass.  Work-group blockIdx.y holds 4 G groups of 16 rows, G per wave;
+// the four waves take every key tile of split blockIdx.x in the same order, so
+// a tile comes from L2 once per work-group; pair blockIdx.z.  part_s
+// [S][B][n_pad]: m_i (first) or e_i; part_v [S][B][n_pad][d]: O_i (first) or W_i
+// (final); part_q: Q_i (first).
 template <int DK, int G, int MODE>
 __global__ __launch_bounds__(kWavesH *kWave) void hvp_rows_kernel(
     const uint16_t *__restrict__ X, const float *__restrict__ h, int n, int n_pad,
@@ -86,23 +96,20 @@ __global__ __launch_bounds__(kWavesH *kWave) void hvp_rows_kernel(
 {
     constexpr int d = 32 * DK;
     constexpr int NB = d / 16;
-    constexpr int R = 16 * G;
+    constexpr int R = 16 * G;   // rows per wave
     constexpr bool kVec = MODE != kRowsCg;
     constexpr bool kQ = MODE == kRowsFirst;
-    __shared__ float vsum[kVec ? R : 1][kVec ? d + 1 : 1];
-    __shared__ float qsum[kQ ? R : 1][kQ ? d + 1 : 1];
-    __shared__ float ssum[R];
-    const int b = blockIdx.z, split = blockIdx.y, B = gridDim.z;
+    const int split = blockIdx.x, b = blockIdx.z, B = gridDim.z;
     const int lane = lane_id(), w = wave_id_uniform();
     const int kq = lane >> 4, c16 = lane & 15;
-    const int row0 = blockIdx.x * R;
+    const int row0 = (blockIdx.y * kWavesH + w) * R;   // + R <= n_pad
 
     // the rows as the B operand of the transposed score, h_i in the accumulator
     bf16x8 Xo[G][2], Vh[kQ ? G : 1][2], Vl[kQ ? G : 1][2];
     f32x4 Cin[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-        const int ra = row0 + 16 * g + c16;   // < n_pad
+        const int ra = row0 + 16 * g + c16;
         const int rc = min(ra, n - 1);
 #pragma unroll
         for (int kb = 0; kb < DK; ++kb)
@@ -141,28 +148,40 @@ __global__ __launch_bounds__(kWavesH *kWave) void hvp_rows_kernel(
     const float *ub = MODE != kRowsFirst ? u + (size_t)b * m_pad : nullptr;
     const int n_tiles = m_pad / kKeysH;
     const int t0 = split * tps, t1 = min(n_tiles, t0 + tps);
-    for (int t = t0 + w; t < t1; t += kWavesH) {
+    // Key values of a tile: two register sets, so that the next tile's loads stay
+    // in flight while the current one is used (no copy, no wait between tiles).
+    struct Tile {
+        bf16x8 K[2];
+        float4 be, u;
+    };
+    auto fetch = [&](Tile &T, int t) {
         // padding keys read the last key; their bias (kNeg) gives E = 0
         const int j = min(t * kKeysH + c16, m - 1);
-        bf16x8 Ka[2];
 #pragma unroll
         for (int kb = 0; kb < DK; ++kb)
-            Ka[kb] = load8(yb + (size_t)j * d + 32 * kb + 8 * kq);
-        const float4 be = *reinterpret_cast<const float4 *>(beb + t * kKeysH + 4 * kq);
-        float4 uu = make_float4(0.f, 0.f, 0.f, 0.f);
+            T.K[kb] = load8(yb + (size_t)j * d + 32 * kb + 8 * kq);
+        T.be = *reinterpret_cast<const float4 *>(beb + t * kKeysH + 4 * kq);
         if constexpr (MODE != kRowsFirst)
-            uu = *reinterpret_cast<const float4 *>(ub + t * kKeysH + 4 * kq);
+            T.u = *reinterpret_cast<const float4 *>(ub + t * kKeysH + 4 * kq);
+    };
+    auto tile = [&](const Tile &T, int t) {
         i16x4 Bt[kVec ? NB : 1];
         if constexpr (kVec) {
 #pragma unroll
             for (int q = 0; q < NB; ++q)
                 Bt[q] = load4(ytb + (size_t)(16 * q + c16) * m_pad + t * kKeysH + 4 * kq);
         }
+        // every group's scores first, so the exponentials do not wait on the
+        // matrix cores
+        f32x4 D[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+            D[g] = score(T.K, Xo[g], Cin[g], DK);
+        const float4 be = T.be, uu = T.u;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-            const f32x4 D = score(Ka, Xo[g], Cin[g], DK);
-            const float E[4] = {ex2(fmaf(two_c, D[0], be.x)), ex2(fmaf(two_c, D[1], be.y)),
-                                ex2(fmaf(two_c, D[2], be.z)), ex2(fmaf(two_c, D[3], be.w))};
+            const float E[4] = {ex2(fmaf(two_c, D[g][0], be.x)), ex2(fmaf(two_c, D[g][1], be.y)),
+                                ex2(fmaf(two_c, D[g][2], be.z)), ex2(fmaf(two_c, D[g][3], be.w))};
             if constexpr (MODE == kRowsCg) {
                 float s = fmaf(E[0], uu.x, acc[g]);
                 s = fmaf(E[1], uu.y, s);
@@ -170,13 +189,13 @@ __global__ __launch_bounds__(kWavesH *kWave) void hvp_rows_kernel(
                 acc[g] = fmaf(E[3], uu.w, s);
             } else if constexpr (MODE == kRowsFirst) {
                 acc[g] += (E[0] + E[1]) + (E[2] + E[3]);
-                f32x4 S = f32x4{0.f, 0.f, 0.f, 0.f};
+                f32x4 Sv = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kb = 0; kb < DK; ++kb) {
-                    S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ka[kb], Vh[g][kb], S, 0, 0, 0);
-                    S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ka[kb], Vl[g][kb], S, 0, 0, 0);
+                    Sv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(T.K[kb], Vh[g][kb], Sv, 0, 0, 0);
+                    Sv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(T.K[kb], Vl[g][kb], Sv, 0, 0, 0);
                 }
-                const float es[4] = {E[0] * S[0], E[1] * S[1], E[2] * S[2], E[3] * S[3]};
+                const float es[4] = {E[0] * Sv[0], E[1] * Sv[1], E[2] * Sv[2], E[3] * Sv[3]};
                 i16x4 hi, lo;
                 split2(E, hi, lo);
 #pragma unroll
@@ -202,60 +221,53 @@ __global__ __launch_bounds__(kWavesH *kWave) void hvp_rows_kernel(
                 }
             }
         }
+    };
+    // Loads are issued unconditionally (the last prefetch re-reads the final
+    // tile) and kept ahead of the tile's work by a scheduling barrier, so every
+    // wait counts only the tile about to be used.
+    if (t0 < t1) {
+        Tile TA, TB;
+        TB.u = TA.u = make_float4(0.f, 0.f, 0.f, 0.f);
+        fetch(TA, t0);
+        int t = t0;
+        for (; t + 1 < t1; t += 2) {
+            fetch(TB, t + 1);
+            __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the tile
+            tile(TA, t);
+            fetch(TA, min(t + 2, t1 - 1));
+            __builtin_amdgcn_sched_barrier(0);
+            tile(TB, t + 1);
+        }
+        if (t < t1)
+            tile(TA, t);
     }
     // a row's scalar is spread over the four lanes sharing l % 16
+    const size_t base = ((size_t)split * B + b) * n_pad + row0;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-        acc[g] += __shfl_xor(acc[g], 16, kWave);
-        acc[g] += __shfl_xor(acc[g], 32, kWave);
-    }
-    for (int v = 0; v < kWavesH; ++v) {
-        if (w == v) {
+        float s = acc[g] + __shfl_xor(acc[g], 16, kWave);
+        s += __shfl_xor(s, 32, kWave);
+        if (kq == 0)
+            part_s[base + 16 * g + c16] = s;
+        if constexpr (kVec) {
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-                if constexpr (kVec) {
+            for (int q = 0; q < NB; ++q)
 #pragma unroll
-                    for (int q = 0; q < NB; ++q)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            float &o = vsum[16 * g + 4 * kq + r][16 * q + c16];
-                            o = v == 0 ? O[g][q][r] : o + O[g][q][r];
-                        }
+                for (int r = 0; r < 4; ++r) {
+                    const size_t o = (base + 16 * g + 4 * kq + r) * d + 16 * q + c16;
+                    part_v[o] = O[g][q][r];
+                    if constexpr (kQ)
+                        part_q[o] = Q[g][q][r];
                 }
-                if constexpr (kQ) {
-#pragma unroll
-                    for (int q = 0; q < NB; ++q)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            float &o = qsum[16 * g + 4 * kq + r][16 * q + c16];
-                            o = v == 0 ? Q[g][q][r] : o + Q[g][q][r];
-                        }
-                }
-                if (kq == 0) {
-                    float &s = ssum[16 * g + c16];
-                    s = v == 0 ? acc[g] : s + acc[g];
-                }
-            }
-        }
-        __syncthreads();
-    }
-    const size_t base = ((size_t)split * B + b) * n_pad + row0;
-    for (int e = threadIdx.x; e < R; e += kWavesH * kWave)
-        part_s[base + e] = ssum[e];
-    if constexpr (kVec) {
-        for (int e = threadIdx.x; e < R * d; e += kWavesH * kWave) {
-            const int r = e / d, k = e % d;
-            part_v[(base + r) * d + k] = vsum[r][k];
-            if constexpr (kQ)
-                part_q[(base + r) * d + k] = qsum[r][k];
         }
     }
 }
 
-// Columns pass over key block blockIdx.x (16 G keys), the row tiles of split
-// blockIdx.y, pair blockIdx.z.  part_s [NS][S][B][m_pad] with NS = 3 (first:
-// sums against w0 = a, w1 = a ur, w2 = a t) or 1 (CG: against w0);
-// part_v [S][B][m_pad][d]: PV_j (first).
+// Columns pass.  Work-group blockIdx.y holds 4 G groups of 16 keys, G per wave;
+// the four waves take every row tile of split blockIdx.x in the same order;
+// pair blockIdx.z.  part_s [NS][S][B][m_pad] with NS = 3 (first: sums against
+// w0 = a, w1 = a ur, w2 = a t) or 1 (CG: against w0); part_v [S][B][m_pad][d]:
+// PV_j (first).
 template <int DK, int G, int MODE>
 __global__ __launch_bounds__(kWavesH *kWave) void hvp_cols_kernel(
     const uint16_t *__restrict__ X, const float *__restrict__ h, int n, int n_pad,
@@ -266,22 +278,20 @@ __global__ __launch_bounds__(kWavesH *kWave) void hvp_cols_kernel(
 {
     constexpr int d = 32 * DK;
     constexpr int NB = d / 16;
-    constexpr int R = 16 * G;
+    constexpr int R = 16 * G;   // keys per wave
     constexpr bool kFirst = MODE == kColsFirst;
     constexpr int NS = kFirst ? 3 : 1;
-    __shared__ float vsum[kFirst ? R : 1][kFirst ? d + 1 : 1];
-    __shared__ float ssum[NS][R];
-    const int b = blockIdx.z, split = blockIdx.y, S = gridDim.y, B = gridDim.z;
+    const int split = blockIdx.x, S = gridDim.x, b = blockIdx.z, B = gridDim.z;
     const int lane = lane_id(), w = wave_id_uniform();
     const int kq = lane >> 4, c16 = lane & 15;
-    const int key0 = blockIdx.x * R;
+    const int key0 = (blockIdx.y * kWavesH + w) * R;   // + R <= m_pad
 
     // the keys as the B operand (the rows pass's A), beta_j added after the sum
     bf16x8 Yo[G][2];
     float bk[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-        const int ka = key0 + 16 * g + c16;   // < m_pad
+        const int ka = key0 + 16 * g + c16;
         const int kc = min(ka, m - 1);
 #pragma unroll
         for (int kb = 0; kb < DK; ++kb)
@@ -307,17 +317,25 @@ __global__ __launch_bounds__(kWavesH *kWave) void hvp_cols_kernel(
     const size_t wo = (size_t)b * n_pad;
     const int n_tiles = n_pad / kKeysH;
     const int t0 = split * tps, t1 = min(n_tiles, t0 + tps);
-    for (int t = t0 + w; t < t1; t += kWavesH) {
+    // Row values of a tile: two register sets, as in the rows pass.
+    struct Tile {
+        bf16x8 X[2];
+        float4 h, a;
+    };
+    auto fetch = [&](Tile &T, int t) {
         // padding rows read the last row; their h (kNeg) gives E = 0
         const int i = min(t * kKeysH + c16, n - 1);
-        bf16x8 Xa[2];
 #pragma unroll
         for (int kb = 0; kb < DK; ++kb)
-            Xa[kb] = load8(xb + (size_t)i * d + 32 * kb + 8 * kq);
+            T.X[kb] = load8(xb + (size_t)i * d + 32 * kb + 8 * kq);
+        const int r = t * kKeysH + 4 * kq;
+        T.h = *reinterpret_cast<const float4 *>(hb + r);
+        T.a = *reinterpret_cast<const float4 *>(w0 + wo + r);
+    };
+    auto tile = [&](const Tile &T, int t) {
         const int r0 = t * kKeysH + 4 * kq;
-        const float4 h4 = *reinterpret_cast<const float4 *>(hb + r0);
-        const f32x4 Cin = f32x4{h4.x, h4.y, h4.z, h4.w};
-        const float4 a4 = *reinterpret_cast<const float4 *>(w0 + wo + r0);
+        const f32x4 Cin = f32x4{T.h.x, T.h.y, T.h.z, T.h.w};
+        const float4 a4 = T.a;
         float4 u4 = make_float4(0.f, 0.f, 0.f, 0.f), t4 = u4;
         i16x4 Bh[kFirst ? NB : 1], Bl[kFirst ? NB : 1];
         if constexpr (kFirst) {
@@ -330,11 +348,14 @@ __global__ __launch_bounds__(kWavesH *kWave) void hvp_cols_kernel(
                 Bl[q] = load4(vtl + o);
             }
         }
+        f32x4 D[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+            D[g] = score(T.X, Yo[g], Cin, DK);
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-            const f32x4 D = score(Xa, Yo[g], Cin, DK);
-            const float E[4] = {ex2(fmaf(two_c, D[0], bk[g])), ex2(fmaf(two_c, D[1], bk[g])),
-                                ex2(fmaf(two_c, D[2], bk[g])), ex2(fmaf(two_c, D[3], bk[g]))};
+            const float E[4] = {ex2(fmaf(two_c, D[g][0], bk[g])), ex2(fmaf(two_c, D[g][1], bk[g])),
+                                ex2(fmaf(two_c, D[g][2], bk[g])), ex2(fmaf(two_c, D[g][3], bk[g]))};
             {
                 float s = fmaf(E[0], a4.x, acc[0][g]);
                 s = fmaf(E[1], a4.y, s);
@@ -361,48 +382,40 @@ __global__ __launch_bounds__(kWavesH *kWave) void hvp_cols_kernel(
                 }
             }
         }
+    };
+    if (t0 < t1) {
+        Tile TA, TB;
+        fetch(TA, t0);
+        int t = t0;
+        for (; t + 1 < t1; t += 2) {
+            fetch(TB, t + 1);
+            __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the tile
+            tile(TA, t);
+            fetch(TA, min(t + 2, t1 - 1));
+            __builtin_amdgcn_sched_barrier(0);
+            tile(TB, t + 1);
+        }
+        if (t < t1)
+            tile(TA, t);
     }
     // a key's scalars are spread over the four lanes sharing l % 16
+    const size_t base = ((size_t)split * B + b) * m_pad + key0;
+    const size_t plane = (size_t)S * B * m_pad;
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
+    for (int g = 0; g < G; ++g) {
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            acc[s][g] += __shfl_xor(acc[s][g], 16, kWave);
-            acc[s][g] += __shfl_xor(acc[s][g], 32, kWave);
+        for (int s = 0; s < NS; ++s) {
+            float v = acc[s][g] + __shfl_xor(acc[s][g], 16, kWave);
+            v += __shfl_xor(v, 32, kWave);
+            if (kq == 0)
+                part_s[s * plane + base + 16 * g + c16] = v;
         }
-    for (int v = 0; v < kWavesH; ++v) {
-        if (w == v) {
+        if constexpr (kFirst) {
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-                if constexpr (kFirst) {
+            for (int q = 0; q < NB; ++q)
 #pragma unroll
-                    for (int q = 0; q < NB; ++q)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            float &o = vsum[16 * g + 4 * kq + r][16 * q + c16];
-                            o = v == 0 ? PV[g][q][r] : o + PV[g][q][r];
-                        }
-                }
-                if (kq == 0) {
-#pragma unroll
-                    for (int s = 0; s < NS; ++s) {
-                        float &o = ssum[s][16 * g + c16];
-                        o = v == 0 ? acc[s][g] : o + acc[s][g];
-                    }
-                }
-            }
-        }
-        __syncthreads();
-    }
-    for (int e = threadIdx.x; e < NS * R; e += kWavesH * kWave) {
-        const int s = e / R, r = e % R;
-        part_s[(((size_t)s * S + split) * B + b) * m_pad + key0 + r] = ssum[s][r];
-    }
-    if constexpr (kFirst) {
-        const size_t base = ((size_t)split * B + b) * m_pad + key0;
-        for (int e = threadIdx.x; e < R * d; e += kWavesH * kWave) {
-            const int r = e / d, k = e % d;
-            part_v[(base + r) * d + k] = vsum[r][k];
+                for (int r = 0; r < 4; ++r)
+                    part_v[(base + 16 * g + 4 * kq + r) * d + 16 * q + c16] = PV[g][q][r];
         }
     }
 }
@@ -603,14 +616,25 @@ hipError_t zero(void *p, size_t bytes, hipStream_t st)
     return hipGetLastError();
 }
 
+// the split of each pass; launches and combines take these
+HvpSplit rows_split(int G, int target, int B, int np, int mp)
+{
+    return hvp_split(np / (kWavesH * 16 * G) * B, mp / kKeysH, target);
+}
+
+HvpSplit cols_split(int G, int target, int B, int np, int mp)
+{
+    return hvp_split(mp / (kWavesH * 16 * G) * B, np / kKeysH, target);
+}
+
 template <int MODE>
 void rows_pass(const uint16_t *X, const uint16_t *Y, const HvpFeatWs &w, int d, int B, int n,
                int n_pad, int m, int m_pad, float two_c, const float *u, hipStream_t st)
 {
     constexpr int G = MODE == kRowsCg ? kGroupsCg : MODE == kRowsFirst ? kGroupsRows1
                                                                        : kGroupsOther;
-    const HvpSplit sp = hvp_split(n_pad / (16 * G) * B, m_pad / kKeysH);
-    dim3 grid(n_pad / (16 * G), sp.S, B), block(kWavesH * kWave);
+    const HvpSplit sp = rows_split(G, MODE == kRowsCg ? kTargetCg : kTargetVec, B, n_pad, m_pad);
+    dim3 grid(sp.S, n_pad / (kWavesH * 16 * G), B), block(kWavesH * kWave);
     auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, grid, block, 0, st, X, (const float *)w.h, n, n_pad, Y,
                            (const uint16_t *)w.yt, (const float *)w.y.bias, m, m_pad,
@@ -628,8 +652,8 @@ void cols_pass(const uint16_t *X, const uint16_t *Y, const HvpFeatWs &w, int d, 
                int n_pad, int m, int m_pad, float two_c, const float *w0, hipStream_t st)
 {
     constexpr int G = MODE == kColsCg ? kGroupsCg : kGroupsOther;
-    const HvpSplit sp = hvp_split(m_pad / (16 * G) * B, n_pad / kKeysH);
-    dim3 grid(m_pad / (16 * G), sp.S, B), block(kWavesH * kWave);
+    const HvpSplit sp = cols_split(G, MODE == kColsCg ? kTargetCg : kTargetVec, B, n_pad, m_pad);
+    dim3 grid(sp.S, m_pad / (kWavesH * 16 * G), B), block(kWavesH * kWave);
     auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, grid, block, 0, st, X, (const float *)w.h, n, n_pad, Y,
                            (const float *)w.y.bias, m, m_pad, w0, (const float *)w.wu,
@@ -646,31 +670,30 @@ void cols_pass(const uint16_t *X, const uint16_t *Y, const HvpFeatWs &w, int d, 
 
 bool hvp_matrix_cores(int dtype, int d) { return dtype == 1 && (d == 32 || d == 64); }
 
-HvpSplit hvp_split(int blocks, int tiles)
+HvpSplit hvp_split(int blocks, int tiles, int target)
 {
-    const int want = std::max(1, std::min(kMaxSplits, ceil_div(kTargetGroups, blocks)));
+    // a multiple of the 8 XCDs: work-groups are dealt to them round-robin by
+    // linear index, split fastest, so each XCD keeps to the same key ranges
+    const int want = std::min(round_up(std::max(1, ceil_div(target, blocks)), 8), kMaxSplits);
     HvpSplit sp;
-    sp.tps = round_up(ceil_div(tiles, want), kWavesH);
+    sp.tps = ceil_div(tiles, want);
     sp.S = ceil_div(tiles, sp.tps);
     return sp;
 }
 
 HvpFeatSizes hvp_feat_sizes(int B, int n, int m, int d)
 {
-    const int np = round_up(n, kPad), mp = round_up(m, kPad);
+    const int np = round_up(n, kHvpPad), mp = round_up(m, kHvpPad);
+    const int r_cg = rows_split(kGroupsCg, kTargetCg, B, np, mp).S;
+    const int r_1 = rows_split(kGroupsRows1, kTargetVec, B, np, mp).S;
+    const int r_f = rows_split(kGroupsOther, kTargetVec, B, np, mp).S;
+    const int c_cg = cols_split(kGroupsCg, kTargetCg, B, np, mp).S;
+    const int c_1 = cols_split(kGroupsOther, kTargetVec, B, np, mp).S;
     HvpFeatSizes z;
-    const int rows_s = std::max({hvp_split(np / (16 * kGroupsCg) * B, mp / kKeysH).S,
-                                 hvp_split(np / (16 * kGroupsRows1) * B, mp / kKeysH).S,
-                                 hvp_split(np / (16 * kGroupsOther) * B, mp / kKeysH).S});
-    const int rows_v = std::max(hvp_split(np / (16 * kGroupsRows1) * B, mp / kKeysH).S,
-                                hvp_split(np / (16 * kGroupsOther) * B, mp / kKeysH).S);
-    const int cols_s = std::max(hvp_split(mp / (16 * kGroupsCg) * B, np / kKeysH).S,
-                                3 * hvp_split(mp / (16 * kGroupsOther) * B, np / kKeysH).S);
-    const int cols_v = hvp_split(mp / (16 * kGroupsOther) * B, np / kKeysH).S;
-    z.part_r = (size_t)rows_s * B * np;
-    z.part_rv = (size_t)rows_v * B * np * d;
-    z.part_c = (size_t)cols_s * B * mp;
-    z.part_cv = (size_t)cols_v * B * mp * d;
+    z.part_r = (size_t)std::max({r_cg, r_1, r_f}) * B * np;
+    z.part_rv = (size_t)std::max(r_1, r_f) * B * np * d;
+    z.part_c = (size_t)std::max(c_cg, 3 * c_1) * B * mp;
+    z.part_cv = (size_t)c_1 * B * mp * d;
     return z;
 }
 
@@ -680,7 +703,7 @@ hipError_t launch_hvp_feat(const void *X_, const void *Y_, const float *a, const
                            const HvpFeatWs &w, hipStream_t st)
 {
     const uint16_t *X = (const uint16_t *)X_, *Y = (const uint16_t *)Y_;
-    const int np = round_up(n, kPad), mp = round_up(m, kPad);
+    const int np = round_up(n, kHvpPad), mp = round_up(m, kHvpPad);
     const float c = scale_of(eps);
     const float two_c = 2.0f * c;
     hipError_t e;
@@ -703,7 +726,7 @@ hipError_t launch_hvp_feat(const void *X_, const void *Y_, const float *a, const
     // first row pass: m, O, Q -> ma, D1, tv, Tv, and the column pass's row values
     rows_pass<kRowsFirst>(X, Y, w, d, B, n, np, m, mp, two_c, nullptr, st);
     {
-        const int S = hvp_split(np / (16 * kGroupsRows1) * B, mp / kKeysH).S;
+        const int S = rows_split(kGroupsRows1, kTargetVec, B, np, mp).S;
         hipLaunchKernelGGL(hvp_rows_first_combine, dim3(ceil_div(n, 4), B), dim3(256), 0, st,
                            (const float *)w.part_r, (const float *)w.part_rv,
                            (const float *)w.part_rq, S, B, n, np, d, X, a,
@@ -713,7 +736,7 @@ hipError_t launch_hvp_feat(const void *X_, const void *Y_, const float *a, const
     // first column pass: mb, P^T ur, sum a t E, PV -> rhs
     cols_pass<kColsFirst>(X, Y, w, d, B, n, np, m, mp, two_c, w.wa, st);
     {
-        const int S = hvp_split(mp / (16 * kGroupsOther) * B, np / kKeysH).S;
+        const int S = cols_split(kGroupsOther, kTargetVec, B, np, mp).S;
         hipLaunchKernelGGL(hvp_cols_first_combine, dim3(ceil_div(m, 4), B), dim3(256), 0, st,
                            (const float *)w.part_c, (const float *)w.part_cv, S, B, m, mp, d, Y,
                            w.mb, w.rhs);
@@ -722,8 +745,8 @@ hipError_t launch_hvp_feat(const void *X_, const void *Y_, const float *a, const
         (e = launch_cg_start(w.rhs, B, m, w.x, w.res, w.dir, w.rr, w.rr0, w.x32, w.u32, mp, true,
                              st)))
         return e;
-    const int s_rows = hvp_split(np / (16 * kGroupsCg) * B, mp / kKeysH).S;
-    const int s_cols = hvp_split(mp / (16 * kGroupsCg) * B, np / kKeysH).S;
+    const int s_rows = rows_split(kGroupsCg, kTargetCg, B, np, mp).S;
+    const int s_cols = cols_split(kGroupsCg, kTargetCg, B, np, mp).S;
     for (int it = 0; it < cg_iters; ++it) {
         // q2 = P^T ((P dir) / ma): e = sum_j E dir_j, w = a e / m, then sum_i w_i E_ij
         rows_pass<kRowsCg>(X, Y, w, d, B, n, np, m, mp, two_c, w.u32, st);
@@ -731,14 +754,17 @@ hipError_t launch_hvp_feat(const void *X_, const void *Y_, const float *a, const
                            (const float *)w.part_r, s_rows, B, n, np, (const double *)w.mrow, a,
                            w.wu);
         cols_pass<kColsCg>(X, Y, w, d, B, n, np, m, mp, two_c, w.wu, st);
-        if ((e = launch_cg_step(w.mb, nullptr, w.part_c, s_cols, mp, B, m, w.x, w.res, w.dir,
-                                w.rr, w.rr0, kCgStop * kCgStop, true, w.x32, w.u32, st)))
+        const double *rr_cur = w.rr + (size_t)(it & 1) * B;
+        double *rr_next = w.rr + (size_t)((it + 1) & 1) * B;
+        if ((e = launch_cg_step_wide(w.mb, w.part_c, s_cols, mp, B, m, w.x, w.res, w.dir, w.rhs,
+                                     rr_cur, rr_next, w.rr0, kCgStop * kCgStop, true, w.red_pq,
+                                     w.red_s, w.red_q, w.x32, w.u32, st)))
             return e;
     }
     // final row pass with u = dg: P dg and Du -> HV
     rows_pass<kRowsFinal>(X, Y, w, d, B, n, np, m, mp, two_c, w.x32, st);
     {
-        const int S = hvp_split(np / (16 * kGroupsOther) * B, mp / kKeysH).S;
+        const int S = rows_split(kGroupsOther, kTargetVec, B, np, mp).S;
         hipLaunchKernelGGL(hvp_final_combine, dim3(ceil_div(n, 4), B), dim3(256), 0, st,
                            (const float *)w.part_r, (const float *)w.part_rv, S, B, n, np, d, X,
                            a, (const double *)w.ma, (const double *)w.tv, (const double *)w.D1,
@@ -747,7 +773,8 @@ hipError_t launch_hvp_feat(const void *X_, const void *Y_, const float *a, const
     if ((e = hipGetLastError()))
         return e;
     if (cg_residual)
-        return launch_cg_report(w.rr, w.rr0, w.bad, B, cg_residual, st);
+        return launch_cg_report(w.rr + (size_t)(cg_iters & 1) * B, w.rr0, w.bad, B, cg_residual,
+                                st);
     return hipSuccess;
 }
 
