@@ -1,6 +1,7 @@
 // abi.hip -- the C ABI declared in include/sinkhorn.h: argument checks,
 // workspace carve-up, the eps-annealing driver and kernel launches.
 #include "common.h"
+#include "hvp.h"
 #include "sinkhorn.h"
 
 #include <math.h>
@@ -28,6 +29,7 @@ int hip_fail(hipError_t e, const char *where)
     return fail(SK_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
 }
 
+constexpr int kPad = 64;
 constexpr int kMaxPoints = 1 << 24;
 constexpr int kMaxPairs = 65535;     // pairs index a grid dimension (y or z), at most 65535
 constexpr int kMaxNormDim = 4096;   // dimensions accepted by the normalisation

@@ -119,9 +119,6 @@ template <> struct Elem<uint16_t> {
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 inline int round_up(int a, int b) { return ceil_div(a, b) * b; }
 
-// Point counts are padded to a multiple of this in every packed layout.
-constexpr int kPad = 64;
-
 // ---------------------------------------------------------------- launchers
 // Every launcher enqueues on `stream` and returns hipGetLastError().
 
@@ -281,64 +278,6 @@ struct HvpWs {
 };
 hipError_t launch_hvp(const PlanArgs &px, const PlanArgs &py, const float *V, int cg_iters,
                       float *HV, float *cg_residual, const HvpWs &w, hipStream_t st);
-// Conjugate-gradient kernels of the HVP (one work-group per pair, fp64).  With
-// x32 / dir32 ([B][m_pad]) they also write fp32 copies of x and dir; cg_step
-// takes q2 = P^T ((P dir) / ma) either as an fp64 vector or as S fp32 partial
-// sums [S][B][m_pad] (added in order), leaves a pair alone once rr <= stop2 rr0,
-// and with project keeps the residual orthogonal to the constants; cg_report
-// gives NaN for a pair marked in bad.
-hipError_t launch_cg_start(const double *rhs, int B, int m, double *x, double *res, double *dir,
-                           double *rr, double *rr0, float *x32, float *dir32, int m_pad,
-                           bool project, hipStream_t st);
-hipError_t launch_cg_step(const double *mb, const double *q2, const float *q2_part, int S,
-                          int m_pad, int B, int m, double *x, double *res, double *dir,
-                          double *rr, const double *rr0, double stop2, bool project, float *x32,
-                          float *dir32, hipStream_t st);
-hipError_t launch_cg_report(const double *rr, const double *rr0, const int *bad, int B,
-                            float *out, hipStream_t st);
-// The CG step spread over cg_wide_blocks(m) work-groups per pair (three
-// launches), for q2 as S fp32 partials: q [B][m] scratch, red_* [B][blocks]
-// scratch; reads rr_cur [B], writes rr_next [B].
-int cg_wide_blocks(int m);
-hipError_t launch_cg_step_wide(const double *mb, const float *q2_part, int S, int m_pad, int B,
-                               int m, double *x, double *res, double *dir, double *q,
-                               const double *rr_cur, double *rr_next, const double *rr0,
-                               double stop2, bool project, double *red_pq, double *red_s,
-                               double *red_q, float *x32, float *dir32, hipStream_t st);
-// The same product on the matrix cores for bf16 with d = 32 or 64 (X, Y 16-byte
-// aligned).  Passes are split over S work-group columns of tps 16-point tiles.
-// Point counts are padded to kHvpPad there.
-constexpr int kHvpPad = 512;
-bool hvp_matrix_cores(int dtype, int d);
-struct HvpSplit {
-    int S, tps;
-};
-// `blocks` work-groups' worth of points (all pairs) against `tiles` streamed
-// 16-point tiles, aiming at `target` work-groups: S splits of tps tiles.
-HvpSplit hvp_split(int blocks, int tiles, int target);
-struct HvpFeatSizes {
-    size_t part_r, part_rv, part_c, part_cv;   // floats of the partial-sum buffers
-};
-HvpFeatSizes hvp_feat_sizes(int B, int n, int m, int d);
-struct HvpFeatWs {
-    SideF y;                          // keys: biases at eps, squared norms, log weights
-    uint16_t *yt;                     // [B][d][m_pad] transposed key points
-    float *h, *wa, *wu, *wt;          // [B][n_pad] row offsets and row values
-    uint16_t *vh, *vl;                // [B][n_pad][d] the direction in two bf16 pieces
-    uint16_t *vth, *vtl;              // [B][d][n_pad] the same, transposed
-    float *u32, *x32;                 // [B][m_pad] fp32 key vectors (dir, dg)
-    float *part_r, *part_rv, *part_rq;   // row-pass partial sums
-    float *part_c, *part_cv;             // column-pass partial sums
-    double *mrow, *ma, *tv, *D1, *Tv;    // [B][n], [B][n][d]
-    double *mb, *rhs, *x, *res, *dir;    // [B][m] (rhs doubles as the CG step's q)
-    double *rr, *rr0;                    // [2][B], [B]
-    double *red_pq, *red_s, *red_q;      // [B][cg_wide_blocks(m)]
-    int *bad;                            // [B] pairs outside the path's range
-};
-hipError_t launch_hvp_feat(const void *X, const void *Y, const float *a, const float *b,
-                           const float *f, const float *g, const float *V, int B, int n, int m,
-                           int d, float eps, int cg_iters, float *HV, float *cg_residual,
-                           const HvpFeatWs &w, hipStream_t st);
 // Cosine cost support: points to unit length (fp32 out, norms kept), and the
 // gradient through that map.
 hipError_t launch_normalize(const void *X, int dtype, long count, int d, float *Xh,

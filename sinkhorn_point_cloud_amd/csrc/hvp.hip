@@ -23,6 +23,7 @@
 // work-group per pair reduces in a fixed order.  Deterministic throughout.
 // bf16 clouds with d = 32 or 64 take the matrix-core passes of hvp_feat.hip,
 // which share the conjugate-gradient kernels below.
+#include "hvp.h"
 #include "plan_eval.h"
 
 namespace sk {
@@ -293,78 +294,36 @@ __global__ __launch_bounds__(256) void cg_start(const double *__restrict__ rhs, 
     }
 }
 
-// q2_j of pair b: the fp64 vector, or the sum of S fp32 partials [S][B][m_pad]
-// added in split order
-__device__ __forceinline__ double q2_at(const double *q2, const float *part, int S, int B,
-                                        int m, int m_pad, int b, int j)
-{
-    if (!part)
-        return q2[(size_t)b * m + j];
-    double s = 0.0;
-    for (int p = 0; p < S; ++p)
-        s += (double)part[((size_t)p * B + b) * m_pad + j];
-    return s;
-}
-
 // One conjugate-gradient step, with S dir = mb o dir - q2 (q2 = P^T((P dir)/ma)).
-// A pair whose residual has reached stop2 * rr0 (squared) is left as it is.  With
-// project, the new residual is taken orthogonal to the constants, so that
-// rounding does not feed S's null space (which does not change HV: a constant
-// added to dg moves df by minus that constant and the two uses cancel).
 __global__ __launch_bounds__(256) void cg_step(const double *__restrict__ mb,
-                                               const double *__restrict__ q2,
-                                               const float *__restrict__ q2_part, int S, int B,
-                                               int m, int m_pad, double *__restrict__ x,
-                                               double *__restrict__ res, double *__restrict__ dir,
-                                               double *__restrict__ rr,
-                                               const double *__restrict__ rr0, double stop2,
-                                               int project, float *__restrict__ x32,
-                                               float *__restrict__ dir32)
+                                               const double *__restrict__ q2, int m,
+                                               double *__restrict__ x, double *__restrict__ res,
+                                               double *__restrict__ dir, double *__restrict__ rr)
 {
     __shared__ double sm[256];
     const int b = blockIdx.x;
-    const double rr_old = rr[b];
-    if (!(rr_old > stop2 * rr0[b]))   // uniform over the work-group
-        return;
     double acc = 0.0;
     for (int j = threadIdx.x; j < m; j += 256) {
         const size_t k = (size_t)b * m + j;
-        const double q = fma(mb[k], dir[k], -q2_at(q2, q2_part, S, B, m, m_pad, b, j));
+        const double q = fma(mb[k], dir[k], -q2[k]);
         acc = fma(dir[k], q, acc);
     }
     const double pq = block_sum(acc, sm);
+    const double rr_old = rr[b];
     const double alpha = pq > 0.0 ? rr_old / pq : 0.0;
     acc = 0.0;
-    double rsum = 0.0;
     for (int j = threadIdx.x; j < m; j += 256) {
         const size_t k = (size_t)b * m + j;
-        const double q = fma(mb[k], dir[k], -q2_at(q2, q2_part, S, B, m, m_pad, b, j));
+        const double q = fma(mb[k], dir[k], -q2[k]);
         x[k] = fma(alpha, dir[k], x[k]);
-        const double r = fma(-alpha, q, res[k]);
-        res[k] = r;
-        acc = fma(r, r, acc);
-        rsum += r;
+        res[k] = fma(-alpha, q, res[k]);
+        acc = fma(res[k], res[k], acc);
     }
-    double rr_new;
-    if (project) {
-        const double mean = block_sum(rsum, sm) / (double)m;
-        acc = 0.0;
-        for (int j = threadIdx.x; j < m; j += 256) {
-            const size_t k = (size_t)b * m + j;
-            const double r = res[k] - mean;
-            res[k] = r;
-            acc = fma(r, r, acc);
-        }
-    }
-    rr_new = block_sum(acc, sm);
+    const double rr_new = block_sum(acc, sm);
     const double beta = rr_old > 0.0 ? rr_new / rr_old : 0.0;
     for (int j = threadIdx.x; j < m; j += 256) {
         const size_t k = (size_t)b * m + j;
         dir[k] = fma(beta, dir[k], res[k]);
-        if (dir32) {
-            x32[(size_t)b * m_pad + j] = (float)x[k];
-            dir32[(size_t)b * m_pad + j] = (float)dir[k];
-        }
     }
     if (threadIdx.x == 0)
         rr[b] = rr_new;
@@ -574,8 +533,7 @@ hipError_t launch_hvp(const PlanArgs &px, const PlanArgs &py, const float *V, in
         pass<F_U>(py, nullptr, w.ur, nullptr, nullptr, w.muc, nullptr, nullptr, nullptr, nullptr,
                   nullptr, st);
         hipLaunchKernelGGL(cg_step, dim3(B), dim3(256), 0, st, (const double *)w.mb,
-                           (const double *)w.muc, nullptr, 0, B, m, m, w.x, w.res, w.dir, w.rr,
-                           (const double *)w.rr0, 0.0, 0, nullptr, nullptr);
+                           (const double *)w.muc, m, w.x, w.res, w.dir, w.rr);
     }
     // rows X with u = dg: P dg and Du
     // (D1 comes out bit-identical to the first pass's and is simply rewritten)
@@ -597,16 +555,6 @@ hipError_t launch_cg_start(const double *rhs, int B, int m, double *x, double *r
 {
     hipLaunchKernelGGL(cg_start, dim3(B), dim3(256), 0, st, rhs, m, x, res, dir, rr, rr0, x32,
                        dir32, m_pad, project ? 1 : 0);
-    return hipGetLastError();
-}
-
-hipError_t launch_cg_step(const double *mb, const double *q2, const float *q2_part, int S,
-                          int m_pad, int B, int m, double *x, double *res, double *dir,
-                          double *rr, const double *rr0, double stop2, bool project, float *x32,
-                          float *dir32, hipStream_t st)
-{
-    hipLaunchKernelGGL(cg_step, dim3(B), dim3(256), 0, st, mb, q2, q2_part, S, B, m, m_pad, x,
-                       res, dir, rr, rr0, stop2, project ? 1 : 0, x32, dir32);
     return hipGetLastError();
 }
 

@@ -39,6 +39,7 @@
 // The potentials are meant to solve the problem at eps: a live row whose mass
 // m_i falls outside [2^-64, 2^100] marks its pair, whose output (HV and the
 // residual) is then NaN.
+#include "hvp.h"
 #include "mfma_bf16.h"
 
 #include <algorithm>
