@@ -410,6 +410,13 @@ def main():
                    "eps": f"{eps[0]:g}->{eps[-1]:g} over {len(eps)} stage(s)",
                    "iters": total_iters,
                    "launch": "hip graph replay of the step" if args.graph else "eager",
+                   # the d = 3 score does not run on the vector ALUs as the pages expected:
+                   # it runs on bf16 matrix cores from an exact three-piece split of the
+                   # fp32 operands (--valu-scores times the vector-score kernel instead)
+                   "scores": ("vector ALUs (fp32 FMAs)" if args.valu_scores or kernel.startswith(
+                       ("lse3_kernel", "lseF_kernel")) else
+                              "bf16 matrix cores, exact 3-piece split of the fp32 operands"
+                              if d == 3 else "bf16 matrix cores (bf16 inputs)"),
                    "outputs": ("potentials, COO plan at %g x max P per pair, loss and dL/dX"
                                % w["threshold"]) if sparse
                    else "potentials f, g and transport cost",
