@@ -47,17 +47,19 @@
 namespace sk {
 namespace {
 
-constexpr int kWavesH = 4;
+constexpr int kWavesH = 8;   // waves per work-group of the plan passes
 constexpr int kKeysH = 16;   // keys (or rows) per streamed tile
 constexpr float kMassLoH = 5.421010862e-20f;   // 2^-64
 constexpr float kMassHiH = 1.2676506e30f;      // 2^100
-constexpr int kGroupsCg = 8;      // 16-point groups per wave, CG passes
+constexpr int kGroupsCg = 4;      // 16-point groups per wave, CG passes
 constexpr int kGroupsRows1 = 2;   // the first row pass (three products)
 constexpr int kGroupsOther = 4;   // the first column pass and the final row pass
+constexpr int kTilesCg = 8;       // 16-point tiles per LDS stage, CG passes
+constexpr int kTilesVec = 4;      // the same, passes with d-vector sums
 // work-groups a pass aims for: the CG passes (scalar partials) split finely, the
 // passes with d-vector partials less so
-constexpr int kTargetCg = 8192;
-constexpr int kTargetVec = 2048;
+constexpr int kTargetCg = 4096;
+constexpr int kTargetVec = 1024;
 // Relative CG residual at which the solve stops: the plan products carry fp32
 // rounding (2^-24 relative), and past about 2^-20 further steps only move the
 // iterate along that rounding.
@@ -73,6 +75,8 @@ static_assert(kHvpPad % (kWavesH * 16 * kGroupsCg) == 0 &&
 enum : int { kRowsCg = 0, kRowsFirst = 1, kRowsFinal = 2 };
 enum : int { kColsCg = 0, kColsFirst = 1 };
 
+__device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
+
 __device__ __forceinline__ f32x4 score(const bf16x8 (&A)[2], const bf16x8 (&Bm)[2], f32x4 C,
                                        int dk)
 {
@@ -82,12 +86,14 @@ __device__ __forceinline__ f32x4 score(const bf16x8 (&A)[2], const bf16x8 (&Bm)[
     return D;
 }
 
-// Rows pass.  Work-group blockIdx.y holds 4 G groups of 16 rows, G per wave;
-// the four waves take every key tile of split blockIdx.x in the same order, so
-// a tile comes from L2 once per work-group; pair blockIdx.z.  part_s
-// [S][B][n_pad]: m_i (first) or e_i; part_v [S][B][n_pad][d]: O_i (first) or W_i
-// (final); part_q: Q_i (first).
-template <int DK, int G, int MODE>
+// Rows pass.  Work-group blockIdx.y holds kWavesH G groups of 16 rows, G per
+// wave; pair blockIdx.z; the key tiles of split blockIdx.x stream through LDS
+// NT tiles a stage (double buffered: every thread loads its share of the next
+// stage into registers while the current one is used, then writes it to the
+// other buffer), and every wave reads its operands from there, so a key tile
+// is fetched once per work-group.  part_s [S][B][n_pad]: m_i (first) or e_i;
+// part_v [S][B][n_pad][d]: O_i (first) or W_i (final); part_q: Q_i (first).
+template <int DK, int G, int NT, int MODE>
 __global__ __launch_bounds__(kWavesH *kWave) void hvp_rows_kernel(
     const uint16_t *__restrict__ X, const float *__restrict__ h, int n, int n_pad,
     const uint16_t *__restrict__ Y, const uint16_t *__restrict__ Yt,
@@ -100,8 +106,22 @@ __global__ __launch_bounds__(kWavesH *kWave) void hvp_rows_kernel(
     constexpr int R = 16 * G;   // rows per wave
     constexpr bool kVec = MODE != kRowsCg;
     constexpr bool kQ = MODE == kRowsFirst;
+    constexpr bool kU = MODE != kRowsFirst;
+    constexpr int SK = NT * kKeysH;                        // keys per stage
+    constexpr int kCh = d / 8;                             // 16-byte chunks per key
+    constexpr int kStr = kCh + 1;                          // padded key stride (bank spread)
+    constexpr int kThr = kWavesH * kWave;
+    constexpr int kKL = (SK * kCh + kThr - 1) / kThr;      // key chunks per thread
+    constexpr int kTCh = SK / 8;                           // chunks of one dim row of Yt
+    constexpr int kTStr = SK + 8;                          // padded dim row (bf16)
+    constexpr int kTL = kVec ? (d * kTCh + kThr - 1) / kThr : 1;
+    static_assert(SK <= kThr && kKL <= 2 && kTL <= 2, "a stage in at most two chunks a thread");
+    __shared__ uint4 kbuf[2][SK * kStr];
+    __shared__ __align__(16) float bbuf[2][SK];
+    __shared__ __align__(16) float ubuf[2][kU ? SK : 4];
+    __shared__ __align__(16) uint16_t tbuf[2][kVec ? d * kTStr : 8];
     const int split = blockIdx.x, b = blockIdx.z, B = gridDim.z;
-    const int lane = lane_id(), w = wave_id_uniform();
+    const int tid = threadIdx.x, lane = lane_id(), w = wave_id_uniform();
     const int kq = lane >> 4, c16 = lane & 15;
     const int row0 = (blockIdx.y * kWavesH + w) * R;   // + R <= n_pad
 
@@ -143,104 +163,152 @@ __global__ __launch_bounds__(kWavesH *kWave) void hvp_rows_kernel(
         }
     }
 
-    const uint16_t *yb = Y + (size_t)b * m * d;
+    const uint4 *yk = reinterpret_cast<const uint4 *>(Y + (size_t)b * m * d);
     const uint16_t *ytb = Yt + (size_t)b * d * m_pad;
     const float *beb = ybias + (size_t)b * m_pad;
-    const float *ub = MODE != kRowsFirst ? u + (size_t)b * m_pad : nullptr;
+    const float *ub = kU ? u + (size_t)b * m_pad : nullptr;
     const int n_tiles = m_pad / kKeysH;
     const int t0 = split * tps, t1 = min(n_tiles, t0 + tps);
-    // Key values of a tile: two register sets, so that the next tile's loads stay
-    // in flight while the current one is used (no copy, no wait between tiles).
-    struct Tile {
-        bf16x8 K[2];
-        float4 be, u;
+    const int n_st = t0 < t1 ? (t1 - t0 + NT - 1) / NT : 0;   // uniform per work-group
+    // A stage's values: key chunk e is chunk e % kCh of key e / kCh (keys past
+    // the pair clamped inside it; their bias is kNeg), bias and u of key tid,
+    // and chunk e of the transposed keys (dim e / kTCh, 8 keys from 8 (e % kTCh)).
+    // (named registers, not arrays: an array written in one lambda and read in
+    // the other stays in scratch memory)
+    uint4 kr0 = zero4(), kr1 = zero4(), tr0 = zero4(), tr1 = zero4();
+    float br = kNeg, ur = 0.f;
+    const int kend = t1 * kKeysH;
+    auto key_chunk = [&](int key0, int e) {
+        return e < SK * kCh ? yk[(size_t)min(key0 + e / kCh, m - 1) * kCh + e % kCh] : zero4();
     };
-    auto fetch = [&](Tile &T, int t) {
-        // padding keys read the last key; their bias (kNeg) gives E = 0
-        const int j = min(t * kKeysH + c16, m - 1);
-#pragma unroll
-        for (int kb = 0; kb < DK; ++kb)
-            T.K[kb] = load8(yb + (size_t)j * d + 32 * kb + 8 * kq);
-        T.be = *reinterpret_cast<const float4 *>(beb + t * kKeysH + 4 * kq);
-        if constexpr (MODE != kRowsFirst)
-            T.u = *reinterpret_cast<const float4 *>(ub + t * kKeysH + 4 * kq);
+    auto yt_chunk = [&](int key0, int e) {
+        const int kk = key0 + 8 * (e % kTCh);   // a multiple of 8, as is m_pad
+        return e < d * kTCh && kk < m_pad
+                   ? *reinterpret_cast<const uint4 *>(ytb + (size_t)(e / kTCh) * m_pad + kk)
+                   : zero4();
     };
-    auto tile = [&](const Tile &T, int t) {
-        i16x4 Bt[kVec ? NB : 1];
-        if constexpr (kVec) {
-#pragma unroll
-            for (int q = 0; q < NB; ++q)
-                Bt[q] = load4(ytb + (size_t)(16 * q + c16) * m_pad + t * kKeysH + 4 * kq);
+    auto fetch = [&](int st) {
+        const int key0 = (t0 + st * NT) * kKeysH;
+        kr0 = key_chunk(key0, tid);
+        if constexpr (kKL > 1)
+            kr1 = key_chunk(key0, tid + kThr);
+        if (tid < SK) {
+            const int kk = key0 + tid;
+            br = kk < kend ? beb[kk] : kNeg;
+            if constexpr (kU)
+                ur = kk < kend ? ub[kk] : 0.f;
         }
-        // every group's scores first, so the exponentials do not wait on the
-        // matrix cores
-        f32x4 D[G];
+        if constexpr (kVec) {
+            tr0 = yt_chunk(key0, tid);
+            if constexpr (kTL > 1)
+                tr1 = yt_chunk(key0, tid + kThr);
+        }
+    };
+    auto put_key = [&](int bf, int e, uint4 v) {
+        if (e < SK * kCh)
+            kbuf[bf][(e / kCh) * kStr + e % kCh] = v;
+    };
+    auto put_yt = [&](int bf, int e, uint4 v) {
+        if (e < d * kTCh)
+            *reinterpret_cast<uint4 *>(&tbuf[bf][(e / kTCh) * kTStr + 8 * (e % kTCh)]) = v;
+    };
+    auto stash = [&](int bf) {
+        put_key(bf, tid, kr0);
+        if constexpr (kKL > 1)
+            put_key(bf, tid + kThr, kr1);
+        if (tid < SK) {
+            bbuf[bf][tid] = br;
+            if constexpr (kU)
+                ubuf[bf][tid] = ur;
+        }
+        if constexpr (kVec) {
+            put_yt(bf, tid, tr0);
+            if constexpr (kTL > 1)
+                put_yt(bf, tid + kThr, tr1);
+        }
+    };
+    if (n_st > 0) {
+        fetch(0);
+        stash(0);
+        __syncthreads();
+    }
+    for (int st = 0; st < n_st; ++st) {
+        const int bf = st & 1;
+        if (st + 1 < n_st)
+            fetch(st + 1);   // in flight while this stage is used
+        const int nt = min(NT, t1 - (t0 + st * NT));
+        for (int tt = 0; tt < nt; ++tt) {
+            bf16x8 Ka[2];
 #pragma unroll
-        for (int g = 0; g < G; ++g)
-            D[g] = score(T.K, Xo[g], Cin[g], DK);
-        const float4 be = T.be, uu = T.u;
+            for (int kb = 0; kb < DK; ++kb)
+                Ka[kb] = __builtin_bit_cast(bf16x8,
+                                            kbuf[bf][(tt * kKeysH + c16) * kStr + 4 * kb + kq]);
+            const float4 be = *reinterpret_cast<const float4 *>(&bbuf[bf][tt * kKeysH + 4 * kq]);
+            float4 uu = make_float4(0.f, 0.f, 0.f, 0.f);
+            if constexpr (kU)
+                uu = *reinterpret_cast<const float4 *>(&ubuf[bf][tt * kKeysH + 4 * kq]);
+            i16x4 Bt[kVec ? NB : 1];
+            if constexpr (kVec) {
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const float E[4] = {ex2(fmaf(two_c, D[g][0], be.x)), ex2(fmaf(two_c, D[g][1], be.y)),
-                                ex2(fmaf(two_c, D[g][2], be.z)), ex2(fmaf(two_c, D[g][3], be.w))};
-            if constexpr (MODE == kRowsCg) {
-                float s = fmaf(E[0], uu.x, acc[g]);
-                s = fmaf(E[1], uu.y, s);
-                s = fmaf(E[2], uu.z, s);
-                acc[g] = fmaf(E[3], uu.w, s);
-            } else if constexpr (MODE == kRowsFirst) {
-                acc[g] += (E[0] + E[1]) + (E[2] + E[3]);
-                f32x4 Sv = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int q = 0; q < NB; ++q)
+                    Bt[q] = *reinterpret_cast<const i16x4 *>(
+                        &tbuf[bf][(16 * q + c16) * kTStr + tt * kKeysH + 4 * kq]);
+            }
+            // every group's scores first, so the exponentials do not wait on the
+            // matrix cores
+            f32x4 D[G];
 #pragma unroll
-                for (int kb = 0; kb < DK; ++kb) {
-                    Sv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(T.K[kb], Vh[g][kb], Sv, 0, 0, 0);
-                    Sv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(T.K[kb], Vl[g][kb], Sv, 0, 0, 0);
-                }
-                const float es[4] = {E[0] * Sv[0], E[1] * Sv[1], E[2] * Sv[2], E[3] * Sv[3]};
-                i16x4 hi, lo;
-                split2(E, hi, lo);
+            for (int g = 0; g < G; ++g)
+                D[g] = score(Ka, Xo[g], Cin[g], DK);
 #pragma unroll
-                for (int q = 0; q < NB; ++q) {
-                    O[g][q] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(hi, Bt[q], O[g][q], 0, 0, 0);
-                    O[g][q] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lo, Bt[q], O[g][q], 0, 0, 0);
-                }
-                split2(es, hi, lo);
+            for (int g = 0; g < G; ++g) {
+                const float E[4] = {ex2(fmaf(two_c, D[g][0], be.x)),
+                                    ex2(fmaf(two_c, D[g][1], be.y)),
+                                    ex2(fmaf(two_c, D[g][2], be.z)),
+                                    ex2(fmaf(two_c, D[g][3], be.w))};
+                if constexpr (MODE == kRowsCg) {
+                    float s = fmaf(E[0], uu.x, acc[g]);
+                    s = fmaf(E[1], uu.y, s);
+                    s = fmaf(E[2], uu.z, s);
+                    acc[g] = fmaf(E[3], uu.w, s);
+                } else if constexpr (MODE == kRowsFirst) {
+                    acc[g] += (E[0] + E[1]) + (E[2] + E[3]);
+                    f32x4 Sv = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int q = 0; q < NB; ++q) {
-                    Q[g][q] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(hi, Bt[q], Q[g][q], 0, 0, 0);
-                    Q[g][q] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lo, Bt[q], Q[g][q], 0, 0, 0);
-                }
-            } else {
-                const float eu[4] = {E[0] * uu.x, E[1] * uu.y, E[2] * uu.z, E[3] * uu.w};
-                acc[g] += (eu[0] + eu[1]) + (eu[2] + eu[3]);
-                i16x4 hi, lo;
-                split2(eu, hi, lo);
+                    for (int kb = 0; kb < DK; ++kb) {
+                        Sv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ka[kb], Vh[g][kb], Sv, 0, 0, 0);
+                        Sv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ka[kb], Vl[g][kb], Sv, 0, 0, 0);
+                    }
+                    const float es[4] = {E[0] * Sv[0], E[1] * Sv[1], E[2] * Sv[2], E[3] * Sv[3]};
+                    i16x4 hi, lo;
+                    split2(E, hi, lo);
 #pragma unroll
-                for (int q = 0; q < NB; ++q) {
-                    O[g][q] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(hi, Bt[q], O[g][q], 0, 0, 0);
-                    O[g][q] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lo, Bt[q], O[g][q], 0, 0, 0);
+                    for (int q = 0; q < NB; ++q) {
+                        O[g][q] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(hi, Bt[q], O[g][q], 0, 0, 0);
+                        O[g][q] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lo, Bt[q], O[g][q], 0, 0, 0);
+                    }
+                    split2(es, hi, lo);
+#pragma unroll
+                    for (int q = 0; q < NB; ++q) {
+                        Q[g][q] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(hi, Bt[q], Q[g][q], 0, 0, 0);
+                        Q[g][q] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lo, Bt[q], Q[g][q], 0, 0, 0);
+                    }
+                } else {
+                    const float eu[4] = {E[0] * uu.x, E[1] * uu.y, E[2] * uu.z, E[3] * uu.w};
+                    acc[g] += (eu[0] + eu[1]) + (eu[2] + eu[3]);
+                    i16x4 hi, lo;
+                    split2(eu, hi, lo);
+#pragma unroll
+                    for (int q = 0; q < NB; ++q) {
+                        O[g][q] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(hi, Bt[q], O[g][q], 0, 0, 0);
+                        O[g][q] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lo, Bt[q], O[g][q], 0, 0, 0);
+                    }
                 }
             }
         }
-    };
-    // Loads are issued unconditionally (the last prefetch re-reads the final
-    // tile) and kept ahead of the tile's work by a scheduling barrier, so every
-    // wait counts only the tile about to be used.
-    if (t0 < t1) {
-        Tile TA, TB;
-        TB.u = TA.u = make_float4(0.f, 0.f, 0.f, 0.f);
-        fetch(TA, t0);
-        int t = t0;
-        for (; t + 1 < t1; t += 2) {
-            fetch(TB, t + 1);
-            __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the tile
-            tile(TA, t);
-            fetch(TA, min(t + 2, t1 - 1));
-            __builtin_amdgcn_sched_barrier(0);
-            tile(TB, t + 1);
-        }
-        if (t < t1)
-            tile(TA, t);
+        if (st + 1 < n_st)
+            stash(bf ^ 1);
+        __syncthreads();
     }
     // a row's scalar is spread over the four lanes sharing l % 16
     const size_t base = ((size_t)split * B + b) * n_pad + row0;
@@ -264,12 +332,12 @@ __global__ __launch_bounds__(kWavesH *kWave) void hvp_rows_kernel(
     }
 }
 
-// Columns pass.  Work-group blockIdx.y holds 4 G groups of 16 keys, G per wave;
-// the four waves take every row tile of split blockIdx.x in the same order;
-// pair blockIdx.z.  part_s [NS][S][B][m_pad] with NS = 3 (first: sums against
+// Columns pass.  Work-group blockIdx.y holds kWavesH G groups of 16 keys, G per
+// wave; pair blockIdx.z; the row tiles of split blockIdx.x stream through LDS as
+// in the rows pass.  part_s [NS][S][B][m_pad] with NS = 3 (first: sums against
 // w0 = a, w1 = a ur, w2 = a t) or 1 (CG: against w0); part_v [S][B][m_pad][d]:
 // PV_j (first).
-template <int DK, int G, int MODE>
+template <int DK, int G, int NT, int MODE>
 __global__ __launch_bounds__(kWavesH *kWave) void hvp_cols_kernel(
     const uint16_t *__restrict__ X, const float *__restrict__ h, int n, int n_pad,
     const uint16_t *__restrict__ Y, const float *__restrict__ ybias, int m, int m_pad,
@@ -282,8 +350,22 @@ __global__ __launch_bounds__(kWavesH *kWave) void hvp_cols_kernel(
     constexpr int R = 16 * G;   // keys per wave
     constexpr bool kFirst = MODE == kColsFirst;
     constexpr int NS = kFirst ? 3 : 1;
+    constexpr int SR = NT * kKeysH;                        // rows per stage
+    constexpr int kCh = d / 8;
+    constexpr int kStr = kCh + 1;
+    constexpr int kThr = kWavesH * kWave;
+    constexpr int kXL = (SR * kCh + kThr - 1) / kThr;      // row chunks per thread
+    constexpr int kTCh = SR / 8;
+    constexpr int kTStr = SR + 8;
+    constexpr int kTL = kFirst ? (d * kTCh + kThr - 1) / kThr : 1;
+    static_assert(SR <= kThr && kXL <= 2 && kTL <= 1, "a stage in few chunks a thread");
+    __shared__ uint4 xbuf[2][SR * kStr];
+    __shared__ __align__(16) float hbuf[2][SR];
+    __shared__ __align__(16) float wbuf[2][NS][SR];
+    __shared__ __align__(16) uint16_t vhbuf[2][kFirst ? d * kTStr : 8];
+    __shared__ __align__(16) uint16_t vlbuf[2][kFirst ? d * kTStr : 8];
     const int split = blockIdx.x, S = gridDim.x, b = blockIdx.z, B = gridDim.z;
-    const int lane = lane_id(), w = wave_id_uniform();
+    const int tid = threadIdx.x, lane = lane_id(), w = wave_id_uniform();
     const int kq = lane >> 4, c16 = lane & 15;
     const int key0 = (blockIdx.y * kWavesH + w) * R;   // + R <= m_pad
 
@@ -313,91 +395,145 @@ __global__ __launch_bounds__(kWavesH *kWave) void hvp_cols_kernel(
         }
     }
 
-    const uint16_t *xb = X + (size_t)b * n * d;
-    const float *hb = h + (size_t)b * n_pad;
+    const uint4 *xk = reinterpret_cast<const uint4 *>(X + (size_t)b * n * d);
     const size_t wo = (size_t)b * n_pad;
+    const float *const ws[3] = {w0 + wo, w1 + wo, w2 + wo};
+    const uint16_t *vhb = vth + (size_t)b * d * n_pad;
+    const uint16_t *vlb = vtl + (size_t)b * d * n_pad;
     const int n_tiles = n_pad / kKeysH;
     const int t0 = split * tps, t1 = min(n_tiles, t0 + tps);
-    // Row values of a tile: two register sets, as in the rows pass.
-    struct Tile {
-        bf16x8 X[2];
-        float4 h, a;
+    const int n_st = t0 < t1 ? (t1 - t0 + NT - 1) / NT : 0;
+    // a stage's values: row chunks (rows clamped inside the pair; rows past the
+    // pair have h = kNeg, rows past the split are not read), h and the row
+    // values of row tid, and the transposed direction's chunks
+    // (named registers, not arrays: see the rows pass)
+    uint4 xr0 = zero4(), xr1 = zero4(), vhr = zero4(), vlr = zero4();
+    float hr = kNeg, wr0 = 0.f, wr1 = 0.f, wr2 = 0.f;
+    const int rend = t1 * kKeysH;
+    auto row_chunk = [&](int r0, int e) {
+        return e < SR * kCh ? xk[(size_t)min(r0 + e / kCh, n - 1) * kCh + e % kCh] : zero4();
     };
-    auto fetch = [&](Tile &T, int t) {
-        // padding rows read the last row; their h (kNeg) gives E = 0
-        const int i = min(t * kKeysH + c16, n - 1);
-#pragma unroll
-        for (int kb = 0; kb < DK; ++kb)
-            T.X[kb] = load8(xb + (size_t)i * d + 32 * kb + 8 * kq);
-        const int r = t * kKeysH + 4 * kq;
-        T.h = *reinterpret_cast<const float4 *>(hb + r);
-        T.a = *reinterpret_cast<const float4 *>(w0 + wo + r);
-    };
-    auto tile = [&](const Tile &T, int t) {
-        const int r0 = t * kKeysH + 4 * kq;
-        const f32x4 Cin = f32x4{T.h.x, T.h.y, T.h.z, T.h.w};
-        const float4 a4 = T.a;
-        float4 u4 = make_float4(0.f, 0.f, 0.f, 0.f), t4 = u4;
-        i16x4 Bh[kFirst ? NB : 1], Bl[kFirst ? NB : 1];
-        if constexpr (kFirst) {
-            u4 = *reinterpret_cast<const float4 *>(w1 + wo + r0);
-            t4 = *reinterpret_cast<const float4 *>(w2 + wo + r0);
-#pragma unroll
-            for (int q = 0; q < NB; ++q) {
-                const size_t o = ((size_t)b * d + 16 * q + c16) * n_pad + r0;
-                Bh[q] = load4(vth + o);
-                Bl[q] = load4(vtl + o);
+    auto fetch = [&](int st) {
+        const int r0 = (t0 + st * NT) * kKeysH;
+        xr0 = row_chunk(r0, tid);
+        if constexpr (kXL > 1)
+            xr1 = row_chunk(r0, tid + kThr);
+        if (tid < SR) {
+            const int rr = r0 + tid;
+            const bool in = rr < rend;
+            hr = in ? h[wo + rr] : kNeg;
+            wr0 = in ? ws[0][rr] : 0.f;
+            if constexpr (kFirst) {
+                wr1 = in ? ws[1][rr] : 0.f;
+                wr2 = in ? ws[2][rr] : 0.f;
             }
         }
-        f32x4 D[G];
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-            D[g] = score(T.X, Yo[g], Cin, DK);
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const float E[4] = {ex2(fmaf(two_c, D[g][0], bk[g])), ex2(fmaf(two_c, D[g][1], bk[g])),
-                                ex2(fmaf(two_c, D[g][2], bk[g])), ex2(fmaf(two_c, D[g][3], bk[g]))};
-            {
-                float s = fmaf(E[0], a4.x, acc[0][g]);
-                s = fmaf(E[1], a4.y, s);
-                s = fmaf(E[2], a4.z, s);
-                acc[0][g] = fmaf(E[3], a4.w, s);
-            }
+        if constexpr (kFirst) {
+            const int e = tid;
+            const int rr = r0 + 8 * (e % kTCh);   // a multiple of 8, as is n_pad
+            const size_t o = (size_t)(e / kTCh) * n_pad + rr;
+            const bool in = e < d * kTCh && rr < n_pad;
+            vhr = in ? *reinterpret_cast<const uint4 *>(vhb + o) : zero4();
+            vlr = in ? *reinterpret_cast<const uint4 *>(vlb + o) : zero4();
+        }
+    };
+    auto put_row = [&](int bf, int e, uint4 v) {
+        if (e < SR * kCh)
+            xbuf[bf][(e / kCh) * kStr + e % kCh] = v;
+    };
+    auto stash = [&](int bf) {
+        put_row(bf, tid, xr0);
+        if constexpr (kXL > 1)
+            put_row(bf, tid + kThr, xr1);
+        if (tid < SR) {
+            hbuf[bf][tid] = hr;
+            wbuf[bf][0][tid] = wr0;
             if constexpr (kFirst) {
-                float s = fmaf(E[0], u4.x, acc[1][g]);
-                s = fmaf(E[1], u4.y, s);
-                s = fmaf(E[2], u4.z, s);
-                acc[1][g] = fmaf(E[3], u4.w, s);
-                s = fmaf(E[0], t4.x, acc[2][g]);
-                s = fmaf(E[1], t4.y, s);
-                s = fmaf(E[2], t4.z, s);
-                acc[2][g] = fmaf(E[3], t4.w, s);
-                const float aE[4] = {E[0] * a4.x, E[1] * a4.y, E[2] * a4.z, E[3] * a4.w};
-                i16x4 hi, lo;
-                split2(aE, hi, lo);
+                wbuf[bf][1][tid] = wr1;
+                wbuf[bf][2][tid] = wr2;
+            }
+        }
+        if constexpr (kFirst) {
+            const int e = tid;
+            if (e < d * kTCh) {
+                const int o = (e / kTCh) * kTStr + 8 * (e % kTCh);
+                *reinterpret_cast<uint4 *>(&vhbuf[bf][o]) = vhr;
+                *reinterpret_cast<uint4 *>(&vlbuf[bf][o]) = vlr;
+            }
+        }
+    };
+    if (n_st > 0) {
+        fetch(0);
+        stash(0);
+        __syncthreads();
+    }
+    for (int st = 0; st < n_st; ++st) {
+        const int bf = st & 1;
+        if (st + 1 < n_st)
+            fetch(st + 1);
+        const int nt = min(NT, t1 - (t0 + st * NT));
+        for (int tt = 0; tt < nt; ++tt) {
+            bf16x8 Xa[2];
+#pragma unroll
+            for (int kb = 0; kb < DK; ++kb)
+                Xa[kb] = __builtin_bit_cast(bf16x8,
+                                            xbuf[bf][(tt * kKeysH + c16) * kStr + 4 * kb + kq]);
+            const int r4 = tt * kKeysH + 4 * kq;
+            const float4 h4 = *reinterpret_cast<const float4 *>(&hbuf[bf][r4]);
+            const f32x4 Cin = f32x4{h4.x, h4.y, h4.z, h4.w};
+            const float4 a4 = *reinterpret_cast<const float4 *>(&wbuf[bf][0][r4]);
+            float4 u4 = make_float4(0.f, 0.f, 0.f, 0.f), t4 = u4;
+            i16x4 Bh[kFirst ? NB : 1], Bl[kFirst ? NB : 1];
+            if constexpr (kFirst) {
+                u4 = *reinterpret_cast<const float4 *>(&wbuf[bf][1][r4]);
+                t4 = *reinterpret_cast<const float4 *>(&wbuf[bf][2][r4]);
 #pragma unroll
                 for (int q = 0; q < NB; ++q) {
-                    PV[g][q] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(hi, Bh[q], PV[g][q], 0, 0, 0);
-                    PV[g][q] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(hi, Bl[q], PV[g][q], 0, 0, 0);
-                    PV[g][q] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lo, Bh[q], PV[g][q], 0, 0, 0);
+                    const int o = (16 * q + c16) * kTStr + r4;
+                    Bh[q] = *reinterpret_cast<const i16x4 *>(&vhbuf[bf][o]);
+                    Bl[q] = *reinterpret_cast<const i16x4 *>(&vlbuf[bf][o]);
+                }
+            }
+            f32x4 D[G];
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+                D[g] = score(Xa, Yo[g], Cin, DK);
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const float E[4] = {ex2(fmaf(two_c, D[g][0], bk[g])),
+                                    ex2(fmaf(two_c, D[g][1], bk[g])),
+                                    ex2(fmaf(two_c, D[g][2], bk[g])),
+                                    ex2(fmaf(two_c, D[g][3], bk[g]))};
+                {
+                    float s = fmaf(E[0], a4.x, acc[0][g]);
+                    s = fmaf(E[1], a4.y, s);
+                    s = fmaf(E[2], a4.z, s);
+                    acc[0][g] = fmaf(E[3], a4.w, s);
+                }
+                if constexpr (kFirst) {
+                    float s = fmaf(E[0], u4.x, acc[1][g]);
+                    s = fmaf(E[1], u4.y, s);
+                    s = fmaf(E[2], u4.z, s);
+                    acc[1][g] = fmaf(E[3], u4.w, s);
+                    s = fmaf(E[0], t4.x, acc[2][g]);
+                    s = fmaf(E[1], t4.y, s);
+                    s = fmaf(E[2], t4.z, s);
+                    acc[2][g] = fmaf(E[3], t4.w, s);
+                    const float aE[4] = {E[0] * a4.x, E[1] * a4.y, E[2] * a4.z, E[3] * a4.w};
+                    i16x4 hi, lo;
+                    split2(aE, hi, lo);
+#pragma unroll
+                    for (int q = 0; q < NB; ++q) {
+                        PV[g][q] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(hi, Bh[q], PV[g][q], 0, 0, 0);
+                        PV[g][q] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(hi, Bl[q], PV[g][q], 0, 0, 0);
+                        PV[g][q] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lo, Bh[q], PV[g][q], 0, 0, 0);
+                    }
                 }
             }
         }
-    };
-    if (t0 < t1) {
-        Tile TA, TB;
-        fetch(TA, t0);
-        int t = t0;
-        for (; t + 1 < t1; t += 2) {
-            fetch(TB, t + 1);
-            __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the tile
-            tile(TA, t);
-            fetch(TA, min(t + 2, t1 - 1));
-            __builtin_amdgcn_sched_barrier(0);
-            tile(TB, t + 1);
-        }
-        if (t < t1)
-            tile(TA, t);
+        if (st + 1 < n_st)
+            stash(bf ^ 1);
+        __syncthreads();
     }
     // a key's scalars are spread over the four lanes sharing l % 16
     const size_t base = ((size_t)split * B + b) * m_pad + key0;
@@ -642,10 +778,11 @@ void rows_pass(const uint16_t *X, const uint16_t *Y, const HvpFeatWs &w, int d, 
                            (const uint16_t *)w.vh, (const uint16_t *)w.vl, u, two_c, sp.tps,
                            w.part_r, w.part_rv, w.part_rq);
     };
+    constexpr int NT = MODE == kRowsCg ? kTilesCg : kTilesVec;
     if (d == 32)
-        go(hvp_rows_kernel<1, G, MODE>);
+        go(hvp_rows_kernel<1, G, NT, MODE>);
     else
-        go(hvp_rows_kernel<2, G, MODE>);
+        go(hvp_rows_kernel<2, G, NT, MODE>);
 }
 
 template <int MODE>
@@ -661,10 +798,11 @@ void cols_pass(const uint16_t *X, const uint16_t *Y, const HvpFeatWs &w, int d, 
                            (const float *)w.wt, (const uint16_t *)w.vth, (const uint16_t *)w.vtl,
                            two_c, sp.tps, w.part_c, w.part_cv);
     };
+    constexpr int NT = MODE == kColsCg ? kTilesCg : kTilesVec;
     if (d == 32)
-        go(hvp_cols_kernel<1, G, MODE>);
+        go(hvp_cols_kernel<1, G, NT, MODE>);
     else
-        go(hvp_cols_kernel<2, G, MODE>);
+        go(hvp_cols_kernel<2, G, NT, MODE>);
 }
 
 }  // namespace
