@@ -158,6 +158,7 @@ struct GradWs {
     float *l2a = nullptr, *l2b = nullptr;
     uint16_t *xt = nullptr, *yt = nullptr;
     int *xredo = nullptr, *yredo = nullptr;
+    GradFWs mc{nullptr, nullptr, nullptr};
 };
 
 GradWs carve_grad(Carve &c, int B, int n, int m, int d, int dtype)
@@ -170,7 +171,7 @@ GradWs carve_grad(Carve &c, int B, int n, int m, int d, int dtype)
         w.kdy = c.take<KeyD>((size_t)B * m);
     }
     if (gradF_matrix_cores(dtype, d)) {
-        const int np = round_up(n, kPad), mp = round_up(m, kPad);
+        const int np = round_up(n, kGradPad), mp = round_up(m, kGradPad);
         w.xbias = c.take<float>((size_t)B * np);
         w.ybias = c.take<float>((size_t)B * mp);
         w.xsq = c.take<float>((size_t)B * n);
@@ -179,8 +180,12 @@ GradWs carve_grad(Carve &c, int B, int n, int m, int d, int dtype)
         w.l2b = c.take<float>((size_t)B * m);
         w.xt = c.take<uint16_t>((size_t)B * d * np);
         w.yt = c.take<uint16_t>((size_t)B * d * mp);
-        w.xredo = c.take<int>((size_t)B * (np / kPad));
-        w.yredo = c.take<int>((size_t)B * (mp / kPad));
+        w.xredo = c.take<int>((size_t)B * ceil_div(n, kPad));
+        w.yredo = c.take<int>((size_t)B * ceil_div(m, kPad));
+        const GradFSizes z = gradF_sizes(B, n, m, d);
+        w.mc.h = c.take<float>(z.h);
+        w.mc.part_s = c.take<float>(z.part_s);
+        w.mc.part_v = c.take<float>(z.part_v);
     }
     return w;
 }
@@ -718,7 +723,7 @@ int sinkhorn_dense_grad(const void *X, const void *Y, int dtype, const float *a,
         return hip_fail(e, "dense gradient: keys");
     const bool aligned = (uintptr_t)X % 16 == 0 && (uintptr_t)Y % 16 == 0;
     if (gradF_matrix_cores(dtype, d) && aligned) {
-        const int np = round_up(n, kPad), mp = round_up(m, kPad);
+        const int np = round_up(n, kGradPad), mp = round_up(m, kGradPad);
         // potentials are only read (warm start): biases c (pot - ||.||^2) + log2 w at eps
         SideF sx{X, w.xbias, const_cast<float *>(f), w.l2a, w.xsq, w.xredo, n, np};
         SideF sy{Y, w.ybias, const_cast<float *>(g), w.l2b, w.ysq, w.yredo, m, mp};
@@ -728,13 +733,13 @@ int sinkhorn_dense_grad(const void *X, const void *Y, int dtype, const float *a,
             return hip_fail(e, "dense gradient: biases");
         if (want_x) {
             if ((e = launch_transpose_bf16(Y, B, m, mp, d, w.yt, st)) ||
-                (e = launch_gradFm(sx, a, sy, w.yt, d, B, eps, dX, TX, st)) ||
+                (e = launch_gradF(sx, a, sy, w.yt, d, B, eps, w.mc, dX, TX, st)) ||
                 (e = launch_dense_grad(px, dX, TX, w.xredo, st)))
                 return hip_fail(e, "dense gradient (X side)");
         }
         if (want_y) {
             if ((e = launch_transpose_bf16(X, B, n, np, d, w.xt, st)) ||
-                (e = launch_gradFm(sy, b, sx, w.xt, d, B, eps, dY, TY, st)) ||
+                (e = launch_gradF(sy, b, sx, w.xt, d, B, eps, w.mc, dY, TY, st)) ||
                 (e = launch_dense_grad(py, dY, TY, w.yredo, st)))
                 return hip_fail(e, "dense gradient (Y side)");
         }

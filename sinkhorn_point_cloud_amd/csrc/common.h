@@ -229,14 +229,24 @@ hipError_t launch_copy_total(const int64_t *src, int64_t *dst, hipStream_t st);
 // log P in fp64.  only != NULL: just the 64-row blocks flagged there.
 hipError_t launch_dense_grad(const PlanArgs &p, float *grad, float *proj, const int *only,
                              hipStream_t st);
-// The same on the matrix cores for bf16 with d = 32 or 64: rows' side (points,
-// potential, squared norms; its redo array receives the per-block fallback
-// flags), row weights (NULL: uniform), and the key side's points, biases at
-// eps (from launch_packF with warm start) and transposed points [B][d][n_pad].
+// The same on the matrix cores for bf16 with d = 32 or 64, one side: the rows'
+// side (points, potential, squared norms; n_pad a multiple of kGradPad; its redo
+// array [B][ceil(n / 64)] receives the 64-row blocks left to the fp64 pass), row
+// weights (NULL: uniform), the key side's points, biases at eps (launch_packF
+// with warm start, n_pad a multiple of kGradPad) and transposed points
+// [B][d][n_pad], and scratch sized by gradF_sizes.
+constexpr int kGradPad = 512;
 bool gradF_matrix_cores(int dtype, int d);
-hipError_t launch_gradFm(const SideF &rows, const float *row_w, const SideF &keys,
-                         const uint16_t *keys_t, int d, int B, float eps, float *grad,
-                         float *proj, hipStream_t st);
+struct GradFSizes {
+    size_t h, part_s, part_v;   // floats
+};
+GradFSizes gradF_sizes(int B, int n, int m, int d);
+struct GradFWs {
+    float *h, *part_s, *part_v;
+};
+hipError_t launch_gradF(const SideF &rows, const float *row_w, const SideF &keys,
+                        const uint16_t *keys_t, int d, int B, float eps, const GradFWs &w,
+                        float *grad, float *proj, hipStream_t st);
 hipError_t launch_transpose_bf16(const void *X, int B, int n, int n_pad, int d, uint16_t *Xt,
                                  hipStream_t st);
 // Runs of equal keys in a key-sorted COO (per pair), by binary search:

@@ -6,177 +6,103 @@
 // projection are weighted averages over the plan, streamed like the update
 // without storing the plan).  With c = log2(e)/eps and the potentials f, g of
 // the solution,
-//     P_ij / a_i = E_ij = 2^(2c x_i.y_j + alpha_i + beta_j),
-//     alpha_i = c (f_i - ||x_i||^2),   beta_j = c (g_j - ||y_j||^2) + log2 b_j,
-// and per row the kernel accumulates the mass m_i = sum_j E_ij and
-// O_i = sum_j E_ij y_j, then writes
+//     P_ij / a_i = E_ij = 2^(2c (x_i.y_j + h_i) + beta_j),
+//     h_i = (f_i - ||x_i||^2) / 2,   beta_j = c (g_j - ||y_j||^2) + log2 b_j,
+// the mass pass of plan_rows_mc.h accumulates per row m_i = sum_j E_ij and
+// O_i = sum_j E_ij y_j (keys streamed through LDS, both sums on the matrix
+// cores and in fp32, key ranges split over work-groups), and the combine adds
+// the splits in order in fp64 and writes
 //     dX_i = 2 a_i (m_i x_i - O_i)   (= sum_j 2 P_ij (x_i - y_j)),
 //     T_i  = O_i / m_i               (= sum_j P_ij y_j / sum_j P_ij).
 // E is the plan divided by the row weight, so m_i is near 1 for potentials
-// that solve the problem, whatever the sizes.
-//
-// Two contractions per key tile of 16 keys, both on the matrix cores:
-//   - scores, transposed: D' = Y_tile X_group^T on v_mfma_f32_16x16x32_bf16
-//     (exact bf16 products, fp32 sums), keys in the rows of D', so lane l
-//     holds E for row l % 16 and keys 4 (l / 16) + r;
-//   - O += E Y_tile on v_mfma_f32_16x16x16_bf16: those four values are exactly
-//     the lane's A operand (A[row = l % 16][key = 4 (l / 16) + e]); E enters as
-//     two bf16 pieces, hi + lo, which keep 16 of its bits.  The B operand
-//     (keys 4 (l / 16) + e, dim l % 16 of a 16-dim block) is one 8-byte load
-//     from a transposed copy of the keys, Yt[d][m_pad].
-//
-// A work-group is 4 waves on 64 rows, each wave taking every 4th key tile; the
-// waves merge in LDS in a fixed order.  A row block with a row whose mass
-// falls outside [2^-64, 2^100] (potentials far from solving these weights) is
-// flagged; the fp64 plan pass redoes it.
-#include "mfma_bf16.h"
+// that solve the problem, whatever the sizes.  A 64-row block with a live row
+// whose mass falls outside [2^-64, 2^100] (potentials far from solving these
+// weights) is flagged and left unwritten; the fp64 plan pass redoes it.
+#include "plan_rows_mc.h"
 
 namespace sk {
 namespace {
 
-constexpr int kWavesG = 4;
-constexpr int kKeysG = 16;
-constexpr int kGroupsG = 4;
-constexpr float kMassLo = 5.421010862e-20f;  // 2^-64
-constexpr float kMassHi = 1.2676506e30f;     // 2^100
+constexpr int kGroupsG = 4;                          // 16-row groups per wave
+constexpr int kTilesG = 4;                           // 16-key tiles per LDS stage
+constexpr int kTargetG = 512;                        // work-groups a pass aims for
+constexpr int kRowsPerWg = mc::kWaves * 16 * kGroupsG;
+constexpr double kMassLoG = 5.421010862427522e-20;   // 2^-64
+constexpr double kMassHiG = 1.2676506002282294e30;   // 2^100
+static_assert(kGradPad % kRowsPerWg == 0, "padding must hold whole work-groups");
 
-template <int DK>
-__global__ __launch_bounds__(kWavesG *kWave) void gradFm_kernel(
-    const uint16_t *__restrict__ X, const float *__restrict__ xpot, const float *__restrict__ xsq,
-    const float *__restrict__ xw, int n, const uint16_t *__restrict__ Y,
-    const uint16_t *__restrict__ Yt, const float *__restrict__ ybias, int m, int m_pad,
-    float c, float *__restrict__ grad, float *__restrict__ proj, int *__restrict__ redo)
+mc::Split grad_split(int B, int n_pad, int m_pad)
 {
-    constexpr int d = 32 * DK;
-    constexpr int NB = d / 16;   // 16-dim blocks of the output
-    __shared__ float osum[kWave][d + 1];
-    __shared__ float msum[kWave];
+    return mc::split_of(n_pad / kRowsPerWg * B, m_pad / mc::kTile, kTargetG);
+}
+
+// h_i for the rows of one side ([B][n_pad]); rows of weight 0 and padding rows
+// get kNeg, so their E is 0 and they add nothing
+__global__ void grad_h_kernel(const float *__restrict__ pot, const float *__restrict__ sq,
+                              const float *__restrict__ w, int n, int n_pad, float *__restrict__ h)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    const int b = blockIdx.y;
+    if (i >= n_pad)
+        return;
+    const size_t k = (size_t)b * n + i;
+    const bool live = i < n && (w ? w[k] > 0.f : true);
+    h[(size_t)b * n_pad + i] = live ? (float)(0.5 * ((double)pot[k] - (double)sq[k])) : kNeg;
+}
+
+// One work-group per 64-row block: the splits of m and O added in order (fp64),
+// the block's range check, then dX and T (left to the fp64 pass when flagged).
+__global__ __launch_bounds__(256) void grad_combine(const float *__restrict__ part_s,
+                                                    const float *__restrict__ part_v, int S,
+                                                    int B, int n, int n_pad, int d,
+                                                    const uint16_t *__restrict__ X,
+                                                    const float *__restrict__ w,
+                                                    float *__restrict__ grad,
+                                                    float *__restrict__ proj,
+                                                    int *__restrict__ redo)
+{
+    __shared__ double ms[kWave];
     __shared__ int flag;
-    const int b = blockIdx.z;
-    const int lane = lane_id();
-    const int w = wave_id_uniform();
-    const int row0 = blockIdx.x * kWave;
-    const int kq = lane >> 4;
-    const int c16 = lane & 15;
-    const float two_c = 2.0f * c;
-
-    // rows as the B operand of the transposed score; alpha / 2c rides in the
-    // accumulator input: 2c (x.y + (f - ||x||^2) / 2) = 2c x.y + alpha
-    bf16x8 Xo[kGroupsG][DK];
-    f32x4 Cin[kGroupsG];
-#pragma unroll
-    for (int g = 0; g < kGroupsG; ++g) {
-        const int ra = row0 + 16 * g + c16;
-        const int rc = min(ra, n - 1);
-#pragma unroll
-        for (int kb = 0; kb < DK; ++kb) {
-            bf16x8 v = load8(X + ((size_t)b * n + rc) * d + 32 * kb + 8 * kq);
-            if (ra >= n)
-                v = bf16x8{};
-            Xo[g][kb] = v;
+    const int blk = blockIdx.x, b = blockIdx.y, nb = gridDim.x;
+    const int tid = threadIdx.x;
+    if (tid < kWave) {   // wave 0: a row per lane
+        const int row = blk * kWave + tid;
+        double s = 0.0;
+        bool bad = false;
+        if (row < n) {
+            for (int p = 0; p < S; ++p)
+                s += (double)part_s[((size_t)p * B + b) * n_pad + row];
+            const bool live = w ? w[(size_t)b * n + row] > 0.f : true;
+            bad = live && !(s >= kMassLoG && s <= kMassHiG);
         }
-        const size_t k = (size_t)b * n + rc;
-        const float h = ra < n ? (float)(0.5 * ((double)xpot[k] - (double)xsq[k])) : 0.f;
-        Cin[g] = f32x4{h, h, h, h};
-    }
-    f32x4 O[kGroupsG][NB];
-    float mass[kGroupsG];
-#pragma unroll
-    for (int g = 0; g < kGroupsG; ++g) {
-        mass[g] = 0.f;
-#pragma unroll
-        for (int q = 0; q < NB; ++q)
-            O[g][q] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-
-    const uint16_t *yb = Y + (size_t)b * m * d;
-    const uint16_t *ytb = Yt + (size_t)b * d * m_pad;
-    const float *beb = ybias + (size_t)b * m_pad;
-    const int n_tiles = m_pad / kKeysG;
-    for (int t = w; t < n_tiles; t += kWavesG) {
-        const int j = min(t * kKeysG + c16, m - 1);   // padding keys: bias -1e30, E = 0
-        bf16x8 Ka[DK];
-#pragma unroll
-        for (int kb = 0; kb < DK; ++kb)
-            Ka[kb] = load8(yb + (size_t)j * d + 32 * kb + 8 * kq);
-        const float4 be = *reinterpret_cast<const float4 *>(beb + t * kKeysG + 4 * kq);
-        i16x4 Bt[NB];
-#pragma unroll
-        for (int q = 0; q < NB; ++q)
-            Bt[q] = load4(ytb + (size_t)(16 * q + c16) * m_pad + t * kKeysG + 4 * kq);
-#pragma unroll
-        for (int g = 0; g < kGroupsG; ++g) {
-            f32x4 D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ka[0], Xo[g][0], Cin[g], 0, 0, 0);
-#pragma unroll
-            for (int kb = 1; kb < DK; ++kb)
-                D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ka[kb], Xo[g][kb], D, 0, 0, 0);
-            const float E[4] = {ex2(fmaf(two_c, D[0], be.x)), ex2(fmaf(two_c, D[1], be.y)),
-                                ex2(fmaf(two_c, D[2], be.z)), ex2(fmaf(two_c, D[3], be.w))};
-            mass[g] += (E[0] + E[1]) + (E[2] + E[3]);
-            i16x4 hi, lo;
-            split2(E, hi, lo);
-#pragma unroll
-            for (int q = 0; q < NB; ++q) {
-                O[g][q] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(hi, Bt[q], O[g][q], 0, 0, 0);
-                O[g][q] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lo, Bt[q], O[g][q], 0, 0, 0);
-            }
-        }
-    }
-    // a row's mass is spread over the four lanes sharing l % 16
-#pragma unroll
-    for (int g = 0; g < kGroupsG; ++g) {
-        mass[g] += __shfl_xor(mass[g], 16, kWave);
-        mass[g] += __shfl_xor(mass[g], 32, kWave);
-    }
-    // waves add their partials into LDS one after another (fixed order)
-    for (int v = 0; v < kWavesG; ++v) {
-        if (w == v) {
-#pragma unroll
-            for (int g = 0; g < kGroupsG; ++g) {
-#pragma unroll
-                for (int q = 0; q < NB; ++q)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        float &o = osum[16 * g + 4 * kq + r][16 * q + c16];
-                        o = v == 0 ? O[g][q][r] : o + O[g][q][r];
-                    }
-                if (kq == 0) {
-                    float &s = msum[16 * g + c16];
-                    s = v == 0 ? mass[g] : s + mass[g];
-                }
-            }
-        }
-        __syncthreads();
-    }
-    if (w == 0) {
-        const int row = row0 + lane;
-        const float ms = msum[lane];
-        const bool live = row < n && (xw ? xw[(size_t)b * n + row] > 0.f : true);
-        const bool bad = live && !(ms >= kMassLo && ms <= kMassHi);
-        const int f = __ballot(bad) != 0 ? 1 : 0;
-        if (lane == 0) {
-            flag = f;
-            redo[b * gridDim.x + blockIdx.x] = f;
+        ms[tid] = s;
+        const bool any = __ballot(bad) != 0;
+        if (tid == 0) {
+            flag = any ? 1 : 0;
+            redo[(size_t)b * nb + blk] = any ? 1 : 0;
         }
     }
     __syncthreads();
     if (flag)
         return;
-    const float inv_n = 1.0f / (float)n;
-    for (int e = threadIdx.x; e < kWave * d; e += kWavesG * kWave) {
+    const double inv_n = 1.0 / (double)n;
+    for (int e = tid; e < kWave * d; e += 256) {
         const int r = e / d, k = e % d;
-        const int row = row0 + r;
+        const int row = blk * kWave + r;
         if (row >= n)
             continue;
+        double O = 0.0;
+        for (int p = 0; p < S; ++p)
+            O += (double)part_v[(((size_t)p * B + b) * n_pad + row) * d + k];
         const size_t o = ((size_t)b * n + row) * d + k;
-        const float wi = xw ? xw[(size_t)b * n + row] : inv_n;
-        const float ms = msum[r], Ok = osum[r][k];
-        const float x = bf16_to_float(X[o]);
-        const bool live = wi > 0.f;
+        const double wi = w ? (double)w[(size_t)b * n + row] : inv_n;
+        const double m = ms[r];
+        const bool live = wi > 0.0;
+        const double x = (double)bf16_to_float(X[o]);
         if (grad)
-            grad[o] = live ? 2.0f * wi * fmaf(ms, x, -Ok) : 0.f;
+            grad[o] = live ? (float)(2.0 * wi * (m * x - O)) : 0.f;
         if (proj)
-            proj[o] = live ? Ok / ms : 0.f;
+            proj[o] = live && m > 0.0 ? (float)(O / m) : 0.f;
     }
 }
 
@@ -213,24 +139,41 @@ hipError_t launch_transpose_bf16(const void *X, int B, int n, int n_pad, int d, 
     return hipGetLastError();
 }
 
-hipError_t launch_gradFm(const SideF &rows, const float *row_w, const SideF &keys,
-                         const uint16_t *keys_t, int d, int B, float eps, float *grad,
-                         float *proj, hipStream_t st)
+GradFSizes gradF_sizes(int B, int n, int m, int d)
 {
-    const float c = scale_of(eps);
-    dim3 grid(rows.n_pad / kWave, 1, B);
+    const int np = round_up(n, kGradPad), mp = round_up(m, kGradPad);
+    const int S = std::max(grad_split(B, np, mp).S, grad_split(B, mp, np).S);
+    const size_t rows = (size_t)B * std::max(np, mp);
+    GradFSizes z;
+    z.h = rows;
+    z.part_s = (size_t)S * rows;
+    z.part_v = (size_t)S * rows * d;
+    return z;
+}
+
+hipError_t launch_gradF(const SideF &rows, const float *row_w, const SideF &keys,
+                        const uint16_t *keys_t, int d, int B, float eps, const GradFWs &w,
+                        float *grad, float *proj, hipStream_t st)
+{
+    const float two_c = 2.0f * scale_of(eps);
+    const int np = rows.n_pad, mp = keys.n_pad;
+    hipLaunchKernelGGL(grad_h_kernel, dim3(ceil_div(np, 256), B), dim3(256), 0, st,
+                       (const float *)rows.pot, (const float *)rows.sq, row_w, rows.n, np, w.h);
+    const mc::Split sp = grad_split(B, np, mp);
+    const dim3 grid(sp.S, np / kRowsPerWg, B), block(mc::kWaves * kWave);
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid, block, 0, st, (const uint16_t *)rows.pts,
+                           (const float *)w.h, rows.n, np, (const uint16_t *)keys.pts, keys_t,
+                           (const float *)keys.bias, keys.n, mp, nullptr, nullptr, nullptr,
+                           two_c, sp.tps, w.part_s, w.part_v, nullptr);
+    };
     if (d == 32)
-        hipLaunchKernelGGL((gradFm_kernel<1>), grid, dim3(kWavesG * kWave), 0, st,
-                           (const uint16_t *)rows.pts, (const float *)rows.pot,
-                           (const float *)rows.sq, row_w, rows.n, (const uint16_t *)keys.pts,
-                           keys_t, (const float *)keys.bias, keys.n, keys.n_pad, c, grad, proj,
-                           rows.redo);
+        go(mc::rows_kernel<1, kGroupsG, kTilesG, mc::kRowsMass>);
     else
-        hipLaunchKernelGGL((gradFm_kernel<2>), grid, dim3(kWavesG * kWave), 0, st,
-                           (const uint16_t *)rows.pts, (const float *)rows.pot,
-                           (const float *)rows.sq, row_w, rows.n, (const uint16_t *)keys.pts,
-                           keys_t, (const float *)keys.bias, keys.n, keys.n_pad, c, grad, proj,
-                           rows.redo);
+        go(mc::rows_kernel<2, kGroupsG, kTilesG, mc::kRowsMass>);
+    hipLaunchKernelGGL(grad_combine, dim3(ceil_div(rows.n, kWave), B), dim3(256), 0, st,
+                       (const float *)w.part_s, (const float *)w.part_v, sp.S, B, rows.n, np, d,
+                       (const uint16_t *)rows.pts, row_w, grad, proj, rows.redo);
     return hipGetLastError();
 }
 

@@ -25,16 +25,9 @@ hipError_t launch_cg_step_wide(const double *mb, const float *q2_part, int S, in
                                double stop2, bool project, double *red_pq, double *red_s,
                                double *red_q, float *x32, float *dir32, hipStream_t st);
 // The same product on the matrix cores for bf16 with d = 32 or 64 (X, Y 16-byte
-// aligned).  Passes are split over S work-group columns of tps 16-point tiles.
-// Point counts are padded to kHvpPad there.
+// aligned).  Point counts are padded to kHvpPad there.
 constexpr int kHvpPad = 512;
 bool hvp_matrix_cores(int dtype, int d);
-struct HvpSplit {
-    int S, tps;
-};
-// `blocks` work-groups' worth of points (all pairs) against `tiles` streamed
-// 16-point tiles, aiming at `target` work-groups: S splits of tps tiles.
-HvpSplit hvp_split(int blocks, int tiles, int target);
 struct HvpFeatSizes {
     size_t part_r, part_rv, part_c, part_cv;   // floats of the partial-sum buffers
 };

@@ -640,6 +640,7 @@ def check_dense_grad(c, eps, fo, go, sel_x=None, sel_y=None, tol=1e-4):
     (2, 300, 257, 3, "f32", "dirichlet", 0.01, 1e-4),
     (1, 130, 77, 8, "f32", "dirichlet", 0.1, 1e-4),
     (1, 200, 190, 64, "bf16", "uniform", 0.2, 1e-4),
+    (2, 1100, 900, 64, "bf16", "dirichlet", 0.1, 1e-4),
     (2, 300, 170, 32, "bf16", "dirichlet", 0.05, 1e-4),
     (1, 129, 1000, 64, "bf16", "dirichlet", 0.02, 1e-3),
     (1, 90, 100, 100, "f32", "uniform", 0.5, 1e-4),
