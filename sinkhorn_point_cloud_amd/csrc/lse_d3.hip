@@ -538,21 +538,29 @@ __device__ __forceinline__ void load_rows(bf16x8 (&A)[G], const uint16_t *qrec_r
 }
 
 // Their shifts M_i = c (||x_i||^2 - f_i), carried as -M in the accumulator
-// input, and empty sums.
+// input, and empty sums.  Each lane loads one row's point and potential and
+// forms its shift; the wave hands the shifts through shv (64 floats of LDS,
+// 16-byte aligned, the wave's own) to the lanes whose results hold the row:
+// two loads a lane instead of one per (row group, result register).
 template <int G = kGroups>
 __device__ __forceinline__ void load_shifts(f32x4 (&Cn)[G], f32x4 (&S)[G], const float4 *qrow,
-                                            const float *qpot_b, int nq, int row0, int kq, float c)
+                                            const float *qpot_b, int nq, int row0, int kq, float c,
+                                            float *shv)
 {
+    const int lane = lane_id();
+    if (lane < 16 * G) {
+        const float4 p = qrow[lane];
+        const float f = row0 + lane < nq ? qpot_b[row0 + lane] : 0.f;
+        shv[lane] = -(c * (sq3(p.x, p.y, p.z) - f));
+    }
+    __builtin_amdgcn_wave_barrier();   // a wave's LDS accesses complete in order
 #pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int lr = 16 * g + 4 * kq + r;
-            const float4 p = qrow[lr];
-            const float f = row0 + lr < nq ? qpot_b[row0 + lr] : 0.f;
-            Cn[g][r] = -(c * (sq3(p.x, p.y, p.z) - f));
-            S[g][r] = 0.f;
-        }
+    for (int g = 0; g < G; ++g) {
+        const float4 v = *reinterpret_cast<const float4 *>(shv + 16 * g + 4 * kq);
+        Cn[g] = f32x4{v.x, v.y, v.z, v.w};
+        S[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    __builtin_amdgcn_wave_barrier();   // shv is written again later
 }
 
 __device__ __forceinline__ float row16_max(float v)
@@ -645,7 +653,7 @@ __global__ __launch_bounds__(W *kWave) void lse3m_kernel(
     float2 *__restrict__ part, const int *__restrict__ redo, int nq, int nq_pad, int nk_pad,
     int tiles_per_split, float two_c, double eps_ln2, double c_next)
 {
-    __shared__ float2 red[W][kWave];
+    __shared__ __align__(16) float2 red[W][kWave];
     __shared__ int stale;
     // XCD-aware placement for batches: the dispatcher deals work-groups to the
     // XCDs in turn, so the linear id is remapped to give each XCD a contiguous
@@ -686,7 +694,8 @@ __global__ __launch_bounds__(W *kWave) void lse3m_kernel(
     bf16x8 A[G];
     f32x4 Cn[G], S[G];
     load_rows<G>(A, qrec_rows, lane_off);
-    load_shifts<G>(Cn, S, qrow, qpot + (size_t)b * nq, nq, row0, kq, 0.5f * two_c);
+    load_shifts<G>(Cn, S, qrow, qpot + (size_t)b * nq, nq, row0, kq, 0.5f * two_c,
+                   reinterpret_cast<float *>(red[w]));
     const int row = row0 + lane;
     const bool mine = lane < R && row < nq;   // lane of wave 0 that finishes a row
     // the finishing lanes fetch their row's point and log2 weight now, off the
@@ -776,7 +785,8 @@ __device__ __forceinline__ void wave_rows(const Side3 &q, const Side3 &k, int b,
     bf16x8 A[kGroups];
     f32x4 Cn[kGroups], S[kGroups];
     load_rows(A, qrec_rows, lane_off);
-    load_shifts(Cn, S, qrow, q.pot + (size_t)b * q.n, q.n, row0, kq, 0.5f * two_c);
+    load_shifts(Cn, S, qrow, q.pot + (size_t)b * q.n, q.n, row0, kq, 0.5f * two_c,
+                reinterpret_cast<float *>(red));
     float M = 0.f, Sf = 0.f;
     const int row = row0 + lane;
     if (!stale) {
@@ -818,7 +828,7 @@ __global__ __launch_bounds__(kPairWaves *kWave) void lse3p_kernel(Side3 x, Side3
                                                                   float two_c, double eps_ln2,
                                                                   double c_next_last, int cold)
 {
-    __shared__ float2 red[kPairWaves][kWave];
+    __shared__ __align__(16) float2 red[kPairWaves][kWave];
     __shared__ uint4 recs[2][kLds ? kLdsMaxPoints * kRec / 8 : 1];   // unused without kLds
     const int b = blockIdx.x;
     const int w = wave_id_uniform();
