@@ -789,6 +789,14 @@ __device__ __forceinline__ void wave_rows(const Side3 &q, const Side3 &k, int b,
                 reinterpret_cast<float *>(red));
     float M = 0.f, Sf = 0.f;
     const int row = row0 + lane;
+    // the row this lane finishes: its point and log2 weight, fetched now, off the
+    // path that follows the stream
+    float4 prow = make_float4(0.f, 0.f, 0.f, 0.f);
+    float lw = 0.f;
+    if (row < q.n) {
+        prow = qrow[lane];
+        lw = q.l2w[(size_t)b * q.n + row];
+    }
     if (!stale) {
         shifted_stream<1, kGroups, kLds>(A, Cn, S, kb, k.n_pad, lane_off, 0, n_tiles, k_lds);
         wave_sums(Cn, S, red, kq, c16);
@@ -810,9 +818,8 @@ __device__ __forceinline__ void wave_rows(const Side3 &q, const Side3 &k, int b,
         Sf = red[lane].y;
     }
     if (row < q.n) {
-        const float beta = finish_row(q.pts, q.krec, q.pot, q.l2w[(size_t)b * q.n + row],
-                                      (size_t)b * q.n_pad + row, (size_t)b * q.n + row,
-                                      q.pts[(size_t)b * q.n_pad + row], M, Sf, eps_ln2, c_next);
+        const float beta = finish_row(q.pts, q.krec, q.pot, lw, (size_t)b * q.n_pad + row,
+                                      (size_t)b * q.n + row, prow, M, Sf, eps_ln2, c_next);
         if constexpr (kLds)
             store_key_bias_lds(q_lds, row, beta);
     }
