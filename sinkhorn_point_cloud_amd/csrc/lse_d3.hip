@@ -464,11 +464,15 @@ __device__ __forceinline__ void key_stream(const bf16x8 (&A)[G], const f32x4 (&C
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
         (void *)kb, (short)0, nk_pad * kRec * (int)sizeof(uint16_t), 0x00020000);
     const int voff = lane_off * (int)sizeof(uint16_t);
+    // the lane's chunk of record t kTile + (l & 15) sits at 4 kTile t + lane_lds:
+    // the swizzle (r >> 1) & 3 of lds_chunk depends on the low bits of r only
+    static_assert(kTile % 8 == 0, "tile starts keep the swizzle");
     const int lane_rec = lane_id() & 15, lane_chunk = lane_id() >> 4;
+    const int lane_lds = lds_chunk(lane_rec, lane_chunk);
     auto key = [&](int k) {
         const int t = min(first + k * W, last);
         if constexpr (kLds)
-            return __builtin_bit_cast(bf16x8, lds[lds_chunk(t * kTile + lane_rec, lane_chunk)]);
+            return __builtin_bit_cast(bf16x8, lds[4 * kTile * t + lane_lds]);
         else
             return __builtin_bit_cast(
                 bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
