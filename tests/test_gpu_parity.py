@@ -1251,6 +1251,52 @@ def test_forward_and_gradient_replay_from_a_captured_graph():
             assert torch.equal(t, r), f"replay {rep}"
 
 
+@pytest.mark.parametrize("d,dtype", [(3, "f32"), (64, "bf16")])
+def test_hvp_and_dense_grad_replay_from_a_captured_graph(d, dtype):
+    # the Hessian-vector product (fp64 passes for d = 3, matrix cores for bf16
+    # d = 64, with its CG stop decided on the device) and the dense gradient
+    # launch kernels only: captured once, every replay equals the eager run
+    B, n, m = 2, 150, 170
+    eps = 0.5 if d == 64 else 0.1
+    c = workloads.random_case(66, B, n, m, d, weights="dirichlet", dtype=dtype)
+    X, Y = points(c)
+    a, b = dev(c["a"]), dev(c["b"])
+    f, g, _ = sk.potentials(X, Y, a, b, eps=[eps], iters=[300])
+    V = dev(np.random.default_rng(12).normal(size=(B, n, d)).astype(np.float32))
+    dt = sk.SK_BF16 if dtype == "bf16" else sk.SK_F32
+    hws = torch.empty(sk.workspace_bytes(sk.SK_OP_HVP, B, n, m, d, dt), dtype=torch.uint8,
+                      device=X.device)
+    gws = torch.empty(sk.workspace_bytes(sk.SK_OP_DENSE_GRAD, B, n, m, d, dt),
+                      dtype=torch.uint8, device=X.device)
+    HV = torch.empty(B, n, d, device=X.device)
+    dg = (torch.empty(B, n, d, device=X.device), torch.empty(B, n, d, device=X.device),
+          torch.empty(B, m, d, device=X.device), torch.empty(B, m, d, device=X.device))
+
+    def step():
+        _, res = sk.hvp(X, Y, a, b, f, g, eps, V, cg_iters=40, workspace=hws, out=HV)
+        sk.dense_grad(X, Y, a, b, f, g, eps, workspace=gws, out=dg)
+        return res
+
+    res = step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (HV, *dg, res)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            res_g = step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in (HV, *dg, res_g):
+            t.fill_(float("nan"))          # eager work between the replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for t, r in zip((HV, *dg, res_g), ref):
+            assert torch.equal(t, r), f"replay {rep}"
+
+
 def test_binding_refuses_bad_output_buffers_before_the_call():
     # each public function checks caller-provided outputs (dtype, exact shape,
     # contiguous layout, device) before a pointer reaches the C ABI; the
