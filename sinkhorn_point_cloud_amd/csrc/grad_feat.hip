@@ -141,13 +141,14 @@ hipError_t launch_transpose_bf16(const void *X, int B, int n, int n_pad, int d, 
 
 GradFSizes gradF_sizes(int B, int n, int m, int d)
 {
+    // one side at a time: X rows against Y keys, then Y rows against X keys
     const int np = round_up(n, kGradPad), mp = round_up(m, kGradPad);
-    const int S = std::max(grad_split(B, np, mp).S, grad_split(B, mp, np).S);
-    const size_t rows = (size_t)B * std::max(np, mp);
+    const size_t px = (size_t)grad_split(B, np, mp).S * np;
+    const size_t py = (size_t)grad_split(B, mp, np).S * mp;
     GradFSizes z;
-    z.h = rows;
-    z.part_s = (size_t)S * rows;
-    z.part_v = (size_t)S * rows * d;
+    z.h = (size_t)B * std::max(np, mp);
+    z.part_s = (size_t)B * std::max(px, py);
+    z.part_v = z.part_s * d;
     return z;
 }
 

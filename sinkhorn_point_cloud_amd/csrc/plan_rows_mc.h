@@ -43,7 +43,8 @@ __device__ __forceinline__ f32x4 score(const bf16x8 (&A)[2], const bf16x8 (&Bm)[
 }
 
 // S splits of tps tiles for `blocks` work-groups' worth of points (all pairs)
-// against `tiles` streamed tiles, aiming at `target` work-groups.  S is a
+// against `tiles` streamed tiles, aiming at `target` work-groups.  When the
+// points alone give enough work-groups there is one split; otherwise S is a
 // multiple of the 8 XCDs where the tiles allow: work-groups are dealt to them
 // round-robin by linear index, split fastest, so each XCD keeps to the same
 // key ranges.
@@ -52,7 +53,8 @@ struct Split {
 };
 inline Split split_of(int blocks, int tiles, int target)
 {
-    const int want = std::min(round_up(std::max(1, ceil_div(target, blocks)), 8), kMaxSplits);
+    const int need = ceil_div(target, std::max(1, blocks));
+    const int want = need <= 1 ? 1 : std::min(round_up(need, 8), kMaxSplits);
     Split sp;
     sp.tps = ceil_div(tiles, want);
     sp.S = ceil_div(tiles, sp.tps);

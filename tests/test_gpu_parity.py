@@ -150,6 +150,32 @@ def test_largest_cloud_per_pair(n, m):
     check_potentials(c, [0.1], [1])
 
 
+def test_feature_matrix_cores_at_a_million_points():
+    # 2^20 bf16 points of d = 64 against 300: the row pass's d-vector partials
+    # hold 2^26 floats, the Y side's keys are split 64 ways; the dense gradient
+    # on sampled rows of both sides against the oracle, and the HVP's symmetry
+    n, m, d, eps = 1 << 20, 300, 64, 0.5
+    c = workloads.random_case(503, 1, n, m, d, weights="uniform", dtype="bf16")
+    X, Y = points(c)
+    a, b = dev(c["a"]), dev(c["b"])
+    f, g, _ = sk.potentials(X, Y, a, b, eps=[eps], iters=[20])
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(13)
+    sel_x = np.sort(rng.choice(n, 64, replace=False))
+    sel_y = np.sort(rng.choice(m, 16, replace=False))
+    check_dense_grad(c, eps, host(f), host(g), sel_x, sel_y, tol=1e-4)
+    U = dev((rng.normal(size=(1, n, d)) / 8).astype(np.float32))
+    V = dev((rng.normal(size=(1, n, d)) / 8).astype(np.float32))
+    HU, ru = sk.hvp(X, Y, a, b, f, g, eps, U, cg_iters=60)
+    HV, rv = sk.hvp(X, Y, a, b, f, g, eps, V, cg_iters=60)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(HU).all()) and bool(torch.isfinite(HV).all())
+    assert float(ru[0]) < 1e-4 and float(rv[0]) < 1e-4
+    uhv = float((U.double() * HV.double()).sum())
+    vhu = float((V.double() * HU.double()).sum())
+    assert abs(uhv - vhu) <= 1e-4 * float((U.double() * HV.double()).abs().sum())
+
+
 def test_most_pairs_per_call():
     # 65535 pairs (the largest batch the boundary accepts) of small clouds: every
     # per-pair grid dimension at its limit, potentials, plan and fused loss
