@@ -777,7 +777,8 @@ template <bool kLds>
 __device__ __forceinline__ void wave_rows(const Side3 &q, const Side3 &k, int b, int row0,
                                           float two_c, double eps_ln2, double c_next,
                                           float2 *red, bool stale, const uint4 *k_lds,
-                                          uint4 *q_lds)
+                                          uint4 *q_lds, const float *q_sq, float *q_pot,
+                                          bool last)
 {
     const int lane = lane_id();
     const int kq = lane >> 4, c16 = lane & 15;
@@ -789,18 +790,36 @@ __device__ __forceinline__ void wave_rows(const Side3 &q, const Side3 &k, int b,
     bf16x8 A[kGroups];
     f32x4 Cn[kGroups], S[kGroups];
     load_rows(A, qrec_rows, lane_off);
-    load_shifts(Cn, S, qrow, q.pot + (size_t)b * q.n, q.n, row0, kq, 0.5f * two_c,
-                reinterpret_cast<float *>(red));
-    float M = 0.f, Sf = 0.f;
     const int row = row0 + lane;
-    // the row this lane finishes: its point and log2 weight, fetched now, off the
-    // path that follows the stream
     float4 prow = make_float4(0.f, 0.f, 0.f, 0.f);
     float lw = 0.f;
-    if (row < q.n) {
-        prow = qrow[lane];
-        lw = q.l2w[(size_t)b * q.n + row];
+    if constexpr (kLds) {
+        // squared norms and potentials from the stage's LDS copy (the same values
+        // the global arrays would give: written by this work-group)
+        const float sh = -(0.5f * two_c * (q_sq[row] - q_pot[row]));
+        float *shv = reinterpret_cast<float *>(red);
+        shv[lane] = sh;
+        __builtin_amdgcn_wave_barrier();   // a wave's LDS accesses complete in order
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g) {
+            const float4 v = *reinterpret_cast<const float4 *>(shv + 16 * g + 4 * kq);
+            Cn[g] = f32x4{v.x, v.y, v.z, v.w};
+            S[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        __builtin_amdgcn_wave_barrier();
+        if (row < q.n)
+            lw = q.l2w[(size_t)b * q.n + row];
+    } else {
+        load_shifts(Cn, S, qrow, q.pot + (size_t)b * q.n, q.n, row0, kq, 0.5f * two_c,
+                    reinterpret_cast<float *>(red));
+        // the row this lane finishes: its point and log2 weight, fetched now, off
+        // the path that follows the stream
+        if (row < q.n) {
+            prow = qrow[lane];
+            lw = q.l2w[(size_t)b * q.n + row];
+        }
     }
+    float M = 0.f, Sf = 0.f;
     if (!stale) {
         shifted_stream<1, kGroups, kLds>(A, Cn, S, kb, k.n_pad, lane_off, 0, n_tiles, k_lds);
         wave_sums(Cn, S, red, kq, c16);
@@ -822,10 +841,25 @@ __device__ __forceinline__ void wave_rows(const Side3 &q, const Side3 &k, int b,
         Sf = red[lane].y;
     }
     if (row < q.n) {
-        const float beta = finish_row(q.pts, q.krec, q.pot, lw, (size_t)b * q.n_pad + row,
-                                      (size_t)b * q.n + row, prow, M, Sf, eps_ln2, c_next);
-        if constexpr (kLds)
+        if constexpr (kLds) {
+            // the arithmetic of finish_row, the state kept in LDS; the global
+            // arrays are written by the stage's last iteration only
+            const float sq = q_sq[row];
+            const double lse2 = (double)M + (double)lg2(Sf);
+            const float f = (float)((double)sq - lse2 * eps_ln2);
+            q_pot[row] = f;
+            const float beta = lw == kNeg ? kNeg : bias_of(c_next, f, sq, lw);
             store_key_bias_lds(q_lds, row, beta);
+            if (last) {
+                const size_t pt = (size_t)b * q.n_pad + row;
+                q.pot[(size_t)b * q.n + row] = f;
+                q.pts[pt].w = beta;
+                store_key_bias(q.krec + pt * kRec, beta);
+            }
+        } else {
+            finish_row(q.pts, q.krec, q.pot, lw, (size_t)b * q.n_pad + row, (size_t)b * q.n + row,
+                       prow, M, Sf, eps_ln2, c_next);
+        }
     }
     __builtin_amdgcn_wave_barrier();   // red is reused by the next block
 }
@@ -841,6 +875,8 @@ __global__ __launch_bounds__(kPairWaves *kWave) void lse3p_kernel(Side3 x, Side3
 {
     __shared__ __align__(16) float2 red[kPairWaves][kWave];
     __shared__ uint4 recs[2][kLds ? kLdsMaxPoints * kRec / 8 : 1];   // unused without kLds
+    // with kLds also every point's squared norm and potential, both sides
+    __shared__ float sqs[2][kLds ? kLdsMaxPoints : 1], pots[2][kLds ? kLdsMaxPoints : 1];
     const int b = blockIdx.x;
     const int w = wave_id_uniform();
     const double c_same = 0.5 * (double)two_c;
@@ -853,19 +889,27 @@ __global__ __launch_bounds__(kPairWaves *kWave) void lse3p_kernel(Side3 x, Side3
             const int chunks = side[sd]->n_pad * (kRec / 8);   // n_pad <= kLdsMaxPoints
             for (int e = threadIdx.x; e < chunks; e += kPairWaves * kWave)
                 recs[sd][lds_chunk(e >> 2, e & 3)] = src[e];
+            const float4 *pts = side[sd]->pts + (size_t)b * side[sd]->n_pad;
+            const float *pot = side[sd]->pot + (size_t)b * side[sd]->n;
+            for (int i = threadIdx.x; i < side[sd]->n_pad; i += kPairWaves * kWave) {
+                const float4 p = pts[i];
+                sqs[sd][i] = sq3(p.x, p.y, p.z);
+                pots[sd][i] = i < side[sd]->n ? pot[i] : 0.f;
+            }
         }
         __syncthreads();
     }
     for (int it = 0; it < iters; ++it) {
         const bool stale = cold && it == 0;
+        const bool last = it + 1 == iters;
         for (int rb = w; rb < x.n_pad / kWave; rb += kPairWaves)
             wave_rows<kLds>(x, y, b, rb * kWave, two_c, eps_ln2, c_same, red[w], stale, recs[1],
-                            recs[0]);
+                            recs[0], sqs[0], pots[0], last);
         __syncthreads();   // f and the X-side biases are complete
         const double cn = it + 1 < iters ? c_same : c_next_last;
         for (int rb = w; rb < y.n_pad / kWave; rb += kPairWaves)
             wave_rows<kLds>(y, x, b, rb * kWave, two_c, eps_ln2, cn, red[w], stale, recs[0],
-                            recs[1]);
+                            recs[1], sqs[1], pots[1], last);
         __syncthreads();   // g and the Y-side biases are complete
     }
 }
