@@ -778,18 +778,16 @@ __device__ __forceinline__ void wave_rows(const Side3 &q, const Side3 &k, int b,
                                           float two_c, double eps_ln2, double c_next,
                                           float2 *red, bool stale, const uint4 *k_lds,
                                           uint4 *q_lds, const float *q_sq, float *q_pot,
-                                          bool last)
+                                          bool last, const bf16x8 (&A)[kGroups],
+                                          const uint16_t *next_rows, bf16x8 (&An)[kGroups])
 {
     const int lane = lane_id();
     const int kq = lane >> 4, c16 = lane & 15;
     const int lane_off = c16 * kRec + 8 * kq;
     const float4 *qrow = q.pts + (size_t)b * q.n_pad + row0;
-    const uint16_t *qrec_rows = q.qrec + ((size_t)b * q.n_pad + row0) * kRec;
     const uint16_t *kb = k.krec + (size_t)b * k.n_pad * kRec;
     const int n_tiles = k.n_pad / kTile;
-    bf16x8 A[kGroups];
     f32x4 Cn[kGroups], S[kGroups];
-    load_rows(A, qrec_rows, lane_off);
     const int row = row0 + lane;
     float4 prow = make_float4(0.f, 0.f, 0.f, 0.f);
     float lw = 0.f;
@@ -840,6 +838,11 @@ __device__ __forceinline__ void wave_rows(const Side3 &q, const Side3 &k, int b,
         M = red[lane].x;
         Sf = red[lane].y;
     }
+    // the next block's query operands (records fixed for the stage: no
+    // dependency on this pass) load now, while the rows finish and the
+    // work-group meets at the barrier
+    if (next_rows)
+        load_rows(An, next_rows, lane_off);
     if (row < q.n) {
         if constexpr (kLds) {
             // the arithmetic of finish_row, the state kept in LDS; the global
@@ -899,17 +902,48 @@ __global__ __launch_bounds__(kPairWaves *kWave) void lse3p_kernel(Side3 x, Side3
         }
         __syncthreads();
     }
+    // Query operands of a wave's row blocks: the records are fixed for the
+    // stage, so each block's are loaded during the finish of the block before
+    // (pre: the records An holds)
+    const int lane = lane_id();
+    const int lane_off = (lane & 15) * kRec + 8 * (lane >> 4);
+    const int nbx = x.n_pad / kWave, nby = y.n_pad / kWave;
+    auto rec_of = [&](const Side3 &s, int rb) {
+        return s.qrec + ((size_t)b * s.n_pad + (size_t)rb * kWave) * kRec;
+    };
+    bf16x8 An[kGroups];
+    const uint16_t *pre = nullptr;
     for (int it = 0; it < iters; ++it) {
         const bool stale = cold && it == 0;
         const bool last = it + 1 == iters;
-        for (int rb = w; rb < x.n_pad / kWave; rb += kPairWaves)
+        for (int rb = w; rb < nbx; rb += kPairWaves) {
+            const uint16_t *need = rec_of(x, rb);
+            if (pre != need)
+                load_rows(An, need, lane_off);
+            bf16x8 A[kGroups];
+#pragma unroll
+            for (int g = 0; g < kGroups; ++g)
+                A[g] = An[g];
+            pre = rb + kPairWaves < nbx ? rec_of(x, rb + kPairWaves)
+                                        : (w < nby ? rec_of(y, w) : nullptr);
             wave_rows<kLds>(x, y, b, rb * kWave, two_c, eps_ln2, c_same, red[w], stale, recs[1],
-                            recs[0], sqs[0], pots[0], last);
+                            recs[0], sqs[0], pots[0], last, A, pre, An);
+        }
         __syncthreads();   // f and the X-side biases are complete
         const double cn = it + 1 < iters ? c_same : c_next_last;
-        for (int rb = w; rb < y.n_pad / kWave; rb += kPairWaves)
+        for (int rb = w; rb < nby; rb += kPairWaves) {
+            const uint16_t *need = rec_of(y, rb);
+            if (pre != need)
+                load_rows(An, need, lane_off);
+            bf16x8 A[kGroups];
+#pragma unroll
+            for (int g = 0; g < kGroups; ++g)
+                A[g] = An[g];
+            pre = rb + kPairWaves < nby ? rec_of(y, rb + kPairWaves)
+                                        : (w < nbx && !last ? rec_of(x, w) : nullptr);
             wave_rows<kLds>(y, x, b, rb * kWave, two_c, eps_ln2, cn, red[w], stale, recs[0],
-                            recs[1], sqs[1], pots[1], last);
+                            recs[1], sqs[1], pots[1], last, A, pre, An);
+        }
         __syncthreads();   // g and the Y-side biases are complete
     }
 }
