@@ -778,7 +778,8 @@ __device__ __forceinline__ void wave_rows(const Side3 &q, const Side3 &k, int b,
                                           float two_c, double eps_ln2, double c_next,
                                           float2 *red, bool stale, const uint4 *k_lds,
                                           uint4 *q_lds, const float *q_sq, float *q_pot,
-                                          bool last, const bf16x8 (&A)[kGroups],
+                                          const float *q_lw, bool last,
+                                          const bf16x8 (&A)[kGroups],
                                           const uint16_t *next_rows, bf16x8 (&An)[kGroups])
 {
     const int lane = lane_id();
@@ -805,8 +806,7 @@ __device__ __forceinline__ void wave_rows(const Side3 &q, const Side3 &k, int b,
             S[g] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
         __builtin_amdgcn_wave_barrier();
-        if (row < q.n)
-            lw = q.l2w[(size_t)b * q.n + row];
+        lw = q_lw[row];
     } else {
         load_shifts(Cn, S, qrow, q.pot + (size_t)b * q.n, q.n, row0, kq, 0.5f * two_c,
                     reinterpret_cast<float *>(red));
@@ -878,8 +878,10 @@ __global__ __launch_bounds__(kPairWaves *kWave) void lse3p_kernel(Side3 x, Side3
 {
     __shared__ __align__(16) float2 red[kPairWaves][kWave];
     __shared__ uint4 recs[2][kLds ? kLdsMaxPoints * kRec / 8 : 1];   // unused without kLds
-    // with kLds also every point's squared norm and potential, both sides
+    // with kLds also every point's squared norm, potential and log2 weight, both
+    // sides (the stage's state)
     __shared__ float sqs[2][kLds ? kLdsMaxPoints : 1], pots[2][kLds ? kLdsMaxPoints : 1];
+    __shared__ float lws[2][kLds ? kLdsMaxPoints : 1];   // log2 weights
     const int b = blockIdx.x;
     const int w = wave_id_uniform();
     const double c_same = 0.5 * (double)two_c;
@@ -898,6 +900,7 @@ __global__ __launch_bounds__(kPairWaves *kWave) void lse3p_kernel(Side3 x, Side3
                 const float4 p = pts[i];
                 sqs[sd][i] = sq3(p.x, p.y, p.z);
                 pots[sd][i] = i < side[sd]->n ? pot[i] : 0.f;
+                lws[sd][i] = i < side[sd]->n ? side[sd]->l2w[(size_t)b * side[sd]->n + i] : 0.f;
             }
         }
         __syncthreads();
@@ -927,7 +930,7 @@ __global__ __launch_bounds__(kPairWaves *kWave) void lse3p_kernel(Side3 x, Side3
             pre = rb + kPairWaves < nbx ? rec_of(x, rb + kPairWaves)
                                         : (w < nby ? rec_of(y, w) : nullptr);
             wave_rows<kLds>(x, y, b, rb * kWave, two_c, eps_ln2, c_same, red[w], stale, recs[1],
-                            recs[0], sqs[0], pots[0], last, A, pre, An);
+                            recs[0], sqs[0], pots[0], lws[0], last, A, pre, An);
         }
         __syncthreads();   // f and the X-side biases are complete
         const double cn = it + 1 < iters ? c_same : c_next_last;
@@ -942,7 +945,7 @@ __global__ __launch_bounds__(kPairWaves *kWave) void lse3p_kernel(Side3 x, Side3
             pre = rb + kPairWaves < nby ? rec_of(y, rb + kPairWaves)
                                         : (w < nbx && !last ? rec_of(x, w) : nullptr);
             wave_rows<kLds>(y, x, b, rb * kWave, two_c, eps_ln2, cn, red[w], stale, recs[0],
-                            recs[1], sqs[1], pots[1], last, A, pre, An);
+                            recs[1], sqs[1], pots[1], lws[1], last, A, pre, An);
         }
         __syncthreads();   // g and the Y-side biases are complete
     }
