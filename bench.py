@@ -469,6 +469,23 @@ def main():
         t_cn = timed(normalise, 2)
         line["phases_ms"]["transposed_plan"] = t_tr * 1e3
         line["phases_ms"]["coo_sinkhorn_normalisation_10_rounds"] = t_cn * 1e3
+        # the cosine cost's own kernels: both clouds to unit length, dL/dY from the
+        # transposed plan, and dL/dX, dL/dY back through the normalisation (the
+        # potentials and plans of the normalised clouds are the kernels above)
+        lg_ws = torch.empty(sk.workspace_bytes(sk.SK_OP_LOSS_GRAD, B, m, n, d, dt),
+                            dtype=torch.uint8, device=dev)
+        ly, dY = torch.empty(B, device=dev), torch.empty(B, m, d, device=dev)
+        gX = torch.ones(B, n, d, device=dev)
+
+        def cosine_kernels():
+            Xh, nx = sk.normalize(X)
+            Yh, ny = sk.normalize(Y)
+            sk.loss_grad(Y, X, *tr, workspace=lg_ws, out=(ly, dY))
+            return sk.normalize_backward(Xh, nx, gX), sk.normalize_backward(Yh, ny, dY)
+
+        cosine_kernels()
+        t_cos = timed(cosine_kernels, 2)
+        line["phases_ms"]["cosine_normalise_dY_and_backward"] = t_cos * 1e3
     if not sparse:
         # dense gradient and barycentric projection of both clouds at the final eps
         # (one streamed pass per side); reported beside the step, not inside it

@@ -426,9 +426,9 @@ __global__ __launch_bounds__(kEmitWaves *kWave) void emit_staged(
     const float *gb = p.g + (size_t)b * p.m;
     const double *lbb = p.lb + (size_t)b * p.m;
     const double t = thr[b];
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     RowCtx<DP> r[kRowsPerWave];
-    int64_t pos[kRowsPerWave], end[kRowsPerWave];
+    int64_t pos[kRowsPerWave];   // the row's next entry
+    int rem[kRowsPerWave];       // and how many are still to come (wave-uniform)
     double loss[kRowsPerWave];
     float gr[kRowsPerWave][DP];
 #pragma unroll
@@ -436,7 +436,7 @@ __global__ __launch_bounds__(kEmitWaves *kWave) void emit_staged(
         const int i = min(i0 + q, p.n - 1);   // rows past n are loaded but never emitted
         load_row<T, DP>(r[q], p, b, i);
         pos[q] = row_off[(size_t)b * p.n + i];
-        end[q] = i0 + q < p.n ? pos[q] + row_cnt[(size_t)b * p.n + i] : pos[q];
+        rem[q] = i0 + q < p.n ? row_cnt[(size_t)b * p.n + i] : 0;
         loss[q] = 0.0;
 #pragma unroll
         for (int c = 0; c < DP; ++c)
@@ -457,35 +457,46 @@ __global__ __launch_bounds__(kEmitWaves *kWave) void emit_staged(
         __syncthreads();
 #pragma unroll
         for (int q = 0; q < kRowsPerWave; ++q) {
-            for (int j0 = 0; j0 < kc && pos[q] < end[q]; j0 += kWave) {   // wave-uniform
+            // wave-uniform bases at the row's next entry; a lane stores at its
+            // 32-bit rank among the step's kept entries
+            int32_t *rq = rows + pos[q];
+            int32_t *cq = cols + pos[q];
+            float *vq = vals + pos[q];
+            int left = rem[q];
+            for (int j0 = 0; j0 < kc && left > 0; j0 += kWave) {
                 const int j = j0 + lane;
-                bool keep = false;
-                double lp = 0.0, C = 0.0;
-                double diff[LG ? DP : 1];
-                if (j < kc) {
-                    KeyVals<DP> kv;
+                const int jc = min(j, kc - 1);   // lanes past the chunk evaluate its last column
+                KeyVals<DP> kv;
 #pragma unroll
-                    for (int k = 0; k < DP; ++k)
-                        kv.y[k] = ys[k][j];
-                    kv.g = gs[j];
-                    lp = log_plan_kv<DP>(r[q], kv, lbs[j], p.inv_eps, p.d, &C,
-                                         LG ? diff : nullptr);
-                    keep = lp >= t;
+                for (int k = 0; k < DP; ++k)
+                    kv.y[k] = ys[k][jc];
+                kv.g = gs[jc];
+                double C;
+                double diff[LG ? DP : 1];
+                const double lp =
+                    log_plan_kv<DP>(r[q], kv, lbs[jc], p.inv_eps, p.d, &C, LG ? diff : nullptr);
+                const bool keep = j < kc && lp >= t;
+                const uint64_t mask = __builtin_amdgcn_ballot_w64(keep);
+                // kept lanes below this one
+                const uint32_t idx = __builtin_amdgcn_mbcnt_hi(
+                    (uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+                if (keep && idx < (uint32_t)left) {   // always: count and emit agree
+                    const float P = ex2((float)(lp * 1.4426950408889634));
+                    const uint32_t at = idx * 4u;   // 32-bit byte offset from the bases
+                    *(int32_t *)((char *)rq + at) = i0 + q;
+                    *(int32_t *)((char *)cq + at) = c0 + j;
+                    *(float *)((char *)vq + at) = P;
+                    if constexpr (LG)
+                        loss_term<DP>(diff, C, p.d, P, loss[q], gr[q]);
                 }
-                const uint64_t mask = __ballot(keep);
-                if (keep) {
-                    const int64_t k = pos[q] + __popcll(mask & below);
-                    if (k < end[q]) {   // always true: count and emit make identical decisions
-                        const float P = ex2((float)(lp * 1.4426950408889634));
-                        rows[k] = i0 + q;
-                        cols[k] = c0 + j;
-                        vals[k] = P;
-                        if constexpr (LG)
-                            loss_term<DP>(diff, C, p.d, P, loss[q], gr[q]);
-                    }
-                }
-                pos[q] += __popcll(mask);
+                const int nk = __popcll(mask);
+                rq += nk;
+                cq += nk;
+                vq += nk;
+                left -= nk;
             }
+            pos[q] += rem[q] - left;
+            rem[q] = left;
         }
     }
     if (LG) {
