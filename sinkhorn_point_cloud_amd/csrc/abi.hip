@@ -118,7 +118,7 @@ struct CooWs {
     double *row_max, *pair_thr;
     int32_t *row_count;
     int64_t *row_off, *pair_tot;
-    KeyD *kd = nullptr;   // d = 3: fp64 keys of the max and count passes
+    KeyB *kb = nullptr;   // d = 3: fp64 keys of the max, count and emit passes
 };
 
 CooWs carve_coo(Carve &c, int B, int n, int m, int d)
@@ -132,7 +132,7 @@ CooWs carve_coo(Carve &c, int B, int n, int m, int d)
     w.row_off = c.take<int64_t>((size_t)B * n);
     w.pair_tot = c.take<int64_t>(B);
     if (d == 3)
-        w.kd = c.take<KeyD>((size_t)B * m);
+        w.kb = c.take<KeyB>((size_t)B * m);
     return w;
 }
 
@@ -596,10 +596,11 @@ int sinkhorn_plan_coo(const void *X, const void *Y, int dtype, const float *a, c
     hipStream_t st = (hipStream_t)stream;
     Carve c{(char *)ws};
     CooWs w = carve_coo(c, B, n, m, d);
-    PlanArgs p{X, Y, dtype, d, B, n, m, f, g, w.la, w.lb, 1.0 / (double)eps, w.kd};
+    PlanArgs p{X, Y, dtype, d, B, n, m, f, g, w.la, w.lb, 1.0 / (double)eps};
+    p.kb = w.kb;
     hipError_t e;
     if ((e = launch_log_weights(a, B, n, w.la, st)) || (e = launch_log_weights(b, B, m, w.lb, st)) ||
-        (w.kd && (e = launch_keys_d3(Y, dtype, g, B, m, w.kd, st))))
+        (w.kb && (e = launch_keys_plan_d3(Y, dtype, g, w.lb, p.inv_eps, B, m, w.kb, st))))
         return hip_fail(e, "log weights");
     if ((e = launch_plan_max(p, w.row_max, w.pair_thr, log((double)rel_threshold), st)))
         return hip_fail(e, "plan max");
@@ -651,10 +652,11 @@ int sinkhorn_plan_coo_async(const void *X, const void *Y, int dtype, const float
     hipStream_t st = (hipStream_t)stream;
     Carve c{(char *)ws};
     CooWs w = carve_coo(c, B, n, m, d);
-    PlanArgs p{X, Y, dtype, d, B, n, m, f, g, w.la, w.lb, 1.0 / (double)eps, w.kd};
+    PlanArgs p{X, Y, dtype, d, B, n, m, f, g, w.la, w.lb, 1.0 / (double)eps};
+    p.kb = w.kb;
     hipError_t e;
     if ((e = launch_log_weights(a, B, n, w.la, st)) || (e = launch_log_weights(b, B, m, w.lb, st)) ||
-        (w.kd && (e = launch_keys_d3(Y, dtype, g, B, m, w.kd, st))))
+        (w.kb && (e = launch_keys_plan_d3(Y, dtype, g, w.lb, p.inv_eps, B, m, w.kb, st))))
         return hip_fail(e, "log weights");
     if ((e = launch_plan_max(p, w.row_max, w.pair_thr, log((double)rel_threshold), st)) ||
         (e = launch_plan_count(p, w.pair_thr, w.row_count, st)) ||

@@ -192,6 +192,15 @@ struct alignas(32) KeyD {
     double g;
 };
 
+// One key of the sparse plan's passes for d = 3 as fp64: point components and
+// B_j = (g_j - ||y_j||^2)/eps + log b_j, 32 bytes.  With the row's
+// A_i = (f_i - ||x_i||^2)/eps + log a_i they give
+//     log P_ij = (2/eps) x_i . y_j + A_i + B_j.
+struct alignas(32) KeyB {
+    double y[3];
+    double B;
+};
+
 // Plan evaluation passes, shared by the cost, max, count and emit steps.
 struct PlanArgs {
     const void *X, *Y;
@@ -200,10 +209,14 @@ struct PlanArgs {
     const double *la, *lb;   // natural log of the weights, [B][n] and [B][m] (-inf for 0)
     double inv_eps;
     const KeyD *kd = nullptr;   // d = 3: the keys (Y, g) as KeyD [B][m], or NULL
+    const KeyB *kb = nullptr;   // d = 3 sparse plan (max, count, emit): the keys as KeyB
 };
 // KeyD records of the keys (Y [B][m][3], g [B][m]) of a d = 3 pass.
 hipError_t launch_keys_d3(const void *Y, int dtype, const float *g, int B, int m, KeyD *out,
                           hipStream_t st);
+// KeyB records of the keys (Y [B][m][3], g [B][m], lb [B][m]) at 1/eps = inv_eps.
+hipError_t launch_keys_plan_d3(const void *Y, int dtype, const float *g, const double *lb,
+                               double inv_eps, int B, int m, KeyB *out, hipStream_t st);
 // log of the weights in fp64 (w == NULL: uniform 1/count)
 hipError_t launch_log_weights(const float *w, int B, int count, double *out, hipStream_t st);
 hipError_t launch_cost(const PlanArgs &p, double *row_part, float *cost, hipStream_t st);

@@ -81,6 +81,18 @@ __global__ __launch_bounds__(kTileWaves *kWave) void tile_pass(
     const float *gb = p.g + (size_t)b * p.m;
     const double *lbb = p.lb + (size_t)b * p.m;
     const KeyD *kdb = p.kd ? p.kd + (size_t)b * p.m : nullptr;
+    // the sparse plan's max and count passes over staged d = 3 keys take the
+    // expanded form of log P (KeyB records, the row's A_i)
+    constexpr bool kPB = (MODE == 1 || MODE == 2) && KD;
+    const KeyB *kbb = kPB ? p.kb + (size_t)b * p.m : nullptr;
+    double xd[3] = {0.0, 0.0, 0.0}, A = 0.0;
+    if constexpr (kPB) {
+#pragma unroll
+        for (int k = 0; k < 3; ++k)
+            xd[k] = (double)r.x[k];
+        A = side_term_d3(xd[0], xd[1], xd[2], r.f, r.la, p.inv_eps);
+    }
+    const double two_inv_eps = 2.0 * p.inv_eps;
     const double t = MODE == 2 ? thr[b] : 0.0;
     double acc = MODE == 1 ? -INFINITY : 0.0;
     int cnt = 0;
@@ -98,12 +110,18 @@ __global__ __launch_bounds__(kTileWaves *kWave) void tile_pass(
     // differences
     constexpr bool kRegs = DP <= kKeyRegDims;
     constexpr bool kDiff = kRegs && MODE == 3 && KC == DP;
-    __shared__ KeyD kst[KD ? kKeyStage : 1];
-    __shared__ double lbst[KD ? kKeyStage : 1];
+    __shared__ KeyD kst[KD && !kPB ? kKeyStage : 1];
+    __shared__ double lbst[KD && !kPB ? kKeyStage : 1];
+    __shared__ KeyB kbst[kPB ? kKeyStage : 1];
     auto visit = [&](int j, int js) {
         double C, lp;
         double diff[kDiff ? DP : 1];
-        if constexpr (KD) {
+        if constexpr (kPB) {
+            // staged in LDS: every lane of the wave reads the same record
+            const KeyB kr = kbst[js];
+            const double y[3] = {kr.y[0], kr.y[1], kr.y[2]};
+            lp = log_plan_b3(xd, A, y, kr.B, two_inv_eps);
+        } else if constexpr (KD) {
             // staged in LDS: every lane of the wave reads the same record
             const KeyD kr = kst[js];
             KeyVals<DP> kv;
@@ -149,8 +167,12 @@ __global__ __launch_bounds__(kTileWaves *kWave) void tile_pass(
             const int kc = min(kKeyStage, p.m - c0);
             __syncthreads();   // the previous stage is no longer read
             for (int e = threadIdx.x; e < kc; e += kTileWaves * kWave) {
-                kst[e] = kdb[c0 + e];
-                lbst[e] = lbb[c0 + e];
+                if constexpr (kPB) {
+                    kbst[e] = kbb[c0 + e];
+                } else {
+                    kst[e] = kdb[c0 + e];
+                    lbst[e] = lbb[c0 + e];
+                }
             }
             __syncthreads();
             int js = w;
@@ -416,17 +438,23 @@ __global__ __launch_bounds__(kEmitWaves *kWave) void emit_staged(
         return;   // the plan does not fit: nothing is written
     static_assert(DP <= 4, "staged emit holds at most 4 components per column");
     constexpr int kRowsPerWave = kEmitRows / kEmitWaves;
+    // d = 3: the expanded log P from KeyB records (the count pass's values);
+    // gs then holds B_j and lbs is not used
+    constexpr bool kPB = DP == 3;
     __shared__ double ys[DP][kEmitChunk];
     __shared__ double gs[kEmitChunk];
-    __shared__ double lbs[kEmitChunk];
+    __shared__ double lbs[kPB ? 1 : kEmitChunk];
     const int b = blockIdx.y;
     const int wave = wave_id_uniform(), lane = lane_id();
     const int i0 = blockIdx.x * kEmitRows + wave * kRowsPerWave;
     const T *Yb = (const T *)p.Y + (size_t)b * p.m * p.d;
     const float *gb = p.g + (size_t)b * p.m;
     const double *lbb = p.lb + (size_t)b * p.m;
+    const KeyB *kbb = kPB ? p.kb + (size_t)b * p.m : nullptr;
     const double t = thr[b];
+    const double two_inv_eps = 2.0 * p.inv_eps;
     RowCtx<DP> r[kRowsPerWave];
+    double xd[kRowsPerWave][3], A[kRowsPerWave];   // kPB: the rows as fp64 and their A_i
     int64_t pos[kRowsPerWave];   // the row's next entry
     int rem[kRowsPerWave];       // and how many are still to come (wave-uniform)
     double loss[kRowsPerWave];
@@ -435,6 +463,12 @@ __global__ __launch_bounds__(kEmitWaves *kWave) void emit_staged(
     for (int q = 0; q < kRowsPerWave; ++q) {
         const int i = min(i0 + q, p.n - 1);   // rows past n are loaded but never emitted
         load_row<T, DP>(r[q], p, b, i);
+        if constexpr (kPB) {
+#pragma unroll
+            for (int k = 0; k < 3; ++k)
+                xd[q][k] = (double)r[q].x[k];
+            A[q] = side_term_d3(xd[q][0], xd[q][1], xd[q][2], r[q].f, r[q].la, p.inv_eps);
+        }
         pos[q] = row_off[(size_t)b * p.n + i];
         rem[q] = i0 + q < p.n ? row_cnt[(size_t)b * p.n + i] : 0;
         loss[q] = 0.0;
@@ -446,13 +480,21 @@ __global__ __launch_bounds__(kEmitWaves *kWave) void emit_staged(
         const int kc = min(kEmitChunk, p.m - c0);
         __syncthreads();   // the previous chunk is no longer read
         for (int j = threadIdx.x; j < kc; j += kEmitWaves * kWave) {
-            KeyVals<DP> kv;
-            load_key<T, DP, false>(kv, p, Yb, gb, nullptr, c0 + j);
+            if constexpr (kPB) {
+                const KeyB kr = kbb[c0 + j];
 #pragma unroll
-            for (int k = 0; k < DP; ++k)
-                ys[k][j] = kv.y[k];
-            gs[j] = kv.g;
-            lbs[j] = lbb[c0 + j];
+                for (int k = 0; k < 3; ++k)
+                    ys[k][j] = kr.y[k];
+                gs[j] = kr.B;
+            } else {
+                KeyVals<DP> kv;
+                load_key<T, DP, false>(kv, p, Yb, gb, nullptr, c0 + j);
+#pragma unroll
+                for (int k = 0; k < DP; ++k)
+                    ys[k][j] = kv.y[k];
+                gs[j] = kv.g;
+                lbs[j] = lbb[c0 + j];
+            }
         }
         __syncthreads();
 #pragma unroll
@@ -471,10 +513,22 @@ __global__ __launch_bounds__(kEmitWaves *kWave) void emit_staged(
                 for (int k = 0; k < DP; ++k)
                     kv.y[k] = ys[k][jc];
                 kv.g = gs[jc];
-                double C;
+                double C = 0.0, lp;
                 double diff[LG ? DP : 1];
-                const double lp =
-                    log_plan_kv<DP>(r[q], kv, lbs[jc], p.inv_eps, p.d, &C, LG ? diff : nullptr);
+                if constexpr (kPB) {
+                    const double y[3] = {kv.y[0], kv.y[1], kv.y[2]};
+                    lp = log_plan_b3(xd[q], A[q], y, kv.g, two_inv_eps);
+                    if constexpr (LG) {   // the loss term's differences and C as log_plan_kv
+#pragma unroll
+                        for (int k = 0; k < 3; ++k) {
+                            diff[k] = xd[q][k] - y[k];
+                            C = fma(diff[k], diff[k], C);
+                        }
+                    }
+                } else {
+                    lp = log_plan_kv<DP>(r[q], kv, lbs[jc], p.inv_eps, p.d, &C,
+                                         LG ? diff : nullptr);
+                }
                 const bool keep = j < kc && lp >= t;
                 const uint64_t mask = __builtin_amdgcn_ballot_w64(keep);
                 // kept lanes below this one
@@ -537,6 +591,22 @@ __global__ void keys_d3_kernel(const T *__restrict__ Y, const float *__restrict_
     out[k] = r;
 }
 
+template <typename T>
+__global__ void keys_plan_d3_kernel(const T *__restrict__ Y, const float *__restrict__ g,
+                                    const double *__restrict__ lb, double inv_eps, size_t count,
+                                    KeyB *__restrict__ out)
+{
+    const size_t k = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (k >= count)
+        return;
+    KeyB r;
+#pragma unroll
+    for (int c = 0; c < 3; ++c)
+        r.y[c] = (double)Elem<T>::get(Y, 3 * k + c);
+    r.B = side_term_d3(r.y[0], r.y[1], r.y[2], (double)g[k], lb[k], inv_eps);
+    out[k] = r;
+}
+
 template <typename F>
 void with_dp(int d, F fn)
 {
@@ -568,7 +638,7 @@ void tile_dispatch(const PlanArgs &p, const double *thr, double *outd, int32_t *
             }
         };
         if constexpr (DP == 3) {
-            if (p.kd) {
+            if (MODE == 1 || MODE == 2 ? p.kb != nullptr : p.kd != nullptr) {
                 go.template operator()<true>();
                 return;
             }
@@ -590,6 +660,20 @@ hipError_t launch_keys_d3(const void *Y, int dtype, const float *g, int B, int m
     else
         hipLaunchKernelGGL(keys_d3_kernel<float>, grid, dim3(256), 0, st, (const float *)Y, g,
                            count, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_keys_plan_d3(const void *Y, int dtype, const float *g, const double *lb,
+                               double inv_eps, int B, int m, KeyB *out, hipStream_t st)
+{
+    const size_t count = (size_t)B * m;
+    const dim3 grid((unsigned)((count + 255) / 256));
+    if (dtype == 1)
+        hipLaunchKernelGGL(keys_plan_d3_kernel<uint16_t>, grid, dim3(256), 0, st,
+                           (const uint16_t *)Y, g, lb, inv_eps, count, out);
+    else
+        hipLaunchKernelGGL(keys_plan_d3_kernel<float>, grid, dim3(256), 0, st, (const float *)Y,
+                           g, lb, inv_eps, count, out);
     return hipGetLastError();
 }
 
@@ -619,6 +703,8 @@ hipError_t launch_row_sums(const double *row_part, int B, int n, float *out, hip
 hipError_t launch_plan_max(const PlanArgs &p, double *row_max, double *pair_thr,
                            double log_rel_thr, hipStream_t st)
 {
+    if (p.d == 3 && !p.kb)
+        return hipErrorInvalidValue;   // d = 3 plans take KeyB records in every pass
     tile_dispatch<1>(p, nullptr, row_max, nullptr, nullptr, nullptr, st);
     hipLaunchKernelGGL(pair_reduce<1>, dim3(p.B), dim3(256), 0, st, (const double *)row_max,
                        p.n, (float *)nullptr, pair_thr, log_rel_thr, (const int64_t *)nullptr,
@@ -629,6 +715,8 @@ hipError_t launch_plan_max(const PlanArgs &p, double *row_max, double *pair_thr,
 hipError_t launch_plan_count(const PlanArgs &p, const double *pair_thr, int32_t *row_count,
                              hipStream_t st)
 {
+    if (p.d == 3 && !p.kb)
+        return hipErrorInvalidValue;
     tile_dispatch<2>(p, pair_thr, nullptr, row_count, nullptr, nullptr, st);
     return hipGetLastError();
 }
@@ -651,6 +739,8 @@ hipError_t launch_plan_emit(const PlanArgs &p, const double *pair_thr, const int
 {
     const bool lg = loss || dX;
     double *rl = loss ? row_loss : nullptr;
+    if (p.d == 3 && !p.kb)
+        return hipErrorInvalidValue;
     if (p.d <= 4) {
         const dim3 grid(ceil_div(p.n, kEmitRows), p.B), block(kEmitWaves * kWave);
         auto go = [&]<int DP, bool LG>() {

@@ -11,7 +11,9 @@
 // whose lanes share the key reads them whole (staged in LDS, or with scalar
 // loads) and spends no vector instruction on conversions; otherwise they are
 // converted where they are read.
-// The values, and so every result, are the same either way.
+// The values, and so every result, are the same either way.  The sparse plan's
+// passes for d = 3 (max, count, emit) instead take the expanded form of log P
+// from KeyB records (log_plan_b3 below), the same in all three.
 #pragma once
 #include "common.h"
 
@@ -108,6 +110,31 @@ __device__ __forceinline__ double log_plan(const RowCtx<DP> &r, const PlanArgs &
     }
     *C = s;
     return fma((r.f + (double)gb[j]) - s, p.inv_eps, r.la + lbj);
+}
+
+// The sparse plan's log P for d = 3 (max, count and emit passes), in the
+// expanded form
+//     log P_ij = (2/eps) x_i . y_j + A_i + B_j,
+//     A_i = (f_i - ||x_i||^2)/eps + log a_i,   B_j = (g_j - ||y_j||^2)/eps + log b_j,
+// five fp64 operations per entry instead of the ten of log_plan_kv.  Both
+// sides' constant terms come from side_term_d3 and the three products of the
+// dot product are exact in fp64 and summed with fma in component order, so the
+// value is the same with the roles of X and Y exchanged (the plan of (Y, X) is
+// exactly the transpose).  Its rounding differs from log_plan_kv's by a few
+// units in the last place of the larger terms, which only moves threshold
+// decisions of entries at the threshold to within that.
+__device__ __forceinline__ double side_term_d3(double v0, double v1, double v2, double pot,
+                                               double lw, double inv_eps)
+{
+    const double sq = fma(v0, v0, fma(v1, v1, v2 * v2));
+    return fma(pot - sq, inv_eps, lw);
+}
+
+__device__ __forceinline__ double log_plan_b3(const double (&x)[3], double A,
+                                              const double (&y)[3], double B, double two_inv_eps)
+{
+    const double dot = fma(x[0], y[0], fma(x[1], y[1], x[2] * y[2]));
+    return fma(dot, two_inv_eps, A + B);
 }
 
 // Points up to this width keep a key's values (and differences) in registers;
