@@ -157,12 +157,31 @@ __global__ __launch_bounds__(kSegsPerGroup *kWave) void scale_pass(
     if (isfinite(Msh)) {   // uniform over the segment
         double Ssh = 0.0;
         int64_t q = lo + sl;
-        for (; q + kSegLanes < hi; q += 2 * kSegLanes) {
+        // four entries per lane and step: their indices and values, then their
+        // partners' scalings, are all in flight before the first is used
+        for (; q + 3 * kSegLanes < hi; q += 4 * kSegLanes) {
+            int pp[4];
+            float lq[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                pp[u] = partner[q + u * kSegLanes];
+                lq[u] = lv[q + u * kSegLanes];
+            }
+            double z[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                z[u] = pp[u] < 0 || pp[u] >= other_count ? -INFINITY : (double)lq[u] + ob[pp[u]];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                Ssh += (double)expf((float)(z[u] - Msh));
+        }
+        if (q + kSegLanes < hi) {   // two more, loaded together
             const double z0 = term(q), z1 = term(q + kSegLanes);
             Ssh += (double)expf((float)(z0 - Msh));
             Ssh += (double)expf((float)(z1 - Msh));
+            q += 2 * kSegLanes;
         }
-        if (q < hi)
+        for (; q < hi; q += kSegLanes)
             Ssh += (double)expf((float)(term(q) - Msh));
         Ssh = seg_sum(Ssh);
         if (Ssh >= 0x1p-40 && Ssh <= 0x1p60) {
