@@ -94,11 +94,20 @@ __global__ void zero_u64(uint64_t *__restrict__ p, int count)
         p[i] = 0;
 }
 
-__global__ void log_kernel(const float *__restrict__ vals, int64_t nnz, float *__restrict__ lv)
+// lv = log vals, four entries per thread: with 16-byte accesses when both
+// arrays are 16-byte aligned (vec), the last nnz % 4 entries one at a time
+__global__ void log_kernel(const float *__restrict__ vals, int64_t nnz, float *__restrict__ lv,
+                           bool vec)
 {
-    const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (k < nnz)
-        lv[k] = logf(vals[k]);
+    const int64_t k = 4 * ((int64_t)blockIdx.x * blockDim.x + threadIdx.x);
+    if (vec && k + 4 <= nnz) {
+        const float4 v = *reinterpret_cast<const float4 *>(vals + k);
+        *reinterpret_cast<float4 *>(lv + k) = make_float4(logf(v.x), logf(v.y), logf(v.z),
+                                                          logf(v.w));
+    } else {
+        for (int64_t q = k; q < k + 4 && q < nnz; ++q)
+            lv[q] = logf(vals[q]);
+    }
 }
 
 // One scaling update per segment (a row of the plan or a row of the transpose,
@@ -229,14 +238,30 @@ __global__ void apply_kernel(const int32_t *__restrict__ ri, const int32_t *__re
 {
     const int b = blockIdx.y;
     const int64_t lo = offs[b], hi = offs[b + 1];
-    for (int64_t k = lo + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < hi;
-         k += (int64_t)gridDim.x * blockDim.x) {
-        const int i = ri[k], j = ci[k];
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const double *alb = al + (size_t)b * n, *beb = be + (size_t)b * m;
+    auto one = [&](int64_t k, int i, int j, float l) {
         if (i < 0 || i >= n || j < 0 || j >= m)
-            continue;
-        const double z = (double)lv[k] + al[(size_t)b * n + i] + be[(size_t)b * m + j];
-        vals[k] = expf((float)z);
+            return;
+        vals[k] = expf((float)((double)l + alb[i] + beb[j]));
+    };
+    int64_t k = lo + (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    // four entries per thread and step, their loads in flight together
+    for (; k + 3 * stride < hi; k += 4 * stride) {
+        int i[4], j[4];
+        float l[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            i[u] = ri[k + u * stride];
+            j[u] = ci[k + u * stride];
+            l[u] = lv[k + u * stride];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            one(k + u * stride, i[u], j[u], l[u]);
     }
+    for (; k < hi; k += stride)
+        one(k, ri[k], ci[k], lv[k]);
 }
 
 // |sum of the segment's values - weight| per row (of the plan or of the transpose)
@@ -308,11 +333,15 @@ hipError_t launch_coo_normalize(const int32_t *rows, const int32_t *cols, float 
                                 int64_t nnz, int iters, float *err, const float *a,
                                 const float *b, const CooNormWs &w, hipStream_t st)
 {
-    const unsigned nb = (unsigned)((nnz + 255) / 256);
+    const unsigned nb = (unsigned)((nnz + 1023) / 1024);   // log_kernel: 4 entries a thread
     if (nnz > 0) {
-        hipLaunchKernelGGL(log_kernel, dim3(nb), dim3(256), 0, st, (const float *)vals, nnz, w.lv);
+        auto a16 = [](const void *q1, const void *q2) {
+            return (((uintptr_t)q1 | (uintptr_t)q2) & 15) == 0;
+        };
+        hipLaunchKernelGGL(log_kernel, dim3(nb), dim3(256), 0, st, (const float *)vals, nnz, w.lv,
+                           a16(vals, w.lv));
         hipLaunchKernelGGL(log_kernel, dim3(nb), dim3(256), 0, st, (const float *)t_vals, nnz,
-                           w.lvt);
+                           w.lvt, a16(t_vals, w.lvt));
     }
     const size_t cn = (size_t)B * m;
     const size_t rn = (size_t)B * n;
