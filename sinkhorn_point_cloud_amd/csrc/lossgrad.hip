@@ -139,23 +139,32 @@ __global__ __launch_bounds__(kStagedWaves *kWave) void loss_grad_staged(
         }
         const int64_t k0 = begin[ri], k1 = end[ri];
         double loss = 0.0;
-        auto entry = [&](int64_t k) {
-            const int j = cols[k];
+        auto entry = [&](int j, float v) {
             if (j < 0 || j >= m)
                 return;
             float y[DP];
 #pragma unroll
             for (int c = 0; c < DP; ++c)
                 y[c] = ys[(size_t)c * m + j];
-            loss_term_xy<DP>(x, y, d, vals[k], loss, gr);
+            loss_term_xy<DP>(x, y, d, v, loss, gr);
         };
+        // a lane takes the row's entries lane, lane + 64, ... in order, four per
+        // step with their loads in flight together
         int64_t k = k0 + lane;
-        for (; k + kWave < k1; k += 2 * kWave) {
-            entry(k);
-            entry(k + kWave);
+        for (; k + 3 * kWave < k1; k += 4 * kWave) {
+            int j[4];
+            float v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                j[u] = cols[k + u * kWave];
+                v[u] = vals[k + u * kWave];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                entry(j[u], v[u]);
         }
-        if (k < k1)
-            entry(k);
+        for (; k < k1; k += kWave)
+            entry(cols[k], vals[k]);
         loss = wave_sum(loss);
         if (lane == 0)
             row_loss[ri] = loss;
