@@ -152,7 +152,7 @@ LossWs carve_loss(Carve &c, int B, int n)
 
 struct GradWs {
     double *la, *lb;
-    KeyD *kdx = nullptr, *kdy = nullptr;   // d = 3: fp64 keys of the two sides
+    KeyB *kbx = nullptr, *kby = nullptr;   // d = 3: fp64 keys of the two sides
     // matrix-core path (bf16, d = 32 or 64)
     float *xbias = nullptr, *ybias = nullptr, *xsq = nullptr, *ysq = nullptr;
     float *l2a = nullptr, *l2b = nullptr;
@@ -167,8 +167,8 @@ GradWs carve_grad(Carve &c, int B, int n, int m, int d, int dtype)
     w.la = c.take<double>((size_t)B * n);
     w.lb = c.take<double>((size_t)B * m);
     if (d == 3) {
-        w.kdx = c.take<KeyD>((size_t)B * n);
-        w.kdy = c.take<KeyD>((size_t)B * m);
+        w.kbx = c.take<KeyB>((size_t)B * n);
+        w.kby = c.take<KeyB>((size_t)B * m);
     }
     if (gradF_matrix_cores(dtype, d)) {
         const int np = round_up(n, kGradPad), mp = round_up(m, kGradPad);
@@ -235,8 +235,8 @@ HvpWs carve_hvp(Carve &c, int B, int n, int m, int d)
     w.rr = c.take<double>(B);
     w.rr0 = c.take<double>(B);
     if (d == 3) {
-        w.kdx = c.take<KeyD>(Bn);
-        w.kdy = c.take<KeyD>(Bm);
+        w.kbx = c.take<KeyB>(Bn);
+        w.kby = c.take<KeyB>(Bm);
     }
     return w;
 }
@@ -718,10 +718,14 @@ int sinkhorn_dense_grad(const void *X, const void *Y, int dtype, const float *a,
     const double inv_eps = 1.0 / (double)eps;
     const bool want_x = dX || TX, want_y = dY || TY;
     // log P is symmetric in (X, a, f) and (Y, b, g): the Y side is the same pass
-    PlanArgs px{X, Y, dtype, d, B, n, m, f, g, w.la, w.lb, inv_eps, w.kdy};
-    PlanArgs py{Y, X, dtype, d, B, m, n, g, f, w.lb, w.la, inv_eps, w.kdx};
-    if ((want_x && w.kdy && (e = launch_keys_d3(Y, dtype, g, B, m, w.kdy, st))) ||
-        (want_y && w.kdx && (e = launch_keys_d3(X, dtype, f, B, n, w.kdx, st))))
+    PlanArgs px{X, Y, dtype, d, B, n, m, f, g, w.la, w.lb, inv_eps};
+    PlanArgs py{Y, X, dtype, d, B, m, n, g, f, w.lb, w.la, inv_eps};
+    px.kb = w.kby;
+    py.kb = w.kbx;
+    if ((want_x && w.kby &&
+         (e = launch_keys_plan_d3(Y, dtype, g, w.lb, inv_eps, B, m, w.kby, st))) ||
+        (want_y && w.kbx &&
+         (e = launch_keys_plan_d3(X, dtype, f, w.la, inv_eps, B, n, w.kbx, st))))
         return hip_fail(e, "dense gradient: keys");
     const bool aligned = (uintptr_t)X % 16 == 0 && (uintptr_t)Y % 16 == 0;
     if (gradF_matrix_cores(dtype, d) && aligned) {
@@ -797,10 +801,12 @@ int sinkhorn_hvp(const void *X, const void *Y, int dtype, const float *a, const 
     if ((e = launch_log_weights(a, B, n, w.la, st)) || (e = launch_log_weights(b, B, m, w.lb, st)))
         return hip_fail(e, "log weights");
     const double inv_eps = 1.0 / (double)eps;
-    PlanArgs px{X, Y, dtype, d, B, n, m, f, g, w.la, w.lb, inv_eps, w.kdy};
-    PlanArgs py{Y, X, dtype, d, B, m, n, g, f, w.lb, w.la, inv_eps, w.kdx};
-    if (w.kdx && ((e = launch_keys_d3(Y, dtype, g, B, m, w.kdy, st)) ||
-                  (e = launch_keys_d3(X, dtype, f, B, n, w.kdx, st))))
+    PlanArgs px{X, Y, dtype, d, B, n, m, f, g, w.la, w.lb, inv_eps};
+    PlanArgs py{Y, X, dtype, d, B, m, n, g, f, w.lb, w.la, inv_eps};
+    px.kb = w.kby;
+    py.kb = w.kbx;
+    if (w.kbx && ((e = launch_keys_plan_d3(Y, dtype, g, w.lb, inv_eps, B, m, w.kby, st)) ||
+                  (e = launch_keys_plan_d3(X, dtype, f, w.la, inv_eps, B, n, w.kbx, st))))
         return hip_fail(e, "Hessian-vector product: keys");
     if ((e = launch_hvp(px, py, V, cg_iters, HV, cg_residual, w, st)))
         return hip_fail(e, "Hessian-vector product");

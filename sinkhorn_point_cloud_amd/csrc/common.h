@@ -192,7 +192,8 @@ struct alignas(32) KeyD {
     double g;
 };
 
-// One key of the sparse plan's passes for d = 3 as fp64: point components and
+// One key of the d = 3 passes that evaluate log P in the expanded form (sparse
+// plan, dense gradient, Hessian-vector product) as fp64: point components and
 // B_j = (g_j - ||y_j||^2)/eps + log b_j, 32 bytes.  With the row's
 // A_i = (f_i - ||x_i||^2)/eps + log a_i they give
 //     log P_ij = (2/eps) x_i . y_j + A_i + B_j.
@@ -209,7 +210,7 @@ struct PlanArgs {
     const double *la, *lb;   // natural log of the weights, [B][n] and [B][m] (-inf for 0)
     double inv_eps;
     const KeyD *kd = nullptr;   // d = 3: the keys (Y, g) as KeyD [B][m], or NULL
-    const KeyB *kb = nullptr;   // d = 3 sparse plan (max, count, emit): the keys as KeyB
+    const KeyB *kb = nullptr;   // d = 3 (all but the cost pass): the keys as KeyB [B][m]
 };
 // KeyD records of the keys (Y [B][m][3], g [B][m]) of a d = 3 pass.
 hipError_t launch_keys_d3(const void *Y, int dtype, const float *g, int B, int m, KeyD *out,
@@ -297,7 +298,7 @@ struct HvpWs {
     double *mb, *muc, *tw, *rhs;        // [B][m]
     double *x, *res, *dir;              // conjugate-gradient vectors [B][m]
     double *rr, *rr0;                   // [B]
-    KeyD *kdx = nullptr, *kdy = nullptr;   // d = 3: fp64 keys of the two sides
+    KeyB *kbx = nullptr, *kby = nullptr;   // d = 3: fp64 keys of the two sides
 };
 hipError_t launch_hvp(const PlanArgs &px, const PlanArgs &py, const float *V, int cg_iters,
                       float *HV, float *cg_residual, const HvpWs &w, hipStream_t st);

@@ -60,34 +60,45 @@ __global__ __launch_bounds__(kHvpWaves *kWave) void transport_pass(
     const T *Yb = (const T *)p.Y + (size_t)b * p.m * p.d;
     const float *gb = p.g + (size_t)b * p.m;
     const double *lbb = p.lb + (size_t)b * p.m;
-    const KeyD *kdb = p.kd ? p.kd + (size_t)b * p.m : nullptr;
+    // d = 3: log P in the expanded form from KeyB records and the row's A_i
+    const KeyB *kbb = KD ? p.kb + (size_t)b * p.m : nullptr;
+    double xd[3] = {0.0, 0.0, 0.0}, A = 0.0;
+    if constexpr (KD) {
+#pragma unroll
+        for (int k = 0; k < 3; ++k)
+            xd[k] = (double)r.x[k];
+        A = side_term_d3(xd[0], xd[1], xd[2], r.f, r.la, p.inv_eps);
+    }
+    const double two_inv_eps = 2.0 * p.inv_eps;
     double m0 = 0.0, mu = 0.0, tv = 0.0, tw = 0.0;
     double D1[DP], Du[DP], Tv[DP];
 #pragma unroll
     for (int k = 0; k < DP; ++k)
         D1[k] = Du[k] = Tv[k] = 0.0;
-    // d = 3: the key side's values (fp64 record, log weight, u_j, w_j) pass through
-    // LDS a stage at a time and every lane of a wave reads the same key
-    __shared__ KeyD kst[KD ? kHvpStage : 1];
-    __shared__ double lbst[KD ? kHvpStage : 1];
+    // d = 3: the key side's values (fp64 record, u_j, w_j) pass through LDS a
+    // stage at a time and every lane of a wave reads the same key
+    __shared__ KeyB kst[KD ? kHvpStage : 1];
     __shared__ double ust[KD && (FL & F_U) ? kHvpStage : 1];
     __shared__ float wst[KD && (FL & F_W) ? 3 * kHvpStage : 1];
+    constexpr bool kNeedDiff = (FL & (F_D | F_V | F_W)) != 0;
     auto visit = [&](int j, int js) {
-        double C, diff[DP];
-        KeyVals<DP> kv;
-        double lbj;
+        double diff[DP];
+        double lp;
         if constexpr (KD) {
-            const KeyD kr = kst[js];
+            const KeyB kr = kst[js];
+            const double y[3] = {kr.y[0], kr.y[1], kr.y[2]};
+            lp = log_plan_b3(xd, A, y, kr.B, two_inv_eps);
+            if constexpr (kNeedDiff) {
 #pragma unroll
-            for (int k = 0; k < DP; ++k)
-                kv.y[k] = kr.y[k];
-            kv.g = kr.g;
-            lbj = lbst[js];
+                for (int k = 0; k < 3; ++k)
+                    diff[k] = xd[k] - y[k];
+            }
         } else {
-            load_key<T, DP, KD>(kv, p, Yb, gb, kdb, j);
-            lbj = lbb[j];
+            KeyVals<DP> kv;
+            double C;
+            load_key<T, DP, false>(kv, p, Yb, gb, nullptr, j);
+            lp = log_plan_kv<DP>(r, kv, lbb[j], p.inv_eps, p.d, &C, diff);
         }
-        const double lp = log_plan_kv<DP>(r, kv, lbj, p.inv_eps, p.d, &C, diff);
         const double P = (double)ex2((float)(lp * 1.4426950408889634));
         m0 += P;
         double uj = 0.0;
@@ -131,8 +142,7 @@ __global__ __launch_bounds__(kHvpWaves *kWave) void transport_pass(
             const int kc = min(kHvpStage, p.m - c0);
             __syncthreads();   // the previous stage is no longer read
             for (int e = threadIdx.x; e < kc; e += kHvpWaves * kWave) {
-                kst[e] = kdb[c0 + e];
-                lbst[e] = lbb[c0 + e];
+                kst[e] = kbb[c0 + e];
                 if constexpr ((FL & F_U) != 0)
                     ust[e] = u[(size_t)b * p.m + c0 + e];
                 if constexpr ((FL & F_W) != 0) {
@@ -496,7 +506,7 @@ void pass(const PlanArgs &p, const float *v, const double *u, const float *wk, d
             hipLaunchKernelGGL((transport_pass<float, DP, FL, KD>), grid, block, 0, st, p, v, u, wk,
                                m0, mu, tv, tw, D1, Du, Tv);
     };
-    if (p.d == 3 && p.kd) go.template operator()<3, true>();
+    if (p.d == 3 && p.kb) go.template operator()<3, true>();
     else if (p.d == 3) go.template operator()<3>();
     else if (p.d <= 4) go.template operator()<4>();
     else if (p.d <= 8) go.template operator()<8>();

@@ -81,9 +81,10 @@ __global__ __launch_bounds__(kTileWaves *kWave) void tile_pass(
     const float *gb = p.g + (size_t)b * p.m;
     const double *lbb = p.lb + (size_t)b * p.m;
     const KeyD *kdb = p.kd ? p.kd + (size_t)b * p.m : nullptr;
-    // the sparse plan's max and count passes over staged d = 3 keys take the
-    // expanded form of log P (KeyB records, the row's A_i)
-    constexpr bool kPB = (MODE == 1 || MODE == 2) && KD;
+    // the sparse plan's max and count passes and the dense gradient over staged
+    // d = 3 keys take the expanded form of log P (KeyB records, the row's A_i);
+    // the cost pass (which needs C_ij) takes KeyD records
+    constexpr bool kPB = MODE != 0 && KD;
     const KeyB *kbb = kPB ? p.kb + (size_t)b * p.m : nullptr;
     double xd[3] = {0.0, 0.0, 0.0}, A = 0.0;
     if constexpr (kPB) {
@@ -121,6 +122,11 @@ __global__ __launch_bounds__(kTileWaves *kWave) void tile_pass(
             const KeyB kr = kbst[js];
             const double y[3] = {kr.y[0], kr.y[1], kr.y[2]};
             lp = log_plan_b3(xd, A, y, kr.B, two_inv_eps);
+            if constexpr (kDiff) {
+#pragma unroll
+                for (int k = 0; k < 3; ++k)
+                    diff[k] = xd[k] - y[k];
+            }
         } else if constexpr (KD) {
             // staged in LDS: every lane of the wave reads the same record
             const KeyD kr = kst[js];
@@ -638,7 +644,7 @@ void tile_dispatch(const PlanArgs &p, const double *thr, double *outd, int32_t *
             }
         };
         if constexpr (DP == 3) {
-            if (MODE == 1 || MODE == 2 ? p.kb != nullptr : p.kd != nullptr) {
+            if (MODE != 0 ? p.kb != nullptr : p.kd != nullptr) {
                 go.template operator()<true>();
                 return;
             }

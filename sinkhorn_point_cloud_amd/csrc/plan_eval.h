@@ -11,9 +11,11 @@
 // whose lanes share the key reads them whole (staged in LDS, or with scalar
 // loads) and spends no vector instruction on conversions; otherwise they are
 // converted where they are read.
-// The values, and so every result, are the same either way.  The sparse plan's
-// passes for d = 3 (max, count, emit) instead take the expanded form of log P
-// from KeyB records (log_plan_b3 below), the same in all three.
+// The values, and so every result, are the same either way.  For d = 3 the
+// sparse plan's passes (max, count, emit), the dense gradient and the
+// Hessian-vector product's transport passes instead take the expanded form of
+// log P from KeyB records (log_plan_b3 below); only the cost pass, which needs
+// C_ij itself, keeps the form above.
 #pragma once
 #include "common.h"
 
@@ -112,8 +114,7 @@ __device__ __forceinline__ double log_plan(const RowCtx<DP> &r, const PlanArgs &
     return fma((r.f + (double)gb[j]) - s, p.inv_eps, r.la + lbj);
 }
 
-// The sparse plan's log P for d = 3 (max, count and emit passes), in the
-// expanded form
+// log P for d = 3 in the expanded form
 //     log P_ij = (2/eps) x_i . y_j + A_i + B_j,
 //     A_i = (f_i - ||x_i||^2)/eps + log a_i,   B_j = (g_j - ||y_j||^2)/eps + log b_j,
 // five fp64 operations per entry instead of the ten of log_plan_kv.  Both
