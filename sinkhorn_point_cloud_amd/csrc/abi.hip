@@ -600,7 +600,7 @@ int sinkhorn_plan_coo(const void *X, const void *Y, int dtype, const float *a, c
     p.kb = w.kb;
     hipError_t e;
     if ((e = launch_log_weights(a, B, n, w.la, st)) || (e = launch_log_weights(b, B, m, w.lb, st)) ||
-        (w.kb && (e = launch_keys_plan_d3(Y, dtype, g, w.lb, p.inv_eps, B, m, w.kb, st))))
+        (w.kb && (e = launch_keys_plan_d3(Y, dtype, g, w.lb, p.inv_eps, 1.0, B, m, w.kb, st))))
         return hip_fail(e, "log weights");
     if ((e = launch_plan_max(p, w.row_max, w.pair_thr, log((double)rel_threshold), st)))
         return hip_fail(e, "plan max");
@@ -656,7 +656,7 @@ int sinkhorn_plan_coo_async(const void *X, const void *Y, int dtype, const float
     p.kb = w.kb;
     hipError_t e;
     if ((e = launch_log_weights(a, B, n, w.la, st)) || (e = launch_log_weights(b, B, m, w.lb, st)) ||
-        (w.kb && (e = launch_keys_plan_d3(Y, dtype, g, w.lb, p.inv_eps, B, m, w.kb, st))))
+        (w.kb && (e = launch_keys_plan_d3(Y, dtype, g, w.lb, p.inv_eps, 1.0, B, m, w.kb, st))))
         return hip_fail(e, "log weights");
     if ((e = launch_plan_max(p, w.row_max, w.pair_thr, log((double)rel_threshold), st)) ||
         (e = launch_plan_count(p, w.pair_thr, w.row_count, st)) ||
@@ -723,9 +723,9 @@ int sinkhorn_dense_grad(const void *X, const void *Y, int dtype, const float *a,
     px.kb = w.kby;
     py.kb = w.kbx;
     if ((want_x && w.kby &&
-         (e = launch_keys_plan_d3(Y, dtype, g, w.lb, inv_eps, B, m, w.kby, st))) ||
+         (e = launch_keys_plan_d3(Y, dtype, g, w.lb, inv_eps, kLog2eD, B, m, w.kby, st))) ||
         (want_y && w.kbx &&
-         (e = launch_keys_plan_d3(X, dtype, f, w.la, inv_eps, B, n, w.kbx, st))))
+         (e = launch_keys_plan_d3(X, dtype, f, w.la, inv_eps, kLog2eD, B, n, w.kbx, st))))
         return hip_fail(e, "dense gradient: keys");
     const bool aligned = (uintptr_t)X % 16 == 0 && (uintptr_t)Y % 16 == 0;
     if (gradF_matrix_cores(dtype, d) && aligned) {
@@ -805,8 +805,9 @@ int sinkhorn_hvp(const void *X, const void *Y, int dtype, const float *a, const 
     PlanArgs py{Y, X, dtype, d, B, m, n, g, f, w.lb, w.la, inv_eps};
     px.kb = w.kby;
     py.kb = w.kbx;
-    if (w.kbx && ((e = launch_keys_plan_d3(Y, dtype, g, w.lb, inv_eps, B, m, w.kby, st)) ||
-                  (e = launch_keys_plan_d3(X, dtype, f, w.la, inv_eps, B, n, w.kbx, st))))
+    if (w.kbx &&
+        ((e = launch_keys_plan_d3(Y, dtype, g, w.lb, inv_eps, kLog2eD, B, m, w.kby, st)) ||
+         (e = launch_keys_plan_d3(X, dtype, f, w.la, inv_eps, kLog2eD, B, n, w.kbx, st))))
         return hip_fail(e, "Hessian-vector product: keys");
     if ((e = launch_hvp(px, py, V, cg_iters, HV, cg_residual, w, st)))
         return hip_fail(e, "Hessian-vector product");

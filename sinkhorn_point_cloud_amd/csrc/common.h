@@ -197,6 +197,8 @@ struct alignas(32) KeyD {
 // B_j = (g_j - ||y_j||^2)/eps + log b_j, 32 bytes.  With the row's
 // A_i = (f_i - ||x_i||^2)/eps + log a_i they give
 //     log P_ij = (2/eps) x_i . y_j + A_i + B_j.
+// The dense gradient's and the Hessian-vector product's records (and row terms)
+// carry these in base 2, ready for the exponential: B_j log2 e.
 struct alignas(32) KeyB {
     double y[3];
     double B;
@@ -215,9 +217,11 @@ struct PlanArgs {
 // KeyD records of the keys (Y [B][m][3], g [B][m]) of a d = 3 pass.
 hipError_t launch_keys_d3(const void *Y, int dtype, const float *g, int B, int m, KeyD *out,
                           hipStream_t st);
-// KeyB records of the keys (Y [B][m][3], g [B][m], lb [B][m]) at 1/eps = inv_eps.
+// KeyB records of the keys (Y [B][m][3], g [B][m], lb [B][m]) at 1/eps = inv_eps,
+// B_j multiplied by scale (1: natural log; log2 e: base 2).
 hipError_t launch_keys_plan_d3(const void *Y, int dtype, const float *g, const double *lb,
-                               double inv_eps, int B, int m, KeyB *out, hipStream_t st);
+                               double inv_eps, double scale, int B, int m, KeyB *out,
+                               hipStream_t st);
 // log of the weights in fp64 (w == NULL: uniform 1/count)
 hipError_t launch_log_weights(const float *w, int B, int count, double *out, hipStream_t st);
 hipError_t launch_cost(const PlanArgs &p, double *row_part, float *cost, hipStream_t st);

@@ -31,10 +31,10 @@ namespace {
 
 constexpr int kHvpWaves = 4;
 constexpr int kHvpStage = 512;   // d = 3 key-side values staged in LDS per step
-enum : int { F_V = 1, F_U = 2, F_W = 4, F_D = 8 };
+enum : int { F_V = 1, F_U = 2, F_W = 4, F_D = 8, F_M = 16 };
 
 // Per row i of p.X against the keys of p.Y:
-//   m0 = sum P;  mu = sum P u_j (F_U);  D1 = sum P (x - y), Du = sum P u_j (x - y) (F_D);
+//   m0 = sum P (F_M);  mu = sum P u_j (F_U);  D1 = sum P (x - y), Du = sum P u_j (x - y) (F_D);
 //   tv = sum P (x - y).v_i, Tv = sum P ((x - y).v_i)(x - y) (F_V);  tw = sum P (x - y).w_j (F_W).
 template <typename T, int DP, int FL, bool KD>
 __global__ __launch_bounds__(kHvpWaves *kWave) void transport_pass(
@@ -67,9 +67,10 @@ __global__ __launch_bounds__(kHvpWaves *kWave) void transport_pass(
 #pragma unroll
         for (int k = 0; k < 3; ++k)
             xd[k] = (double)r.x[k];
-        A = side_term_d3(xd[0], xd[1], xd[2], r.f, r.la, p.inv_eps);
+        // base 2, as the records: log2 P ready for the exponential
+        A = kLog2eD * side_term_d3(xd[0], xd[1], xd[2], r.f, r.la, p.inv_eps);
     }
-    const double two_inv_eps = 2.0 * p.inv_eps;
+    const double two_inv_eps = 2.0 * p.inv_eps * kLog2eD;
     double m0 = 0.0, mu = 0.0, tv = 0.0, tw = 0.0;
     double D1[DP], Du[DP], Tv[DP];
 #pragma unroll
@@ -99,8 +100,9 @@ __global__ __launch_bounds__(kHvpWaves *kWave) void transport_pass(
             load_key<T, DP, false>(kv, p, Yb, gb, nullptr, j);
             lp = log_plan_kv<DP>(r, kv, lbb[j], p.inv_eps, p.d, &C, diff);
         }
-        const double P = (double)ex2((float)(lp * 1.4426950408889634));
-        m0 += P;
+        const double P = (double)ex2((float)(KD ? lp : lp * kLog2eD));
+        if (FL & F_M)
+            m0 += P;
         double uj = 0.0;
         if (FL & F_U) {
             if constexpr (KD)
@@ -191,7 +193,7 @@ __global__ __launch_bounds__(kHvpWaves *kWave) void transport_pass(
         return s;
     };
     const size_t ri = (size_t)b * p.n + i;
-    {
+    if (FL & F_M) {
         const double s = merged(m0);
         if (w == 0 && live && o_m0)
             o_m0[ri] = s;
@@ -523,13 +525,13 @@ hipError_t launch_hvp(const PlanArgs &px, const PlanArgs &py, const float *V, in
     const int B = px.B, n = px.n, m = px.m, d = px.d;
     const size_t Bn = (size_t)B * n, Bm = (size_t)B * m;
     // rows X: ma, D1, tv, Tv
-    pass<F_V | F_D>(px, V, nullptr, nullptr, w.ma, nullptr, w.tv, nullptr, w.D1, nullptr, w.Tv,
-                    st);
+    pass<F_M | F_V | F_D>(px, V, nullptr, nullptr, w.ma, nullptr, w.tv, nullptr, w.D1, nullptr,
+                          w.Tv, st);
     // u_i = r_i / ma_i = 2 tv_i / ma_i; rows Y (keys X carry v): mb, P^T u, tw
     hipLaunchKernelGGL(ratio_kernel, dim3(blocks_for(Bn)), dim3(256), 0, st,
                        (const double *)w.tv, (const double *)w.ma, Bn, 2.0, w.ur);
-    pass<F_U | F_W>(py, nullptr, w.ur, V, w.mb, w.muc, nullptr, w.tw, nullptr, nullptr, nullptr,
-                    st);
+    pass<F_M | F_U | F_W>(py, nullptr, w.ur, V, w.mb, w.muc, nullptr, w.tw, nullptr, nullptr,
+                          nullptr, st);
     hipLaunchKernelGGL(rhs_kernel, dim3(blocks_for(Bm)), dim3(256), 0, st, (const double *)w.tw,
                        (const double *)w.muc, Bm, w.rhs);
     hipLaunchKernelGGL(cg_start, dim3(B), dim3(256), 0, st, (const double *)w.rhs, m, w.x, w.res,

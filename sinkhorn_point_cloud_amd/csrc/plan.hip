@@ -93,7 +93,11 @@ __global__ __launch_bounds__(kTileWaves *kWave) void tile_pass(
             xd[k] = (double)r.x[k];
         A = side_term_d3(xd[0], xd[1], xd[2], r.f, r.la, p.inv_eps);
     }
-    const double two_inv_eps = 2.0 * p.inv_eps;
+    // the dense gradient's records and A_i carry log P in base 2
+    constexpr double kLs = kPB && MODE == 3 ? kLog2eD : 1.0;
+    if constexpr (kLs != 1.0)
+        A *= kLs;
+    const double two_inv_eps = 2.0 * p.inv_eps * kLs;
     const double t = MODE == 2 ? thr[b] : 0.0;
     double acc = MODE == 1 ? -INFINITY : 0.0;
     int cnt = 0;
@@ -151,7 +155,7 @@ __global__ __launch_bounds__(kTileWaves *kWave) void tile_pass(
         } else if (MODE == 2) {
             cnt += lp >= t ? 1 : 0;
         } else {
-            const double P = (double)ex2((float)(lp * 1.4426950408889634));
+            const double P = (double)ex2((float)(kLs != 1.0 ? lp : lp * kLog2eD));
             acc += P;
             if constexpr (kDiff) {
 #pragma unroll
@@ -599,8 +603,8 @@ __global__ void keys_d3_kernel(const T *__restrict__ Y, const float *__restrict_
 
 template <typename T>
 __global__ void keys_plan_d3_kernel(const T *__restrict__ Y, const float *__restrict__ g,
-                                    const double *__restrict__ lb, double inv_eps, size_t count,
-                                    KeyB *__restrict__ out)
+                                    const double *__restrict__ lb, double inv_eps, double scale,
+                                    size_t count, KeyB *__restrict__ out)
 {
     const size_t k = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (k >= count)
@@ -609,7 +613,7 @@ __global__ void keys_plan_d3_kernel(const T *__restrict__ Y, const float *__rest
 #pragma unroll
     for (int c = 0; c < 3; ++c)
         r.y[c] = (double)Elem<T>::get(Y, 3 * k + c);
-    r.B = side_term_d3(r.y[0], r.y[1], r.y[2], (double)g[k], lb[k], inv_eps);
+    r.B = scale * side_term_d3(r.y[0], r.y[1], r.y[2], (double)g[k], lb[k], inv_eps);
     out[k] = r;
 }
 
@@ -670,16 +674,17 @@ hipError_t launch_keys_d3(const void *Y, int dtype, const float *g, int B, int m
 }
 
 hipError_t launch_keys_plan_d3(const void *Y, int dtype, const float *g, const double *lb,
-                               double inv_eps, int B, int m, KeyB *out, hipStream_t st)
+                               double inv_eps, double scale, int B, int m, KeyB *out,
+                               hipStream_t st)
 {
     const size_t count = (size_t)B * m;
     const dim3 grid((unsigned)((count + 255) / 256));
     if (dtype == 1)
         hipLaunchKernelGGL(keys_plan_d3_kernel<uint16_t>, grid, dim3(256), 0, st,
-                           (const uint16_t *)Y, g, lb, inv_eps, count, out);
+                           (const uint16_t *)Y, g, lb, inv_eps, scale, count, out);
     else
         hipLaunchKernelGGL(keys_plan_d3_kernel<float>, grid, dim3(256), 0, st, (const float *)Y,
-                           g, lb, inv_eps, count, out);
+                           g, lb, inv_eps, scale, count, out);
     return hipGetLastError();
 }
 
