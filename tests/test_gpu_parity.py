@@ -664,6 +664,7 @@ def check_dense_grad(c, eps, fo, go, sel_x=None, sel_y=None, tol=1e-4):
 @pytest.mark.parametrize("B,n,m,d,dtype,w,eps,tol", [
     (1, 33, 47, 3, "f32", "uniform", 0.05, 1e-4),
     (2, 300, 257, 3, "f32", "dirichlet", 0.01, 1e-4),
+    (1, 150, 140, 3, "bf16", "dirichlet", 0.05, 1e-4),
     (1, 130, 77, 8, "f32", "dirichlet", 0.1, 1e-4),
     (1, 200, 190, 64, "bf16", "uniform", 0.2, 1e-4),
     (2, 1100, 900, 64, "bf16", "dirichlet", 0.1, 1e-4),
@@ -985,6 +986,8 @@ def test_workload_coo_normalize_sampled_pairs(name, pairs):
 # pieces (2^-17) and fp32 sums, all below the 1e-4 held for the fp64 path.
 @pytest.mark.parametrize("B,n,m,d,dtype,eps,zw", [(1, 40, 50, 3, "f32", 0.1, 0),
                                                   (2, 120, 90, 3, "f32", 0.05, 0),
+                                                  (1, 60, 70, 3, "bf16", 0.1, 0),
+                                                  (1, 80, 90, 3, "f32", 0.1, 5),
                                                   (1, 64, 70, 8, "f32", 0.2, 0),
                                                   (1, 50, 45, 16, "bf16", 0.5, 0),
                                                   (1, 50, 45, 64, "bf16", 0.5, 0),
