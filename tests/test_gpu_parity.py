@@ -866,6 +866,30 @@ def test_coo_normalize_matches_oracle(B, n, m, eps, thr, iters):
     _assert_transposes(P, T, B)
 
 
+def test_coo_normalize_unaligned_values():
+    # value arrays that start 4 bytes past a 16-byte boundary take the log pass's
+    # one-entry-at-a-time form; the result is the aligned call's, bit for bit
+    c = workloads.random_case(19, 2, 150, 170, 3, weights="dirichlet")
+    fo, go = oracle.potentials(c["X"], c["Y"], c["a"], c["b"], eps=[0.03], iters=[10])
+    plan = oracle.plan_coo(c["X"], c["Y"], c["a"], c["b"], fo, go, 0.03, rel_thr=1e-8)
+    tr = oracle.plan_coo(c["Y"], c["X"], c["b"], c["a"], go, fo, 0.03, rel_thr=1e-8)
+    runs = []
+    for shift in (0, 1):
+        P = list(_coo_dev((plan[0], plan[1], plan[2].astype(np.float32), plan[3])))
+        T = list(_coo_dev(tr))
+        for Z in (P, T):
+            buf = torch.zeros(Z[2].numel() + 4, dtype=torch.float32, device=Z[2].device)
+            view = buf[shift:shift + Z[2].numel()]
+            view.copy_(Z[2])
+            Z[2] = view
+        assert (P[2].data_ptr() % 16 == 0) == (shift == 0)
+        err = sk.coo_normalize(tuple(P), tuple(T), dev(c["a"]), dev(c["b"]), 150, 170, 20)
+        torch.cuda.synchronize()
+        runs.append((host(P[2]), host(T[2]), host(err)))
+    for u, v in zip(runs[0], runs[1]):
+        np.testing.assert_array_equal(u, v)
+
+
 def _assert_transposes(P, T, B):
     """T holds P's entries and values, bit for bit, in column-major order."""
     r1, c1, v1, o1 = (host(t) for t in P)
