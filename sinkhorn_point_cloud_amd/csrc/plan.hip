@@ -431,10 +431,11 @@ __global__ __launch_bounds__(kRowsPerGroup *kWave) void emit_pass(
 // Emit pass for small d with the keys staged in LDS: a work-group of
 // kEmitWaves waves takes kEmitRows consecutive rows of one pair (a wave per row
 // at a time, lanes across 64 consecutive columns, as above) and shares one
-// staged copy of each chunk of kEmitChunk columns (point components and g_j as
-// fp64, log b_j), so the column data is read and converted once per work-group
-// instead of once per row.  The evaluation is log_plan_kv on the same values as
-// the count pass, so the decisions agree bit for bit.
+// staged copy of each chunk of kEmitChunk columns (d = 3: the KeyB records'
+// point components and B_j; d = 4: point components and g_j as fp64, log b_j),
+// so the column data is read and converted once per work-group instead of once
+// per row.  The evaluation is the count pass's (log_plan_b3 for d = 3,
+// log_plan_kv otherwise) on the same values, so the decisions agree bit for bit.
 constexpr int kEmitWaves = 8, kEmitRows = 32, kEmitChunk = 1024;
 
 template <typename T, int DP, bool LG>
