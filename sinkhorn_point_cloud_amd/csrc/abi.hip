@@ -599,14 +599,15 @@ int sinkhorn_plan_coo(const void *X, const void *Y, int dtype, const float *a, c
     PlanArgs p{X, Y, dtype, d, B, n, m, f, g, w.la, w.lb, 1.0 / (double)eps};
     p.kb = w.kb;
     hipError_t e;
-    if ((e = launch_log_weights(a, B, n, w.la, st)) || (e = launch_log_weights(b, B, m, w.lb, st)) ||
-        (w.kb && (e = launch_keys_plan_d3(Y, dtype, g, w.lb, p.inv_eps, 1.0, B, m, w.kb, st))))
+    if ((e = launch_plan_prep(a, b, B, n, m, w.la, w.lb, X, Y, dtype, f, g, p.inv_eps, 1.0,
+                              nullptr, w.kb, st)))
         return hip_fail(e, "log weights");
     if ((e = launch_plan_max(p, w.row_max, w.pair_thr, log((double)rel_threshold), st)))
         return hip_fail(e, "plan max");
     if ((e = launch_plan_count(p, w.pair_thr, w.row_count, st)))
         return hip_fail(e, "plan count");
-    if ((e = launch_plan_scan(w.row_count, B, n, w.row_off, pair_offsets, w.pair_tot, st)))
+    if ((e = launch_plan_scan(w.row_count, B, n, w.row_off, pair_offsets, w.pair_tot, nullptr,
+                              st)))
         return hip_fail(e, "plan scan");
     int64_t total = 0;
     if ((e = hipMemcpyAsync(&total, pair_offsets + B, sizeof total, hipMemcpyDeviceToHost, st)))
@@ -655,13 +656,13 @@ int sinkhorn_plan_coo_async(const void *X, const void *Y, int dtype, const float
     PlanArgs p{X, Y, dtype, d, B, n, m, f, g, w.la, w.lb, 1.0 / (double)eps};
     p.kb = w.kb;
     hipError_t e;
-    if ((e = launch_log_weights(a, B, n, w.la, st)) || (e = launch_log_weights(b, B, m, w.lb, st)) ||
-        (w.kb && (e = launch_keys_plan_d3(Y, dtype, g, w.lb, p.inv_eps, 1.0, B, m, w.kb, st))))
+    if ((e = launch_plan_prep(a, b, B, n, m, w.la, w.lb, X, Y, dtype, f, g, p.inv_eps, 1.0,
+                              nullptr, w.kb, st)))
         return hip_fail(e, "log weights");
     if ((e = launch_plan_max(p, w.row_max, w.pair_thr, log((double)rel_threshold), st)) ||
         (e = launch_plan_count(p, w.pair_thr, w.row_count, st)) ||
-        (e = launch_plan_scan(w.row_count, B, n, w.row_off, pair_offsets, w.pair_tot, st)) ||
-        (e = launch_copy_total(pair_offsets + B, nnz_device, st)))
+        (e = launch_plan_scan(w.row_count, B, n, w.row_off, pair_offsets, w.pair_tot,
+                              nnz_device, st)))
         return hip_fail(e, "plan count");
     if ((e = launch_plan_emit(p, w.pair_thr, w.row_off, w.row_count, rows, cols, vals, w.row_max,
                               loss, dX, pair_offsets + B, capacity, st)))
@@ -713,20 +714,17 @@ int sinkhorn_dense_grad(const void *X, const void *Y, int dtype, const float *a,
     Carve c{(char *)ws};
     GradWs w = carve_grad(c, B, n, m, d, dtype);
     hipError_t e;
-    if ((e = launch_log_weights(a, B, n, w.la, st)) || (e = launch_log_weights(b, B, m, w.lb, st)))
-        return hip_fail(e, "log weights");
     const double inv_eps = 1.0 / (double)eps;
     const bool want_x = dX || TX, want_y = dY || TY;
+    // log weights and, for d = 3, the key records of the sides in use
+    if ((e = launch_plan_prep(a, b, B, n, m, w.la, w.lb, X, Y, dtype, f, g, inv_eps, kLog2eD,
+                              want_y ? w.kbx : nullptr, want_x ? w.kby : nullptr, st)))
+        return hip_fail(e, "log weights");
     // log P is symmetric in (X, a, f) and (Y, b, g): the Y side is the same pass
     PlanArgs px{X, Y, dtype, d, B, n, m, f, g, w.la, w.lb, inv_eps};
     PlanArgs py{Y, X, dtype, d, B, m, n, g, f, w.lb, w.la, inv_eps};
     px.kb = w.kby;
     py.kb = w.kbx;
-    if ((want_x && w.kby &&
-         (e = launch_keys_plan_d3(Y, dtype, g, w.lb, inv_eps, kLog2eD, B, m, w.kby, st))) ||
-        (want_y && w.kbx &&
-         (e = launch_keys_plan_d3(X, dtype, f, w.la, inv_eps, kLog2eD, B, n, w.kbx, st))))
-        return hip_fail(e, "dense gradient: keys");
     const bool aligned = (uintptr_t)X % 16 == 0 && (uintptr_t)Y % 16 == 0;
     if (gradF_matrix_cores(dtype, d) && aligned) {
         const int np = round_up(n, kGradPad), mp = round_up(m, kGradPad);
@@ -798,17 +796,14 @@ int sinkhorn_hvp(const void *X, const void *Y, int dtype, const float *a, const 
         return SK_OK;
     }
     HvpWs w = carve_hvp(c, B, n, m, d);
-    if ((e = launch_log_weights(a, B, n, w.la, st)) || (e = launch_log_weights(b, B, m, w.lb, st)))
-        return hip_fail(e, "log weights");
     const double inv_eps = 1.0 / (double)eps;
+    if ((e = launch_plan_prep(a, b, B, n, m, w.la, w.lb, X, Y, dtype, f, g, inv_eps, kLog2eD,
+                              w.kbx, w.kby, st)))
+        return hip_fail(e, "log weights");
     PlanArgs px{X, Y, dtype, d, B, n, m, f, g, w.la, w.lb, inv_eps};
     PlanArgs py{Y, X, dtype, d, B, m, n, g, f, w.lb, w.la, inv_eps};
     px.kb = w.kby;
     py.kb = w.kbx;
-    if (w.kbx &&
-        ((e = launch_keys_plan_d3(Y, dtype, g, w.lb, inv_eps, kLog2eD, B, m, w.kby, st)) ||
-         (e = launch_keys_plan_d3(X, dtype, f, w.la, inv_eps, kLog2eD, B, n, w.kbx, st))))
-        return hip_fail(e, "Hessian-vector product: keys");
     if ((e = launch_hvp(px, py, V, cg_iters, HV, cg_residual, w, st)))
         return hip_fail(e, "Hessian-vector product");
     return SK_OK;

@@ -217,11 +217,13 @@ struct PlanArgs {
 // KeyD records of the keys (Y [B][m][3], g [B][m]) of a d = 3 pass.
 hipError_t launch_keys_d3(const void *Y, int dtype, const float *g, int B, int m, KeyD *out,
                           hipStream_t st);
-// KeyB records of the keys (Y [B][m][3], g [B][m], lb [B][m]) at 1/eps = inv_eps,
-// B_j multiplied by scale (1: natural log; log2 e: base 2).
-hipError_t launch_keys_plan_d3(const void *Y, int dtype, const float *g, const double *lb,
-                               double inv_eps, double scale, int B, int m, KeyB *out,
-                               hipStream_t st);
+// log a, log b (fp64, as launch_log_weights) and, for d = 3, the KeyB records of
+// X (kx, from f and log a) and of Y (ky, from g and log b) where not NULL, in one
+// launch.
+hipError_t launch_plan_prep(const float *a, const float *b, int B, int n, int m, double *la,
+                            double *lb, const void *X, const void *Y, int dtype, const float *f,
+                            const float *g, double inv_eps, double scale, KeyB *kx, KeyB *ky,
+                            hipStream_t st);
 // log of the weights in fp64 (w == NULL: uniform 1/count)
 hipError_t launch_log_weights(const float *w, int B, int count, double *out, hipStream_t st);
 hipError_t launch_cost(const PlanArgs &p, double *row_part, float *cost, hipStream_t st);
@@ -229,8 +231,10 @@ hipError_t launch_plan_max(const PlanArgs &p, double *row_max, double *pair_thr,
                            double log_rel_thr, hipStream_t st);
 hipError_t launch_plan_count(const PlanArgs &p, const double *pair_thr, int32_t *row_count,
                              hipStream_t st);
+// total_copy != NULL: the entry count is also written there (device int64).
 hipError_t launch_plan_scan(const int32_t *row_count, int B, int n, int64_t *row_off,
-                            int64_t *pair_offsets, int64_t *pair_tot, hipStream_t st);
+                            int64_t *pair_offsets, int64_t *pair_tot, int64_t *total_copy,
+                            hipStream_t st);
 // Emission of the counted entries; with loss / dX (either may be NULL) also the
 // loss per pair and its gradient in X on the emitted support (row_loss: [B][n]
 // scratch, needed with loss).
@@ -240,8 +244,6 @@ hipError_t launch_plan_emit(const PlanArgs &p, const double *pair_thr, const int
                             const int32_t *row_count, int32_t *rows, int32_t *cols,
                             float *vals, double *row_loss, float *loss, float *dX,
                             const int64_t *gate, int64_t gate_cap, hipStream_t st);
-// *dst = *src on the device (one int64)
-hipError_t launch_copy_total(const int64_t *src, int64_t *dst, hipStream_t st);
 // Dense gradient 2 sum_j P_ij (x_i - y_j) and barycentric projection
 // sum_j P_ij y_j / sum_j P_ij of every row of p.X (either output may be NULL),
 // log P in fp64.  only != NULL: just the 64-row blocks flagged there.

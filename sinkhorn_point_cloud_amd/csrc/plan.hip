@@ -321,8 +321,10 @@ __device__ int64_t block_exclusive_scan(int64_t *sm, int64_t v)
 }
 
 // Single group: pair_offsets[0..B] from the pair totals.
+// (total != NULL: the plan's entry count is also written there)
 __global__ __launch_bounds__(256) void pair_offsets_scan(const int64_t *__restrict__ tot, int B,
-                                                         int64_t *__restrict__ offs)
+                                                         int64_t *__restrict__ offs,
+                                                         int64_t *__restrict__ total_out)
 {
     __shared__ int64_t sm[256];
     int64_t carry = 0;
@@ -335,8 +337,11 @@ __global__ __launch_bounds__(256) void pair_offsets_scan(const int64_t *__restri
         carry += total;
         __syncthreads();
     }
-    if (threadIdx.x == 0)
+    if (threadIdx.x == 0) {
         offs[B] = carry;
+        if (total_out)
+            *total_out = carry;
+    }
 }
 
 // One group per pair: global offset of every row.
@@ -602,20 +607,45 @@ __global__ void keys_d3_kernel(const T *__restrict__ Y, const float *__restrict_
     out[k] = r;
 }
 
+// The plan passes' per-point inputs in one launch: la = log a [B][n] and
+// lb = log b [B][m] (as log_weights_kernel), and for d = 3 the KeyB records of
+// either side, from the point, its potential and the log weight just computed,
+// B times scale: kx from (X, f, la) when not NULL, ky from (Y, g, lb) when not
+// NULL.
 template <typename T>
-__global__ void keys_plan_d3_kernel(const T *__restrict__ Y, const float *__restrict__ g,
-                                    const double *__restrict__ lb, double inv_eps, double scale,
-                                    size_t count, KeyB *__restrict__ out)
+__global__ void plan_prep_kernel(const float *__restrict__ a, const float *__restrict__ b,
+                                 int B, int n, int m, double *__restrict__ la,
+                                 double *__restrict__ lb, const T *__restrict__ X,
+                                 const T *__restrict__ Y, const float *__restrict__ f,
+                                 const float *__restrict__ g, double inv_eps, double scale,
+                                 KeyB *__restrict__ kx, KeyB *__restrict__ ky)
 {
-    const size_t k = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (k >= count)
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t bn = (size_t)B * n, bm = (size_t)B * m;
+    const bool xs = i < bn;
+    if (!xs && i >= bn + bm)
         return;
-    KeyB r;
+    const size_t k = xs ? i : i - bn;
+    const float *w = xs ? a : b;
+    const int count = xs ? n : m;
+    double lw;
+    if (!w) {
+        lw = -log((double)count);
+    } else {
+        const float v = w[k];
+        lw = v > 0.f ? log((double)v) : -INFINITY;
+    }
+    (xs ? la : lb)[k] = lw;
+    KeyB *out = xs ? kx : ky;
+    if (out) {
+        const T *P = xs ? X : Y;
+        KeyB r;
 #pragma unroll
-    for (int c = 0; c < 3; ++c)
-        r.y[c] = (double)Elem<T>::get(Y, 3 * k + c);
-    r.B = scale * side_term_d3(r.y[0], r.y[1], r.y[2], (double)g[k], lb[k], inv_eps);
-    out[k] = r;
+        for (int c = 0; c < 3; ++c)
+            r.y[c] = (double)Elem<T>::get(P, 3 * k + c);
+        r.B = scale * side_term_d3(r.y[0], r.y[1], r.y[2], (double)(xs ? f : g)[k], lw, inv_eps);
+        out[k] = r;
+    }
 }
 
 template <typename F>
@@ -674,18 +704,20 @@ hipError_t launch_keys_d3(const void *Y, int dtype, const float *g, int B, int m
     return hipGetLastError();
 }
 
-hipError_t launch_keys_plan_d3(const void *Y, int dtype, const float *g, const double *lb,
-                               double inv_eps, double scale, int B, int m, KeyB *out,
-                               hipStream_t st)
+hipError_t launch_plan_prep(const float *a, const float *b, int B, int n, int m, double *la,
+                            double *lb, const void *X, const void *Y, int dtype, const float *f,
+                            const float *g, double inv_eps, double scale, KeyB *kx, KeyB *ky,
+                            hipStream_t st)
 {
-    const size_t count = (size_t)B * m;
-    const dim3 grid((unsigned)((count + 255) / 256));
+    const size_t total = (size_t)B * n + (size_t)B * m;
+    const dim3 grid((unsigned)((total + 255) / 256));
     if (dtype == 1)
-        hipLaunchKernelGGL(keys_plan_d3_kernel<uint16_t>, grid, dim3(256), 0, st,
-                           (const uint16_t *)Y, g, lb, inv_eps, scale, count, out);
+        hipLaunchKernelGGL(plan_prep_kernel<uint16_t>, grid, dim3(256), 0, st, a, b, B, n, m, la,
+                           lb, (const uint16_t *)X, (const uint16_t *)Y, f, g, inv_eps, scale, kx,
+                           ky);
     else
-        hipLaunchKernelGGL(keys_plan_d3_kernel<float>, grid, dim3(256), 0, st, (const float *)Y,
-                           g, lb, inv_eps, scale, count, out);
+        hipLaunchKernelGGL(plan_prep_kernel<float>, grid, dim3(256), 0, st, a, b, B, n, m, la, lb,
+                           (const float *)X, (const float *)Y, f, g, inv_eps, scale, kx, ky);
     return hipGetLastError();
 }
 
@@ -734,11 +766,12 @@ hipError_t launch_plan_count(const PlanArgs &p, const double *pair_thr, int32_t 
 }
 
 hipError_t launch_plan_scan(const int32_t *row_count, int B, int n, int64_t *row_off,
-                            int64_t *pair_offsets, int64_t *pair_tot, hipStream_t st)
+                            int64_t *pair_offsets, int64_t *pair_tot, int64_t *total_copy,
+                            hipStream_t st)
 {
     hipLaunchKernelGGL(pair_totals, dim3(B), dim3(256), 0, st, row_count, n, pair_tot);
     hipLaunchKernelGGL(pair_offsets_scan, dim3(1), dim3(256), 0, st, (const int64_t *)pair_tot,
-                       B, pair_offsets);
+                       B, pair_offsets, total_copy);
     hipLaunchKernelGGL(row_offsets_scan, dim3(B), dim3(256), 0, st, row_count, n,
                        (const int64_t *)pair_offsets, row_off);
     return hipGetLastError();
@@ -784,20 +817,6 @@ hipError_t launch_plan_emit(const PlanArgs &p, const double *pair_thr, const int
     if (loss)
         hipLaunchKernelGGL(pair_reduce<0>, dim3(p.B), dim3(256), 0, st, (const double *)row_loss,
                            p.n, loss, (double *)nullptr, 0.0, gate, gate_cap);
-    return hipGetLastError();
-}
-
-namespace {
-__global__ void copy_total(const int64_t *__restrict__ src, int64_t *__restrict__ dst)
-{
-    if (threadIdx.x == 0 && blockIdx.x == 0)
-        *dst = *src;
-}
-}  // namespace
-
-hipError_t launch_copy_total(const int64_t *src, int64_t *dst, hipStream_t st)
-{
-    hipLaunchKernelGGL(copy_total, dim3(1), dim3(64), 0, st, src, dst);
     return hipGetLastError();
 }
 
