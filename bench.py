@@ -54,11 +54,12 @@ EXP_LANES_PER_CLK_CU = 32
 TILE_CYCLES = {
     "lse3m_kernel": 220.0,
     "lse3p_kernel": 220.0,
+    "lse3s_kernel": 220.0,
     "lseFs_kernel": 314.0,
     "lse3_kernel": 16 * 8.8 + 64 * 2.3,        # 3 fma + 1 add per entry on top of the exp
     "lseF_kernel": 16 * 8.8 + 16 * 66 * 2.3,   # 64-dim dot products on the vector ALUs
 }
-TILE_PROBE = {"lse3m_kernel": "d3_tile", "lse3p_kernel": "d3_tile",
+TILE_PROBE = {"lse3m_kernel": "d3_tile", "lse3p_kernel": "d3_tile", "lse3s_kernel": "d3_tile",
               "lseFs_kernel": "feature_tile"}
 
 
@@ -79,7 +80,7 @@ def roofline_evals_per_s(d, kernel):
     exp = N_CU * CLOCK_HZ * EXP_LANES_PER_CLK_CU
     fp32 = FP32_VECTOR_PEAK / FLOPS_PER_EVAL_D3
     algo = min(fp32, exp)
-    if d == 3 and kernel in ("lse3m_kernel", "lse3p_kernel"):
+    if d == 3 and kernel in ("lse3m_kernel", "lse3p_kernel", "lse3s_kernel"):
         return exp, "alu", ("exp issue: 256 CUs x 32 v_exp_f32 lanes/clk x 2.4 GHz, one exp per "
                             "entry (score and bias on the matrix cores)"), algo
     if d == 3:
@@ -95,6 +96,8 @@ KERNEL_SOURCES = {
     "lse3m_kernel": ("sinkhorn_point_cloud_amd/csrc/lse_d3.hip",
                      "sinkhorn_point_cloud_amd/csrc/common.h"),
     "lse3p_kernel": ("sinkhorn_point_cloud_amd/csrc/lse_d3.hip",
+                     "sinkhorn_point_cloud_amd/csrc/common.h"),
+    "lse3s_kernel": ("sinkhorn_point_cloud_amd/csrc/lse_d3.hip",
                      "sinkhorn_point_cloud_amd/csrc/common.h"),
     "lseFs_kernel": ("sinkhorn_point_cloud_amd/csrc/lse_feat.hip",
                      "sinkhorn_point_cloud_amd/csrc/common.h"),
@@ -360,13 +363,18 @@ def main():
 
     if d == 3:
         # the library runs whole stages per pair in one launch when the batch has at
-        # least one pair per compute unit and both padded clouds hold <= 8192 points
+        # least one pair per compute unit and both padded clouds hold <= 8192 points,
+        # and whole stages of a small batch split over work-groups of 16 rows when
+        # both padded clouds hold <= 1024 points and those work-groups fit on half of
+        # the compute units
         pad = lambda k: (k + 63) // 64 * 64
-        pairwise = (not args.valu_scores
-                    and B >= torch.cuda.get_device_properties(dev).multi_processor_count
-                    and pad(n) <= 8192 and pad(m) <= 8192)
-        kernel = ("lse3_kernel" if args.valu_scores else
-                  "lse3p_kernel" if pairwise else "lse3m_kernel")
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        per_pair = (not args.valu_scores and B >= cus and pad(n) <= 8192 and pad(m) <= 8192)
+        split = (not args.valu_scores and not per_pair and pad(n) <= 1024 and pad(m) <= 1024
+                 and 2 * B * (max(pad(n), pad(m)) // 16) <= cus)
+        pairwise = per_pair or split   # one launch per stage
+        kernel = ("lse3_kernel" if args.valu_scores else "lse3p_kernel" if per_pair else
+                  "lse3s_kernel" if split else "lse3m_kernel")
     else:
         pairwise = False
         kernel = "lseFs_kernel" if dt == sk.SK_BF16 and d % 32 == 0 else "lseF_kernel"
@@ -427,9 +435,11 @@ def main():
                      if kernel in KERNEL_SOURCES else None,
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
                                      "scaled by a 256 MiB copy)",
-                     "kernel": kernel + (" (one launch: a stage of %d iterations for every pair)"
-                                         % (total_iters // launches) if pairwise
-                                         else " (one launch: a half-iteration)"),
+                     "kernel": kernel + (" (one launch: a stage of %d iterations for every pair%s)"
+                                         % (total_iters // launches,
+                                            ", each pair over work-groups of 16 rows"
+                                            if kernel == "lse3s_kernel" else "")
+                                         if pairwise else " (one launch: a half-iteration)"),
                      "launch_ms": t_launch * 1e3, "evals_per_launch": evals_per_launch,
                      "peak_basis": basis,
                      # the metric's exp/FP32 roofline: min(FP32 vector / 9 flops, exp issue)

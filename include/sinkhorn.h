@@ -118,6 +118,14 @@ size_t sinkhorn_workspace_bytes(int op, int B, int n, int m, int d, int dtype);
  * With n_stages == 0 (or all iters 0) the potentials are returned unchanged
  * (zero without SK_WARM_START) and cost is that of those potentials, at
  * eps[n_stages-1] if n_stages > 0; cost must be NULL when n_stages == 0.
+ *
+ * For d == 3, a small batch of clouds of at most 1024 points runs each stage
+ * in one launch whose work-groups (at most half of the device's compute units)
+ * wait for one another's results between half-iterations [FS Methodologie 2:
+ * the update fused into as few launches as possible].  Those waits are
+ * bounded: if the work-groups could not all run at once (the compute units
+ * held by other work for about a second), the affected pairs' f and g come
+ * back NaN instead of the call blocking.
  */
 int sinkhorn_potentials(const void *X, const void *Y, int dtype,
                         const float *a, const float *b,

@@ -40,6 +40,22 @@ int sinkhorn_probe_rates(int kind, int blocks, int iters, float *sink,
                          unsigned long long *clocks, double *wall_clock_hz,
                          void *stream);
 
+/*
+ * Wait limit of the split stage launch, a test hook for its failure path.
+ * For a small batch of pairs of at most 1024 points, sinkhorn_potentials (d = 3)
+ * runs each stage of iterations in one launch whose work-groups each own a
+ * slice of a pair's rows and hand their new potentials to one another between
+ * half-iterations [FS Methodologie 2: fusing the update into as few launches
+ * as possible].  Each hand-over is a bounded wait: when it runs out (the
+ * work-groups were not all resident at once, e.g. another process held the
+ * compute units), the pair's potentials come back NaN instead of the launch
+ * hanging.  This sets that bound, in microseconds of wall clock, for every
+ * launch enqueued after the call, process-wide (default 1000000, one second);
+ * microseconds < 0 makes every wait fail at once, so that a test can see the
+ * NaN results.  Returns the previous value.
+ */
+long long sinkhorn_probe_wait_limit(long long microseconds);
+
 #ifdef __cplusplus
 }
 #endif

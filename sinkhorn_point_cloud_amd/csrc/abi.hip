@@ -68,6 +68,8 @@ struct PotWs {
     float *xbias = nullptr, *ybias = nullptr, *xsq = nullptr, *ysq = nullptr;
     // both: per 64-row block marks of rows to recompute
     int *xredo = nullptr, *yredo = nullptr;
+    // d = 3: (tag, bias) words of the split stage launch
+    uint64_t *xxch = nullptr, *yxch = nullptr;
     // both
     float *l2a, *l2b;
     float2 *part;
@@ -92,6 +94,8 @@ PotWs carve_potentials(Carve &c, int B, int n, int m, int d, int dtype)
         w.boxes = c.take<float4>((size_t)2 * B * center3_parts(n, m));
         w.xredo = c.take<int>((size_t)B * (np / kPad));
         w.yredo = c.take<int>((size_t)B * (mp / kPad));
+        w.xxch = c.take<uint64_t>((size_t)B * np);
+        w.yxch = c.take<uint64_t>((size_t)B * mp);
         parts = std::max(lse3_partial_floats2(B, np, mp), lse3_partial_floats2(B, mp, np));
     } else {
         w.xbias = c.take<float>((size_t)B * np);
@@ -379,9 +383,11 @@ int run_potentials(const void *X, const void *Y, int dtype, const float *a, cons
     hipError_t e;
     const bool p3 = path3(dtype, d);
     const bool pairwise = p3 && mfma && lse3_pairwise(B, np, mp);
+    // work-groups per pair of the split stage launch (0: not used)
+    const int split = p3 && mfma && !pairwise ? lse3_split_parts(B, np, mp) : 0;
     // the caller's f and g are the state of the iteration
-    Side3 sx3{w.px, f, w.l2a, w.kxrec, w.qxrec, n, np, w.xredo};
-    Side3 sy3{w.py, g, w.l2b, w.kyrec, w.qyrec, m, mp, w.yredo};
+    Side3 sx3{w.px, f, w.l2a, w.kxrec, w.qxrec, n, np, w.xredo, split ? w.xxch : nullptr};
+    Side3 sy3{w.py, g, w.l2b, w.kyrec, w.qyrec, m, mp, w.yredo, split ? w.yxch : nullptr};
     SideF sxf{X, w.xbias, f, w.l2a, w.xsq, w.xredo, n, np};
     SideF syf{Y, w.ybias, g, w.l2b, w.ysq, w.yredo, m, mp};
     if (p3) {
@@ -403,7 +409,7 @@ int run_potentials(const void *X, const void *Y, int dtype, const float *a, cons
             if ((e = launch_qrec3(sx3, B, eps[s], st)) || (e = launch_qrec3(sy3, B, eps[s], st)))
                 return hip_fail(e, "query records");
         }
-        if (p3 && mfma && iters[s] > 0 && pairwise) {
+        if (p3 && mfma && iters[s] > 0 && (pairwise || split)) {
             float eps_next = eps[s];   // eps of the f-update after the stage's last g-update
             for (int t = s + 1; t < n_stages; ++t)
                 if (iters[t] > 0) {
@@ -411,7 +417,10 @@ int run_potentials(const void *X, const void *Y, int dtype, const float *a, cons
                     break;
                 }
             const bool cold = !warm && s == first;
-            if ((e = launch_lse3_pairwise(sx3, sy3, B, eps[s], iters[s], eps_next, cold, st)))
+            if ((e = pairwise ? launch_lse3_pairwise(sx3, sy3, B, eps[s], iters[s], eps_next,
+                                                     cold, st)
+                              : launch_lse3_split(sx3, sy3, B, split, eps[s], iters[s], eps_next,
+                                                  cold, st)))
                 return hip_fail(e, "iterations");
             continue;
         }

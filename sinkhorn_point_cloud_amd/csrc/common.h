@@ -131,10 +131,14 @@ struct Side3 {
     uint16_t *qrec;   // [B][n_pad][32] bf16 query records at the current eps
     int n, n_pad;
     int *redo = nullptr;   // [B][n_pad / 64] row blocks to recompute after a split merge
+    // [B][n_pad] (tag, bias) words of the split stage launch, zeroed by the
+    // query-record kernel of each stage (nullptr: that path is not used)
+    uint64_t *xch = nullptr;
 };
 constexpr int kRec = 32;  // bf16 slots per record (one 16x16x32 MFMA k-range)
 
-// Query records of one side for the scale of eps (rebuilt when eps changes).
+// Query records of one side for the scale of eps (rebuilt when eps changes);
+// also zeroes s.xch when it is set.
 hipError_t launch_qrec3(Side3 s, int B, float eps, hipStream_t st);
 // Whole stages per pair in one launch (matrix-core scores): used when the batch
 // has at least as many pairs as the device has compute units and each cloud has
@@ -145,6 +149,19 @@ constexpr int kPairMaxPoints = 8192;
 bool lse3_pairwise(int B, int n_pad, int m_pad);
 hipError_t launch_lse3_pairwise(Side3 x, Side3 y, int B, float eps, int iters, float eps_next,
                                 bool cold, hipStream_t st);
+// Whole stages of a small batch of pairs of at most 1024 points (padded), each
+// pair split over work-groups of 16 rows per side, in one launch: used when the
+// batch's work-groups fit on half of the compute units.  Returns the
+// work-groups per pair, or 0 where the path does not apply.  The launch needs
+// x.xch and y.xch, zeroed since the last launch (launch_qrec3 does it).  Its
+// waits are bounded: a pair whose wait ran out gets NaN potentials.
+int lse3_split_parts(int B, int n_pad, int m_pad);
+hipError_t launch_lse3_split(Side3 x, Side3 y, int B, int parts, float eps, int iters,
+                             float eps_next, bool cold, hipStream_t st);
+// Wall-clock limit of each wait of the split stage launch, in microseconds, for
+// the launches that follow (process-wide; below 0: every wait fails at once);
+// returns the previous limit.
+long long lse3_split_set_wait_us(long long us);
 
 // Per-pair center (bounding-box midpoint of both clouds) for the d = 3 path;
 // part holds center3_parts(n, m) * B partial boxes.

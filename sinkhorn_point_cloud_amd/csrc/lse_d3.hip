@@ -40,7 +40,17 @@
 // kernel merges the partial states; on the matrix-core path a third launch
 // recomputes, with exact shifts, the row blocks whose merged sums left the
 // range (it returns at once for every other block).
+//
+// Two stage kernels run every iteration of an eps stage in one launch, for
+// batches where a launch per half-iteration would cost more than its work:
+// lse3p_kernel (one work-group per pair, for batches of at least one pair per
+// compute unit) and lse3s_kernel (a small batch of clouds of at most 1024
+// points, each pair spread over work-groups of 16 rows that hand their new
+// biases to one another between half-iterations).
 #include "common.h"
+
+#include <algorithm>
+#include <atomic>
 
 namespace sk {
 namespace {
@@ -273,8 +283,10 @@ __global__ void pack3_kernel(const T *__restrict__ X, const float *__restrict__ 
 }
 
 // Query records at the scale c of the current eps: q = 2c (x, y, z).
+// With xch set, the side's (tag, bias) words of the split stage launch are
+// zeroed as well.
 __global__ void qrec3_kernel(const float4 *__restrict__ pts, int n_pad, float two_c,
-                             uint16_t *__restrict__ qrec)
+                             uint16_t *__restrict__ qrec, uint64_t *__restrict__ xch)
 {
     const int b = blockIdx.y;
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -283,6 +295,8 @@ __global__ void qrec3_kernel(const float4 *__restrict__ pts, int n_pad, float tw
     const size_t k = (size_t)b * n_pad + i;
     const float4 p = pts[k];
     store_query_record(qrec + k * kRec, two_c * p.x, two_c * p.y, two_c * p.z);
+    if (xch)
+        xch[k] = 0;
 }
 
 // Row result: true potential from the (M, S) state, and the bias of this row
@@ -951,6 +965,265 @@ __global__ __launch_bounds__(kPairWaves *kWave) void lse3p_kernel(Side3 x, Side3
     }
 }
 
+// ---------------------------------------------------------------------------
+// Whole stages of a small batch of small pairs in one launch, each pair split
+// over work-groups (a single pair of 1024 points: 64 of them).  A launch per
+// half-iteration costs more than the half-iteration's own work there (its
+// fixed start and end cost is about 2.3 us; the work on 64 compute units is
+// well under that), so the stage runs in one launch instead:
+// work-group (b, part) owns rows 16 part .. 16 part + 15 of both sides of pair
+// b, keeps both sides' key records in LDS (as the per-pair launch does) and,
+// per half-iteration, streams all keys against its 16 rows, W waves each
+// taking every W-th key tile.  The rows' new biases are what the other
+// work-groups need next: each finished row publishes (tag, bias) as one 64-bit
+// word in `xch`, and the next half-iteration starts by reading every key's
+// word of the other side until it carries that half-iteration's tag, writing
+// the bias pieces into its LDS copy of the records.  The words are read and
+// written with device-scope (relaxed atomic) loads and stores, which are
+// coherent across the XCDs' L2 caches; no other memory is shared within the
+// launch.  A word holds one value of one half-iteration: the producer of the
+// next value for the same row first needs this half-iteration's results of
+// every work-group, each of which has read the word by then, so no value is
+// overwritten before it is read.  Tags count half-iterations from 1 within the
+// launch and the words are zeroed before it (by the query-record kernel of the
+// stage), so a word from an earlier launch never matches.
+//
+// Every wait is bounded by a wall-clock limit (wait_ticks of the constant
+// 100 MHz counter; below 0, every wait fails at once): a work-group whose wait
+// runs out stops waiting for the rest of the launch, publishes NaN biases and,
+// at its end, writes NaN as the potentials of its rows, so every row that
+// depends on the failed wait comes back NaN instead of the launch hanging.
+// The launch needs all of its work-groups resident at once: it takes at most
+// one work-group per two compute units, so that it fits beside other work.  Per row the arithmetic is that of the
+// other matrix-core kernels (shifted stream, merged over the waves, made
+// exact and streamed again when a row's sum leaves the range).
+constexpr int kSplitRows = 16;   // rows of each side per work-group
+
+// Key biases of half-iteration tag - 1, published by every work-group, into
+// the LDS records recs (keys 0 .. nk-1; the padding keys' records keep their
+// bias).  Each thread reads its keys' words together and polls again only
+// those that do not yet carry the tag.
+template <int T>
+__device__ __forceinline__ void split_refresh(uint4 *recs, const uint64_t *xk, int nk,
+                                              unsigned tag, long long wait_ticks, bool &dead)
+{
+    constexpr int kPer = kLdsMaxPoints / T;
+    static_assert(kPer * T == kLdsMaxPoints, "threads divide the key count");
+    uint64_t v[kPer];
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+        const int j = threadIdx.x + e * T;
+        v[e] = j < nk ? __hip_atomic_load(xk + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                      : (uint64_t)tag << 32;
+    }
+    auto ready = [&]() {
+        bool ok = true;
+#pragma unroll
+        for (int e = 0; e < kPer; ++e)
+            ok = ok && (unsigned)(v[e] >> 32) == tag;
+        return ok;
+    };
+    if (!dead && !ready()) {
+        const long long t0 = (long long)wall_clock64();
+        while (true) {
+            if (wait_ticks < 0 || (long long)wall_clock64() - t0 > wait_ticks) {
+                dead = true;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+            for (int e = 0; e < kPer; ++e) {
+                const int j = threadIdx.x + e * T;
+                if ((unsigned)(v[e] >> 32) != tag)
+                    v[e] = __hip_atomic_load(xk + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            if (ready())
+                break;
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+        const int j = threadIdx.x + e * T;
+        if (j < nk)
+            store_key_bias_lds(recs, j, __uint_as_float((unsigned)v[e]));
+    }
+}
+
+// State of one owned row, held by lane l < 16 of wave 0 for row 16 part + l.
+struct SplitRow {
+    float sq, pot, lw;
+};
+
+// One half-iteration of a work-group: its 16 rows of side q against all keys of
+// side k (records in k_lds).  h: the half-iteration's index in the launch
+// (its results carry tag h + 1; for h > 0 the keys' biases are those of tag h).
+template <int W>
+__device__ __forceinline__ void split_half(const Side3 &q, const Side3 &k, int b, int row0,
+                                           bool has_rows, const bf16x8 (&A)[1], SplitRow &st,
+                                           uint4 *k_lds, float2 (*red)[kWave], float *shv,
+                                           int *flag, int *dead_any, int h, bool stale,
+                                           bool last, bool publish, float two_c,
+                                           double eps_ln2, double c_next, long long wait_ticks,
+                                           bool &dead)
+{
+    const int lane = lane_id();
+    const int w = wave_id_uniform();
+    const int kq = lane >> 4, c16 = lane & 15;
+    const int lane_off = c16 * kRec + 8 * kq;
+    const bool fin = w == 0 && lane < kSplitRows;   // the lanes that own a row
+    const int row = row0 + lane;
+    if (h > 0) {
+        if (*dead_any)   // a wait of this work-group already ran out
+            dead = true;
+        split_refresh<W * kWave>(k_lds, k.xch + (size_t)b * k.n_pad, k.n, (unsigned)h,
+                                 wait_ticks, dead);
+        if (dead)
+            *dead_any = 1;
+    }
+    if (fin)
+        shv[lane] = -(0.5f * two_c * (st.sq - st.pot));
+    if (threadIdx.x == 0)
+        *flag = 0;
+    __syncthreads();   // key biases, shifts and the flag are in place
+    if (*dead_any)
+        dead = true;
+    if (!has_rows)
+        return;
+    const uint16_t *kb = k.krec + (size_t)b * k.n_pad * kRec;
+    const int n_tiles = k.n_pad / kTile;
+    const int cnt = w < n_tiles ? (n_tiles - w + W - 1) / W : 0;
+    f32x4 Cn[1], S[1];
+    {
+        const float4 v = *reinterpret_cast<const float4 *>(shv + 4 * kq);
+        Cn[0] = f32x4{v.x, v.y, v.z, v.w};
+        S[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    float M = 0.f, Ssum = 0.f;
+    if (!stale) {
+        shifted_stream<W, 1, true>(A, Cn, S, kb, k.n_pad, lane_off, w, cnt, k_lds);
+        wave_sums<1>(Cn, S, red[w], kq, c16);
+        __syncthreads();
+        if (fin) {
+            M = red[0][lane].x;
+#pragma unroll
+            for (int v = 0; v < W; ++v)
+                Ssum += red[v][lane].y;
+            if (row < q.n && !(Ssum >= kSumLo && Ssum <= kSumHi))
+                *flag = 1;   // benign race: every writer stores 1
+        }
+        __syncthreads();
+        stale = *flag != 0;
+    }
+    if (stale) {
+        exact_shifts<W, 1, true>(A, Cn, S, kb, k.n_pad, lane_off, w, cnt, red, w, kq, c16, k_lds);
+        shifted_stream<W, 1, true>(A, Cn, S, kb, k.n_pad, lane_off, w, cnt, k_lds);
+        wave_sums<1>(Cn, S, red[w], kq, c16);
+        __syncthreads();
+        if (fin) {
+            M = red[0][lane].x;
+            Ssum = 0.f;
+#pragma unroll
+            for (int v = 0; v < W; ++v)
+                Ssum += red[v][lane].y;
+        }
+    }
+    if (fin && row < q.n) {
+        // the arithmetic of finish_row, the state held by the lane
+        const double lse2 = (double)M + (double)lg2(Ssum);
+        const float f = (float)((double)st.sq - lse2 * eps_ln2);
+        st.pot = f;
+        const float beta = st.lw == kNeg ? kNeg : bias_of(c_next, f, st.sq, st.lw);
+        // after a failed wait the row's bias goes out as NaN, so that every
+        // row computed from it is NaN as well
+        const float out = dead ? __builtin_nanf("") : beta;
+        if (publish)
+            __hip_atomic_store(q.xch + (size_t)b * q.n_pad + row,
+                               (uint64_t)(unsigned)(h + 1) << 32 | __float_as_uint(out),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (last) {
+            const size_t pt = (size_t)b * q.n_pad + row;
+            q.pot[(size_t)b * q.n + row] = f;
+            q.pts[pt].w = beta;
+            store_key_bias(q.krec + pt * kRec, beta);
+        }
+    }
+}
+
+template <int W>
+__global__ __launch_bounds__(W *kWave) void lse3s_kernel(Side3 x, Side3 y, int parts, int iters,
+                                                         float two_c, double eps_ln2,
+                                                         double c_next_last, int cold,
+                                                         long long wait_ticks)
+{
+    __shared__ uint4 recs[2][kLdsMaxPoints * kRec / 8];
+    __shared__ __align__(16) float2 red[W][kWave];
+    __shared__ __align__(16) float shv[kSplitRows];
+    __shared__ int flag, dead_any;
+    const int b = blockIdx.x / parts;
+    const int row0 = (blockIdx.x - b * parts) * kSplitRows;
+    const int lane = lane_id();
+    const int w = wave_id_uniform();
+    const Side3 *side[2] = {&x, &y};
+    if (threadIdx.x == 0)
+        dead_any = 0;
+#pragma unroll
+    for (int sd = 0; sd < 2; ++sd) {
+        const uint4 *src =
+            reinterpret_cast<const uint4 *>(side[sd]->krec + (size_t)b * side[sd]->n_pad * kRec);
+        const int chunks = side[sd]->n_pad * (kRec / 8);   // n_pad <= kLdsMaxPoints
+        for (int e = threadIdx.x; e < chunks; e += W * kWave)
+            recs[sd][lds_chunk(e >> 2, e & 3)] = src[e];
+    }
+    // the rows of both sides: query operands (fixed for the stage) in every
+    // wave, the state in the owning lanes of wave 0
+    const bool has_x = row0 < x.n_pad, has_y = row0 < y.n_pad;
+    const int lane_off = (lane & 15) * kRec + 8 * (lane >> 4);
+    bf16x8 Ax[1], Ay[1];
+    if (has_x)
+        load_rows<1>(Ax, x.qrec + ((size_t)b * x.n_pad + row0) * kRec, lane_off);
+    if (has_y)
+        load_rows<1>(Ay, y.qrec + ((size_t)b * y.n_pad + row0) * kRec, lane_off);
+    SplitRow rx{0.f, 0.f, 0.f}, ry{0.f, 0.f, 0.f};
+    if (w == 0 && lane < kSplitRows) {
+        const int row = row0 + lane;
+        if (has_x) {
+            const float4 p = x.pts[(size_t)b * x.n_pad + row];
+            rx.sq = sq3(p.x, p.y, p.z);
+            if (row < x.n) {
+                rx.pot = x.pot[(size_t)b * x.n + row];
+                rx.lw = x.l2w[(size_t)b * x.n + row];
+            }
+        }
+        if (has_y) {
+            const float4 p = y.pts[(size_t)b * y.n_pad + row];
+            ry.sq = sq3(p.x, p.y, p.z);
+            if (row < y.n) {
+                ry.pot = y.pot[(size_t)b * y.n + row];
+                ry.lw = y.l2w[(size_t)b * y.n + row];
+            }
+        }
+    }
+    bool dead = false;
+    const double c_same = 0.5 * (double)two_c;
+    for (int it = 0; it < iters; ++it) {
+        const bool stale = cold && it == 0;
+        const bool last = it + 1 == iters;
+        split_half<W>(x, y, b, row0, has_x, Ax, rx, recs[1], red, shv, &flag, &dead_any, 2 * it,
+                      stale, last, true, two_c, eps_ln2, c_same, wait_ticks, dead);
+        split_half<W>(y, x, b, row0, has_y, Ay, ry, recs[0], red, shv, &flag, &dead_any,
+                      2 * it + 1, stale, last, !last, two_c, eps_ln2,
+                      last ? c_next_last : c_same, wait_ticks, dead);
+    }
+    __syncthreads();
+    if (dead_any && w == 0 && lane < kSplitRows) {
+        const int row = row0 + lane;
+        if (has_x && row < x.n)
+            x.pot[(size_t)b * x.n + row] = __builtin_nanf("");
+        if (has_y && row < y.n)
+            y.pot[(size_t)b * y.n + row] = __builtin_nanf("");
+    }
+}
+
 // Merge of the split partials of every row.  Matrix-core partials of a row
 // share one shift (vector-pass partials are exact states), so the merge is a
 // sum.  With redo, a row whose merged sum left [2^-64, 2^100] is not finished;
@@ -1102,7 +1375,7 @@ hipError_t launch_qrec3(Side3 s, int B, float eps, hipStream_t st)
 {
     dim3 grid(ceil_div(s.n_pad, 256), B);
     hipLaunchKernelGGL(qrec3_kernel, grid, dim3(256), 0, st, (const float4 *)s.pts, s.n_pad,
-                       2.0f * scale_of(eps), s.qrec);
+                       2.0f * scale_of(eps), s.qrec, s.xch);
     return hipGetLastError();
 }
 
@@ -1127,6 +1400,43 @@ hipError_t launch_lse3_pairwise(Side3 x, Side3 y, int B, float eps, int iters, f
         hipLaunchKernelGGL(lse3p_kernel<false>, dim3(B), dim3(kPairWaves * kWave), 0, st, x, y,
                            iters, 2.0f * c, 1.0 / (double)c, (double)scale_of(eps_next),
                            cold ? 1 : 0);
+    return hipGetLastError();
+}
+
+constexpr int kSplitWaves = 8;   // waves per work-group of the split stage launch
+std::atomic<long long> g_split_wait_us{1000000};
+
+long long lse3_split_set_wait_us(long long us) { return g_split_wait_us.exchange(us); }
+
+int lse3_split_parts(int B, int n_pad, int m_pad)
+{
+    if (n_pad > kLdsMaxPoints || m_pad > kLdsMaxPoints)
+        return 0;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    const int parts = std::max(n_pad, m_pad) / kSplitRows;
+    return 2L * B * parts <= cus ? parts : 0;
+}
+
+hipError_t launch_lse3_split(Side3 x, Side3 y, int B, int parts, float eps, int iters,
+                             float eps_next, bool cold, hipStream_t st)
+{
+    if (!x.xch || !y.xch || x.n_pad > kLdsMaxPoints || y.n_pad > kLdsMaxPoints ||
+        parts * kSplitRows < std::max(x.n_pad, y.n_pad))
+        return hipErrorInvalidValue;
+    int dev = 0, khz = 0;
+    hipError_t e;
+    if ((e = hipGetDevice(&dev)) != hipSuccess ||
+        (e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev)) != hipSuccess)
+        return e;
+    const long long us = g_split_wait_us.load();
+    const long long ticks = us < 0 ? -1 : us * (long long)khz / 1000;
+    const float c = scale_of(eps);
+    hipLaunchKernelGGL(lse3s_kernel<kSplitWaves>, dim3(B * parts), dim3(kSplitWaves * kWave), 0,
+                       st, x, y, parts, iters, 2.0f * c, 1.0 / (double)c,
+                       (double)scale_of(eps_next), cold ? 1 : 0, ticks);
     return hipGetLastError();
 }
 

@@ -202,3 +202,8 @@ extern "C" int sinkhorn_probe_rates(int kind, int blocks, int iters, float *sink
     }
     return hipGetLastError() == hipSuccess ? SK_OK : SK_ERR_HIP;
 }
+
+extern "C" long long sinkhorn_probe_wait_limit(long long microseconds)
+{
+    return lse3_split_set_wait_us(microseconds);
+}

@@ -325,9 +325,11 @@ def test_plan_buffer_checks():
 
 def test_rate_probe_is_declared_exported_and_checks_arguments(lib):
     text = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
-    assert re.findall(r"\b(sinkhorn_\w+)\s*\(", text) == ["sinkhorn_probe_rates"]
+    names = re.findall(r"\b(sinkhorn_\w+)\s*\(", text)
+    assert names == ["sinkhorn_probe_rates", "sinkhorn_probe_wait_limit"]
     out = os.popen(f"nm -D --defined-only {sk.library_path()}").read()
-    assert re.search(r"\bT sinkhorn_probe_rates$", out, flags=re.M)
+    for name in names:
+        assert re.search(rf"\bT {name}$", out, flags=re.M), name
     f = lib.sinkhorn_probe_rates
     f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                   ctypes.c_void_p, ctypes.c_void_p]

@@ -259,6 +259,69 @@ def test_batch_of_many_pairs_from_a_stale_start():
         assert rel_inf(host(g)[p], go[p], eps) <= 1e-4
 
 
+# A small batch of clouds of at most 1024 points (padded) whose work-groups fit
+# on half of the compute units runs each stage in one launch: work-group (pair,
+# part) owns 16 rows of each side and the work-groups hand their new biases to
+# one another between half-iterations through bounded waits.
+SPLIT = [  # (B, n, m, weights, zero weights, eps, iters)
+    # one pair of 1024 points (64 work-groups), eps falling between stages
+    (1, 1024, 1024, "uniform", 0, [0.5, 0.05, 0.01], [3, 5, 8]),
+    # a stage of one iteration (its first f-update is the cold start's exact
+    # pass and its g-update the stage's last), ragged sides, zero weights
+    (2, 1000, 700, "dirichlet", 3, [0.1, 0.02], [1, 6]),
+    # most work-groups own no row of the short side
+    (2, 17, 650, "dirichlet", 0, [0.2, 0.03], [4, 6]),
+    (1, 1024, 16, "dirichlet", 0, [0.05], [7]),
+]
+
+
+@pytest.mark.parametrize("B,n,m,w,zw,eps,iters", SPLIT)
+def test_split_stage_launch_matches_oracle(B, n, m, w, zw, eps, iters):
+    c = workloads.random_case(700 + n + m, B, n, m, 3, weights=w, zero_weights=zw)
+    check_potentials(c, eps, iters)
+
+
+def test_split_stage_launch_from_a_stale_start_and_far_from_the_origin():
+    # warm start from potentials far off, clouds far from the origin at small
+    # eps: every work-group finds its shifts stale on the first pass
+    c = workloads.random_case(708, 1, 900, 1000, 3, weights="dirichlet", spread=4.0)
+    c = dict(c, X=c["X"] + np.float32(10.0), Y=c["Y"] + np.float32(10.0))
+    f0 = np.full((1, 900), 30.0, dtype=np.float32)
+    g0 = np.full((1, 1000), -25.0, dtype=np.float32)
+    eps = [0.01, 0.003]
+    f, g, _ = run_gpu(c, eps, [2, 3], f0=dev(f0), g0=dev(g0))
+    fo, go = oracle.potentials(c["X"], c["Y"], c["a"], c["b"], eps=np.float32(eps), iters=[2, 3],
+                               f0=f0.astype(np.float64), g0=g0.astype(np.float64))
+    assert rel_inf(host(f), fo, eps[-1]) <= 1e-4
+    assert rel_inf(host(g), go, eps[-1]) <= 1e-4
+
+
+def test_split_stage_launch_is_deterministic():
+    c = workloads.random_case(709, 2, 1000, 1024, 3, weights="dirichlet")
+    r1 = run_gpu(c, [0.3, 0.02], [3, 8])
+    r2 = run_gpu(c, [0.3, 0.02], [3, 8])
+    for u, v in zip(r1, r2):
+        assert torch.equal(u, v)
+
+
+def test_split_stage_launch_wait_that_runs_out_gives_nan():
+    # the hand-over waits are bounded: with the limit set so that every wait
+    # fails at once (the host-side test hook), the launch still ends and the
+    # potentials come back NaN; with the default limit the same call is exact
+    import ctypes
+    lib = sk.load_library()
+    lib.sinkhorn_probe_wait_limit.argtypes = [ctypes.c_longlong]
+    lib.sinkhorn_probe_wait_limit.restype = ctypes.c_longlong
+    c = workloads.random_case(710, 1, 1024, 1000, 3, weights="dirichlet")
+    prev = lib.sinkhorn_probe_wait_limit(-1)
+    try:
+        f, g, _ = run_gpu(c, [0.05], [4])
+    finally:
+        assert lib.sinkhorn_probe_wait_limit(prev) == -1
+    assert torch.isnan(f).all() and torch.isnan(g).all()
+    check_potentials(c, [0.05], [4])
+
+
 def test_schedule_with_empty_stages_and_zero_iterations():
     c = workloads.random_case(5, 1, 90, 70, 3, weights="dirichlet")
     check_potentials(c, [0.5, 0.2, 0.05], [0, 6, 8])
@@ -266,12 +329,12 @@ def test_schedule_with_empty_stages_and_zero_iterations():
     assert torch.all(f == 0) and torch.all(g == 0)
 
 
-@pytest.mark.parametrize("B,n,m", [(256, 130, 140), (1, 300, 20000)])
+@pytest.mark.parametrize("B,n,m", [(256, 130, 140), (1, 300, 20000), (1, 800, 1000)])
 def test_empty_stages_on_per_pair_and_split_launches(B, n, m):
     # empty stages before, between and after others: the cold start's exact
     # shifts belong to the first stage that runs, and each stage hands the next
     # running stage's eps to its last g-update (per-pair stage launches; split
-    # key ranges with merge marks and repair)
+    # key ranges with merge marks and repair; split stage launches)
     c = workloads.random_case(506 + B, B, n, m, 3, weights="dirichlet", spread=2.0)
     check_potentials(c, [1.0, 0.1, 0.05, 0.03, 0.02], [0, 3, 0, 4, 0])
 
@@ -1178,13 +1241,15 @@ def test_work_follows_the_callers_stream():
         assert torch.equal(u, v)
 
 
-@pytest.mark.parametrize("shape", ["batch", "split_keys_stale", "per_pair_stages"])
+@pytest.mark.parametrize("shape", ["batch", "split_keys_stale", "per_pair_stages",
+                                   "split_stages"])
 def test_potentials_replay_from_a_captured_graph(shape):
     # the potentials entry point launches kernels only (no allocation, copy or
     # wait), so a caller can capture it; every replay equals the eager result.
     # Shapes: one launch per half-iteration; split key ranges whose merged rows
     # go stale (merge marks and repair launch inside the graph); whole stages
-    # per pair (cold start with exact shifts)
+    # per pair (cold start with exact shifts); whole stages of one pair split
+    # over work-groups (the hand-over words zeroed by a kernel in each stage)
     if shape == "batch":
         B, n, m, seed, sched = 2, 700, 600, 62, dict(eps=[0.3, 0.05, 0.02], iters=[3, 5, 10])
         c = workloads.random_case(seed, B, n, m, 3, weights="dirichlet")
@@ -1192,8 +1257,11 @@ def test_potentials_replay_from_a_captured_graph(shape):
         B, n, m, seed, sched = 1, 300, 20000, 64, dict(eps=[0.05, 0.003], iters=[2, 3])
         c = workloads.random_case(seed, B, n, m, 3, weights="dirichlet", spread=4.0)
         c = dict(c, X=c["X"] + np.float32(10.0), Y=c["Y"] + np.float32(10.0))
-    else:
+    elif shape == "per_pair_stages":
         B, n, m, seed, sched = 256, 130, 140, 65, dict(eps=[0.1, 0.02], iters=[2, 4])
+        c = workloads.random_case(seed, B, n, m, 3, weights="dirichlet")
+    else:
+        B, n, m, seed, sched = 1, 1000, 900, 66, dict(eps=[0.1, 0.1, 0.02], iters=[1, 3, 4])
         c = workloads.random_case(seed, B, n, m, 3, weights="dirichlet")
     X, Y = points(c)
     a, b = dev(c["a"]), dev(c["b"])
