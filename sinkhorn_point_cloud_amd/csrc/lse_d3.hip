@@ -976,9 +976,10 @@ __global__ __launch_bounds__(kPairWaves *kWave) void lse3p_kernel(Side3 x, Side3
 // per half-iteration, streams all keys against its 16 rows, W waves each
 // taking every W-th key tile.  The rows' new biases are what the other
 // work-groups need next: each finished row publishes (tag, bias) as one 64-bit
-// word in `xch`, and the next half-iteration starts by reading every key's
-// word of the other side until it carries that half-iteration's tag, writing
-// the bias pieces into its LDS copy of the records.  The words are read and
+// word in `xch`, and in the next half-iteration each wave reads the words of
+// the keys of its own tiles until they carry that half-iteration's tag,
+// writing the bias pieces into the LDS copy of the records, and streams them
+// at once: the waves meet only to merge their sums.  The words are read and
 // written with device-scope (relaxed atomic) loads and stores, which are
 // coherent across the XCDs' L2 caches; no other memory is shared within the
 // launch.  A word holds one value of one half-iteration: the producer of the
@@ -999,22 +1000,29 @@ __global__ __launch_bounds__(kPairWaves *kWave) void lse3p_kernel(Side3 x, Side3
 // exact and streamed again when a row's sum leaves the range).
 constexpr int kSplitRows = 16;   // rows of each side per work-group
 
-// Key biases of half-iteration tag - 1, published by every work-group, into
-// the LDS records recs (keys 0 .. nk-1; the padding keys' records keep their
-// bias).  Each thread reads its keys' words together and polls again only
-// those that do not yet carry the tag.
-template <int T>
-__device__ __forceinline__ void split_refresh(uint4 *recs, const uint64_t *xk, int nk,
-                                              unsigned tag, long long wait_ticks, bool &dead)
+// Key biases of half-iteration tag - 1 for the keys that wave w streams (the 16
+// keys of each of its tiles w, w + W, ...; cnt tiles), from the words that
+// every work-group publishes, into the LDS records recs (keys 0 .. nk-1; the
+// padding keys' records keep their bias).  Each lane reads its keys' words
+// together and polls again only those that do not yet carry the tag.
+template <int W>
+__device__ __forceinline__ void split_refresh(uint4 *recs, const uint64_t *xk, int nk, int w,
+                                              int cnt, unsigned tag, long long wait_ticks,
+                                              bool &dead)
 {
-    constexpr int kPer = kLdsMaxPoints / T;
-    static_assert(kPer * T == kLdsMaxPoints, "threads divide the key count");
+    constexpr int kMaxTiles = (kLdsMaxPoints / kTile + W - 1) / W;   // tiles of one wave
+    constexpr int kPer = kMaxTiles * kTile / kWave;                  // keys of one lane
+    static_assert(kPer >= 1 && kPer * kWave == kMaxTiles * kTile, "lanes divide the keys");
+    const int lane = lane_id();
     uint64_t v[kPer];
+    int key[kPer];
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
-        const int j = threadIdx.x + e * T;
-        v[e] = j < nk ? __hip_atomic_load(xk + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                      : (uint64_t)tag << 32;
+        const int i = lane + e * kWave;   // the wave's i-th key: tile i / 16 of its list
+        const int j = (w + (i / kTile) * W) * kTile + i % kTile;
+        key[e] = i / kTile < cnt && j < nk ? j : -1;
+        v[e] = key[e] >= 0 ? __hip_atomic_load(xk + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                           : (uint64_t)tag << 32;
     }
     auto ready = [&]() {
         bool ok = true;
@@ -1032,110 +1040,107 @@ __device__ __forceinline__ void split_refresh(uint4 *recs, const uint64_t *xk, i
             }
             __builtin_amdgcn_s_sleep(1);
 #pragma unroll
-            for (int e = 0; e < kPer; ++e) {
-                const int j = threadIdx.x + e * T;
+            for (int e = 0; e < kPer; ++e)
                 if ((unsigned)(v[e] >> 32) != tag)
-                    v[e] = __hip_atomic_load(xk + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
+                    v[e] = __hip_atomic_load(xk + key[e], __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
             if (ready())
                 break;
         }
     }
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) {
-        const int j = threadIdx.x + e * T;
-        if (j < nk)
-            store_key_bias_lds(recs, j, __uint_as_float((unsigned)v[e]));
-    }
+    for (int e = 0; e < kPer; ++e)
+        if (key[e] >= 0)
+            store_key_bias_lds(recs, key[e], __uint_as_float((unsigned)v[e]));
 }
-
-// State of one owned row, held by lane l < 16 of wave 0 for row 16 part + l.
-struct SplitRow {
-    float sq, pot, lw;
-};
 
 // One half-iteration of a work-group: its 16 rows of side q against all keys of
 // side k (records in k_lds).  h: the half-iteration's index in the launch
 // (its results carry tag h + 1; for h > 0 the keys' biases are those of tag h).
+// The rows' state (squared norm, potential, log2 weight) is in LDS (q_sq,
+// q_pot, q_lw), the potentials written by wave 0 as it finishes the rows.
+// Each wave refreshes the biases of its own tiles' keys and forms the shifts
+// itself, so the only barrier is the one before the merge of the waves' sums
+// (red: this half-iteration's buffer of two, so that the waves may start the
+// next half-iteration while wave 0 merges).  A row whose merged sum leaves the
+// range after a shifted pass is recomputed by wave 0 alone over all keys with
+// exact shifts (the records stay in place until every wave has passed the next
+// half-iteration's barrier, which wave 0 reaches only after this).
 template <int W>
 __device__ __forceinline__ void split_half(const Side3 &q, const Side3 &k, int b, int row0,
-                                           bool has_rows, const bf16x8 (&A)[1], SplitRow &st,
-                                           uint4 *k_lds, float2 (*red)[kWave], float *shv,
-                                           int *flag, int *dead_any, int h, bool stale,
-                                           bool last, bool publish, float two_c,
-                                           double eps_ln2, double c_next, long long wait_ticks,
-                                           bool &dead)
+                                           bool has_rows, const bf16x8 (&A)[1],
+                                           const float *q_sq, float *q_pot, const float *q_lw,
+                                           uint4 *k_lds, float2 (*red)[kWave],
+                                           float (*shv)[kSplitRows], float2 *redo_red,
+                                           int *dead_any, int h, bool stale, bool last,
+                                           bool publish, float two_c, double eps_ln2,
+                                           double c_next, long long wait_ticks, bool &dead)
 {
+    if (!has_rows)
+        return;   // the whole work-group: it holds no row of side q
     const int lane = lane_id();
     const int w = wave_id_uniform();
     const int kq = lane >> 4, c16 = lane & 15;
     const int lane_off = c16 * kRec + 8 * kq;
-    const bool fin = w == 0 && lane < kSplitRows;   // the lanes that own a row
     const int row = row0 + lane;
+    const int n_tiles = k.n_pad / kTile;
+    const int cnt = w < n_tiles ? (n_tiles - w + W - 1) / W : 0;
     if (h > 0) {
         if (*dead_any)   // a wait of this work-group already ran out
             dead = true;
-        split_refresh<W * kWave>(k_lds, k.xch + (size_t)b * k.n_pad, k.n, (unsigned)h,
-                                 wait_ticks, dead);
+        split_refresh<W>(k_lds, k.xch + (size_t)b * k.n_pad, k.n, w, cnt, (unsigned)h,
+                         wait_ticks, dead);
         if (dead)
             *dead_any = 1;
     }
-    if (fin)
-        shv[lane] = -(0.5f * two_c * (st.sq - st.pot));
-    if (threadIdx.x == 0)
-        *flag = 0;
-    __syncthreads();   // key biases, shifts and the flag are in place
-    if (*dead_any)
-        dead = true;
-    if (!has_rows)
-        return;
-    const uint16_t *kb = k.krec + (size_t)b * k.n_pad * kRec;
-    const int n_tiles = k.n_pad / kTile;
-    const int cnt = w < n_tiles ? (n_tiles - w + W - 1) / W : 0;
+    if (lane < kSplitRows)
+        shv[w][lane] = -(0.5f * two_c * (q_sq[lane] - q_pot[lane]));
+    __builtin_amdgcn_wave_barrier();   // a wave's LDS accesses complete in order
     f32x4 Cn[1], S[1];
-    {
-        const float4 v = *reinterpret_cast<const float4 *>(shv + 4 * kq);
-        Cn[0] = f32x4{v.x, v.y, v.z, v.w};
-        S[0] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    float M = 0.f, Ssum = 0.f;
-    if (!stale) {
-        shifted_stream<W, 1, true>(A, Cn, S, kb, k.n_pad, lane_off, w, cnt, k_lds);
-        wave_sums<1>(Cn, S, red[w], kq, c16);
-        __syncthreads();
-        if (fin) {
-            M = red[0][lane].x;
-#pragma unroll
-            for (int v = 0; v < W; ++v)
-                Ssum += red[v][lane].y;
-            if (row < q.n && !(Ssum >= kSumLo && Ssum <= kSumHi))
-                *flag = 1;   // benign race: every writer stores 1
-        }
-        __syncthreads();
-        stale = *flag != 0;
-    }
-    if (stale) {
+    const float4 sh = *reinterpret_cast<const float4 *>(&shv[w][4 * kq]);
+    Cn[0] = f32x4{sh.x, sh.y, sh.z, sh.w};
+    S[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const uint16_t *kb = k.krec + (size_t)b * k.n_pad * kRec;
+    if (stale)
         exact_shifts<W, 1, true>(A, Cn, S, kb, k.n_pad, lane_off, w, cnt, red, w, kq, c16, k_lds);
-        shifted_stream<W, 1, true>(A, Cn, S, kb, k.n_pad, lane_off, w, cnt, k_lds);
-        wave_sums<1>(Cn, S, red[w], kq, c16);
-        __syncthreads();
-        if (fin) {
-            M = red[0][lane].x;
-            Ssum = 0.f;
+    shifted_stream<W, 1, true>(A, Cn, S, kb, k.n_pad, lane_off, w, cnt, k_lds);
+    wave_sums<1>(Cn, S, red[w], kq, c16);
+    __syncthreads();   // every wave's sums are in red
+    if (w != 0)
+        return;
+    float M = 0.f, Ssum = 0.f;
+    bool bad = false;
+    if (lane < kSplitRows) {
+        M = red[0][lane].x;
 #pragma unroll
-            for (int v = 0; v < W; ++v)
-                Ssum += red[v][lane].y;
-        }
+        for (int v = 0; v < W; ++v)
+            Ssum += red[v][lane].y;
+        bad = row < q.n && !(Ssum >= kSumLo && Ssum <= kSumHi);
     }
-    if (fin && row < q.n) {
-        // the arithmetic of finish_row, the state held by the lane
+    if (!stale && __ballot(bad) != 0) {
+        Cn[0] = f32x4{sh.x, sh.y, sh.z, sh.w};
+        S[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+        exact_shifts<1, 1, true>(A, Cn, S, kb, k.n_pad, lane_off, 0, n_tiles, nullptr, 0, kq, c16,
+                                 k_lds);
+        shifted_stream<1, 1, true>(A, Cn, S, kb, k.n_pad, lane_off, 0, n_tiles, k_lds);
+        wave_sums<1>(Cn, S, redo_red, kq, c16);
+        __builtin_amdgcn_wave_barrier();
+        if (lane < kSplitRows) {
+            M = redo_red[lane].x;
+            Ssum = redo_red[lane].y;
+        }
+        __builtin_amdgcn_wave_barrier();   // redo_red is written again later
+    }
+    if (lane < kSplitRows && row < q.n) {
+        // the arithmetic of finish_row, the state in LDS
+        const float sq = q_sq[lane], lw = q_lw[lane];
         const double lse2 = (double)M + (double)lg2(Ssum);
-        const float f = (float)((double)st.sq - lse2 * eps_ln2);
-        st.pot = f;
-        const float beta = st.lw == kNeg ? kNeg : bias_of(c_next, f, st.sq, st.lw);
+        const float f = (float)((double)sq - lse2 * eps_ln2);
+        q_pot[lane] = f;
+        const float beta = lw == kNeg ? kNeg : bias_of(c_next, f, sq, lw);
         // after a failed wait the row's bias goes out as NaN, so that every
         // row computed from it is NaN as well
-        const float out = dead ? __builtin_nanf("") : beta;
+        const float out = dead || *dead_any ? __builtin_nanf("") : beta;
         if (publish)
             __hip_atomic_store(q.xch + (size_t)b * q.n_pad + row,
                                (uint64_t)(unsigned)(h + 1) << 32 | __float_as_uint(out),
@@ -1156,9 +1161,12 @@ __global__ __launch_bounds__(W *kWave) void lse3s_kernel(Side3 x, Side3 y, int p
                                                          long long wait_ticks)
 {
     __shared__ uint4 recs[2][kLdsMaxPoints * kRec / 8];
-    __shared__ __align__(16) float2 red[W][kWave];
-    __shared__ __align__(16) float shv[kSplitRows];
-    __shared__ int flag, dead_any;
+    __shared__ __align__(16) float2 red[2][W][kWave];
+    __shared__ __align__(16) float shv[W][kSplitRows];
+    __shared__ __align__(16) float2 redo_red[kWave];
+    // the rows' state, per side: squared norm, potential, log2 weight
+    __shared__ float sqs[2][kSplitRows], pots[2][kSplitRows], lws[2][kSplitRows];
+    __shared__ int dead_any;
     const int b = blockIdx.x / parts;
     const int row0 = (blockIdx.x - b * parts) * kSplitRows;
     const int lane = lane_id();
@@ -1173,9 +1181,23 @@ __global__ __launch_bounds__(W *kWave) void lse3s_kernel(Side3 x, Side3 y, int p
         const int chunks = side[sd]->n_pad * (kRec / 8);   // n_pad <= kLdsMaxPoints
         for (int e = threadIdx.x; e < chunks; e += W * kWave)
             recs[sd][lds_chunk(e >> 2, e & 3)] = src[e];
+        if (threadIdx.x < kSplitRows) {
+            const int row = row0 + threadIdx.x;
+            float sq = 0.f, pot = 0.f, lw = 0.f;
+            if (row < side[sd]->n_pad) {
+                const float4 p = side[sd]->pts[(size_t)b * side[sd]->n_pad + row];
+                sq = sq3(p.x, p.y, p.z);
+                if (row < side[sd]->n) {
+                    pot = side[sd]->pot[(size_t)b * side[sd]->n + row];
+                    lw = side[sd]->l2w[(size_t)b * side[sd]->n + row];
+                }
+            }
+            sqs[sd][threadIdx.x] = sq;
+            pots[sd][threadIdx.x] = pot;
+            lws[sd][threadIdx.x] = lw;
+        }
     }
-    // the rows of both sides: query operands (fixed for the stage) in every
-    // wave, the state in the owning lanes of wave 0
+    // the rows' query operands (fixed for the stage), in every wave
     const bool has_x = row0 < x.n_pad, has_y = row0 < y.n_pad;
     const int lane_off = (lane & 15) * kRec + 8 * (lane >> 4);
     bf16x8 Ax[1], Ay[1];
@@ -1183,35 +1205,17 @@ __global__ __launch_bounds__(W *kWave) void lse3s_kernel(Side3 x, Side3 y, int p
         load_rows<1>(Ax, x.qrec + ((size_t)b * x.n_pad + row0) * kRec, lane_off);
     if (has_y)
         load_rows<1>(Ay, y.qrec + ((size_t)b * y.n_pad + row0) * kRec, lane_off);
-    SplitRow rx{0.f, 0.f, 0.f}, ry{0.f, 0.f, 0.f};
-    if (w == 0 && lane < kSplitRows) {
-        const int row = row0 + lane;
-        if (has_x) {
-            const float4 p = x.pts[(size_t)b * x.n_pad + row];
-            rx.sq = sq3(p.x, p.y, p.z);
-            if (row < x.n) {
-                rx.pot = x.pot[(size_t)b * x.n + row];
-                rx.lw = x.l2w[(size_t)b * x.n + row];
-            }
-        }
-        if (has_y) {
-            const float4 p = y.pts[(size_t)b * y.n_pad + row];
-            ry.sq = sq3(p.x, p.y, p.z);
-            if (row < y.n) {
-                ry.pot = y.pot[(size_t)b * y.n + row];
-                ry.lw = y.l2w[(size_t)b * y.n + row];
-            }
-        }
-    }
+    __syncthreads();   // records and row state are in LDS
     bool dead = false;
     const double c_same = 0.5 * (double)two_c;
     for (int it = 0; it < iters; ++it) {
         const bool stale = cold && it == 0;
         const bool last = it + 1 == iters;
-        split_half<W>(x, y, b, row0, has_x, Ax, rx, recs[1], red, shv, &flag, &dead_any, 2 * it,
-                      stale, last, true, two_c, eps_ln2, c_same, wait_ticks, dead);
-        split_half<W>(y, x, b, row0, has_y, Ay, ry, recs[0], red, shv, &flag, &dead_any,
-                      2 * it + 1, stale, last, !last, two_c, eps_ln2,
+        split_half<W>(x, y, b, row0, has_x, Ax, sqs[0], pots[0], lws[0], recs[1], red[0], shv,
+                      redo_red, &dead_any, 2 * it, stale, last, true, two_c, eps_ln2, c_same,
+                      wait_ticks, dead);
+        split_half<W>(y, x, b, row0, has_y, Ay, sqs[1], pots[1], lws[1], recs[0], red[1], shv,
+                      redo_red, &dead_any, 2 * it + 1, stale, last, !last, two_c, eps_ln2,
                       last ? c_next_last : c_same, wait_ticks, dead);
     }
     __syncthreads();
