@@ -146,8 +146,8 @@ int sinkhorn_potentials(const void *X, const void *Y, int dtype,
  *
  * Sizes whose workspace (sinkhorn_workspace_bytes(SK_OP_POTENTIALS, ...)) is
  * above SK_NOALLOC_SCRATCH_BYTES return SK_ERR_WORKSPACE with nothing written
- * (one pair of 65536 x 65536 points at d = 3 needs about 22 MiB; 256 pairs of
- * 1024 x 1024, 88 MiB).  The call allocates nothing (no hipMalloc or
+ * (one pair of 65536 x 65536 points at d = 3 needs about 23 MiB; 256 pairs of
+ * 1024 x 1024, 92 MiB).  The call allocates nothing (no hipMalloc or
  * allocating library routine) and launches the kernels of sinkhorn_potentials,
  * with the same results.  All calls on one GPU share its array: two calls that
  * overlap on one GPU (other streams, other threads) race and give undefined
