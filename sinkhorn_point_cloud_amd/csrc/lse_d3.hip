@@ -51,6 +51,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 namespace sk {
 namespace {
@@ -590,19 +591,59 @@ __device__ __forceinline__ float row16_max(float v)
     return v;
 }
 
-// Row sums of one wave's states, with the row's shift, into red_w[row].
-template <int G = kGroups>
+// Row sums of one wave's states, with the row's shift, into red_w[row].  The
+// 16 lanes of a DPP row hold the same rows (16 G of them) for different key
+// columns.  With G = 4 the sums are a reduce-scatter over those 16 lanes: four
+// pairings (lanes i and 15 - i, then i and 7 - i within each half row, then
+// i ^ 1, then i ^ 2) each halve the values a lane carries, the lane keeping
+// the half its bit of the pairing selects and adding the partner's copy of it,
+// so that every lane ends with one row's sum (and selects that row's shift)
+// and writes it: 45 selects and 15 adds instead of 64 adds, 16 negations and
+// 16 masked stores.  It pays where a wave's rows are short (sphere-2k's 32
+// tiles per wave: 3% off the half-iteration); with 8 waves on long rows
+// (gmm-64k) the sum is a rounding error of the launch and that kernel keeps
+// the all-lane sums (kScatter false), which measured 0.9% faster there.  With
+// G = 1 every lane sums all 16 lanes of each row.
+template <int G = kGroups, bool kScatter = true>
 __device__ __forceinline__ void wave_sums(const f32x4 (&Cn)[G], const f32x4 (&S)[G],
                                           float2 *red_w, int kq, int c16)
 {
+    if constexpr (G == 4 && kScatter) {
+        float x[16], m[16];
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+        for (int g = 0; g < 4; ++g)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float Sr = row16_sum(S[g][r]);
-            if (c16 == 0)
-                red_w[16 * g + 4 * kq + r] = make_float2(-Cn[g][r], Sr);
-        }
+            for (int r = 0; r < 4; ++r) {
+                x[4 * g + r] = S[g][r];
+                m[4 * g + r] = -Cn[g][r];
+            }
+        const bool b3 = c16 & 8, b2 = c16 & 4, b1 = c16 & 2, b0 = c16 & 1;
+        auto step = [&](auto ctrl, int half, bool hi) {
+            constexpr int kCtrl = decltype(ctrl)::value;
+#pragma unroll
+            for (int v = 0; v < half; ++v) {
+                const float keep = hi ? x[v + half] : x[v];
+                const float send = hi ? x[v] : x[v + half];
+                x[v] = keep + dpp_move<kCtrl>(send);
+                m[v] = hi ? m[v + half] : m[v];
+            }
+        };
+        step(std::integral_constant<int, kDppMirror>{}, 8, b3);
+        step(std::integral_constant<int, kDppHalfMirror>{}, 4, b2);
+        step(std::integral_constant<int, kDppXor1>{}, 2, b0);
+        step(std::integral_constant<int, kDppXor2>{}, 1, b1);
+        const int v = 8 * b3 + 4 * b2 + 2 * b0 + b1;   // the row value this lane holds
+        red_w[16 * (v >> 2) + 4 * kq + (v & 3)] = make_float2(m[0], x[0]);
+    } else {
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float Sr = row16_sum(S[g][r]);
+                if (c16 == 0)
+                    red_w[16 * g + 4 * kq + r] = make_float2(-Cn[g][r], Sr);
+            }
+    }
 }
 
 // Makes the shifts of a 64-row block exact: the maximum of s - M over the
@@ -728,7 +769,7 @@ __global__ __launch_bounds__(W *kWave) void lse3m_kernel(
     if (redo == nullptr) {
         shifted_stream<W, G>(A, Cn, S, kb, nk_pad, lane_off, first, cnt);
         // every partial of a row has the same shift: the merge is a sum
-        wave_sums<G>(Cn, S, red[w], kq, c16);
+        wave_sums<G, (W < 8)>(Cn, S, red[w], kq, c16);
         if (threadIdx.x == 0)
             stale = 0;
         __syncthreads();
@@ -756,7 +797,7 @@ __global__ __launch_bounds__(W *kWave) void lse3m_kernel(
 
     exact_shifts<W, G>(A, Cn, S, kb, nk_pad, lane_off, first, cnt, red, w, kq, c16);
     shifted_stream<W, G>(A, Cn, S, kb, nk_pad, lane_off, first, cnt);
-    wave_sums<G>(Cn, S, red[w], kq, c16);
+    wave_sums<G, (W < 8)>(Cn, S, red[w], kq, c16);
     __syncthreads();
     if (w != 0 || !mine)
         return;
