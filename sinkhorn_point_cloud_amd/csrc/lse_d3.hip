@@ -512,11 +512,33 @@ __device__ __forceinline__ void key_stream(const bf16x8 (&A)[G], const f32x4 (&C
             __builtin_amdgcn_sched_group_barrier(0x002, 8 * G, 0);   // then the vector work
         }
     };
+    // From LDS, the tiles of the groups whose loads all stay below cnt are read
+    // unclamped (the index affine in k: one address add per group of three, the
+    // rest immediate offsets), the last group with the clamp.
+    auto key_in = [&](int k) {
+        return __builtin_bit_cast(bf16x8, lds[4 * kTile * (first + k * W) + lane_lds]);
+    };
     int k = 0;
     for (; k < cnt % 3; ++k)
         tile(key(k));
     if (k < cnt) {
         bf16x8 Ra = key(k), Rb = key(k + 1), Rc;
+        if constexpr (kLds) {
+            for (; k + 4 < cnt; k += 3) {
+                Rc = key_in(k + 2);
+                __builtin_amdgcn_sched_barrier(0);
+                tile(Ra);
+                __builtin_amdgcn_sched_barrier(0);
+                Ra = key_in(k + 3);
+                __builtin_amdgcn_sched_barrier(0);
+                tile(Rb);
+                __builtin_amdgcn_sched_barrier(0);
+                Rb = key_in(k + 4);
+                __builtin_amdgcn_sched_barrier(0);
+                tile(Rc);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
         for (; k < cnt; k += 3) {
             Rc = key(k + 2);
             __builtin_amdgcn_sched_barrier(0);
