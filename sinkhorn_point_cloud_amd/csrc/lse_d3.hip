@@ -1031,9 +1031,10 @@ __global__ __launch_bounds__(kPairWaves *kWave) void lse3p_kernel(Side3 x, Side3
 // ---------------------------------------------------------------------------
 // Whole stages of a small batch of small pairs in one launch, each pair split
 // over work-groups (a single pair of 1024 points: 64 of them).  A launch per
-// half-iteration costs more than the half-iteration's own work there (its
-// fixed start and end cost is about 2.3 us; the work on 64 compute units is
-// well under that), so the stage runs in one launch instead:
+// half-iteration costs more than the half-iteration's own work there (a
+// separate launch took 4.5 us for a pair of 1024 points, of which the stream
+// itself is under 1 us on 64 compute units), so the stage runs in one launch
+// instead:
 // work-group (b, part) owns rows 16 part .. 16 part + 15 of both sides of pair
 // b, keeps both sides' key records in LDS (as the per-pair launch does) and,
 // per half-iteration, streams all keys against its 16 rows, W waves each
