@@ -1098,6 +1098,28 @@ def test_hvp_matches_oracle(B, n, m, d, dtype, eps, zw):
         assert rel_inf(host(HV)[p], HVo[p]) <= 1e-4
 
 
+@pytest.mark.parametrize("B,n,m,d,dtype,eps,iters", [(1, 1000, 1100, 3, "f32", 0.1, 2000),
+                                                    (1, 1000, 900, 64, "bf16", 0.5, 200),
+                                                    (2, 700, 650, 64, "bf16", 1.0, 200)])
+def test_hvp_matches_oracle_at_a_thousand_points(B, n, m, d, dtype, eps, iters):
+    # the product against the oracle's dense one at sizes that span many row
+    # blocks and key splits of either path (fp64 passes for d = 3, matrix cores
+    # for bf16 features), with ragged sides
+    c = workloads.random_case(22, B, n, m, d, weights="dirichlet", dtype=dtype)
+    fo, go = oracle.potentials(c["X"], c["Y"], c["a"], c["b"], eps=[eps], iters=[iters])
+    f32, g32 = fo.astype(np.float32), go.astype(np.float32)
+    V = np.random.default_rng(3).normal(size=(B, n, d)).astype(np.float32)
+    X, Y = points(c)
+    HV, res = sk.hvp(X, Y, dev(c["a"]), dev(c["b"]), dev(f32), dev(g32), eps, dev(V),
+                     cg_iters=300)
+    torch.cuda.synchronize()
+    HVo = oracle.hvp(c["X"], c["Y"], c["a"], c["b"], f32.astype(np.float64),
+                     g32.astype(np.float64), np.float32(eps), V)
+    assert np.all(host(res) < 1e-4), host(res)
+    for p in range(B):
+        assert rel_inf(host(HV)[p], HVo[p]) <= 1e-4
+
+
 def hvp_case(seed, B, n, m, d, eps, iters=2000, dtype="bf16"):
     c = workloads.random_case(seed, B, n, m, d, weights="dirichlet", dtype=dtype)
     fo, go = oracle.potentials(c["X"], c["Y"], c["a"], c["b"], eps=[eps], iters=[iters])
