@@ -304,6 +304,33 @@ def test_split_stage_launch_is_deterministic():
         assert torch.equal(u, v)
 
 
+def test_split_stage_launches_on_two_streams_at_once():
+    # two small batches on two streams at the same time: each split stage
+    # launch takes at most half of the compute units (64 and 120 work-groups
+    # here), so both fit on the chip together and neither's waits run out; each
+    # result equals its run alone bit for bit
+    sched = dict(eps=[0.1, 0.02], iters=[5, 20])
+    cases = [workloads.random_case(730, 1, 1024, 1000, 3, weights="dirichlet"),
+             workloads.random_case(731, 2, 700, 900, 3, weights="dirichlet")]
+    args = []
+    for c in cases:
+        X, Y = points(c)
+        args.append((X, Y, dev(c["a"]), dev(c["b"])))
+    refs = [sk.potentials(*a, **sched) for a in args]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    for a, st in zip(args, streams):
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            outs.append(sk.potentials(*a, **sched))
+    torch.cuda.synchronize()
+    for out, ref in zip(outs, refs):
+        for u, v in zip(out, ref):
+            assert torch.isfinite(u).all()
+            assert torch.equal(u, v)
+
+
 def test_split_stage_launch_wait_that_runs_out_gives_nan():
     # the hand-over waits are bounded: with the limit set so that every wait
     # fails at once (the host-side test hook), the launch still ends and the
