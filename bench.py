@@ -362,19 +362,19 @@ def main():
     assert not sparse or int(nnz_dev) <= coo[0].numel(), "plan outgrew its buffers"
 
     if d == 3:
-        # the library runs whole stages per pair in one launch when the batch has at
-        # least one pair per compute unit and both padded clouds hold <= 8192 points,
-        # and whole stages of a small batch split over work-groups of 16 rows when
-        # both padded clouds hold <= 1024 points and those work-groups fit on half of
-        # the compute units
-        pad = lambda k: (k + 63) // 64 * 64
-        cus = torch.cuda.get_device_properties(dev).multi_processor_count
-        per_pair = (not args.valu_scores and B >= cus and pad(n) <= 8192 and pad(m) <= 8192)
-        split = (not args.valu_scores and not per_pair and pad(n) <= 1024 and pad(m) <= 1024
-                 and 2 * B * (max(pad(n), pad(m)) // 16) <= cus)
-        pairwise = per_pair or split   # one launch per stage
-        kernel = ("lse3_kernel" if args.valu_scores else "lse3p_kernel" if per_pair else
-                  "lse3s_kernel" if split else "lse3m_kernel")
+        # how the library runs the iterations for these sizes on this device: one
+        # launch per half-iteration, or one per eps stage (a work-group per pair for
+        # large batches, each pair over 16-row work-groups for small ones)
+        import ctypes
+
+        lib = sk.load_library()
+        lib.sinkhorn_probe_potentials_path.argtypes = [ctypes.c_int] * 5 + [ctypes.c_uint]
+        lib.sinkhorn_probe_potentials_path.restype = ctypes.c_int
+        shape = lib.sinkhorn_probe_potentials_path(
+            B, n, m, d, dt, sk.SK_VALU_SCORES if args.valu_scores else 0)
+        assert 0 <= shape <= 3, f"launch shape query: {shape}"
+        kernel = ("lse3m_kernel", "lse3p_kernel", "lse3s_kernel", "lse3_kernel")[shape]
+        pairwise = shape in (1, 2)   # one launch per stage
     else:
         pairwise = False
         kernel = "lseFs_kernel" if dt == sk.SK_BF16 and d % 32 == 0 else "lseF_kernel"

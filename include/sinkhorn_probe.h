@@ -56,6 +56,24 @@ int sinkhorn_probe_rates(int kind, int blocks, int iters, float *sink,
  */
 long long sinkhorn_probe_wait_limit(long long microseconds);
 
+/*
+ * How sinkhorn_potentials runs its iterations for these sizes on the current
+ * device, so that a measurement names the kernel it times [FS Methodologie 2:
+ * one fused pass per update]:
+ *   0  d = 3, one launch per half-iteration, scores on the matrix cores
+ *   1  d = 3, one launch per eps stage, one work-group per pair (batches of at
+ *      least one pair per compute unit, clouds of at most 8192 points)
+ *   2  d = 3, one launch per eps stage, each pair over 16-row work-groups that
+ *      hand over their biases (clouds of at most 1024 points, the work-groups
+ *      on at most half of the compute units)
+ *   3  d = 3 with SK_VALU_SCORES: one launch per half-iteration, vector scores
+ *   4  the feature path (d != 3)
+ * Returns -1 for sizes, dtype or d that sinkhorn_potentials refuses, -2 when
+ * no HIP device is current.  B, n, m, d, dtype and flags mean what they mean
+ * for sinkhorn_potentials; nothing is launched.
+ */
+int sinkhorn_probe_potentials_path(int B, int n, int m, int d, int dtype, unsigned flags);
+
 #ifdef __cplusplus
 }
 #endif

@@ -3,6 +3,7 @@
 #include "common.h"
 #include "hvp.h"
 #include "sinkhorn.h"
+#include "sinkhorn_probe.h"
 
 #include <math.h>
 #include <stdarg.h>
@@ -59,6 +60,20 @@ bool shape_ok(int B, int n, int m, int d)
 bool path3(int dtype, int d) { return (dtype == SK_F32 || dtype == SK_BF16) && d == 3; }
 
 bool supported(int dtype, int d) { return path3(dtype, d) || lseF_supported(dtype, d); }
+
+// How the iterations of a d = 3 solve run on the current device (the value of
+// sinkhorn_probe_potentials_path): 0 one launch per half-iteration on the
+// matrix cores, 1 one launch per stage with a work-group per pair, 2 one
+// launch per stage with each pair over 16-row work-groups, 3 one launch per
+// half-iteration with vector scores.
+int d3_launch_shape(int B, int n_pad, int m_pad, bool mfma)
+{
+    if (!mfma)
+        return 3;
+    if (lse3_pairwise(B, n_pad, m_pad))
+        return 1;
+    return lse3_split_parts(B, n_pad, m_pad) ? 2 : 0;
+}
 
 struct PotWs {
     // d = 3 path
@@ -382,9 +397,10 @@ int run_potentials(const void *X, const void *Y, int dtype, const float *a, cons
     const double c0 = (double)scale_of(first >= 0 ? eps[first] : 1.0f);
     hipError_t e;
     const bool p3 = path3(dtype, d);
-    const bool pairwise = p3 && mfma && lse3_pairwise(B, np, mp);
+    const int shape = p3 ? d3_launch_shape(B, np, mp, mfma) : -1;
+    const bool pairwise = shape == 1;
     // work-groups per pair of the split stage launch (0: not used)
-    const int split = p3 && mfma && !pairwise ? lse3_split_parts(B, np, mp) : 0;
+    const int split = shape == 2 ? lse3_split_parts(B, np, mp) : 0;
     // the caller's f and g are the state of the iteration
     Side3 sx3{w.px, f, w.l2a, w.kxrec, w.qxrec, n, np, w.xredo, split ? w.xxch : nullptr};
     Side3 sy3{w.py, g, w.l2b, w.kyrec, w.qyrec, m, mp, w.yredo, split ? w.yxch : nullptr};
@@ -540,6 +556,18 @@ const char *sinkhorn_status_string(int s)
 }
 
 const char *sinkhorn_last_error(void) { return g_err; }
+
+int sinkhorn_probe_potentials_path(int B, int n, int m, int d, int dtype, unsigned flags)
+{
+    if (!shape_ok(B, n, m, d) || !supported(dtype, d))
+        return -1;
+    if (!path3(dtype, d))
+        return 4;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return -2;
+    return d3_launch_shape(B, round_up(n, kPad), round_up(m, kPad), !(flags & SK_VALU_SCORES));
+}
 
 int sinkhorn_potentials(const void *X, const void *Y, int dtype, const float *a, const float *b,
                         int B, int n, int m, int d, const float *eps, const int *iters,

@@ -326,7 +326,8 @@ def test_plan_buffer_checks():
 def test_rate_probe_is_declared_exported_and_checks_arguments(lib):
     text = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
     names = re.findall(r"\b(sinkhorn_\w+)\s*\(", text)
-    assert names == ["sinkhorn_probe_rates", "sinkhorn_probe_wait_limit"]
+    assert names == ["sinkhorn_probe_rates", "sinkhorn_probe_wait_limit",
+                     "sinkhorn_probe_potentials_path"]
     out = os.popen(f"nm -D --defined-only {sk.library_path()}").read()
     for name in names:
         assert re.search(rf"\bT {name}$", out, flags=re.M), name
@@ -341,3 +342,19 @@ def test_rate_probe_is_declared_exported_and_checks_arguments(lib):
     assert f(0, 8, 0, DUMMY, DUMMY, ctypes.byref(hz), None) == 1
     assert f(0, 8, 10, None, DUMMY, ctypes.byref(hz), None) == 1
     assert f(0, 8, 10, DUMMY, DUMMY, None, None) == 1
+
+
+def test_launch_shape_query_refuses_what_potentials_refuses(lib):
+    # sizes, dtypes and dimensions that sinkhorn_potentials refuses give -1; the
+    # feature path needs no device to be named (4); the d = 3 shapes depend on
+    # the device's compute units, and without a device the query says so (-2)
+    f = lib.sinkhorn_probe_potentials_path
+    f.argtypes = [ctypes.c_int] * 5 + [ctypes.c_uint]
+    f.restype = ctypes.c_int
+    assert f(0, 10, 10, 3, sk.SK_F32, 0) == -1
+    assert f(1, 0, 10, 3, sk.SK_F32, 0) == -1
+    assert f(1, 10, 10, 3, 7, 0) == -1
+    assert f(1, 10, 10, 200, sk.SK_F32, 0) == -1
+    assert f(65536, 10, 10, 3, sk.SK_F32, 0) == -1
+    assert f(2, 300, 257, 64, sk.SK_BF16, 0) == 4
+    assert f(1, 1024, 1024, 3, sk.SK_F32, 0) == -2

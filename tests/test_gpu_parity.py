@@ -304,6 +304,23 @@ def test_split_stage_launch_is_deterministic():
         assert torch.equal(u, v)
 
 
+def test_launch_shape_query_names_the_launch_each_workload_takes():
+    # the probe that bench.py asks which kernel it times: on this device the
+    # five workloads' d = 3 shapes and the vector-score flag
+    import ctypes
+    lib = sk.load_library()
+    f = lib.sinkhorn_probe_potentials_path
+    f.argtypes = [ctypes.c_int] * 5 + [ctypes.c_uint]
+    f.restype = ctypes.c_int
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert f(1, 1024, 1024, 3, sk.SK_F32, 0) == (2 if 2 * 64 <= cus else 0)       # pair-1k
+    assert f(32, 2048, 2048, 3, sk.SK_F32, 0) == 0                                # sphere-2k
+    assert f(256, 1024, 1024, 3, sk.SK_F32, 0) == (1 if 256 >= cus else 0)        # blobs-1k
+    assert f(1, 65536, 65536, 3, sk.SK_F32, 0) == 0                               # gmm-64k
+    assert f(1, 50000, 60000, 64, sk.SK_BF16, 0) == 4                             # feat-50k
+    assert f(1, 1024, 1024, 3, sk.SK_F32, sk.SK_VALU_SCORES) == 3
+
+
 def test_split_stage_launches_on_two_streams_at_once():
     # two small batches on two streams at the same time: each split stage
     # launch takes at most half of the compute units (64 and 120 work-groups
