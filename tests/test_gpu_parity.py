@@ -272,6 +272,10 @@ SPLIT = [  # (B, n, m, weights, zero weights, eps, iters)
     # most work-groups own no row of the short side
     (2, 17, 650, "dirichlet", 0, [0.2, 0.03], [4, 6]),
     (1, 1024, 16, "dirichlet", 0, [0.05], [7]),
+    # 32 small pairs of 4 work-groups each (the batch at the half-chip limit)
+    (32, 50, 60, "dirichlet", 0, [0.2, 0.05], [3, 5]),
+    # one point on one side: 60 of the 64 work-groups own no row of it
+    (2, 1, 1000, "uniform", 0, [0.1], [6]),
 ]
 
 
