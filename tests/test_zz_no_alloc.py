@@ -79,6 +79,10 @@ def test_noalloc_feature_and_per_pair_paths():
     # bf16 features on the matrix cores, then a batch with whole stages per pair
     c = workloads.random_case(74, 1, 8192, 1000, 64, dtype="bf16", spread=0.25)
     _compare(c, [0.5, 0.05], [3, 4])
+    # whole stages split over 16-row work-groups, at the largest batch of
+    # 1024-point clouds that launch takes (two pairs on half of 256 compute units)
+    c = workloads.random_case(77, 2, 1000, 1024, 3, weights="dirichlet")
+    _compare(c, [0.1, 0.02], [3, 5])
     c = workloads.random_case(75, 256, 130, 140, 3, weights="dirichlet")
     _compare(c, [0.1, 0.02], [2, 4])
     c = workloads.random_case(76, 1, 64, 70, 3)
